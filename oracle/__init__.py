@@ -1,0 +1,258 @@
+"""CPU oracle for packed mixed-bit GEMV -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's cpu_baseline leg may use
+this package. The product library never imports it, and it imports nothing
+from the product. It wraps ``vbq_oracle.c`` (plain scalar C, fp64 dequantise
+and dot, binary32 quantiser decisions) through ctypes, and ``exact.py`` holds a
+pure-Python rational-arithmetic mini-oracle for tiny cases.
+
+Citations are in ``vbq_oracle.c``; every function here is a thin wrapper.
+Parity status: every function is pinned by tests under ``tests/`` (see the
+tests named ``test_oracle_*``); nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vbq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+             "-fexcess-precision=standard"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = C.CDLL(build())
+        _declare(_lib)
+    return _lib
+
+
+P = C.c_void_p
+I64 = C.c_int64
+
+
+def _declare(L):
+    L.orc_f64_to_f16.restype = C.c_uint16
+    L.orc_f64_to_f16.argtypes = [C.c_double]
+    L.orc_f16_to_f64.restype = C.c_double
+    L.orc_f16_to_f64.argtypes = [C.c_uint16]
+    for name in ("orc_f64_to_f16_array", "orc_f32_to_f16_array", "orc_f16_to_f64_array"):
+        getattr(L, name).restype = None
+        getattr(L, name).argtypes = [P, I64, P]
+    L.orc_quantize_group.restype = None
+    L.orc_quantize_group.argtypes = [P, C.c_int, P, P, P]
+    L.orc_quantize_matrix.restype = C.c_int
+    L.orc_quantize_matrix.argtypes = [P, P, C.c_int, C.c_int, P, P, P]
+    for name in ("orc_pack_group_canonical", "orc_unpack_group_canonical",
+                 "orc_pack_group_record", "orc_unpack_group_record"):
+        getattr(L, name).restype = None
+        getattr(L, name).argtypes = [P, C.c_int, P]
+    L.orc_layout_sizes.restype = C.c_int
+    L.orc_layout_sizes.argtypes = [P, C.c_int, C.c_int, P, P, P]
+    L.orc_pack.restype = C.c_int
+    L.orc_pack.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P]
+    L.orc_unpack.restype = C.c_int
+    L.orc_unpack.argtypes = [P, P, P, P, C.c_int, C.c_int, P, I64, P, P, P, P]
+    L.orc_gemv.restype = None
+    L.orc_gemv.argtypes = [P, P, P, C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]
+    L.orc_make_cell_residual.restype = None
+    L.orc_make_cell_residual.argtypes = [P, P, C.c_int, C.c_int, P]
+    L.orc_requant_verify.restype = None
+    L.orc_requant_verify.argtypes = [P, P, P, P, P, C.c_int, C.c_int, P, P]
+    L.orc_set_mutation.restype = None
+    L.orc_set_mutation.argtypes = [C.c_int]
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(P)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+@contextlib.contextmanager
+def mutation(m: int):
+    """Plant deliberate mistake number ``m`` in the oracle (tests of the pins)."""
+    lib().orc_set_mutation(int(m))
+    try:
+        yield
+    finally:
+        lib().orc_set_mutation(0)
+
+
+# ---- conversions -----------------------------------------------------------
+def f16_from_f64(v) -> np.ndarray:
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_f64_to_f16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def f16_from_f32(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_f32_to_f16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def f64_from_f16(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().orc_f16_to_f64_array(_p(h), h.size, _p(out))
+    return out
+
+
+# ---- quantiser and packing ----------------------------------------------------
+def quantize_group(w, b: int):
+    w = _c(w, np.float32)
+    assert w.shape == (64,)
+    s = np.zeros(1, np.uint16)
+    o = np.zeros(1, np.uint16)
+    q = np.zeros(64, np.uint8)
+    lib().orc_quantize_group(_p(w), int(b), _p(s), _p(o), _p(q))
+    return int(s[0]), int(o[0]), q
+
+
+def quantize_matrix(W, widths):
+    W = _c(W, np.float32)
+    widths = _c(widths, np.uint8)
+    N, K = W.shape
+    q = np.zeros((N, K), np.uint8)
+    s = np.zeros((N, K // 64), np.uint16)
+    o = np.zeros((N, K // 64), np.uint16)
+    if lib().orc_quantize_matrix(_p(W), _p(widths), N, K, _p(q), _p(s), _p(o)) != 0:
+        raise ValueError("bad shape or width")
+    return q, s, o
+
+
+def _group_words(fn, q, b):
+    q = _c(q, np.uint8)
+    w = np.zeros(2 * b, np.uint32)
+    getattr(lib(), fn)(_p(q), int(b), _p(w))
+    return w
+
+
+def _group_codes(fn, words, b):
+    words = _c(words, np.uint32)
+    assert words.shape == (2 * b,)
+    q = np.zeros(64, np.uint8)
+    getattr(lib(), fn)(_p(words), int(b), _p(q))
+    return q
+
+
+def pack_group_canonical(q, b):
+    return _group_words("orc_pack_group_canonical", q, b)
+
+
+def unpack_group_canonical(words, b):
+    return _group_codes("orc_unpack_group_canonical", words, b)
+
+
+def pack_group_record(q, b):
+    return _group_words("orc_pack_group_record", q, b)
+
+
+def unpack_group_record(words, b):
+    return _group_codes("orc_unpack_group_record", words, b)
+
+
+def layout_sizes(widths):
+    widths = _c(widths, np.uint8)
+    N, G = widths.shape
+    t = np.zeros(3, np.int64)
+    if lib().orc_layout_sizes(_p(widths), N, 64 * G, _p(t[0:1]), _p(t[1:2]), _p(t[2:3])) != 0:
+        raise ValueError("bad shape or width")
+    return int(t[0]), int(t[1]), int(t[2])
+
+
+def pack(W, widths) -> dict:
+    """Quantise and write the execution layout. Returns numpy arrays."""
+    W = _c(W, np.float32)
+    widths = _c(widths, np.uint8)
+    N, K = W.shape
+    T, R, C16 = layout_sizes(widths)
+    out = dict(tiles=np.zeros(4 * (T + 1), np.uint32), so=np.zeros(R, np.uint32),
+               meta=np.zeros(R, np.uint16), codes=np.zeros(4 * C16, np.uint32), N=N, K=K)
+    rc = lib().orc_pack(_p(W), _p(widths), N, K, _p(out["tiles"]), _p(out["so"]), _p(out["meta"]),
+                        _p(out["codes"]))
+    if rc != 0:
+        raise ValueError("bad shape or width")
+    return out
+
+
+def unpack(layout: dict, rows=None):
+    """Read a layout (numpy arrays) back to natural order.
+    Returns (codes [R][K] u8, scale16 [R][G], offset16 [R][G], widths [R][G])."""
+    N, K = int(layout["N"]), int(layout["K"])
+    G = K // 64
+    r = None if rows is None else _c(rows, np.int64)
+    nr = N if r is None else len(r)
+    q = np.zeros((nr, K), np.uint8)
+    s = np.zeros((nr, G), np.uint16)
+    o = np.zeros((nr, G), np.uint16)
+    w = np.zeros((nr, G), np.uint8)
+    arrs = [_c(layout[k], t) for k, t in (("tiles", np.uint32), ("so", np.uint32),
+                                           ("meta", np.uint16), ("codes", np.uint32))]
+    rc = lib().orc_unpack(*[_p(a) for a in arrs], N, K, _p(r), nr, _p(q), _p(s), _p(o), _p(w))
+    if rc != 0:
+        raise ValueError("inconsistent layout")
+    return q, s, o, w
+
+
+# ---- GEMV / GEMM / in-cell ------------------------------------------------------
+def gemv(q, s16, o16, x, resid=None, bf16: bool = False) -> np.ndarray:
+    """y [B][N] fp64 = x . Wdq^T with Wdq = s*q + o (+ resid), natural k order."""
+    q = _c(q, np.uint8)
+    s16 = _c(s16, np.uint16)
+    o16 = _c(o16, np.uint16)
+    x = _c(np.atleast_2d(x), np.uint16)
+    N, K = q.shape
+    B = x.shape[0]
+    assert x.shape[1] == K
+    r = None if resid is None else _c(resid, np.uint16)
+    if r is not None:
+        assert r.shape == (N, K)
+    y = np.zeros((B, N), np.float64)
+    lib().orc_gemv(_p(q), _p(s16), _p(o16), N, K, _p(x), B, int(bf16), _p(r), _p(y))
+    return y
+
+
+def make_cell_residual(u, s16) -> np.ndarray:
+    u = _c(u, np.float64)
+    s16 = _c(s16, np.uint16)
+    N, K = u.shape
+    r = np.zeros((N, K), np.uint16)
+    lib().orc_make_cell_residual(_p(u), _p(s16), N, K, _p(r))
+    return r
+
+
+def requant_verify(q, s16, o16, widths, r16, want_codes: bool = False):
+    """Returns (mismatches, out_of_cell, first_bad_index, q_prime or None)."""
+    q = _c(q, np.uint8)
+    N, K = q.shape
+    counts = np.zeros(3, np.uint64)
+    qp = np.zeros((N, K), np.uint8) if want_codes else None
+    lib().orc_requant_verify(_p(q), _p(_c(s16, np.uint16)), _p(_c(o16, np.uint16)),
+                             _p(_c(widths, np.uint8)), _p(_c(r16, np.uint16)), N, K, _p(counts), _p(qp))
+    return int(counts[0]), int(counts[1]), int(counts[2]), qp

@@ -1,0 +1,473 @@
+/*
+ * Plain, slow CPU oracle for packed mixed-bit GEMV (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only tests/, the smoke check and the benchmark's cpu_baseline leg may load
+ * this library. The product path never calls it and shares no code with it.
+ *
+ * What it follows:
+ *  - Variable bit-width quantisation (VBQ abstract, page "In-Cell Learning:
+ *    Language Models That Update Their Own Weights in Sequence Without
+ *    Changing the File They Ship"): every contiguous group of 64 weights along
+ *    K carries its own width b in {1,2,4,8}; the recipe maps to packed low-bit
+ *    storage; a fused dequantise-and-multiply gives "equal output", i.e. the
+ *    GEMV result is the plain product with the dequantised matrix.
+ *  - Asymmetric quantisation with a scale and an offset (SLQ abstract, page
+ *    thelatestinai.com/papers/2512.18934): w = scale*q + offset, q in [0, 2^b-1].
+ *  - CellFill (page "Nothing Changed but the Model: CellFill -- Bounded In-Cell
+ *    Learning for Bit-Identical, Revocable Updates to Quantized LLMs",
+ *    section Abstract): codes and scales frozen, a per-weight residual inside
+ *    each quantisation cell, re-quantisation returns the artifact bit-for-bit,
+ *    updates revocable by dropping the residual, drift bounded.
+ *
+ * Where the pages are silent the readings are: scale and offset stored as
+ * IEEE binary16; round-to-nearest (min/max) quantiser evaluated in binary32 with
+ * round-half-even; codes computed against the fp16-rounded scale and offset;
+ * a group whose scale rounds to zero gets all-zero codes.
+ *
+ * Precision: dequantisation and dot products are fp64 (exact widening of the
+ * fp16/bf16 inputs). The quantiser and the re-quantisation check decide
+ * integers, so they run in binary32 with the exact operation sequence stated
+ * at each function (no FMA contraction; build with -ffp-contract=off).
+ *
+ * Execution layout written and read here (the format the GPU library uses;
+ * this file implements it independently from its written specification):
+ *   rows are cut into tiles of 16; inside a tile the groups are split by
+ *   width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class, ordered by
+ *   (k-group ascending, row ascending). Each such "record" has
+ *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
+ *     meta : u16, row-in-tile in bits 0-3, k-group index in bits 4-15
+ *     codes: 2b u32 words; code j (0<=j<32) sits in word j/h at bit (j%h)*b and
+ *            code 32+j in the same word at bit 16+(j%h)*b, h = 16/b.
+ *   Per tile 4 u32: record base, code base (16-byte units), n0|n1<<16,
+ *   n2|n3<<16; one extra entry after the last tile holds the totals.
+ *   A tile's code area is the class segments 0..3 in order; segment c holds
+ *   its records in blocks of 64 (the last block may be short, m records):
+ *   b=1: record i at byte 8*i of the segment; b>=2: 16-byte chunk q of record
+ *   i (block-local index l) at block base + (q*m + l)*16. Segment 0 is padded
+ *   to a multiple of 16 bytes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_GROUP 64
+#define ORC_TILE 16
+
+/* Deliberate-mistake switch used only by the tests that show the pins catch
+ * plausible mistakes. 0 = correct oracle. */
+static int g_mut = 0;
+void orc_set_mutation(int m) { g_mut = m; }
+int orc_get_mutation(void) { return g_mut; }
+
+/* ------------------------------------------------------------------ */
+/* IEEE 754 binary16 / bfloat16 conversions, written from the format   */
+/* definition: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits */
+/* ------------------------------------------------------------------ */
+
+/* Round a double to the nearest binary16 value, ties to even. */
+uint16_t orc_f64_to_f16(double v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  double a = fabs(v);
+  if (isnan(v)) return 0x7E00u;
+  if (a >= 65520.0) return sign | 0x7C00u;            /* rounds past 65504 */
+  if (a < ldexp(1.0, -14)) {                            /* subnormal range */
+    double m = nearbyint(ldexp(a, 24));                 /* units of 2^-24 */
+    return sign | (uint16_t)m;                          /* m==1024 -> smallest normal */
+  }
+  int e2;
+  (void)frexp(a, &e2);                                  /* a = f * 2^e2, f in [0.5,1) */
+  int E = e2 - 1;                                       /* a in [2^E, 2^(E+1)) */
+  double m = nearbyint(ldexp(a, 10 - E));               /* in [1024, 2048] */
+  if (m >= 2048.0) { m = 1024.0; E += 1; }
+  if (E + 15 >= 31) return sign | 0x7C00u;
+  return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)m - 1024);
+}
+
+uint16_t orc_f32_to_f16(float f) { return orc_f64_to_f16((double)f); }
+
+double orc_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+float orc_f16_to_f32(uint16_t h) { return (float)orc_f16_to_f64(h); }
+
+double orc_bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------------ */
+/* Round-to-nearest asymmetric quantiser for one 64-weight group       */
+/* ------------------------------------------------------------------ */
+
+/* lo = min, hi = max (sequential scan, strict comparisons);
+ * L = 2^b - 1; scale16 = f16(f32(f32(hi - lo) / L)); offset16 = f16(lo);
+ * s, o = the fp16 values widened to f32;
+ * q_j = s == 0 ? 0 : clamp(rint(f32(f32(w_j - o) / s)), 0, L). */
+void orc_quantize_group(const float* w, int b, uint16_t* s16, uint16_t* o16, uint8_t* q) {
+  float lo = w[0], hi = w[0];
+  for (int j = 1; j < ORC_GROUP; ++j) {
+    if (w[j] < lo) lo = w[j];
+    if (w[j] > hi) hi = w[j];
+  }
+  int L = (1 << b) - 1;
+  float Lf = (float)L;
+  if (g_mut == 7) Lf = (float)(L + 1);                 /* mutation: wrong level count */
+  float range = hi - lo;
+  float sf = range / Lf;
+  *s16 = orc_f32_to_f16(sf);
+  *o16 = orc_f32_to_f16(lo);
+  float s = orc_f16_to_f32(*s16), o = orc_f16_to_f32(*o16);
+  for (int j = 0; j < ORC_GROUP; ++j) {
+    if (s == 0.0f) { q[j] = 0; continue; }
+    float t = (w[j] - o) / s;
+    float r = (g_mut == 3) ? floorf(t) : rintf(t);     /* mutation: truncation */
+    if (r < 0.0f) r = 0.0f;
+    if (r > (float)L) r = (float)L;
+    q[j] = (uint8_t)r;
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Canonical LSB-first packing of one group: code j at bit (j*b) mod 32 */
+/* of word floor(j*b/32); 2b words per group.                           */
+/* ------------------------------------------------------------------ */
+void orc_pack_group_canonical(const uint8_t* q, int b, uint32_t* words) {
+  for (int w = 0; w < 2 * b; ++w) words[w] = 0;
+  for (int j = 0; j < ORC_GROUP; ++j) {
+    int bit = j * b;
+    int sh = bit % 32;
+    if (g_mut == 4) sh = 32 - b - sh;                   /* mutation: MSB-first */
+    words[bit / 32] |= (uint32_t)q[j] << sh;
+  }
+}
+
+void orc_unpack_group_canonical(const uint32_t* words, int b, uint8_t* q) {
+  uint32_t mask = (1u << b) - 1u;
+  for (int j = 0; j < ORC_GROUP; ++j) {
+    int bit = j * b;
+    q[j] = (uint8_t)((words[bit / 32] >> (bit % 32)) & mask);
+  }
+}
+
+/* Record word layout (half-interleaved): see the file header. */
+void orc_pack_group_record(const uint8_t* q, int b, uint32_t* words) {
+  int h = 16 / b;
+  for (int w = 0; w < 2 * b; ++w) {
+    uint32_t lo = 0, hi = 0;
+    for (int f = 0; f < h; ++f) {
+      lo |= (uint32_t)q[w * h + f] << (f * b);
+      hi |= (uint32_t)q[32 + w * h + f] << (f * b);
+    }
+    words[w] = (g_mut == 9) ? (hi | (lo << 16)) : (lo | (hi << 16));  /* mutation: halves swapped */
+  }
+}
+
+void orc_unpack_group_record(const uint32_t* words, int b, uint8_t* q) {
+  int h = 16 / b;
+  uint32_t mask = (1u << b) - 1u;
+  for (int j = 0; j < 32; ++j) {
+    uint32_t w = words[j / h];
+    q[j] = (uint8_t)((w >> ((j % h) * b)) & mask);
+    q[32 + j] = (uint8_t)((w >> (16 + (j % h) * b)) & mask);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Execution layout: sizes, writer, reader                              */
+/* ------------------------------------------------------------------ */
+static int width_class(int b) {
+  switch (b) { case 1: return 0; case 2: return 1; case 4: return 2; case 8: return 3; default: return -1; }
+}
+static int class_bits(int c) { return 1 << c; }
+
+/* Bytes of a tile's code area for class counts n[4]. */
+static int64_t tile_code_bytes(const int64_t n[4]) {
+  int64_t s0 = ((8 * n[0]) + 15) / 16 * 16;
+  return s0 + 16 * n[1] + 32 * n[2] + 64 * n[3];
+}
+
+static int64_t seg_offset(const int64_t n[4], int c) {
+  int64_t off = 0;
+  if (c > 0) off += ((8 * n[0]) + 15) / 16 * 16;
+  if (c > 1) off += 16 * n[1];
+  if (c > 2) off += 32 * n[2];
+  return off;
+}
+
+/* Byte offset, from the start of class segment c, of the 16-byte chunk `chunk`
+ * of record i (b >= 2), or of the 8-byte record (b == 1, chunk 0). */
+static int64_t record_chunk_offset(int c, int64_t n_c, int64_t i, int chunk) {
+  int b = class_bits(c);
+  if (b == 1) return 8 * i;
+  int64_t blk = i / 64, l = i % 64;
+  int64_t m = n_c - 64 * blk;
+  if (m > 64) m = 64;
+  return blk * 64 * 8 * b + (chunk * m + l) * 16;
+}
+
+/* Counts the sizes of the layout. Returns 0, or -1 for a bad shape or width. */
+int orc_layout_sizes(const uint8_t* widths, int N, int K, int64_t* n_tiles, int64_t* n_records,
+                     int64_t* n_code16) {
+  if (N < 1 || K < 64 || K % 64 != 0 || K / 64 >= 4096) return -1;
+  int G = K / 64;
+  int64_t T = (N + ORC_TILE - 1) / ORC_TILE, code = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t n[4] = {0, 0, 0, 0};
+    for (int r = (int)(t * ORC_TILE); r < N && r < (t + 1) * ORC_TILE; ++r)
+      for (int g = 0; g < G; ++g) {
+        int c = width_class(widths[(int64_t)r * G + g]);
+        if (c < 0) return -1;
+        n[c]++;
+      }
+    code += tile_code_bytes(n) / 16;
+  }
+  *n_tiles = T;
+  *n_records = (int64_t)N * G;
+  *n_code16 = code;
+  return 0;
+}
+
+/* Quantises W (f32 [N][K]) with the per-group widths and writes the execution
+ * layout: tiles [(n_tiles+1)*4], so [n_records], meta [n_records],
+ * codes [n_code16*4]. Returns 0 or -1. */
+int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tiles, uint32_t* so,
+             uint16_t* meta, uint32_t* codes) {
+  int64_t T, R, C16;
+  if (orc_layout_sizes(widths, N, K, &T, &R, &C16) != 0) return -1;
+  int G = K / 64;
+  memset(codes, 0, (size_t)C16 * 16);
+  int64_t rec = 0, code16 = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    int r0 = (int)(t * ORC_TILE), r1 = r0 + ORC_TILE;
+    if (r1 > N) r1 = N;
+    int64_t n[4] = {0, 0, 0, 0};
+    for (int r = r0; r < r1; ++r)
+      for (int g = 0; g < G; ++g) n[width_class(widths[(int64_t)r * G + g])]++;
+    tiles[4 * t + 0] = (uint32_t)rec;
+    tiles[4 * t + 1] = (uint32_t)code16;
+    tiles[4 * t + 2] = (uint32_t)(n[0] | (n[1] << 16));
+    tiles[4 * t + 3] = (uint32_t)(n[2] | (n[3] << 16));
+    int64_t rec_c = rec;
+    uint8_t* tile_bytes = (uint8_t*)codes + code16 * 16;
+    for (int c = 0; c < 4; ++c) {
+      int b = class_bits(c);
+      int64_t i = 0;
+      for (int it = 0; it < G * (r1 - r0); ++it) {
+          /* (k-group, row) order; mutation 8 walks (row, k-group) instead */
+          int g = (g_mut == 8) ? it % G : it / (r1 - r0);
+          int r = r0 + ((g_mut == 8) ? it / G : it % (r1 - r0));
+          if (width_class(widths[(int64_t)r * G + g]) != c) continue;
+          uint16_t s16, o16;
+          uint8_t q[64];
+          uint32_t words[16];
+          orc_quantize_group(W + (int64_t)r * K + 64 * g, b, &s16, &o16, q);
+          orc_pack_group_record(q, b, words);
+          so[rec_c + i] = (uint32_t)s16 | ((uint32_t)o16 << 16);
+          meta[rec_c + i] = (uint16_t)((r - r0) | (g << 4));
+          uint8_t* seg = tile_bytes + seg_offset(n, c);
+          if (b == 1) {
+            memcpy(seg + record_chunk_offset(c, n[c], i, 0), words, 8);
+          } else {
+            for (int ch = 0; ch < b / 2; ++ch)
+              memcpy(seg + record_chunk_offset(c, n[c], i, ch), words + 4 * ch, 16);
+          }
+          ++i;
+        }
+      rec_c += n[c];
+    }
+    rec += n[0] + n[1] + n[2] + n[3];
+    code16 += tile_code_bytes(n) / 16;
+  }
+  tiles[4 * T + 0] = (uint32_t)rec;
+  tiles[4 * T + 1] = (uint32_t)code16;
+  tiles[4 * T + 2] = 0;
+  tiles[4 * T + 3] = 0;
+  return 0;
+}
+
+/* Reads the execution layout back into natural order: codes [N][K], and per
+ * group scale16/offset16/width [N][G]. Rows listed in `rows` only (n_rows of
+ * them) when rows != NULL; outputs are then [n_rows][...] in that order.
+ * Returns 0, or -1 if the layout is inconsistent (a group missing or repeated,
+ * a meta field out of range). */
+int orc_unpack(const uint32_t* tiles, const uint32_t* so, const uint16_t* meta, const uint32_t* codes,
+               int N, int K, const int64_t* rows, int64_t n_rows, uint8_t* q_out, uint16_t* s_out,
+               uint16_t* o_out, uint8_t* w_out) {
+  if (N < 1 || K < 64 || K % 64 != 0) return -1;
+  int G = K / 64;
+  int64_t nr = rows ? n_rows : N;
+  for (int64_t i = 0; i < nr * G; ++i) w_out[i] = 0;
+  for (int64_t ri = 0; ri < nr; ++ri) {
+    int64_t row = rows ? rows[ri] : ri;
+    if (row < 0 || row >= N) return -1;
+    int64_t t = row / ORC_TILE;
+    int64_t n[4] = {tiles[4 * t + 2] & 0xFFFF, tiles[4 * t + 2] >> 16, tiles[4 * t + 3] & 0xFFFF,
+                    tiles[4 * t + 3] >> 16};
+    int64_t rec = tiles[4 * t + 0];
+    const uint8_t* tile_bytes = (const uint8_t*)codes + (int64_t)tiles[4 * t + 1] * 16;
+    for (int c = 0; c < 4; ++c) {
+      int b = class_bits(c);
+      const uint8_t* seg = tile_bytes + seg_offset(n, c);
+      for (int64_t i = 0; i < n[c]; ++i) {
+        uint16_t m = meta[rec + i];
+        int64_t r = t * ORC_TILE + (m & 15);
+        int g = m >> 4;
+        if (r != row) continue;
+        if (g >= G) return -1;
+        if (w_out[ri * G + g] != 0) return -1;
+        uint32_t words[16];
+        if (b == 1) memcpy(words, seg + record_chunk_offset(c, n[c], i, 0), 8);
+        else
+          for (int ch = 0; ch < b / 2; ++ch)
+            memcpy(words + 4 * ch, seg + record_chunk_offset(c, n[c], i, ch), 16);
+        uint8_t q[64];
+        orc_unpack_group_record(words, b, q);
+        memcpy(q_out + ri * K + 64 * g, q, 64);
+        s_out[ri * G + g] = (uint16_t)(so[rec + i] & 0xFFFF);
+        o_out[ri * G + g] = (uint16_t)(so[rec + i] >> 16);
+        w_out[ri * G + g] = (uint8_t)b;
+      }
+      rec += n[c];
+    }
+    for (int g = 0; g < G; ++g)
+      if (w_out[ri * G + g] == 0) return -1;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantise + dot, fp64, natural k order                              */
+/* ------------------------------------------------------------------ */
+
+/* Wdq[n][k] = s_g*q + o_g (+ r[n][k]), exact widening of the fp16 inputs. */
+static double dequant(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, const uint16_t* resid,
+                      int64_t n, int64_t k, int K) {
+  int G = K / 64;
+  int64_t g = n * G + k / 64;
+  double s = orc_f16_to_f64(s16[g]);
+  double o = orc_f16_to_f64(o16[g]);
+  if (g_mut == 1) o = 0.0;                              /* mutation: offset dropped */
+  double w = s * (double)q[n * K + k] + o;
+  if (resid) {
+    double r = orc_f16_to_f64(resid[n * K + k]);
+    w += (g_mut == 6) ? -r : r;                         /* mutation: residual sign */
+  }
+  return w;
+}
+
+/* y[b][n] = sum_k x[b][k] * Wdq[n][k] for n < N (rows of the natural arrays),
+ * x fp16 [B][K] (or bf16 when x_is_bf16), y fp64 [B][N]. */
+void orc_gemv(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, int N, int K,
+              const uint16_t* x, int B, int x_is_bf16, const uint16_t* resid, double* y) {
+  double* xd = (double*)malloc(sizeof(double) * (size_t)B * K);
+  for (int64_t i = 0; i < (int64_t)B * K; ++i) xd[i] = x_is_bf16 ? orc_bf16_to_f64(x[i]) : orc_f16_to_f64(x[i]);
+  for (int64_t n = 0; n < N; ++n)
+    for (int b = 0; b < B; ++b) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        int64_t kx = (g_mut == 2) ? (k ^ 1) : k;        /* mutation: wrong x index */
+        acc += xd[(int64_t)b * K + kx] * dequant(q, s16, o16, resid, n, k, K);
+      }
+      y[(int64_t)b * N + n] = acc;
+    }
+  free(xd);
+}
+
+/* ------------------------------------------------------------------ */
+/* In-cell residual and the re-quantisation check (binary32)            */
+/* ------------------------------------------------------------------ */
+
+/* r16[n][k] = f16(u[n][k] * s_g) with the product in fp64. */
+void orc_make_cell_residual(const double* u, const uint16_t* s16, int N, int K, uint16_t* r16) {
+  int G = K / 64;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      r16[n * K + k] = orc_f64_to_f16(u[n * K + k] * orc_f16_to_f64(s16[n * G + k / 64]));
+}
+
+/* For every weight, in binary32 with this operation order:
+ *   s, o, r = widened fp16; deq = f32(f32(s*q) + o); v = f32(deq + r);
+ *   q' = s == 0 ? 0 : clamp(rint(f32(f32(v - o) / s)), 0, L)
+ *   mismatch   : q' != q
+ *   out of cell: s > 0 ? |r| >= f32(0.5*s) : r != 0
+ * Scales and offsets are carried through unchanged (frozen).
+ * counts[0] = mismatches, counts[1] = out of cell, counts[2] = smallest linear
+ * index n*K+k that has either (UINT64_MAX if none). q_prime (natural order)
+ * may be NULL. */
+void orc_requant_verify(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, const uint8_t* widths,
+                        const uint16_t* r16, int N, int K, uint64_t* counts, uint8_t* q_prime) {
+  int G = K / 64;
+  uint64_t mism = 0, ooc = 0, first = UINT64_MAX;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t gi = n * G + k / 64;
+      int L = (1 << widths[gi]) - 1;
+      float s = orc_f16_to_f32(s16[gi]), o = orc_f16_to_f32(o16[gi]);
+      float r = orc_f16_to_f32(r16[n * K + k]);
+      float qf = (float)q[n * K + k];
+      float sq = s * qf;
+      float deq = sq + o;
+      float v = deq + r;
+      int qp;
+      if (s == 0.0f) qp = 0;
+      else {
+        float d = v - o;
+        float t = d / s;
+        float rr = rintf(t);
+        if (rr < 0.0f) rr = 0.0f;
+        if (rr > (float)L) rr = (float)L;
+        qp = (int)rr;
+      }
+      int bad_code = qp != (int)q[n * K + k];
+      int bad_cell;
+      if (s > 0.0f) {
+        float half = 0.5f * s;
+        bad_cell = (g_mut == 5) ? (fabsf(r) > half) : (fabsf(r) >= half);  /* mutation: boundary */
+      } else {
+        bad_cell = r != 0.0f;
+      }
+      mism += (uint64_t)bad_code;
+      ooc += (uint64_t)bad_cell;
+      if ((bad_code || bad_cell) && (uint64_t)(n * K + k) < first) first = (uint64_t)(n * K + k);
+      if (q_prime) q_prime[n * K + k] = (uint8_t)qp;
+    }
+  counts[0] = mism;
+  counts[1] = ooc;
+  counts[2] = first;
+}
+
+/* ------------------------------------------------------------------ */
+/* Array helpers for the Python wrapper                                 */
+/* ------------------------------------------------------------------ */
+void orc_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_f16(v[i]);
+}
+void orc_f32_to_f16_array(const float* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(v[i]);
+}
+void orc_f16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f64(h[i]);
+}
+/* Quantises every group of W [N][K] with widths [N][G] into natural-order
+ * codes [N][K] and scale16/offset16 [N][G]. Returns 0 or -1. */
+int orc_quantize_matrix(const float* W, const uint8_t* widths, int N, int K, uint8_t* q, uint16_t* s16,
+                        uint16_t* o16) {
+  if (N < 1 || K < 64 || K % 64 != 0) return -1;
+  int G = K / 64;
+  for (int64_t n = 0; n < N; ++n)
+    for (int g = 0; g < G; ++g) {
+      int b = widths[n * G + g];
+      if (width_class(b) < 0) return -1;
+      orc_quantize_group(W + n * K + 64 * g, b, &s16[n * G + g], &o16[n * G + g], q + n * K + 64 * g);
+    }
+  return 0;
+}

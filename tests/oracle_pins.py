@@ -1,0 +1,445 @@
+"""Pins that tie the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError on failure. ``test_oracle_pins``
+runs them; ``test_oracle_mutations`` plants each deliberate mistake in the
+oracle and checks that at least one pin fails, which shows that the pins
+would catch a dropped term, a wrong sign or index, a wrong rounding or a
+wrong bit order.
+
+Sources of truth used here (none of them is the oracle's own formula):
+  * numpy's independent IEEE binary16 conversion;
+  * brute-force nearest-level search in exact rational arithmetic;
+  * groups built on an exactly representable grid (closed form);
+  * hand-written bit patterns of LSB-first packing;
+  * a hand-worked layout example;
+  * exact integer matvec (int64) and exact rational dot products;
+  * closed-form bounds of the in-cell residual (CellFill abstract:
+    residual strictly inside the cell, bit-identical re-quantisation,
+    revocable, bounded drift).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle import exact
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# binary16 conversion vs numpy (an independent implementation)
+# --------------------------------------------------------------------------
+def pin_f16_conversion():
+    r = _rng(1)
+    mags = 10.0 ** r.uniform(-9, 5.2, 100_000)
+    vals = r.choice([-1.0, 1.0], mags.size) * mags
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    f = h.view(np.float16).astype(np.float64)
+    mids = (f[:-1] + f[1:]) / 2                       # exact ties
+    special = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, 2.0 ** -24, 2.0 ** -25,
+                        3 * 2.0 ** -25, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25])
+    vals = np.concatenate([vals, mids, -mids, f, -f, special, -special])
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    got = oracle.f16_from_f64(vals)
+    assert np.array_equal(got, want), "f64->f16 differs from numpy"
+    v32 = vals.astype(np.float32)
+    with np.errstate(over="ignore"):
+        want32 = v32.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f16_from_f32(v32), want32), "f32->f16 differs from numpy"
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (allh & 0x7C00) != 0x7C00
+    dec = oracle.f64_from_f16(allh[finite])
+    assert np.array_equal(dec, allh[finite].view(np.float16).astype(np.float64)), "f16 decode"
+
+
+# --------------------------------------------------------------------------
+# Quantiser: brute-force nearest level, exact grids, scale/offset nearness
+# --------------------------------------------------------------------------
+def pin_rtn_nearest_level(trials=(60, 40, 20, 6)):
+    r = _rng(11)
+    checked = 0
+    for b, n_trials in zip((1, 2, 4, 8), trials):
+        L = (1 << b) - 1
+        for _ in range(n_trials):
+            w = (r.standard_normal(64) * 0.02).astype(np.float32)
+            s16, o16, q = oracle.quantize_group(w, b)
+            s, o = exact.f16_value(s16), exact.f16_value(o16)
+            assert s > 0
+            for j in range(64):
+                wj = Fraction(float(w[j]))
+                t = (wj - o) / s
+                frac = t - math.floor(t)
+                if abs(frac - Fraction(1, 2)) < Fraction(1, 10 ** 4):
+                    continue                          # binary32 evaluation may round across .5
+                near = exact.nearest_levels(wj, s, o, L)
+                assert len(near) == 1 and int(q[j]) == near[0], (b, j, int(q[j]), near)
+                checked += 1
+    assert checked > 5000
+
+
+def pin_rtn_scale_offset_nearest():
+    """offset16 is the binary16 value nearest to min(w); scale16 is within half
+    a binary16 ulp (plus binary32 slop) of (max - min) / (2^b - 1)."""
+    r = _rng(12)
+    for b in (1, 2, 4, 8):
+        L = (1 << b) - 1
+        for _ in range(200):
+            w = (r.standard_normal(64) * 0.02).astype(np.float32)
+            s16, o16, _ = oracle.quantize_group(w, b)
+            lo, hi = Fraction(float(w.min())), Fraction(float(w.max()))
+            o = exact.f16_value(o16)
+            for nb in (o16 - 1, o16 + 1):
+                if 0 <= nb < 0x7C00 or 0x8000 <= nb < 0xFC00:
+                    assert abs(o - lo) <= abs(exact.f16_value(nb) - lo)
+            s = exact.f16_value(s16)
+            ratio = (hi - lo) / L
+            e = math.floor(math.log2(float(s)))
+            half_ulp = Fraction(2) ** (max(e, -14) - 11)
+            assert abs(s - ratio) <= half_ulp + ratio * Fraction(2) ** -22, (b, float(s), float(ratio))
+
+
+def pin_rtn_exact_grid():
+    """Weights placed exactly on an fp16 grid o + s*q (with both ends present)
+    must give back s, o and q exactly."""
+    r = _rng(13)
+    for b in (1, 2, 4, 8):
+        L = (1 << b) - 1
+        for _ in range(60):
+            s = np.float32(int(r.integers(1, 8)) * 2.0 ** -int(r.integers(6, 12)))
+            o = np.float32(-int(r.integers(0, 64)) * 2.0 ** -8)
+            qt = r.integers(0, L + 1, 64)
+            i0, i1 = r.choice(64, 2, replace=False)
+            qt[i0], qt[i1] = 0, L
+            w = (np.float64(o) + np.float64(s) * qt).astype(np.float32)
+            assert np.array_equal(w.astype(np.float64), np.float64(o) + np.float64(s) * qt)
+            s16, o16, q = oracle.quantize_group(w, b)
+            assert exact.f16_value(s16) == Fraction(float(s)), (b, s16, float(s))
+            assert exact.f16_value(o16) == Fraction(float(o))
+            assert np.array_equal(q, qt), b
+
+
+def pin_rtn_degenerate_group():
+    """A constant group has range 0: scale 0, offset = the value, codes 0."""
+    w = np.full(64, 0.0123, np.float32)
+    for b in (1, 2, 4, 8):
+        s16, o16, q = oracle.quantize_group(w, b)
+        assert s16 == 0 and (q == 0).all()
+        assert o16 == int(np.float32(0.0123).astype(np.float16).view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# Packing: hand-written LSB-first bit patterns and round trips
+# --------------------------------------------------------------------------
+def pin_canonical_lsb_first():
+    j = np.arange(64)
+    # b=1, codes 0,1,0,1,...: every odd bit set
+    assert list(oracle.pack_group_canonical(j % 2, 1)) == [0xAAAAAAAA] * 2
+    # b=2, codes 0,1,2,3 repeating: each byte is 0b11_10_01_00
+    assert list(oracle.pack_group_canonical(j % 4, 2)) == [0xE4E4E4E4] * 4
+    # b=4, codes j % 16: nibbles ascending from the low end
+    assert list(oracle.pack_group_canonical(j % 16, 4)) == [0x76543210, 0xFEDCBA98] * 4
+    # b=8, codes j: bytes ascending from the low end
+    assert list(oracle.pack_group_canonical(j, 8)) == [
+        (4 * i) | ((4 * i + 1) << 8) | ((4 * i + 2) << 16) | ((4 * i + 3) << 24) for i in range(16)]
+    # b=1, a single code at position 33 -> word 1, bit 1
+    q = np.zeros(64, np.uint8)
+    q[33] = 1
+    assert list(oracle.pack_group_canonical(q, 1)) == [0, 2]
+    r = _rng(14)
+    for b in (1, 2, 4, 8):
+        for _ in range(50):
+            q = r.integers(0, 1 << b, 64).astype(np.uint8)
+            assert np.array_equal(oracle.unpack_group_canonical(oracle.pack_group_canonical(q, b), b), q)
+
+
+def pin_record_half_interleaved():
+    j = np.arange(64)
+    # b=8, codes j: word w = q[2w] | q[2w+1]<<8 | q[32+2w]<<16 | q[33+2w]<<24
+    assert list(oracle.pack_group_record(j, 8)) == [
+        (2 * w) | ((2 * w + 1) << 8) | ((32 + 2 * w) << 16) | ((33 + 2 * w) << 24) for w in range(16)]
+    # b=1: codes 32..63 set, 0..31 clear -> high halves full
+    q = (j >= 32).astype(np.uint8)
+    assert list(oracle.pack_group_record(q, 1)) == [0xFFFF0000, 0xFFFF0000]
+    # b=1: only code 17 set -> word 1 (codes 16..31 low half), bit 1
+    q = np.zeros(64, np.uint8)
+    q[17] = 1
+    assert list(oracle.pack_group_record(q, 1)) == [0, 2]
+    # b=4, codes j % 16: word w low half = codes 4w..4w+3, high = codes 36+4w-4..
+    words = oracle.pack_group_record(j % 16, 4)
+    for w in range(8):
+        lo = sum(((4 * w + f) % 16) << (4 * f) for f in range(4))
+        hi = sum(((32 + 4 * w + f) % 16) << (4 * f) for f in range(4))
+        assert int(words[w]) == lo | (hi << 16)
+    r = _rng(15)
+    for b in (1, 2, 4, 8):
+        for _ in range(50):
+            q = r.integers(0, 1 << b, 64).astype(np.uint8)
+            assert np.array_equal(oracle.unpack_group_record(oracle.pack_group_record(q, b), b), q)
+
+
+# --------------------------------------------------------------------------
+# Layout: hand-worked example and structural invariants
+# --------------------------------------------------------------------------
+def pin_layout_worked_example():
+    """N=2, K=128, widths [[1,8],[2,1]] (hand-worked).
+    Tile 0 holds all four groups. Class 0 (1-bit) in (k-group,row) order:
+    (kg0,row0), (kg1,row1); class 1: (kg0,row1); class 3: (kg1,row0).
+    meta = row | kg<<4 -> [0, 17, 1, 16]. Code bytes: class 0 = 2*8 = 16,
+    class 1 = 16, class 3 = 64 -> 96 bytes = 6 units of 16."""
+    widths = np.array([[1, 8], [2, 1]], np.uint8)
+    r = _rng(16)
+    W = (r.standard_normal((2, 128)) * 0.02).astype(np.float32)
+    lay = oracle.pack(W, widths)
+    assert oracle.layout_sizes(widths) == (1, 4, 6)
+    assert list(lay["tiles"]) == [0, 0, 2 | (1 << 16), 0 | (1 << 16), 4, 6, 0, 0]
+    assert list(lay["meta"]) == [0, 17, 1, 16]
+    qs = {}
+    for (row, kg, b) in ((0, 0, 1), (1, 1, 1), (1, 0, 2), (0, 1, 8)):
+        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], b)
+        qs[(row, kg)] = (s16, o16, oracle.pack_group_record(q, b))
+    order = [(0, 0), (1, 1), (1, 0), (0, 1)]
+    assert list(lay["so"]) == [qs[k][0] | (qs[k][1] << 16) for k in order]
+    codes = lay["codes"]
+    assert list(codes[0:2]) == list(qs[(0, 0)][2]) and list(codes[2:4]) == list(qs[(1, 1)][2])
+    assert list(codes[4:8]) == list(qs[(1, 0)][2])
+    assert list(codes[8:24]) == list(qs[(0, 1)][2])   # one 8-bit record: 4 chunks, m = 1
+
+
+def pin_layout_block_chunks():
+    """Chunk placement inside a block of m records (b >= 2): chunk q of record l
+    sits at (q*m + l)*16 bytes. Checked on one tile with 3 four-bit records."""
+    widths = np.array([[4, 4, 4]], np.uint8)
+    W = (_rng(17).standard_normal((1, 192)) * 0.02).astype(np.float32)
+    lay = oracle.pack(W, widths)
+    codes = lay["codes"].reshape(-1, 4)               # 16-byte chunks
+    for kg in range(3):
+        _, _, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
+        words = oracle.pack_group_record(q, 4)
+        assert list(codes[0 * 3 + kg]) == list(words[0:4])
+        assert list(codes[1 * 3 + kg]) == list(words[4:8])
+
+
+def pin_layout_invariants():
+    r = _rng(18)
+    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70)]
+    for (N, K) in cases:
+        G = K // 64
+        widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G), p=[0.55, 0.2, 0.15, 0.1])
+        W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+        lay = oracle.pack(W, widths)
+        T, R, C16 = oracle.layout_sizes(widths)
+        assert T == (N + 15) // 16 and R == N * G
+        tiles = lay["tiles"].reshape(-1, 4)
+        # closed-form sizes and bases
+        rec = code = 0
+        for t in range(T):
+            rows = widths[16 * t:16 * t + 16]
+            n = [int((rows == b).sum()) for b in (1, 2, 4, 8)]
+            assert list(tiles[t]) == [rec, code, n[0] | (n[1] << 16), n[2] | (n[3] << 16)]
+            rec += sum(n)
+            code += (-(-8 * n[0] // 16) * 16 + 16 * n[1] + 32 * n[2] + 64 * n[3]) // 16
+            # per class: records sorted by (kg, row), each group once
+            base = int(tiles[t][0])
+            seen = set()
+            for c, b in enumerate((1, 2, 4, 8)):
+                m = lay["meta"][base:base + n[c]].astype(np.int64)
+                key = (m >> 4) * 16 + (m & 15)
+                assert np.all(np.diff(key) > 0)
+                for v in m:
+                    row, kg = 16 * t + (v & 15), v >> 4
+                    assert widths[row, kg] == b
+                    seen.add((row, kg))
+                base += n[c]
+            assert len(seen) == rows.size
+        assert list(tiles[T]) == [rec, code, 0, 0] and code == C16
+        # reading back gives the quantiser's output in natural order
+        q, s, o, w = oracle.unpack(lay)
+        q2, s2, o2 = oracle.quantize_matrix(W, widths)
+        assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(o, o2)
+        assert np.array_equal(w, widths)
+        rows = r.choice(N, min(N, 5), replace=False)
+        qr, sr, orr, wr = oracle.unpack(lay, rows)
+        assert np.array_equal(qr, q2[rows]) and np.array_equal(wr, widths[rows])
+
+
+# --------------------------------------------------------------------------
+# GEMV: exact integer case, exact rationals on tiny matrices
+# --------------------------------------------------------------------------
+def pin_exact_integer_matvec():
+    """All groups 8-bit with integer weights in [0,255] and both 0 and 255 in
+    every group: the quantiser must give scale 1, offset 0, codes = weights,
+    so y equals the int64 product exactly."""
+    r = _rng(19)
+    N, K = 96, 768
+    Wi = r.integers(0, 256, (N, K))
+    Wi[:, 0::64] = 0
+    Wi[:, 1::64] = 255
+    widths = np.full((N, K // 64), 8, np.uint8)
+    lay = oracle.pack(Wi.astype(np.float32), widths)
+    q, s, o, _ = oracle.unpack(lay)
+    assert (s == 0x3C00).all() and (o == 0).all()
+    xi = r.integers(-2, 3, (3, K))
+    y = oracle.gemv(q, s, o, xi.astype(np.float16).view(np.uint16))
+    assert np.array_equal(y, (xi @ Wi.T).astype(np.float64))
+
+
+def _tiny_case(seed, N, K, with_resid):
+    r = _rng(seed)
+    G = K // 64
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G))
+    widths.flat[:4] = [1, 2, 4, 8][:widths.size] if widths.size >= 4 else widths.flat[:4]
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    x = r.standard_normal((2, K)).astype(np.float16).view(np.uint16)
+    resid = None
+    if with_resid:
+        resid = oracle.make_cell_residual(r.uniform(-0.49, 0.49, (N, K)), np.repeat(s, 64, axis=1)[:, ::64])
+    return q, s, o, x, resid
+
+
+def pin_gemv_exact_rationals():
+    for seed, (N, K) in enumerate([(4, 64), (4, 128), (3, 192)]):
+        for with_resid in (False, True):
+            q, s, o, x, resid = _tiny_case(100 + seed, N, K, with_resid)
+            y = oracle.gemv(q, s, o, x, resid)
+            ye = exact.gemv_exact(q.tolist(), s.tolist(), o.tolist(), x.tolist(),
+                                  None if resid is None else resid.tolist())
+            for b in range(2):
+                for n in range(N):
+                    e = ye[b][n]
+                    assert abs(Fraction(float(y[b, n])) - e) <= abs(e) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 300), \
+                        (seed, with_resid, b, n, float(y[b, n]), float(e))
+
+
+def pin_gemm_bf16_exact():
+    r = _rng(21)
+    N, K = 3, 128
+    widths = np.array([[1, 8], [2, 4], [8, 1]], np.uint8)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    import synth
+    xb = synth.x_bf16(0, (99,), 3, K)
+    y = oracle.gemv(q, s, o, xb, bf16=True)
+    ye = exact.gemv_exact(q.tolist(), s.tolist(), o.tolist(), xb.tolist(), bf16=True)
+    for m in range(3):
+        for n in range(N):
+            assert abs(Fraction(float(y[m, n])) - ye[m][n]) <= abs(ye[m][n]) * Fraction(1, 10 ** 14)
+
+
+# --------------------------------------------------------------------------
+# In-cell residual: drift bound, revocation, re-quantisation check
+# --------------------------------------------------------------------------
+def _cell_case(seed, N=24, K=256, b=4):
+    r = _rng(seed)
+    widths = np.full((N, K // 64), b, np.uint8)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    s_full = np.repeat(s, 64, axis=1)
+    u = r.uniform(-0.49, 0.49, (N, K))
+    resid = oracle.make_cell_residual(u, s)
+    return r, widths, q, s, o, s_full, resid
+
+
+def pin_drift_bound_and_revocation():
+    r, widths, q, s, o, s_full, resid = _cell_case(30)
+    K = q.shape[1]
+    x = r.standard_normal((2, K)).astype(np.float16).view(np.uint16)
+    y0 = oracle.gemv(q, s, o, x)
+    yr = oracle.gemv(q, s, o, x, resid)
+    xd = oracle.f64_from_f16(x)
+    rd = oracle.f64_from_f16(resid)
+    sd = oracle.f64_from_f16(s_full)
+    drift = np.abs(yr - y0)
+    bound = np.abs(xd) @ np.abs(rd).T                 # sum_k |x_k| |r_nk|
+    cell = np.abs(xd) @ (sd / 2).T                    # sum_k |x_k| s_g(k) / 2
+    assert np.all(drift <= bound * (1 + 1e-12) + 1e-15)
+    assert np.all(bound < cell)
+    # the residual changes the output, and the change is linear in it
+    assert np.max(drift) > 0
+    lin = xd @ rd.T
+    assert np.allclose(yr - y0, lin, rtol=1e-9, atol=1e-12)
+    # revocation: dropping the residual gives back the base output bit-for-bit
+    assert np.array_equal(oracle.gemv(q, s, o, x, None), y0)
+
+
+def pin_requant_verify():
+    r, widths, q, s, o, s_full, resid = _cell_case(31)
+    N, K = q.shape
+    mism, ooc, first, qp = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    assert np.array_equal(qp, q)
+    # zero residual: trivially in every cell
+    zero = np.zeros_like(resid)
+    assert oracle.requant_verify(q, s, o, widths, zero)[:3] == (0, 0, 2 ** 64 - 1)
+    # |r| exactly half a cell is outside the (open) cell
+    planted = [(3, 5), (7, 130), (20, 255)]
+    bad = resid.copy()
+    for (n, k) in planted:
+        bad[n, k] = oracle.f16_from_f64(np.array([0.5]) * oracle.f64_from_f16(s_full[n, k:k + 1]))[0]
+    mism, ooc, first, _ = oracle.requant_verify(q, s, o, widths, bad)
+    assert ooc == len(planted) and first == min(n * K + k for n, k in planted)
+    # 0.6 of a cell at an interior code moves the code
+    interior = np.argwhere((q > 0) & (q < 15))
+    sel = interior[r.choice(len(interior), 5, replace=False)]
+    bad = resid.copy()
+    for n, k in sel:
+        bad[n, k] = oracle.f16_from_f64(np.array([0.6]) * oracle.f64_from_f16(s_full[n, k:k + 1]))[0]
+    mism, ooc, first, qp = oracle.requant_verify(q, s, o, widths, bad, want_codes=True)
+    assert mism == 5 and ooc == 5
+    for n, k in sel:
+        assert qp[n, k] == q[n, k] + 1
+    # A flipped bit in a served artifact: the check re-quantises against the
+    # artifact it is given, so it passes; the emitted codes then differ from the
+    # released ones in exactly that position (the bit-for-bit comparison).
+    q2 = q.copy()
+    q2[11, 77] ^= 1
+    mism, ooc, first, qp2 = oracle.requant_verify(q2, s, o, widths, resid, want_codes=True)
+    assert (mism, ooc) == (0, 0)
+    diff = np.argwhere(qp2 != q)
+    assert diff.tolist() == [[11, 77]]
+
+
+def pin_residual_inside_cell():
+    """The generated residual satisfies |r| < s/2 and so stays in the cell."""
+    _, _, q, s, o, s_full, resid = _cell_case(32)
+    rd = np.abs(oracle.f64_from_f16(resid))
+    sd = oracle.f64_from_f16(s_full)
+    assert np.all(rd <= 0.49 * sd * (1 + 2.0 ** -11)) and np.all(rd < 0.5 * sd)
+
+
+# --------------------------------------------------------------------------
+# Accounting (VBQ abstract: 69% of groups at 1 bit, LM head ~1.09 mean bits,
+# 131M model at 1.82 mean bits)
+# --------------------------------------------------------------------------
+def pin_mean_bits_accounting():
+    import synth
+    assert abs(synth.mean_bits(synth.MIX_DEFAULT) - 1.79) < 1e-12
+    assert abs(synth.mean_bits(synth.MIX_LM_HEAD) - 1.10) < 1e-12
+    w = synth.widths(0, (0, 0, 0), 768, 12, synth.MIX_DEFAULT)
+    mean = float(w.mean())
+    var = sum(p * (b - 1.79) ** 2 for b, p in synth.MIX_DEFAULT.items())
+    se = math.sqrt(var / w.size)
+    assert abs(mean - 1.79) < 4 * se and abs(mean - 1.82) < 4 * se + 0.03
+    assert abs(float((w == 1).mean()) - 0.69) < 0.03
+    # bytes of a layout: codes 8*sum(b) per group plus 4 (scale+offset) + 2 (meta)
+    lay_w = w[:64]
+    T, R, C16 = oracle.layout_sizes(lay_w)
+    code_bytes = 8 * int(lay_w.astype(np.int64).sum())
+    assert code_bytes <= 16 * C16 <= code_bytes + 8 * T
+
+
+ALL_PINS = [
+    pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
+    pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_half_interleaved,
+    pin_layout_worked_example, pin_layout_block_chunks, pin_layout_invariants,
+    pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
+    pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
+    pin_mean_bits_accounting,
+]

@@ -1,0 +1,45 @@
+"""The CPU oracle against facts fixed outside it (runs without a GPU)."""
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle
+
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin):
+    pin()
+
+
+# Each deliberate mistake planted in the oracle (see orc_set_mutation in
+# oracle/vbq_oracle.c) must make at least one pin fail.
+MUTATIONS = {
+    1: "dequantisation drops the offset",
+    2: "dot product reads the wrong x index",
+    3: "quantiser truncates instead of rounding",
+    4: "canonical packing is MSB-first",
+    5: "cell test uses > instead of >=",
+    6: "residual added with the wrong sign",
+    7: "scale divides by 2^b instead of 2^b - 1",
+    8: "records ordered by (row, k-group)",
+    9: "record halves swapped",
+}
+
+
+@pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
+def test_oracle_mutation_is_caught(m):
+    failed = []
+    with oracle.mutation(m):
+        for pin in ALL_PINS:
+            if pin.__name__ == "pin_f16_conversion":
+                continue
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+    assert failed, f"mutation {m} ({MUTATIONS[m]}) passed every pin"
