@@ -1,0 +1,184 @@
+/*
+ * vbq.h -- C ABI of the packed mixed-bit weight library for MI355X (gfx950).
+ *
+ * The library computes y = x . W^T for a frozen weight matrix W (N x K) that
+ * is stored group-quantised: every contiguous group of 64 weights along K has
+ * its own bit-width b in {1, 2, 4, 8}, an fp16 scale s and an fp16 offset o,
+ * and dequantises as w = s*q + o with integer code q in [0, 2^b - 1].
+ *   - Per-group widths from {1,2,4,8} on 64-weight groups, packed low-bit
+ *     storage and a fused dequantise-and-multiply for bandwidth-bound decode:
+ *     VBQ abstract, page "In-Cell Learning: Language Models That Update Their
+ *     Own Weights in Sequence Without Changing the File They Ship".
+ *   - Asymmetric (scale + offset) quantisation: SLQ abstract, page
+ *     thelatestinai.com/papers/2512.18934.
+ *   - Per-weight residual inside each quantisation cell, bit-identical
+ *     re-quantisation, revocation by dropping the residual: page "Nothing
+ *     Changed but the Model: CellFill -- Bounded In-Cell Learning for
+ *     Bit-Identical, Revocable Updates to Quantized LLMs", section Abstract.
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller allocates and frees every buffer. Buffers marked
+ *     "device" live in GPU memory of the current HIP device; "host" buffers
+ *     are ordinary CPU memory. The library keeps no state beyond a cached
+ *     kernel-attribute setup and never allocates device memory.
+ *   - Asynchrony: compute calls enqueue work on `stream` and return without
+ *     waiting. Argument errors are found before anything is enqueued: the
+ *     call returns a non-zero vbq_status and enqueues nothing. A failed kernel
+ *     launch returns VBQ_ERR_HIP. No C++ exception crosses this boundary.
+ *   - fp16 and bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Calls that share output buffers must not overlap in time.
+ *
+ * Execution layout of a packed matrix (see vbq_matrix):
+ *   Rows are cut into tiles of VBQ_TILE_ROWS = 16. Inside a tile the groups
+ *   are split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
+ *   ordered by (k-group ascending, row ascending), so that one wavefront
+ *   decodes groups of a single width and neighbouring lanes share k-groups.
+ *   Each such group is a "record" with
+ *     so[r]   : u32, fp16 scale bits 0-15, fp16 offset bits 16-31
+ *     meta[r] : u16, row within the tile bits 0-3, k-group index bits 4-15
+ *     codes   : 2b u32 words; with h = 16/b, code j (0 <= j < 32) of the group
+ *               sits in word j/h at bit (j%h)*b (LSB first) and code 32+j in
+ *               the same word at bit 16 + (j%h)*b.
+ *   tiles[4t..4t+3] = { first record of tile t, first 16-byte unit of its
+ *   codes, n0 | n1 << 16, n2 | n3 << 16 } where n_c counts its class-c
+ *   records; records of a tile are stored class 0..3 in order. Entry
+ *   t = n_tiles holds { total records, total 16-byte units, invalid-width
+ *   count, error flags }. A tile's code area holds the class segments 0..3
+ *   in order; a segment keeps its records in blocks of 64 (the last block may
+ *   hold m < 64): for b = 1 record i is 8 bytes at byte 8*i of the segment;
+ *   for b >= 2 the 16-byte chunk q of block-local record l sits at
+ *   block start + (q*m + l)*16. Segment 0 is padded to 16 bytes.
+ */
+#ifndef VBQ_H
+#define VBQ_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VBQ_ABI_VERSION 1
+#define VBQ_GROUP 64          /* weights per quantisation group (along K) */
+#define VBQ_TILE_ROWS 16      /* rows per layout tile */
+#define VBQ_MAX_GROUPS 4095   /* K / 64 must not exceed this */
+#define VBQ_MAX_BATCH 8       /* largest batch of vbq_gemv */
+
+typedef enum vbq_status {
+  VBQ_OK = 0,
+  VBQ_ERR_INVALID_ARG = 1,   /* null pointer or bad count */
+  VBQ_ERR_SHAPE = 2,         /* N < 1, K < 64, K % 64 != 0, K/64 > VBQ_MAX_GROUPS, M < 1 */
+  VBQ_ERR_BITWIDTH = 3,      /* a width not in {1,2,4,8} */
+  VBQ_ERR_ALIGNMENT = 4,     /* a buffer not aligned as documented */
+  VBQ_ERR_UNSUPPORTED = 5,   /* batch out of range, or the batch does not fit on-chip */
+  VBQ_ERR_CAPACITY = 6,      /* the layout does not match the buffers it was given */
+  VBQ_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed */
+} vbq_status;
+
+/* Descriptor of caller-owned device buffers holding one packed matrix.
+ * Sizes come from vbq_pack_query; vbq_pack fills the buffers. */
+typedef struct vbq_matrix {
+  int32_t n_rows;      /* N, output features */
+  int32_t n_cols;      /* K, input features, multiple of 64 */
+  int64_t n_tiles;     /* ceil(N / 16) */
+  int64_t n_records;   /* N * K / 64 (one record per group) */
+  int64_t n_code16;    /* size of `codes` in 16-byte units */
+  uint32_t* tiles;     /* device, (n_tiles + 1) * 4 words, 4-byte aligned */
+  uint32_t* so;        /* device, n_records words, 4-byte aligned */
+  uint16_t* meta;      /* device, n_records halfwords, 2-byte aligned */
+  uint32_t* codes;     /* device, n_code16 * 4 words, 16-byte aligned */
+} vbq_matrix;
+
+/* Sizes of the buffers of a packed matrix, plus accounting figures. */
+typedef struct vbq_layout_sizes {
+  int64_t n_tiles;
+  int64_t n_records;
+  int64_t n_code16;
+  int64_t code_bits;   /* sum of widths * 64: bits of codes proper */
+  int64_t groups_by_width[4]; /* number of groups of width 1, 2, 4, 8 */
+} vbq_layout_sizes;
+
+/* ABI version (VBQ_ABI_VERSION of the built library). */
+int vbq_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* vbq_status_string(int status);
+
+/* Host-only sizing of the execution layout.
+ * widths_host: host, N x K/64 uint8 in natural (row, k-group) order.
+ * out: host. Returns VBQ_ERR_SHAPE or VBQ_ERR_BITWIDTH on bad input.
+ * Touches no GPU. */
+vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_layout_sizes* out);
+
+/* Quantise W and write the execution layout (offline step).
+ * Quantiser, per group of 64 (VBQ abstract for the groups and widths; SLQ
+ * abstract for scale + offset), in binary32 without contraction:
+ *   lo = min, hi = max; scale16 = fp16(f32(hi - lo) / (2^b - 1));
+ *   offset16 = fp16(lo); s, o = those fp16 values;
+ *   q = s == 0 ? 0 : clamp(rint(f32(w - o) / s), 0, 2^b - 1)   (ties to even).
+ * W: device, N x K float32, row-major, 4-byte aligned.
+ * widths: device, N x K/64 uint8 in natural order (the same values given to
+ *   vbq_pack_query for the sizes in m).
+ * m: host descriptor; n_rows, n_cols, n_tiles, n_records, n_code16 and the four
+ *   device pointers must be set. Invalid widths or a layout larger than the
+ *   buffers are detected on the device: nothing is then written beyond the
+ *   tile table, and vbq_matrix_check reports the error. */
+vbq_status vbq_pack(const float* W, const uint8_t* widths, const vbq_matrix* m, hipStream_t stream);
+
+/* Waits for `stream` and reads the totals entry written by vbq_pack.
+ * Returns VBQ_OK, VBQ_ERR_BITWIDTH (invalid widths on the device) or
+ * VBQ_ERR_CAPACITY (layout larger than the descriptor's sizes). */
+vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
+
+/* Fused dequantise-and-multiply (VBQ abstract, "custom fused
+ * dequantize-and-multiply kernels" for bandwidth-bound decode):
+ *   y[b][n] = sum_k x[b][k] * (s*q + o + r[n][k])     (r only if residual != NULL)
+ * accumulated in fp32; codes are never expanded in memory.
+ * x: device, B x K fp16, 4-byte aligned. B in [1, VBQ_MAX_BATCH]; B x K must fit
+ *   on-chip (B * K <= 57344 without residual, <= 36864 with).
+ * residual: device, N x K fp16 row-major (natural order), 16-byte aligned, or
+ *   NULL. NULL serves the released artifact; the in-cell update (CellFill
+ *   abstract) is revoked simply by passing NULL.
+ * y: device, B x N float32, 4-byte aligned; fully overwritten. */
+vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
+                    hipStream_t stream);
+
+/* Several independent GEMVs in one launch (same batch B, no residual):
+ * y_i = x_i . W_i^T for i < count. ms, xs, ys: host arrays of `count` entries
+ * (descriptors and device pointers as for vbq_gemv). Used to run all
+ * projections of a decoder layer, or a whole stack, as one launch. */
+vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
+                            int32_t B, hipStream_t stream);
+
+/* Batched dequantise-and-multiply for M >= 64 tokens: tiles of W are decoded
+ * to bf16 in LDS and contracted on MFMA with fp32 accumulation.
+ *   y[m][n] = sum_k x[m][k] * bf16(s*q + o)
+ * x_bf16: device, M x K bfloat16, 16-byte aligned. y: device, M x N float32,
+ * 16-byte aligned, fully overwritten. */
+vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, float* y, hipStream_t stream);
+
+/* Re-quantisation check of an in-cell update (CellFill abstract: codes and
+ * scales of the release frozen, residual strictly inside each cell,
+ * re-quantisation returns the released artifact bit-for-bit). For every weight,
+ * in binary32 without contraction, with s, o, r the fp16 values:
+ *   deq = f32(s*q) + o;  v = deq + r;
+ *   q'  = s == 0 ? 0 : clamp(rint((v - o) / s), 0, 2^b - 1)
+ *   mismatch    when q' != q
+ *   out of cell when s > 0 ? |r| >= 0.5*s : r != 0
+ * Scales and offsets are frozen (carried through unchanged).
+ * residual: device, N x K fp16 natural order, 16-byte aligned.
+ * result: device, 3 x uint64, 8-byte aligned: { mismatches, out-of-cell
+ *   count, smallest linear index n*K + k with either, or UINT64_MAX }.
+ * requant_codes: device, same size and layout as m->codes (16-byte aligned),
+ *   receives the re-quantised codes so the artifact can be compared
+ *   bit-for-bit; may be NULL. */
+vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
+                               uint32_t* requant_codes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VBQ_H */

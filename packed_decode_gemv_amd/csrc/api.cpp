@@ -1,0 +1,197 @@
+// C ABI entry points: argument checks, sizing and kernel dispatch.
+// Every check happens before anything is enqueued; no C++ exception leaves
+// these functions.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "vbq_common.h"
+
+using namespace vbq;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+vbq_status check_shape(int32_t N, int32_t K) {
+  if (N < 1 || K < kGroup || K % kGroup != 0 || K / kGroup > VBQ_MAX_GROUPS) return VBQ_ERR_SHAPE;
+  return VBQ_OK;
+}
+
+vbq_status check_matrix(const vbq_matrix* m) {
+  if (!m) return VBQ_ERR_INVALID_ARG;
+  vbq_status st = check_shape(m->n_rows, m->n_cols);
+  if (st != VBQ_OK) return st;
+  if (m->n_tiles != (m->n_rows + kTile - 1) / kTile) return VBQ_ERR_CAPACITY;
+  if (m->n_records != (int64_t)m->n_rows * (m->n_cols / kGroup)) return VBQ_ERR_CAPACITY;
+  if (m->n_code16 < 1 || m->n_code16 > 0xFFFFFFFFll) return VBQ_ERR_CAPACITY;
+  if (!m->tiles || !m->so || !m->meta || !m->codes) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(m->tiles, 4) || !aligned(m->so, 4) || !aligned(m->meta, 2) || !aligned(m->codes, 16))
+    return VBQ_ERR_ALIGNMENT;
+  return VBQ_OK;
+}
+
+vbq_status from_hip(hipError_t e) { return e == hipSuccess ? VBQ_OK : VBQ_ERR_HIP; }
+
+constexpr size_t kLdsLimit = 160 * 1024;
+
+// Tiles per workgroup: aim for at least ~2 workgroups per CU across the launch,
+// then as few tiles per workgroup as that allows (x staging is per workgroup).
+int pick_tiles_per_wg(int64_t n_tiles, int64_t total_tiles) {
+  const int64_t target_wg = 2048;
+  int tpw = (int)std::max<int64_t>(1, total_tiles / target_wg);
+  tpw = std::min(tpw, gemv_max_tiles_per_wg());
+  (void)n_tiles;
+  return tpw;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vbq_abi_version(void) { return VBQ_ABI_VERSION; }
+
+const char* vbq_status_string(int s) {
+  switch (s) {
+    case VBQ_OK: return "ok";
+    case VBQ_ERR_INVALID_ARG: return "invalid argument";
+    case VBQ_ERR_SHAPE: return "bad shape";
+    case VBQ_ERR_BITWIDTH: return "width not in {1,2,4,8}";
+    case VBQ_ERR_ALIGNMENT: return "misaligned buffer";
+    case VBQ_ERR_UNSUPPORTED: return "unsupported size";
+    case VBQ_ERR_CAPACITY: return "layout does not match its buffers";
+    case VBQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_layout_sizes* out) {
+  if (!widths_host || !out) return VBQ_ERR_INVALID_ARG;
+  vbq_status st = check_shape(N, K);
+  if (st != VBQ_OK) return st;
+  const int G = K / kGroup;
+  const int64_t T = (N + kTile - 1) / kTile;
+  int64_t code16 = 0, bits = 0, byw[4] = {0, 0, 0, 0};
+  for (int64_t t = 0; t < T; ++t) {
+    uint32_t n[4] = {0, 0, 0, 0};
+    const int64_t r1 = std::min<int64_t>((t + 1) * kTile, N);
+    for (int64_t i = t * kTile * G; i < r1 * G; ++i) {
+      const int c = class_of_width(widths_host[i]);
+      if (c < 0) return VBQ_ERR_BITWIDTH;
+      n[c]++;
+      bits += 64 * widths_host[i];
+    }
+    for (int c = 0; c < 4; ++c) byw[c] += n[c];
+    code16 += (int64_t)(tile_code_bytes(n[0], n[1], n[2], n[3]) / 16);
+  }
+  out->n_tiles = T;
+  out->n_records = (int64_t)N * G;
+  out->n_code16 = code16;
+  out->code_bits = bits;
+  for (int c = 0; c < 4; ++c) out->groups_by_width[c] = byw[c];
+  return VBQ_OK;
+}
+
+vbq_status vbq_pack(const float* W, const uint8_t* widths, const vbq_matrix* m, hipStream_t stream) {
+  if (!W || !widths) return VBQ_ERR_INVALID_ARG;
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!aligned(W, 16)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_pack(W, widths, *m, stream));
+}
+
+vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  uint32_t tot[4] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(tot, m->tiles + 4 * m->n_tiles, sizeof(tot), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return VBQ_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return VBQ_ERR_HIP;
+  if (tot[3] & kFlagInvalidWidth) return VBQ_ERR_BITWIDTH;
+  if (tot[3] & kFlagCapacity) return VBQ_ERR_CAPACITY;
+  if ((int64_t)tot[0] != m->n_records || (int64_t)tot[1] != m->n_code16) return VBQ_ERR_CAPACITY;
+  return VBQ_OK;
+}
+
+static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, const uint16_t* resid,
+                            float* const* ys, int32_t B, hipStream_t stream) {
+  if (count < 1 || !ms || !xs || !ys) return VBQ_ERR_INVALID_ARG;
+  if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
+  int max_groups = 0;
+  int64_t total_tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    vbq_status st = check_matrix(&ms[i]);
+    if (st != VBQ_OK) return st;
+    if (!xs[i] || !ys[i]) return VBQ_ERR_INVALID_ARG;
+    if (!aligned(xs[i], 4) || !aligned(ys[i], 4)) return VBQ_ERR_ALIGNMENT;
+    max_groups = std::max(max_groups, ms[i].n_cols / kGroup);
+    total_tiles += ms[i].n_tiles;
+  }
+  if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
+  const int tpw = pick_tiles_per_wg(0, total_tiles);
+  const size_t lds = gemv_lds_bytes(B, max_groups, resid != nullptr, tpw);
+  if (lds > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
+  // Split into launches of at most kMaxMats matrices.
+  for (int base = 0; base < count; base += kMaxMats) {
+    GemvLaunch L;
+    memset(&L, 0, sizeof(L));
+    const int nm = std::min(kMaxMats, count - base);
+    int wg = 0;
+    for (int i = 0; i < nm; ++i) {
+      const vbq_matrix& m = ms[base + i];
+      GemvMat& g = L.mats[i];
+      g.tiles = m.tiles;
+      g.so = m.so;
+      g.meta = m.meta;
+      g.codes = m.codes;
+      g.x = xs[base + i];
+      g.resid = resid;
+      g.y = ys[base + i];
+      g.n_rows = m.n_rows;
+      g.n_groups = m.n_cols / kGroup;
+      g.n_tiles = (int32_t)m.n_tiles;
+      g.tiles_per_wg = tpw;
+      g.wg_begin = wg;
+      wg += (int)((m.n_tiles + tpw - 1) / tpw);
+    }
+    L.n_mats = nm;
+    L.max_groups = max_groups;
+    hipError_t e = launch_gemv(L, B, resid != nullptr, wg, lds, stream);
+    if (e != hipSuccess) return VBQ_ERR_HIP;
+  }
+  return VBQ_OK;
+}
+
+vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
+                    hipStream_t stream) {
+  return gemv_impl(1, m, &x, residual, &y, B, stream);
+}
+
+vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
+                            int32_t B, hipStream_t stream) {
+  return gemv_impl(count, ms, xs, nullptr, ys, B, stream);
+}
+
+vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, float* y, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!x_bf16 || !y) return VBQ_ERR_INVALID_ARG;
+  if (M < 1) return VBQ_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return VBQ_ERR_ALIGNMENT;
+  hipError_t e = launch_gemm(*m, x_bf16, M, y, stream);
+  if (e == hipErrorNotSupported) return VBQ_ERR_UNSUPPORTED;
+  return from_hip(e);
+}
+
+vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
+                               uint32_t* requant_codes, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!residual || !result) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(residual, 16) || !aligned(result, 8)) return VBQ_ERR_ALIGNMENT;
+  if (requant_codes && !aligned(requant_codes, 16)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_verify(*m, residual, result, requant_codes, stream));
+}
+
+}  // extern "C"

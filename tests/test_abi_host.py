@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI library (no GPU needed): it loads, exports
+every function that include/vbq.h declares, sizes layouts like the oracle,
+and rejects bad arguments before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "vbq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("vbq_pack", "vbq_gemv", "vbq_gemm", "cell_requant_verify", "vbq_pack_query",
+              "vbq_gemv_batched", "vbq_matrix_check", "vbq_abi_version", "vbq_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import packed_decode_gemv_amd as vbq
+    lib = C.CDLL(vbq.LIB_PATH)
+    for n in header_functions():
+        assert hasattr(lib, n), f"{n} declared in vbq.h but not exported"
+    assert vbq.abi_version() == 1
+    assert vbq.lib.vbq_status_string(3) == b"width not in {1,2,4,8}"
+
+
+@pytest.mark.parametrize("shape", [(1, 64), (16, 128), (17, 192), (33, 640), (100, 64 * 37)])
+def test_pack_query_matches_oracle(shape):
+    import oracle
+    import packed_decode_gemv_amd as vbq
+    N, K = shape
+    r = np.random.default_rng(N + K)
+    w = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64), p=[0.6, 0.2, 0.15, 0.05])
+    s = vbq.pack_query(w)
+    assert (s.n_tiles, s.n_records, s.n_code16) == oracle.layout_sizes(w)
+    assert s.code_bits == 64 * int(w.astype(np.int64).sum())
+    assert list(s.groups_by_width) == [int((w == b).sum()) for b in (1, 2, 4, 8)]
+
+
+def test_pack_query_rejects_bad_input():
+    import packed_decode_gemv_amd as vbq
+    w = np.ones((4, 2), np.uint8)
+    out = vbq.vbq_layout_sizes()
+    p = w.ctypes.data_as(C.c_void_p)
+    assert vbq.lib.vbq_pack_query(p, 4, 100, C.byref(out)) == 2          # K % 64
+    assert vbq.lib.vbq_pack_query(p, 0, 128, C.byref(out)) == 2          # N < 1
+    assert vbq.lib.vbq_pack_query(None, 4, 128, C.byref(out)) == 1       # null
+    w[1, 1] = 3
+    assert vbq.lib.vbq_pack_query(p, 4, 128, C.byref(out)) == 3          # width 3
+
+
+def _fake_matrix(vbq, N=32, K=128, align=256):
+    # Descriptor with plausible (never dereferenced) device addresses.
+    T = (N + 15) // 16
+    base = 0x7F0000000000
+    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, base, base + 4096, base + 8192, base + align * 64)
+
+
+def test_compute_calls_reject_bad_arguments_without_a_gpu():
+    import packed_decode_gemv_amd as vbq
+    L = vbq.lib
+    m = _fake_matrix(vbq)
+    x = C.c_void_p(0x7F0000100000)
+    y = C.c_void_p(0x7F0000200000)
+    assert L.vbq_gemv(None, x, 1, None, y, None) == 1
+    assert L.vbq_gemv(C.byref(m), None, 1, None, y, None) == 1
+    assert L.vbq_gemv(C.byref(m), x, 0, None, y, None) == 5
+    assert L.vbq_gemv(C.byref(m), x, 9, None, y, None) == 5
+    assert L.vbq_gemv(C.byref(m), C.c_void_p(0x7F0000100002), 1, None, y, None) == 4
+    assert L.vbq_gemv(C.byref(m), x, 1, C.c_void_p(0x7F0000300008), y, None) == 4
+    bad = _fake_matrix(vbq, K=100)
+    assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 2
+    bad = _fake_matrix(vbq)
+    bad.n_tiles = 5
+    assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 6
+    bad = _fake_matrix(vbq, align=8)
+    bad.codes = 0x7F0000000008
+    assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 4
+    big = _fake_matrix(vbq, K=64 * 4000)
+    assert L.vbq_gemv(C.byref(big), x, 8, None, y, None) == 5      # batch does not fit on-chip
+    assert L.vbq_gemm(C.byref(m), x, 0, y, None) == 2
+    assert L.vbq_gemm(C.byref(m), C.c_void_p(0x7F0000100004), 64, y, None) == 4
+    assert L.cell_requant_verify(C.byref(m), None, y, None, None) == 1
+    assert L.cell_requant_verify(C.byref(m), x, C.c_void_p(0x7F0000200004), None, None) == 4
+    assert L.vbq_pack(None, x, C.byref(m), None) == 1
+    assert L.vbq_pack(C.c_void_p(0x7F0000100004), x, C.byref(m), None) == 4
+    ms = (vbq.vbq_matrix * 2)(m, m)
+    xs = (C.c_void_p * 2)(x.value, x.value)
+    ys = (C.c_void_p * 2)(y.value, None)
+    assert L.vbq_gemv_batched(2, ms, xs, ys, 1, None) == 1
+    assert L.vbq_gemv_batched(0, ms, xs, ys, 1, None) == 1

@@ -1,0 +1,309 @@
+"""Parity of the HIP library against the CPU oracle (needs an MI355X).
+
+Bars: the packed layout (tiles, scale/offset, meta, codes) and the
+re-quantisation check are bit-exact; GEMV/GEMM outputs are within 2e-3
+relative L2 of the fp64 oracle over each call's whole output.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def vbq():
+    import torch
+    assert torch.cuda.is_available()
+    import packed_decode_gemv_amd as m
+    return m
+
+
+def _t(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def rand_case(N, K, seed, p=(0.55, 0.2, 0.15, 0.1), B=1):
+    r = np.random.default_rng(seed)
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64), p=list(p))
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = r.standard_normal((B, K)).astype(np.float16).view(np.uint16)
+    return W, widths, x
+
+
+def layout_equal(pm, lay):
+    got = pm.host_layout()
+    for k in ("tiles", "so", "meta", "codes"):
+        assert got[k].shape == lay[k].shape, k
+        if not np.array_equal(got[k], lay[k]):
+            bad = np.flatnonzero(got[k] != lay[k])
+            raise AssertionError(f"{k}: {bad.size} differences, first at {bad[:5]}")
+
+
+SHAPES = [(1, 64), (15, 128), (16, 192), (17, 320), (100, 448), (768, 768), (300, 64 * 70), (40, 14336)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{n}x{k}" for n, k in SHAPES])
+def test_pack_bit_exact(vbq, shape):
+    N, K = shape
+    W, widths, _ = rand_case(N, K, seed=N * 7 + K)
+    print(f"case pack {N}x{K}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    layout_equal(pm, oracle.pack(W, widths))
+
+
+GEMV_CASES = [(1, 64, 1), (15, 128, 1), (17, 320, 2), (100, 448, 3), (768, 768, 1), (300, 64 * 70, 4),
+              (40, 14336, 1), (64, 4096, 8), (33, 2048, 5), (48, 1024, 6), (20, 512, 7)]
+
+
+@pytest.mark.parametrize("case", GEMV_CASES, ids=[f"{n}x{k}b{b}" for n, k, b in GEMV_CASES])
+def test_gemv_parity(vbq, case):
+    import torch
+    N, K, B = case
+    W, widths, x = rand_case(N, K, seed=N + 3 * K + B, B=B)
+    print(f"case gemv {N}x{K} B={B}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    y = vbq.vbq_gemv(pm, _t(x, torch.float16)).cpu().numpy()
+    q, s, o = oracle.quantize_matrix(W, widths)
+    ref = oracle.gemv(q, s, o, x)
+    assert y.shape == ref.shape
+    assert rel_l2(y, ref) <= TOL
+    # also per batch row
+    for b in range(B):
+        assert rel_l2(y[b], ref[b]) <= TOL
+
+
+def test_gemv_exact_integer(vbq):
+    """All groups 8-bit with integer weights (0 and 255 in every group) and small
+    integer x: scale 1, offset 0, every partial sum an exact integer in fp32,
+    so the GPU result must equal the int64 product exactly."""
+    import torch
+    r = np.random.default_rng(5)
+    N, K = 768, 768
+    Wi = r.integers(0, 256, (N, K))
+    Wi[:, 0::64] = 0
+    Wi[:, 1::64] = 255
+    widths = np.full((N, K // 64), 8, np.uint8)
+    xi = r.integers(-2, 3, (4, K))
+    pm = vbq.vbq_pack(_t(Wi.astype(np.float32)), widths)
+    y = vbq.vbq_gemv(pm, _t(xi.astype(np.float16).view(np.uint16), torch.float16)).cpu().numpy()
+    assert np.array_equal(y.astype(np.int64), xi @ Wi.T)
+    assert np.array_equal(y, (xi @ Wi.T).astype(np.float32))
+
+
+def test_gemv_deterministic_and_batched(vbq):
+    import torch
+    mats = []
+    for i, (N, K) in enumerate([(1024, 4096), (96, 2048), (4096, 1024)]):
+        W, widths, x = rand_case(N, K, seed=40 + i, B=2)
+        mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
+    singles = [vbq.vbq_gemv(pm, x) for pm, x in mats]
+    again = [vbq.vbq_gemv(pm, x) for pm, x in mats]
+    batched = vbq.vbq_gemv_batched([pm for pm, _ in mats], [x for _, x in mats])
+    torch.cuda.synchronize()
+    for a, b, c in zip(singles, again, batched):
+        assert torch.equal(a, b), "GEMV not deterministic"
+        assert torch.equal(a, c), "batched launch differs from single launches"
+
+
+def test_gemv_batch_rows_match_single_rows(vbq):
+    import torch
+    W, widths, x = rand_case(512, 4096, seed=77, B=4)
+    pm = vbq.vbq_pack(_t(W), widths)
+    xt = _t(x, torch.float16)
+    y4 = vbq.vbq_gemv(pm, xt)
+    for b in range(4):
+        y1 = vbq.vbq_gemv(pm, xt[b:b + 1].contiguous())
+        assert torch.allclose(y1[0], y4[b], rtol=1e-5, atol=1e-6)
+
+
+def _cell_inputs(N, K, seed, u_scale=1.0):
+    r = np.random.default_rng(seed)
+    widths = np.full((N, K // 64), 4, np.uint8)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    u = r.uniform(-0.49, 0.49, (N, K)) * u_scale
+    resid = oracle.make_cell_residual(u, s)
+    x = r.standard_normal((1, K)).astype(np.float16).view(np.uint16)
+    return W, widths, q, s, o, resid, x
+
+
+@pytest.mark.parametrize("shape", [(16, 256), (50, 1024), (33, 4096)])
+def test_residual_gemv_and_revocation(vbq, shape):
+    import torch
+    N, K = shape
+    W, widths, q, s, o, resid, x = _cell_inputs(N, K, seed=N + K)
+    pm = vbq.vbq_pack(_t(W), widths)
+    xt = _t(x, torch.float16)
+    rt = _t(resid, torch.float16)
+    y = vbq.vbq_gemv(pm, xt, residual=rt).cpu().numpy()
+    ref = oracle.gemv(q, s, o, x, resid)
+    assert rel_l2(y, ref) <= TOL
+    y0 = vbq.vbq_gemv(pm, xt).cpu().numpy()
+    assert rel_l2(y0, oracle.gemv(q, s, o, x)) <= TOL
+    # a zero residual serves the base weights
+    yz = vbq.vbq_gemv(pm, xt, residual=torch.zeros_like(rt)).cpu().numpy()
+    assert np.allclose(yz, y0, rtol=1e-6, atol=1e-6)
+
+
+def test_requant_verify_small(vbq):
+    import torch
+    N, K = 40, 1024
+    W, widths, q, s, o, resid, _ = _cell_inputs(N, K, seed=9)
+    pm = vbq.vbq_pack(_t(W), widths)
+    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    assert torch.equal(rq, pm.codes), "re-quantised artifact differs from the release"
+    # planted: exactly half a cell at three places, 0.6 of a cell at two interior codes
+    bad = resid.copy()
+    sf = oracle.f64_from_f16(np.repeat(s, 64, axis=1))
+    for (n, k) in [(3, 5), (17, 600), (39, 1023)]:
+        bad[n, k] = oracle.f16_from_f64(np.array([0.5 * sf[n, k]]))[0]
+    interior = np.argwhere((q > 0) & (q < 15))
+    for n, k in interior[[10, 2000]]:
+        bad[n, k] = oracle.f16_from_f64(np.array([0.6 * sf[n, k]]))[0]
+    ref = oracle.requant_verify(q, s, o, widths, bad, want_codes=True)
+    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(bad, torch.float16), requant_codes=True)
+    assert (mism, ooc, first) == ref[:3]
+    # half a cell can round the code across (ties to even), so >= 2 mismatches
+    assert ref[0] >= 2 and ref[1] == 5
+    # the emitted codes are the oracle's re-quantised codes, packed in the same layout
+    lay_rq = pm.host_layout()
+    lay_rq["codes"] = rq.cpu().numpy().view(np.uint32)
+    q_rq, _, _, _ = oracle.unpack(lay_rq)
+    assert np.array_equal(q_rq, ref[3])
+
+
+def test_requant_verify_mixed_widths(vbq):
+    import torch
+    N, K = 48, 2048
+    r = np.random.default_rng(21)
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    u = r.uniform(-0.7, 0.7, (N, K))              # some residuals leave their cells
+    resid = oracle.make_cell_residual(u, s)
+    pm = vbq.vbq_pack(_t(W), widths)
+    got = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    assert got[:3] == ref[:3]
+    assert ref[0] > 0 and ref[1] > 0
+    lay = pm.host_layout()
+    lay["codes"] = got[3].cpu().numpy().view(np.uint32)
+    assert np.array_equal(oracle.unpack(lay)[0], ref[3])
+
+
+def test_invalid_widths_on_device_are_reported(vbq):
+    import ctypes as C
+
+    import torch
+    N, K = 32, 256
+    W, widths, _ = rand_case(N, K, seed=3)
+    sizes = vbq.pack_query(widths)
+    pm = vbq.PackedMatrix(N, K, sizes)
+    bad = widths.copy()
+    bad[5, 2] = 3
+    st = vbq.lib.vbq_pack(C.c_void_p(_t(W).data_ptr()), C.c_void_p(_t(bad).data_ptr()), C.byref(pm.desc),
+                          vbq._stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert vbq.lib.vbq_matrix_check(C.byref(pm.desc), vbq._stream()) == 3
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (sampled rows where the oracle would be slow)
+# ---------------------------------------------------------------------------
+def _sample_rows(N, r, n=96):
+    rows = set(r.choice(N, min(N, n), replace=False).tolist())
+    rows.update([0, N - 1, (N // 16) * 16 - 1 if N >= 16 else 0])
+    return np.array(sorted(rows), np.int64)
+
+
+def _check_proj(vbq, cid, layer, pi, proj, B, full=False):
+    import torch
+    key = synth.proj_key(cid, layer, pi)
+    G = proj.k // 64
+    widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix)
+    W = synth.weights(synth.SEED, key, proj.n, proj.k)
+    x = synth.x_f16(synth.SEED, key, B, proj.k)
+    print(f"case workload {cid} layer {layer} {proj.name} {proj.n}x{proj.k} B={B}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    y = vbq.vbq_gemv(pm, _t(x, torch.float16)).cpu().numpy()
+    rows = np.arange(proj.n) if full else _sample_rows(proj.n, np.random.default_rng(pi + 100 * (layer + 1)))
+    q, s, o = oracle.quantize_matrix(W[rows], widths[rows])
+    ref = oracle.gemv(q, s, o, x)
+    assert rel_l2(y[:, rows], ref) <= TOL
+    # the GPU layout of those rows reads back to the oracle's codes and scales
+    qg, sg, og, wg = oracle.unpack(pm.host_layout(), rows)
+    assert np.array_equal(qg, q) and np.array_equal(sg, s) and np.array_equal(og, o)
+    assert np.array_equal(wg, widths[rows])
+    return pm
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_workload_1b_layer_full(vbq, B):
+    for pi, proj in enumerate(synth.C1.projs):
+        _check_proj(vbq, 1, 0, pi, proj, B, full=True)
+
+
+def test_workload_131m_projection_full(vbq):
+    _check_proj(vbq, 0, 0, 0, synth.C0.projs[0], 1, full=True)
+
+
+@pytest.mark.parametrize("pi", range(7))
+def test_workload_9b_layer_sampled(vbq, pi):
+    _check_proj(vbq, 3, 0, pi, synth.C3.projs[pi], 1)
+
+
+def test_workload_9b_lm_head_sampled(vbq):
+    _check_proj(vbq, 3, -1, 0, synth.C3.head, 1)
+
+
+def test_workload_9b_layer_batch4_sampled(vbq):
+    for pi in (0, 4, 6):
+        _check_proj(vbq, 3, 5, pi, synth.C3.projs[pi], 4)
+
+
+def test_workload_in_cell_full_size(vbq):
+    """4-bit release 14336 x 4096 with an in-cell residual: residual GEMV on
+    sampled rows, and the re-quantisation check over the whole matrix."""
+    import torch
+    proj = synth.C2.projs[0]
+    key = synth.proj_key(2, 0, 0)
+    N, K = proj.n, proj.k
+    widths = synth.widths(synth.SEED, key, N, K // 64, proj.mix)
+    W = synth.weights(synth.SEED, key, N, K)
+    x = synth.x_f16(synth.SEED, key, 1, K)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    u = synth.cell_u(synth.SEED, key, N, K)
+    resid = oracle.make_cell_residual(u, s)
+    print("case workload 2 in-cell 14336x4096", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    rt = _t(resid, torch.float16)
+    y = vbq.vbq_gemv(pm, _t(x, torch.float16), residual=rt).cpu().numpy()
+    rows = _sample_rows(N, np.random.default_rng(2))
+    ref = oracle.gemv(q[rows], s[rows], o[rows], x, resid[rows])
+    assert rel_l2(y[:, rows], ref) <= TOL
+    mism, ooc, first, rq = vbq.cell_requant_verify(pm, rt, requant_codes=True)
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    assert torch.equal(rq, pm.codes)
+    ref_v = oracle.requant_verify(q[rows], s[rows], o[rows], widths[rows], resid[rows])
+    assert ref_v[:2] == (0, 0)
