@@ -29,16 +29,19 @@
  *   - Calls that share output buffers must not overlap in time.
  *
  * Execution layout of a packed matrix (see vbq_matrix):
- *   Rows are cut into tiles of VBQ_TILE_ROWS = 16. Inside a tile the groups
- *   are split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
- *   ordered by (k-group ascending, row ascending), so that one wavefront
- *   decodes groups of a single width and neighbouring lanes share k-groups.
- *   Each such group is a "record" with
+ *   The matrix is cut into tiles of VBQ_TILE_ROWS = 16 rows by
+ *   VBQ_TILE_GROUPS = 64 k-groups (4096 columns); tile t = rt * KT + kt covers
+ *   rows 16rt.. and k-groups 64kt.., with KT = ceil(K / 4096). Inside a tile
+ *   the groups are split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside
+ *   a class, ordered by (k-group ascending, row ascending), so that one
+ *   wavefront decodes groups of a single width and neighbouring lanes share
+ *   k-groups. Each such group is a "record" with
  *     so[r]   : u32, fp16 scale bits 0-15, fp16 offset bits 16-31
- *     meta[r] : u16, row within the tile bits 0-3, k-group index bits 4-15
- *     codes   : 2b u32 words; with h = 16/b, code j (0 <= j < 32) of the group
- *               sits in word j/h at bit (j%h)*b (LSB first) and code 32+j in
- *               the same word at bit 16 + (j%h)*b.
+ *     meta[r] : u16, row within the tile bits 0-3, k-group index (of the
+ *               matrix) bits 4-15
+ *     codes   : 2b u32 words; with h = 16/b, the pair p = (code 2p, code 2p+1),
+ *               p < 32, sits in word p/h: code 2p at bit (p%h)*b (LSB first)
+ *               and code 2p+1 at bit 16 + (p%h)*b.
  *   tiles[4t..4t+3] = { first record of tile t, first 16-byte unit of its
  *   codes, n0 | n1 << 16, n2 | n3 << 16 } where n_c counts its class-c
  *   records; records of a tile are stored class 0..3 in order. Entry
@@ -63,6 +66,7 @@ extern "C" {
 #define VBQ_ABI_VERSION 1
 #define VBQ_GROUP 64          /* weights per quantisation group (along K) */
 #define VBQ_TILE_ROWS 16      /* rows per layout tile */
+#define VBQ_TILE_GROUPS 64    /* k-groups (of 64 weights) per layout tile */
 #define VBQ_MAX_GROUPS 4095   /* K / 64 must not exceed this */
 #define VBQ_MAX_BATCH 8       /* largest batch of vbq_gemv */
 
@@ -78,16 +82,20 @@ typedef enum vbq_status {
 } vbq_status;
 
 /* Descriptor of caller-owned device buffers holding one packed matrix.
- * Sizes come from vbq_pack_query; vbq_pack fills the buffers. */
+ * Sizes (including the largest-tile figures, which size on-chip buffers of
+ * the GEMV) come from vbq_pack_query; vbq_pack fills the buffers. */
 typedef struct vbq_matrix {
   int32_t n_rows;      /* N, output features */
   int32_t n_cols;      /* K, input features, multiple of 64 */
-  int64_t n_tiles;     /* ceil(N / 16) */
+  int64_t n_tiles;     /* ceil(N / 16) * ceil(K / 4096) */
   int64_t n_records;   /* N * K / 64 (one record per group) */
   int64_t n_code16;    /* size of `codes` in 16-byte units */
-  uint32_t* tiles;     /* device, (n_tiles + 1) * 4 words, 4-byte aligned */
+  int64_t max_tile_code16;   /* largest code area of one tile, 16-byte units */
+  int64_t max_tile_records;  /* largest record count of one tile */
+  uint32_t* tiles;     /* device, (n_tiles + 1) * 4 words, 16-byte aligned */
   uint32_t* so;        /* device, n_records words, 4-byte aligned */
-  uint16_t* meta;      /* device, n_records halfwords, 2-byte aligned */
+  uint16_t* meta;      /* device, n_records halfwords rounded up to an even count
+                          (a whole number of 4-byte words), 4-byte aligned */
   uint32_t* codes;     /* device, n_code16 * 4 words, 16-byte aligned */
 } vbq_matrix;
 
@@ -96,6 +104,8 @@ typedef struct vbq_layout_sizes {
   int64_t n_tiles;
   int64_t n_records;
   int64_t n_code16;
+  int64_t max_tile_code16;
+  int64_t max_tile_records;
   int64_t code_bits;   /* sum of widths * 64: bits of codes proper */
   int64_t groups_by_width[4]; /* number of groups of width 1, 2, 4, 8 */
 } vbq_layout_sizes;
@@ -118,12 +128,12 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
  *   lo = min, hi = max; scale16 = fp16(f32(hi - lo) / (2^b - 1));
  *   offset16 = fp16(lo); s, o = those fp16 values;
  *   q = s == 0 ? 0 : clamp(rint(f32(w - o) / s), 0, 2^b - 1)   (ties to even).
- * W: device, N x K float32, row-major, 4-byte aligned.
+ * W: device, N x K float32, row-major, 16-byte aligned.
  * widths: device, N x K/64 uint8 in natural order (the same values given to
  *   vbq_pack_query for the sizes in m).
- * m: host descriptor; n_rows, n_cols, n_tiles, n_records, n_code16 and the four
- *   device pointers must be set. Invalid widths or a layout larger than the
- *   buffers are detected on the device: nothing is then written beyond the
+ * m: host descriptor; every field must be set from vbq_pack_query and the
+ *   four device pointers. Invalid widths, or a layout that does not match the
+ *   descriptor, are detected on the device: nothing is then written beyond the
  *   tile table, and vbq_matrix_check reports the error. */
 vbq_status vbq_pack(const float* W, const uint8_t* widths, const vbq_matrix* m, hipStream_t stream);
 
@@ -136,8 +146,10 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
  * dequantize-and-multiply kernels" for bandwidth-bound decode):
  *   y[b][n] = sum_k x[b][k] * (s*q + o + r[n][k])     (r only if residual != NULL)
  * accumulated in fp32; codes are never expanded in memory.
- * x: device, B x K fp16, 4-byte aligned. B in [1, VBQ_MAX_BATCH]; B x K must fit
- *   on-chip (B * K <= 57344 without residual, <= 36864 with).
+ * x: device, B x K fp16, 16-byte aligned. B in [1, VBQ_MAX_BATCH]. x is staged
+ *   on-chip 4096 columns at a time next to the packed tiles in flight; a
+ *   launch whose on-chip footprint exceeds the 160 KiB LDS returns
+ *   VBQ_ERR_UNSUPPORTED.
  * residual: device, N x K fp16 row-major (natural order), 16-byte aligned, or
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.

@@ -177,6 +177,15 @@ def unpack_group_record(words, b):
     return _group_codes("orc_unpack_group_record", words, b)
 
 
+TILE_ROWS = 16
+TILE_GROUPS = 64
+
+
+def tile_grid(N: int, K: int):
+    """(row-tiles, k-tiles) of the layout."""
+    return (N + TILE_ROWS - 1) // TILE_ROWS, (K // 64 + TILE_GROUPS - 1) // TILE_GROUPS
+
+
 def layout_sizes(widths):
     widths = _c(widths, np.uint8)
     N, G = widths.shape

@@ -31,13 +31,15 @@
  *
  * Execution layout written and read here (the format the GPU library uses;
  * this file implements it independently from its written specification):
- *   rows are cut into tiles of 16; inside a tile the groups are split by
- *   width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class, ordered by
- *   (k-group ascending, row ascending). Each such "record" has
+ *   the matrix is cut into tiles of 16 rows x 64 k-groups (4096 columns); tile
+ *   t = rt * KT + kt covers rows 16rt.. and k-groups 64kt.., KT = ceil(G/64).
+ *   Inside a tile the groups are split by width class c (b = 1,2,4,8 -> c = 0..3)
+ *   and, inside a class, ordered by (k-group ascending, row ascending). Each
+ *   such "record" has
  *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
- *     meta : u16, row-in-tile in bits 0-3, k-group index in bits 4-15
- *     codes: 2b u32 words; code j (0<=j<32) sits in word j/h at bit (j%h)*b and
- *            code 32+j in the same word at bit 16+(j%h)*b, h = 16/b.
+ *     meta : u16, row-in-tile in bits 0-3, k-group index (of the matrix) in bits 4-15
+ *     codes: 2b u32 words; with h = 16/b, pair p = (code 2p, code 2p+1), p < 32,
+ *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b.
  *   Per tile 4 u32: record base, code base (16-byte units), n0|n1<<16,
  *   n2|n3<<16; one extra entry after the last tile holds the totals.
  *   A tile's code area is the class segments 0..3 in order; segment c holds
@@ -52,7 +54,9 @@
 #include <string.h>
 
 #define ORC_GROUP 64
-#define ORC_TILE 16
+
+#define ORC_TILE_ROWS 16
+#define ORC_TILE_GROUPS 64
 
 /* Deliberate-mistake switch used only by the tests that show the pins catch
  * plausible mistakes. 0 = correct oracle. */
@@ -158,14 +162,16 @@ void orc_unpack_group_canonical(const uint32_t* words, int b, uint8_t* q) {
   }
 }
 
-/* Record word layout (half-interleaved): see the file header. */
+/* Record word layout (even codes in the low halves, odd codes in the high
+ * halves): see the file header. */
 void orc_pack_group_record(const uint8_t* q, int b, uint32_t* words) {
   int h = 16 / b;
   for (int w = 0; w < 2 * b; ++w) {
     uint32_t lo = 0, hi = 0;
     for (int f = 0; f < h; ++f) {
-      lo |= (uint32_t)q[w * h + f] << (f * b);
-      hi |= (uint32_t)q[32 + w * h + f] << (f * b);
+      int p = w * h + f;
+      lo |= (uint32_t)q[2 * p] << (f * b);
+      hi |= (uint32_t)q[2 * p + 1] << (f * b);
     }
     words[w] = (g_mut == 9) ? (hi | (lo << 16)) : (lo | (hi << 16));  /* mutation: halves swapped */
   }
@@ -174,10 +180,10 @@ void orc_pack_group_record(const uint8_t* q, int b, uint32_t* words) {
 void orc_unpack_group_record(const uint32_t* words, int b, uint8_t* q) {
   int h = 16 / b;
   uint32_t mask = (1u << b) - 1u;
-  for (int j = 0; j < 32; ++j) {
-    uint32_t w = words[j / h];
-    q[j] = (uint8_t)((w >> ((j % h) * b)) & mask);
-    q[32 + j] = (uint8_t)((w >> (16 + (j % h) * b)) & mask);
+  for (int p = 0; p < 32; ++p) {
+    uint32_t w = words[p / h];
+    q[2 * p] = (uint8_t)((w >> ((p % h) * b)) & mask);
+    q[2 * p + 1] = (uint8_t)((w >> (16 + (p % h) * b)) & mask);
   }
 }
 
@@ -214,23 +220,39 @@ static int64_t record_chunk_offset(int c, int64_t n_c, int64_t i, int chunk) {
   return blk * 64 * 8 * b + (chunk * m + l) * 16;
 }
 
+/* Tile geometry: number of row-tiles and k-tiles. */
+static void tile_grid(int N, int K, int64_t* RT, int64_t* KT) {
+  int G = K / 64;
+  *RT = (N + ORC_TILE_ROWS - 1) / ORC_TILE_ROWS;
+  *KT = (G + ORC_TILE_GROUPS - 1) / ORC_TILE_GROUPS;
+}
+
+/* Class counts of tile (rt, kt). Returns -1 on an invalid width. */
+static int tile_counts(const uint8_t* widths, int N, int G, int64_t rt, int64_t kt, int64_t n[4]) {
+  n[0] = n[1] = n[2] = n[3] = 0;
+  for (int64_t r = rt * ORC_TILE_ROWS; r < N && r < (rt + 1) * ORC_TILE_ROWS; ++r)
+    for (int64_t g = kt * ORC_TILE_GROUPS; g < G && g < (kt + 1) * ORC_TILE_GROUPS; ++g) {
+      int c = width_class(widths[r * G + g]);
+      if (c < 0) return -1;
+      n[c]++;
+    }
+  return 0;
+}
+
 /* Counts the sizes of the layout. Returns 0, or -1 for a bad shape or width. */
 int orc_layout_sizes(const uint8_t* widths, int N, int K, int64_t* n_tiles, int64_t* n_records,
                      int64_t* n_code16) {
   if (N < 1 || K < 64 || K % 64 != 0 || K / 64 >= 4096) return -1;
   int G = K / 64;
-  int64_t T = (N + ORC_TILE - 1) / ORC_TILE, code = 0;
-  for (int64_t t = 0; t < T; ++t) {
-    int64_t n[4] = {0, 0, 0, 0};
-    for (int r = (int)(t * ORC_TILE); r < N && r < (t + 1) * ORC_TILE; ++r)
-      for (int g = 0; g < G; ++g) {
-        int c = width_class(widths[(int64_t)r * G + g]);
-        if (c < 0) return -1;
-        n[c]++;
-      }
-    code += tile_code_bytes(n) / 16;
-  }
-  *n_tiles = T;
+  int64_t RT, KT, code = 0;
+  tile_grid(N, K, &RT, &KT);
+  for (int64_t rt = 0; rt < RT; ++rt)
+    for (int64_t kt = 0; kt < KT; ++kt) {
+      int64_t n[4];
+      if (tile_counts(widths, N, G, rt, kt, n) != 0) return -1;
+      code += tile_code_bytes(n) / 16;
+    }
+  *n_tiles = RT * KT;
   *n_records = (int64_t)N * G;
   *n_code16 = code;
   return 0;
@@ -244,27 +266,32 @@ int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tile
   int64_t T, R, C16;
   if (orc_layout_sizes(widths, N, K, &T, &R, &C16) != 0) return -1;
   int G = K / 64;
+  int64_t RT, KT;
+  tile_grid(N, K, &RT, &KT);
   memset(codes, 0, (size_t)C16 * 16);
   int64_t rec = 0, code16 = 0;
   for (int64_t t = 0; t < T; ++t) {
-    int r0 = (int)(t * ORC_TILE), r1 = r0 + ORC_TILE;
+    int64_t rt = t / KT, kt = t % KT;
+    int r0 = (int)(rt * ORC_TILE_ROWS), r1 = r0 + ORC_TILE_ROWS;
     if (r1 > N) r1 = N;
-    int64_t n[4] = {0, 0, 0, 0};
-    for (int r = r0; r < r1; ++r)
-      for (int g = 0; g < G; ++g) n[width_class(widths[(int64_t)r * G + g])]++;
+    int g0 = (int)(kt * ORC_TILE_GROUPS), g1 = g0 + ORC_TILE_GROUPS;
+    if (g1 > G) g1 = G;
+    int64_t n[4];
+    tile_counts(widths, N, G, rt, kt, n);
     tiles[4 * t + 0] = (uint32_t)rec;
     tiles[4 * t + 1] = (uint32_t)code16;
     tiles[4 * t + 2] = (uint32_t)(n[0] | (n[1] << 16));
     tiles[4 * t + 3] = (uint32_t)(n[2] | (n[3] << 16));
     int64_t rec_c = rec;
     uint8_t* tile_bytes = (uint8_t*)codes + code16 * 16;
+    const int nr = r1 - r0, ng = g1 - g0;
     for (int c = 0; c < 4; ++c) {
       int b = class_bits(c);
       int64_t i = 0;
-      for (int it = 0; it < G * (r1 - r0); ++it) {
+      for (int it = 0; it < ng * nr; ++it) {
           /* (k-group, row) order; mutation 8 walks (row, k-group) instead */
-          int g = (g_mut == 8) ? it % G : it / (r1 - r0);
-          int r = r0 + ((g_mut == 8) ? it / G : it % (r1 - r0));
+          int g = g0 + ((g_mut == 8) ? it % ng : it / nr);
+          int r = r0 + ((g_mut == 8) ? it / ng : it % nr);
           if (width_class(widths[(int64_t)r * G + g]) != c) continue;
           uint16_t s16, o16;
           uint8_t q[64];
@@ -304,39 +331,44 @@ int orc_unpack(const uint32_t* tiles, const uint32_t* so, const uint16_t* meta, 
                uint16_t* o_out, uint8_t* w_out) {
   if (N < 1 || K < 64 || K % 64 != 0) return -1;
   int G = K / 64;
+  int64_t RT, KT;
+  tile_grid(N, K, &RT, &KT);
   int64_t nr = rows ? n_rows : N;
   for (int64_t i = 0; i < nr * G; ++i) w_out[i] = 0;
   for (int64_t ri = 0; ri < nr; ++ri) {
     int64_t row = rows ? rows[ri] : ri;
     if (row < 0 || row >= N) return -1;
-    int64_t t = row / ORC_TILE;
-    int64_t n[4] = {tiles[4 * t + 2] & 0xFFFF, tiles[4 * t + 2] >> 16, tiles[4 * t + 3] & 0xFFFF,
-                    tiles[4 * t + 3] >> 16};
-    int64_t rec = tiles[4 * t + 0];
-    const uint8_t* tile_bytes = (const uint8_t*)codes + (int64_t)tiles[4 * t + 1] * 16;
-    for (int c = 0; c < 4; ++c) {
-      int b = class_bits(c);
-      const uint8_t* seg = tile_bytes + seg_offset(n, c);
-      for (int64_t i = 0; i < n[c]; ++i) {
-        uint16_t m = meta[rec + i];
-        int64_t r = t * ORC_TILE + (m & 15);
-        int g = m >> 4;
-        if (r != row) continue;
-        if (g >= G) return -1;
-        if (w_out[ri * G + g] != 0) return -1;
-        uint32_t words[16];
-        if (b == 1) memcpy(words, seg + record_chunk_offset(c, n[c], i, 0), 8);
-        else
-          for (int ch = 0; ch < b / 2; ++ch)
-            memcpy(words + 4 * ch, seg + record_chunk_offset(c, n[c], i, ch), 16);
-        uint8_t q[64];
-        orc_unpack_group_record(words, b, q);
-        memcpy(q_out + ri * K + 64 * g, q, 64);
-        s_out[ri * G + g] = (uint16_t)(so[rec + i] & 0xFFFF);
-        o_out[ri * G + g] = (uint16_t)(so[rec + i] >> 16);
-        w_out[ri * G + g] = (uint8_t)b;
+    int64_t rt = row / ORC_TILE_ROWS;
+    for (int64_t kt = 0; kt < KT; ++kt) {
+      int64_t t = rt * KT + kt;
+      int64_t n[4] = {tiles[4 * t + 2] & 0xFFFF, tiles[4 * t + 2] >> 16, tiles[4 * t + 3] & 0xFFFF,
+                      tiles[4 * t + 3] >> 16};
+      int64_t rec = tiles[4 * t + 0];
+      const uint8_t* tile_bytes = (const uint8_t*)codes + (int64_t)tiles[4 * t + 1] * 16;
+      for (int c = 0; c < 4; ++c) {
+        int b = class_bits(c);
+        const uint8_t* seg = tile_bytes + seg_offset(n, c);
+        for (int64_t i = 0; i < n[c]; ++i) {
+          uint16_t m = meta[rec + i];
+          int64_t r = rt * ORC_TILE_ROWS + (m & 15);
+          int g = m >> 4;
+          if (r != row) continue;
+          if (g >= G || g / ORC_TILE_GROUPS != kt) return -1;
+          if (w_out[ri * G + g] != 0) return -1;
+          uint32_t words[16];
+          if (b == 1) memcpy(words, seg + record_chunk_offset(c, n[c], i, 0), 8);
+          else
+            for (int ch = 0; ch < b / 2; ++ch)
+              memcpy(words + 4 * ch, seg + record_chunk_offset(c, n[c], i, ch), 16);
+          uint8_t q[64];
+          orc_unpack_group_record(words, b, q);
+          memcpy(q_out + ri * K + 64 * g, q, 64);
+          s_out[ri * G + g] = (uint16_t)(so[rec + i] & 0xFFFF);
+          o_out[ri * G + g] = (uint16_t)(so[rec + i] >> 16);
+          w_out[ri * G + g] = (uint8_t)b;
+        }
+        rec += n[c];
       }
-      rec += n[c];
     }
     for (int g = 0; g < G; ++g)
       if (w_out[ri * G + g] == 0) return -1;

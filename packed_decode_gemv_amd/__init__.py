@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libvbq.so")
 
 GROUP = 64
 TILE_ROWS = 16
+TILE_GROUPS = 64
 MAX_BATCH = 8
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "bad shape", 3: "width not in {1,2,4,8}", 4: "misaligned buffer",
@@ -34,12 +35,13 @@ class VbqError(RuntimeError):
 
 class vbq_matrix(C.Structure):
     _fields_ = [("n_rows", C.c_int32), ("n_cols", C.c_int32), ("n_tiles", C.c_int64), ("n_records", C.c_int64),
-                ("n_code16", C.c_int64), ("tiles", C.c_void_p), ("so", C.c_void_p), ("meta", C.c_void_p),
-                ("codes", C.c_void_p)]
+                ("n_code16", C.c_int64), ("max_tile_code16", C.c_int64), ("max_tile_records", C.c_int64),
+                ("tiles", C.c_void_p), ("so", C.c_void_p), ("meta", C.c_void_p), ("codes", C.c_void_p)]
 
 
 class vbq_layout_sizes(C.Structure):
     _fields_ = [("n_tiles", C.c_int64), ("n_records", C.c_int64), ("n_code16", C.c_int64),
+                ("max_tile_code16", C.c_int64), ("max_tile_records", C.c_int64),
                 ("code_bits", C.c_int64), ("groups_by_width", C.c_int64 * 4)]
 
 
@@ -114,9 +116,11 @@ class PackedMatrix:
         self.sizes = sizes
         self.tiles = torch.empty(4 * (sizes.n_tiles + 1), dtype=torch.int32, device=device)
         self.so = torch.empty(sizes.n_records, dtype=torch.int32, device=device)
-        self.meta = torch.empty(sizes.n_records, dtype=torch.int16, device=device)
+        # meta: a whole number of 4-byte words (the GEMV reads it in words)
+        self.meta = torch.empty((sizes.n_records + 1) // 2 * 2, dtype=torch.int16, device=device)
         self.codes = torch.empty(4 * sizes.n_code16, dtype=torch.int32, device=device)
         self.desc = vbq_matrix(self.N, self.K, sizes.n_tiles, sizes.n_records, sizes.n_code16,
+                               sizes.max_tile_code16, sizes.max_tile_records,
                                self.tiles.data_ptr(), self.so.data_ptr(), self.meta.data_ptr(),
                                self.codes.data_ptr())
 
@@ -127,7 +131,8 @@ class PackedMatrix:
     def host_layout(self) -> dict:
         """The layout as numpy arrays (device-to-host copy), in the oracle's format."""
         return dict(tiles=self.tiles.cpu().numpy().view(np.uint32), so=self.so.cpu().numpy().view(np.uint32),
-                    meta=self.meta.cpu().numpy().view(np.uint16), codes=self.codes.cpu().numpy().view(np.uint32),
+                    meta=self.meta.cpu().numpy().view(np.uint16)[:self.sizes.n_records],
+                    codes=self.codes.cpu().numpy().view(np.uint32),
                     N=self.N, K=self.K)
 
 

@@ -1,5 +1,6 @@
 // Device-side packing: per-group round-to-nearest quantisation to fp16
-// scale/offset and the tiled, width-sorted execution layout.
+// scale/offset and the tiled (16 rows x 64 k-groups), width-sorted execution
+// layout.
 //
 // Groups of 64 weights with per-group widths {1,2,4,8} and packed low-bit
 // storage: VBQ abstract (page "In-Cell Learning: Language Models That Update
@@ -19,18 +20,19 @@
 
 namespace vbq {
 
-__global__ __launch_bounds__(256) void k_pack_count(const uint8_t* __restrict__ widths, int N, int G,
+__global__ __launch_bounds__(256) void k_pack_count(const uint8_t* __restrict__ widths, int N, int G, int KT,
                                                     uint32_t* __restrict__ tiles) {
   __shared__ uint32_t cnt[5];
   const int t = blockIdx.x;
   if (threadIdx.x < 5) cnt[threadIdx.x] = 0;
   __syncthreads();
-  const int r0 = t * kTile;
-  const int rows = min(kTile, N - r0);
+  const int rt = t / KT, kt = t - rt * KT;
+  const int r0 = rt * kTile, rows = min(kTile, N - r0);
+  const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
   uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0, bad = 0;
-  const uint8_t* wt = widths + (size_t)r0 * G;   // the tile's rows are contiguous
-  for (int i = threadIdx.x; i < rows * G; i += blockDim.x) {
-    const int b = wt[i];
+  for (int i = threadIdx.x; i < rows * ng; i += blockDim.x) {
+    const int r = i / ng, g = i - r * ng;
+    const int b = widths[(size_t)(r0 + r) * G + g0 + g];
     c0 += b == 1;
     c1 += b == 2;
     c2 += b == 4;
@@ -62,15 +64,17 @@ __device__ inline uint64_t wave_incl_scan(uint64_t v, int lane) {
 }
 
 __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles, int n_tiles,
-                                                    uint64_t cap_records, uint64_t cap_code16) {
+                                                    uint64_t cap_records, uint64_t cap_code16,
+                                                    uint64_t cap_tile_records, uint64_t cap_tile_code16) {
   __shared__ uint64_t wr[16], wc[16];
   __shared__ uint64_t carry_r, carry_c;
-  __shared__ uint32_t bad_total;
+  __shared__ uint32_t bad_total, too_big;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
     carry_r = 0;
     carry_c = 0;
     bad_total = 0;
+    too_big = 0;
   }
   __syncthreads();
   for (int base = 0; base < n_tiles; base += 1024) {
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles
       nr = (uint64_t)n0 + n1 + n2 + n3;
       nc = tile_code_bytes(n0, n1, n2, n3) / 16;
       bad = tiles[4 * t + 0];
+      if (nr > cap_tile_records || nc > cap_tile_code16) atomicOr(&too_big, 1u);
     }
     const uint64_t ir = wave_incl_scan(nr, lane), ic = wave_incl_scan(nc, lane);
     if (lane == 63) {
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles
     if (bad_total) flags |= kFlagInvalidWidth;
     if (carry_r > cap_records || carry_c > cap_code16 || carry_r > 0xFFFFFFFFull || carry_c > 0xFFFFFFFFull)
       flags |= kFlagCapacity;
+    if (too_big) flags |= kFlagTileSize;
     tiles[4 * n_tiles + 0] = (uint32_t)carry_r;
     tiles[4 * n_tiles + 1] = (uint32_t)carry_c;
     tiles[4 * n_tiles + 2] = bad_total;
@@ -159,14 +165,14 @@ __device__ inline void quantize_pack_group(const float* __restrict__ wg, uint32_
     r = r > (float)L ? (float)L : r;
     q[j] = (s == 0.0f) ? 0u : (uint32_t)r;
   }
-  constexpr int H = 16 / B;
+  constexpr int H = 16 / B;   // pair p = (code 2p, code 2p+1) -> word p / H, field p % H
 #pragma unroll
   for (int w = 0; w < 2 * B; ++w) {
     uint32_t lo16 = 0, hi16 = 0;
 #pragma unroll
     for (int f = 0; f < H; ++f) {
-      lo16 |= q[w * H + f] << (f * B);
-      hi16 |= q[32 + w * H + f] << (f * B);
+      lo16 |= q[2 * (w * H + f)] << (f * B);
+      hi16 |= q[2 * (w * H + f) + 1] << (f * B);
     }
     words[w] = lo16 | (hi16 << 16);
   }
@@ -198,14 +204,16 @@ __device__ inline void write_record(const float* __restrict__ wg, uint32_t rec, 
 }
 
 __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W, const uint8_t* __restrict__ widths,
-                                                    int N, int G, const uint32_t* __restrict__ tiles, int n_tiles,
-                                                    uint32_t* __restrict__ so, uint16_t* __restrict__ meta,
-                                                    uint32_t* __restrict__ codes) {
-  if (tiles[4 * n_tiles + 3] != 0) return;   // invalid widths or too-small buffers: write nothing
+                                                    int N, int G, int KT, const uint32_t* __restrict__ tiles,
+                                                    int n_tiles, uint32_t* __restrict__ so,
+                                                    uint16_t* __restrict__ meta, uint32_t* __restrict__ codes) {
+  if (tiles[4 * n_tiles + 3] != 0) return;   // invalid widths or mismatched buffers: write nothing
   __shared__ uint32_t carry[4];
   __shared__ uint32_t wcnt[4][4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = t * kTile, rows = min(kTile, N - r0);
+  const int rt = t / KT, kt = t - rt * KT;
+  const int r0 = rt * kTile, rows = min(kTile, N - r0);
+  const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
   const size_t K = (size_t)G * kGroup;
   const uint32_t rec0 = tiles[4 * t + 0];
   const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
@@ -215,13 +223,14 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W,
   const uint64_t s1 = seg_bytes(0, n[0]), s2 = s1 + seg_bytes(1, n[1]), s3 = s2 + seg_bytes(2, n[2]);
   if (tid < 4) carry[tid] = 0;
   __syncthreads();
-  const int total = rows * G;
+  const int total = rows * ng;
   for (int base = 0; base < total; base += 256) {
     const int i = base + tid;
     int c = -1, kg = 0, r = 0;
     if (i < total) {
-      kg = i / rows;   // (k-group, row) order
-      r = i - kg * rows;
+      const int kl = i / rows;   // (k-group, row) order
+      r = i - kl * rows;
+      kg = g0 + kl;
       c = class_of_width(widths[(size_t)(r0 + r) * G + kg]);
     }
     uint32_t rank = 0;
@@ -252,12 +261,13 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W,
 
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s) {
   const int G = m.n_cols / kGroup;
+  const int KT = k_tiles(G);
   const int T = (int)m.n_tiles;
-  hipLaunchKernelGGL(k_pack_count, dim3(T), dim3(256), 0, s, widths, m.n_rows, G, m.tiles);
+  hipLaunchKernelGGL(k_pack_count, dim3(T), dim3(256), 0, s, widths, m.n_rows, G, KT, m.tiles);
   hipLaunchKernelGGL(k_pack_scan, dim3(1), dim3(1024), 0, s, m.tiles, T, (uint64_t)m.n_records,
-                     (uint64_t)m.n_code16);
-  hipLaunchKernelGGL(k_pack_tiles, dim3(T), dim3(256), 0, s, W, widths, m.n_rows, G, m.tiles, T, m.so, m.meta,
-                     m.codes);
+                     (uint64_t)m.n_code16, (uint64_t)m.max_tile_records, (uint64_t)m.max_tile_code16);
+  hipLaunchKernelGGL(k_pack_tiles, dim3(T), dim3(256), 0, s, W, widths, m.n_rows, G, KT, m.tiles, T, m.so,
+                     m.meta, m.codes);
   return hipGetLastError();
 }
 

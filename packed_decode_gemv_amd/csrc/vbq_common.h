@@ -11,12 +11,17 @@ namespace vbq {
 
 constexpr int kGroup = VBQ_GROUP;
 constexpr int kTile = VBQ_TILE_ROWS;
+constexpr int kTileGroups = VBQ_TILE_GROUPS;
 constexpr int kWave = 64;
 constexpr int kBlock = 64;  // records per layout block (one per lane)
 
 // Error flags in the totals entry of the tile table.
 constexpr uint32_t kFlagInvalidWidth = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
+constexpr uint32_t kFlagTileSize = 4u;
+
+__host__ __device__ inline int row_tiles(int N) { return (N + kTile - 1) / kTile; }
+__host__ __device__ inline int k_tiles(int G) { return (G + kTileGroups - 1) / kTileGroups; }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -47,10 +52,13 @@ struct GemvMat {
   float* y;                // [B][N]
   int32_t n_rows;
   int32_t n_groups;        // K / 64
-  int32_t n_tiles;
-  int32_t tiles_per_wg;
+  int32_t row_tiles;       // ceil(N / 16)
+  int32_t k_tiles;         // ceil(G / 64)
+  int32_t rt_per_wg;       // row-tiles per workgroup
   int32_t wg_begin;        // first workgroup index of this matrix in the launch
-  int32_t pad_;
+  uint32_t so_bytes;       // sizes of so / meta / codes, for buffer range checks
+  uint32_t meta_bytes;
+  uint32_t code_bytes;
 };
 
 constexpr int kMaxMats = 8;
@@ -58,12 +66,13 @@ constexpr int kMaxMats = 8;
 struct GemvLaunch {
   GemvMat mats[kMaxMats];
   int32_t n_mats;
-  int32_t max_groups;      // largest K/64 of the matrices (LDS layout stride)
+  int32_t rt_per_wg;       // largest row-tiles per workgroup (LDS row sums)
+  uint32_t ring_bytes;     // LDS ring of each wavefront (multiple of 16)
 };
 
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s);
-size_t gemv_lds_bytes(int nb, int max_groups, bool resid, int tiles_per_wg);
-int gemv_max_tiles_per_wg();
+size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes);
+uint32_t gemv_ring_min_bytes();
 
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s);

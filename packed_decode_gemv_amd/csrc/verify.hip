@@ -68,8 +68,8 @@ __device__ inline void verify_record(const uint8_t* seg, uint8_t* rq_seg, uint32
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * ch + e;                     // natural index inside the group
-      const int jj = j & 31, hi = j >> 5;
-      const int wi = jj / H, sh = 16 * hi + (jj % H) * B;
+      const int pr = j >> 1, odd = j & 1;           // pair (code 2p, code 2p+1)
+      const int wi = pr / H, sh = 16 * odd + (pr % H) * B;
       const uint32_t q = (w[wi] >> sh) & (uint32_t)L;
       const uint32_t rw = (e >> 1) == 0 ? rv.x : (e >> 1) == 1 ? rv.y : (e >> 1) == 2 ? rv.z : rv.w;
       const unsigned short rb = (unsigned short)((e & 1) ? (rw >> 16) : (rw & 0xFFFF));
@@ -105,8 +105,8 @@ __device__ inline void verify_record(const uint8_t* seg, uint8_t* rq_seg, uint32
 
 __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ tiles, const uint32_t* __restrict__ so,
                                                 const uint16_t* __restrict__ meta, const uint32_t* __restrict__ codes,
-                                                int G, const uint16_t* __restrict__ resid, uint64_t* result,
-                                                uint32_t* requant) {
+                                                int G, int KT, const uint16_t* __restrict__ resid,
+                                                uint64_t* result, uint32_t* requant) {
   __shared__ uint32_t s_mism, s_ooc;
   __shared__ unsigned long long s_first;
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
     s_first = ~0ull;
   }
   __syncthreads();
-  const int K = G * kGroup, r0 = t * kTile;
+  const int K = G * kGroup, r0 = (t / KT) * kTile;
   const uint32_t rec0 = tiles[4 * t + 0];
   const uint64_t tb = (uint64_t)tiles[4 * t + 1] * 16;
   const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
@@ -161,7 +161,7 @@ hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* r
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
   hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(256), 0, s, m.tiles, m.so, m.meta, m.codes,
-                     m.n_cols / kGroup, resid, result, requant);
+                     m.n_cols / kGroup, k_tiles(m.n_cols / kGroup), resid, result, requant);
   return hipGetLastError();
 }
 

@@ -159,23 +159,30 @@ def pin_canonical_lsb_first():
             assert np.array_equal(oracle.unpack_group_canonical(oracle.pack_group_canonical(q, b), b), q)
 
 
-def pin_record_half_interleaved():
+def pin_record_even_odd():
+    """Record words: with h = 16/b, pair p = (code 2p, code 2p+1) sits in word
+    p // h, code 2p at bit (p % h)*b of the low half, code 2p+1 at the same
+    position of the high half."""
     j = np.arange(64)
-    # b=8, codes j: word w = q[2w] | q[2w+1]<<8 | q[32+2w]<<16 | q[33+2w]<<24
+    # b=8, codes j: word w holds pairs 2w and 2w+1
     assert list(oracle.pack_group_record(j, 8)) == [
-        (2 * w) | ((2 * w + 1) << 8) | ((32 + 2 * w) << 16) | ((33 + 2 * w) << 24) for w in range(16)]
-    # b=1: codes 32..63 set, 0..31 clear -> high halves full
-    q = (j >= 32).astype(np.uint8)
+        (4 * w) | ((4 * w + 2) << 8) | ((4 * w + 1) << 16) | ((4 * w + 3) << 24) for w in range(16)]
+    # b=1: odd codes set, even clear -> high halves full
+    q = (j % 2).astype(np.uint8)
     assert list(oracle.pack_group_record(q, 1)) == [0xFFFF0000, 0xFFFF0000]
-    # b=1: only code 17 set -> word 1 (codes 16..31 low half), bit 1
+    # b=1: only code 17 set -> pair 8 (odd member), word 0, bit 16 + 8
     q = np.zeros(64, np.uint8)
     q[17] = 1
+    assert list(oracle.pack_group_record(q, 1)) == [1 << 24, 0]
+    # b=1: only code 34 set -> pair 17 (even member), word 1, bit 1
+    q = np.zeros(64, np.uint8)
+    q[34] = 1
     assert list(oracle.pack_group_record(q, 1)) == [0, 2]
-    # b=4, codes j % 16: word w low half = codes 4w..4w+3, high = codes 36+4w-4..
+    # b=4, codes j % 16: word w low half = codes 8w, 8w+2, 8w+4, 8w+6; high = the odd ones
     words = oracle.pack_group_record(j % 16, 4)
     for w in range(8):
-        lo = sum(((4 * w + f) % 16) << (4 * f) for f in range(4))
-        hi = sum(((32 + 4 * w + f) % 16) << (4 * f) for f in range(4))
+        lo = sum(((8 * w + 2 * f) % 16) << (4 * f) for f in range(4))
+        hi = sum(((8 * w + 2 * f + 1) % 16) << (4 * f) for f in range(4))
         assert int(words[w]) == lo | (hi << 16)
     r = _rng(15)
     for b in (1, 2, 4, 8):
@@ -228,19 +235,21 @@ def pin_layout_block_chunks():
 
 def pin_layout_invariants():
     r = _rng(18)
-    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70)]
+    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70), (18, 64 * 130)]
     for (N, K) in cases:
         G = K // 64
         widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G), p=[0.55, 0.2, 0.15, 0.1])
         W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
         lay = oracle.pack(W, widths)
         T, R, C16 = oracle.layout_sizes(widths)
-        assert T == (N + 15) // 16 and R == N * G
+        RT, KT = oracle.tile_grid(N, K)
+        assert T == RT * KT and R == N * G
         tiles = lay["tiles"].reshape(-1, 4)
         # closed-form sizes and bases
         rec = code = 0
         for t in range(T):
-            rows = widths[16 * t:16 * t + 16]
+            rt, kt = divmod(t, KT)
+            rows = widths[16 * rt:16 * rt + 16, 64 * kt:64 * kt + 64]
             n = [int((rows == b).sum()) for b in (1, 2, 4, 8)]
             assert list(tiles[t]) == [rec, code, n[0] | (n[1] << 16), n[2] | (n[3] << 16)]
             rec += sum(n)
@@ -253,7 +262,8 @@ def pin_layout_invariants():
                 key = (m >> 4) * 16 + (m & 15)
                 assert np.all(np.diff(key) > 0)
                 for v in m:
-                    row, kg = 16 * t + (v & 15), v >> 4
+                    row, kg = 16 * rt + (v & 15), v >> 4
+                    assert 64 * kt <= kg < 64 * kt + 64
                     assert widths[row, kg] == b
                     seen.add((row, kg))
                 base += n[c]
@@ -435,9 +445,39 @@ def pin_mean_bits_accounting():
     assert code_bytes <= 16 * C16 <= code_bytes + 8 * T
 
 
-ALL_PINS = [
+def pin_layout_k_tiles():
+    """Tiles are 16 rows x 64 k-groups. N=17, K=64*65 (hand-worked): 2 row-tiles
+    x 2 k-tiles; tile t = rt*2 + kt; tile (0,0) holds rows 0-15 x k-groups 0-63
+    (1024 groups), tile (0,1) rows 0-15 x k-group 64 (16 groups), tile (1,0)
+    row 16 x k-groups 0-63 (64 groups), tile (1,1) row 16 x k-group 64."""
+    N, K = 17, 64 * 65
+    assert oracle.tile_grid(N, K) == (2, 2)
+    widths = np.ones((N, 65), np.uint8)
+    widths[16, 64] = 8
+    widths[3, 64] = 2
+    W = (_rng(19).standard_normal((N, K)) * 0.02).astype(np.float32)
+    lay = oracle.pack(W, widths)
+    tiles = lay["tiles"].reshape(-1, 4)
+    assert oracle.layout_sizes(widths)[0] == 4
+    # record bases: 0, 1024, 1040, 1104; counts per class
+    assert [int(t[0]) for t in tiles[:4]] == [0, 1024, 1040, 1104]
+    assert [int(t[2]) for t in tiles[:4]] == [1024, 15 | (1 << 16), 64, 0]
+    assert [int(t[3]) for t in tiles[:4]] == [0, 0, 0, 1 << 16]
+    # code units: 1024 1-bit records = 8192 B; 15 1-bit (120 B, padded 128) + one 2-bit (16 B);
+    # 64 1-bit = 512 B; one 8-bit = 64 B
+    assert [int(t[1]) for t in tiles[:4]] == [0, 512, 512 + 9, 512 + 9 + 32]
+    assert list(tiles[4]) == [1105, 512 + 9 + 32 + 4, 0, 0]
+    # the k-group field is the matrix's k-group; row field is the row in the tile
+    assert int(lay["meta"][1024]) == (0 | (64 << 4))
+    assert int(lay["meta"][1038]) == (15 | (64 << 4))       # last 1-bit record of tile (0,1)
+    assert int(lay["meta"][1039]) == (3 | (64 << 4))        # its 2-bit record (row 3)
+    assert int(lay["meta"][1040]) == (0 | (0 << 4))         # first record of tile (1,0)
+    assert int(lay["meta"][1104]) == (0 | (64 << 4))
+
+
+ALL_PINS = [pin_layout_k_tiles, 
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
-    pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_half_interleaved,
+    pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd,
     pin_layout_worked_example, pin_layout_block_chunks, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,

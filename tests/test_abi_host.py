@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert vbq.lib.vbq_status_string(3) == b"width not in {1,2,4,8}"
 
 
-@pytest.mark.parametrize("shape", [(1, 64), (16, 128), (17, 192), (33, 640), (100, 64 * 37)])
+@pytest.mark.parametrize("shape", [(1, 64), (16, 128), (17, 192), (33, 640), (100, 64 * 37), (20, 64 * 200)])
 def test_pack_query_matches_oracle(shape):
     import oracle
     import packed_decode_gemv_amd as vbq
@@ -42,6 +42,11 @@ def test_pack_query_matches_oracle(shape):
     w = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64), p=[0.6, 0.2, 0.15, 0.05])
     s = vbq.pack_query(w)
     assert (s.n_tiles, s.n_records, s.n_code16) == oracle.layout_sizes(w)
+    lay = oracle.pack((np.random.default_rng(1).standard_normal((N, K)) * 0.02).astype(np.float32), w)
+    tiles = lay["tiles"].reshape(-1, 4)[:-1].astype(np.int64)
+    recs = (tiles[:, 2] & 0xFFFF) + (tiles[:, 2] >> 16) + (tiles[:, 3] & 0xFFFF) + (tiles[:, 3] >> 16)
+    code16 = np.diff(np.append(tiles[:, 1], s.n_code16))
+    assert s.max_tile_records == int(recs.max()) and s.max_tile_code16 == int(code16.max())
     assert s.code_bits == 64 * int(w.astype(np.int64).sum())
     assert list(s.groups_by_width) == [int((w == b).sum()) for b in (1, 2, 4, 8)]
 
@@ -60,9 +65,9 @@ def test_pack_query_rejects_bad_input():
 
 def _fake_matrix(vbq, N=32, K=128, align=256):
     # Descriptor with plausible (never dereferenced) device addresses.
-    T = (N + 15) // 16
+    T = ((N + 15) // 16) * ((K // 64 + 63) // 64)
     base = 0x7F0000000000
-    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, base, base + 4096, base + 8192, base + align * 64)
+    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, 8, 64, base, base + 4096, base + 8192, base + align * 64)
 
 
 def test_compute_calls_reject_bad_arguments_without_a_gpu():
@@ -75,7 +80,7 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     assert L.vbq_gemv(C.byref(m), None, 1, None, y, None) == 1
     assert L.vbq_gemv(C.byref(m), x, 0, None, y, None) == 5
     assert L.vbq_gemv(C.byref(m), x, 9, None, y, None) == 5
-    assert L.vbq_gemv(C.byref(m), C.c_void_p(0x7F0000100002), 1, None, y, None) == 4
+    assert L.vbq_gemv(C.byref(m), C.c_void_p(0x7F0000100008), 1, None, y, None) == 4
     assert L.vbq_gemv(C.byref(m), x, 1, C.c_void_p(0x7F0000300008), y, None) == 4
     bad = _fake_matrix(vbq, K=100)
     assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 2
@@ -86,7 +91,7 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     bad.codes = 0x7F0000000008
     assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 4
     big = _fake_matrix(vbq, K=64 * 4000)
-    assert L.vbq_gemv(C.byref(big), x, 8, None, y, None) == 5      # batch does not fit on-chip
+    assert L.vbq_gemv(C.byref(big), x, 9, None, y, None) == 5      # batch above the maximum
     assert L.vbq_gemm(C.byref(m), x, 0, y, None) == 2
     assert L.vbq_gemm(C.byref(m), C.c_void_p(0x7F0000100004), 64, y, None) == 4
     assert L.cell_requant_verify(C.byref(m), None, y, None, None) == 1
