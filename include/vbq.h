@@ -17,10 +17,12 @@
  *     Bit-Identical, Revocable Updates to Quantized LLMs", section Abstract.
  *
  * Conventions for every call:
- *   - Ownership: the caller allocates and frees every buffer. Buffers marked
- *     "device" live in GPU memory of the current HIP device; "host" buffers
- *     are ordinary CPU memory. The library keeps no state beyond a cached
- *     kernel-attribute setup and never allocates device memory.
+ *   - Ownership: the caller allocates and frees every buffer it passes.
+ *     Buffers marked "device" live in GPU memory of the current HIP device;
+ *     "host" buffers are ordinary CPU memory. The library itself keeps, per
+ *     (device, stream), one device workspace for the partial row sums of
+ *     matrices with K > 4096 (allocated on first need, grown when a larger
+ *     one is needed, kept until the process ends); nothing else.
  *   - Asynchrony: compute calls enqueue work on `stream` and return without
  *     waiting. Argument errors are found before anything is enqueued: the
  *     call returns a non-zero vbq_status and enqueues nothing. A failed kernel
@@ -30,27 +32,33 @@
  *
  * Execution layout of a packed matrix (see vbq_matrix):
  *   The matrix is cut into tiles of VBQ_TILE_ROWS = 16 rows by
- *   VBQ_TILE_GROUPS = 64 k-groups (4096 columns); tile t = rt * KT + kt covers
- *   rows 16rt.. and k-groups 64kt.., with KT = ceil(K / 4096). Inside a tile
- *   the groups are split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside
- *   a class, ordered by (k-group ascending, row ascending), so that one
- *   wavefront decodes groups of a single width and neighbouring lanes share
- *   k-groups. Each such group is a "record" with
- *     so[r]   : u32, fp16 scale bits 0-15, fp16 offset bits 16-31
- *     meta[r] : u16, row within the tile bits 0-3, k-group index (of the
- *               matrix) bits 4-15
- *     codes   : 2b u32 words; with h = 16/b, the pair p = (code 2p, code 2p+1),
- *               p < 32, sits in word p/h: code 2p at bit (p%h)*b (LSB first)
- *               and code 2p+1 at bit 16 + (p%h)*b.
+ *   VBQ_TILE_GROUPS = 64 k-groups (4096 columns), stored k-tile major: tile
+ *   t = kt * RT + rt covers rows 16rt.. and k-groups 64kt.., with
+ *   RT = ceil(N / 16), KT = ceil(K / 4096). Inside a tile the groups are
+ *   split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
+ *   ordered by (k-group ascending, row ascending), so that a wavefront decodes
+ *   groups of a single width and neighbouring lanes share k-groups. Each group
+ *   is a "record" with
+ *     codes : 2b u32 words; with h = 16/b, the pair p = (code 2p, code 2p+1),
+ *             p < 32, sits in word p/h: code 2p at bit (p%h)*b (LSB first)
+ *             and code 2p+1 at bit 16 + (p%h)*b;
+ *     so    : u32, fp16 scale bits 0-15, fp16 offset bits 16-31;
+ *     meta  : u16, row within the tile bits 0-3, k-group within the tile
+ *             bits 4-9 (bits 10-15 zero).
+ *   A class segment keeps its records in blocks of 64, 64, 32, 16 records
+ *   (b = 1, 2, 4, 8; a full block carries 512, 1024, 1024, 1024 code bytes);
+ *   the last block may hold m fewer. A block of m records is, in order:
+ *     codes area: b = 1: record l at byte 8l (area rounded up to 16 bytes);
+ *                 b >= 2: 16-byte chunk q of record l at byte (q*m + l)*16;
+ *     so area   : record l at byte 4l, rounded up to 16 bytes;
+ *     meta area : record l at byte 2l, rounded up to 16 bytes;
+ *   padding is zero. A tile is its class segments 0..3 in order, and the tiles
+ *   follow each other in storage order in one byte stream, so any range of
+ *   consecutive tiles is one contiguous range of bytes.
  *   tiles[4t..4t+3] = { first record of tile t, first 16-byte unit of its
- *   codes, n0 | n1 << 16, n2 | n3 << 16 } where n_c counts its class-c
- *   records; records of a tile are stored class 0..3 in order. Entry
- *   t = n_tiles holds { total records, total 16-byte units, invalid-width
- *   count, error flags }. A tile's code area holds the class segments 0..3
- *   in order; a segment keeps its records in blocks of 64 (the last block may
- *   hold m < 64): for b = 1 record i is 8 bytes at byte 8*i of the segment;
- *   for b >= 2 the 16-byte chunk q of block-local record l sits at
- *   block start + (q*m + l)*16. Segment 0 is padded to 16 bytes.
+ *   bytes, n0 | n1 << 16, n2 | n3 << 16 } where n_c counts its class-c
+ *   records. Entry t = n_tiles holds { total records, total 16-byte units,
+ *   invalid-width count, error flags }.
  */
 #ifndef VBQ_H
 #define VBQ_H
@@ -63,7 +71,7 @@
 extern "C" {
 #endif
 
-#define VBQ_ABI_VERSION 1
+#define VBQ_ABI_VERSION 2
 #define VBQ_GROUP 64          /* weights per quantisation group (along K) */
 #define VBQ_TILE_ROWS 16      /* rows per layout tile */
 #define VBQ_TILE_GROUPS 64    /* k-groups (of 64 weights) per layout tile */
@@ -82,29 +90,24 @@ typedef enum vbq_status {
 } vbq_status;
 
 /* Descriptor of caller-owned device buffers holding one packed matrix.
- * Sizes (including the largest-tile figures, which size on-chip buffers of
- * the GEMV) come from vbq_pack_query; vbq_pack fills the buffers. */
+ * Sizes come from vbq_pack_query; vbq_pack fills the buffers. */
 typedef struct vbq_matrix {
   int32_t n_rows;      /* N, output features */
   int32_t n_cols;      /* K, input features, multiple of 64 */
   int64_t n_tiles;     /* ceil(N / 16) * ceil(K / 4096) */
   int64_t n_records;   /* N * K / 64 (one record per group) */
-  int64_t n_code16;    /* size of `codes` in 16-byte units */
-  int64_t max_tile_code16;   /* largest code area of one tile, 16-byte units */
-  int64_t max_tile_records;  /* largest record count of one tile */
+  int64_t n_bytes16;   /* size of `stream` in 16-byte units */
+  int64_t max_tile_bytes16;  /* largest tile, 16-byte units */
   uint32_t* tiles;     /* device, (n_tiles + 1) * 4 words, 16-byte aligned */
-  uint32_t* so;        /* device, n_records words, 4-byte aligned */
-  uint16_t* meta;      /* device, n_records halfwords rounded up to an even count
-                          (a whole number of 4-byte words), 4-byte aligned */
-  uint32_t* codes;     /* device, n_code16 * 4 words, 16-byte aligned */
+  uint32_t* stream;    /* device, n_bytes16 * 4 words, 16-byte aligned */
 } vbq_matrix;
 
 /* Sizes of the buffers of a packed matrix, plus accounting figures. */
 typedef struct vbq_layout_sizes {
   int64_t n_tiles;
   int64_t n_records;
-  int64_t n_code16;
-  int64_t max_tile_code16;
+  int64_t n_bytes16;
+  int64_t max_tile_bytes16;
   int64_t max_tile_records;
   int64_t code_bits;   /* sum of widths * 64: bits of codes proper */
   int64_t groups_by_width[4]; /* number of groups of width 1, 2, 4, 8 */
@@ -132,7 +135,7 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
  * widths: device, N x K/64 uint8 in natural order (the same values given to
  *   vbq_pack_query for the sizes in m).
  * m: host descriptor; every field must be set from vbq_pack_query and the
- *   four device pointers. Invalid widths, or a layout that does not match the
+ *   two device pointers. Invalid widths, or a layout that does not match the
  *   descriptor, are detected on the device: nothing is then written beyond the
  *   tile table, and vbq_matrix_check reports the error. */
 vbq_status vbq_pack(const float* W, const uint8_t* widths, const vbq_matrix* m, hipStream_t stream);
@@ -146,10 +149,10 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
  * dequantize-and-multiply kernels" for bandwidth-bound decode):
  *   y[b][n] = sum_k x[b][k] * (s*q + o + r[n][k])     (r only if residual != NULL)
  * accumulated in fp32; codes are never expanded in memory.
- * x: device, B x K fp16, 16-byte aligned. B in [1, VBQ_MAX_BATCH]. x is staged
- *   on-chip 4096 columns at a time next to the packed tiles in flight; a
- *   launch whose on-chip footprint exceeds the 160 KiB LDS returns
- *   VBQ_ERR_UNSUPPORTED.
+ * x: device, B x K fp16, 16-byte aligned. B in [1, VBQ_MAX_BATCH]. Each
+ *   workgroup stages the 4096 columns of x of one k-tile on-chip; matrices
+ *   with K > 4096 are summed over k-tiles through the library's workspace in
+ *   a fixed order, so results are identical from run to run.
  * residual: device, N x K fp16 row-major (natural order), 16-byte aligned, or
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.
@@ -183,9 +186,10 @@ vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, floa
  * residual: device, N x K fp16 natural order, 16-byte aligned.
  * result: device, 3 x uint64, 8-byte aligned: { mismatches, out-of-cell
  *   count, smallest linear index n*K + k with either, or UINT64_MAX }.
- * requant_codes: device, same size and layout as m->codes (16-byte aligned),
- *   receives the re-quantised codes so the artifact can be compared
- *   bit-for-bit; may be NULL. */
+ * requant_codes: device, same size as m->stream (16-byte aligned), receives a
+ *   copy of the stream with every code replaced by its re-quantised value
+ *   (scales, offsets, meta and padding copied), so the artifact can be
+ *   compared bit-for-bit; may be NULL. */
 vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
                                uint32_t* requant_codes, hipStream_t stream);
 

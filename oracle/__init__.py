@@ -70,9 +70,9 @@ def _declare(L):
     L.orc_layout_sizes.restype = C.c_int
     L.orc_layout_sizes.argtypes = [P, C.c_int, C.c_int, P, P, P]
     L.orc_pack.restype = C.c_int
-    L.orc_pack.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P]
+    L.orc_pack.argtypes = [P, P, C.c_int, C.c_int, P, P]
     L.orc_unpack.restype = C.c_int
-    L.orc_unpack.argtypes = [P, P, P, P, C.c_int, C.c_int, P, I64, P, P, P, P]
+    L.orc_unpack.argtypes = [P, P, C.c_int, C.c_int, P, I64, P, P, P, P]
     L.orc_gemv.restype = None
     L.orc_gemv.argtypes = [P, P, P, C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]
     L.orc_make_cell_residual.restype = None
@@ -196,15 +196,14 @@ def layout_sizes(widths):
 
 
 def pack(W, widths) -> dict:
-    """Quantise and write the execution layout. Returns numpy arrays."""
+    """Quantise and write the execution layout: the tile table and the byte
+    stream (as u32 words). Returns numpy arrays."""
     W = _c(W, np.float32)
     widths = _c(widths, np.uint8)
     N, K = W.shape
-    T, R, C16 = layout_sizes(widths)
-    out = dict(tiles=np.zeros(4 * (T + 1), np.uint32), so=np.zeros(R, np.uint32),
-               meta=np.zeros(R, np.uint16), codes=np.zeros(4 * C16, np.uint32), N=N, K=K)
-    rc = lib().orc_pack(_p(W), _p(widths), N, K, _p(out["tiles"]), _p(out["so"]), _p(out["meta"]),
-                        _p(out["codes"]))
+    T, R, B16 = layout_sizes(widths)
+    out = dict(tiles=np.zeros(4 * (T + 1), np.uint32), stream=np.zeros(4 * B16, np.uint32), N=N, K=K)
+    rc = lib().orc_pack(_p(W), _p(widths), N, K, _p(out["tiles"]), _p(out["stream"]))
     if rc != 0:
         raise ValueError("bad shape or width")
     return out
@@ -221,8 +220,7 @@ def unpack(layout: dict, rows=None):
     s = np.zeros((nr, G), np.uint16)
     o = np.zeros((nr, G), np.uint16)
     w = np.zeros((nr, G), np.uint8)
-    arrs = [_c(layout[k], t) for k, t in (("tiles", np.uint32), ("so", np.uint32),
-                                           ("meta", np.uint16), ("codes", np.uint32))]
+    arrs = [_c(layout[k], np.uint32) for k in ("tiles", "stream")]
     rc = lib().orc_unpack(*[_p(a) for a in arrs], N, K, _p(r), nr, _p(q), _p(s), _p(o), _p(w))
     if rc != 0:
         raise ValueError("inconsistent layout")

@@ -31,22 +31,26 @@
  *
  * Execution layout written and read here (the format the GPU library uses;
  * this file implements it independently from its written specification):
- *   the matrix is cut into tiles of 16 rows x 64 k-groups (4096 columns); tile
- *   t = rt * KT + kt covers rows 16rt.. and k-groups 64kt.., KT = ceil(G/64).
- *   Inside a tile the groups are split by width class c (b = 1,2,4,8 -> c = 0..3)
- *   and, inside a class, ordered by (k-group ascending, row ascending). Each
- *   such "record" has
- *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
- *     meta : u16, row-in-tile in bits 0-3, k-group index (of the matrix) in bits 4-15
+ *   the matrix is cut into tiles of 16 rows x 64 k-groups (4096 columns),
+ *   stored k-tile major: tile t = kt * RT + rt covers rows 16rt.. and k-groups
+ *   64kt.., RT = ceil(N/16), KT = ceil(G/64). Inside a tile the groups are
+ *   split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
+ *   ordered by (k-group ascending, row ascending). Each group is a "record":
  *     codes: 2b u32 words; with h = 16/b, pair p = (code 2p, code 2p+1), p < 32,
- *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b.
- *   Per tile 4 u32: record base, code base (16-byte units), n0|n1<<16,
- *   n2|n3<<16; one extra entry after the last tile holds the totals.
- *   A tile's code area is the class segments 0..3 in order; segment c holds
- *   its records in blocks of 64 (the last block may be short, m records):
- *   b=1: record i at byte 8*i of the segment; b>=2: 16-byte chunk q of record
- *   i (block-local index l) at block base + (q*m + l)*16. Segment 0 is padded
- *   to a multiple of 16 bytes.
+ *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b
+ *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
+ *     meta : u16, row in the tile in bits 0-3, k-group in the tile in bits 4-9
+ *   A class segment holds its records in blocks of 64, 64, 32, 16 records
+ *   (b = 1, 2, 4, 8: 1024 code bytes per full block); the last block may be
+ *   short (m records). A block of m records is, in order:
+ *     codes area: b=1: record l at byte 8l (area rounded up to 16 bytes);
+ *                 b>=2: 16-byte chunk q of record l at byte (q*m + l)*16
+ *     so area   : record l at byte 4l, rounded up to 16 bytes
+ *     meta area : record l at byte 2l, rounded up to 16 bytes
+ *   with zero padding. A tile is its class segments 0..3 in order; tiles follow
+ *   each other in storage order in one byte stream. Per tile 4 u32: record
+ *   base, byte base (16-byte units), n0|n1<<16, n2|n3<<16; one extra entry
+ *   after the last tile holds the totals (records, 16-byte units, 0, 0).
  */
 #include <math.h>
 #include <stdint.h>
@@ -195,29 +199,41 @@ static int width_class(int b) {
 }
 static int class_bits(int c) { return 1 << c; }
 
-/* Bytes of a tile's code area for class counts n[4]. */
-static int64_t tile_code_bytes(const int64_t n[4]) {
-  int64_t s0 = ((8 * n[0]) + 15) / 16 * 16;
-  return s0 + 16 * n[1] + 32 * n[2] + 64 * n[3];
+static int64_t up16(int64_t v) { return (v + 15) / 16 * 16; }
+
+/* Records per block of class c: every full block holds 1024 code bytes. */
+static int64_t block_records(int c) { return c == 0 ? 64 : c == 1 ? 64 : c == 2 ? 32 : 16; }
+
+/* Areas of a block of class c holding m records: codes, scale/offset words,
+ * meta halfwords, each rounded up to 16 bytes. */
+static int64_t codes_area(int c, int64_t m) { return c == 0 ? up16(8 * m) : 8 * (int64_t)class_bits(c) * m; }
+static int64_t so_area(int64_t m) { return up16(4 * m); }
+static int64_t meta_area(int64_t m) { return up16(2 * m); }
+static int64_t block_bytes(int c, int64_t m) { return codes_area(c, m) + so_area(m) + meta_area(m); }
+
+/* Bytes of class segment c with n records (full blocks, then the remainder). */
+static int64_t seg_bytes(int c, int64_t n) {
+  int64_t br = block_records(c);
+  return (n / br) * block_bytes(c, br) + ((n % br) ? block_bytes(c, n % br) : 0);
 }
 
-static int64_t seg_offset(const int64_t n[4], int c) {
-  int64_t off = 0;
-  if (c > 0) off += ((8 * n[0]) + 15) / 16 * 16;
-  if (c > 1) off += 16 * n[1];
-  if (c > 2) off += 32 * n[2];
-  return off;
+static int64_t tile_bytes(const int64_t n[4]) {
+  return seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2]) + seg_bytes(3, n[3]);
 }
 
-/* Byte offset, from the start of class segment c, of the 16-byte chunk `chunk`
- * of record i (b >= 2), or of the 8-byte record (b == 1, chunk 0). */
-static int64_t record_chunk_offset(int c, int64_t n_c, int64_t i, int chunk) {
-  int b = class_bits(c);
-  if (b == 1) return 8 * i;
-  int64_t blk = i / 64, l = i % 64;
-  int64_t m = n_c - 64 * blk;
-  if (m > 64) m = 64;
-  return blk * 64 * 8 * b + (chunk * m + l) * 16;
+/* Where record i of class segment c (n records) lives, relative to the
+ * segment: block base, its record count m, and the index l inside it. */
+static void record_place(int c, int64_t n, int64_t i, int64_t* base, int64_t* m, int64_t* l) {
+  int64_t br = block_records(c), k = i / br;
+  *base = k * block_bytes(c, br);
+  *m = (n - k * br < br) ? n - k * br : br;
+  *l = i % br;
+}
+
+/* Byte offset, inside a block of m records, of 16-byte chunk q of record l
+ * (b >= 2), or of the 8-byte record l (b == 1, q == 0). */
+static int64_t chunk_offset(int c, int64_t m, int64_t l, int q) {
+  return c == 0 ? 8 * l : (q * m + l) * 16;
 }
 
 /* Tile geometry: number of row-tiles and k-tiles. */
@@ -241,37 +257,36 @@ static int tile_counts(const uint8_t* widths, int N, int G, int64_t rt, int64_t 
 
 /* Counts the sizes of the layout. Returns 0, or -1 for a bad shape or width. */
 int orc_layout_sizes(const uint8_t* widths, int N, int K, int64_t* n_tiles, int64_t* n_records,
-                     int64_t* n_code16) {
+                     int64_t* n_bytes16) {
   if (N < 1 || K < 64 || K % 64 != 0 || K / 64 >= 4096) return -1;
   int G = K / 64;
-  int64_t RT, KT, code = 0;
+  int64_t RT, KT, bytes = 0;
   tile_grid(N, K, &RT, &KT);
-  for (int64_t rt = 0; rt < RT; ++rt)
-    for (int64_t kt = 0; kt < KT; ++kt) {
+  for (int64_t kt = 0; kt < KT; ++kt)
+    for (int64_t rt = 0; rt < RT; ++rt) {
       int64_t n[4];
       if (tile_counts(widths, N, G, rt, kt, n) != 0) return -1;
-      code += tile_code_bytes(n) / 16;
+      bytes += tile_bytes(n);
     }
   *n_tiles = RT * KT;
   *n_records = (int64_t)N * G;
-  *n_code16 = code;
+  *n_bytes16 = bytes / 16;
   return 0;
 }
 
 /* Quantises W (f32 [N][K]) with the per-group widths and writes the execution
- * layout: tiles [(n_tiles+1)*4], so [n_records], meta [n_records],
- * codes [n_code16*4]. Returns 0 or -1. */
-int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tiles, uint32_t* so,
-             uint16_t* meta, uint32_t* codes) {
-  int64_t T, R, C16;
-  if (orc_layout_sizes(widths, N, K, &T, &R, &C16) != 0) return -1;
+ * layout: tiles [(n_tiles+1)*4] and the byte stream [n_bytes16*4 u32].
+ * Returns 0 or -1. */
+int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tiles, uint32_t* stream) {
+  int64_t T, R, B16;
+  if (orc_layout_sizes(widths, N, K, &T, &R, &B16) != 0) return -1;
   int G = K / 64;
   int64_t RT, KT;
   tile_grid(N, K, &RT, &KT);
-  memset(codes, 0, (size_t)C16 * 16);
-  int64_t rec = 0, code16 = 0;
+  memset(stream, 0, (size_t)B16 * 16);
+  int64_t rec = 0, byte = 0;
   for (int64_t t = 0; t < T; ++t) {
-    int64_t rt = t / KT, kt = t % KT;
+    int64_t kt = t / RT, rt = t % RT;                   /* k-tile major */
     int r0 = (int)(rt * ORC_TILE_ROWS), r1 = r0 + ORC_TILE_ROWS;
     if (r1 > N) r1 = N;
     int g0 = (int)(kt * ORC_TILE_GROUPS), g1 = g0 + ORC_TILE_GROUPS;
@@ -279,43 +294,45 @@ int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tile
     int64_t n[4];
     tile_counts(widths, N, G, rt, kt, n);
     tiles[4 * t + 0] = (uint32_t)rec;
-    tiles[4 * t + 1] = (uint32_t)code16;
+    tiles[4 * t + 1] = (uint32_t)(byte / 16);
     tiles[4 * t + 2] = (uint32_t)(n[0] | (n[1] << 16));
     tiles[4 * t + 3] = (uint32_t)(n[2] | (n[3] << 16));
-    int64_t rec_c = rec;
-    uint8_t* tile_bytes = (uint8_t*)codes + code16 * 16;
+    uint8_t* seg = (uint8_t*)stream + byte;
     const int nr = r1 - r0, ng = g1 - g0;
     for (int c = 0; c < 4; ++c) {
       int b = class_bits(c);
       int64_t i = 0;
       for (int it = 0; it < ng * nr; ++it) {
-          /* (k-group, row) order; mutation 8 walks (row, k-group) instead */
-          int g = g0 + ((g_mut == 8) ? it % ng : it / nr);
-          int r = r0 + ((g_mut == 8) ? it / ng : it % nr);
-          if (width_class(widths[(int64_t)r * G + g]) != c) continue;
-          uint16_t s16, o16;
-          uint8_t q[64];
-          uint32_t words[16];
-          orc_quantize_group(W + (int64_t)r * K + 64 * g, b, &s16, &o16, q);
-          orc_pack_group_record(q, b, words);
-          so[rec_c + i] = (uint32_t)s16 | ((uint32_t)o16 << 16);
-          meta[rec_c + i] = (uint16_t)((r - r0) | (g << 4));
-          uint8_t* seg = tile_bytes + seg_offset(n, c);
-          if (b == 1) {
-            memcpy(seg + record_chunk_offset(c, n[c], i, 0), words, 8);
-          } else {
-            for (int ch = 0; ch < b / 2; ++ch)
-              memcpy(seg + record_chunk_offset(c, n[c], i, ch), words + 4 * ch, 16);
-          }
-          ++i;
+        /* (k-group, row) order; mutation 8 walks (row, k-group) instead */
+        int g = g0 + ((g_mut == 8) ? it % ng : it / nr);
+        int r = r0 + ((g_mut == 8) ? it / ng : it % nr);
+        if (width_class(widths[(int64_t)r * G + g]) != c) continue;
+        uint16_t s16, o16;
+        uint8_t q[64];
+        uint32_t words[16];
+        orc_quantize_group(W + (int64_t)r * K + 64 * g, b, &s16, &o16, q);
+        orc_pack_group_record(q, b, words);
+        int64_t base, m, l;
+        record_place(c, n[c], i, &base, &m, &l);
+        uint8_t* blk = seg + base;
+        if (b == 1) {
+          memcpy(blk + chunk_offset(c, m, l, 0), words, 8);
+        } else {
+          for (int ch = 0; ch < b / 2; ++ch) memcpy(blk + chunk_offset(c, m, l, ch), words + 4 * ch, 16);
         }
-      rec_c += n[c];
+        uint32_t so = (uint32_t)s16 | ((uint32_t)o16 << 16);
+        uint16_t mt = (uint16_t)((r - r0) | ((g - g0) << 4));
+        memcpy(blk + codes_area(c, m) + 4 * l, &so, 4);
+        memcpy(blk + codes_area(c, m) + so_area(m) + 2 * l, &mt, 2);
+        ++i;
+      }
+      seg += seg_bytes(c, n[c]);
     }
     rec += n[0] + n[1] + n[2] + n[3];
-    code16 += tile_code_bytes(n) / 16;
+    byte += tile_bytes(n);
   }
   tiles[4 * T + 0] = (uint32_t)rec;
-  tiles[4 * T + 1] = (uint32_t)code16;
+  tiles[4 * T + 1] = (uint32_t)(byte / 16);
   tiles[4 * T + 2] = 0;
   tiles[4 * T + 3] = 0;
   return 0;
@@ -325,10 +342,10 @@ int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tile
  * group scale16/offset16/width [N][G]. Rows listed in `rows` only (n_rows of
  * them) when rows != NULL; outputs are then [n_rows][...] in that order.
  * Returns 0, or -1 if the layout is inconsistent (a group missing or repeated,
- * a meta field out of range). */
-int orc_unpack(const uint32_t* tiles, const uint32_t* so, const uint16_t* meta, const uint32_t* codes,
-               int N, int K, const int64_t* rows, int64_t n_rows, uint8_t* q_out, uint16_t* s_out,
-               uint16_t* o_out, uint8_t* w_out) {
+ * a meta field out of range, a tile that does not end where the next begins,
+ * nonzero padding). */
+int orc_unpack(const uint32_t* tiles, const uint32_t* stream, int N, int K, const int64_t* rows, int64_t n_rows,
+               uint8_t* q_out, uint16_t* s_out, uint16_t* o_out, uint8_t* w_out) {
   if (N < 1 || K < 64 || K % 64 != 0) return -1;
   int G = K / 64;
   int64_t RT, KT;
@@ -340,34 +357,46 @@ int orc_unpack(const uint32_t* tiles, const uint32_t* so, const uint16_t* meta, 
     if (row < 0 || row >= N) return -1;
     int64_t rt = row / ORC_TILE_ROWS;
     for (int64_t kt = 0; kt < KT; ++kt) {
-      int64_t t = rt * KT + kt;
+      int64_t t = kt * RT + rt;
       int64_t n[4] = {tiles[4 * t + 2] & 0xFFFF, tiles[4 * t + 2] >> 16, tiles[4 * t + 3] & 0xFFFF,
                       tiles[4 * t + 3] >> 16};
-      int64_t rec = tiles[4 * t + 0];
-      const uint8_t* tile_bytes = (const uint8_t*)codes + (int64_t)tiles[4 * t + 1] * 16;
+      if ((int64_t)tiles[4 * t + 5] * 16 - (int64_t)tiles[4 * t + 1] * 16 != tile_bytes(n)) return -1;
+      const uint8_t* seg = (const uint8_t*)stream + (int64_t)tiles[4 * t + 1] * 16;
       for (int c = 0; c < 4; ++c) {
         int b = class_bits(c);
-        const uint8_t* seg = tile_bytes + seg_offset(n, c);
         for (int64_t i = 0; i < n[c]; ++i) {
-          uint16_t m = meta[rec + i];
-          int64_t r = rt * ORC_TILE_ROWS + (m & 15);
-          int g = m >> 4;
+          int64_t base, m, l;
+          record_place(c, n[c], i, &base, &m, &l);
+          const uint8_t* blk = seg + base;
+          uint16_t mt;
+          uint32_t so;
+          memcpy(&mt, blk + codes_area(c, m) + so_area(m) + 2 * l, 2);
+          memcpy(&so, blk + codes_area(c, m) + 4 * l, 4);
+          int64_t r = rt * ORC_TILE_ROWS + (mt & 15);
+          int64_t g = kt * ORC_TILE_GROUPS + (mt >> 4);
+          if ((mt >> 4) >= ORC_TILE_GROUPS || g >= G || r >= N) return -1;
           if (r != row) continue;
-          if (g >= G || g / ORC_TILE_GROUPS != kt) return -1;
           if (w_out[ri * G + g] != 0) return -1;
           uint32_t words[16];
-          if (b == 1) memcpy(words, seg + record_chunk_offset(c, n[c], i, 0), 8);
+          if (b == 1) memcpy(words, blk + chunk_offset(c, m, l, 0), 8);
           else
-            for (int ch = 0; ch < b / 2; ++ch)
-              memcpy(words + 4 * ch, seg + record_chunk_offset(c, n[c], i, ch), 16);
+            for (int ch = 0; ch < b / 2; ++ch) memcpy(words + 4 * ch, blk + chunk_offset(c, m, l, ch), 16);
           uint8_t q[64];
           orc_unpack_group_record(words, b, q);
           memcpy(q_out + ri * K + 64 * g, q, 64);
-          s_out[ri * G + g] = (uint16_t)(so[rec + i] & 0xFFFF);
-          o_out[ri * G + g] = (uint16_t)(so[rec + i] >> 16);
+          s_out[ri * G + g] = (uint16_t)(so & 0xFFFF);
+          o_out[ri * G + g] = (uint16_t)(so >> 16);
           w_out[ri * G + g] = (uint8_t)b;
         }
-        rec += n[c];
+        /* padding of the last block's areas must be zero */
+        if (n[c] % block_records(c)) {
+          int64_t m = n[c] % block_records(c);
+          const uint8_t* blk = seg + (n[c] / block_records(c)) * block_bytes(c, block_records(c));
+          for (int64_t k = (c == 0 ? 8 * m : codes_area(c, m)); k < codes_area(c, m); ++k) if (blk[k]) return -1;
+          for (int64_t k = codes_area(c, m) + 4 * m; k < codes_area(c, m) + so_area(m); ++k) if (blk[k]) return -1;
+          for (int64_t k = codes_area(c, m) + so_area(m) + 2 * m; k < block_bytes(c, m); ++k) if (blk[k]) return -1;
+        }
+        seg += seg_bytes(c, n[c]);
       }
     }
     for (int g = 0; g < G; ++g)

@@ -35,13 +35,13 @@ class VbqError(RuntimeError):
 
 class vbq_matrix(C.Structure):
     _fields_ = [("n_rows", C.c_int32), ("n_cols", C.c_int32), ("n_tiles", C.c_int64), ("n_records", C.c_int64),
-                ("n_code16", C.c_int64), ("max_tile_code16", C.c_int64), ("max_tile_records", C.c_int64),
-                ("tiles", C.c_void_p), ("so", C.c_void_p), ("meta", C.c_void_p), ("codes", C.c_void_p)]
+                ("n_bytes16", C.c_int64), ("max_tile_bytes16", C.c_int64),
+                ("tiles", C.c_void_p), ("stream", C.c_void_p)]
 
 
 class vbq_layout_sizes(C.Structure):
-    _fields_ = [("n_tiles", C.c_int64), ("n_records", C.c_int64), ("n_code16", C.c_int64),
-                ("max_tile_code16", C.c_int64), ("max_tile_records", C.c_int64),
+    _fields_ = [("n_tiles", C.c_int64), ("n_records", C.c_int64), ("n_bytes16", C.c_int64),
+                ("max_tile_bytes16", C.c_int64), ("max_tile_records", C.c_int64),
                 ("code_bits", C.c_int64), ("groups_by_width", C.c_int64 * 4)]
 
 
@@ -115,24 +115,17 @@ class PackedMatrix:
         self.N, self.K = int(N), int(K)
         self.sizes = sizes
         self.tiles = torch.empty(4 * (sizes.n_tiles + 1), dtype=torch.int32, device=device)
-        self.so = torch.empty(sizes.n_records, dtype=torch.int32, device=device)
-        # meta: a whole number of 4-byte words (the GEMV reads it in words)
-        self.meta = torch.empty((sizes.n_records + 1) // 2 * 2, dtype=torch.int16, device=device)
-        self.codes = torch.empty(4 * sizes.n_code16, dtype=torch.int32, device=device)
-        self.desc = vbq_matrix(self.N, self.K, sizes.n_tiles, sizes.n_records, sizes.n_code16,
-                               sizes.max_tile_code16, sizes.max_tile_records,
-                               self.tiles.data_ptr(), self.so.data_ptr(), self.meta.data_ptr(),
-                               self.codes.data_ptr())
+        self.stream = torch.empty(4 * sizes.n_bytes16, dtype=torch.int32, device=device)
+        self.desc = vbq_matrix(self.N, self.K, sizes.n_tiles, sizes.n_records, sizes.n_bytes16,
+                               sizes.max_tile_bytes16, self.tiles.data_ptr(), self.stream.data_ptr())
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.tiles, self.so, self.meta, self.codes))
+        return sum(t.numel() * t.element_size() for t in (self.tiles, self.stream))
 
     def host_layout(self) -> dict:
         """The layout as numpy arrays (device-to-host copy), in the oracle's format."""
-        return dict(tiles=self.tiles.cpu().numpy().view(np.uint32), so=self.so.cpu().numpy().view(np.uint32),
-                    meta=self.meta.cpu().numpy().view(np.uint16)[:self.sizes.n_records],
-                    codes=self.codes.cpu().numpy().view(np.uint32),
+        return dict(tiles=self.tiles.cpu().numpy().view(np.uint32), stream=self.stream.cpu().numpy().view(np.uint32),
                     N=self.N, K=self.K)
 
 
@@ -210,10 +203,10 @@ def vbq_gemm(pm: PackedMatrix, x_bf16, out=None, stream=None):
 
 
 def cell_requant_verify(pm: PackedMatrix, residual, requant_codes: bool = False, stream=None):
-    """Returns (mismatches, out_of_cell, first_bad_index, requantised codes tensor or None)."""
+    """Returns (mismatches, out_of_cell, first_bad_index, re-quantised stream tensor or None)."""
     import torch
     res = torch.empty(3, dtype=torch.int64, device=residual.device)
-    rq = torch.empty_like(pm.codes) if requant_codes else None
+    rq = torch.empty_like(pm.stream) if requant_codes else None
     _check(lib.cell_requant_verify(C.byref(pm.desc), _ptr(residual), _ptr(res), _ptr(rq), _stream(stream)),
            "cell_requant_verify")
     r = res.cpu().numpy().view(np.uint64)

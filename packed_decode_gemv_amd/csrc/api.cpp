@@ -1,10 +1,13 @@
-// C ABI entry points: argument checks, sizing and kernel dispatch.
+// C ABI entry points: argument checks, sizing, workspace and kernel dispatch.
 // Every check happens before anything is enqueued; no C++ exception leaves
 // these functions.
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "vbq_common.h"
@@ -20,57 +23,118 @@ vbq_status check_shape(int32_t N, int32_t K) {
   return VBQ_OK;
 }
 
+// Largest possible tile: 1024 eight-bit records in full blocks of 16 plus the
+// partial blocks of every class.
+constexpr int64_t kMaxTileBytes16 = 8192;
+
 vbq_status check_matrix(const vbq_matrix* m) {
   if (!m) return VBQ_ERR_INVALID_ARG;
   vbq_status st = check_shape(m->n_rows, m->n_cols);
   if (st != VBQ_OK) return st;
   const int G = m->n_cols / kGroup;
   if (m->n_tiles != (int64_t)row_tiles(m->n_rows) * k_tiles(G)) return VBQ_ERR_CAPACITY;
-  if (m->max_tile_records < 1 || m->max_tile_records > (int64_t)kTile * kTileGroups) return VBQ_ERR_CAPACITY;
-  if (m->max_tile_code16 < 1 || m->max_tile_code16 > (int64_t)kTile * kTileGroups * 4) return VBQ_ERR_CAPACITY;
-  if (m->n_records != (int64_t)m->n_rows * (m->n_cols / kGroup)) return VBQ_ERR_CAPACITY;
-  if (m->n_code16 < 1 || m->n_code16 > 0x07FFFFFFll) return VBQ_ERR_CAPACITY;   // < 2 GiB of codes
-  if (m->n_records > 0x1FFFFFFFll) return VBQ_ERR_SHAPE;                           // < 2 GiB of scales
-  if (!m->tiles || !m->so || !m->meta || !m->codes) return VBQ_ERR_INVALID_ARG;
-  if (!aligned(m->tiles, 16) || !aligned(m->so, 4) || !aligned(m->meta, 4) || !aligned(m->codes, 16))
-    return VBQ_ERR_ALIGNMENT;
+  if (m->n_records != (int64_t)m->n_rows * G) return VBQ_ERR_CAPACITY;
+  if (m->max_tile_bytes16 < 1 || m->max_tile_bytes16 > kMaxTileBytes16) return VBQ_ERR_CAPACITY;
+  // Stream byte offsets are 32-bit on the device.
+  if (m->n_bytes16 < 1 || m->n_bytes16 > 0x0FFFFFFFll) return VBQ_ERR_CAPACITY;
+  if (!m->tiles || !m->stream) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(m->tiles, 16) || !aligned(m->stream, 16)) return VBQ_ERR_ALIGNMENT;
   return VBQ_OK;
 }
 
 vbq_status from_hip(hipError_t e) { return e == hipSuccess ? VBQ_OK : VBQ_ERR_HIP; }
 
-constexpr size_t kLdsLimit = 160 * 1024;
+constexpr size_t kLdsLimit = 160 * 1024 - 64;   // dynamic LDS (a few static bytes besides)
 
-
-// Tiles per workgroup: x is staged once per 4096-column window per workgroup,
-// so several tiles per workgroup amortise it, while the launch should still
-// hold several workgroups per CU. VBQ_TILES_PER_WG overrides the target
-// (tuning knob).
-int target_tiles_per_wg() {
-  static int env = -1;
-  if (env < 0) {
-    const char* e = getenv("VBQ_TILES_PER_WG");
-    env = e ? std::max(0, atoi(e)) : 0;
-  }
-  return env > 0 ? env : 4;
+int env_int(const char* name) {
+  const char* e = getenv(name);
+  return e ? std::max(0, atoi(e)) : 0;
 }
 
-// Per-wavefront LDS ring: as large as the budget of two workgroups per CU
-// allows (80 KiB each), at least one 8-bit block.
+// Tiles per workgroup: the launch's tiles spread over one workgroup per CU
+// (the rings fill most of the LDS), at most 16 per workgroup.
+// VBQ_TILES_PER_WG overrides the target (tuning knob).
+int tiles_per_wg(int64_t total_tiles, int cus) {
+  static const int env = env_int("VBQ_TILES_PER_WG");
+  if (env > 0) return std::min(env, kMaxWgTiles - 1);
+  const int64_t t = (total_tiles + cus - 1) / cus;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(16, t));
+}
+
+// Per-wavefront LDS ring: a power of two of 1 KiB slots, as large as fits next
+// to the x table and the row sums, at most 8 KiB. VBQ_RING_BYTES overrides it
+// (rounded down to a power of two).
+uint32_t pow2_floor(size_t v) {
+  uint32_t p = 1;
+  while ((size_t)p * 2 <= v && p < (1u << 30)) p *= 2;
+  return v ? p : 0;
+}
+
 uint32_t pick_ring_bytes(int nb, int rpw) {
-  static int env = -1;
-  if (env < 0) {
-    const char* e = getenv("VBQ_RING_BYTES");
-    env = e ? std::max(0, atoi(e)) : 0;
-  }
-  if (env > 0) return (uint32_t)env & ~15u;
+  static const int env = env_int("VBQ_RING_BYTES");
+  if (env > 0) return pow2_floor((size_t)env);
   const size_t fixed = gemv_lds_bytes(nb, rpw, 0);
-  size_t budget = 80 * 1024;
-  if (fixed + 8 * (size_t)gemv_ring_min_bytes() > budget) budget = kLdsLimit;
-  size_t ring = fixed < budget ? (budget - fixed) / 8 : 0;
-  ring = std::min<size_t>(ring, 16384) & ~(size_t)15;
-  return (uint32_t)ring;
+  if (fixed >= kLdsLimit) return 0;
+  return pow2_floor(std::min<size_t>((kLdsLimit - fixed) / gemv_waves(nb), 8192));
 }
+
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Device workspace per (device, stream), two regions:
+//   counters: arrival counters of the row ranges of matrices with K > 4096.
+//             They are zeroed when the region is allocated and every launch
+//             leaves the ones it used at zero again (the last workgroup of a
+//             row range resets its counter), so they are zero at each launch.
+//             Nothing else is ever stored there.
+//   partials: partial rows, written before they are read in every launch.
+// Both only grow; growing waits for the stream and clears the counters.
+struct Workspace {
+  void* base = nullptr;
+  size_t counter_bytes = 0, partial_bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+hipError_t workspace(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, uint32_t** counters,
+                     float** partials) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.counter_bytes < counter_bytes || w.partial_bytes < partial_bytes) {
+    const size_t cb = std::max<size_t>({w.counter_bytes, counter_bytes, 64 * 1024});
+    const size_t pb = std::max<size_t>({w.partial_bytes, partial_bytes, 1 << 20});
+    if (w.base) {
+      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+      if ((e = hipFree(w.base)) != hipSuccess) return e;
+      w = Workspace();
+    }
+    void* base = nullptr;
+    if ((e = hipMalloc(&base, cb + pb)) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(base, 0, cb, stream)) != hipSuccess) {
+      (void)hipFree(base);
+      return e;
+    }
+    w.base = base;
+    w.counter_bytes = cb;
+    w.partial_bytes = pb;
+  }
+  *counters = static_cast<uint32_t*>(w.base);
+  *partials = reinterpret_cast<float*>(static_cast<uint8_t*>(w.base) + w.counter_bytes);
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,7 +161,7 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
   if (st != VBQ_OK) return st;
   const int G = K / kGroup;
   const int RT = row_tiles(N), KT = k_tiles(G);
-  int64_t code16 = 0, bits = 0, byw[4] = {0, 0, 0, 0}, max_c = 0, max_r = 0;
+  int64_t bytes16 = 0, bits = 0, byw[4] = {0, 0, 0, 0}, max_b = 0, max_r = 0;
   for (int rt = 0; rt < RT; ++rt)
     for (int kt = 0; kt < KT; ++kt) {
       uint32_t n[4] = {0, 0, 0, 0};
@@ -111,15 +175,15 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
           bits += 64 * w;
         }
       for (int c = 0; c < 4; ++c) byw[c] += n[c];
-      const int64_t tc = (int64_t)(tile_code_bytes(n[0], n[1], n[2], n[3]) / 16);
-      code16 += tc;
-      max_c = std::max(max_c, tc);
+      const int64_t tb = (int64_t)(tile_bytes(n[0], n[1], n[2], n[3]) / 16);
+      bytes16 += tb;
+      max_b = std::max(max_b, tb);
       max_r = std::max<int64_t>(max_r, (int64_t)n[0] + n[1] + n[2] + n[3]);
     }
   out->n_tiles = (int64_t)RT * KT;
   out->n_records = (int64_t)N * G;
-  out->n_code16 = code16;
-  out->max_tile_code16 = max_c;
+  out->n_bytes16 = bytes16;
+  out->max_tile_bytes16 = max_b;
   out->max_tile_records = max_r;
   out->code_bits = bits;
   for (int c = 0; c < 4; ++c) out->groups_by_width[c] = byw[c];
@@ -143,7 +207,7 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream) {
   if (hipStreamSynchronize(stream) != hipSuccess) return VBQ_ERR_HIP;
   if (tot[3] & kFlagInvalidWidth) return VBQ_ERR_BITWIDTH;
   if (tot[3] & (kFlagCapacity | kFlagTileSize)) return VBQ_ERR_CAPACITY;
-  if ((int64_t)tot[0] != m->n_records || (int64_t)tot[1] != m->n_code16) return VBQ_ERR_CAPACITY;
+  if ((int64_t)tot[0] != m->n_records || (int64_t)tot[1] != m->n_bytes16) return VBQ_ERR_CAPACITY;
   return VBQ_OK;
 }
 
@@ -152,25 +216,43 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   if (count < 1 || !ms || !xs || !ys) return VBQ_ERR_INVALID_ARG;
   if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
   if (resid && count != 1) return VBQ_ERR_INVALID_ARG;
-  const int target = target_tiles_per_wg();
+  int64_t total_tiles = 0;
   for (int i = 0; i < count; ++i) {
     vbq_status st = check_matrix(&ms[i]);
     if (st != VBQ_OK) return st;
     if (!xs[i] || !ys[i]) return VBQ_ERR_INVALID_ARG;
     if (!aligned(xs[i], 16) || !aligned(ys[i], 4)) return VBQ_ERR_ALIGNMENT;
+    total_tiles += ms[i].n_tiles;
   }
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
-  // Row-tiles per workgroup of each matrix: about `target` tiles per workgroup.
-  std::vector<int> rpw(count);
+  // Row-tiles per workgroup, then the largest ring that fits; with a large
+  // batch the row sums may have to shrink to leave room for a ring.
+  int target = tiles_per_wg(total_tiles, cu_count());
+  uint32_t ring = pick_ring_bytes(B, target);
+  while (ring < gemv_ring_min_bytes() && target > 1) ring = pick_ring_bytes(B, --target);
+  if (ring < gemv_ring_min_bytes() || gemv_lds_bytes(B, target, ring) > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
+  std::vector<int> rpw(count), wpc(count);
   int rpw_max = 1;
+  size_t n_counters = 0, n_partials = 0;
+  std::vector<size_t> c_off(count, 0), p_off(count, 0);
   for (int i = 0; i < count; ++i) {
-    const int KT = k_tiles(ms[i].n_cols / kGroup);
-    rpw[i] = std::max(1, std::min(row_tiles(ms[i].n_rows), (target + KT - 1) / KT));
+    const int RT = row_tiles(ms[i].n_rows), KT = k_tiles(ms[i].n_cols / kGroup);
+    rpw[i] = std::max(1, std::min(RT, target));
+    wpc[i] = (RT + rpw[i] - 1) / rpw[i];
     rpw_max = std::max(rpw_max, rpw[i]);
+    if (KT > 1) {
+      c_off[i] = n_counters;
+      n_counters += (size_t)wpc[i];
+      p_off[i] = n_partials;
+      n_partials += ((size_t)KT * B * ms[i].n_rows + 63) / 64 * 64;
+    }
   }
-  const uint32_t ring = pick_ring_bytes(B, rpw_max);
   const size_t lds = gemv_lds_bytes(B, rpw_max, ring);
-  if (ring < gemv_ring_min_bytes() || lds > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
+  if (lds > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
+  uint32_t* counters = nullptr;
+  float* partials = nullptr;
+  if (n_counters > 0 && workspace(stream, n_counters * 4, n_partials * 4, &counters, &partials) != hipSuccess)
+    return VBQ_ERR_HIP;
   // Split into launches of at most kMaxMats matrices.
   for (int base = 0; base < count; base += kMaxMats) {
     GemvLaunch L;
@@ -181,9 +263,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       const vbq_matrix& m = ms[base + i];
       GemvMat& g = L.mats[i];
       g.tiles = m.tiles;
-      g.so = m.so;
-      g.meta = m.meta;
-      g.codes = m.codes;
+      g.stream = reinterpret_cast<const uint8_t*>(m.stream);
       g.x = xs[base + i];
       g.resid = resid;
       g.y = ys[base + i];
@@ -192,11 +272,14 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.row_tiles = row_tiles(m.n_rows);
       g.k_tiles = k_tiles(g.n_groups);
       g.rt_per_wg = rpw[base + i];
+      g.wg_per_col = wpc[base + i];
       g.wg_begin = wg;
-      g.so_bytes = (uint32_t)(m.n_records * 4);
-      g.meta_bytes = (uint32_t)((m.n_records + 1) / 2 * 4);   // whole 4-byte words
-      g.code_bytes = (uint32_t)(m.n_code16 * 16);
-      wg += (g.row_tiles + g.rt_per_wg - 1) / g.rt_per_wg;
+      g.stream_bytes = (uint32_t)(m.n_bytes16 * 16);
+      if (g.k_tiles > 1) {
+        g.arrivals = counters + c_off[base + i];
+        g.part = partials + p_off[base + i];
+      }
+      wg += g.k_tiles * g.wg_per_col;
     }
     L.n_mats = nm;
     L.rt_per_wg = rpw_max;

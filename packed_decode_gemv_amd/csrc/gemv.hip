@@ -1,4 +1,4 @@
-// Fused dequantise-and-multiply GEMV over the tiled mixed-width layout.
+// Fused dequantise-and-multiply GEMV over the block stream of a packed matrix.
 //
 // Follows the VBQ abstract (page "In-Cell Learning: Language Models That
 // Update Their Own Weights in Sequence Without Changing the File They Ship"):
@@ -15,45 +15,41 @@
 // mantissa of an fp16 whose exponent makes the field's unit exactly 1, so the
 // fp16 value is bias + q with bias = 2^(10-p) for a field at mantissa bit p.
 // v_dot2_f32_f16 multiplies two such values by two activations at once. The
-// bias part, sum_j bias_j (x_j + x_{32+j}), depends only on x and the field
+// bias part, sum_j bias_j (x_2j + x_2j+1), depends only on x and the field
 // positions of the width, so it is computed once per (k-group, width) in LDS
-// and subtracted per group. Masks and exponent patterns live in registers so
-// that building one fp16 pair is a single v_and_or_b32.
+// and subtracted per group. Fields sit at mantissa bits 0..9 where they
+// already are in the word, so most need no shift; masks and exponent patterns
+// live in registers so that building one fp16 pair is a single v_and_or_b32.
 //
-// Work split: a workgroup (8 wavefronts) owns a range of 16-row row-tiles of
-// one matrix (several matrices per launch for batched calls) and walks its
-// tiles k-tile by k-tile, staging the matching 4096-column window of x in LDS.
-// Inside a tile the records are grouped by width in blocks of 64, so every
-// block is decoded by one wavefront with a single width: no divergence, and
-// neighbouring lanes mostly share a k-group, so their x reads are broadcasts.
-// Each wavefront copies its own upcoming blocks from HBM straight into a
-// private LDS ring with buffer-to-LDS loads, keeping several kilobytes in
-// flight without spending registers, and waits on exact load counts before it
-// decodes a block. Wavefronts accumulate rows in their own LDS slices, summed
-// in a fixed order at the end, so results are identical from run to run.
+// Work split: a workgroup owns a range of row-tiles of one k-tile column of
+// one matrix (several matrices per launch for batched calls). Those tiles are
+// consecutive in the stream, so the workgroup's data is one contiguous byte
+// range; its blocks are split evenly over the wavefronts, and each wavefront
+// streams its own sub-range from HBM into a private LDS ring in 1 KiB pieces
+// with buffer-to-LDS loads, keeping several kilobytes in flight without
+// spending registers. Because a wavefront's bytes are one stream, the wait
+// before decoding a block is a closed form (pieces issued minus pieces that
+// cover the block's end). Each block holds records of a single width, so a
+// wavefront decodes without divergence; neighbouring lanes mostly share a
+// k-group, so their x reads are broadcasts. Wavefronts accumulate rows in
+// their own LDS slices, summed in a fixed order at the end; with several
+// k-tiles, the last workgroup of a row range to finish adds the partial rows
+// in k-tile order. Results are therefore identical from run to run.
 #include <utility>
 
 #include "vbq_common.h"
 
 namespace vbq {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
-
-// Field placement of pair index f within a word, per width class c.
-// shift kind: 0 none, 1 left by 4, 2 right by 2, 3 right by 8.
+// ---- Decoding ----------------------------------------------------------------
+// Field placement of pair-field index f (pair p of a word: f = p % (16/b)) per
+// width class c. shift kind: 0 none, 1 right by 6, 2 right by 8.
 __host__ __device__ constexpr int shift_kind(int c, int f) {
-  return c == 0 ? (f < 6 ? 1 : f < 12 ? 2 : 3)
-       : c == 1 ? (f < 3 ? 1 : f < 6 ? 2 : 3)
-       : c == 2 ? (f < 2 ? 0 : 3)
-       : (f < 1 ? 0 : 3);
+  return c == 0 ? (f < 10 ? 0 : 1) : c == 1 ? (f < 5 ? 0 : 1) : c == 2 ? (f < 2 ? 0 : 2) : (f < 1 ? 0 : 2);
 }
 // Mantissa bit of the field after the shift.
 __host__ __device__ constexpr int field_pos(int c, int f) {
-  return c == 0 ? (f < 6 ? f + 4 : f < 12 ? f - 2 : f - 8)
-       : c == 1 ? (f < 3 ? 4 + 2 * f : f < 6 ? 4 + 2 * (f - 3) : 4 + 2 * (f - 6))
-       : c == 2 ? ((f & 1) ? 4 : 0)
-       : 0;
+  return c == 0 ? (f < 10 ? f : f - 6) : c == 1 ? (f < 5 ? 2 * f : 2 * f - 6) : c == 2 ? ((f & 1) ? 4 : 0) : 0;
 }
 __host__ __device__ constexpr uint32_t field_mask(int c, int p) {
   return (((1u << (1 << c)) - 1u) << p) * 0x00010001u;
@@ -64,7 +60,7 @@ __host__ __device__ constexpr float field_bias(int c, int f) { return (float)(1 
 
 template <int KIND>
 __device__ inline uint32_t shifted(uint32_t w) {
-  return KIND == 0 ? w : KIND == 1 ? (w << 4) : KIND == 2 ? (w >> 2) : (w >> 8);
+  return KIND == 0 ? w : KIND == 1 ? (w >> 6) : (w >> 8);
 }
 
 // A constant materialised in a VGPR that the compiler cannot fold back into a
@@ -106,9 +102,18 @@ __device__ inline Consts<C> make_consts() {
   return make_consts_impl<C>(std::make_integer_sequence<int, 10>{});
 }
 
+// Pairs per word and words per lane of class C: a lane holds 8 (b = 1) or 16
+// code bytes.
+template <int C>
+struct Geo {
+  static constexpr int H = 16 >> C;              // pairs per word
+  static constexpr int NW = C == 0 ? 2 : 4;      // words per lane
+  static constexpr int NP = NW * H;              // pairs per lane: 32, 32, 16, 8
+};
+
 template <int C, int J, int NB>
 __device__ inline void pair_step(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[NB], float (&acc)[NB]) {
-  constexpr int H = 16 >> C, F = J % H, P = field_pos(C, F);
+  constexpr int H = Geo<C>::H, F = J % H, P = field_pos(C, F);
   const uint32_t src = shifted<shift_kind(C, F)>(w[J / H]);
   const uint32_t hv = (src & k.mask[P]) | k.magic[P];
 #pragma unroll
@@ -127,176 +132,220 @@ __device__ inline void chunk_step(const Consts<C>& k, const uint32_t* w, const u
   pair_step<C, 4 * CH + 3, NB>(k, w, xv, acc);
 }
 
-// acc[nb] += sum_j (bias_j + q_j) x_j + (bias_j + q_{32+j}) x_{32+j} over the
-// 32 pairs of one record. xk points at the record's k-group in the x table of
-// batch row 0; batch rows are xstride dwords apart.
+// acc[nb] += sum_j (bias_j + q_2j) x_2j + (bias_j + q_2j+1) x_2j+1 over the
+// lane's pairs. xk points at the lane's first pair in the x table of batch
+// row 0; batch rows are xstride dwords apart.
 template <int C, int NB, int... CH>
-__device__ inline void dot_record_impl(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
-                                       float (&acc)[NB], std::integer_sequence<int, CH...>) {
+__device__ inline void dot_lane_impl(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
+                                     float (&acc)[NB], std::integer_sequence<int, CH...>) {
   (chunk_step<C, CH, NB>(k, w, xk, xstride, acc), ...);
 }
 
-// x pairs of one k-group take 32 dwords plus 4 of padding: neighbouring
-// k-groups start 144 bytes apart, which spreads lanes that read different
-// k-groups over the LDS banks while every read keeps an immediate offset.
-constexpr int kXStride = 36;
-// Ring bytes of one block: codes (64 records of 8b bytes), scale/offset
-// (64 x 4 bytes), meta (64 x 2 bytes plus one halfword of alignment slack).
-__host__ __device__ constexpr uint32_t ring_block_bytes(int c) { return (512u << c) + 256u + 144u; }
-constexpr uint32_t kRingMinBytes = ring_block_bytes(3);
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-struct Rsrc {
-  __amdgpu_buffer_rsrc_t so, meta, codes;
-};
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
+// ---- Synchronisation helpers ---------------------------------------------------
+#define VBQ_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Waits until at most n vector-memory instructions of this wavefront are
-// outstanding (n is wavefront-uniform). Loads complete in issue order, so this
-// waits for everything issued before the last n.
-#define VBQ_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-#define VBQ_W(n) case n: __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(n)); break;
+// outstanding (n is wavefront-uniform, clamped to [0, 63]). Loads complete in
+// issue order, so this waits for everything issued before the last n.
+// s_waitcnt takes its count as an immediate, so this jumps into a table of
+// 64 (wait, branch) pairs of 8 bytes each: s_getpc_b64 yields the address of
+// the next instruction and the table starts four 4-byte instructions later.
+// A switch over the 64 counts compiles into a long chain of scalar branches.
 __device__ inline void wait_vmcnt(int n) {
-  switch (n < 63 ? n : 63) {
-    VBQ_W(0) VBQ_W(1) VBQ_W(2) VBQ_W(3) VBQ_W(4) VBQ_W(5) VBQ_W(6) VBQ_W(7)
-    VBQ_W(8) VBQ_W(9) VBQ_W(10) VBQ_W(11) VBQ_W(12) VBQ_W(13) VBQ_W(14) VBQ_W(15)
-    VBQ_W(16) VBQ_W(17) VBQ_W(18) VBQ_W(19) VBQ_W(20) VBQ_W(21) VBQ_W(22) VBQ_W(23)
-    VBQ_W(24) VBQ_W(25) VBQ_W(26) VBQ_W(27) VBQ_W(28) VBQ_W(29) VBQ_W(30) VBQ_W(31)
-    VBQ_W(32) VBQ_W(33) VBQ_W(34) VBQ_W(35) VBQ_W(36) VBQ_W(37) VBQ_W(38) VBQ_W(39)
-    VBQ_W(40) VBQ_W(41) VBQ_W(42) VBQ_W(43) VBQ_W(44) VBQ_W(45) VBQ_W(46) VBQ_W(47)
-    VBQ_W(48) VBQ_W(49) VBQ_W(50) VBQ_W(51) VBQ_W(52) VBQ_W(53) VBQ_W(54) VBQ_W(55)
-    VBQ_W(56) VBQ_W(57) VBQ_W(58) VBQ_W(59) VBQ_W(60) VBQ_W(61) VBQ_W(62)
-    default: __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(63)); break;
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep LDS reads of the landed data after the wait
+  n = n < 0 ? 0 : (n > 63 ? 63 : n);
+  asm volatile(
+      "s_getpc_b64 s[94:95]\n\t"
+      "s_lshl3_add_u32 s96, %0, 16\n\t"
+      "s_add_u32 s94, s94, s96\n\t"
+      "s_addc_u32 s95, s95, 0\n\t"
+      "s_setpc_b64 s[94:95]\n\t"
+      "s_waitcnt vmcnt(0)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(1)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(2)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(3)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(4)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(5)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(6)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(7)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(8)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(9)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(10)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(11)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(12)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(13)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(14)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(15)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(16)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(17)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(18)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(19)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(20)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(21)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(22)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(23)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(24)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(25)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(26)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(27)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(28)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(29)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(30)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(31)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(32)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(33)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(34)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(35)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(36)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(37)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(38)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(39)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(40)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(41)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(42)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(43)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(44)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(45)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(46)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(47)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(48)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(49)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(50)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(51)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(52)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(53)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(54)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(55)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(56)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(57)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(58)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(59)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(60)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(61)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(62)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      "s_waitcnt vmcnt(63)\n\ts_branch .Lvbq_wait_end_%=\n\t"
+      ".Lvbq_wait_end_%=:"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(n))
+      : "s94", "s95", "s96", "scc", "memory");
 }
-#undef VBQ_W
 
-// Position of a wavefront in its block sequence. A workgroup owns row-tiles
-// [rt0, rt0 + nrl) of one matrix; its blocks are ordered (k-tile, row-tile,
-// width class, block) -- the storage order inside each tile -- and wavefront w
-// takes every kWaves-th block starting at w. All fields are wavefront-uniform.
-struct Cur {
-  int kt, rl, c, bi;
-  uint32_t rec0, code0, n[4];
-  bool valid;
-};
-
-__device__ inline int nblk_of(uint32_t n) { return (int)((n + kBlock - 1) / kBlock); }
-
-__device__ inline void cur_tile(Cur& q, const GemvMat& M, int rt0) {
-  const uint4 th = *reinterpret_cast<const uint4*>(M.tiles + 4 * ((rt0 + q.rl) * M.k_tiles + q.kt));
-  q.rec0 = th.x;
-  q.code0 = th.y;
-  q.n[0] = th.z & 0xFFFF;
-  q.n[1] = th.z >> 16;
-  q.n[2] = th.w & 0xFFFF;
-  q.n[3] = th.w >> 16;
+// Workgroup barrier for data written with ordinary LDS stores. It waits for
+// this wavefront's LDS operations only: a full __syncthreads() would also wait
+// for every buffer-to-LDS copy in flight (they count as memory loads), which
+// drains the rings. Ring data is covered by the count waits instead.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Moves forward k blocks (k >= 0) in the workgroup's sequence.
-__device__ inline void cur_advance(Cur& q, const GemvMat& M, int rt0, int nrl, int k) {
-  while (q.valid) {
-    const int left = nblk_of(q.n[q.c]) - q.bi;
-    if (k < left) {
-      q.bi += k;
-      return;
-    }
-    k -= left;
-    q.bi = 0;
-    if (++q.c == 4) {
-      q.c = 0;
-      if (++q.rl == nrl) {
-        q.rl = 0;
-        if (++q.kt == M.k_tiles) {
-          q.valid = false;
-          return;
-        }
-      }
-      cur_tile(q, M, rt0);
-    }
-  }
-}
+// ---- Buffer-to-LDS copies -------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline Cur cur_first(const GemvMat& M, int rt0, int nrl, int wave) {
-  Cur q;
-  q.kt = 0;
-  q.rl = 0;
-  q.c = 0;
-  q.bi = 0;
-  q.valid = true;
-  cur_tile(q, M, rt0);
-  cur_advance(q, M, rt0, nrl, wave);
-  return q;
-}
-
-__device__ inline uint32_t cur_m(const Cur& q) { return min((uint32_t)kBlock, q.n[q.c] - (uint32_t)q.bi * kBlock); }
-
-__device__ inline uint32_t cur_rec(const Cur& q) {
-  uint32_t r = q.rec0 + (uint32_t)q.bi * kBlock;
-  for (int c = 0; c < q.c; ++c) r += q.n[c];
+// Raw buffer descriptor (base, no stride, size in bytes): loads past `bytes`
+// return zeros instead of touching memory.
+__device__ inline u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;
   return r;
 }
 
-__device__ inline uint32_t cur_code(const Cur& q) {
-  uint32_t o = q.code0 * 16u + (uint32_t)q.bi * (kBlock * 8u << q.c);
-  for (int c = 0; c < q.c; ++c) o += (uint32_t)seg_bytes(c, q.n[c]);
-  return o;
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 
-// Number of DMA instructions one block issues (codes pieces of 1 KiB, one for
-// the scale/offset words, one for the meta halfwords).
-__device__ inline int block_dma_count(int c, uint32_t m) { return (int)((8u * (1u << c) * m + 1023u) / 1024u) + 2; }
-
-// Ring placement: blocks take consecutive ring bytes; a block that would
-// straddle the end of the ring starts again at offset 0.
-__device__ inline uint32_t ring_place(uint32_t& pos, uint32_t bytes, uint32_t ring) {
-  const uint32_t off = pos % ring;
-  if (off + bytes > ring) pos += ring - off;
-  const uint32_t at = pos % ring;
-  pos += bytes;
-  return at;
+// Buffer-to-LDS copy: the active lane l reads 16 bytes at byte offset voff of
+// the buffer and writes them to LDS address lds + 16 l. It is written as
+// assembly so that the compiler does not treat it as a pending LDS store: it
+// would otherwise wait for every copy in flight before any LDS read.
+// Completion is tracked by the explicit load-count waits instead. The
+// instruction has no register result, so nothing is left pending in registers.
+__device__ inline void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
 }
 
-// Copies one block of class C from HBM into the wavefront's ring at byte
-// offset `at` of the LDS: codes (1 KiB per instruction, 16 bytes per lane),
-// scale/offset words and meta halfwords (4 bytes per lane). Lanes past the
-// block's data are inactive, so nothing beyond it is read or written.
-template <int C>
-__device__ inline void dma_block(const Rsrc& R, uint8_t* lds, uint32_t at, uint32_t code_src, uint32_t rec_src,
-                                 uint32_t m, uint32_t lane) {
-  constexpr uint32_t B = 1u << C;
-  const uint32_t cbytes = 8u * B * m;
-  const int pieces = (int)((cbytes + 1023u) / 1024u);
-  for (int p = 0; p < pieces; ++p) {
-    if (1024u * p + 16u * lane < cbytes)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(R.codes, (lds_void*)(lds + at + 1024u * p), 16,
-                                               code_src + 1024u * p + 16u * lane, 0, 0, 0);
+// ---- Workgroup tile list -------------------------------------------------------
+// Lane i (< nt) of every wavefront holds the header of tile i of the
+// workgroup (consecutive tiles of one k-tile column) and the number of blocks
+// before it; lane nt holds the header of the next tile, whose byte base ends
+// the workgroup's range.
+struct TileLanes {
+  uint32_t byte0, n01, n23, pre;   // per lane
+  int nt, total;                   // tiles, blocks (uniform)
+};
+
+__device__ inline uint32_t tile_blocks(uint32_t n01, uint32_t n23) {
+  return seg_blocks(0, n01 & 0xFFFF) + seg_blocks(1, n01 >> 16) + seg_blocks(2, n23 & 0xFFFF) +
+         seg_blocks(3, n23 >> 16);
+}
+
+// h: the header loaded by this lane (zeros past the end of the list).
+__device__ inline TileLanes make_tile_lanes(const uint4& h, int nt, uint32_t lane) {
+  TileLanes T;
+  T.nt = nt;
+  T.byte0 = h.y * 16u;
+  T.n01 = (int)lane < nt ? h.z : 0u;
+  T.n23 = (int)lane < nt ? h.w : 0u;
+  const uint32_t nb = tile_blocks(T.n01, T.n23);
+  uint32_t inc = nb;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t v = __shfl_up(inc, d, kWave);
+    if ((int)lane >= d) inc += v;
   }
-  const uint32_t so_at = at + (512u << C);
-  if (lane < m)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.so, (lds_void*)(lds + so_at), 4, (rec_src + lane) * 4u, 0, 0, 0);
-  const uint32_t d = rec_src & 1u;                       // meta starts at an odd halfword
-  if (lane < (m + d + 1u) / 2u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.meta, (lds_void*)(lds + so_at + 256u), 4,
-                                             (rec_src - d) * 2u + 4u * lane, 0, 0, 0);
+  T.pre = inc - nb;
+  T.total = __builtin_amdgcn_readlane(inc, nt - 1);
+  return T;
 }
 
-__device__ inline int issue_block(const Rsrc& R, uint8_t* lds, uint32_t at, const Cur& q, uint32_t lane) {
-  const uint32_t m = cur_m(q), code = cur_code(q), rec = cur_rec(q);
-  switch (q.c) {
-    case 0: dma_block<0>(R, lds, at, code, rec, m, lane); break;
-    case 1: dma_block<1>(R, lds, at, code, rec, m, lane); break;
-    case 2: dma_block<2>(R, lds, at, code, rec, m, lane); break;
-    default: dma_block<3>(R, lds, at, code, rec, m, lane); break;
-  }
-  return block_dma_count(q.c, m);
+// ---- Per-lane block lookup ---------------------------------------------------------
+// Where block j of the workgroup (j < total) sits, computed with vector
+// instructions so that a whole wavefront finds its blocks at once.
+struct BlockInfo {
+  uint32_t byte, size, m;
+  int c, t;
+};
+
+__device__ inline uint32_t sel4(int c, uint32_t a, uint32_t b, uint32_t d, uint32_t e) {
+  return c == 0 ? a : c == 1 ? b : c == 2 ? d : e;
 }
 
+__device__ inline BlockInfo block_info(const TileLanes& T, uint32_t j) {
+  BlockInfo r;
+  // the tile: the last one whose first block is at or before j
+  int t = 0;
+  for (int tt = 1; tt < T.nt; ++tt) t += j >= (uint32_t)__builtin_amdgcn_readlane(T.pre, tt) ? 1 : 0;
+  const uint32_t byte0 = __shfl(T.byte0, t, kWave), n01 = __shfl(T.n01, t, kWave);
+  const uint32_t n23 = __shfl(T.n23, t, kWave), pre = __shfl(T.pre, t, kWave);
+  const uint32_t n0 = n01 & 0xFFFF, n1 = n01 >> 16, n2 = n23 & 0xFFFF, n3 = n23 >> 16;
+  const uint32_t k0 = seg_blocks(0, n0), k01 = k0 + seg_blocks(1, n1), k012 = k01 + seg_blocks(2, n2);
+  const uint32_t jb = j - pre;
+  const int c = (jb >= k0) + (jb >= k01) + (jb >= k012);
+  const uint32_t kb = sel4(c, 0u, k0, k01, k012);
+  const uint32_t s1 = (uint32_t)seg_bytes(0, n0), s2 = s1 + (uint32_t)seg_bytes(1, n1);
+  const uint32_t sb = sel4(c, 0u, s1, s2, s2 + (uint32_t)seg_bytes(2, n2));
+  const uint32_t bi = jb - kb;
+  const uint32_t n = sel4(c, n0, n1, n2, n3);
+  const uint32_t br = sel4(c, block_records(0), block_records(1), block_records(2), block_records(3));
+  const uint32_t full = sel4(c, block_bytes(0, block_records(0)), block_bytes(1, block_records(1)),
+                             block_bytes(2, block_records(2)), block_bytes(3, block_records(3)));
+  r.m = min(br, n - bi * br);
+  r.byte = byte0 + sb + bi * full;
+  r.size = (c == 0 ? up16(8u * r.m) : (8u << c) * r.m) + up16(4u * r.m) + up16(2u * r.m);
+  r.c = c;
+  r.t = t;
+  return r;
+}
+
+// ---- LDS layout and block decode ---------------------------------------------------
 struct AllConsts {
   Consts<0> k0;
   Consts<1> k1;
@@ -305,46 +354,57 @@ struct AllConsts {
 };
 
 struct Smem {
-  uint32_t* xs;    // [NB][64][36] pairs (x_2p, x_2p+1) of the current 4096-column window
+  uint32_t* xs;    // [NB][64][36] pairs (x_2p, x_2p+1) of the k-tile
   float* cx;       // [NB][4][64] bias constants per width class
   float* xsum;     // [NB][64] sum of x over the group
-  float* yw;       // [kWaves][NB][nrl*16] per-wavefront row sums
-  uint8_t* ring;   // this wavefront's ring
+  float* yw;       // [waves][NB][nrow] per-wavefront row sums
+  const uint8_t* ring;   // this wavefront's ring
+  uint32_t ring_mask;    // ring bytes - 1 (a power of two)
 };
 
-// Decodes one block of class C from the ring at byte offset `at`.
+// Decodes one block of class C (m records) at ring offset `boff`.
 template <int C, int NB>
-__device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t at, uint32_t rec_src, uint32_t m,
-                                     int kt, int rl, int nrow, int wave, uint32_t lane) {
-  if (lane < m) {
-    constexpr int B = 1 << C;
-    const uint8_t* blk = S.ring + at;
-    uint32_t w[2 * B];
-    if constexpr (B == 1) {
-      const uint2 v = *reinterpret_cast<const uint2*>(blk + 8u * lane);
+__device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t boff, uint32_t m, int rl, int nrow,
+                                     int wave, uint32_t lane) {
+  constexpr uint32_t LPR = lanes_per_record(C), BR = block_records(C);
+  if (lane < m * LPR) {
+    uint32_t q = 0, l = lane;
+    if constexpr (LPR > 1) {
+      if (m == BR) {
+        q = lane / BR;
+        l = lane % BR;
+      } else {
+        // lane = q*m + l; (lane + 1/2)/m is at least 1/64 away from an integer
+        q = (uint32_t)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)m));
+        l = lane - q * m;
+      }
+    }
+    constexpr int NW = Geo<C>::NW;
+    const uint32_t mask = S.ring_mask;
+    uint32_t w[NW];
+    if constexpr (C == 0) {
+      const uint2 v = *reinterpret_cast<const uint2*>(S.ring + ((boff + 8u * lane) & mask));
       w[0] = v.x;
       w[1] = v.y;
     } else {
-#pragma unroll
-      for (int q = 0; q < B / 2; ++q) {
-        const uint4 v = *reinterpret_cast<const uint4*>(blk + (q * m + lane) * 16u);
-        w[4 * q + 0] = v.x;
-        w[4 * q + 1] = v.y;
-        w[4 * q + 2] = v.z;
-        w[4 * q + 3] = v.w;
-      }
+      const uint4 v = *reinterpret_cast<const uint4*>(S.ring + ((boff + 16u * lane) & mask));
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
     }
-    const uint8_t* so_p = blk + (512u << C);
-    const uint32_t so = *reinterpret_cast<const uint32_t*>(so_p + 4u * lane);
-    const uint32_t mt = *reinterpret_cast<const uint16_t*>(so_p + 256u + 2u * ((rec_src & 1u) + lane));
-    const int row = mt & 15, kgl = (int)(mt >> 4) - kt * kTileGroups;
+    const uint32_t ca = codes_area(C, m);
+    const uint32_t so = *reinterpret_cast<const uint32_t*>(S.ring + ((boff + ca + 4u * l) & mask));
+    const uint32_t mt = *reinterpret_cast<const uint16_t*>(S.ring + ((boff + ca + so_area(m) + 2u * l) & mask));
+    const int row = mt & 15, kgl = (int)(mt >> 4) & (kTileGroups - 1);   // in range whatever the bytes
     float acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = -S.cx[(nb * 4 + C) * kTileGroups + kgl];   // remove the bias part
-    const uint32_t* xk = S.xs + ((kgl << 5) + (kgl << 2));   // kgl * kXStride
-    dot_record_impl<C, NB>(k, w, xk, kTileGroups * kXStride, acc, std::make_integer_sequence<int, 8>{});
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
+    const uint32_t* xk = S.xs + kgl * kXStride + q * (uint32_t)Geo<C>::NP;
+    dot_lane_impl<C, NB>(k, w, xk, kTileGroups * kXStride, acc,
+                         std::make_integer_sequence<int, Geo<C>::NP / 4>{});
     const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
-    const float o = __half2float(__ushort_as_half((unsigned short)(so >> 16)));
+    const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float v = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
@@ -354,43 +414,66 @@ __device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t
 }
 
 template <int NB>
-__device__ inline void compute_any(const AllConsts& K, const Smem& S, uint32_t at, const Cur& q, int nrow, int wave,
-                                   uint32_t lane) {
-  const uint32_t m = cur_m(q), rec = cur_rec(q);
-  switch (q.c) {
-    case 0: compute_block<0, NB>(K.k0, S, at, rec, m, q.kt, q.rl, nrow, wave, lane); break;
-    case 1: compute_block<1, NB>(K.k1, S, at, rec, m, q.kt, q.rl, nrow, wave, lane); break;
-    case 2: compute_block<2, NB>(K.k2, S, at, rec, m, q.kt, q.rl, nrow, wave, lane); break;
-    default: compute_block<3, NB>(K.k3, S, at, rec, m, q.kt, q.rl, nrow, wave, lane); break;
+__device__ inline void compute_any(const AllConsts& K, const Smem& S, int c, uint32_t boff, uint32_t m, int rl,
+                                   int nrow, int wave, uint32_t lane) {
+  switch (c) {
+    case 0: compute_block<0, NB>(K.k0, S, boff, m, rl, nrow, wave, lane); break;
+    case 1: compute_block<1, NB>(K.k1, S, boff, m, rl, nrow, wave, lane); break;
+    case 2: compute_block<2, NB>(K.k2, S, boff, m, rl, nrow, wave, lane); break;
+    default: compute_block<3, NB>(K.k3, S, boff, m, rl, nrow, wave, lane); break;
   }
 }
 
-// Stages the x window of k-tile kt into LDS as pairs (x_2p, x_2p+1) with the
-// per-group sums and bias constants: four threads per (batch row, k-group),
-// each owning 8 of the 32 pairs, reduced across the four lanes.
-template <int NB>
-__device__ inline void stage_x(const GemvMat& M, const Smem& S, int kt, int tid) {
-  const int G = M.n_groups, K = G * kGroup;
-  const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
-  for (int i = tid; i < NB * kTileGroups * 4; i += kThreads) {
-    const int nb = i / (kTileGroups * 4), rem = i - nb * kTileGroups * 4, kgl = rem >> 2, qt = rem & 3;
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-    if (kgl < ng) {
+// x of k-groups [g0, g0 + ng): four threads per (batch row, k-group), each
+// owning 8 of the 32 pairs. The loads are issued first, together with the
+// tile headers, and waited for once.
+template <int NB, int WAVES>
+struct XItems {
+  static constexpr int N = (NB * kTileGroups * 4 + WAVES * kWave - 1) / (WAVES * kWave);
+  uint4 lo[N], hi[N];
+};
+
+template <int NB, int WAVES>
+__device__ inline void load_x(const GemvMat& M, XItems<NB, WAVES>& X, int g0, int ng, int tid) {
+  const int K = M.n_groups * kGroup;
+#pragma unroll
+  for (int it = 0; it < XItems<NB, WAVES>::N; ++it) {
+    const int i = tid + it * WAVES * kWave;
+    X.lo[it] = make_uint4(0, 0, 0, 0);
+    X.hi[it] = make_uint4(0, 0, 0, 0);
+    if (i < NB * ng * 4) {
+      const int nb = i / (ng * 4), rem = i - nb * ng * 4, kgl = rem >> 2, qt = rem & 3;
       const uint16_t* xr = M.x + (size_t)nb * K + (size_t)(g0 + kgl) * kGroup + 16 * qt;
-      lo = *reinterpret_cast<const uint4*>(xr);        // pairs 8qt .. 8qt+3
-      hi = *reinterpret_cast<const uint4*>(xr + 8);    // pairs 8qt+4 .. 8qt+7
+      X.lo[it] = *reinterpret_cast<const uint4*>(xr);        // pairs 8qt .. 8qt+3
+      X.hi[it] = *reinterpret_cast<const uint4*>(xr + 8);    // pairs 8qt+4 .. 8qt+7
     }
-    uint32_t* xk = S.xs + (nb * kTileGroups + kgl) * kXStride + 8 * qt;
-    *reinterpret_cast<uint4*>(xk) = lo;
-    *reinterpret_cast<uint4*>(xk + 4) = hi;
-    const uint32_t p[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    float X = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
-    const bool odd = qt & 1;   // pair index 8qt + e; for 1-bit fields f = pair % 16
+  }
+}
+
+// Writes the pairs (x_2p, x_2p+1) to LDS with the per-group sums and bias
+// constants, reduced across the four threads of a (batch row, k-group).
+template <int NB, int WAVES>
+__device__ inline void stage_x(const Smem& S, const XItems<NB, WAVES>& X, int ng, int tid) {
+#pragma unroll
+  for (int it = 0; it < XItems<NB, WAVES>::N; ++it) {
+    const int i = tid + it * WAVES * kWave;
+    if (it * WAVES * kWave >= NB * ng * 4) break;            // uniform: no item of this round
+    const int nb = i / (ng * 4), rem = i - nb * ng * 4, kgl = rem >> 2, qt = rem & 3;
+    const bool live = i < NB * ng * 4;
+    const uint32_t p[8] = {X.lo[it].x, X.lo[it].y, X.lo[it].z, X.lo[it].w,
+                           X.hi[it].x, X.hi[it].y, X.hi[it].z, X.hi[it].w};
+    if (live) {
+      uint32_t* xk = S.xs + (nb * kTileGroups + kgl) * kXStride + 8 * qt;
+      *reinterpret_cast<uint4*>(xk) = X.lo[it];
+      *reinterpret_cast<uint4*>(xk + 4) = X.hi[it];
+    }
+    float Xs = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    const bool odd = qt & 1;   // pair index 8qt + e: f = pair % 16 for 1-bit, pair % 8 for 2-bit
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const half2_t h = as_h2(p[e]);
       const float sj = (float)h.x + (float)h.y;
-      X += sj;
+      Xs += sj;
       c0 += (odd ? field_bias(0, 8 + e) : field_bias(0, e)) * sj;
       c1 += field_bias(1, e) * sj;
       c2 += field_bias(2, e % 4) * sj;
@@ -398,176 +481,247 @@ __device__ inline void stage_x(const GemvMat& M, const Smem& S, int kt, int tid)
     }
 #pragma unroll
     for (int d = 1; d <= 2; d <<= 1) {
-      X += __shfl_xor(X, d, kWave);
+      Xs += __shfl_xor(Xs, d, kWave);
       c0 += __shfl_xor(c0, d, kWave);
       c1 += __shfl_xor(c1, d, kWave);
       c2 += __shfl_xor(c2, d, kWave);
       c3 += __shfl_xor(c3, d, kWave);
     }
-    if (qt == 0) {
+    if (live && qt == 0) {
       S.cx[(nb * 4 + 0) * kTileGroups + kgl] = c0;
       S.cx[(nb * 4 + 1) * kTileGroups + kgl] = c1;
       S.cx[(nb * 4 + 2) * kTileGroups + kgl] = c2;
       S.cx[(nb * 4 + 3) * kTileGroups + kgl] = c3;
-      S.xsum[nb * kTileGroups + kgl] = X;
+      S.xsum[nb * kTileGroups + kgl] = Xs;
     }
   }
 }
 
-template <int NB, bool RESID>
-__global__ __launch_bounds__(kThreads) void k_gemv(const GemvLaunch L) {
+// y[b][n] += sum_k x[b][k] r[n][k] over the workgroup's k-tile, one row per
+// wavefront at a time (all copies are consumed by then, so plain loads wait
+// for nothing else).
+template <int NB, int WAVES>
+__device__ inline void residual_rows(const GemvMat& M, const Smem& S, int r0, int nrow, int g0, int ng, int wave,
+                                     uint32_t lane) {
+  const int K = M.n_groups * kGroup;
+  for (int ri = wave; ri < nrow; ri += WAVES) {
+    const int row = r0 + ri;
+    if (row >= M.n_rows) break;
+    const uint4* rr = reinterpret_cast<const uint4*>(M.resid + (size_t)row * K + (size_t)g0 * kGroup);
+    float acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = 0.f;
+    const int n16 = ng * 8;                                  // 16-byte chunks in the window
+    uint4 rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = (int)lane + kWave * u;
+      rv[u] = c < n16 ? rr[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = (int)lane + kWave * u;
+      if (c < n16) {
+        const int kgl = c >> 3, qq = c & 7;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(S.xs + (nb * kTileGroups + kgl) * kXStride + 4 * qq);
+          acc[nb] = dot2(rv[u].x, xv.x, acc[nb]);
+          acc[nb] = dot2(rv[u].y, xv.y, acc[nb]);
+          acc[nb] = dot2(rv[u].z, xv.z, acc[nb]);
+          acc[nb] = dot2(rv[u].w, xv.w, acc[nb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float v = acc[nb];
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+      if (lane == 0) S.yw[(wave * NB + nb) * nrow + ri] += v;
+    }
+  }
+}
+
+// Descriptor of one block of a wavefront, built by one lane, read back with
+// v_readlane in the block loop:
+//   bits 0-8 ring offset / 16, 9-10 width class, 11-17 records, 18-23 tile,
+//   24-29 copies that may still be outstanding when the block is decoded,
+//   30-31 copies to issue after it.
+// With pieces of 1 KiB at stream offset 1024 p going to ring slot p mod S, and
+// piece p issued as soon as every block before stream offset 1024 (p - S + 1)
+// is decoded, the pieces issued before block j are min(np, pos_j / 1024 + S)
+// and the block needs the first ceil((pos_j + size_j) / 1024): both closed
+// forms of the block's stream position.
+__device__ inline uint32_t make_desc(const BlockInfo& b, uint32_t B0, uint32_t np, uint32_t slots, uint32_t ring_mask) {
+  const uint32_t pos = b.byte - B0;
+  const uint32_t need = (pos + b.size + 1023u) >> 10;
+  const uint32_t before = min(np, (pos >> 10) + slots);
+  const uint32_t after = min(np, ((pos + b.size) >> 10) + slots);
+  return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 9) | (b.m << 11) | ((uint32_t)b.t << 18) |
+         ((before - need) << 24) | ((after - before) << 30);
+}
+
+template <int NB, int WAVES, bool RESID>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint32_t s_last;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps block bookkeeping scalar
   int mi = 0;
   for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
   const GemvMat& M = L.mats[mi];
-  const int rt0 = ((int)blockIdx.x - M.wg_begin) * M.rt_per_wg;
+  const int j = (int)blockIdx.x - M.wg_begin;
+  const int kt = j / M.wg_per_col, cj = j - kt * M.wg_per_col;
+  const int rt0 = cj * M.rt_per_wg;
   const int nrl = min(M.rt_per_wg, M.row_tiles - rt0);
-  const int nrow = nrl * kTile;
+  const int nrow = nrl * kTile, r0 = rt0 * kTile;
+  const int g0 = kt * kTileGroups, ng = min(kTileGroups, M.n_groups - g0);
 
   Smem S;
   S.xs = reinterpret_cast<uint32_t*>(smem);
   S.cx = reinterpret_cast<float*>(S.xs + NB * kTileGroups * kXStride);
   S.xsum = S.cx + NB * 4 * kTileGroups;
   S.yw = S.xsum + NB * kTileGroups;
-  uint8_t* rings = reinterpret_cast<uint8_t*>(S.yw + kWaves * NB * L.rt_per_wg * kTile);
+  uint8_t* rings = reinterpret_cast<uint8_t*>(S.yw + WAVES * NB * L.rt_per_wg * kTile);
   const uint32_t ring = L.ring_bytes;
   S.ring = rings + wave * ring;
+  S.ring_mask = ring - 1u;
+  const uint32_t ring_lds = lds_addr(S.ring);
+  const uint32_t slots = ring >> 10;
+  const u32x4 rsrc = make_rsrc(M.stream, M.stream_bytes);
 
-  Rsrc R;
-  R.so = make_rsrc(M.so, M.so_bytes);
-  R.meta = make_rsrc(M.meta, M.meta_bytes);
-  R.codes = make_rsrc(M.codes, M.code_bytes);
+  // Ordinary loads (x, tile headers) come before the first copy and are
+  // waited for once, on every path: waiting for them later would also wait
+  // for every copy in flight.
+  XItems<NB, WAVES> X;
+  load_x<NB, WAVES>(M, X, g0, ng, tid);
+  uint4 h = make_uint4(0, 0, 0, 0);
+  if ((int)lane <= nrl) h = *reinterpret_cast<const uint4*>(M.tiles + 4 * (size_t)(kt * M.row_tiles + rt0 + (int)lane));
+  __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));
+  const TileLanes T = make_tile_lanes(h, nrl, lane);
 
-  // Fill the ring before anything else, so HBM latency overlaps the staging.
-  Cur iq = cur_first(M, rt0, nrl, wave);      // next block to copy
-  Cur cq = iq;                                // next block to decode
-  uint32_t ipos = 0, cpos = 0;                // ring byte counters (copy / decode side)
-  int issued = 0, consumed = 0;               // DMA instructions issued / belonging to decoded blocks
-  int pending = 0;                            // blocks copied but not decoded yet
-  // A block may be copied when it ends within one ring length of the oldest
-  // pending block; with nothing pending it always fits (at offset 0 at worst).
-  while (iq.valid) {
-    const uint32_t bytes = ring_block_bytes(iq.c);
-    uint32_t p = ipos;
-    const uint32_t at = ring_place(p, bytes, ring);
-    if (pending > 0 && p - cpos > ring) break;
-    ipos = p;
-    issued += issue_block(R, S.ring, at, iq, lane);
-    ++pending;
-    cur_advance(iq, M, rt0, nrl, kWaves);
+  // This wavefront's blocks [b0, b1) and their bytes [B0, B0 + span), in
+  // pieces of 1 KiB; the first `slots` pieces go out at once.
+  const int b0 = (int)(((int64_t)T.total * wave) / WAVES);
+  const int b1 = (int)(((int64_t)T.total * (wave + 1)) / WAVES);
+  uint32_t B0 = 0, span = 0, np = 0, issued = 0;
+  if (b0 < b1) {
+    B0 = __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b0).byte);
+    const uint32_t B1 = b1 < T.total ? __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b1).byte)
+                                     : __builtin_amdgcn_readlane(T.byte0, T.nt);
+    span = B1 - B0;
+    np = (span + 1023u) >> 10;
   }
+  auto issue = [&](uint32_t upto) {
+    for (; issued < upto; ++issued) {
+      const uint32_t piece = issued << 10;
+      if (16u * lane < span - piece) dma16(rsrc, ring_lds + ((issued & (slots - 1u)) << 10), B0 + piece + 16u * lane);
+    }
+  };
+  issue(min(np, slots));
 
-  for (int i = tid; i < kWaves * NB * nrow; i += kThreads) S.yw[i] = 0.0f;
+  stage_x<NB, WAVES>(S, X, ng, tid);
+  for (int i = tid; i < WAVES * NB * nrow; i += WAVES * kWave) S.yw[i] = 0.0f;
   AllConsts K;
   K.k0 = make_consts<0>();
   K.k1 = make_consts<1>();
   K.k2 = make_consts<2>();
   K.k3 = make_consts<3>();
+  lds_barrier();                              // x table and zeroed row sums visible
 
-  for (int kt = 0; kt < M.k_tiles; ++kt) {
-    if (kt > 0) __syncthreads();              // everyone is done with the previous x window
-    stage_x<NB>(M, S, kt, tid);
-    __syncthreads();
-    while (cq.valid && cq.kt == kt) {
-      const uint32_t bytes = ring_block_bytes(cq.c);
-      const uint32_t at = ring_place(cpos, bytes, ring);
-      consumed += block_dma_count(cq.c, cur_m(cq));
-      wait_vmcnt(issued - consumed);
-      compute_any<NB>(K, S, at, cq, nrow, wave, lane);
-      cur_advance(cq, M, rt0, nrl, kWaves);
-      --pending;
-      // Refill the freed ring space; the decode's LDS reads are complete first.
-      __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0)
-      while (iq.valid) {
-        const uint32_t ib = ring_block_bytes(iq.c);
-        uint32_t p = ipos;
-        const uint32_t iat = ring_place(p, ib, ring);
-        if (pending > 0 && p - cpos > ring) break;
-        ipos = p;
-        issued += issue_block(R, S.ring, iat, iq, lane);
-        ++pending;
-        cur_advance(iq, M, rt0, nrl, kWaves);
-      }
-    }
-    if constexpr (RESID) {
-      // y[b][n] += sum_k x[b][k] r[n][k] over this window, one row per wavefront.
-      const int K = M.n_groups * kGroup;
-      const int g0 = kt * kTileGroups, ng = min(kTileGroups, M.n_groups - g0);
-      for (int ri = wave; ri < nrow; ri += kWaves) {
-        const int row = rt0 * kTile + ri;
-        if (row >= M.n_rows) break;
-        const uint4* rr = reinterpret_cast<const uint4*>(M.resid + (size_t)row * K + (size_t)g0 * kGroup);
-        float acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = 0.f;
-        for (int c = lane; c < ng * 8; c += kWave) {           // 16-byte chunks of the window
-          const uint4 rv = rr[c];
-          const int kgl = c >> 3, q = c & 7;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(S.xs + (nb * kTileGroups + kgl) * kXStride + 4 * q);
-            acc[nb] = dot2(rv.x, xv.x, acc[nb]);
-            acc[nb] = dot2(rv.y, xv.y, acc[nb]);
-            acc[nb] = dot2(rv.z, xv.z, acc[nb]);
-            acc[nb] = dot2(rv.w, xv.w, acc[nb]);
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float v = acc[nb];
-#pragma unroll
-          for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-          if (lane == 0) S.yw[(wave * NB + nb) * nrow + ri] += v;
-        }
-      }
+  for (int base = b0; base < b1; base += kWave) {
+    const uint32_t jl = min((uint32_t)(base + (int)lane), (uint32_t)(b1 - 1));
+    const uint32_t desc = make_desc(block_info(T, jl), B0, np, slots, S.ring_mask);
+    const int n_here = min(kWave, b1 - base);
+    for (int k = 0; k < n_here; ++k) {
+      const uint32_t d = __builtin_amdgcn_readlane(desc, k);
+      wait_vmcnt((int)((d >> 24) & 63u));
+      compute_any<NB>(K, S, (int)((d >> 9) & 3u), (d & 511u) << 4, (d >> 11) & 127u, (int)((d >> 18) & 63u), nrow,
+                      wave, lane);
+      // Refill the freed ring slots; the decode's LDS reads are complete first.
+      __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+      issue(issued + (d >> 30));
     }
   }
-  wait_vmcnt(0);
-  __syncthreads();
+  if constexpr (RESID) residual_rows<NB, WAVES>(M, S, r0, nrow, g0, ng, wave, lane);
+  lds_barrier();
 
-  for (int i = tid; i < NB * nrow; i += kThreads) {
+  // Rows of this workgroup: sum the wavefront slices in a fixed order.
+  const bool split = M.k_tiles > 1;
+  for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
     const int nb = i / nrow, ri = i - nb * nrow;
-    const int row = rt0 * kTile + ri;
+    const int row = r0 + ri;
     if (row < M.n_rows) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += S.yw[(w * NB + nb) * nrow + ri];
+      for (int w = 0; w < WAVES; ++w) v += S.yw[(w * NB + nb) * nrow + ri];
+      if (split)
+        M.part[((size_t)kt * NB + nb) * M.n_rows + row] = v;
+      else
+        M.y[(size_t)nb * M.n_rows + row] = v;
+    }
+  }
+  if (!split) return;
+  // Several k-tiles: the last workgroup of this row range to arrive adds the
+  // partial rows of all k-tiles in k-tile order.
+  __syncthreads();                            // partial rows stored by every wavefront
+  if (tid == 0) {
+    __threadfence();                          // release the partial rows device-wide
+    const uint32_t before = atomicAdd(&M.arrivals[cj], 1u);
+    s_last = before == (uint32_t)(M.k_tiles - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();                            // acquire the other workgroups' rows
+  for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
+    const int nb = i / nrow, ri = i - nb * nrow;
+    const int row = r0 + ri;
+    if (row < M.n_rows) {
+      float v = 0.f;
+      for (int t = 0; t < M.k_tiles; ++t)
+        v += __builtin_nontemporal_load(&M.part[((size_t)t * NB + nb) * M.n_rows + row]);
       M.y[(size_t)nb * M.n_rows + row] = v;
     }
   }
+  if (tid == 0) atomicExch(&M.arrivals[cj], 0u);   // ready for the next launch
 }
 
+int gemv_waves(int nb) { return nb <= 2 ? 16 : 8; }
+
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes) {
-  size_t b = (size_t)nb * kTileGroups * kXStride * 4;   // x window
+  const int waves = gemv_waves(nb);
+  size_t b = (size_t)nb * kTileGroups * kXStride * 4;   // x pairs
   b += (size_t)nb * 4 * kTileGroups * 4;                // bias constants
   b += (size_t)nb * kTileGroups * 4;                    // x sums
-  b += (size_t)kWaves * nb * rt_per_wg * kTile * 4;     // per-wavefront row sums
-  b += (size_t)kWaves * ring_bytes;                     // rings
+  b += (size_t)waves * nb * rt_per_wg * kTile * 4;      // per-wavefront row sums
+  b += (size_t)waves * ring_bytes;                      // rings
   return b;
 }
 
-uint32_t gemv_ring_min_bytes() { return kRingMinBytes; }
+// The ring is a power of two of at least four 1 KiB slots: a block spans at
+// most three pieces (1408 bytes at an odd start).
+uint32_t gemv_ring_min_bytes() { return 4u * 1024u; }
 
-template <int NB, bool RESID>
+template <int NB, int WAVES, bool RESID>
 static hipError_t launch_one(const GemvLaunch& L, int n_wg, size_t lds, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, RESID>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, WAVES, RESID>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemv<NB, RESID>), dim3(n_wg), dim3(kThreads), lds, s, L);
+  hipLaunchKernelGGL((k_gemv<NB, WAVES, RESID>), dim3(n_wg), dim3(WAVES * kWave), lds, s, L);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s) {
-#define VBQ_CASE(N)                                                              \
-  case N:                                                                        \
-    return resid ? launch_one<N, true>(L, n_wg, lds, s) : launch_one<N, false>(L, n_wg, lds, s);
+#define VBQ_CASE(N)                                                                                  \
+  case N:                                                                                            \
+    return resid ? launch_one<N, (N <= 2 ? 16 : 8), true>(L, n_wg, lds, s)                           \
+                 : launch_one<N, (N <= 2 ? 16 : 8), false>(L, n_wg, lds, s);
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)

@@ -1,6 +1,6 @@
 // Device-side packing: per-group round-to-nearest quantisation to fp16
-// scale/offset and the tiled (16 rows x 64 k-groups), width-sorted execution
-// layout.
+// scale/offset and the tiled (16 rows x 64 k-groups), width-sorted byte
+// stream of blocks.
 //
 // Groups of 64 weights with per-group widths {1,2,4,8} and packed low-bit
 // storage: VBQ abstract (page "In-Cell Learning: Language Models That Update
@@ -9,10 +9,11 @@
 //
 // Three launches on the caller's stream:
 //   1. k_pack_count: per tile, how many groups of each width class.
-//   2. k_pack_scan : one workgroup scans the tiles into record and code bases
+//   2. k_pack_scan : one workgroup scans the tiles into record and byte bases
 //                    and writes the totals entry (with error flags).
-//   3. k_pack_tiles: per tile, rank every group inside its class in
-//                    (k-group, row) order, quantise it and write its record.
+//   3. k_pack_tiles: per tile, clear its bytes, rank every group inside its
+//                    class in (k-group, row) order, quantise it and write its
+//                    codes, scale/offset and meta into its block.
 // The quantiser's arithmetic must give the same bits on every run and match the
 // documented binary32 sequence, so this file is built with -ffp-contract=off and
 // uses correctly rounded division and round-half-even conversions.
@@ -20,13 +21,14 @@
 
 namespace vbq {
 
-__global__ __launch_bounds__(256) void k_pack_count(const uint8_t* __restrict__ widths, int N, int G, int KT,
+// Tiles are stored k-tile major: t = kt * RT + rt.
+__global__ __launch_bounds__(256) void k_pack_count(const uint8_t* __restrict__ widths, int N, int G, int RT,
                                                     uint32_t* __restrict__ tiles) {
   __shared__ uint32_t cnt[5];
   const int t = blockIdx.x;
   if (threadIdx.x < 5) cnt[threadIdx.x] = 0;
   __syncthreads();
-  const int rt = t / KT, kt = t - rt * KT;
+  const int kt = t / RT, rt = t - kt * RT;
   const int r0 = rt * kTile, rows = min(kTile, N - r0);
   const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
   uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0, bad = 0;
@@ -64,8 +66,8 @@ __device__ inline uint64_t wave_incl_scan(uint64_t v, int lane) {
 }
 
 __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles, int n_tiles,
-                                                    uint64_t cap_records, uint64_t cap_code16,
-                                                    uint64_t cap_tile_records, uint64_t cap_tile_code16) {
+                                                    uint64_t cap_records, uint64_t cap_bytes16,
+                                                    uint64_t cap_tile_bytes16) {
   __shared__ uint64_t wr[16], wc[16];
   __shared__ uint64_t carry_r, carry_c;
   __shared__ uint32_t bad_total, too_big;
@@ -85,9 +87,9 @@ __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles
       const uint32_t a = tiles[4 * t + 2], b = tiles[4 * t + 3];
       const uint32_t n0 = a & 0xFFFF, n1 = a >> 16, n2 = b & 0xFFFF, n3 = b >> 16;
       nr = (uint64_t)n0 + n1 + n2 + n3;
-      nc = tile_code_bytes(n0, n1, n2, n3) / 16;
+      nc = tile_bytes(n0, n1, n2, n3) / 16;
       bad = tiles[4 * t + 0];
-      if (nr > cap_tile_records || nc > cap_tile_code16) atomicOr(&too_big, 1u);
+      if (nc > cap_tile_bytes16) atomicOr(&too_big, 1u);
     }
     const uint64_t ir = wave_incl_scan(nr, lane), ic = wave_incl_scan(nc, lane);
     if (lane == 63) {
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(1024) void k_pack_scan(uint32_t* __restrict__ tiles
   if (tid == 0) {
     uint32_t flags = 0;
     if (bad_total) flags |= kFlagInvalidWidth;
-    if (carry_r > cap_records || carry_c > cap_code16 || carry_r > 0xFFFFFFFFull || carry_c > 0xFFFFFFFFull)
+    if (carry_r != cap_records || carry_c > cap_bytes16 || carry_r > 0xFFFFFFFFull || carry_c > 0xFFFFFFFFull)
       flags |= kFlagCapacity;
     if (too_big) flags |= kFlagTileSize;
     tiles[4 * n_tiles + 0] = (uint32_t)carry_r;
@@ -178,60 +180,59 @@ __device__ inline void quantize_pack_group(const float* __restrict__ wg, uint32_
   }
 }
 
+// Writes record idx of class segment C (n_c records, segment at `seg`).
 template <int C>
-__device__ inline void write_record(const float* __restrict__ wg, uint32_t rec, uint32_t idx, uint32_t n_c,
-                                    uint8_t* __restrict__ seg, uint32_t* __restrict__ so,
-                                    uint16_t* __restrict__ meta, uint16_t meta_v) {
+__device__ inline void write_record(const float* __restrict__ wg, uint32_t idx, uint32_t n_c, uint8_t* __restrict__ seg,
+                                    uint16_t meta_v) {
   constexpr int B = 1 << C;
+  constexpr uint32_t BR = block_records(C);
   uint32_t words[2 * B];
   uint32_t so_v;
   quantize_pack_group<B>(wg, &so_v, words);
-  so[rec] = so_v;
-  meta[rec] = meta_v;
-  if (B == 1) {
-    *reinterpret_cast<uint2*>(seg + 8ull * idx) = make_uint2(words[0], words[1]);
-    if ((n_c & 1) && idx == n_c - 1)  // pad segment 0 to 16 bytes with zeros
-      *reinterpret_cast<uint2*>(seg + 8ull * idx + 8) = make_uint2(0u, 0u);
+  const uint32_t k = idx / BR, l = idx - k * BR;
+  const uint32_t m = min(BR, n_c - k * BR);
+  uint8_t* blk = seg + (uint64_t)k * block_bytes(C, BR);
+  if constexpr (B == 1) {
+    *reinterpret_cast<uint2*>(blk + 8u * l) = make_uint2(words[0], words[1]);
   } else {
-    const uint32_t blk = idx / kBlock, l = idx % kBlock;
-    const uint32_t m = min((uint32_t)kBlock, n_c - blk * kBlock);
-    uint8_t* bbase = seg + (uint64_t)blk * kBlock * 8 * B;
 #pragma unroll
     for (int q = 0; q < B / 2; ++q)
-      *reinterpret_cast<uint4*>(bbase + ((uint64_t)q * m + l) * 16) =
+      *reinterpret_cast<uint4*>(blk + ((uint32_t)q * m + l) * 16u) =
           make_uint4(words[4 * q + 0], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
   }
+  *reinterpret_cast<uint32_t*>(blk + codes_area(C, m) + 4u * l) = so_v;
+  *reinterpret_cast<uint16_t*>(blk + codes_area(C, m) + so_area(m) + 2u * l) = meta_v;
 }
 
 __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W, const uint8_t* __restrict__ widths,
-                                                    int N, int G, int KT, const uint32_t* __restrict__ tiles,
-                                                    int n_tiles, uint32_t* __restrict__ so,
-                                                    uint16_t* __restrict__ meta, uint32_t* __restrict__ codes) {
+                                                    int N, int G, int RT, const uint32_t* __restrict__ tiles,
+                                                    int n_tiles, uint8_t* __restrict__ stream) {
   if (tiles[4 * n_tiles + 3] != 0) return;   // invalid widths or mismatched buffers: write nothing
   __shared__ uint32_t carry[4];
   __shared__ uint32_t wcnt[4][4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rt = t / KT, kt = t - rt * KT;
+  const int kt = t / RT, rt = t - kt * RT;
   const int r0 = rt * kTile, rows = min(kTile, N - r0);
   const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
   const size_t K = (size_t)G * kGroup;
-  const uint32_t rec0 = tiles[4 * t + 0];
   const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
   const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
-  const uint32_t cbase[4] = {rec0, rec0 + n[0], rec0 + n[0] + n[1], rec0 + n[0] + n[1] + n[2]};
-  uint8_t* tile_bytes = reinterpret_cast<uint8_t*>(codes) + (uint64_t)tiles[4 * t + 1] * 16;
+  uint8_t* tile_base = stream + (uint64_t)tiles[4 * t + 1] * 16;
   const uint64_t s1 = seg_bytes(0, n[0]), s2 = s1 + seg_bytes(1, n[1]), s3 = s2 + seg_bytes(2, n[2]);
+  const uint64_t tb = s3 + seg_bytes(3, n[3]);
+  // Clear the tile (padding must be zero), then write the records over it.
+  for (uint64_t i = tid; i < tb / 16; i += blockDim.x)
+    reinterpret_cast<uint4*>(tile_base)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 4) carry[tid] = 0;
   __syncthreads();
   const int total = rows * ng;
   for (int base = 0; base < total; base += 256) {
     const int i = base + tid;
-    int c = -1, kg = 0, r = 0;
+    int c = -1, kl = 0, r = 0;
     if (i < total) {
-      const int kl = i / rows;   // (k-group, row) order
+      kl = i / rows;   // (k-group, row) order
       r = i - kl * rows;
-      kg = g0 + kl;
-      c = class_of_width(widths[(size_t)(r0 + r) * G + kg]);
+      c = class_of_width(widths[(size_t)(r0 + r) * G + g0 + kl]);
     }
     uint32_t rank = 0;
 #pragma unroll
@@ -244,13 +245,13 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W,
     if (c >= 0) {
       uint32_t idx = carry[c] + rank;
       for (int w = 0; w < wave; ++w) idx += wcnt[w][c];
-      const float* wg = W + (size_t)(r0 + r) * K + (size_t)kg * kGroup;
-      const uint16_t mv = (uint16_t)(r | (kg << 4));
+      const float* wg = W + (size_t)(r0 + r) * K + (size_t)(g0 + kl) * kGroup;
+      const uint16_t mv = (uint16_t)(r | (kl << 4));
       switch (c) {
-        case 0: write_record<0>(wg, cbase[0] + idx, idx, n[0], tile_bytes, so, meta, mv); break;
-        case 1: write_record<1>(wg, cbase[1] + idx, idx, n[1], tile_bytes + s1, so, meta, mv); break;
-        case 2: write_record<2>(wg, cbase[2] + idx, idx, n[2], tile_bytes + s2, so, meta, mv); break;
-        default: write_record<3>(wg, cbase[3] + idx, idx, n[3], tile_bytes + s3, so, meta, mv); break;
+        case 0: write_record<0>(wg, idx, n[0], tile_base, mv); break;
+        case 1: write_record<1>(wg, idx, n[1], tile_base + s1, mv); break;
+        case 2: write_record<2>(wg, idx, n[2], tile_base + s2, mv); break;
+        default: write_record<3>(wg, idx, n[3], tile_base + s3, mv); break;
       }
     }
     __syncthreads();
@@ -261,13 +262,13 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W,
 
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s) {
   const int G = m.n_cols / kGroup;
-  const int KT = k_tiles(G);
+  const int RT = row_tiles(m.n_rows);
   const int T = (int)m.n_tiles;
-  hipLaunchKernelGGL(k_pack_count, dim3(T), dim3(256), 0, s, widths, m.n_rows, G, KT, m.tiles);
+  hipLaunchKernelGGL(k_pack_count, dim3(T), dim3(256), 0, s, widths, m.n_rows, G, RT, m.tiles);
   hipLaunchKernelGGL(k_pack_scan, dim3(1), dim3(1024), 0, s, m.tiles, T, (uint64_t)m.n_records,
-                     (uint64_t)m.n_code16, (uint64_t)m.max_tile_records, (uint64_t)m.max_tile_code16);
-  hipLaunchKernelGGL(k_pack_tiles, dim3(T), dim3(256), 0, s, W, widths, m.n_rows, G, KT, m.tiles, T, m.so,
-                     m.meta, m.codes);
+                     (uint64_t)m.n_bytes16, (uint64_t)m.max_tile_bytes16);
+  hipLaunchKernelGGL(k_pack_tiles, dim3(T), dim3(256), 0, s, W, widths, m.n_rows, G, RT, m.tiles, T,
+                     reinterpret_cast<uint8_t*>(m.stream));
   return hipGetLastError();
 }
 

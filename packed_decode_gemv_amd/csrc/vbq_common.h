@@ -13,7 +13,6 @@ constexpr int kGroup = VBQ_GROUP;
 constexpr int kTile = VBQ_TILE_ROWS;
 constexpr int kTileGroups = VBQ_TILE_GROUPS;
 constexpr int kWave = 64;
-constexpr int kBlock = 64;  // records per layout block (one per lane)
 
 // Error flags in the totals entry of the tile table.
 constexpr uint32_t kFlagInvalidWidth = 1u;
@@ -29,47 +28,74 @@ __host__ __device__ inline int class_of_width(int b) {
   return b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : b == 8 ? 3 : -1;
 }
 
-// Byte size of the code segment of class c holding n records.
-__host__ __device__ inline uint64_t seg_bytes(int c, uint64_t n) {
-  return c == 0 ? ((8 * n + 15) / 16) * 16 : n * (8ull << c);
+// ---- Block geometry of the byte stream ------------------------------------
+// Records per block of width class c: a full block of width 2, 4 or 8 carries
+// 1024 code bytes (one 16-byte piece per lane), width 1 carries 512.
+__host__ __device__ constexpr uint32_t block_records(int c) { return c < 2 ? 64u : c == 2 ? 32u : 16u; }
+// Lanes that share one record when a block is decoded (16 code bytes each).
+__host__ __device__ constexpr uint32_t lanes_per_record(int c) { return c < 2 ? 1u : c == 2 ? 2u : 4u; }
+__host__ __device__ constexpr uint32_t up16(uint32_t v) { return (v + 15u) & ~15u; }
+__host__ __device__ constexpr uint32_t codes_area(int c, uint32_t m) { return c == 0 ? up16(8u * m) : (8u << c) * m; }
+__host__ __device__ constexpr uint32_t so_area(uint32_t m) { return up16(4u * m); }
+__host__ __device__ constexpr uint32_t meta_area(uint32_t m) { return up16(2u * m); }
+__host__ __device__ constexpr uint32_t block_bytes(int c, uint32_t m) {
+  return codes_area(c, m) + so_area(m) + meta_area(m);
 }
-
-// Byte size of a tile's code area.
-__host__ __device__ inline uint64_t tile_code_bytes(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
+// Bytes of class segment c holding n records: full blocks, then the rest.
+__host__ __device__ inline uint64_t seg_bytes(int c, uint64_t n) {
+  const uint32_t br = block_records(c);
+  const uint64_t full = n / br, rem = n - full * br;
+  return full * block_bytes(c, br) + (rem ? block_bytes(c, (uint32_t)rem) : 0u);
+}
+__host__ __device__ inline uint64_t tile_bytes(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
   return seg_bytes(0, n0) + seg_bytes(1, n1) + seg_bytes(2, n2) + seg_bytes(3, n3);
 }
+__host__ __device__ inline uint32_t seg_blocks(int c, uint32_t n) {
+  return (n + block_records(c) - 1) / block_records(c);
+}
 
-// Host-side launch helpers (defined in api.cpp).
+// Host-side launch helpers.
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s);
 
+// One matrix of a GEMV launch. Its workgroups are laid out k-tile column by
+// k-tile column: workgroup j of the matrix takes column kt = j / wg_per_col and
+// row-tiles [rt0, rt0 + rt_per_wg) with rt0 = (j % wg_per_col) * rt_per_wg.
 struct GemvMat {
   const uint32_t* tiles;
-  const uint32_t* so;
-  const uint16_t* meta;
-  const uint32_t* codes;
+  const uint8_t* stream;
   const uint16_t* x;       // [B][K] fp16
   const uint16_t* resid;   // [N][K] fp16 or null
   float* y;                // [B][N]
+  float* part;             // [KT][B][N] partial rows (k_tiles > 1), else null
+  uint32_t* arrivals;      // [wg_per_col] arrival counters (k_tiles > 1), else null
   int32_t n_rows;
   int32_t n_groups;        // K / 64
   int32_t row_tiles;       // ceil(N / 16)
   int32_t k_tiles;         // ceil(G / 64)
   int32_t rt_per_wg;       // row-tiles per workgroup
+  int32_t wg_per_col;      // workgroups per k-tile column
   int32_t wg_begin;        // first workgroup index of this matrix in the launch
-  uint32_t so_bytes;       // sizes of so / meta / codes, for buffer range checks
-  uint32_t meta_bytes;
-  uint32_t code_bytes;
+  uint32_t stream_bytes;   // size of the stream, for the buffer range checks
 };
 
 constexpr int kMaxMats = 8;
+constexpr int kMaxWgTiles = 64;   // tiles of one workgroup (one per lane)
 
 struct GemvLaunch {
   GemvMat mats[kMaxMats];
   int32_t n_mats;
   int32_t rt_per_wg;       // largest row-tiles per workgroup (LDS row sums)
-  uint32_t ring_bytes;     // LDS ring of each wavefront (multiple of 16)
+  uint32_t ring_bytes;     // LDS ring of each wavefront (multiple of 1024)
 };
 
+// x of one k-tile in LDS: pairs of a k-group take 32 dwords plus 4 of padding,
+// so neighbouring k-groups start 144 bytes apart, which spreads lanes that read
+// different k-groups over the LDS banks while every read keeps an immediate
+// offset; plus 4 bias constants and the sum per k-group.
+constexpr int kXStride = 36;
+constexpr int kXBytesPerGroup = kXStride * 4 + 5 * 4;
+
+int gemv_waves(int nb);
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s);
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes);
 uint32_t gemv_ring_min_bytes();

@@ -8,8 +8,8 @@
 // this kernel re-quantises the served value (dequantised code + residual)
 // against the frozen scale and offset, counts codes that change and residuals
 // that leave the cell, keeps the smallest failing index, and optionally writes
-// the re-quantised codes in the same layout so the artifact can be compared
-// byte for byte.
+// a copy of the byte stream with the re-quantised codes so the artifact can be
+// compared byte for byte.
 //
 // The decision is integer-valued, so the binary32 operation sequence is fixed
 // (built with -ffp-contract=off; correctly rounded division):
@@ -27,33 +27,33 @@ __global__ void k_verify_init(uint64_t* result) {
   }
 }
 
+// Checks record l of a block of class C holding m records (block at `blk`).
 template <int C>
-__device__ inline void verify_record(const uint8_t* seg, uint8_t* rq_seg, uint32_t idx, uint32_t n_c, uint32_t sov,
-                                     uint32_t mt, int r0, int K, const uint16_t* __restrict__ resid,
-                                     uint32_t& mism, uint32_t& ooc, uint64_t& first) {
+__device__ inline void verify_record(const uint8_t* blk, uint8_t* rq_blk, uint32_t m, uint32_t l, int r0, int g0,
+                                     int K, const uint16_t* __restrict__ resid, uint32_t& mism, uint32_t& ooc,
+                                     uint64_t& first) {
   constexpr int B = 1 << C, H = 16 / B, L = (1 << B) - 1;
-  // record words
   uint32_t w[2 * B];
-  uint64_t off[B > 1 ? B / 2 : 1];
+  uint32_t off[B > 1 ? B / 2 : 1];
   if constexpr (B == 1) {
-    off[0] = 8ull * idx;
-    const uint2 v = *reinterpret_cast<const uint2*>(seg + off[0]);
+    off[0] = 8u * l;
+    const uint2 v = *reinterpret_cast<const uint2*>(blk + off[0]);
     w[0] = v.x;
     w[1] = v.y;
   } else {
-    const uint32_t blk = idx / kBlock, l = idx % kBlock;
-    const uint32_t m = min((uint32_t)kBlock, n_c - blk * kBlock);
 #pragma unroll
     for (int q = 0; q < B / 2; ++q) {
-      off[q] = (uint64_t)blk * kBlock * 8 * B + ((uint64_t)q * m + l) * 16;
-      const uint4 v = *reinterpret_cast<const uint4*>(seg + off[q]);
+      off[q] = ((uint32_t)q * m + l) * 16u;
+      const uint4 v = *reinterpret_cast<const uint4*>(blk + off[q]);
       w[4 * q + 0] = v.x;
       w[4 * q + 1] = v.y;
       w[4 * q + 2] = v.z;
       w[4 * q + 3] = v.w;
     }
   }
-  const int row = r0 + (int)(mt & 15), kg = (int)(mt >> 4);
+  const uint32_t sov = *reinterpret_cast<const uint32_t*>(blk + codes_area(C, m) + 4u * l);
+  const uint32_t mt = *reinterpret_cast<const uint16_t*>(blk + codes_area(C, m) + so_area(m) + 2u * l);
+  const int row = r0 + (int)(mt & 15), kg = g0 + (int)(mt >> 4);
   const float s = __half2float(__ushort_as_half((unsigned short)(sov & 0xFFFF)));
   const float o = __half2float(__ushort_as_half((unsigned short)(sov >> 16)));
   const float half_s = __fmul_rn(0.5f, s);
@@ -91,22 +91,31 @@ __device__ inline void verify_record(const uint8_t* seg, uint8_t* rq_seg, uint32
       nw[wi] |= qp << sh;
     }
   }
-  if (rq_seg) {
+  if (rq_blk) {
     if constexpr (B == 1) {
-      *reinterpret_cast<uint2*>(rq_seg + off[0]) = make_uint2(nw[0], nw[1]);
-      if ((n_c & 1) && idx == n_c - 1) *reinterpret_cast<uint2*>(rq_seg + off[0] + 8) = make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(rq_blk + off[0]) = make_uint2(nw[0], nw[1]);
     } else {
 #pragma unroll
       for (int q = 0; q < B / 2; ++q)
-        *reinterpret_cast<uint4*>(rq_seg + off[q]) = make_uint4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
+        *reinterpret_cast<uint4*>(rq_blk + off[q]) = make_uint4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ tiles, const uint32_t* __restrict__ so,
-                                                const uint16_t* __restrict__ meta, const uint32_t* __restrict__ codes,
-                                                int G, int KT, const uint16_t* __restrict__ resid,
-                                                uint64_t* result, uint32_t* requant) {
+// Record i of class segment C (n records) at `seg`.
+template <int C>
+__device__ inline void verify_seg_record(const uint8_t* seg, uint8_t* rq_seg, uint32_t n, uint32_t i, int r0, int g0,
+                                         int K, const uint16_t* resid, uint32_t& mism, uint32_t& ooc,
+                                         uint64_t& first) {
+  constexpr uint32_t BR = block_records(C);
+  const uint32_t k = i / BR, l = i - k * BR, m = min(BR, n - k * BR);
+  const uint64_t bo = (uint64_t)k * block_bytes(C, BR);
+  verify_record<C>(seg + bo, rq_seg ? rq_seg + bo : nullptr, m, l, r0, g0, K, resid, mism, ooc, first);
+}
+
+__global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ tiles, const uint8_t* __restrict__ stream,
+                                                int G, int RT, const uint16_t* __restrict__ resid,
+                                                uint64_t* result, uint8_t* requant) {
   __shared__ uint32_t s_mism, s_ooc;
   __shared__ unsigned long long s_first;
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -115,16 +124,22 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
     s_ooc = 0;
     s_first = ~0ull;
   }
-  __syncthreads();
-  const int K = G * kGroup, r0 = (t / KT) * kTile;
-  const uint32_t rec0 = tiles[4 * t + 0];
+  const int K = G * kGroup;
+  const int kt = t / RT, rt = t - kt * RT;
+  const int r0 = rt * kTile, g0 = kt * kTileGroups;
   const uint64_t tb = (uint64_t)tiles[4 * t + 1] * 16;
   const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
   const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
   const uint64_t sb[4] = {0, seg_bytes(0, n[0]), seg_bytes(0, n[0]) + seg_bytes(1, n[1]),
                           seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2])};
-  const uint8_t* tbytes = reinterpret_cast<const uint8_t*>(codes) + tb;
-  uint8_t* rbytes = requant ? reinterpret_cast<uint8_t*>(requant) + tb : nullptr;
+  const uint64_t size = sb[3] + seg_bytes(3, n[3]);
+  const uint8_t* tbytes = stream + tb;
+  uint8_t* rbytes = requant ? requant + tb : nullptr;
+  // Copy the tile (scales, offsets, meta, padding); codes are rewritten below.
+  if (rbytes)
+    for (uint64_t i = tid; i < size / 16; i += blockDim.x)
+      reinterpret_cast<uint4*>(rbytes)[i] = reinterpret_cast<const uint4*>(tbytes)[i];
+  __syncthreads();
   const uint32_t total = n[0] + n[1] + n[2] + n[3];
   uint32_t mism = 0, ooc = 0;
   uint64_t first = ~0ull;
@@ -135,15 +150,13 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
       idx -= n[c];
       ++c;
     }
-    const uint32_t r = rec0 + (i);
-    const uint32_t sov = so[r], mt = meta[r];
     const uint8_t* seg = tbytes + sb[c];
     uint8_t* rseg = rbytes ? rbytes + sb[c] : nullptr;
     switch (c) {
-      case 0: verify_record<0>(seg, rseg, idx, n[0], sov, mt, r0, K, resid, mism, ooc, first); break;
-      case 1: verify_record<1>(seg, rseg, idx, n[1], sov, mt, r0, K, resid, mism, ooc, first); break;
-      case 2: verify_record<2>(seg, rseg, idx, n[2], sov, mt, r0, K, resid, mism, ooc, first); break;
-      default: verify_record<3>(seg, rseg, idx, n[3], sov, mt, r0, K, resid, mism, ooc, first); break;
+      case 0: verify_seg_record<0>(seg, rseg, n[0], idx, r0, g0, K, resid, mism, ooc, first); break;
+      case 1: verify_seg_record<1>(seg, rseg, n[1], idx, r0, g0, K, resid, mism, ooc, first); break;
+      case 2: verify_seg_record<2>(seg, rseg, n[2], idx, r0, g0, K, resid, mism, ooc, first); break;
+      default: verify_seg_record<3>(seg, rseg, n[3], idx, r0, g0, K, resid, mism, ooc, first); break;
     }
   }
   if (mism) atomicAdd(&s_mism, mism);
@@ -160,8 +173,9 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
-  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(256), 0, s, m.tiles, m.so, m.meta, m.codes,
-                     m.n_cols / kGroup, k_tiles(m.n_cols / kGroup), resid, result, requant);
+  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(256), 0, s, m.tiles,
+                     reinterpret_cast<const uint8_t*>(m.stream), m.n_cols / kGroup, row_tiles(m.n_rows), resid,
+                     result, reinterpret_cast<uint8_t*>(requant));
   return hipGetLastError();
 }
 

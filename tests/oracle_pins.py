@@ -194,81 +194,167 @@ def pin_record_even_odd():
 # --------------------------------------------------------------------------
 # Layout: hand-worked example and structural invariants
 # --------------------------------------------------------------------------
+def _u32_at(stream, byte):
+    assert byte % 4 == 0
+    return int(stream[byte // 4])
+
+
+def _u16_at(stream, byte):
+    w = _u32_at(stream, byte & ~3)
+    return (w >> 16) if (byte & 2) else (w & 0xFFFF)
+
+
 def pin_layout_worked_example():
-    """N=2, K=128, widths [[1,8],[2,1]] (hand-worked).
-    Tile 0 holds all four groups. Class 0 (1-bit) in (k-group,row) order:
-    (kg0,row0), (kg1,row1); class 1: (kg0,row1); class 3: (kg1,row0).
-    meta = row | kg<<4 -> [0, 17, 1, 16]. Code bytes: class 0 = 2*8 = 16,
-    class 1 = 16, class 3 = 64 -> 96 bytes = 6 units of 16."""
+    """N=2, K=128, widths [[1,8],[2,1]] (hand-worked). One tile. Class 0
+    (1-bit) in (k-group,row) order: (kg0,row0), (kg1,row1); class 1: (kg0,row1);
+    class 3: (kg1,row0). Blocks: class 0, m=2: codes 16 B, so 8 -> 16 B,
+    meta 4 -> 16 B = 48 B at byte 0; class 1, m=1: 16 + 16 + 16 = 48 B at 48;
+    class 3, m=1: 64 + 16 + 16 = 96 B at 96; total 192 B = 12 units.
+    meta = row | kg<<4 -> 0, 17 (class 0), 1 (class 1), 16 (class 3)."""
     widths = np.array([[1, 8], [2, 1]], np.uint8)
     r = _rng(16)
     W = (r.standard_normal((2, 128)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 4, 6)
-    assert list(lay["tiles"]) == [0, 0, 2 | (1 << 16), 0 | (1 << 16), 4, 6, 0, 0]
-    assert list(lay["meta"]) == [0, 17, 1, 16]
+    assert oracle.layout_sizes(widths) == (1, 4, 12)
+    assert list(lay["tiles"]) == [0, 0, 2 | (1 << 16), 0 | (1 << 16), 4, 12, 0, 0]
     qs = {}
     for (row, kg, b) in ((0, 0, 1), (1, 1, 1), (1, 0, 2), (0, 1, 8)):
         s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], b)
-        qs[(row, kg)] = (s16, o16, oracle.pack_group_record(q, b))
-    order = [(0, 0), (1, 1), (1, 0), (0, 1)]
-    assert list(lay["so"]) == [qs[k][0] | (qs[k][1] << 16) for k in order]
-    codes = lay["codes"]
-    assert list(codes[0:2]) == list(qs[(0, 0)][2]) and list(codes[2:4]) == list(qs[(1, 1)][2])
-    assert list(codes[4:8]) == list(qs[(1, 0)][2])
-    assert list(codes[8:24]) == list(qs[(0, 1)][2])   # one 8-bit record: 4 chunks, m = 1
+        qs[(row, kg)] = (s16 | (o16 << 16), list(oracle.pack_group_record(q, b)))
+    st = [int(v) for v in lay["stream"]]
+    assert len(st) == 48
+    expect = ([*qs[(0, 0)][1], *qs[(1, 1)][1], qs[(0, 0)][0], qs[(1, 1)][0], 0, 0, 0 | (17 << 16), 0, 0, 0]
+              + [*qs[(1, 0)][1], qs[(1, 0)][0], 0, 0, 0, 1, 0, 0, 0]
+              + [*qs[(0, 1)][1], qs[(0, 1)][0], 0, 0, 0, 16, 0, 0, 0])
+    assert st == expect
+    # the reader rejects a nonzero padding byte (class 0 so padding, word 6)
+    bad = dict(lay, stream=lay["stream"].copy())
+    bad["stream"][6] = 1
+    try:
+        oracle.unpack(bad)
+        raise AssertionError("nonzero padding accepted")
+    except ValueError:
+        pass
 
 
 def pin_layout_block_chunks():
     """Chunk placement inside a block of m records (b >= 2): chunk q of record l
-    sits at (q*m + l)*16 bytes. Checked on one tile with 3 four-bit records."""
+    sits at (q*m + l)*16 bytes. One tile with 3 four-bit records (m=3): codes
+    96 B, then so (12 -> 16 B), then meta (6 -> 16 B)."""
     widths = np.array([[4, 4, 4]], np.uint8)
     W = (_rng(17).standard_normal((1, 192)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    codes = lay["codes"].reshape(-1, 4)               # 16-byte chunks
+    assert oracle.layout_sizes(widths) == (1, 3, 8)
+    chunks = lay["stream"].reshape(-1, 4)               # 16-byte chunks
     for kg in range(3):
-        _, _, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
+        s16, o16, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
         words = oracle.pack_group_record(q, 4)
-        assert list(codes[0 * 3 + kg]) == list(words[0:4])
-        assert list(codes[1 * 3 + kg]) == list(words[4:8])
+        assert list(chunks[0 * 3 + kg]) == list(words[0:4])
+        assert list(chunks[1 * 3 + kg]) == list(words[4:8])
+        assert _u32_at(lay["stream"], 96 + 4 * kg) == s16 | (o16 << 16)
+        assert _u16_at(lay["stream"], 112 + 2 * kg) == kg << 4
+
+
+def pin_layout_block_split():
+    """A class segment longer than one block (hand-worked): N=16, K=192, widths
+    8 in k-group 0 (16 records) and at (row 0, kg 1), 1 elsewhere (31 records).
+    Class 0: one block m=31: codes 248 -> 256, so 124 -> 128, meta 62 -> 64:
+    448 B. Class 3 (capacity 16): a full block (1024 + 64 + 32 = 1120 B) at 448
+    holding kg 0 rows 0..15, then a block of m=1 at 1568 holding (row 0, kg 1):
+    codes at 1568, so at 1632, meta at 1648. Total 1664 B = 104 units."""
+    widths = np.ones((16, 3), np.uint8)
+    widths[:, 0] = 8
+    widths[0, 1] = 8
+    W = (_rng(20).standard_normal((16, 192)) * 0.02).astype(np.float32)
+    lay = oracle.pack(W, widths)
+    assert oracle.layout_sizes(widths) == (1, 48, 104)
+    assert list(lay["tiles"]) == [0, 0, 31, 17 << 16, 48, 104, 0, 0]
+    st = lay["stream"]
+    # full block: chunk q of record l (row l, kg 0) at 448 + (16q + l)*16
+    for row in (0, 7, 15):
+        s16, o16, q = oracle.quantize_group(W[row, 0:64], 8)
+        words = oracle.pack_group_record(q, 8)
+        for qq in range(4):
+            at = 448 + (16 * qq + row) * 16
+            assert [int(v) for v in st[at // 4:at // 4 + 4]] == list(words[4 * qq:4 * qq + 4])
+        assert _u32_at(st, 448 + 1024 + 4 * row) == s16 | (o16 << 16)
+        assert _u16_at(st, 448 + 1024 + 64 + 2 * row) == row
+    s16, o16, q = oracle.quantize_group(W[0, 64:128], 8)
+    assert [int(v) for v in st[1568 // 4:1568 // 4 + 16]] == list(oracle.pack_group_record(q, 8))
+    assert _u32_at(st, 1632) == s16 | (o16 << 16)
+    assert _u16_at(st, 1648) == 16
+    # class 0 block: record l at 8l, so at 256 + 4l, meta at 384 + 2l; first
+    # record is (row 1, kg 1) -- (row 0, kg 1) is 8-bit -- last is (row 15, kg 2)
+    s16, o16, q = oracle.quantize_group(W[1, 64:128], 1)
+    assert [int(v) for v in st[0:2]] == list(oracle.pack_group_record(q, 1))
+    assert _u32_at(st, 256) == s16 | (o16 << 16) and _u16_at(st, 384) == 1 | (1 << 4)
+    assert _u16_at(st, 384 + 2 * 30) == 15 | (2 << 4)
+    assert _u16_at(st, 384 + 2 * 31) == 0 and _u32_at(st, 256 + 4 * 31) == 0   # padding
+
+
+CAP = (64, 64, 32, 16)        # records per block of each width class
+
+
+def _areas(c, m):
+    """(codes, so, meta) area bytes of a block of class c with m records."""
+    up = lambda v: -(-v // 16) * 16
+    return (up(8 * m) if c == 0 else 8 * (1 << c) * m), up(4 * m), up(2 * m)
+
+
+def _walk_tile(base, n):
+    """Independent reading of one tile from the block rules: yields
+    (class, m, l, block byte offset, codes area) per record; returns the tile's
+    end byte via StopIteration.value."""
+    seg = base
+    for c in range(4):
+        full = sum(_areas(c, CAP[c]))
+        for i in range(n[c]):
+            k, l = divmod(i, CAP[c])
+            m = min(CAP[c], n[c] - k * CAP[c])
+            yield c, m, l, seg + k * full, _areas(c, m)
+        k, rem = divmod(n[c], CAP[c])
+        seg += k * full + (sum(_areas(c, rem)) if rem else 0)
+    return seg
 
 
 def pin_layout_invariants():
     r = _rng(18)
-    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70), (18, 64 * 130)]
+    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70), (18, 64 * 130), (64, 512)]
     for (N, K) in cases:
         G = K // 64
         widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G), p=[0.55, 0.2, 0.15, 0.1])
         W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
         lay = oracle.pack(W, widths)
-        T, R, C16 = oracle.layout_sizes(widths)
+        T, R, B16 = oracle.layout_sizes(widths)
         RT, KT = oracle.tile_grid(N, K)
         assert T == RT * KT and R == N * G
         tiles = lay["tiles"].reshape(-1, 4)
-        # closed-form sizes and bases
-        rec = code = 0
+        st = lay["stream"]
+        rec = byte = 0
         for t in range(T):
-            rt, kt = divmod(t, KT)
-            rows = widths[16 * rt:16 * rt + 16, 64 * kt:64 * kt + 64]
-            n = [int((rows == b).sum()) for b in (1, 2, 4, 8)]
-            assert list(tiles[t]) == [rec, code, n[0] | (n[1] << 16), n[2] | (n[3] << 16)]
+            kt, rt = divmod(t, RT)                 # k-tile major storage
+            blkw = widths[16 * rt:16 * rt + 16, 64 * kt:64 * kt + 64]
+            n = [int((blkw == b).sum()) for b in (1, 2, 4, 8)]
+            assert list(tiles[t]) == [rec, byte // 16, n[0] | (n[1] << 16), n[2] | (n[3] << 16)]
+            seen, keys = set(), {0: [], 1: [], 2: [], 3: []}
+            walker = _walk_tile(byte, n)
+            while True:
+                try:
+                    c, m, l, blk, (ca, sa, ma) = next(walker)
+                except StopIteration as e:
+                    end = e.value
+                    break
+                mt = _u16_at(st, blk + ca + sa + 2 * l)
+                row, kg = 16 * rt + (mt & 15), 64 * kt + (mt >> 4)
+                assert (mt >> 10) == 0 and widths[row, kg] == (1 << c)
+                keys[c].append(kg * 16 + row)
+                seen.add((row, kg))
+            for c in range(4):
+                assert all(a < b for a, b in zip(keys[c], keys[c][1:]))     # (kg, row) order
+            assert len(seen) == blkw.size
             rec += sum(n)
-            code += (-(-8 * n[0] // 16) * 16 + 16 * n[1] + 32 * n[2] + 64 * n[3]) // 16
-            # per class: records sorted by (kg, row), each group once
-            base = int(tiles[t][0])
-            seen = set()
-            for c, b in enumerate((1, 2, 4, 8)):
-                m = lay["meta"][base:base + n[c]].astype(np.int64)
-                key = (m >> 4) * 16 + (m & 15)
-                assert np.all(np.diff(key) > 0)
-                for v in m:
-                    row, kg = 16 * rt + (v & 15), v >> 4
-                    assert 64 * kt <= kg < 64 * kt + 64
-                    assert widths[row, kg] == b
-                    seen.add((row, kg))
-                base += n[c]
-            assert len(seen) == rows.size
-        assert list(tiles[T]) == [rec, code, 0, 0] and code == C16
+            byte = end
+        assert list(tiles[T]) == [rec, byte // 16, 0, 0] and byte == 16 * B16
         # reading back gives the quantiser's output in natural order
         q, s, o, w = oracle.unpack(lay)
         q2, s2, o2 = oracle.quantize_matrix(W, widths)
@@ -277,6 +363,7 @@ def pin_layout_invariants():
         rows = r.choice(N, min(N, 5), replace=False)
         qr, sr, orr, wr = oracle.unpack(lay, rows)
         assert np.array_equal(qr, q2[rows]) and np.array_equal(wr, widths[rows])
+
 
 
 # --------------------------------------------------------------------------
@@ -438,18 +525,22 @@ def pin_mean_bits_accounting():
     se = math.sqrt(var / w.size)
     assert abs(mean - 1.79) < 4 * se and abs(mean - 1.82) < 4 * se + 0.03
     assert abs(float((w == 1).mean()) - 0.69) < 0.03
-    # bytes of a layout: codes 8*sum(b) per group plus 4 (scale+offset) + 2 (meta)
+    # bytes of a layout: codes 8*sum(b) per group plus 4 (scale+offset) + 2 (meta),
+    # plus at most 8 + 12 + 14 bytes of padding per class segment of a tile
     lay_w = w[:64]
-    T, R, C16 = oracle.layout_sizes(lay_w)
+    T, R, B16 = oracle.layout_sizes(lay_w)
     code_bytes = 8 * int(lay_w.astype(np.int64).sum())
-    assert code_bytes <= 16 * C16 <= code_bytes + 8 * T
+    assert code_bytes + 6 * R <= 16 * B16 <= code_bytes + 6 * R + 4 * 34 * T
 
 
 def pin_layout_k_tiles():
-    """Tiles are 16 rows x 64 k-groups. N=17, K=64*65 (hand-worked): 2 row-tiles
-    x 2 k-tiles; tile t = rt*2 + kt; tile (0,0) holds rows 0-15 x k-groups 0-63
-    (1024 groups), tile (0,1) rows 0-15 x k-group 64 (16 groups), tile (1,0)
-    row 16 x k-groups 0-63 (64 groups), tile (1,1) row 16 x k-group 64."""
+    """Tiles are 16 rows x 64 k-groups, stored k-tile major. N=17, K=64*65
+    (hand-worked): 2 row-tiles x 2 k-tiles, t = kt*2 + rt. Tile 0 (rt0, kt0):
+    1024 one-bit records = 16 full blocks of 512+256+128 = 896 B; tile 1
+    (rt1, kt0): row 16 x 64 groups = one full block, 896 B; tile 2 (rt0, kt1):
+    15 one-bit records (codes 120 -> 128, so 60 -> 64, meta 30 -> 32 = 224 B)
+    and the 2-bit record of row 3 (16+16+16 = 48 B); tile 3 (rt1, kt1): the
+    8-bit record of row 16 (64+16+16 = 96 B)."""
     N, K = 17, 64 * 65
     assert oracle.tile_grid(N, K) == (2, 2)
     widths = np.ones((N, 65), np.uint8)
@@ -458,27 +549,30 @@ def pin_layout_k_tiles():
     W = (_rng(19).standard_normal((N, K)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
     tiles = lay["tiles"].reshape(-1, 4)
-    assert oracle.layout_sizes(widths)[0] == 4
-    # record bases: 0, 1024, 1040, 1104; counts per class
-    assert [int(t[0]) for t in tiles[:4]] == [0, 1024, 1040, 1104]
-    assert [int(t[2]) for t in tiles[:4]] == [1024, 15 | (1 << 16), 64, 0]
+    assert oracle.layout_sizes(widths) == (4, N * 65, 975)
+    assert [int(t[0]) for t in tiles[:4]] == [0, 1024, 1088, 1104]
+    assert [int(t[1]) for t in tiles[:4]] == [0, 896, 952, 969]
+    assert [int(t[2]) for t in tiles[:4]] == [1024, 64, 15 | (1 << 16), 0]
     assert [int(t[3]) for t in tiles[:4]] == [0, 0, 0, 1 << 16]
-    # code units: 1024 1-bit records = 8192 B; 15 1-bit (120 B, padded 128) + one 2-bit (16 B);
-    # 64 1-bit = 512 B; one 8-bit = 64 B
-    assert [int(t[1]) for t in tiles[:4]] == [0, 512, 512 + 9, 512 + 9 + 32]
-    assert list(tiles[4]) == [1105, 512 + 9 + 32 + 4, 0, 0]
-    # the k-group field is the matrix's k-group; row field is the row in the tile
-    assert int(lay["meta"][1024]) == (0 | (64 << 4))
-    assert int(lay["meta"][1038]) == (15 | (64 << 4))       # last 1-bit record of tile (0,1)
-    assert int(lay["meta"][1039]) == (3 | (64 << 4))        # its 2-bit record (row 3)
-    assert int(lay["meta"][1040]) == (0 | (0 << 4))         # first record of tile (1,0)
-    assert int(lay["meta"][1104]) == (0 | (64 << 4))
+    assert list(tiles[4]) == [1105, 975, 0, 0]
+    st = lay["stream"]
+    # meta holds the row in the tile and the k-group in the tile
+    assert _u16_at(st, 896 * 16 + 512 + 256) == 0                 # tile 1, (row 16, kg 0)
+    assert _u16_at(st, 896 * 16 + 512 + 256 + 10) == 5 << 4       # tile 1, (row 16, kg 5)
+    assert _u16_at(st, 952 * 16 + 128 + 64) == 0                  # tile 2, (row 0, kg 64)
+    assert _u16_at(st, 952 * 16 + 128 + 64 + 28) == 15            # tile 2, (row 15, kg 64)
+    assert _u16_at(st, 952 * 16 + 224 + 32) == 3                  # tile 2, 2-bit record of row 3
+    assert _u16_at(st, 969 * 16 + 64 + 16) == 0                   # tile 3, (row 16, kg 64)
+    s16, o16, q = oracle.quantize_group(W[16, 64 * 64:], 8)
+    assert [int(v) for v in st[969 * 4:969 * 4 + 16]] == list(oracle.pack_group_record(q, 8))
+    assert _u32_at(st, 969 * 16 + 64) == s16 | (o16 << 16)
+
 
 
 ALL_PINS = [pin_layout_k_tiles, 
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd,
-    pin_layout_worked_example, pin_layout_block_chunks, pin_layout_invariants,
+    pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
     pin_mean_bits_accounting,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     lib = C.CDLL(vbq.LIB_PATH)
     for n in header_functions():
         assert hasattr(lib, n), f"{n} declared in vbq.h but not exported"
-    assert vbq.abi_version() == 1
+    assert vbq.abi_version() == 2
     assert vbq.lib.vbq_status_string(3) == b"width not in {1,2,4,8}"
 
 
@@ -41,12 +41,12 @@ def test_pack_query_matches_oracle(shape):
     r = np.random.default_rng(N + K)
     w = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64), p=[0.6, 0.2, 0.15, 0.05])
     s = vbq.pack_query(w)
-    assert (s.n_tiles, s.n_records, s.n_code16) == oracle.layout_sizes(w)
+    assert (s.n_tiles, s.n_records, s.n_bytes16) == oracle.layout_sizes(w)
     lay = oracle.pack((np.random.default_rng(1).standard_normal((N, K)) * 0.02).astype(np.float32), w)
-    tiles = lay["tiles"].reshape(-1, 4)[:-1].astype(np.int64)
-    recs = (tiles[:, 2] & 0xFFFF) + (tiles[:, 2] >> 16) + (tiles[:, 3] & 0xFFFF) + (tiles[:, 3] >> 16)
-    code16 = np.diff(np.append(tiles[:, 1], s.n_code16))
-    assert s.max_tile_records == int(recs.max()) and s.max_tile_code16 == int(code16.max())
+    tiles = lay["tiles"].reshape(-1, 4).astype(np.int64)
+    recs = (tiles[:-1, 2] & 0xFFFF) + (tiles[:-1, 2] >> 16) + (tiles[:-1, 3] & 0xFFFF) + (tiles[:-1, 3] >> 16)
+    bytes16 = np.diff(tiles[:, 1])
+    assert s.max_tile_records == int(recs.max()) and s.max_tile_bytes16 == int(bytes16.max())
     assert s.code_bits == 64 * int(w.astype(np.int64).sum())
     assert list(s.groups_by_width) == [int((w == b).sum()) for b in (1, 2, 4, 8)]
 
@@ -67,7 +67,7 @@ def _fake_matrix(vbq, N=32, K=128, align=256):
     # Descriptor with plausible (never dereferenced) device addresses.
     T = ((N + 15) // 16) * ((K // 64 + 63) // 64)
     base = 0x7F0000000000
-    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, 8, 64, base, base + 4096, base + 8192, base + align * 64)
+    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, 8, base, base + align * 64)
 
 
 def test_compute_calls_reject_bad_arguments_without_a_gpu():
@@ -88,7 +88,7 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     bad.n_tiles = 5
     assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 6
     bad = _fake_matrix(vbq, align=8)
-    bad.codes = 0x7F0000000008
+    bad.stream = 0x7F0000000008
     assert L.vbq_gemv(C.byref(bad), x, 1, None, y, None) == 4
     big = _fake_matrix(vbq, K=64 * 4000)
     assert L.vbq_gemv(C.byref(big), x, 9, None, y, None) == 5      # batch above the maximum
