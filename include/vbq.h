@@ -36,9 +36,9 @@
  *   t = kt * RT + rt covers rows 16rt.. and k-groups 64kt.., with
  *   RT = ceil(N / 16), KT = ceil(K / 4096). Inside a tile the groups are
  *   split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
- *   ordered by (k-group ascending, row ascending), so that a wavefront decodes
- *   groups of a single width and neighbouring lanes share k-groups. Each group
- *   is a "record" with
+ *   ordered by (row ascending, k-group ascending), so that a wavefront decodes
+ *   groups of a single width and neighbouring lanes share rows. Each group is
+ *   a "record" with
  *     codes : 2b u32 words; with h = 16/b, the pair p = (code 2p, code 2p+1),
  *             p < 32, sits in word p/h: code 2p at bit (p%h)*b (LSB first)
  *             and code 2p+1 at bit 16 + (p%h)*b;
@@ -48,8 +48,8 @@
  *   A class segment keeps its records in blocks of 64, 64, 32, 16 records
  *   (b = 1, 2, 4, 8; a full block carries 512, 1024, 1024, 1024 code bytes);
  *   the last block may hold m fewer. A block of m records is, in order:
- *     codes area: b = 1: record l at byte 8l (area rounded up to 16 bytes);
- *                 b >= 2: 16-byte chunk q of record l at byte (q*m + l)*16;
+ *     codes area: record l's 2b words at byte 8b*l, in order (for b = 1
+ *                 the area is rounded up to 16 bytes);
  *     so area   : record l at byte 4l, rounded up to 16 bytes;
  *     meta area : record l at byte 2l, rounded up to 16 bytes;
  *   padding is zero. A tile is its class segments 0..3 in order, and the tiles

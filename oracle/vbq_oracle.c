@@ -35,7 +35,7 @@
  *   stored k-tile major: tile t = kt * RT + rt covers rows 16rt.. and k-groups
  *   64kt.., RT = ceil(N/16), KT = ceil(G/64). Inside a tile the groups are
  *   split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
- *   ordered by (k-group ascending, row ascending). Each group is a "record":
+ *   ordered by (row ascending, k-group ascending). Each group is a "record":
  *     codes: 2b u32 words; with h = 16/b, pair p = (code 2p, code 2p+1), p < 32,
  *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b
  *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
@@ -43,8 +43,8 @@
  *   A class segment holds its records in blocks of 64, 64, 32, 16 records
  *   (b = 1, 2, 4, 8: 1024 code bytes per full block); the last block may be
  *   short (m records). A block of m records is, in order:
- *     codes area: b=1: record l at byte 8l (area rounded up to 16 bytes);
- *                 b>=2: 16-byte chunk q of record l at byte (q*m + l)*16
+ *     codes area: record l's 2b words at byte 8b*l, in order (for b = 1
+ *                 the area is rounded up to 16 bytes)
  *     so area   : record l at byte 4l, rounded up to 16 bytes
  *     meta area : record l at byte 2l, rounded up to 16 bytes
  *   with zero padding. A tile is its class segments 0..3 in order; tiles follow
@@ -230,10 +230,11 @@ static void record_place(int c, int64_t n, int64_t i, int64_t* base, int64_t* m,
   *l = i % br;
 }
 
-/* Byte offset, inside a block of m records, of 16-byte chunk q of record l
- * (b >= 2), or of the 8-byte record l (b == 1, q == 0). */
+/* Byte offset, inside a block, of 16-byte chunk q of record l (b >= 2), or of
+ * the 8-byte record l (b == 1, q == 0): records are contiguous. */
 static int64_t chunk_offset(int c, int64_t m, int64_t l, int q) {
-  return c == 0 ? 8 * l : (q * m + l) * 16;
+  (void)m;
+  return 8 * (int64_t)class_bits(c) * l + 16 * q;
 }
 
 /* Tile geometry: number of row-tiles and k-tiles. */
@@ -303,9 +304,9 @@ int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tile
       int b = class_bits(c);
       int64_t i = 0;
       for (int it = 0; it < ng * nr; ++it) {
-        /* (k-group, row) order; mutation 8 walks (row, k-group) instead */
-        int g = g0 + ((g_mut == 8) ? it % ng : it / nr);
-        int r = r0 + ((g_mut == 8) ? it / ng : it % nr);
+        /* (row, k-group) order; mutation 8 walks (k-group, row) instead */
+        int g = g0 + ((g_mut == 8) ? it / nr : it % ng);
+        int r = r0 + ((g_mut == 8) ? it % nr : it / ng);
         if (width_class(widths[(int64_t)r * G + g]) != c) continue;
         uint16_t s16, o16;
         uint8_t q[64];

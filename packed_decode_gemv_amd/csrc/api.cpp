@@ -90,48 +90,33 @@ int cu_count() {
   return cached[dev];
 }
 
-// Device workspace per (device, stream), two regions:
-//   counters: arrival counters of the row ranges of matrices with K > 4096.
-//             They are zeroed when the region is allocated and every launch
-//             leaves the ones it used at zero again (the last workgroup of a
-//             row range resets its counter), so they are zero at each launch.
-//             Nothing else is ever stored there.
-//   partials: partial rows, written before they are read in every launch.
-// Both only grow; growing waits for the stream and clears the counters.
+// Device workspace per (device, stream): partial rows of matrices with
+// K > 4096, written by the GEMV launch and summed by the launch that follows
+// it on the same stream. It only grows; growing waits for the stream.
 struct Workspace {
   void* base = nullptr;
-  size_t counter_bytes = 0, partial_bytes = 0;
+  size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-hipError_t workspace(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, uint32_t** counters,
-                     float** partials) {
+hipError_t workspace(hipStream_t stream, size_t bytes, float** partials) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, stream}];
-  if (w.counter_bytes < counter_bytes || w.partial_bytes < partial_bytes) {
-    const size_t cb = std::max<size_t>({w.counter_bytes, counter_bytes, 64 * 1024});
-    const size_t pb = std::max<size_t>({w.partial_bytes, partial_bytes, 1 << 20});
+  if (w.bytes < bytes) {
+    const size_t want = std::max<size_t>(bytes, 1 << 20);
     if (w.base) {
       if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
       if ((e = hipFree(w.base)) != hipSuccess) return e;
       w = Workspace();
     }
-    void* base = nullptr;
-    if ((e = hipMalloc(&base, cb + pb)) != hipSuccess) return e;
-    if ((e = hipMemsetAsync(base, 0, cb, stream)) != hipSuccess) {
-      (void)hipFree(base);
-      return e;
-    }
-    w.base = base;
-    w.counter_bytes = cb;
-    w.partial_bytes = pb;
+    if ((e = hipMalloc(&w.base, want)) != hipSuccess) return e;
+    w.bytes = want;
   }
-  *counters = static_cast<uint32_t*>(w.base);
-  *partials = reinterpret_cast<float*>(static_cast<uint8_t*>(w.base) + w.counter_bytes);
+  *partials = static_cast<float*>(w.base);
   return hipSuccess;
 }
 
@@ -233,32 +218,29 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   if (ring < gemv_ring_min_bytes() || gemv_lds_bytes(B, target, ring) > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
   std::vector<int> rpw(count), wpc(count);
   int rpw_max = 1;
-  size_t n_counters = 0, n_partials = 0;
-  std::vector<size_t> c_off(count, 0), p_off(count, 0);
+  size_t n_partials = 0;
+  std::vector<size_t> p_off(count, 0);
   for (int i = 0; i < count; ++i) {
     const int RT = row_tiles(ms[i].n_rows), KT = k_tiles(ms[i].n_cols / kGroup);
     rpw[i] = std::max(1, std::min(RT, target));
     wpc[i] = (RT + rpw[i] - 1) / rpw[i];
     rpw_max = std::max(rpw_max, rpw[i]);
     if (KT > 1) {
-      c_off[i] = n_counters;
-      n_counters += (size_t)wpc[i];
       p_off[i] = n_partials;
       n_partials += ((size_t)KT * B * ms[i].n_rows + 63) / 64 * 64;
     }
   }
   const size_t lds = gemv_lds_bytes(B, rpw_max, ring);
   if (lds > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
-  uint32_t* counters = nullptr;
   float* partials = nullptr;
-  if (n_counters > 0 && workspace(stream, n_counters * 4, n_partials * 4, &counters, &partials) != hipSuccess)
-    return VBQ_ERR_HIP;
+  if (n_partials > 0 && workspace(stream, n_partials * 4, &partials) != hipSuccess) return VBQ_ERR_HIP;
   // Split into launches of at most kMaxMats matrices.
   for (int base = 0; base < count; base += kMaxMats) {
     GemvLaunch L;
     memset(&L, 0, sizeof(L));
     const int nm = std::min(kMaxMats, count - base);
     int wg = 0;
+    int64_t split_outputs = 0;
     for (int i = 0; i < nm; ++i) {
       const vbq_matrix& m = ms[base + i];
       GemvMat& g = L.mats[i];
@@ -276,8 +258,8 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.wg_begin = wg;
       g.stream_bytes = (uint32_t)(m.n_bytes16 * 16);
       if (g.k_tiles > 1) {
-        g.arrivals = counters + c_off[base + i];
         g.part = partials + p_off[base + i];
+        split_outputs += (int64_t)B * m.n_rows;
       }
       wg += g.k_tiles * g.wg_per_col;
     }
@@ -285,6 +267,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     L.rt_per_wg = rpw_max;
     L.ring_bytes = ring;
     hipError_t e = launch_gemv(L, B, resid != nullptr, wg, lds, stream);
+    if (e == hipSuccess) e = launch_splitk_sum(L, B, split_outputs, stream);
     if (e != hipSuccess) return VBQ_ERR_HIP;
   }
   return VBQ_OK;

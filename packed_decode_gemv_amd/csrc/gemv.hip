@@ -362,41 +362,54 @@ struct Smem {
   uint32_t ring_mask;    // ring bytes - 1 (a power of two)
 };
 
-// Decodes one block of class C (m records) at ring offset `boff`.
+// Inclusive sum over the 64 lanes of a wavefront with DPP row shifts and row
+// broadcasts (lanes without a source add zero).
+__device__ inline float wave_incl_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Decodes one block of class C (m records) at ring offset `boff` and adds each
+// record's contribution to its row. Lane L holds 16-byte chunk L % LPR of
+// record L / LPR (8 bytes, the whole record, for 1-bit codes); records run in
+// (row, k-group) order, so rows are sorted along the lanes and each run of
+// equal rows is summed with one wavefront scan: the last lane of a run adds
+// (prefix at the run's end - prefix at the previous run's end) to the row.
 template <int C, int NB>
 __device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t boff, uint32_t m, int rl, int nrow,
                                      int wave, uint32_t lane) {
-  constexpr uint32_t LPR = lanes_per_record(C), BR = block_records(C);
-  if (lane < m * LPR) {
-    uint32_t q = 0, l = lane;
-    if constexpr (LPR > 1) {
-      if (m == BR) {
-        q = lane / BR;
-        l = lane % BR;
-      } else {
-        // lane = q*m + l; (lane + 1/2)/m is at least 1/64 away from an integer
-        q = (uint32_t)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)m));
-        l = lane - q * m;
-      }
-    }
-    constexpr int NW = Geo<C>::NW;
+  constexpr uint32_t LPR = lanes_per_record(C);
+  constexpr int NW = Geo<C>::NW;
+  const bool live = lane < m * LPR;
+  const uint32_t l = lane / LPR, q = lane % LPR;
+  float v[NB];
+  int key = kTile;                            // lanes past the block form their own last run
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) v[nb] = 0.0f;
+  if (live) {
     const uint32_t mask = S.ring_mask;
     uint32_t w[NW];
     if constexpr (C == 0) {
-      const uint2 v = *reinterpret_cast<const uint2*>(S.ring + ((boff + 8u * lane) & mask));
-      w[0] = v.x;
-      w[1] = v.y;
+      const uint2 u = *reinterpret_cast<const uint2*>(S.ring + ((boff + 8u * lane) & mask));
+      w[0] = u.x;
+      w[1] = u.y;
     } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(S.ring + ((boff + 16u * lane) & mask));
-      w[0] = v.x;
-      w[1] = v.y;
-      w[2] = v.z;
-      w[3] = v.w;
+      const uint4 u = *reinterpret_cast<const uint4*>(S.ring + ((boff + 16u * lane) & mask));
+      w[0] = u.x;
+      w[1] = u.y;
+      w[2] = u.z;
+      w[3] = u.w;
     }
     const uint32_t ca = codes_area(C, m);
     const uint32_t so = *reinterpret_cast<const uint32_t*>(S.ring + ((boff + ca + 4u * l) & mask));
     const uint32_t mt = *reinterpret_cast<const uint16_t*>(S.ring + ((boff + ca + so_area(m) + 2u * l) & mask));
-    const int row = mt & 15, kgl = (int)(mt >> 4) & (kTileGroups - 1);   // in range whatever the bytes
+    const int kgl = (int)(mt >> 4) & (kTileGroups - 1);   // in range whatever the bytes
+    key = mt & 15;
     float acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
@@ -406,10 +419,20 @@ __device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t
     const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
     const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float v = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
-      atomicAdd(&S.yw[(wave * NB + nb) * nrow + rl * kTile + row], v);
-    }
+    for (int nb = 0; nb < NB; ++nb) v[nb] = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
+  }
+  // runs of equal rows: a lane ends a run when the next lane's row differs
+  const int next = __builtin_amdgcn_update_dpp(-1, key, 0x130, 0xF, 0xF, false);   // lane + 1 (wave shift)
+  const bool end = key != next;
+  const uint64_t ends = __builtin_amdgcn_ballot_w64(end);
+  const uint64_t below = ends & ((1ull << lane) - 1ull);
+  const int prev = below ? 63 - __builtin_clzll(below) : -1;                      // previous run's end
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float p = wave_incl_sum(v[nb]);
+    const float pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(max(prev, 0) << 2, __builtin_bit_cast(int, p)));
+    if (end && key < kTile)   // one lane per row: no two lanes add to the same place
+      atomicAdd(&S.yw[(wave * NB + nb) * nrow + rl * kTile + key], p - (prev >= 0 ? pp : 0.0f));
   }
 }
 
@@ -565,7 +588,6 @@ __device__ inline uint32_t make_desc(const BlockInfo& b, uint32_t B0, uint32_t n
 template <int NB, int WAVES, bool RESID>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ uint32_t s_last;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps block bookkeeping scalar
@@ -648,7 +670,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   if constexpr (RESID) residual_rows<NB, WAVES>(M, S, r0, nrow, g0, ng, wave, lane);
   lds_barrier();
 
-  // Rows of this workgroup: sum the wavefront slices in a fixed order.
+  // Rows of this workgroup: sum the wavefront slices in a fixed order. With
+  // several k-tiles the rows are partial sums, added up by k_splitk_sum.
   const bool split = M.k_tiles > 1;
   for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
     const int nb = i / nrow, ri = i - nb * nrow;
@@ -663,29 +686,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
         M.y[(size_t)nb * M.n_rows + row] = v;
     }
   }
-  if (!split) return;
-  // Several k-tiles: the last workgroup of this row range to arrive adds the
-  // partial rows of all k-tiles in k-tile order.
-  __syncthreads();                            // partial rows stored by every wavefront
-  if (tid == 0) {
-    __threadfence();                          // release the partial rows device-wide
-    const uint32_t before = atomicAdd(&M.arrivals[cj], 1u);
-    s_last = before == (uint32_t)(M.k_tiles - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();                            // acquire the other workgroups' rows
-  for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
-    const int nb = i / nrow, ri = i - nb * nrow;
-    const int row = r0 + ri;
-    if (row < M.n_rows) {
+}
+
+// y[b][n] = sum over k-tiles of the partial rows, in k-tile order, for every
+// matrix of a launch with K > 4096 (one thread per output).
+__global__ __launch_bounds__(256) void k_splitk_sum(const GemvLaunch L, int nb_rows) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  int64_t base = 0;
+  for (int mi = 0; mi < L.n_mats; ++mi) {
+    const GemvMat& M = L.mats[mi];
+    if (M.k_tiles <= 1) continue;
+    const int64_t n = (int64_t)nb_rows * M.n_rows;
+    if (i >= base && i < base + n) {
+      const int64_t o = i - base;
       float v = 0.f;
-      for (int t = 0; t < M.k_tiles; ++t)
-        v += __builtin_nontemporal_load(&M.part[((size_t)t * NB + nb) * M.n_rows + row]);
-      M.y[(size_t)nb * M.n_rows + row] = v;
+      for (int t = 0; t < M.k_tiles; ++t) v += M.part[(int64_t)t * n + o];
+      M.y[o] = v;
     }
+    base += n;
   }
-  if (tid == 0) atomicExch(&M.arrivals[cj], 0u);   // ready for the next launch
+}
+
+hipError_t launch_splitk_sum(const GemvLaunch& L, int nb, int64_t outputs, hipStream_t s) {
+  if (outputs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)((outputs + 255) / 256)), dim3(256), 0, s, L, nb);
+  return hipGetLastError();
 }
 
 int gemv_waves(int nb) { return nb <= 2 ? 16 : 8; }

@@ -12,7 +12,7 @@
 //   2. k_pack_scan : one workgroup scans the tiles into record and byte bases
 //                    and writes the totals entry (with error flags).
 //   3. k_pack_tiles: per tile, clear its bytes, rank every group inside its
-//                    class in (k-group, row) order, quantise it and write its
+//                    class in (row, k-group) order, quantise it and write its
 //                    codes, scale/offset and meta into its block.
 // The quantiser's arithmetic must give the same bits on every run and match the
 // documented binary32 sequence, so this file is built with -ffp-contract=off and
@@ -194,10 +194,10 @@ __device__ inline void write_record(const float* __restrict__ wg, uint32_t idx, 
   uint8_t* blk = seg + (uint64_t)k * block_bytes(C, BR);
   if constexpr (B == 1) {
     *reinterpret_cast<uint2*>(blk + 8u * l) = make_uint2(words[0], words[1]);
-  } else {
+  } else {   // records are contiguous: chunk q of record l at (l * B/2 + q) * 16
 #pragma unroll
     for (int q = 0; q < B / 2; ++q)
-      *reinterpret_cast<uint4*>(blk + ((uint32_t)q * m + l) * 16u) =
+      *reinterpret_cast<uint4*>(blk + (l * (B / 2) + (uint32_t)q) * 16u) =
           make_uint4(words[4 * q + 0], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
   }
   *reinterpret_cast<uint32_t*>(blk + codes_area(C, m) + 4u * l) = so_v;
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const float* __restrict__ W,
     const int i = base + tid;
     int c = -1, kl = 0, r = 0;
     if (i < total) {
-      kl = i / rows;   // (k-group, row) order
-      r = i - kl * rows;
+      r = i / ng;      // (row, k-group) order
+      kl = i - r * ng;
       c = class_of_width(widths[(size_t)(r0 + r) * G + g0 + kl]);
     }
     uint32_t rank = 0;

@@ -43,7 +43,7 @@ __device__ inline void verify_record(const uint8_t* blk, uint8_t* rq_blk, uint32
   } else {
 #pragma unroll
     for (int q = 0; q < B / 2; ++q) {
-      off[q] = ((uint32_t)q * m + l) * 16u;
+      off[q] = (l * (B / 2) + (uint32_t)q) * 16u;   // records are contiguous
       const uint4 v = *reinterpret_cast<const uint4*>(blk + off[q]);
       w[4 * q + 0] = v.x;
       w[4 * q + 1] = v.y;

@@ -206,8 +206,8 @@ def _u16_at(stream, byte):
 
 def pin_layout_worked_example():
     """N=2, K=128, widths [[1,8],[2,1]] (hand-worked). One tile. Class 0
-    (1-bit) in (k-group,row) order: (kg0,row0), (kg1,row1); class 1: (kg0,row1);
-    class 3: (kg1,row0). Blocks: class 0, m=2: codes 16 B, so 8 -> 16 B,
+    (1-bit) in (row, k-group) order: (row0,kg0), (row1,kg1); class 1: (row1,kg0);
+    class 3: (row0,kg1). Blocks: class 0, m=2: codes 16 B, so 8 -> 16 B,
     meta 4 -> 16 B = 48 B at byte 0; class 1, m=1: 16 + 16 + 16 = 48 B at 48;
     class 3, m=1: 64 + 16 + 16 = 96 B at 96; total 192 B = 12 units.
     meta = row | kg<<4 -> 0, 17 (class 0), 1 (class 1), 16 (class 3)."""
@@ -238,9 +238,9 @@ def pin_layout_worked_example():
 
 
 def pin_layout_block_chunks():
-    """Chunk placement inside a block of m records (b >= 2): chunk q of record l
-    sits at (q*m + l)*16 bytes. One tile with 3 four-bit records (m=3): codes
-    96 B, then so (12 -> 16 B), then meta (6 -> 16 B)."""
+    """Records are contiguous inside a block: 16-byte chunk q of record l
+    (b >= 2) sits at (l*b/2 + q)*16 bytes. One tile with 3 four-bit records
+    (m=3): codes 96 B, then so (12 -> 16 B), then meta (6 -> 16 B)."""
     widths = np.array([[4, 4, 4]], np.uint8)
     W = (_rng(17).standard_normal((1, 192)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
@@ -249,19 +249,21 @@ def pin_layout_block_chunks():
     for kg in range(3):
         s16, o16, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
         words = oracle.pack_group_record(q, 4)
-        assert list(chunks[0 * 3 + kg]) == list(words[0:4])
-        assert list(chunks[1 * 3 + kg]) == list(words[4:8])
+        assert list(chunks[2 * kg + 0]) == list(words[0:4])
+        assert list(chunks[2 * kg + 1]) == list(words[4:8])
         assert _u32_at(lay["stream"], 96 + 4 * kg) == s16 | (o16 << 16)
         assert _u16_at(lay["stream"], 112 + 2 * kg) == kg << 4
 
 
 def pin_layout_block_split():
     """A class segment longer than one block (hand-worked): N=16, K=192, widths
-    8 in k-group 0 (16 records) and at (row 0, kg 1), 1 elsewhere (31 records).
+    8 in k-group 0 and at (row 0, kg 1), 1 elsewhere. In (row, kg) order the
+    17 eight-bit records are (0,0), (0,1), (1,0), (2,0), ..., (15,0) and the 31
+    one-bit records (0,2), (1,1), (1,2), ..., (15,1), (15,2).
     Class 0: one block m=31: codes 248 -> 256, so 124 -> 128, meta 62 -> 64:
-    448 B. Class 3 (capacity 16): a full block (1024 + 64 + 32 = 1120 B) at 448
-    holding kg 0 rows 0..15, then a block of m=1 at 1568 holding (row 0, kg 1):
-    codes at 1568, so at 1632, meta at 1648. Total 1664 B = 104 units."""
+    448 B. Class 3 (capacity 16): a full block at 448 (codes 1024: record l at
+    448 + 64 l; so at 1472; meta at 1536; 1120 B), then a block of m=1 at 1568
+    holding (15,0): codes at 1568, so at 1632, meta at 1648. Total 1664 B."""
     widths = np.ones((16, 3), np.uint8)
     widths[:, 0] = 8
     widths[0, 1] = 8
@@ -270,25 +272,23 @@ def pin_layout_block_split():
     assert oracle.layout_sizes(widths) == (1, 48, 104)
     assert list(lay["tiles"]) == [0, 0, 31, 17 << 16, 48, 104, 0, 0]
     st = lay["stream"]
-    # full block: chunk q of record l (row l, kg 0) at 448 + (16q + l)*16
-    for row in (0, 7, 15):
-        s16, o16, q = oracle.quantize_group(W[row, 0:64], 8)
-        words = oracle.pack_group_record(q, 8)
-        for qq in range(4):
-            at = 448 + (16 * qq + row) * 16
-            assert [int(v) for v in st[at // 4:at // 4 + 4]] == list(words[4 * qq:4 * qq + 4])
-        assert _u32_at(st, 448 + 1024 + 4 * row) == s16 | (o16 << 16)
-        assert _u16_at(st, 448 + 1024 + 64 + 2 * row) == row
-    s16, o16, q = oracle.quantize_group(W[0, 64:128], 8)
+    full = [(0, 0), (0, 1)] + [(r, 0) for r in range(1, 15)]
+    for l in (0, 1, 2, 9, 15):
+        row, kg = full[l]
+        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], 8)
+        at = 448 + 64 * l
+        assert [int(v) for v in st[at // 4:at // 4 + 16]] == list(oracle.pack_group_record(q, 8))
+        assert _u32_at(st, 1472 + 4 * l) == s16 | (o16 << 16)
+        assert _u16_at(st, 1536 + 2 * l) == row | (kg << 4)
+    s16, o16, q = oracle.quantize_group(W[15, 0:64], 8)
     assert [int(v) for v in st[1568 // 4:1568 // 4 + 16]] == list(oracle.pack_group_record(q, 8))
     assert _u32_at(st, 1632) == s16 | (o16 << 16)
-    assert _u16_at(st, 1648) == 16
-    # class 0 block: record l at 8l, so at 256 + 4l, meta at 384 + 2l; first
-    # record is (row 1, kg 1) -- (row 0, kg 1) is 8-bit -- last is (row 15, kg 2)
-    s16, o16, q = oracle.quantize_group(W[1, 64:128], 1)
+    assert _u16_at(st, 1648) == 15
+    # class 0 block: record l at 8l, so at 256 + 4l, meta at 384 + 2l
+    s16, o16, q = oracle.quantize_group(W[0, 128:192], 1)
     assert [int(v) for v in st[0:2]] == list(oracle.pack_group_record(q, 1))
-    assert _u32_at(st, 256) == s16 | (o16 << 16) and _u16_at(st, 384) == 1 | (1 << 4)
-    assert _u16_at(st, 384 + 2 * 30) == 15 | (2 << 4)
+    assert _u32_at(st, 256) == s16 | (o16 << 16) and _u16_at(st, 384) == 0 | (2 << 4)
+    assert _u16_at(st, 386) == 1 | (1 << 4) and _u16_at(st, 384 + 2 * 30) == 15 | (2 << 4)
     assert _u16_at(st, 384 + 2 * 31) == 0 and _u32_at(st, 256 + 4 * 31) == 0   # padding
 
 
@@ -347,10 +347,10 @@ def pin_layout_invariants():
                 mt = _u16_at(st, blk + ca + sa + 2 * l)
                 row, kg = 16 * rt + (mt & 15), 64 * kt + (mt >> 4)
                 assert (mt >> 10) == 0 and widths[row, kg] == (1 << c)
-                keys[c].append(kg * 16 + row)
+                keys[c].append(row * 64 + (kg - 64 * kt))
                 seen.add((row, kg))
             for c in range(4):
-                assert all(a < b for a, b in zip(keys[c], keys[c][1:]))     # (kg, row) order
+                assert all(a < b for a, b in zip(keys[c], keys[c][1:]))     # (row, kg) order
             assert len(seen) == blkw.size
             rec += sum(n)
             byte = end
