@@ -62,8 +62,8 @@ int tiles_per_wg(int64_t total_tiles, int cus) {
 }
 
 // Per-wavefront LDS ring: a power of two of 1 KiB slots, as large as fits next
-// to the x table and the row sums, at most 8 KiB. VBQ_RING_BYTES overrides it
-// (rounded down to a power of two).
+// to the x table and the row sums, at most 16 KiB (the limit of the block
+// descriptors). VBQ_RING_BYTES overrides it (rounded down to a power of two).
 uint32_t pow2_floor(size_t v) {
   uint32_t p = 1;
   while ((size_t)p * 2 <= v && p < (1u << 30)) p *= 2;
@@ -72,10 +72,10 @@ uint32_t pow2_floor(size_t v) {
 
 uint32_t pick_ring_bytes(int nb, int rpw) {
   static const int env = env_int("VBQ_RING_BYTES");
-  if (env > 0) return pow2_floor((size_t)env);
+  if (env > 0) return pow2_floor(std::min<size_t>((size_t)env, 16384));
   const size_t fixed = gemv_lds_bytes(nb, rpw, 0);
   if (fixed >= kLdsLimit) return 0;
-  return pow2_floor(std::min<size_t>((kLdsLimit - fixed) / gemv_waves(nb), 8192));
+  return pow2_floor(std::min<size_t>((kLdsLimit - fixed) / gemv_waves(nb), 16384));
 }
 
 int cu_count() {

@@ -295,12 +295,13 @@ __device__ inline TileLanes make_tile_lanes(const uint4& h, int nt, uint32_t lan
   T.n01 = (int)lane < nt ? h.z : 0u;
   T.n23 = (int)lane < nt ? h.w : 0u;
   const uint32_t nb = tile_blocks(T.n01, T.n23);
-  uint32_t inc = nb;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t v = __shfl_up(inc, d, kWave);
-    if ((int)lane >= d) inc += v;
-  }
+  uint32_t inc = nb;   // inclusive sum over lanes: DPP row shifts, then row broadcasts
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x111, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x112, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x114, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x118, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x142, 0xA, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x143, 0xC, 0xF, false);
   T.pre = inc - nb;
   T.total = __builtin_amdgcn_readlane(inc, nt - 1);
   return T;
@@ -318,11 +319,19 @@ __device__ inline uint32_t sel4(int c, uint32_t a, uint32_t b, uint32_t d, uint3
   return c == 0 ? a : c == 1 ? b : c == 2 ? d : e;
 }
 
-__device__ inline BlockInfo block_info(const TileLanes& T, uint32_t j) {
+// Tile holding block j when the same j is in every lane (wavefront-uniform).
+__device__ inline int tile_of(const TileLanes& T, uint32_t j, uint32_t lane) {
+  return __builtin_popcountll(__builtin_amdgcn_ballot_w64((int)lane < T.nt && T.pre <= j)) - 1;
+}
+
+// Block j of lane (j in [j_lo, j_hi], both wavefront-uniform).
+__device__ inline BlockInfo block_info(const TileLanes& T, uint32_t j, uint32_t j_lo, uint32_t j_hi, uint32_t lane) {
   BlockInfo r;
-  // the tile: the last one whose first block is at or before j
-  int t = 0;
-  for (int tt = 1; tt < T.nt; ++tt) t += j >= (uint32_t)__builtin_amdgcn_readlane(T.pre, tt) ? 1 : 0;
+  // the tile: the last one whose first block is at or before j; only the
+  // tiles between those of j_lo and j_hi can hold it
+  const int t_lo = tile_of(T, j_lo, lane), t_hi = tile_of(T, j_hi, lane);
+  int t = t_lo;
+  for (int tt = t_lo + 1; tt <= t_hi; ++tt) t += j >= (uint32_t)__builtin_amdgcn_readlane(T.pre, tt) ? 1 : 0;
   const uint32_t byte0 = __shfl(T.byte0, t, kWave), n01 = __shfl(T.n01, t, kWave);
   const uint32_t n23 = __shfl(T.n23, t, kWave), pre = __shfl(T.pre, t, kWave);
   const uint32_t n0 = n01 & 0xFFFF, n1 = n01 >> 16, n2 = n23 & 0xFFFF, n3 = n23 >> 16;
@@ -480,7 +489,8 @@ __device__ inline void stage_x(const Smem& S, const XItems<NB, WAVES>& X, int ng
 #pragma unroll
   for (int it = 0; it < XItems<NB, WAVES>::N; ++it) {
     const int i = tid + it * WAVES * kWave;
-    if (it * WAVES * kWave >= NB * ng * 4) break;            // uniform: no item of this round
+    // uniform per wavefront: no item for any lane of it in this round
+    if (it * WAVES * kWave + (tid & ~(kWave - 1)) >= NB * ng * 4) break;
     const int nb = i / (ng * 4), rem = i - nb * ng * 4, kgl = rem >> 2, qt = rem & 3;
     const bool live = i < NB * ng * 4;
     const uint32_t p[8] = {X.lo[it].x, X.lo[it].y, X.lo[it].z, X.lo[it].w,
@@ -568,9 +578,10 @@ __device__ inline void residual_rows(const GemvMat& M, const Smem& S, int r0, in
 
 // Descriptor of one block of a wavefront, built by one lane, read back with
 // v_readlane in the block loop:
-//   bits 0-8 ring offset / 16, 9-10 width class, 11-17 records, 18-23 tile,
-//   24-29 copies that may still be outstanding when the block is decoded,
-//   30-31 copies to issue after it.
+//   bits 0-9 ring offset / 16 (rings up to 16 KiB), 10-11 width class,
+//   12-18 records, 19-24 tile, 25-29 copies that may still be outstanding
+//   when the block is decoded (at most the 16 slots), 30-31 copies to issue
+//   after it.
 // With pieces of 1 KiB at stream offset 1024 p going to ring slot p mod S, and
 // piece p issued as soon as every block before stream offset 1024 (p - S + 1)
 // is decoded, the pieces issued before block j are min(np, pos_j / 1024 + S)
@@ -581,8 +592,8 @@ __device__ inline uint32_t make_desc(const BlockInfo& b, uint32_t B0, uint32_t n
   const uint32_t need = (pos + b.size + 1023u) >> 10;
   const uint32_t before = min(np, (pos >> 10) + slots);
   const uint32_t after = min(np, ((pos + b.size) >> 10) + slots);
-  return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 9) | (b.m << 11) | ((uint32_t)b.t << 18) |
-         ((before - need) << 24) | ((after - before) << 30);
+  return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 10) | (b.m << 12) | ((uint32_t)b.t << 19) |
+         ((before - need) << 25) | ((after - before) << 30);
 }
 
 template <int NB, int WAVES, bool RESID>
@@ -625,21 +636,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   const TileLanes T = make_tile_lanes(h, nrl, lane);
 
   // This wavefront's blocks [b0, b1) and their bytes [B0, B0 + span), in
-  // pieces of 1 KiB; the first `slots` pieces go out at once.
+  // pieces of 1 KiB; the first `slots` pieces go out at once. Lane i looks up
+  // block b0 + i of the first chunk of 64; lane b1 - b0 (if below 64) finds
+  // where the range ends.
   const int b0 = (int)(((int64_t)T.total * wave) / WAVES);
   const int b1 = (int)(((int64_t)T.total * (wave + 1)) / WAVES);
   uint32_t B0 = 0, span = 0, np = 0, issued = 0;
+  BlockInfo first_chunk;
+  first_chunk.byte = first_chunk.size = first_chunk.m = 0;
+  first_chunk.c = first_chunk.t = 0;
   if (b0 < b1) {
-    B0 = __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b0).byte);
-    const uint32_t B1 = b1 < T.total ? __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b1).byte)
-                                     : __builtin_amdgcn_readlane(T.byte0, T.nt);
+    const uint32_t jhi = (uint32_t)min(b1, b0 + kWave - 1);
+    const uint32_t jl = min((uint32_t)b0 + lane, jhi);
+    first_chunk = block_info(T, min(jl, (uint32_t)T.total - 1u), (uint32_t)b0, min(jhi, (uint32_t)T.total - 1u), lane);
+    B0 = __builtin_amdgcn_readfirstlane(first_chunk.byte);
+    uint32_t B1;
+    if (b1 >= T.total) B1 = __builtin_amdgcn_readlane(T.byte0, T.nt);
+    else if (b1 - b0 < kWave) B1 = __builtin_amdgcn_readlane(first_chunk.byte, b1 - b0);
+    else B1 = __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b1, (uint32_t)b1, (uint32_t)b1, lane).byte);
     span = B1 - B0;
     np = (span + 1023u) >> 10;
   }
+  const uint32_t lane16 = 16u * lane;
   auto issue = [&](uint32_t upto) {
     for (; issued < upto; ++issued) {
       const uint32_t piece = issued << 10;
-      if (16u * lane < span - piece) dma16(rsrc, ring_lds + ((issued & (slots - 1u)) << 10), B0 + piece + 16u * lane);
+      const uint32_t lds = ring_lds + ((issued & (slots - 1u)) << 10);
+      if (span - piece >= 1024u) {
+        dma16(rsrc, lds, B0 + piece + lane16);
+      } else if (lane16 < span - piece) {   // the last piece: lanes past the range stay idle
+        dma16(rsrc, lds, B0 + piece + lane16);
+      }
     }
   };
   issue(min(np, slots));
@@ -654,13 +681,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   lds_barrier();                              // x table and zeroed row sums visible
 
   for (int base = b0; base < b1; base += kWave) {
-    const uint32_t jl = min((uint32_t)(base + (int)lane), (uint32_t)(b1 - 1));
-    const uint32_t desc = make_desc(block_info(T, jl), B0, np, slots, S.ring_mask);
+    const uint32_t jhi = (uint32_t)min(b1 - 1, base + kWave - 1);
+    const uint32_t jl = min((uint32_t)(base + (int)lane), jhi);
+    const BlockInfo bi = base == b0 ? first_chunk : block_info(T, jl, (uint32_t)base, jhi, lane);
+    const uint32_t desc = make_desc(bi, B0, np, slots, S.ring_mask);
     const int n_here = min(kWave, b1 - base);
     for (int k = 0; k < n_here; ++k) {
       const uint32_t d = __builtin_amdgcn_readlane(desc, k);
-      wait_vmcnt((int)((d >> 24) & 63u));
-      compute_any<NB>(K, S, (int)((d >> 9) & 3u), (d & 511u) << 4, (d >> 11) & 127u, (int)((d >> 18) & 63u), nrow,
+      wait_vmcnt((int)((d >> 25) & 31u));
+      compute_any<NB>(K, S, (int)((d >> 10) & 3u), (d & 1023u) << 4, (d >> 12) & 127u, (int)((d >> 19) & 63u), nrow,
                       wave, lane);
       // Refill the freed ring slots; the decode's LDS reads are complete first.
       __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
