@@ -13,8 +13,15 @@ One step = one decode token's worth of GEMVs: one batched launch per layer
 HBM when the timed region starts; the stack (2.1 GB) is far larger than the
 on-chip caches, so every launch streams its weights from HBM.
 
-Prints one JSON line (see the fields below). Other workloads are available
-with --workload for reporting; they are not the headline line.
+Prints one JSON line (see the fields below).
+
+Profiling helpers (same file, so every profile is made by committed code):
+  --copy-calibration   after the measurement, run a plain device copy of
+                       known size a few times; its FETCH_SIZE/WRITE_SIZE
+                       readings calibrate the GEMV's counters.
+  --summarize-trace D  (CPU only) summarise a rocprofv3 --kernel-trace run.
+  --summarize-pmc F W  (CPU only) summarise a FETCH_SIZE run F and a
+                       WRITE_SIZE run W into HBM bytes per GEMV launch.
 """
 from __future__ import annotations
 
@@ -117,6 +124,9 @@ class Stack:
 
 
 def time_steps(stack, steps, warmup):
+    """Warm up, then time exactly `steps` steps with HIP events recorded on the
+    stream the kernels are launched on (torch's current stream, which is the
+    stream every launch below is given). Returns ms per step."""
     import torch
     sh = stack.vbq._stream()
     for _ in range(warmup):
@@ -129,11 +139,12 @@ def time_steps(stack, steps, warmup):
         stack.step(sh)
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps   # ms per step
+    return e0.elapsed_time(e1) / steps
 
 
 def time_launches(stack, reps):
-    """Per-launch durations from HIP events around every launch (same stream)."""
+    """Per-launch durations (us) from an event pair around every launch, after
+    the timed region: splits a step into its layer and LM-head launches."""
     import torch
     sh = stack.vbq._stream()
     n = len(stack.plans)
@@ -146,8 +157,134 @@ def time_launches(stack, reps):
             p.launch(sh)
             evs[r][i][1].record()
     torch.cuda.synchronize()
-    d = np.array([[a.elapsed_time(b) * 1e3 for (a, b) in row] for row in evs])   # us
+    d = np.array([[a.elapsed_time(b) * 1e3 for (a, b) in row] for row in evs])
     return d.mean(axis=0)
+
+
+COPY_CAL_BYTES = 1 << 30      # bytes read (and written) by one calibration copy
+COPY_CAL_REPS = 4
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_CAL_BYTES, COPY_CAL_REPS times:
+    the reference whose counter readings convert FETCH_SIZE / WRITE_SIZE into
+    HBM bytes. torch.neg keeps the kernel distinct from the runtime's own
+    copy kernels (it reads and writes each fp32 element once)."""
+    import torch
+    n = COPY_CAL_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(COPY_CAL_REPS):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {COPY_CAL_REPS} x torch.neg over {COPY_CAL_BYTES} B")
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 result summaries (CPU only; read the SQLite result files)
+
+def _db_files(path):
+    import glob
+    if os.path.isfile(path):
+        return [path]
+    return sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+
+
+def _short(name):
+    name = name.split("(")[0]
+    return name.replace("void ", "")
+
+
+def _kernel_rows(path):
+    import sqlite3
+    out = []
+    for f in _db_files(path):
+        c = sqlite3.connect(f)
+        out += c.execute("select name, duration, grid_x / workgroup_x, workgroup_x, lds_size, vgpr_count, "
+                         "sgpr_count from kernels").fetchall()
+    return out
+
+
+def _pmc_rows(path, counter):
+    import sqlite3
+    out = []
+    for f in _db_files(path):
+        c = sqlite3.connect(f)
+        out += c.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
+                         "where counter_name = ? group by dispatch_id, kernel_name", (counter,)).fetchall()
+    return out
+
+
+def summarize_trace(path, command):
+    """Markdown table of dispatch counts and durations per kernel, with the
+    GEMV split by launch shape (workgroups) since layers and the LM head differ."""
+    import collections
+    by = collections.defaultdict(list)
+    for name, dur, wgs, wgsize, lds, vgpr, sgpr in _kernel_rows(path):
+        k = _short(name)
+        key = (k, wgs, wgsize, lds, vgpr, sgpr) if "k_gemv" in k else (k, None, wgsize, lds, vgpr, sgpr)
+        by[key].append(dur / 1e3)
+    lines = ["# rocprofv3 kernel trace", "", "Command (from the repository root on the GPU box):", "",
+             "```", command, "```", "",
+             "| kernel | workgroups | threads/WG | LDS B | VGPR | SGPR | calls | avg us | min us | max us | total us |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        k, wgs, wgsize, lds, vgpr, sgpr = key
+        a = np.array(v)
+        lines.append(f"| `{k}` | {wgs if wgs is not None else 'various'} | {wgsize} | {lds} | {vgpr} | {sgpr} | "
+                     f"{len(a)} | {a.mean():.2f} | {a.min():.2f} | {a.max():.2f} | {a.sum():.1f} |")
+    gem = [d / 1e3 for (n, d, *_) in _kernel_rows(path) if "k_gemv" in n]
+    if gem:
+        lines += ["", f"All `k_gemv` dispatches: {len(gem)} calls, average {np.mean(gem):.2f} us."]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_pmc(fetch_path, write_path):
+    """HBM bytes per k_gemv dispatch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by the reading of the calibration copy, which moves
+    exactly COPY_CAL_BYTES in each direction."""
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        rows = _pmc_rows(path, counter)
+        cal = [v for (_, k, v) in rows if "neg" in k]
+        gem = [v for (_, k, v) in rows if "k_gemv" in k]
+        if not cal or not gem:
+            raise SystemExit(f"{counter}: no calibration copy ({len(cal)}) or k_gemv ({len(gem)}) dispatches")
+        factor = COPY_CAL_BYTES / (float(np.mean(cal)) * 1024.0)
+        res[counter] = dict(kib_per_gemv_dispatch=float(np.mean(gem)), gemv_dispatches=len(gem),
+                            kib_per_copy_dispatch=float(np.mean(cal)), copy_dispatches=len(cal),
+                            copy_factor=factor,
+                            bytes_per_gemv_dispatch=float(np.mean(gem)) * 1024.0 * factor)
+    return res
+
+
+def kernel_source_sha() -> str:
+    """Hash of the GEMV kernel sources; counter readings are valid only for it."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "vbq_common.h"):
+        h.update(open(os.path.join(ROOT, "packed_decode_gemv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_gemv_9b_stack_b1.json")
+
+
+def read_traffic(layers, batch):
+    """HBM bytes per GEMV launch from the committed counter summary, or None
+    when it is missing, for another workload, or for other kernel sources."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_JSON))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if t.get("layers") != layers or t.get("batch") != batch:
+        return None
+    return t.get("bytes_per_launch")
 
 
 def cpu_baseline(stack, budget_s):
@@ -195,6 +332,12 @@ def cpu_baseline(stack, budget_s):
                 seconds=round(spent, 2)), dict(max_rel_l2=worst, matrices=len(checked), tol=2e-3)
 
 
+def workload_name(layers, B):
+    return (f"9B-class stack: {layers} layers x (q 4096x4096, k 1024x4096, v 1024x4096, o 4096x4096, "
+            f"gate 14336x4096, up 14336x4096, down 4096x14336) + LM head 128256x4096, "
+            f"64-weight groups of 1/2/4/8 bits, batch {B}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,10 +348,30 @@ def main(argv=None):
     ap.add_argument("--launch-reps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="RESULTS")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_RESULTS", "WRITE_RESULTS"))
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--out", help="summary file to write")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        text = summarize_trace(args.summarize_trace, args.command)
+        open(args.out, "w").write(text) if args.out else sys.stdout.write(text)
+        return 0
+    if args.summarize_pmc:
+        res = summarize_pmc(*args.summarize_pmc)
+        traffic = res["FETCH_SIZE"]["bytes_per_gemv_dispatch"] + res["WRITE_SIZE"]["bytes_per_gemv_dispatch"]
+        doc = dict(kernel=KERNEL, workload=workload_name(args.layers, args.batch), layers=args.layers,
+                   batch=args.batch, kernel_source_sha=kernel_source_sha(), bytes_per_launch=traffic,
+                   counters=res, command=args.command)
+        out = args.out or TRAFFIC_JSON
+        json.dump(doc, open(out, "w"), indent=1)
+        print(json.dumps(doc, indent=1))
+        return 0
+
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the packed GEMV on a single MI355X and has no "
+        print(f"bench.py measures one GPU: the packed GEMV here runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
@@ -222,32 +385,28 @@ def main(argv=None):
     log(f"  setup {stack.setup_s:.1f} s, packed weights {stack.weight_bytes / 1e9:.3f} GB")
 
     ms = time_steps(stack, args.steps, args.warmup)
+    n_launch = len(stack.plans)
     step_bytes = float(sum(stack.launch_bytes))
     value = step_bytes / (ms * 1e-3) / 1e9
-    log(f"  {ms * 1e3:.1f} us/step, {value:.0f} GB/s")
+    # The dominant kernel is k_gemv: every launch of a step is one. Its average
+    # launch duration is the timed region's event time over its launches.
+    launch_avg_us = ms * 1e3 / n_launch
+    bytes_per_launch = step_bytes / n_launch
+    achieved = bytes_per_launch / (launch_avg_us * 1e-6) / 1e9
+    log(f"  {ms * 1e3:.1f} us/step, {value:.0f} GB/s, {launch_avg_us:.2f} us per launch")
 
     d = time_launches(stack, args.launch_reps)
-    layer_us = d[:-1]
     head_us = float(d[-1])
-    kernel_avg_us = float(d.mean())
-    achieved = (step_bytes / len(d)) / (kernel_avg_us * 1e-6) / 1e9
-    log(f"  per launch: layer {layer_us.mean():.2f} us, lm_head {head_us:.2f} us, avg {kernel_avg_us:.2f} us")
+    layer_us = (ms * 1e3 - head_us) / args.layers
+    log(f"  event pair per launch: layer {d[:-1].mean():.2f} us, lm_head {head_us:.2f} us")
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic_gemv_9b_stack_b1.json")
-    if os.path.exists(tpath):
-        try:
-            t = json.load(open(tpath))
-            if t.get("kernel_source_sha") == kernel_source_sha():
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    if args.copy_calibration:
+        copy_calibration()
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a bounded sample (~{args.cpu_seconds:.0f} s)")
         cpu, parity = cpu_baseline(stack, args.cpu_seconds)
-        cpu["cores"] = 1
         log(f"  oracle {cpu['value']:.4f} GB/s; sampled parity max rel-L2 {parity['max_rel_l2']:.2e}")
 
     out = {
@@ -264,43 +423,33 @@ def main(argv=None):
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": f"9B-class stack: {args.layers} layers x (q,k,v,o 4096-wide; gate,up,down 14336-wide) "
-                        f"+ LM head 128256x4096, mixed 1/2/4/8-bit 64-weight groups, batch {args.batch}",
+            "workload": workload_name(args.layers, args.batch),
             "batch": args.batch,
             "layers": args.layers,
-            "launches_per_step": len(d),
-            "launch": "one vbq_gemv_batched launch per layer (7 projections) + one for the LM head",
+            "launches_per_step": n_launch,
+            "launch": "one vbq_gemv_batched launch per layer (its 7 projections) + one for the LM head",
             "algorithmic_bytes_per_step": step_bytes,
             "packed_bytes_resident": stack.weight_bytes,
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "us_per_layer": round(float(layer_us.mean()), 3),
+        "us_per_layer": round(layer_us, 3),
         "us_lm_head": round(head_us, 3),
-        "us_per_layer_wall": round((ms * 1e3 - head_us) / args.layers, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": KERNEL,
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "avg_launch_us": round(kernel_avg_us, 3),
-            "algorithmic_bytes_per_launch": step_bytes / len(d),
+            "traffic": read_traffic(args.layers, args.batch),
+            "kernel": KERNEL,
+            "avg_launch_us": round(launch_avg_us, 3),
+            "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "cpu_baseline": cpu,
         "parity": parity,
     }
     print(json.dumps(out), flush=True)
     return 0
-
-
-def kernel_source_sha() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in ("gemv.hip", "vbq_common.h"):
-        h.update(open(os.path.join(ROOT, "packed_decode_gemv_amd", "csrc", f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

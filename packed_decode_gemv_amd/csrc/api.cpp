@@ -90,33 +90,50 @@ int cu_count() {
   return cached[dev];
 }
 
-// Device workspace per (device, stream): partial rows of matrices with
-// K > 4096, written by the GEMV launch and summed by the launch that follows
-// it on the same stream. It only grows; growing waits for the stream.
-struct Workspace {
+// Device workspace per (device, stream) for matrices with K > 4096: partial
+// rows, and arrival counters, one per row range. Every counter is zero
+// between calls (the kernel rearms the ones it used), so counter memory is
+// zeroed only when it is created. Both only grow; growing waits for the stream.
+struct Buffer {
   void* base = nullptr;
   size_t bytes = 0;
+};
+struct Workspace {
+  Buffer partials, counters;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-hipError_t workspace(hipStream_t stream, size_t bytes, float** partials) {
+hipError_t grow(Buffer& b, size_t bytes, bool zero, hipStream_t stream) {
+  if (b.bytes >= bytes) return hipSuccess;
+  hipError_t e;
+  const size_t want = std::max<size_t>(bytes, 1 << 16);
+  if (b.base) {
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+    if ((e = hipFree(b.base)) != hipSuccess) return e;
+    b = Buffer();
+  }
+  if ((e = hipMalloc(&b.base, want)) != hipSuccess) return e;
+  if (zero && (e = hipMemsetAsync(b.base, 0, want, stream)) != hipSuccess) {
+    (void)hipFree(b.base);
+    b = Buffer();
+    return e;
+  }
+  b.bytes = want;
+  return hipSuccess;
+}
+
+hipError_t workspace(hipStream_t stream, size_t partial_bytes, size_t counter_bytes, float** partials,
+                     uint32_t** counters) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, stream}];
-  if (w.bytes < bytes) {
-    const size_t want = std::max<size_t>(bytes, 1 << 20);
-    if (w.base) {
-      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-      if ((e = hipFree(w.base)) != hipSuccess) return e;
-      w = Workspace();
-    }
-    if ((e = hipMalloc(&w.base, want)) != hipSuccess) return e;
-    w.bytes = want;
-  }
-  *partials = static_cast<float*>(w.base);
+  if ((e = grow(w.partials, partial_bytes, false, stream)) != hipSuccess) return e;
+  if ((e = grow(w.counters, counter_bytes, true, stream)) != hipSuccess) return e;
+  *partials = static_cast<float*>(w.partials.base);
+  *counters = static_cast<uint32_t*>(w.counters.base);
   return hipSuccess;
 }
 
@@ -218,8 +235,8 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   if (ring < gemv_ring_min_bytes() || gemv_lds_bytes(B, target, ring) > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
   std::vector<int> rpw(count), wpc(count);
   int rpw_max = 1;
-  size_t n_partials = 0;
-  std::vector<size_t> p_off(count, 0);
+  size_t n_partials = 0, n_counters = 0;
+  std::vector<size_t> p_off(count, 0), c_off(count, 0);
   for (int i = 0; i < count; ++i) {
     const int RT = row_tiles(ms[i].n_rows), KT = k_tiles(ms[i].n_cols / kGroup);
     rpw[i] = std::max(1, std::min(RT, target));
@@ -228,19 +245,22 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     if (KT > 1) {
       p_off[i] = n_partials;
       n_partials += ((size_t)KT * B * ms[i].n_rows + 63) / 64 * 64;
+      c_off[i] = n_counters;
+      n_counters += ((size_t)wpc[i] + 63) / 64 * 64;
     }
   }
   const size_t lds = gemv_lds_bytes(B, rpw_max, ring);
   if (lds > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
   float* partials = nullptr;
-  if (n_partials > 0 && workspace(stream, n_partials * 4, &partials) != hipSuccess) return VBQ_ERR_HIP;
+  uint32_t* counters = nullptr;
+  if (n_partials > 0 && workspace(stream, n_partials * 4, n_counters * 4, &partials, &counters) != hipSuccess)
+    return VBQ_ERR_HIP;
   // Split into launches of at most kMaxMats matrices.
   for (int base = 0; base < count; base += kMaxMats) {
     GemvLaunch L;
     memset(&L, 0, sizeof(L));
     const int nm = std::min(kMaxMats, count - base);
     int wg = 0;
-    int64_t split_outputs = 0;
     for (int i = 0; i < nm; ++i) {
       const vbq_matrix& m = ms[base + i];
       GemvMat& g = L.mats[i];
@@ -259,16 +279,14 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.stream_bytes = (uint32_t)(m.n_bytes16 * 16);
       if (g.k_tiles > 1) {
         g.part = partials + p_off[base + i];
-        split_outputs += (int64_t)B * m.n_rows;
+        g.counters = counters + c_off[base + i];
       }
       wg += g.k_tiles * g.wg_per_col;
     }
     L.n_mats = nm;
     L.rt_per_wg = rpw_max;
     L.ring_bytes = ring;
-    hipError_t e = launch_gemv(L, B, resid != nullptr, wg, lds, stream);
-    if (e == hipSuccess) e = launch_splitk_sum(L, B, split_outputs, stream);
-    if (e != hipSuccess) return VBQ_ERR_HIP;
+    if (launch_gemv(L, B, resid != nullptr, wg, lds, stream) != hipSuccess) return VBQ_ERR_HIP;
   }
   return VBQ_OK;
 }

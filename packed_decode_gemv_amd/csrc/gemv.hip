@@ -576,6 +576,56 @@ __device__ inline void residual_rows(const GemvMat& M, const Smem& S, int r0, in
   }
 }
 
+// ---- Split-K finish -------------------------------------------------------------
+// Partial rows of a matrix with several k-tiles meet in a workspace that every
+// XCD of the device sees. Only device-scope read-modify-write atomics touch
+// it: they are performed at the device's coherence point, not in an XCD's own
+// L2, so no L2 write-back or invalidate is needed. A workgroup swaps its
+// partial rows in, waits until those atomics are acknowledged, then counts
+// itself in for its row range; the one that counts last reads every k-tile's
+// partial rows back (again by atomics), adds them in k-tile order and writes
+// y, then rearms the counter for the next call on the stream. Nothing waits
+// on another workgroup, and the sum order is fixed.
+// The swap returns the old value (kept live below), so its completion, which
+// the waits count, means the new value is in place at the coherence point.
+__device__ inline void swap_agent(float* p, float v) {
+  const uint32_t old = __hip_atomic_exchange(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::"v"(old));
+}
+
+__device__ inline float read_agent(float* p) {
+  return __uint_as_float(
+      __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(p), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <int NB, int WAVES>
+__device__ inline void finish_split(const GemvMat& M, const Smem& S, int kt, int cj, int r0, int nrow, int tid) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));   // this lane's swaps are performed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  lds_barrier();                                  // ... and every lane's
+  uint32_t* flag = reinterpret_cast<uint32_t*>(S.cx);
+  if (tid == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(&M.counters[cj], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = before == (uint32_t)(M.k_tiles - 1);
+  }
+  lds_barrier();
+  if (!*flag) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
+    const int nb = i / nrow, ri = i - nb * nrow;
+    const int row = r0 + ri;
+    if (row < M.n_rows) {
+      float v = 0.f;
+      for (int t = 0; t < M.k_tiles; ++t) v += read_agent(&M.part[((size_t)t * NB + nb) * M.n_rows + row]);
+      M.y[(size_t)nb * M.n_rows + row] = v;
+    }
+  }
+  if (tid == 0) __hip_atomic_exchange(&M.counters[cj], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Descriptor of one block of a wavefront, built by one lane, read back with
 // v_readlane in the block loop:
 //   bits 0-9 ring offset / 16 (rings up to 16 KiB), 10-11 width class,
@@ -699,8 +749,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   if constexpr (RESID) residual_rows<NB, WAVES>(M, S, r0, nrow, g0, ng, wave, lane);
   lds_barrier();
 
-  // Rows of this workgroup: sum the wavefront slices in a fixed order. With
-  // several k-tiles the rows are partial sums, added up by k_splitk_sum.
+  // Rows of this workgroup: sum the wavefront slices in a fixed order.
   const bool split = M.k_tiles > 1;
   for (int i = tid; i < NB * nrow; i += WAVES * kWave) {
     const int nb = i / nrow, ri = i - nb * nrow;
@@ -710,36 +759,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) v += S.yw[(w * NB + nb) * nrow + ri];
       if (split)
-        M.part[((size_t)kt * NB + nb) * M.n_rows + row] = v;
+        swap_agent(&M.part[((size_t)kt * NB + nb) * M.n_rows + row], v);
       else
         M.y[(size_t)nb * M.n_rows + row] = v;
     }
   }
-}
-
-// y[b][n] = sum over k-tiles of the partial rows, in k-tile order, for every
-// matrix of a launch with K > 4096 (one thread per output).
-__global__ __launch_bounds__(256) void k_splitk_sum(const GemvLaunch L, int nb_rows) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  int64_t base = 0;
-  for (int mi = 0; mi < L.n_mats; ++mi) {
-    const GemvMat& M = L.mats[mi];
-    if (M.k_tiles <= 1) continue;
-    const int64_t n = (int64_t)nb_rows * M.n_rows;
-    if (i >= base && i < base + n) {
-      const int64_t o = i - base;
-      float v = 0.f;
-      for (int t = 0; t < M.k_tiles; ++t) v += M.part[(int64_t)t * n + o];
-      M.y[o] = v;
-    }
-    base += n;
-  }
-}
-
-hipError_t launch_splitk_sum(const GemvLaunch& L, int nb, int64_t outputs, hipStream_t s) {
-  if (outputs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)((outputs + 255) / 256)), dim3(256), 0, s, L, nb);
-  return hipGetLastError();
+  if (split) finish_split<NB, WAVES>(M, S, kt, cj, r0, nrow, tid);
 }
 
 int gemv_waves(int nb) { return nb <= 2 ? 16 : 8; }

@@ -67,6 +67,7 @@ struct GemvMat {
   const uint16_t* resid;   // [N][K] fp16 or null
   float* y;                // [B][N]
   float* part;             // [KT][B][N] partial rows (k_tiles > 1), else null
+  uint32_t* counters;      // [wg_per_col] arrival counts (k_tiles > 1), zero between calls
   int32_t n_rows;
   int32_t n_groups;        // K / 64
   int32_t row_tiles;       // ceil(N / 16)
@@ -96,7 +97,6 @@ constexpr int kXBytesPerGroup = kXStride * 4 + 5 * 4;
 
 int gemv_waves(int nb);
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s);
-hipError_t launch_splitk_sum(const GemvLaunch& L, int nb, int64_t outputs, hipStream_t s);
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes);
 uint32_t gemv_ring_min_bytes();
 

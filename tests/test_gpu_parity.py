@@ -143,6 +143,48 @@ def test_split_k_calls_in_sequence(vbq):
         assert rel_l2(y, oracle.gemv(q, s, o, x)) <= TOL
 
 
+def test_split_k_repeatable_across_streams(vbq):
+    """The k-tile partial rows are added by the last workgroup of each row
+    range to arrive; its counters must be rearmed after every call, on every
+    stream, and the sum order must not depend on which workgroup came last."""
+    import torch
+    cases = []
+    for (N, K, B) in [(4096, 14336, 1), (1000, 8192, 2)]:
+        W, widths, x = rand_case(N, K, seed=5 * N + K, B=B)
+        pm = vbq.vbq_pack(_t(W), widths)
+        q, s, o = oracle.quantize_matrix(W, widths)
+        cases.append((pm, _t(x, torch.float16), oracle.gemv(q, s, o, x)))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = {0: [], 1: []}
+    for rep in range(6):
+        for ci, (pm, xt, _) in enumerate(cases):
+            st = s1 if (rep + ci) % 2 else s2
+            with torch.cuda.stream(st):
+                outs[ci].append(vbq.vbq_gemv(pm, xt, stream=st))
+    torch.cuda.synchronize()
+    for ci, (_, _, ref) in enumerate(cases):
+        first = outs[ci][0]
+        assert rel_l2(first.cpu().numpy(), ref) <= TOL
+        for o in outs[ci][1:]:
+            assert torch.equal(o, first), "split-K GEMV differs between calls"
+
+
+def test_split_k_batched_mix(vbq):
+    """A batched launch mixing split (K > 4096) and unsplit matrices."""
+    import torch
+    mats, refs = [], []
+    for i, (N, K) in enumerate([(4096, 14336), (512, 4096), (1024, 8192), (64, 4160)]):
+        W, widths, x = rand_case(N, K, seed=90 + i, B=1)
+        q, s, o = oracle.quantize_matrix(W, widths)
+        mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
+        refs.append(oracle.gemv(q, s, o, x))
+    for _ in range(2):
+        ys = vbq.vbq_gemv_batched([pm for pm, _ in mats], [x for _, x in mats])
+        for y, ref in zip(ys, refs):
+            assert rel_l2(y.cpu().numpy(), ref) <= TOL
+
+
 def test_gemv_batch_rows_match_single_rows(vbq):
     import torch
     W, widths, x = rand_case(512, 4096, seed=77, B=4)
@@ -167,7 +209,7 @@ def _cell_inputs(N, K, seed, u_scale=1.0):
     return W, widths, q, s, o, resid, x
 
 
-@pytest.mark.parametrize("shape", [(16, 256), (50, 1024), (33, 4096)])
+@pytest.mark.parametrize("shape", [(16, 256), (50, 1024), (33, 4096), (20, 8192)])
 def test_residual_gemv_and_revocation(vbq, shape):
     import torch
     N, K = shape
