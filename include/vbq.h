@@ -20,9 +20,10 @@
  *   - Ownership: the caller allocates and frees every buffer it passes.
  *     Buffers marked "device" live in GPU memory of the current HIP device;
  *     "host" buffers are ordinary CPU memory. The library itself keeps, per
- *     (device, stream), one device workspace for the partial row sums of
- *     matrices with K > 4096 (allocated on first need, grown when a larger
- *     one is needed, kept until the process ends); nothing else.
+ *     (device, stream), one device workspace for the partial row sums and
+ *     arrival counters of matrices with K > 4096 (allocated on first need,
+ *     grown when a larger one is needed, kept until the process ends);
+ *     nothing else. Growing it waits for the stream.
  *   - Asynchrony: compute calls enqueue work on `stream` and return without
  *     waiting. Argument errors are found before anything is enqueued: the
  *     call returns a non-zero vbq_status and enqueues nothing. A failed kernel
@@ -150,9 +151,12 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
  *   y[b][n] = sum_k x[b][k] * (s*q + o + r[n][k])     (r only if residual != NULL)
  * accumulated in fp32; codes are never expanded in memory.
  * x: device, B x K fp16, 16-byte aligned. B in [1, VBQ_MAX_BATCH]. Each
- *   workgroup stages the 4096 columns of x of one k-tile on-chip; matrices
- *   with K > 4096 are summed over k-tiles through the library's workspace in
- *   a fixed order, so results are identical from run to run.
+ *   workgroup stages the 4096 columns of x of one k-tile on-chip; for
+ *   matrices with K > 4096 the last workgroup of a row range to finish adds
+ *   the k-tiles' partial rows (kept in the library's workspace) in k-tile
+ *   order, so results are identical from run to run. Two calls that use the
+ *   same stream's workspace must not run concurrently (calls on one stream
+ *   never do).
  * residual: device, N x K fp16 row-major (natural order), 16-byte aligned, or
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.

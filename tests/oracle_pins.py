@@ -20,6 +20,7 @@ Sources of truth used here (none of them is the oracle's own formula):
 from __future__ import annotations
 
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -515,8 +516,41 @@ def pin_residual_inside_cell():
 # Accounting (VBQ abstract: 69% of groups at 1 bit, LM head ~1.09 mean bits,
 # 131M model at 1.82 mean bits)
 # --------------------------------------------------------------------------
+def _golden(name):
+    vals = {}
+    for line in open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def pin_abstract_storage_ratios():
+    """The VBQ abstract's storage ratios follow from its mean bits when only
+    code bits are counted (16 / mean bits per parameter), and do not when the
+    fp16 scale and offset per group (+0.5 bit) are counted: so "mean bits" is
+    code bits per weight, the quantity the oracle's accounting reports."""
+    g = _golden("vbq_abstract_figures.txt")
+    codes_only = g["fp16_control_55m_params"] * 16 / (g["model_131m_params"] * g["model_131m_mean_bits"])
+    with_meta = g["fp16_control_55m_params"] * 16 / (g["model_131m_params"] * (g["model_131m_mean_bits"] + 0.5))
+    assert abs(codes_only - g["storage_ratio_131m_vs_55m"]) / g["storage_ratio_131m_vs_55m"] < 0.05
+    assert abs(with_meta - g["storage_ratio_131m_vs_55m"]) / g["storage_ratio_131m_vs_55m"] > 0.2
+    # the 1.46B case implies about 1.76 mean code bits at the printed ratio
+    implied = g["fp16_control_593m_params"] * 16 / (g["model_1p46b_params"] * g["storage_ratio_1p46b_vs_593m"])
+    assert 1.6 < implied < 1.9
+    # the oracle's own accounting: a layout's code bits per weight is the mean width
+    widths = np.array([[1, 1, 2, 8], [4, 1, 1, 2]], np.uint8)
+    lay = oracle.layout_sizes(widths)
+    assert lay[1] == widths.size
+    assert abs(float(widths.mean()) - 2.5) < 1e-12
+
+
 def pin_mean_bits_accounting():
     import synth
+    g = _golden("vbq_abstract_figures.txt")
+    assert abs(synth.mean_bits(synth.MIX_LM_HEAD) - g["lm_head_mean_bits"]) < 0.015
+    assert synth.MIX_DEFAULT[1] == g["share_groups_1bit"]
     assert abs(synth.mean_bits(synth.MIX_DEFAULT) - 1.79) < 1e-12
     assert abs(synth.mean_bits(synth.MIX_LM_HEAD) - 1.10) < 1e-12
     w = synth.widths(0, (0, 0, 0), 768, 12, synth.MIX_DEFAULT)
@@ -569,11 +603,12 @@ def pin_layout_k_tiles():
 
 
 
-ALL_PINS = [pin_layout_k_tiles, 
+ALL_PINS = [
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
-    pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd,
+    pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
     pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
     pin_mean_bits_accounting,
+    pin_abstract_storage_ratios,
 ]
