@@ -76,6 +76,10 @@ def _declare(L):
     L.orc_gemv.restype = None
     L.orc_gemv.argtypes = [P, P, P, C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]
     L.orc_make_cell_residual.restype = None
+    L.orc_f32_to_bf16.restype = C.c_uint16
+    L.orc_f32_to_bf16.argtypes = [C.c_float]
+    L.orc_dequant_bf16.restype = None
+    L.orc_dequant_bf16.argtypes = [P, P, P, C.c_int, C.c_int, P]
     L.orc_make_cell_residual.argtypes = [P, P, C.c_int, C.c_int, P]
     L.orc_requant_verify.restype = None
     L.orc_requant_verify.argtypes = [P, P, P, P, P, C.c_int, C.c_int, P, P]
@@ -243,6 +247,34 @@ def gemv(q, s16, o16, x, resid=None, bf16: bool = False) -> np.ndarray:
     y = np.zeros((B, N), np.float64)
     lib().orc_gemv(_p(q), _p(s16), _p(o16), N, K, _p(x), B, int(bf16), _p(r), _p(y))
     return y
+
+
+def f32_to_bf16(v: float) -> int:
+    return int(lib().orc_f32_to_bf16(float(np.float32(v))))
+
+
+def bf16_to_f64(u16) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns."""
+    u = np.ascontiguousarray(u16, np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def dequant_bf16(q, s16, o16) -> np.ndarray:
+    """bfloat16 bit patterns [N][K] of bf16(f32(s*q) + o)."""
+    q = _c(q, np.uint8)
+    s16 = _c(s16, np.uint16)
+    o16 = _c(o16, np.uint16)
+    N, K = q.shape
+    out = np.zeros((N, K), np.uint16)
+    lib().orc_dequant_bf16(_p(q), _p(s16), _p(o16), N, K, _p(out))
+    return out
+
+
+def gemm_bf16_weights(q, s16, o16, x_bf16) -> np.ndarray:
+    """y [M][N] fp64 = x . Wbf^T with the weights first rounded to bfloat16
+    (dequant_bf16); x bfloat16 bit patterns [M][K]. A library matmul in fp64."""
+    W = bf16_to_f64(dequant_bf16(q, s16, o16))
+    return bf16_to_f64(x_bf16) @ W.T
 
 
 def make_cell_residual(u, s16) -> np.ndarray:

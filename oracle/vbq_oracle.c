@@ -445,6 +445,47 @@ void orc_gemv(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, int N,
 }
 
 /* ------------------------------------------------------------------ */
+/* bfloat16 weights for the batched (matrix-core) product               */
+/* ------------------------------------------------------------------ */
+
+/* Round a binary32 value to bfloat16 (8 significant bits), ties to even:
+ * the two candidates are f with its low 16 bits cleared and the next
+ * bfloat16 away from zero; the nearer wins, a tie goes to the one whose last
+ * kept bit is 0. */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u, up;
+  memcpy(&u, &f, 4);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t lo = u & 0xFFFF0000u;
+  if (lo == u) return (uint16_t)(u >> 16);
+  up = lo + 0x10000u;
+  float flo, fup;
+  memcpy(&flo, &lo, 4);
+  memcpy(&fup, &up, 4);
+  double dlo = fabs((double)f - (double)flo), dup = fabs((double)fup - (double)f);
+  if (dlo < dup) return (uint16_t)(lo >> 16);
+  if (dup < dlo) return (uint16_t)(up >> 16);
+  if (g_mut == 10) return (uint16_t)(up >> 16);         /* mutation: ties away from zero */
+  return (uint16_t)(((lo >> 16) & 1u) ? (up >> 16) : (lo >> 16));
+}
+
+/* Wbf[n][k] = bf16(f32(f32(s) * q) + f32(o)): the product is exact in binary32
+ * (11-bit scale times an 8-bit code), the sum is one binary32 rounding, then
+ * one rounding to bfloat16. This is the weight a bf16 matrix-core product
+ * multiplies; used to separate that rounding from the accumulation order. */
+void orc_dequant_bf16(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, int N, int K, uint16_t* out) {
+  int G = K / ORC_GROUP;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      float s = orc_f16_to_f32(s16[n * G + k / ORC_GROUP]);
+      float o = orc_f16_to_f32(o16[n * G + k / ORC_GROUP]);
+      float sq = s * (float)q[n * K + k];
+      float v = sq + o;
+      out[n * K + k] = orc_f32_to_bf16(v);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* In-cell residual and the re-quantisation check (binary32)            */
 /* ------------------------------------------------------------------ */
 

@@ -431,6 +431,36 @@ def pin_gemm_bf16_exact():
             assert abs(Fraction(float(y[m, n])) - ye[m][n]) <= abs(ye[m][n]) * Fraction(1, 10 ** 14)
 
 
+def pin_bf16_weights():
+    """bfloat16 rounding (8 significant bits, ties to even) on hand-worked
+    values, and the bf16 weights of the batched product."""
+    f = oracle.f32_to_bf16
+    assert f(1.0) == 0x3F80
+    assert f(1.0 + 2.0 ** -8) == 0x3F80            # half an ulp above 1: tie, 1 is even
+    assert f(1.0 + 3 * 2.0 ** -8) == 0x3F82        # tie between 0x3F81 (odd) and 0x3F82
+    assert f(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81
+    assert f(-(1.0 + 2.0 ** -8)) == 0xBF80
+    assert f(255.5) == 0x4380 and f(253.5) == 0x437E and f(255.25) == 0x437F
+    one, half, quarter = 0x3C00, 0x3800, 0x3400     # fp16 1.0, 0.5, 0.25
+    q = np.array([[255, 253, 255, 7] + [0] * 60], np.uint8)
+    s16 = np.array([[one]], np.uint16)
+    assert list(oracle.dequant_bf16(q, s16, np.array([[half]], np.uint16))[0, :4]) == [0x4380, 0x437E, 0x4380, 0x40F0]
+    assert oracle.dequant_bf16(q, s16, np.array([[quarter]], np.uint16))[0, 0] == 0x437F
+    # exact grids stay exact; random weights move by at most half a bf16 ulp
+    r = _rng(31)
+    qi = r.integers(0, 256, (8, 128)).astype(np.uint8)
+    s1 = np.full((8, 2), one, np.uint16)
+    o0 = np.zeros((8, 2), np.uint16)
+    assert np.array_equal(oracle.bf16_to_f64(oracle.dequant_bf16(qi, s1, o0)), qi.astype(np.float64))
+    W = (r.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(16, 4))
+    q, s, o = oracle.quantize_matrix(W, widths)
+    Wd = oracle.bf16_to_f64(oracle.dequant_bf16(q, s, o))
+    Wref = np.repeat(oracle.f64_from_f16(s), 64, 1) * q + np.repeat(oracle.f64_from_f16(o), 64, 1)
+    assert np.all(np.abs(Wd - Wref) <= np.abs(Wref) * 2.0 ** -8 + 1e-30)
+    assert np.any(Wd != Wref)
+
+
 # --------------------------------------------------------------------------
 # In-cell residual: drift bound, revocation, re-quantisation check
 # --------------------------------------------------------------------------
@@ -610,5 +640,5 @@ ALL_PINS = [
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
     pin_mean_bits_accounting,
-    pin_abstract_storage_ratios,
+    pin_abstract_storage_ratios, pin_bf16_weights,
 ]

@@ -26,8 +26,9 @@ MUTATIONS = {
     5: "cell test uses > instead of >=",
     6: "residual added with the wrong sign",
     7: "scale divides by 2^b instead of 2^b - 1",
-    8: "records ordered by (row, k-group)",
+    8: "records ordered by (k-group, row)",
     9: "record halves swapped",
+    10: "bfloat16 rounding breaks ties away from zero",
 }
 
 
