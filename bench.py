@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "packed-weight GEMV: achieved HBM GB/s (% of peak) + µs/layer at batch 1"
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth, decimal GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL = "k_gemv"
 
 
@@ -287,6 +288,167 @@ def read_traffic(layers, batch):
     return t.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------
+# The other workloads: one line each in the JSON's "workloads" list
+
+POOL_BYTES = 600 << 20     # rotate over more than the 256 MB last-level cache
+
+
+def _events_time(fn, calls, warmup=3):
+    """Average us per call of fn(i) over `calls` calls, timed with HIP events
+    on the current stream (the one every call below launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def _pool(pm, extra_bytes=0):
+    n = max(1, POOL_BYTES // max(1, pm.nbytes + extra_bytes))
+    return [pm] + [pm.clone() for _ in range(n - 1)]
+
+
+def _gemv_line(name, us, nbytes, extra=None):
+    d = dict(workload=name, us_per_call=round(us, 3), gb_per_s=round(nbytes / (us * 1e-6) / 1e9, 1),
+             roofline_frac=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), bound="hbm",
+             algorithmic_bytes=nbytes)
+    d.update(extra or {})
+    return d
+
+
+def measure_workloads(stack, calls):
+    """Timed lines for the other workloads (weights and inputs resident in HBM,
+    rotated over a pool larger than the caches where they would fit):
+    131M-class projection, 1.0B-class layer at batch 1 and 4, the 9B-class
+    stack at batch 4, the in-cell update (residual GEMV and the
+    re-quantisation check) and the batched GEMM on MFMA."""
+    import torch
+
+    import synth
+    vbq = stack.vbq
+    dev = torch.device("cuda")
+    out = []
+
+    def packed(cid, layer, pi, proj):
+        key = synth.proj_key(cid, layer, pi)
+        widths = synth.widths(synth.SEED, key, proj.n, proj.k // 64, proj.mix)
+        W = torch.from_numpy(synth.weights(synth.SEED, key, proj.n, proj.k)).to(dev)
+        pm = vbq.vbq_pack(W, widths)
+        return pm, W, key
+
+    def xf16(key, B, K):
+        return torch.from_numpy(synth.x_f16(synth.SEED, key, B, K).view(np.float16)).to(dev)
+
+    # 131M-class projection 768 x 768, batch 1
+    proj = synth.C0.projs[0]
+    pm, _, key = packed(0, 0, 0, proj)
+    x = xf16(key, 1, proj.k)
+    y = torch.empty(1, proj.n, dtype=torch.float32, device=dev)
+    pool = _pool(pm)
+    us = _events_time(lambda i: vbq.vbq_gemv(pool[i % len(pool)], x, out=y), calls)
+    out.append(_gemv_line(f"131M-class projection {proj.n}x{proj.k}, batch 1", us,
+                          algorithmic_bytes(pm.sizes, proj.n, proj.k, 1)))
+
+    # 1.0B-class layer (5 projections in one launch), batch 1 and 4
+    mats = [packed(1, 0, pi, p) for pi, p in enumerate(synth.C1.projs)]
+    layer_bytes = sum(m.nbytes for m, _, _ in mats)
+    n_copies = max(1, POOL_BYTES // layer_bytes)
+    layers = [[m for m, _, _ in mats]] + [[m.clone() for m, _, _ in mats] for _ in range(n_copies - 1)]
+    for B in (1, 4):
+        xs = [xf16(k, B, p.k) for (_, _, k), p in zip(mats, synth.C1.projs)]
+        ys = [torch.empty(B, p.n, dtype=torch.float32, device=dev) for p in synth.C1.projs]
+        plans = [vbq.GemvPlan(L, xs, ys) for L in layers]
+        sh = vbq._stream()
+        us = _events_time(lambda i: plans[i % len(plans)].launch(sh), calls)
+        nb = sum(algorithmic_bytes(m.sizes, p.n, p.k, B) for (m, _, _), p in zip(mats, synth.C1.projs))
+        out.append(_gemv_line(f"1.0B-class layer (qkv 6144x2048, o 2048x2048, up/gate 8192x2048, "
+                              f"down 2048x8192), one launch, batch {B}", us, nb))
+    del mats, layers, plans
+
+    # 9B-class stack at batch 4: the same packed weights, batch-4 activations
+    B = 4
+    plans, nb = [], 0.0
+    for layer in range(stack.layers):
+        pms, xs, ys = [], [], []
+        for pi, p in enumerate(synth.C3.projs):
+            pmx = stack.mats[(layer, pi)][0]
+            pms.append(pmx)
+            xs.append(xf16(synth.proj_key(3, layer, pi), B, p.k))
+            ys.append(torch.empty(B, p.n, dtype=torch.float32, device=dev))
+            nb += algorithmic_bytes(pmx.sizes, p.n, p.k, B)
+        plans.append(vbq.GemvPlan(pms, xs, ys))
+    pmh = stack.mats[(-1, 0)][0]
+    hx = xf16(synth.proj_key(3, -1, 0), B, synth.C3.head.k)
+    plans.append(vbq.GemvPlan([pmh], [hx], [torch.empty(B, synth.C3.head.n, dtype=torch.float32, device=dev)]))
+    nb += algorithmic_bytes(pmh.sizes, synth.C3.head.n, synth.C3.head.k, B)
+    sh = vbq._stream()
+
+    def stack_step(i):
+        for p in plans:
+            p.launch(sh)
+    us = _events_time(stack_step, max(3, calls // 20))
+    out.append(_gemv_line(f"9B-class stack ({stack.layers} layers + LM head), batch 4, one step", us, nb,
+                          {"us_per_layer": round((us) / (stack.layers + 1), 3)}))
+    del plans
+
+    # In-cell update: 4-bit release 14336 x 4096 with an fp16 residual inside
+    # each cell (r = u * scale, u ~ U(-0.49, 0.49)), GEMV and re-quantisation check
+    proj = synth.C2.projs[0]
+    pm, W, key = packed(2, 0, 0, proj)
+    N, K = proj.n, proj.k
+    Wg = W.view(N, K // 64, 64)
+    s_grp = ((Wg.amax(-1) - Wg.amin(-1)) / 15.0).half().float()
+    u = torch.from_numpy(synth.cell_u(synth.SEED, key, N, K)).to(dev)
+    resid = (u.view(N, K // 64, 64) * s_grp.double().unsqueeze(-1)).half().view(N, K)
+    del u, Wg, W
+    x = xf16(key, 1, K)
+    y = torch.empty(1, N, dtype=torch.float32, device=dev)
+    rbytes = resid.numel() * 2
+    n_copies = max(1, POOL_BYTES // (pm.nbytes + rbytes))
+    pool = [(pm, resid)] + [(pm.clone(), resid.clone()) for _ in range(n_copies - 1)]
+    us = _events_time(lambda i: vbq.vbq_gemv(pool[i % len(pool)][0], x, residual=pool[i % len(pool)][1], out=y),
+                      calls)
+    nb = algorithmic_bytes(pm.sizes, N, K, 1, resid=True)
+    out.append(_gemv_line(f"in-cell update {N}x{K} (all 4-bit) + fp16 residual, residual GEMV, batch 1", us, nb))
+    res = torch.empty(3, dtype=torch.int64, device=dev)
+    import ctypes as C
+
+    def verify(i):
+        pmv, rv = pool[i % len(pool)]
+        st = vbq.lib.cell_requant_verify(C.byref(pmv.desc), C.c_void_p(rv.data_ptr()), C.c_void_p(res.data_ptr()),
+                                         None, sh)
+        if st != 0:
+            raise RuntimeError(f"cell_requant_verify status {st}")
+    us = _events_time(verify, calls)
+    counts = res.cpu().numpy().view(np.uint64)
+    nbv = algorithmic_bytes(pm.sizes, N, K, 1, resid=True) - 2 * K - 4 * N + 24
+    out.append(_gemv_line(f"in-cell update {N}x{K}: re-quantisation check (cell_requant_verify)", us, nbv,
+                          {"mismatches": int(counts[0]), "out_of_cell": int(counts[1])}))
+    del pool
+
+    # Batched GEMM on MFMA: M = 256 tokens, K = 4096, N = 14336, default mix
+    proj = synth.C4.projs[0]
+    M = synth.C4.gemm_m
+    pm, _, key = packed(4, 0, 0, proj)
+    xb = torch.from_numpy(synth.x_bf16(synth.SEED, key, M, proj.k).view(np.int16)).to(dev).view(torch.bfloat16)
+    yg = torch.empty(M, proj.n, dtype=torch.float32, device=dev)
+    us = _events_time(lambda i: vbq.vbq_gemm(pm, xb, out=yg), calls)
+    flops = 2.0 * M * proj.n * proj.k
+    tf = flops / (us * 1e-6) / 1e12
+    out.append(dict(workload=f"batched GEMM M={M} K={proj.k} N={proj.n} (bf16 MFMA)", us_per_call=round(us, 3),
+                    tflop_per_s=round(tf, 1), roofline_frac=round(tf / PEAK_BF16_TFLOPS, 4), bound="mfma",
+                    peak_tflop_per_s=PEAK_BF16_TFLOPS, flops=flops))
+    return out
+
+
 def cpu_baseline(stack, budget_s):
     """The CPU oracle (single-threaded, as it stands) on a bounded sample of the
     same workload: whole projections of the first layers, then LM head rows,
@@ -348,6 +510,8 @@ def main(argv=None):
     ap.add_argument("--launch-reps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="only the headline stack")
+    ap.add_argument("--workload-calls", type=int, default=100)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="RESULTS")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_RESULTS", "WRITE_RESULTS"))
@@ -400,6 +564,13 @@ def main(argv=None):
     layer_us = (ms * 1e3 - head_us) / args.layers
     log(f"  event pair per launch: layer {d[:-1].mean():.2f} us, lm_head {head_us:.2f} us")
 
+    workloads = None
+    if not args.no_workloads:
+        log("other workloads")
+        workloads = measure_workloads(stack, args.workload_calls)
+        for w in workloads:
+            log(f"  {w['workload']}: {w['us_per_call']:.2f} us, frac {w['roofline_frac']:.3f}")
+
     if args.copy_calibration:
         copy_calibration()
 
@@ -447,6 +618,7 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
         "parity": parity,
+        "workloads": workloads,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -123,6 +123,13 @@ class PackedMatrix:
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.tiles, self.stream))
 
+    def clone(self) -> "PackedMatrix":
+        """A copy in new device buffers (same layout)."""
+        pm = PackedMatrix(self.N, self.K, self.sizes, device=self.tiles.device)
+        pm.tiles.copy_(self.tiles)
+        pm.stream.copy_(self.stream)
+        return pm
+
     def host_layout(self) -> dict:
         """The layout as numpy arrays (device-to-host copy), in the oracle's format."""
         return dict(tiles=self.tiles.cpu().numpy().view(np.uint32), stream=self.stream.cpu().numpy().view(np.uint32),
