@@ -40,9 +40,9 @@
  *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b
  *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
  *     meta : u16, row in the tile in bits 0-3, k-group in the tile in bits 4-9
- *   A class segment holds its records in blocks of 64, 64, 32, 16 records
- *   (b = 1, 2, 4, 8: 1024 code bytes per full block); the last block may be
- *   short (m records). A block of m records is, in order:
+ *   A class segment holds its records in blocks of 256, 64, 64, 16 records
+ *   (b = 1, 2, 4, 8: 2048, 1024, 2048, 1024 code bytes per full block); the
+ *   last block may be short (m records). A block of m records is, in order:
  *     codes area: record l's 2b words at byte 8b*l, in order (for b = 1
  *                 the area is rounded up to 16 bytes)
  *     so area   : record l at byte 4l, rounded up to 16 bytes
@@ -201,8 +201,9 @@ static int class_bits(int c) { return 1 << c; }
 
 static int64_t up16(int64_t v) { return (v + 15) / 16 * 16; }
 
-/* Records per block of class c: every full block holds 1024 code bytes. */
-static int64_t block_records(int c) { return c == 0 ? 64 : c == 1 ? 64 : c == 2 ? 32 : 16; }
+/* Records per block of class c (full blocks hold 2048, 1024, 2048, 1024 code
+ * bytes for b = 1, 2, 4, 8). */
+static int64_t block_records(int c) { return c == 0 ? 256 : c == 1 ? 64 : c == 2 ? 64 : 16; }
 
 /* Areas of a block of class c holding m records: codes, scale/offset words,
  * meta halfwords, each rounded up to 16 bytes. */

@@ -102,13 +102,16 @@ __device__ inline Consts<C> make_consts() {
   return make_consts_impl<C>(std::make_integer_sequence<int, 10>{});
 }
 
-// Pairs per word and words per lane of class C: a lane holds 8 (b = 1) or 16
-// code bytes.
+// Decode geometry of class C: pairs per word, words of one record (part) a
+// lane decodes at a time and its pairs, records per lane (1-bit: four
+// consecutive records) and lanes per record (8-bit: four quarters).
 template <int C>
 struct Geo {
-  static constexpr int H = 16 >> C;              // pairs per word
-  static constexpr int NW = C == 0 ? 2 : 4;      // words per lane
-  static constexpr int NP = NW * H;              // pairs per lane: 32, 32, 16, 8
+  static constexpr int H = 16 >> C;                              // pairs per word
+  static constexpr int NW = C == 0 ? 2 : C == 2 ? 8 : 4;         // words per record part
+  static constexpr int NP = NW * H;                              // pairs per part: 32, 32, 32, 8
+  static constexpr int RPL = C == 0 ? 4 : 1;                     // records per lane
+  static constexpr int LPR = C == 3 ? 4 : 1;                     // lanes per record
 };
 
 template <int C, int J, int NB>
@@ -383,65 +386,103 @@ __device__ inline float wave_incl_sum(float v) {
   return v;
 }
 
+// Contribution of one record part: s * (sum of decoded pairs * x - bias) +
+// o * sum(x) (the bias and the offset term only on the record's first part).
+template <int C, int NB>
+__device__ inline void record_part(const Consts<C>& k, const Smem& S, const uint32_t* w, uint32_t so, int kgl, int q,
+                                   float (&v)[NB]) {
+  float acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
+  const uint32_t* xk = S.xs + kgl * kXStride + q * (uint32_t)Geo<C>::NP;
+  dot_lane_impl<C, NB>(k, w, xk, kTileGroups * kXStride, acc, std::make_integer_sequence<int, Geo<C>::NP / 4>{});
+  const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
+  const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) v[nb] = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
+}
+
 // Decodes one block of class C (m records) at ring offset `boff` and adds each
-// record's contribution to its row. Lane L holds 16-byte chunk L % LPR of
-// record L / LPR (8 bytes, the whole record, for 1-bit codes); records run in
-// (row, k-group) order, so rows are sorted along the lanes and each run of
-// equal rows is summed with one wavefront scan: the last lane of a run adds
-// (prefix at the run's end - prefix at the previous run's end) to the row.
+// record's contribution to its row. Records run in (row, k-group) order, so
+// rows are sorted along the lanes. Each lane ends with one (row, value) pair:
+// the row of its last record and the sum over its records of that row (a
+// 1-bit lane first adds its other rows straight into the row sums). Runs of
+// equal rows across lanes are then closed with one inclusive wavefront scan P:
+// the last lane of a run adds P to its row and subtracts P from the next
+// run's row, which leaves every row with the sum of its own run.
 template <int C, int NB>
 __device__ inline void compute_block(const Consts<C>& k, const Smem& S, uint32_t boff, uint32_t m, int rl, int nrow,
                                      int wave, uint32_t lane) {
-  constexpr uint32_t LPR = lanes_per_record(C);
-  constexpr int NW = Geo<C>::NW;
-  const bool live = lane < m * LPR;
-  const uint32_t l = lane / LPR, q = lane % LPR;
+  constexpr int LPR = Geo<C>::LPR, NW = Geo<C>::NW;
+  const uint32_t mask = S.ring_mask;
+  const uint32_t ca = codes_area(C, m), sa = so_area(m);
+  float* yw = S.yw + wave * NB * nrow + rl * kTile;
   float v[NB];
   int key = kTile;                            // lanes past the block form their own last run
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) v[nb] = 0.0f;
-  if (live) {
-    const uint32_t mask = S.ring_mask;
-    uint32_t w[NW];
-    if constexpr (C == 0) {
-      const uint2 u = *reinterpret_cast<const uint2*>(S.ring + ((boff + 8u * lane) & mask));
-      w[0] = u.x;
-      w[1] = u.y;
-    } else {
-      const uint4 u = *reinterpret_cast<const uint4*>(S.ring + ((boff + 16u * lane) & mask));
-      w[0] = u.x;
-      w[1] = u.y;
-      w[2] = u.z;
-      w[3] = u.w;
+  if constexpr (C == 0) {
+    if (4u * lane < m) {
+      const uint4 c01 = *reinterpret_cast<const uint4*>(S.ring + ((boff + 32u * lane) & mask));
+      const uint4 c23 = *reinterpret_cast<const uint4*>(S.ring + ((boff + 32u * lane + 16u) & mask));
+      const uint4 so4 = *reinterpret_cast<const uint4*>(S.ring + ((boff + ca + 16u * lane) & mask));
+      const uint2 mt4 = *reinterpret_cast<const uint2*>(S.ring + ((boff + ca + sa + 8u * lane) & mask));
+      const uint32_t mts[4] = {mt4.x & 0xFFFFu, mt4.x >> 16, mt4.y & 0xFFFFu, mt4.y >> 16};
+      const uint32_t sos[4] = {so4.x, so4.y, so4.z, so4.w};
+      const uint32_t ws[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+      const uint32_t n_here = min(4u, m - 4u * lane);
+      const int first = (int)(mts[0] & 15u);
+      key = (int)((n_here == 4u ? mts[3] : n_here == 3u ? mts[2] : n_here == 2u ? mts[1] : mts[0]) & 15u);
+      float head[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) head[nb] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if ((uint32_t)i < n_here) {
+          float r[NB];
+          record_part<0, NB>(k, S, ws + 2 * i, sos[i], (int)(mts[i] >> 4) & (kTileGroups - 1), 0, r);
+          const int row = (int)(mts[i] & 15u);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            if (row == key) v[nb] += r[nb];
+            else if (row == first) head[nb] += r[nb];
+            else atomicAdd(&yw[nb * nrow + row], r[nb]);   // a row wholly inside this lane
+          }
+        }
+      }
+      if (first != key) {   // the lane's first row continues the run of earlier lanes
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) atomicAdd(&yw[nb * nrow + first], head[nb]);
+      }
     }
-    const uint32_t ca = codes_area(C, m);
-    const uint32_t so = *reinterpret_cast<const uint32_t*>(S.ring + ((boff + ca + 4u * l) & mask));
-    const uint32_t mt = *reinterpret_cast<const uint16_t*>(S.ring + ((boff + ca + so_area(m) + 2u * l) & mask));
-    const int kgl = (int)(mt >> 4) & (kTileGroups - 1);   // in range whatever the bytes
-    key = mt & 15;
-    float acc[NB];
+  } else {
+    const uint32_t l = lane / LPR, q = lane % LPR;
+    if (l < m) {
+      uint32_t w[NW];
+      const uint32_t cb = 4u * NW;   // code bytes per lane
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
-    const uint32_t* xk = S.xs + kgl * kXStride + q * (uint32_t)Geo<C>::NP;
-    dot_lane_impl<C, NB>(k, w, xk, kTileGroups * kXStride, acc,
-                         std::make_integer_sequence<int, Geo<C>::NP / 4>{});
-    const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
-    const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) v[nb] = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
+      for (int h = 0; h < NW / 4; ++h) {
+        const uint4 u = *reinterpret_cast<const uint4*>(S.ring + ((boff + cb * lane + 16u * h) & mask));
+        w[4 * h + 0] = u.x;
+        w[4 * h + 1] = u.y;
+        w[4 * h + 2] = u.z;
+        w[4 * h + 3] = u.w;
+      }
+      const uint32_t so = *reinterpret_cast<const uint32_t*>(S.ring + ((boff + ca + 4u * l) & mask));
+      const uint32_t mt = *reinterpret_cast<const uint16_t*>(S.ring + ((boff + ca + sa + 2u * l) & mask));
+      key = (int)(mt & 15u);
+      record_part<C, NB>(k, S, w, so, (int)(mt >> 4) & (kTileGroups - 1), (int)q, v);
+    }
   }
-  // runs of equal rows: a lane ends a run when the next lane's row differs
-  const int next = __builtin_amdgcn_update_dpp(-1, key, 0x130, 0xF, 0xF, false);   // lane + 1 (wave shift)
-  const bool end = key != next;
-  const uint64_t ends = __builtin_amdgcn_ballot_w64(end);
-  const uint64_t below = ends & ((1ull << lane) - 1ull);
-  const int prev = below ? 63 - __builtin_clzll(below) : -1;                      // previous run's end
+  const int next = __builtin_amdgcn_update_dpp(kTile, key, 0x130, 0xF, 0xF, false);   // lane + 1 (wave shift)
+  const bool end = key != next && key < kTile;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float p = wave_incl_sum(v[nb]);
-    const float pp = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(max(prev, 0) << 2, __builtin_bit_cast(int, p)));
-    if (end && key < kTile)   // one lane per row: no two lanes add to the same place
-      atomicAdd(&S.yw[(wave * NB + nb) * nrow + rl * kTile + key], p - (prev >= 0 ? pp : 0.0f));
+    if (end) {   // distinct rows: the end lanes of different runs never share an address
+      atomicAdd(&yw[nb * nrow + key], p);
+      if (next < kTile) atomicAdd(&yw[nb * nrow + next], -p);
+    }
   }
 }
 
@@ -629,21 +670,22 @@ __device__ inline void finish_split(const GemvMat& M, const Smem& S, int kt, int
 // Descriptor of one block of a wavefront, built by one lane, read back with
 // v_readlane in the block loop:
 //   bits 0-9 ring offset / 16 (rings up to 16 KiB), 10-11 width class,
-//   12-18 records, 19-24 tile, 25-29 copies that may still be outstanding
-//   when the block is decoded (at most the 16 slots), 30-31 copies to issue
-//   after it.
+//   12-19 records - 1, 20-24 copies that may still be outstanding when the
+//   block is decoded (fewer than the 16 slots), 25-27 copies to issue after it.
+// The block's tile goes in a second per-lane word.
 // With pieces of 1 KiB at stream offset 1024 p going to ring slot p mod S, and
 // piece p issued as soon as every block before stream offset 1024 (p - S + 1)
 // is decoded, the pieces issued before block j are min(np, pos_j / 1024 + S)
 // and the block needs the first ceil((pos_j + size_j) / 1024): both closed
-// forms of the block's stream position.
+// forms of the block's stream position. A block spans at most five pieces
+// (3584 bytes at an odd start), so S >= 5 keeps all of them in the ring.
 __device__ inline uint32_t make_desc(const BlockInfo& b, uint32_t B0, uint32_t np, uint32_t slots, uint32_t ring_mask) {
   const uint32_t pos = b.byte - B0;
   const uint32_t need = (pos + b.size + 1023u) >> 10;
   const uint32_t before = min(np, (pos >> 10) + slots);
   const uint32_t after = min(np, ((pos + b.size) >> 10) + slots);
-  return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 10) | (b.m << 12) | ((uint32_t)b.t << 19) |
-         ((before - need) << 25) | ((after - before) << 30);
+  return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 10) | ((b.m - 1u) << 12) | ((before - need) << 20) |
+         ((after - before) << 25);
 }
 
 template <int NB, int WAVES, bool RESID>
@@ -738,12 +780,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
     const int n_here = min(kWave, b1 - base);
     for (int k = 0; k < n_here; ++k) {
       const uint32_t d = __builtin_amdgcn_readlane(desc, k);
-      wait_vmcnt((int)((d >> 25) & 31u));
-      compute_any<NB>(K, S, (int)((d >> 10) & 3u), (d & 1023u) << 4, (d >> 12) & 127u, (int)((d >> 19) & 63u), nrow,
-                      wave, lane);
+      const int t = __builtin_amdgcn_readlane(bi.t, k);
+      wait_vmcnt((int)((d >> 20) & 31u));
+      compute_any<NB>(K, S, (int)((d >> 10) & 3u), (d & 1023u) << 4, ((d >> 12) & 255u) + 1u, t, nrow, wave, lane);
       // Refill the freed ring slots; the decode's LDS reads are complete first.
       __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
-      issue(issued + (d >> 30));
+      issue(issued + ((d >> 25) & 7u));
     }
   }
   if constexpr (RESID) residual_rows<NB, WAVES>(M, S, r0, nrow, g0, ng, wave, lane);
@@ -767,7 +809,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   if (split) finish_split<NB, WAVES>(M, S, kt, cj, r0, nrow, tid);
 }
 
-int gemv_waves(int nb) { return nb <= 2 ? 16 : 8; }
+int gemv_waves(int nb) { return nb <= 1 ? 16 : 8; }
 
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes) {
   const int waves = gemv_waves(nb);
@@ -779,9 +821,9 @@ size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes) {
   return b;
 }
 
-// The ring is a power of two of at least four 1 KiB slots: a block spans at
-// most three pieces (1408 bytes at an odd start).
-uint32_t gemv_ring_min_bytes() { return 4u * 1024u; }
+// The ring is a power of two of at least five 1 KiB slots: a block spans at
+// most five pieces (3584 bytes at an odd start).
+uint32_t gemv_ring_min_bytes() { return 8u * 1024u; }
 
 template <int NB, int WAVES, bool RESID>
 static hipError_t launch_one(const GemvLaunch& L, int n_wg, size_t lds, hipStream_t s) {
@@ -799,8 +841,8 @@ static hipError_t launch_one(const GemvLaunch& L, int n_wg, size_t lds, hipStrea
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s) {
 #define VBQ_CASE(N)                                                                                  \
   case N:                                                                                            \
-    return resid ? launch_one<N, (N <= 2 ? 16 : 8), true>(L, n_wg, lds, s)                           \
-                 : launch_one<N, (N <= 2 ? 16 : 8), false>(L, n_wg, lds, s);
+    return resid ? launch_one<N, (N <= 1 ? 16 : 8), true>(L, n_wg, lds, s)                           \
+                 : launch_one<N, (N <= 1 ? 16 : 8), false>(L, n_wg, lds, s);
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)

@@ -29,11 +29,11 @@ __host__ __device__ inline int class_of_width(int b) {
 }
 
 // ---- Block geometry of the byte stream ------------------------------------
-// Records per block of width class c: a full block of width 2, 4 or 8 carries
-// 1024 code bytes (one 16-byte piece per lane), width 1 carries 512.
-__host__ __device__ constexpr uint32_t block_records(int c) { return c < 2 ? 64u : c == 2 ? 32u : 16u; }
-// Lanes that share one record when a block is decoded (16 code bytes each).
-__host__ __device__ constexpr uint32_t lanes_per_record(int c) { return c < 2 ? 1u : c == 2 ? 2u : 4u; }
+// Records per block of width class c. A wavefront decodes one block at a time,
+// lane L taking the code bytes [L * cb, (L + 1) * cb) of the block with
+// cb = 32, 16, 32, 16 for c = 0..3: four 1-bit records, one 2-bit record, one
+// 4-bit record, or a quarter of an 8-bit record.
+__host__ __device__ constexpr uint32_t block_records(int c) { return c == 0 ? 256u : c == 3 ? 16u : 64u; }
 __host__ __device__ constexpr uint32_t up16(uint32_t v) { return (v + 15u) & ~15u; }
 __host__ __device__ constexpr uint32_t codes_area(int c, uint32_t m) { return c == 0 ? up16(8u * m) : (8u << c) * m; }
 __host__ __device__ constexpr uint32_t so_area(uint32_t m) { return up16(4u * m); }

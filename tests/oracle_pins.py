@@ -293,7 +293,48 @@ def pin_layout_block_split():
     assert _u16_at(st, 384 + 2 * 31) == 0 and _u32_at(st, 256 + 4 * 31) == 0   # padding
 
 
-CAP = (64, 64, 32, 16)        # records per block of each width class
+def pin_layout_big_blocks():
+    """Block capacities (hand-worked): N=16, K=64*20, widths 4 at (row 0,
+    kg 0..3) and 1 elsewhere: 316 one-bit records, 4 four-bit records, one
+    tile. In (row, kg) order the one-bit records are (0,4..19) then
+    (r, 0..19) for r = 1..15, so record i >= 16 is (1 + (i-16)//20, (i-16)%20).
+    Class 0, capacity 256: block 0 full (codes 2048, so 1024, meta 512 =
+    3584 B: record l at 8l, so at 2048+4l, meta at 3072+2l); block 1 holds
+    m=60 at 3584 (codes 480, so 240, meta 120 -> 128: record l at 3584+8l,
+    so at 4064+4l, meta at 4304+2l). Class 2 at 4432: codes 4*32 = 128, so
+    16, meta 16 (record l at 4432+32l, so at 4560+4l, meta at 4576+2l).
+    Total 4592 B = 287 units."""
+    N, K = 16, 64 * 20
+    widths = np.ones((N, 20), np.uint8)
+    widths[0, 0:4] = 4
+    W = (_rng(23).standard_normal((N, K)) * 0.02).astype(np.float32)
+    lay = oracle.pack(W, widths)
+    assert oracle.layout_sizes(widths) == (1, 320, 287)
+    assert list(lay["tiles"]) == [0, 0, 316, 4, 320, 287, 0, 0]
+    st = lay["stream"]
+
+    def one_bit(i):
+        return (0, 4 + i) if i < 16 else (1 + (i - 16) // 20, (i - 16) % 20)
+
+    for i, (code_at, so_at, meta_at) in ((0, (0, 2048, 3072)), (15, (120, 2108, 3102)),
+                                         (16, (128, 2112, 3104)), (255, (2040, 3068, 3582)),
+                                         (256, (3584, 4064, 4304)), (315, (4056, 4300, 4422))):
+        row, kg = one_bit(i)
+        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], 1)
+        assert [int(v) for v in st[code_at // 4:code_at // 4 + 2]] == list(oracle.pack_group_record(q, 1))
+        assert _u32_at(st, so_at) == s16 | (o16 << 16)
+        assert _u16_at(st, meta_at) == row | (kg << 4)
+    assert one_bit(255) == (12, 19) and one_bit(256) == (13, 0) and one_bit(315) == (15, 19)
+    assert _u16_at(st, 4424) == 0 and _u32_at(st, 4428) == 0          # meta padding of block 1
+    for kg in range(4):
+        s16, o16, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
+        at = 4432 + 32 * kg
+        assert [int(v) for v in st[at // 4:at // 4 + 8]] == list(oracle.pack_group_record(q, 4))
+        assert _u32_at(st, 4560 + 4 * kg) == s16 | (o16 << 16)
+        assert _u16_at(st, 4576 + 2 * kg) == kg << 4
+
+
+CAP = (256, 64, 64, 16)       # records per block of each width class
 
 
 def _areas(c, m):
@@ -600,8 +641,9 @@ def pin_mean_bits_accounting():
 def pin_layout_k_tiles():
     """Tiles are 16 rows x 64 k-groups, stored k-tile major. N=17, K=64*65
     (hand-worked): 2 row-tiles x 2 k-tiles, t = kt*2 + rt. Tile 0 (rt0, kt0):
-    1024 one-bit records = 16 full blocks of 512+256+128 = 896 B; tile 1
-    (rt1, kt0): row 16 x 64 groups = one full block, 896 B; tile 2 (rt0, kt1):
+    1024 one-bit records = 4 full blocks of 2048+1024+512 = 3584 B (896
+    units); tile 1 (rt1, kt0): row 16 x 64 groups = one block of m=64,
+    512+256+128 = 896 B; tile 2 (rt0, kt1):
     15 one-bit records (codes 120 -> 128, so 60 -> 64, meta 30 -> 32 = 224 B)
     and the 2-bit record of row 3 (16+16+16 = 48 B); tile 3 (rt1, kt1): the
     8-bit record of row 16 (64+16+16 = 96 B)."""
@@ -640,5 +682,5 @@ ALL_PINS = [
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
     pin_mean_bits_accounting,
-    pin_abstract_storage_ratios, pin_bf16_weights,
+    pin_abstract_storage_ratios, pin_bf16_weights, pin_layout_big_blocks,
 ]
