@@ -145,7 +145,6 @@ __device__ inline void dot_lane_impl(const Consts<C>& k, const uint32_t* w, cons
 }
 
 // ---- Synchronisation helpers ---------------------------------------------------
-#define VBQ_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // Waits until at most n vector-memory instructions of this wavefront are
 // outstanding (n is wavefront-uniform, clamped to [0, 63]). Loads complete in
@@ -241,38 +240,6 @@ __device__ inline void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// ---- Buffer-to-LDS copies -------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (base, no stride, size in bytes): loads past `bytes`
-// return zeros instead of touching memory.
-__device__ inline u32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
-  r.z = __builtin_amdgcn_readfirstlane(bytes);
-  r.w = 0x00020000u;
-  return r;
-}
-
-__device__ inline uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
-}
-
-// Buffer-to-LDS copy: the active lane l reads 16 bytes at byte offset voff of
-// the buffer and writes them to LDS address lds + 16 l. It is written as
-// assembly so that the compiler does not treat it as a pending LDS store: it
-// would otherwise wait for every copy in flight before any LDS read.
-// Completion is tracked by the explicit load-count waits instead. The
-// instruction has no register result, so nothing is left pending in registers.
-__device__ inline void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
 }
 
 // ---- Workgroup tile list -------------------------------------------------------
