@@ -12,7 +12,8 @@
 // compared byte for byte.
 //
 // The decision is integer-valued, so the binary32 operation sequence is fixed
-// (built with -ffp-contract=off; correctly rounded division):
+// (built with -ffp-contract=off; the quotient is the correctly rounded one,
+// see rint_quotient):
 //   deq = f32(s*q) + o;  v = deq + r;  q' = clamp(rint((v - o) / s), 0, L)
 //   out of cell: |r| >= 0.5*s  (or r != 0 when s == 0).
 #include "vbq_common.h"
@@ -27,95 +28,133 @@ __global__ void k_verify_init(uint64_t* result) {
   }
 }
 
-// Checks record l of a block of class C holding m records (block at `blk`).
-template <int C>
-__device__ inline void verify_record(const uint8_t* blk, uint8_t* rq_blk, uint32_t m, uint32_t l, int r0, int g0,
-                                     int K, const uint16_t* __restrict__ resid, uint32_t& mism, uint32_t& ooc,
-                                     uint64_t& first) {
+// rint(fl(a / s)) for finite s > 0, with fl the correctly rounded binary32
+// quotient, from the estimate t = a * rcp(s): t is within |t| * 2^-22 of a / s
+// and fl(a / s) within |a / s| * 2^-24 of it, so when t is farther than
+// |t| * 2^-20 (plus a tiny absolute slack) from the nearest half-integer, a / s
+// and fl(a / s) lie on the same side of it as t and all three round to the
+// same integer. `exact` is cleared otherwise (never for residuals inside
+// their cell); the caller then redoes the quotient correctly rounded.
+__device__ inline float rint_quotient_fast(float a, float s, bool& exact) {
+  const float t = a * __builtin_amdgcn_rcpf(s);
+  const float h = floorf(t) + 0.5f;
+  exact = exact && fabsf(t - h) > fabsf(t) * 0x1p-20f + 0x1p-40f;
+  return rintf(t);
+}
+
+// One quarter of a record: 16 consecutive weights (codes 16q .. 16q + 15).
+// The pair layout puts them in pairs 8q .. 8q + 7, i.e. in words
+// [8q / H, (8q + 7) / H] of the record (H = 16 / b pairs per word): loaded as
+// one 16-byte read starting at word 8q / H (reading past the record stays in
+// its block, whose scale/offset and meta areas follow the codes).
+struct Quarter {
+  uint4 w;         // words from 8q / H on
+  uint32_t so;     // scale | offset << 16
+  uint32_t meta;   // row | k-group << 4
+  uint32_t wbyte;  // byte offset of w in the stream
+  int c;           // width class, -1 if no record
+};
+
+// Re-quantises the 16 weights of a quarter: counts into lm / lo, smallest
+// failing index into lf, re-quantised code words into nw. EXACT selects the
+// correctly rounded quotient; otherwise the fast one, clearing `exact` when a
+// quotient falls inside the margin.
+template <int C, bool EXACT>
+__device__ inline void quarter_pass(const uint32_t (&w)[4], const uint4 (&rv)[2], float s, float o, int q,
+                                    uint64_t lin0, uint32_t& lm, uint32_t& lo, uint64_t& lf, uint32_t (&nw)[4],
+                                    bool& exact) {
   constexpr int B = 1 << C, H = 16 / B, L = (1 << B) - 1;
-  uint32_t w[2 * B];
-  uint32_t off[B > 1 ? B / 2 : 1];
-  if constexpr (B == 1) {
-    off[0] = 8u * l;
-    const uint2 v = *reinterpret_cast<const uint2*>(blk + off[0]);
-    w[0] = v.x;
-    w[1] = v.y;
-  } else {
-#pragma unroll
-    for (int q = 0; q < B / 2; ++q) {
-      off[q] = (l * (B / 2) + (uint32_t)q) * 16u;   // records are contiguous
-      const uint4 v = *reinterpret_cast<const uint4*>(blk + off[q]);
-      w[4 * q + 0] = v.x;
-      w[4 * q + 1] = v.y;
-      w[4 * q + 2] = v.z;
-      w[4 * q + 3] = v.w;
-    }
-  }
-  const uint32_t sov = *reinterpret_cast<const uint32_t*>(blk + codes_area(C, m) + 4u * l);
-  const uint32_t mt = *reinterpret_cast<const uint16_t*>(blk + codes_area(C, m) + so_area(m) + 2u * l);
-  const int row = r0 + (int)(mt & 15), kg = g0 + (int)(mt >> 4);
-  const float s = __half2float(__ushort_as_half((unsigned short)(sov & 0xFFFF)));
-  const float o = __half2float(__ushort_as_half((unsigned short)(sov >> 16)));
+  const int p0 = 8 * q, wbase = p0 / H;
   const float half_s = __fmul_rn(0.5f, s);
-  const uint64_t lin0 = (uint64_t)row * K + (uint64_t)kg * kGroup;
-  const uint4* rp = reinterpret_cast<const uint4*>(resid + lin0);
-  uint32_t nw[2 * B];
+  lm = lo = 0;
+  lf = ~0ull;
 #pragma unroll
-  for (int i = 0; i < 2 * B; ++i) nw[i] = 0;
+  for (int i = 0; i < 4; ++i) nw[i] = 0;
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    const uint4 rv = rp[ch];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * ch + e;                     // natural index inside the group
-      const int pr = j >> 1, odd = j & 1;           // pair (code 2p, code 2p+1)
-      const int wi = pr / H, sh = 16 * odd + (pr % H) * B;
-      const uint32_t q = (w[wi] >> sh) & (uint32_t)L;
-      const uint32_t rw = (e >> 1) == 0 ? rv.x : (e >> 1) == 1 ? rv.y : (e >> 1) == 2 ? rv.z : rv.w;
-      const unsigned short rb = (unsigned short)((e & 1) ? (rw >> 16) : (rw & 0xFFFF));
-      const float r = __half2float(__ushort_as_half(rb));
-      const float deq = __fadd_rn(__fmul_rn(s, (float)q), o);
-      const float v = __fadd_rn(deq, r);
-      uint32_t qp = 0;
-      if (s != 0.0f) {
-        float t = rintf(__fdiv_rn(__fsub_rn(v, o), s));
-        t = t < 0.0f ? 0.0f : t;
-        t = t > (float)L ? (float)L : t;
-        qp = (uint32_t)t;
-      }
-      const bool bad_code = qp != q;
-      const bool bad_cell = (s > 0.0f) ? (fabsf(r) >= half_s) : (r != 0.0f);
-      mism += bad_code;
-      ooc += bad_cell;
-      if ((bad_code || bad_cell) && lin0 + j < first) first = lin0 + j;
-      nw[wi] |= qp << sh;
+  for (int j = 0; j < 16; ++j) {
+    const int pr = p0 + j / 2, odd = j & 1;
+    const int wi = pr / H - wbase, sh = 16 * odd + (pr % H) * B;
+    const uint32_t code = (w[wi] >> sh) & (uint32_t)L;
+    const uint4& rr = rv[j / 8];
+    const uint32_t rw = ((j / 2) & 3) == 0 ? rr.x : ((j / 2) & 3) == 1 ? rr.y : ((j / 2) & 3) == 2 ? rr.z : rr.w;
+    const float r = __half2float(__ushort_as_half((unsigned short)(odd ? (rw >> 16) : (rw & 0xFFFF))));
+    const float deq = __fadd_rn(__fmul_rn(s, (float)code), o);
+    const float a = __fsub_rn(__fadd_rn(deq, r), o);
+    uint32_t qp = 0;
+    if (s != 0.0f) {
+      float t = EXACT ? rintf(__fdiv_rn(a, s)) : rint_quotient_fast(a, s, exact);
+      t = t < 0.0f ? 0.0f : t;
+      t = t > (float)L ? (float)L : t;
+      qp = (uint32_t)t;
     }
-  }
-  if (rq_blk) {
-    if constexpr (B == 1) {
-      *reinterpret_cast<uint2*>(rq_blk + off[0]) = make_uint2(nw[0], nw[1]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < B / 2; ++q)
-        *reinterpret_cast<uint4*>(rq_blk + off[q]) = make_uint4(nw[4 * q], nw[4 * q + 1], nw[4 * q + 2], nw[4 * q + 3]);
-    }
+    const bool bad_code = qp != code;
+    const bool bad_cell = (s > 0.0f) ? (fabsf(r) >= half_s) : (r != 0.0f);
+    lm += bad_code;
+    lo += bad_cell;
+    if ((bad_code || bad_cell) && lin0 + j < lf) lf = lin0 + j;
+    nw[wi] |= qp << sh;
   }
 }
 
-// Record i of class segment C (n records) at `seg`.
+// The rare quarter with a quotient inside the margin: redone with correctly
+// rounded divisions, out of line (arguments and results by value, so that
+// nothing has to live in memory) to keep its registers off the common path.
+struct QuarterResult {
+  uint32_t lm, lo;
+  uint64_t lf;
+  uint4 nw;
+};
+
 template <int C>
-__device__ inline void verify_seg_record(const uint8_t* seg, uint8_t* rq_seg, uint32_t n, uint32_t i, int r0, int g0,
-                                         int K, const uint16_t* resid, uint32_t& mism, uint32_t& ooc,
-                                         uint64_t& first) {
-  constexpr uint32_t BR = block_records(C);
-  const uint32_t k = i / BR, l = i - k * BR, m = min(BR, n - k * BR);
-  const uint64_t bo = (uint64_t)k * block_bytes(C, BR);
-  verify_record<C>(seg + bo, rq_seg ? rq_seg + bo : nullptr, m, l, r0, g0, K, resid, mism, ooc, first);
+__device__ __attribute__((noinline)) QuarterResult quarter_exact(uint4 w4, uint4 r0v, uint4 r1v, float s, float o,
+                                                                 int q, uint64_t lin0) {
+  const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+  const uint4 rv[2] = {r0v, r1v};
+  QuarterResult res;
+  uint32_t nw[4];
+  bool exact = true;
+  quarter_pass<C, true>(w, rv, s, o, q, lin0, res.lm, res.lo, res.lf, nw, exact);
+  res.nw = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+  return res;
 }
 
-__global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ tiles, const uint8_t* __restrict__ stream,
-                                                int G, int RT, const uint16_t* __restrict__ resid,
-                                                uint64_t* result, uint8_t* requant) {
+template <int C>
+__device__ inline void check_quarter(const Quarter& Qr, int q, int r0, int g0, int K, const uint4 (&rv)[2],
+                                     uint32_t& mism, uint32_t& ooc, uint64_t& first, uint32_t (&nw)[4]) {
+  const uint32_t w[4] = {Qr.w.x, Qr.w.y, Qr.w.z, Qr.w.w};
+  const int row = r0 + (int)(Qr.meta & 15), kg = g0 + (int)(Qr.meta >> 4);
+  const float s = __half2float(__ushort_as_half((unsigned short)(Qr.so & 0xFFFF)));
+  const float o = __half2float(__ushort_as_half((unsigned short)(Qr.so >> 16)));
+  const uint64_t lin0 = (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * (uint32_t)q;
+  uint32_t lm, lo;
+  uint64_t lf;
+  bool exact = true;
+  quarter_pass<C, false>(w, rv, s, o, q, lin0, lm, lo, lf, nw, exact);
+  if (!exact) {
+    const QuarterResult e = quarter_exact<C>(Qr.w, rv[0], rv[1], s, o, q, lin0);
+    lm = e.lm;
+    lo = e.lo;
+    lf = e.lf;
+    nw[0] = e.nw.x;
+    nw[1] = e.nw.y;
+    nw[2] = e.nw.z;
+    nw[3] = e.nw.w;
+  }
+  mism += lm;
+  ooc += lo;
+  first = lf < first ? lf : first;
+}
+
+// One workgroup per tile, four lanes per record (a quarter each), up to four
+// records per lane group. All loads of a phase are issued together: the
+// records' codes, scale/offset and meta, then the residuals the meta points
+// at.
+constexpr int kVerifyThreads = 1024;
+
+__global__ __launch_bounds__(kVerifyThreads) void k_verify(const uint32_t* __restrict__ tiles,
+                                                           const uint8_t* __restrict__ stream, int G, int RT,
+                                                           const uint16_t* __restrict__ resid, uint64_t* result,
+                                                           uint8_t* requant) {
   __shared__ uint32_t s_mism, s_ooc;
   __shared__ unsigned long long s_first;
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -130,33 +169,81 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
   const uint64_t tb = (uint64_t)tiles[4 * t + 1] * 16;
   const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
   const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
-  const uint64_t sb[4] = {0, seg_bytes(0, n[0]), seg_bytes(0, n[0]) + seg_bytes(1, n[1]),
-                          seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2])};
-  const uint64_t size = sb[3] + seg_bytes(3, n[3]);
+  const uint32_t sb[4] = {0, (uint32_t)seg_bytes(0, n[0]), (uint32_t)(seg_bytes(0, n[0]) + seg_bytes(1, n[1])),
+                          (uint32_t)(seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2]))};
+  const uint32_t size = sb[3] + (uint32_t)seg_bytes(3, n[3]);
   const uint8_t* tbytes = stream + tb;
   uint8_t* rbytes = requant ? requant + tb : nullptr;
   // Copy the tile (scales, offsets, meta, padding); codes are rewritten below.
   if (rbytes)
-    for (uint64_t i = tid; i < size / 16; i += blockDim.x)
+    for (uint32_t i = tid; i < size / 16; i += kVerifyThreads)
       reinterpret_cast<uint4*>(rbytes)[i] = reinterpret_cast<const uint4*>(tbytes)[i];
   __syncthreads();
   const uint32_t total = n[0] + n[1] + n[2] + n[3];
+  const int q = tid & 3;
   uint32_t mism = 0, ooc = 0;
   uint64_t first = ~0ull;
-  for (uint32_t i = tid; i < total; i += blockDim.x) {
-    int c = 0;
-    uint32_t idx = i;
-    while (c < 3 && idx >= n[c]) {
-      idx -= n[c];
-      ++c;
+  constexpr int kPer = kTile * kTileGroups * 4 / kVerifyThreads;   // quarters per thread: 4
+  constexpr int kBatch = 2;                                         // quarters loaded together
+#pragma unroll
+  for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+    Quarter Q[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = (uint32_t)(tid >> 2) + (uint32_t)(b0 + u) * (kVerifyThreads / 4);
+      Q[u].c = -1;
+      Q[u].wbyte = 0;
+      if (i < total) {
+        int c = 0;
+        uint32_t idx = i;
+        while (c < 3 && idx >= n[c]) {
+          idx -= n[c];
+          ++c;
+        }
+        const uint32_t br = block_records(c), k = idx / br, l = idx - k * br, m = min(br, n[c] - k * br);
+        const uint32_t blk = sb[c] + k * (uint32_t)block_bytes(c, br);
+        const uint32_t H = 16u >> c;
+        Q[u].c = c;
+        Q[u].wbyte = blk + (8u << c) * l + 4u * ((8u * (uint32_t)q) / H);
+        Q[u].so = *reinterpret_cast<const uint32_t*>(tbytes + blk + codes_area(c, m) + 4u * l);
+        Q[u].meta = *reinterpret_cast<const uint16_t*>(tbytes + blk + codes_area(c, m) + so_area(m) + 2u * l);
+        // 4-byte aligned; a 16-byte read from here stays inside the block
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(tbytes + Q[u].wbyte);
+        Q[u].w = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+      }
     }
-    const uint8_t* seg = tbytes + sb[c];
-    uint8_t* rseg = rbytes ? rbytes + sb[c] : nullptr;
-    switch (c) {
-      case 0: verify_seg_record<0>(seg, rseg, n[0], idx, r0, g0, K, resid, mism, ooc, first); break;
-      case 1: verify_seg_record<1>(seg, rseg, n[1], idx, r0, g0, K, resid, mism, ooc, first); break;
-      case 2: verify_seg_record<2>(seg, rseg, n[2], idx, r0, g0, K, resid, mism, ooc, first); break;
-      default: verify_seg_record<3>(seg, rseg, n[3], idx, r0, g0, K, resid, mism, ooc, first); break;
+    uint4 R[kBatch][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      R[u][0] = R[u][1] = make_uint4(0, 0, 0, 0);
+      if (Q[u].c >= 0) {
+        const int row = r0 + (int)(Q[u].meta & 15), kg = g0 + (int)(Q[u].meta >> 4);
+        const uint4* rp =
+            reinterpret_cast<const uint4*>(resid + (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * q);
+        R[u][0] = rp[0];
+        R[u][1] = rp[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = Q[u].c;
+      uint32_t nw[4];
+      if (c == 0) check_quarter<0>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
+      else if (c == 1) check_quarter<1>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
+      else if (c == 2) check_quarter<2>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
+      else if (c == 3) check_quarter<3>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
+      if (c < 0) continue;
+      // 1-bit: the two quarters of one code word combine their bits
+      if (c == 0) nw[0] |= __shfl_xor(nw[0], 1, kWave);
+      if (rbytes) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(rbytes + Q[u].wbyte);
+        if (c == 0) {
+          if ((q & 1) == 0) dst[0] = nw[0];
+        } else {
+          const int nword = c == 1 ? 1 : c == 2 ? 2 : 4;
+          for (int i = 0; i < nword; ++i) dst[i] = nw[i];
+        }
+      }
     }
   }
   if (mism) atomicAdd(&s_mism, mism);
@@ -173,7 +260,7 @@ __global__ __launch_bounds__(256) void k_verify(const uint32_t* __restrict__ til
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
-  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(256), 0, s, m.tiles,
+  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(kVerifyThreads), 0, s, m.tiles,
                      reinterpret_cast<const uint8_t*>(m.stream), m.n_cols / kGroup, row_tiles(m.n_rows), resid,
                      result, reinterpret_cast<uint8_t*>(requant));
   return hipGetLastError();

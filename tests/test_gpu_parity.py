@@ -255,6 +255,31 @@ def test_requant_verify_small(vbq):
     assert np.array_equal(q_rq, ref[3])
 
 
+def test_requant_verify_near_half_cells(vbq):
+    """Residuals within a hair of half a cell on every weight, all widths: the
+    re-quantised code is decided right at a half-integer quotient, where the
+    binary32 rounding of the division matters; counts, first index and the
+    re-quantised codes must still equal the oracle's."""
+    import torch
+    r = np.random.default_rng(44)
+    N, K = 48, 1024
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    hair = r.choice(np.array([0.0, 2.0 ** -14, 2.0 ** -12, 2.0 ** -10, 2.0 ** -8]), size=(N, K))
+    u = np.where(r.random((N, K)) < 0.5, -1.0, 1.0) * (0.5 + np.where(r.random((N, K)) < 0.5, -hair, hair))
+    resid = oracle.make_cell_residual(u, s)
+    pm = vbq.vbq_pack(_t(W), widths)
+    ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    assert (mism, ooc, first) == ref[:3]
+    assert ref[0] > 0 and ref[1] > 0
+    lay_rq = pm.host_layout()
+    lay_rq["stream"] = rq.cpu().numpy().view(np.uint32)
+    q_rq, _, _, _ = oracle.unpack(lay_rq)
+    assert np.array_equal(q_rq, ref[3])
+
+
 def test_requant_verify_mixed_widths(vbq):
     import torch
     N, K = 48, 2048
