@@ -143,6 +143,58 @@ def time_steps(stack, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def capture(fn, n):
+    """A HIP graph of n calls fn(0) .. fn(n-1), captured on a stream of our
+    own (fn takes the current stream itself). The calls run once eagerly on
+    that stream first, so that nothing allocates during capture (the
+    library's split-K workspace is per stream)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            fn(i)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n):
+            fn(i)
+    return g
+
+
+def time_graph(g, reps, warmup=2):
+    """us per replay of graph g, HIP events around exactly `reps` replays."""
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def time_steps_graph(stack, steps, warmup):
+    """One step (all launches) captured as a HIP graph, warmed up, then exactly
+    `steps` replays timed with HIP events. Returns (ms per step, graph). The
+    replayed outputs are checked bit for bit against an eager step."""
+    import torch
+    vbq = stack.vbq
+    stack.step(vbq._stream())   # eager: allocates the workspace before capture
+    torch.cuda.synchronize()
+    eager = [y.clone() for (_, _, y) in list(stack.mats.values())[:8]]
+    g = capture(lambda i: stack.step(vbq._stream()), 1)
+    us = time_graph(g, steps, warmup)
+    for (_, _, y), ref in zip(list(stack.mats.values())[:8], eager):
+        if not torch.equal(y, ref):
+            raise RuntimeError("graph replay differs from the eager step")
+    return us / 1e3, g
+
+
 def time_launches(stack, reps):
     """Per-launch durations (us) from an event pair around every launch, after
     the timed region: splits a step into its layer and LM-head launches."""
@@ -294,21 +346,15 @@ def read_traffic(layers, batch):
 POOL_BYTES = 600 << 20     # rotate over more than the 256 MB last-level cache
 
 
-def _events_time(fn, calls, warmup=3):
-    """Average us per call of fn(i) over `calls` calls, timed with HIP events
-    on the current stream (the one every call below launches on)."""
-    import torch
+def _events_time(fn, calls, warmup=3, reps=3):
+    """Average us per call of fn(i): after an eager warm-up, `calls` calls are
+    captured into one HIP graph and replayed `reps` times between HIP events
+    (so the time is the device's, not the host launch path's). fn takes the
+    current stream itself."""
     for i in range(warmup):
         fn(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(calls):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / calls
+    g = capture(fn, calls)
+    return time_graph(g, reps) / calls
 
 
 def _pool(pm, extra_bytes=0):
@@ -366,8 +412,7 @@ def measure_workloads(stack, calls):
         xs = [xf16(k, B, p.k) for (_, _, k), p in zip(mats, synth.C1.projs)]
         ys = [torch.empty(B, p.n, dtype=torch.float32, device=dev) for p in synth.C1.projs]
         plans = [vbq.GemvPlan(L, xs, ys) for L in layers]
-        sh = vbq._stream()
-        us = _events_time(lambda i: plans[i % len(plans)].launch(sh), calls)
+        us = _events_time(lambda i: plans[i % len(plans)].launch(vbq._stream()), calls)
         nb = sum(algorithmic_bytes(m.sizes, p.n, p.k, B) for (m, _, _), p in zip(mats, synth.C1.projs))
         out.append(_gemv_line(f"1.0B-class layer (qkv 6144x2048, o 2048x2048, up/gate 8192x2048, "
                               f"down 2048x8192), one launch, batch {B}", us, nb))
@@ -389,12 +434,12 @@ def measure_workloads(stack, calls):
     hx = xf16(synth.proj_key(3, -1, 0), B, synth.C3.head.k)
     plans.append(vbq.GemvPlan([pmh], [hx], [torch.empty(B, synth.C3.head.n, dtype=torch.float32, device=dev)]))
     nb += algorithmic_bytes(pmh.sizes, synth.C3.head.n, synth.C3.head.k, B)
-    sh = vbq._stream()
 
     def stack_step(i):
+        sh = vbq._stream()
         for p in plans:
             p.launch(sh)
-    us = _events_time(stack_step, max(3, calls // 20))
+    us = _events_time(stack_step, 1, reps=max(3, calls // 20))
     out.append(_gemv_line(f"9B-class stack ({stack.layers} layers + LM head), batch 4, one step", us, nb,
                           {"us_per_layer": round((us) / (stack.layers + 1), 3)}))
     del plans
@@ -424,7 +469,7 @@ def measure_workloads(stack, calls):
     def verify(i):
         pmv, rv = pool[i % len(pool)]
         st = vbq.lib.cell_requant_verify(C.byref(pmv.desc), C.c_void_p(rv.data_ptr()), C.c_void_p(res.data_ptr()),
-                                         None, sh)
+                                         None, vbq._stream())
         if st != 0:
             raise RuntimeError(f"cell_requant_verify status {st}")
     us = _events_time(verify, calls)
@@ -548,7 +593,9 @@ def main(argv=None):
     stack.check_packed()
     log(f"  setup {stack.setup_s:.1f} s, packed weights {stack.weight_bytes / 1e9:.3f} GB")
 
-    ms = time_steps(stack, args.steps, args.warmup)
+    ms_eager = time_steps(stack, args.steps, args.warmup)
+    ms, _ = time_steps_graph(stack, args.steps, args.warmup)
+    log(f"  eager launches {ms_eager * 1e3:.1f} us/step, graph replay {ms * 1e3:.1f} us/step")
     n_launch = len(stack.plans)
     step_bytes = float(sum(stack.launch_bytes))
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -588,6 +635,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_eager_launches": round(ms_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -598,7 +646,8 @@ def main(argv=None):
             "batch": args.batch,
             "layers": args.layers,
             "launches_per_step": n_launch,
-            "launch": "one vbq_gemv_batched launch per layer (its 7 projections) + one for the LM head",
+            "launch": "one vbq_gemv_batched launch per layer (its 7 projections) + one for the LM head; "
+                      "a step's launches replayed as one HIP graph",
             "algorithmic_bytes_per_step": step_bytes,
             "packed_bytes_resident": stack.weight_bytes,
         },

@@ -23,7 +23,9 @@
  *     (device, stream), one device workspace for the partial row sums and
  *     arrival counters of matrices with K > 4096 (allocated on first need,
  *     grown when a larger one is needed, kept until the process ends);
- *     nothing else. Growing it waits for the stream.
+ *     nothing else. Growing it waits for the stream. Calls captured into a
+ *     HIP graph must not need a new or larger workspace: make the same calls
+ *     once on the capturing stream before capture.
  *   - Asynchrony: compute calls enqueue work on `stream` and return without
  *     waiting. Argument errors are found before anything is enqueued: the
  *     call returns a non-zero vbq_status and enqueues nothing. A failed kernel

@@ -185,6 +185,44 @@ def test_split_k_batched_mix(vbq):
             assert rel_l2(y.cpu().numpy(), ref) <= TOL
 
 
+def test_graph_replays_match_eager(vbq):
+    """Launches captured in a HIP graph (as the benchmark replays a decode
+    step) give the eager results on every replay, with other eager work and
+    synchronisations in between; split-K counters are rearmed by the kernel
+    itself, so no replay depends on the previous one."""
+    import torch
+    mats = []
+    for i, (N, K) in enumerate([(4096, 14336), (1024, 4096), (2048, 8192)]):
+        W, widths, x = rand_case(N, K, seed=200 + i, B=1)
+        mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
+    pms, xs = [pm for pm, _ in mats], [x for _, x in mats]
+    ys = [torch.empty(1, pm.N, dtype=torch.float32, device="cuda") for pm in pms]
+    plan = vbq.GemvPlan(pms, xs, ys)
+    plan.launch(vbq._stream())
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    other_W, other_w, other_x = rand_case(300, 4480, seed=210, B=2)
+    other = vbq.vbq_pack(_t(other_W), other_w)
+    ox = _t(other_x, torch.float16)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):   # the workspace is per stream: warm up the capturing one
+        plan.launch(vbq._stream())
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan.launch(vbq._stream())
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, r in zip(ys, ref):
+            assert torch.equal(y, r), f"replay {rep} differs from the eager launch"
+        vbq.vbq_gemv(other, ox)   # eager work with split-K between replays
+        torch.cuda.synchronize()
+
+
 def test_gemv_batch_rows_match_single_rows(vbq):
     import torch
     W, widths, x = rand_case(512, 4096, seed=77, B=4)
