@@ -51,31 +51,34 @@ int env_int(const char* name) {
   return e ? std::max(0, atoi(e)) : 0;
 }
 
-// Tiles per workgroup: the launch's tiles spread over one workgroup per CU
-// (the rings fill most of the LDS), at most 16 per workgroup.
+// Tiles per workgroup: the launch's tiles spread over the workgroups that are
+// resident at once (gemv_wgs_per_cu per CU), at most 16 per workgroup.
 // VBQ_TILES_PER_WG overrides the target (tuning knob).
-int tiles_per_wg(int64_t total_tiles, int cus) {
+int tiles_per_wg(int64_t total_tiles, int slots) {
   static const int env = env_int("VBQ_TILES_PER_WG");
   if (env > 0) return std::min(env, kMaxWgTiles - 1);
-  const int64_t t = (total_tiles + cus - 1) / cus;
+  const int64_t t = (total_tiles + slots - 1) / slots;
   return (int)std::max<int64_t>(1, std::min<int64_t>(16, t));
 }
 
 // Per-wavefront LDS ring: a power of two of 1 KiB slots, as large as fits next
-// to the x table and the row sums, at most 16 KiB (the limit of the block
-// descriptors). VBQ_RING_BYTES overrides it (rounded down to a power of two).
+// to the x table and the row sums in a workgroup's share of the LDS, at most
+// 16 KiB (the limit of the block descriptors). VBQ_RING_BYTES overrides it
+// (rounded down to a power of two).
 uint32_t pow2_floor(size_t v) {
   uint32_t p = 1;
   while ((size_t)p * 2 <= v && p < (1u << 30)) p *= 2;
   return v ? p : 0;
 }
 
+size_t wg_lds_budget(int nb) { return kLdsLimit / gemv_wgs_per_cu(nb) / 256 * 256; }
+
 uint32_t pick_ring_bytes(int nb, int rpw) {
   static const int env = env_int("VBQ_RING_BYTES");
   if (env > 0) return pow2_floor(std::min<size_t>((size_t)env, 16384));
-  const size_t fixed = gemv_lds_bytes(nb, rpw, 0);
-  if (fixed >= kLdsLimit) return 0;
-  return pow2_floor(std::min<size_t>((kLdsLimit - fixed) / gemv_waves(nb), 16384));
+  const size_t fixed = gemv_lds_bytes(nb, rpw, 0), budget = wg_lds_budget(nb);
+  if (fixed >= budget) return 0;
+  return pow2_floor(std::min<size_t>((budget - fixed) / gemv_waves(nb), 16384));
 }
 
 int cu_count() {
@@ -229,7 +232,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
   // Row-tiles per workgroup, then the largest ring that fits; with a large
   // batch the row sums may have to shrink to leave room for a ring.
-  int target = tiles_per_wg(total_tiles, cu_count());
+  int target = tiles_per_wg(total_tiles, cu_count() * gemv_wgs_per_cu(B));
   uint32_t ring = pick_ring_bytes(B, target);
   while (ring < gemv_ring_min_bytes() && target > 1) ring = pick_ring_bytes(B, --target);
   if (ring < gemv_ring_min_bytes() || gemv_lds_bytes(B, target, ring) > kLdsLimit) return VBQ_ERR_UNSUPPORTED;
@@ -260,10 +263,17 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     GemvLaunch L;
     memset(&L, 0, sizeof(L));
     const int nm = std::min(kMaxMats, count - base);
+    // Matrices with several k-tiles take the first workgroups: those start
+    // first, so their cross-workgroup finish overlaps the others' streaming.
+    int order[kMaxMats], no = 0;
+    for (int pass = 0; pass < 2; ++pass)
+      for (int i = 0; i < nm; ++i)
+        if ((k_tiles(ms[base + i].n_cols / kGroup) > 1) == (pass == 0)) order[no++] = i;
     int wg = 0;
-    for (int i = 0; i < nm; ++i) {
+    for (int pos = 0; pos < nm; ++pos) {
+      const int i = order[pos];
       const vbq_matrix& m = ms[base + i];
-      GemvMat& g = L.mats[i];
+      GemvMat& g = L.mats[pos];
       g.tiles = m.tiles;
       g.stream = reinterpret_cast<const uint8_t*>(m.stream);
       g.x = xs[base + i];

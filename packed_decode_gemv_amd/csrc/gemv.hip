@@ -123,25 +123,45 @@ __device__ inline void pair_step(const Consts<C>& k, const uint32_t* w, const ui
   for (int nb = 0; nb < NB; ++nb) acc[nb] = dot2(hv, lane_of<J & 3>(xv[nb]), acc[nb]);
 }
 
+// Two accumulators per batch row (even and odd pairs) halve the chain of
+// dependent dot products.
 template <int C, int CH, int NB>
-__device__ inline void chunk_step(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
-                                  float (&acc)[NB]) {
-  uint4 xv[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) xv[nb] = *reinterpret_cast<const uint4*>(xk + nb * xstride + 4 * CH);
+__device__ inline void chunk_compute(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[NB], float (&acc)[NB],
+                                     float (&acc2)[NB]) {
   pair_step<C, 4 * CH + 0, NB>(k, w, xv, acc);
-  pair_step<C, 4 * CH + 1, NB>(k, w, xv, acc);
+  pair_step<C, 4 * CH + 1, NB>(k, w, xv, acc2);
   pair_step<C, 4 * CH + 2, NB>(k, w, xv, acc);
-  pair_step<C, 4 * CH + 3, NB>(k, w, xv, acc);
+  pair_step<C, 4 * CH + 3, NB>(k, w, xv, acc2);
+}
+
+template <int C, int NB, int CH0, int G, int... g>
+__device__ inline void compute_group(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[G][NB], float (&acc)[NB],
+                                     float (&acc2)[NB], std::integer_sequence<int, g...>) {
+  (chunk_compute<C, CH0 + g, NB>(k, w, xv[g], acc, acc2), ...);
 }
 
 // acc[nb] += sum_j (bias_j + q_2j) x_2j + (bias_j + q_2j+1) x_2j+1 over the
 // lane's pairs. xk points at the lane's first pair in the x table of batch
-// row 0; batch rows are xstride dwords apart.
-template <int C, int NB, int... CH>
-__device__ inline void dot_lane_impl(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
-                                     float (&acc)[NB], std::integer_sequence<int, CH...>) {
-  (chunk_step<C, CH, NB>(k, w, xk, xstride, acc), ...);
+// row 0; batch rows are xstride dwords apart. The x chunks of a group (all of
+// them for one batch row) are loaded into registers before any is used, so a
+// record waits for LDS once rather than once per chunk; the scheduling
+// barrier keeps the compiler from interleaving loads and uses again.
+template <int C, int NB, int CH0>
+__device__ inline void dot_from(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
+                                float (&acc)[NB], float (&acc2)[NB]) {
+  constexpr int NCH = Geo<C>::NP / 4;
+  if constexpr (CH0 < NCH) {
+    constexpr int GMAX = 8 / NB > 1 ? 8 / NB : 1;
+    constexpr int G = NCH - CH0 < GMAX ? NCH - CH0 : GMAX;
+    uint4 xv[G][NB];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) xv[g][nb] = *reinterpret_cast<const uint4*>(xk + nb * xstride + 4 * (CH0 + g));
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group<C, NB, CH0, G>(k, w, xv, acc, acc2, std::make_integer_sequence<int, G>{});
+    dot_from<C, NB, CH0 + G>(k, w, xk, xstride, acc, acc2);
+  }
 }
 
 // ---- Synchronisation helpers ---------------------------------------------------
@@ -248,13 +268,35 @@ __device__ inline void lds_barrier() {
 // before it; lane nt holds the header of the next tile, whose byte base ends
 // the workgroup's range.
 struct TileLanes {
-  uint32_t byte0, n01, n23, pre;   // per lane
-  int nt, total;                   // tiles, blocks (uniform)
+  uint32_t byte0, n01, n23, pre, cpre;   // per lane
+  int nt, total;                         // tiles, blocks (uniform)
+  uint32_t cost;                         // decode cost of all blocks (uniform)
 };
 
 __device__ inline uint32_t tile_blocks(uint32_t n01, uint32_t n23) {
   return seg_blocks(0, n01 & 0xFFFF) + seg_blocks(1, n01 >> 16) + seg_blocks(2, n23 & 0xFFFF) +
          seg_blocks(3, n23 >> 16);
+}
+
+// Relative decode cost of one block per width class (VALU instructions of a
+// wavefront: a 1-bit block holds four records per lane, the others one).
+__host__ __device__ constexpr uint32_t block_cost(int c) { return c == 0 ? 6u : c == 3 ? 1u : 2u; }
+
+__device__ inline uint32_t tile_cost(uint32_t n01, uint32_t n23) {
+  return block_cost(0) * seg_blocks(0, n01 & 0xFFFF) + block_cost(1) * seg_blocks(1, n01 >> 16) +
+         block_cost(2) * seg_blocks(2, n23 & 0xFFFF) + block_cost(3) * seg_blocks(3, n23 >> 16);
+}
+
+// Exclusive sum over the 64 lanes (DPP row shifts, then row broadcasts).
+__device__ inline uint32_t wave_excl_sum(uint32_t v) {
+  uint32_t inc = v;
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x111, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x112, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x114, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x118, 0xF, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x142, 0xA, 0xF, false);
+  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x143, 0xC, 0xF, false);
+  return inc - v;
 }
 
 // h: the header loaded by this lane (zeros past the end of the list).
@@ -264,17 +306,44 @@ __device__ inline TileLanes make_tile_lanes(const uint4& h, int nt, uint32_t lan
   T.byte0 = h.y * 16u;
   T.n01 = (int)lane < nt ? h.z : 0u;
   T.n23 = (int)lane < nt ? h.w : 0u;
-  const uint32_t nb = tile_blocks(T.n01, T.n23);
-  uint32_t inc = nb;   // inclusive sum over lanes: DPP row shifts, then row broadcasts
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x111, 0xF, 0xF, false);
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x112, 0xF, 0xF, false);
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x114, 0xF, 0xF, false);
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x118, 0xF, 0xF, false);
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x142, 0xA, 0xF, false);
-  inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x143, 0xC, 0xF, false);
-  T.pre = inc - nb;
-  T.total = __builtin_amdgcn_readlane(inc, nt - 1);
+  const uint32_t nb = tile_blocks(T.n01, T.n23), cb = tile_cost(T.n01, T.n23);
+  T.pre = wave_excl_sum(nb);
+  T.cpre = wave_excl_sum(cb);
+  T.total = __builtin_amdgcn_readlane(T.pre + nb, nt - 1);
+  T.cost = __builtin_amdgcn_readlane(T.cpre + cb, nt - 1);
   return T;
+}
+
+// First block of the workgroup whose cost prefix (the summed block_cost of
+// the blocks before it) is at least `target` (< the workgroup's total cost),
+// as wavefront-uniform (block index, byte offset). Blocks of a class are laid
+// out back to back and all but the last are full, so the search is a ballot
+// over the tiles' cost prefixes and closed forms per class.
+__device__ inline void first_block_at(const TileLanes& T, uint32_t target, uint32_t lane, uint32_t& j_out,
+                                      uint32_t& byte_out) {
+  const int t = __builtin_popcountll(__builtin_amdgcn_ballot_w64((int)lane < T.nt && T.cpre <= target)) - 1;
+  const uint32_t n01 = __builtin_amdgcn_readlane(T.n01, t), n23 = __builtin_amdgcn_readlane(T.n23, t);
+  const uint32_t n[4] = {n01 & 0xFFFFu, n01 >> 16, n23 & 0xFFFFu, n23 >> 16};
+  uint32_t s = __builtin_amdgcn_readlane(T.byte0, t), j = __builtin_amdgcn_readlane(T.pre, t);
+  uint32_t cs = __builtin_amdgcn_readlane(T.cpre, t);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (target <= cs) break;   // the class (or the next tile) starts at or after the target
+    constexpr uint32_t kFull[4] = {block_bytes(0, block_records(0)), block_bytes(1, block_records(1)),
+                                   block_bytes(2, block_records(2)), block_bytes(3, block_records(3))};
+    const uint32_t kc = seg_blocks(c, n[c]);
+    const uint32_t k = (target - cs + block_cost(c) - 1u) / block_cost(c);
+    if (k < kc) {
+      j += k;
+      s += k * kFull[c];
+      break;
+    }
+    cs += block_cost(c) * kc;
+    s += (uint32_t)seg_bytes(c, n[c]);
+    j += kc;
+  }
+  j_out = j;
+  byte_out = s;
 }
 
 // ---- Per-lane block lookup ---------------------------------------------------------
@@ -362,7 +431,12 @@ __device__ inline void record_part(const Consts<C>& k, const Smem& S, const uint
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
   const uint32_t* xk = S.xs + kgl * kXStride + q * (uint32_t)Geo<C>::NP;
-  dot_lane_impl<C, NB>(k, w, xk, kTileGroups * kXStride, acc, std::make_integer_sequence<int, Geo<C>::NP / 4>{});
+  float acc2[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc2[nb] = 0.0f;
+  dot_from<C, NB, 0>(k, w, xk, kTileGroups * kXStride, acc, acc2);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] += acc2[nb];
   const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
   const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
 #pragma unroll
@@ -638,7 +712,7 @@ __device__ inline void finish_split(const GemvMat& M, const Smem& S, int kt, int
 // v_readlane in the block loop:
 //   bits 0-9 ring offset / 16 (rings up to 16 KiB), 10-11 width class,
 //   12-19 records - 1, 20-24 copies that may still be outstanding when the
-//   block is decoded (fewer than the 16 slots), 25-27 copies to issue after it.
+//   block is decoded (fewer than the 16 slots), 25-29 copies to issue after it.
 // The block's tile goes in a second per-lane word.
 // With pieces of 1 KiB at stream offset 1024 p going to ring slot p mod S, and
 // piece p issued as soon as every block before stream offset 1024 (p - S + 1)
@@ -646,10 +720,15 @@ __device__ inline void finish_split(const GemvMat& M, const Smem& S, int kt, int
 // and the block needs the first ceil((pos_j + size_j) / 1024): both closed
 // forms of the block's stream position. A block spans at most five pieces
 // (3584 bytes at an odd start), so S >= 5 keeps all of them in the ring.
+// Only kFirstPieces go out before the first block (at stream offset 0, so it
+// needs at most four): a wavefront starts decoding as soon as its first block
+// has landed, and issues the rest of its ring after that block.
+constexpr uint32_t kFirstPieces = 4;
+
 __device__ inline uint32_t make_desc(const BlockInfo& b, uint32_t B0, uint32_t np, uint32_t slots, uint32_t ring_mask) {
   const uint32_t pos = b.byte - B0;
   const uint32_t need = (pos + b.size + 1023u) >> 10;
-  const uint32_t before = min(np, (pos >> 10) + slots);
+  const uint32_t before = min(np, pos == 0 ? kFirstPieces : (pos >> 10) + slots);
   const uint32_t after = min(np, ((pos + b.size) >> 10) + slots);
   return ((pos & ring_mask) >> 4) | ((uint32_t)b.c << 10) | ((b.m - 1u) << 12) | ((before - need) << 20) |
          ((after - before) << 25);
@@ -694,25 +773,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));
   const TileLanes T = make_tile_lanes(h, nrl, lane);
 
-  // This wavefront's blocks [b0, b1) and their bytes [B0, B0 + span), in
-  // pieces of 1 KiB; the first `slots` pieces go out at once. Lane i looks up
-  // block b0 + i of the first chunk of 64; lane b1 - b0 (if below 64) finds
-  // where the range ends.
-  const int b0 = (int)(((int64_t)T.total * wave) / WAVES);
-  const int b1 = (int)(((int64_t)T.total * (wave + 1)) / WAVES);
-  uint32_t B0 = 0, span = 0, np = 0, issued = 0;
+  // This wavefront's blocks [b0, b1) and their bytes [B0, B1): the blocks
+  // whose cost prefix falls in its equal share of the workgroup's decode cost.
+  // They stream in pieces of 1 KiB.
+  uint32_t ub0, B0, ub1, B1;
+  first_block_at(T, (uint32_t)(((uint64_t)T.cost * wave) / WAVES), lane, ub0, B0);
+  if (wave == WAVES - 1) {
+    ub1 = (uint32_t)T.total;
+    B1 = __builtin_amdgcn_readlane(T.byte0, T.nt);
+  } else {
+    first_block_at(T, (uint32_t)(((uint64_t)T.cost * (wave + 1)) / WAVES), lane, ub1, B1);
+  }
+  const int b0 = (int)ub0, b1 = (int)ub1;
+  uint32_t span = 0, np = 0, issued = 0;
   BlockInfo first_chunk;
   first_chunk.byte = first_chunk.size = first_chunk.m = 0;
   first_chunk.c = first_chunk.t = 0;
   if (b0 < b1) {
-    const uint32_t jhi = (uint32_t)min(b1, b0 + kWave - 1);
+    const uint32_t jhi = (uint32_t)min(b1 - 1, b0 + kWave - 1);
     const uint32_t jl = min((uint32_t)b0 + lane, jhi);
-    first_chunk = block_info(T, min(jl, (uint32_t)T.total - 1u), (uint32_t)b0, min(jhi, (uint32_t)T.total - 1u), lane);
-    B0 = __builtin_amdgcn_readfirstlane(first_chunk.byte);
-    uint32_t B1;
-    if (b1 >= T.total) B1 = __builtin_amdgcn_readlane(T.byte0, T.nt);
-    else if (b1 - b0 < kWave) B1 = __builtin_amdgcn_readlane(first_chunk.byte, b1 - b0);
-    else B1 = __builtin_amdgcn_readfirstlane(block_info(T, (uint32_t)b1, (uint32_t)b1, (uint32_t)b1, lane).byte);
+    first_chunk = block_info(T, jl, (uint32_t)b0, jhi, lane);
     span = B1 - B0;
     np = (span + 1023u) >> 10;
   }
@@ -728,7 +808,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
       }
     }
   };
-  issue(min(np, slots));
+  issue(min(np, kFirstPieces));
 
   stage_x<NB, WAVES>(S, X, ng, tid);
   for (int i = tid; i < WAVES * NB * nrow; i += WAVES * kWave) S.yw[i] = 0.0f;
@@ -752,7 +832,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
       compute_any<NB>(K, S, (int)((d >> 10) & 3u), (d & 1023u) << 4, ((d >> 12) & 255u) + 1u, t, nrow, wave, lane);
       // Refill the freed ring slots; the decode's LDS reads are complete first.
       __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
-      issue(issued + ((d >> 25) & 7u));
+      issue(issued + ((d >> 25) & 31u));
     }
   }
   if constexpr (RESID) residual_rows<NB, WAVES>(M, S, r0, nrow, g0, ng, wave, lane);
@@ -776,7 +856,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   if (split) finish_split<NB, WAVES>(M, S, kt, cj, r0, nrow, tid);
 }
 
-int gemv_waves(int nb) { return nb <= 1 ? 16 : 8; }
+// Eight wavefronts per workgroup. With one batch row the x table is small,
+// so two workgroups (with 8 KiB rings) share a CU: one's start-up and final
+// reduction overlap the other's streaming.
+int gemv_waves(int) { return 8; }
+int gemv_wgs_per_cu(int nb) { return nb <= 1 ? 2 : 1; }
 
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes) {
   const int waves = gemv_waves(nb);
@@ -808,8 +892,8 @@ static hipError_t launch_one(const GemvLaunch& L, int n_wg, size_t lds, hipStrea
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s) {
 #define VBQ_CASE(N)                                                                                  \
   case N:                                                                                            \
-    return resid ? launch_one<N, (N <= 1 ? 16 : 8), true>(L, n_wg, lds, s)                           \
-                 : launch_one<N, (N <= 1 ? 16 : 8), false>(L, n_wg, lds, s);
+    return resid ? launch_one<N, 8, true>(L, n_wg, lds, s)                           \
+                 : launch_one<N, 8, false>(L, n_wg, lds, s);
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)

@@ -132,6 +132,7 @@ constexpr int kXStride = 36;
 constexpr int kXBytesPerGroup = kXStride * 4 + 5 * 4;
 
 int gemv_waves(int nb);
+int gemv_wgs_per_cu(int nb);
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, size_t lds, hipStream_t s);
 size_t gemv_lds_bytes(int nb, int rt_per_wg, uint32_t ring_bytes);
 uint32_t gemv_ring_min_bytes();
