@@ -48,9 +48,10 @@
  *     so    : u32, fp16 scale bits 0-15, fp16 offset bits 16-31;
  *     meta  : u16, row within the tile bits 0-3, k-group within the tile
  *             bits 4-9 (bits 10-15 zero).
- *   A class segment keeps its records in blocks of 64, 64, 32, 16 records
- *   (b = 1, 2, 4, 8; a full block carries 512, 1024, 1024, 1024 code bytes);
- *   the last block may hold m fewer. A block of m records is, in order:
+ *   A class segment keeps its records in blocks of 256, 64, 64, 16 records
+ *   (b = 1, 2, 4, 8; a full block carries 2048, 1024, 2048, 1024 code bytes);
+ *   the last block may hold fewer (m records). A block of m records is, in
+ *   order:
  *     codes area: record l's 2b words at byte 8b*l, in order (for b = 1
  *                 the area is rounded up to 16 bytes);
  *     so area   : record l at byte 4l, rounded up to 16 bytes;
@@ -175,8 +176,11 @@ vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t*
 
 /* Batched dequantise-and-multiply for M >= 64 tokens: tiles of W are decoded
  * to bf16 in LDS and contracted on MFMA with fp32 accumulation.
- *   y[m][n] = sum_k x[m][k] * bf16(s*q + o)
- * x_bf16: device, M x K bfloat16, 16-byte aligned. y: device, M x N float32,
+ *   y[m][n] = sum_k x[m][k] * bf16(fma(s, q, o))
+ * where fma is the binary32 fused multiply-add (one rounding of s*q + o) and
+ * bf16 rounds to nearest even. Any M >= 1 is accepted; the path pays off from
+ * about 64 tokens. x_bf16: device, M x K bfloat16, 16-byte aligned, with
+ * M * K * 2 < 2^32 (else VBQ_ERR_UNSUPPORTED). y: device, M x N float32,
  * 16-byte aligned, fully overwritten. */
 vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, float* y, hipStream_t stream);
 

@@ -5,15 +5,17 @@
 // Changing the File They Ship") for a batch of M tokens: with enough tokens
 // the product is compute-bound, so W is decoded on the fly to bfloat16 and
 // contracted on MFMA with fp32 accumulation:
-//   y[m][n] = sum_k x[m][k] * bf16(f32(s*q) + o)      (x bfloat16)
+//   y[m][n] = sum_k x[m][k] * bf16(fma(s, q, o))      (x bfloat16; fma rounds s*q + o once)
 //
 // A workgroup owns 128 tokens x 128 weight rows (8 row-tiles) of y and walks
-// K one 64-weight group at a time. Four producer wavefronts load x and the
-// codes and decode the weights; four consumer wavefronts run the MFMAs. Per group it stages
-// x[128 tokens][64] and the 128 rows' decoded weights W[128 rows][64] in LDS
-// (bf16, rows padded to 72 elements so the 16-byte operand reads of 16
-// consecutive lanes hit disjoint banks), and each wavefront runs 2 x 2
-// v_mfma_f32_32x32x16_bf16 tiles over the group: 64 tokens x 64 rows.
+// K one 64-weight group at a time. Four producer wavefronts load the codes
+// and decode the weights; four consumer wavefronts copy x into an LDS ring
+// with buffer-to-LDS loads and run the MFMAs. Per group the workgroup stages
+// x[128 tokens][64] (rows XOR-swizzled by 16-byte column) and the 128 rows'
+// decoded weights W[128 rows][64] in LDS (bf16, rows padded to 72 elements so
+// the 16-byte operand reads of 16 consecutive lanes hit disjoint banks), and
+// each consumer wavefront runs 2 x 2 v_mfma_f32_32x32x16_bf16 tiles over the
+// group: 64 tokens x 64 rows.
 //
 // Finding a row's record for a given k-group: the layout keeps a tile's
 // records by width class, then (row, k-group). At every k-tile the workgroup
