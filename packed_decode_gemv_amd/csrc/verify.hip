@@ -12,8 +12,8 @@
 // compared byte for byte.
 //
 // The decision is integer-valued, so the binary32 operation sequence is fixed
-// (built with -ffp-contract=off; the quotient is the correctly rounded one,
-// see rint_quotient):
+// (built with -ffp-contract=off; the quotient decides as the correctly
+// rounded one does, see quarter_fast):
 //   deq = f32(s*q) + o;  v = deq + r;  q' = clamp(rint((v - o) / s), 0, L)
 //   out of cell: |r| >= 0.5*s  (or r != 0 when s == 0).
 #include "vbq_common.h"
@@ -26,20 +26,6 @@ __global__ void k_verify_init(uint64_t* result) {
     result[1] = 0;
     result[2] = ~0ull;
   }
-}
-
-// rint(fl(a / s)) for finite s > 0, with fl the correctly rounded binary32
-// quotient, from the estimate t = a * rcp(s): t is within |t| * 2^-22 of a / s
-// and fl(a / s) within |a / s| * 2^-24 of it, so when t is farther than
-// |t| * 2^-20 (plus a tiny absolute slack) from the nearest half-integer, a / s
-// and fl(a / s) lie on the same side of it as t and all three round to the
-// same integer. `exact` is cleared otherwise (never for residuals inside
-// their cell); the caller then redoes the quotient correctly rounded.
-__device__ inline float rint_quotient_fast(float a, float s, bool& exact) {
-  const float t = a * __builtin_amdgcn_rcpf(s);
-  const float h = floorf(t) + 0.5f;
-  exact = exact && fabsf(t - h) > fabsf(t) * 0x1p-20f + 0x1p-40f;
-  return rintf(t);
 }
 
 // One quarter of a record: 16 consecutive weights (codes 16q .. 16q + 15).
@@ -55,14 +41,12 @@ struct Quarter {
   int c;           // width class, -1 if no record
 };
 
-// Re-quantises the 16 weights of a quarter: counts into lm / lo, smallest
-// failing index into lf, re-quantised code words into nw. EXACT selects the
-// correctly rounded quotient; otherwise the fast one, clearing `exact` when a
-// quotient falls inside the margin.
-template <int C, bool EXACT>
+// Re-quantises the 16 weights of a quarter with correctly rounded quotients:
+// counts into lm / lo, smallest failing index into lf, re-quantised code words
+// into nw. Any scale is handled (zero, negative or not finite).
+template <int C>
 __device__ inline void quarter_pass(const uint32_t (&w)[4], const uint4 (&rv)[2], float s, float o, int q,
-                                    uint64_t lin0, uint32_t& lm, uint32_t& lo, uint64_t& lf, uint32_t (&nw)[4],
-                                    bool& exact) {
+                                    uint64_t lin0, uint32_t& lm, uint32_t& lo, uint64_t& lf, uint32_t (&nw)[4]) {
   constexpr int B = 1 << C, H = 16 / B, L = (1 << B) - 1;
   const int p0 = 8 * q, wbase = p0 / H;
   const float half_s = __fmul_rn(0.5f, s);
@@ -82,7 +66,7 @@ __device__ inline void quarter_pass(const uint32_t (&w)[4], const uint4 (&rv)[2]
     const float a = __fsub_rn(__fadd_rn(deq, r), o);
     uint32_t qp = 0;
     if (s != 0.0f) {
-      float t = EXACT ? rintf(__fdiv_rn(a, s)) : rint_quotient_fast(a, s, exact);
+      float t = rintf(__fdiv_rn(a, s));
       t = t < 0.0f ? 0.0f : t;
       t = t > (float)L ? (float)L : t;
       qp = (uint32_t)t;
@@ -96,8 +80,50 @@ __device__ inline void quarter_pass(const uint32_t (&w)[4], const uint4 (&rv)[2]
   }
 }
 
-// The rare quarter with a quotient inside the margin: redone with correctly
-// rounded divisions, out of line (arguments and results by value, so that
+// The common case, for a finite s > 0: re-quantised code words into nw, and
+// true when every weight keeps its code and its residual is inside the cell,
+// i.e. the quarter contributes nothing to the counts. False sends the quarter
+// to quarter_exact.
+//   - s*q is exact in binary32 (at most 11 x 8 significant bits), so
+//     fma(s, q, o) rounds exactly like f32(s*q) + o.
+//   - The quotient is estimated as t = a * rcp(s), within |a/s| * 2^-22 of
+//     the correctly rounded a / s. Only quotients in [0, L] (L <= 255) decide
+//     a code, since the clamp maps everything else to 0 or L either way. There
+//     the estimate is within 2^-14 of the correctly rounded quotient, so if it
+//     is at least 2^-12 away from every half-integer, both round to the same
+//     integer. Closer estimates go to the exact path.
+template <int C>
+__device__ inline bool quarter_fast(const uint32_t (&w)[4], const uint4 (&rv)[2], float s, float o, int q,
+                                    uint32_t (&nw)[4]) {
+  constexpr int B = 1 << C, H = 16 / B, L = (1 << B) - 1;
+  const int p0 = 8 * q, wbase = p0 / H;
+  const float half_s = 0.5f * s;   // exact
+  const float rs = __builtin_amdgcn_rcpf(s);
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nw[i] = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int pr = p0 + j / 2, odd = j & 1;
+    const int wi = pr / H - wbase, sh = 16 * odd + (pr % H) * B;
+    const uint32_t code = (w[wi] >> sh) & (uint32_t)L;
+    const uint4& rr = rv[j / 8];
+    const uint32_t rw = ((j / 2) & 3) == 0 ? rr.x : ((j / 2) & 3) == 1 ? rr.y : ((j / 2) & 3) == 2 ? rr.z : rr.w;
+    const float r = __half2float(__ushort_as_half((unsigned short)(odd ? (rw >> 16) : (rw & 0xFFFF))));
+    const float deq = __builtin_fmaf(s, (float)code, o);
+    const float a = __fsub_rn(__fadd_rn(deq, r), o);
+    const float t = a * rs;
+    const float rt = rintf(t);
+    const uint32_t qp = (uint32_t)__builtin_amdgcn_fmed3f(rt, 0.0f, (float)L);
+    ok = ok && (fabsf(t - rt) < 0.5f - 0x1p-12f) && (qp == code) && (fabsf(r) < half_s);
+    nw[wi] |= qp << sh;
+  }
+  return ok;
+}
+
+// The rare quarter that changes a code, leaves its cell, has a quotient near a
+// rounding boundary or a scale that is not a finite positive number: redone
+// with correctly rounded divisions, out of line (arguments and results by value, so that
 // nothing has to live in memory) to keep its registers off the common path.
 struct QuarterResult {
   uint32_t lm, lo;
@@ -112,8 +138,7 @@ __device__ __attribute__((noinline)) QuarterResult quarter_exact(uint4 w4, uint4
   const uint4 rv[2] = {r0v, r1v};
   QuarterResult res;
   uint32_t nw[4];
-  bool exact = true;
-  quarter_pass<C, true>(w, rv, s, o, q, lin0, res.lm, res.lo, res.lf, nw, exact);
+  quarter_pass<C>(w, rv, s, o, q, lin0, res.lm, res.lo, res.lf, nw);
   res.nw = make_uint4(nw[0], nw[1], nw[2], nw[3]);
   return res;
 }
@@ -122,36 +147,32 @@ template <int C>
 __device__ inline void check_quarter(const Quarter& Qr, int q, int r0, int g0, int K, const uint4 (&rv)[2],
                                      uint32_t& mism, uint32_t& ooc, uint64_t& first, uint32_t (&nw)[4]) {
   const uint32_t w[4] = {Qr.w.x, Qr.w.y, Qr.w.z, Qr.w.w};
-  const int row = r0 + (int)(Qr.meta & 15), kg = g0 + (int)(Qr.meta >> 4);
   const float s = __half2float(__ushort_as_half((unsigned short)(Qr.so & 0xFFFF)));
   const float o = __half2float(__ushort_as_half((unsigned short)(Qr.so >> 16)));
-  const uint64_t lin0 = (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * (uint32_t)q;
-  uint32_t lm, lo;
-  uint64_t lf;
-  bool exact = true;
-  quarter_pass<C, false>(w, rv, s, o, q, lin0, lm, lo, lf, nw, exact);
-  if (!exact) {
+  const bool fast = s > 0.0f && s <= 65504.0f && quarter_fast<C>(w, rv, s, o, q, nw);
+  if (!fast) {
+    const int row = r0 + (int)(Qr.meta & 15), kg = g0 + (int)(Qr.meta >> 4);
+    const uint64_t lin0 = (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * (uint32_t)q;
     const QuarterResult e = quarter_exact<C>(Qr.w, rv[0], rv[1], s, o, q, lin0);
-    lm = e.lm;
-    lo = e.lo;
-    lf = e.lf;
     nw[0] = e.nw.x;
     nw[1] = e.nw.y;
     nw[2] = e.nw.z;
     nw[3] = e.nw.w;
+    mism += e.lm;
+    ooc += e.lo;
+    first = e.lf < first ? e.lf : first;
   }
-  mism += lm;
-  ooc += lo;
-  first = lf < first ? lf : first;
 }
 
-// One workgroup per tile, four lanes per record (a quarter each), up to four
-// records per lane group. All loads of a phase are issued together: the
-// records' codes, scale/offset and meta, then the residuals the meta points
-// at.
-constexpr int kVerifyThreads = 1024;
+// One workgroup of 256 threads per tile (several resident per CU, so one's
+// memory round trips overlap another's arithmetic), four lanes per record (a
+// quarter each), sixteen quarters per lane in batches of two (at most 96
+// VGPRs: five wavefronts per SIMD). All loads of a batch are issued together:
+// the records' codes, scale/offset and meta, then the residuals the meta
+// points at.
+constexpr int kVerifyThreads = 256;
 
-__global__ __launch_bounds__(kVerifyThreads) void k_verify(const uint32_t* __restrict__ tiles,
+__global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __restrict__ tiles,
                                                            const uint8_t* __restrict__ stream, int G, int RT,
                                                            const uint16_t* __restrict__ resid, uint64_t* result,
                                                            uint8_t* requant) {
@@ -183,9 +204,8 @@ __global__ __launch_bounds__(kVerifyThreads) void k_verify(const uint32_t* __res
   const int q = tid & 3;
   uint32_t mism = 0, ooc = 0;
   uint64_t first = ~0ull;
-  constexpr int kPer = kTile * kTileGroups * 4 / kVerifyThreads;   // quarters per thread: 4
+  constexpr int kPer = kTile * kTileGroups * 4 / kVerifyThreads;   // quarters per thread: 16
   constexpr int kBatch = 2;                                         // quarters loaded together
-#pragma unroll
   for (int b0 = 0; b0 < kPer; b0 += kBatch) {
     Quarter Q[kBatch];
 #pragma unroll

@@ -318,6 +318,33 @@ def test_requant_verify_near_half_cells(vbq):
     assert np.array_equal(q_rq, ref[3])
 
 
+def test_requant_verify_in_cell_near_half(vbq):
+    """Residuals inside their cells but within 2^-11 .. 2^-8 of half a cell
+    most quarters keep every code and take the kernel's estimated-quotient
+    path, whose rounding decisions sit right next to the half-integers; the
+    counts, first index and re-quantised codes must equal the oracle's."""
+    import torch
+    r = np.random.default_rng(45)
+    N, K = 64, 2048
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[5, 64:128] = 0.01          # constant groups: scale 0, residual must be 0 (exact path)
+    W[40, 1024:1088] = -0.02
+    q, s, o = oracle.quantize_matrix(W, widths)
+    assert s[5, 1] == 0 and s[40, 16] == 0
+    hair = r.choice(np.array([2.0 ** -11, 2.0 ** -10, 2.0 ** -9, 2.0 ** -8]), size=(N, K))
+    u = np.where(r.random((N, K)) < 0.5, -1.0, 1.0) * (0.5 - hair)
+    resid = oracle.make_cell_residual(u, s)
+    pm = vbq.vbq_pack(_t(W), widths)
+    ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    assert (mism, ooc, first) == ref[:3]
+    lay_rq = pm.host_layout()
+    lay_rq["stream"] = rq.cpu().numpy().view(np.uint32)
+    q_rq, _, _, _ = oracle.unpack(lay_rq)
+    assert np.array_equal(q_rq, ref[3])
+
+
 def test_requant_verify_mixed_widths(vbq):
     import torch
     N, K = 48, 2048
