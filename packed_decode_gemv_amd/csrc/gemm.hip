@@ -20,9 +20,9 @@
 // Finding a row's record for a given k-group: the layout keeps a tile's
 // records by width class, then (row, k-group). At every k-tile the workgroup
 // reads the meta of all its records once and builds, per k-group, the list of
-// its 128 rows' records sorted by width class (LDS, 64 KiB). The decode of a
+// its 128 rows' records grouped by width class (LDS, 64 KiB). The decode of a
 // group then gives lane pairs consecutive entries of that list, so a
-// wavefront mostly decodes a single width without divergence.
+// wavefront decodes one or two widths.
 //
 // Producers load groups into registers three ahead of the one being
 // multiplied (covering the load latency) and decode into the other half of
@@ -164,11 +164,17 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
     for (int it = 0; it < kRecPerThread; ++it)
       if (valid >> (r * kRecPerThread + it) & 1u) atomicAdd(&S.cnt[tag[r][it] >> 26][(tag[r][it] >> 24) & 3u], 1u);
   gemm_barrier();
-  if (tid < kTileGroups) {   // class c of k-group kgl starts after the narrower classes
+  if (tid < kTileGroups) {
+    // Class order in a k-group's list: 8-bit, 1-bit, 2-bit, 4-bit. Producer
+    // wavefronts take 32 consecutive entries each and run one decode path
+    // per class they hold, so the short classes are kept apart: with the
+    // usual mixes (mostly 1-bit) no wavefront holds more than two classes.
+    constexpr int kOrder[4] = {3, 0, 1, 2};
     uint32_t sum = 0;
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t v = S.cnt[tid][c];
-      S.cnt[tid][c] = sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = S.cnt[tid][kOrder[i]];
+      S.cnt[tid][kOrder[i]] = sum;
       sum += v;
     }
   }
@@ -259,15 +265,17 @@ __device__ inline void store_weights(GemmSmem& S, int buf, const CodeRegs& R, in
   for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
 }
 
-// One x-loading wavefront copies the 64 token rows [r0, r0 + 64) of group g
-// into slot `slot`: eight copies of 1 KiB (eight rows each), lane l taking
+// One consumer wavefront copies the 32 token rows [r0, r0 + 32) of group g
+// into slot `slot`: four copies of 1 KiB (eight rows each), lane l taking
 // row r0 + 8i + l / 8, stored column l % 8. Rows past M read as zeros (the
 // buffer ends at M rows).
+constexpr int kXCopies = 4;   // copies per consumer wavefront and group
+
 __device__ inline void copy_x(const GemmArgs& a, const u32x4& rsrc, uint32_t slot_lds, int m0, int r0, int g,
                               int lane) {
   const uint32_t K2 = (uint32_t)a.G * kXRow;   // bytes per token row of x
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kXCopies; ++i) {
     const int R = r0 + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     dma16(rsrc, slot_lds + (uint32_t)(r0 + 8 * i) * kXRow,
@@ -309,15 +317,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   //  - producers hold the codes of groups g+1..g+3 in three register stages:
   //    they load group g + 3 and decode group g + 1 into the free weight
   //    buffer while the consumers multiply group g;
-  //  - the two consumer wavefronts of weight half 0 also copy x of group
-  //    g + 2 into the free x slot (buffer-to-LDS, no registers) and, before
-  //    the barrier, wait until their copy of group g + 1 has landed.
+  //  - each consumer wavefront also copies a quarter of x of group g + 2
+  //    into the free x slot (buffer-to-LDS, no registers) and, before the
+  //    barrier, waits until its copy of group g + 1 has landed.
   // Producers issue only register loads and consumers only copies, so the
   // compiler's load-count waits in the producers are exact and the copies
   // are waited for explicitly. Every step issues the same loads (group
   // indices clamped to the k-tile's last), steps past the end only keep the
   // barrier schedule.
-  const bool x_loader = !producer && wn == 0;
+  const bool x_loader = !producer;
+  const int xr0 = cw * 32;   // this wavefront's x rows
   const u32x4 xrsrc = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.G * kXRow);
   const uint32_t xs_lds = lds_addr(&S.xs[0][0]);
   const int KT = (a.G + kTileGroups - 1) / kTileGroups;
@@ -332,10 +341,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
       load_codes(a, S, base16, min(g0 + 2, g1 - 1) & (kTileGroups - 1), nvalid, tid, st2);
       store_weights(S, g0 & 1, st0, tid);
     } else if (x_loader) {
-      copy_x(a, xrsrc, xs_lds + (uint32_t)(g0 % kXSlots) * kBM * kXRow, m0, wm * 64, g0, lane);
-      copy_x(a, xrsrc, xs_lds + (uint32_t)((g0 + 1) % kXSlots) * kBM * kXRow, m0, wm * 64, min(g0 + 1, g1 - 1),
+      copy_x(a, xrsrc, xs_lds + (uint32_t)(g0 % kXSlots) * kBM * kXRow, m0, xr0, g0, lane);
+      copy_x(a, xrsrc, xs_lds + (uint32_t)((g0 + 1) % kXSlots) * kBM * kXRow, m0, xr0, min(g0 + 1, g1 - 1),
              lane);
-      __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(8));   // group g0 landed
+      __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g0 landed
     }
     gemm_barrier();
     auto step = [&](int g, CodeRegs& reload, const CodeRegs& next) {
@@ -345,30 +354,34 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
         if (g + 1 < g1) store_weights(S, buf ^ 1, next, tid);
       } else {
         if (x_loader)
-          copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, wm * 64, min(g + 2, g1 - 1),
+          copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
                  lane);
         if (g < g1) {
+          // All operands of the group are read from LDS before the first
+          // MFMA, so the wavefront waits for LDS once per group, not per step.
           const uint8_t* xslot = S.xs[g % kXSlots];
+          bf16x8 av[4][2], bv[4][2];
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 av[2], bv[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               const int R = wm * 64 + 32 * i + (lane & 31);
-              av[i] = *reinterpret_cast<const bf16x8*>(xslot + x_offset(R, 2 * kk + (lane >> 5)));
+              av[kk][i] = *reinterpret_cast<const bf16x8*>(xslot + x_offset(R, 2 * kk + (lane >> 5)));
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-              bv[j] = *reinterpret_cast<const bf16x8*>(
+              bv[kk][j] = *reinterpret_cast<const bf16x8*>(
                   &S.ws[buf][wn * 64 + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
               for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-          }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
         }
-        if (x_loader) __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(8));   // group g + 1 landed
+        if (x_loader) __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g + 1 landed
       }
       gemm_barrier();
     };
