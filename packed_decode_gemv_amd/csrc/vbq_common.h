@@ -114,7 +114,7 @@ struct GemvMat {
   uint32_t stream_bytes;   // size of the stream, for the buffer range checks
 };
 
-constexpr int kMaxMats = 8;
+constexpr int kMaxMats = 32;   // matrices per launch (about 3 KiB of kernel arguments)
 constexpr int kMaxWgTiles = 64;   // tiles of one workgroup (one per lane)
 
 struct GemvLaunch {

@@ -185,6 +185,26 @@ def test_split_k_batched_mix(vbq):
             assert rel_l2(y.cpu().numpy(), ref) <= TOL
 
 
+def test_batched_more_matrices_than_one_launch(vbq):
+    """40 matrices in one call (more than a launch takes, so the library
+    splits them), of mixed shapes, some with K > 4096: every output matches
+    the oracle."""
+    import torch
+    r = np.random.default_rng(77)
+    mats, refs = [], []
+    for i in range(40):
+        N = int(r.choice([16, 40, 96, 256, 513]))
+        K = int(r.choice([64, 1024, 4096, 4160, 8192]))
+        W, widths, x = rand_case(N, K, seed=300 + i, B=1)
+        q, s, o = oracle.quantize_matrix(W, widths)
+        mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
+        refs.append(oracle.gemv(q, s, o, x))
+    print("case batched 40 matrices", flush=True)
+    ys = vbq.vbq_gemv_batched([pm for pm, _ in mats], [x for _, x in mats])
+    for y, ref in zip(ys, refs):
+        assert rel_l2(y.cpu().numpy(), ref) <= TOL
+
+
 def test_graph_replays_match_eager(vbq):
     """Launches captured in a HIP graph (as the benchmark replays a decode
     step) give the eager results on every replay, with other eager work and
