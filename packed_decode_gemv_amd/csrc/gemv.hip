@@ -775,7 +775,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
 
   // This wavefront's blocks [b0, b1) and their bytes [B0, B1): the blocks
   // whose cost prefix falls in its equal share of the workgroup's decode cost.
-  // They stream in pieces of 1 KiB.
+  // They stream in pieces of 1 KiB; the first pieces go out before anything
+  // else is set up.
   uint32_t ub0, B0, ub1, B1;
   first_block_at(T, (uint32_t)(((uint64_t)T.cost * wave) / WAVES), lane, ub0, B0);
   if (wave == WAVES - 1) {
@@ -785,17 +786,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
     first_block_at(T, (uint32_t)(((uint64_t)T.cost * (wave + 1)) / WAVES), lane, ub1, B1);
   }
   const int b0 = (int)ub0, b1 = (int)ub1;
-  uint32_t span = 0, np = 0, issued = 0;
-  BlockInfo first_chunk;
-  first_chunk.byte = first_chunk.size = first_chunk.m = 0;
-  first_chunk.c = first_chunk.t = 0;
-  if (b0 < b1) {
-    const uint32_t jhi = (uint32_t)min(b1 - 1, b0 + kWave - 1);
-    const uint32_t jl = min((uint32_t)b0 + lane, jhi);
-    first_chunk = block_info(T, jl, (uint32_t)b0, jhi, lane);
-    span = B1 - B0;
-    np = (span + 1023u) >> 10;
-  }
+  const uint32_t span = b0 < b1 ? B1 - B0 : 0u, np = (span + 1023u) >> 10;
+  uint32_t issued = 0;
   const uint32_t lane16 = 16u * lane;
   auto issue = [&](uint32_t upto) {
     for (; issued < upto; ++issued) {
@@ -808,7 +800,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
       }
     }
   };
-  issue(min(np, kFirstPieces));
+  issue(min(np, kFirstPieces));   // first, so that the setup below overlaps the copies
 
   stage_x<NB, WAVES>(S, X, ng, tid);
   for (int i = tid; i < WAVES * NB * nrow; i += WAVES * kWave) S.yw[i] = 0.0f;
@@ -822,7 +814,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const GemvLaunch L) {
   for (int base = b0; base < b1; base += kWave) {
     const uint32_t jhi = (uint32_t)min(b1 - 1, base + kWave - 1);
     const uint32_t jl = min((uint32_t)(base + (int)lane), jhi);
-    const BlockInfo bi = base == b0 ? first_chunk : block_info(T, jl, (uint32_t)base, jhi, lane);
+    const BlockInfo bi = block_info(T, jl, (uint32_t)base, jhi, lane);
     const uint32_t desc = make_desc(bi, B0, np, slots, S.ring_mask);
     const int n_here = min(kWave, b1 - base);
     for (int k = 0; k < n_here; ++k) {

@@ -123,6 +123,7 @@ struct GemvLaunch {
   int32_t rt_per_wg;       // largest row-tiles per workgroup (LDS row sums)
   uint32_t ring_bytes;     // LDS ring of each wavefront (multiple of 1024)
 };
+static_assert(sizeof(GemvLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // x of one k-tile in LDS: pairs of a k-group take 32 dwords plus 4 of padding,
 // so neighbouring k-groups start 144 bytes apart, which spreads lanes that read
