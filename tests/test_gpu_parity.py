@@ -338,6 +338,24 @@ def test_requant_verify_near_half_cells(vbq):
     assert np.array_equal(q_rq, ref[3])
 
 
+def test_requant_verify_flipped_bit(vbq):
+    """A served artifact with one code bit flipped: the check re-quantises
+    against the artifact it is given, so it passes, and the re-quantised
+    stream it emits is that artifact bit for bit, so comparing it with the
+    release finds exactly the flipped word."""
+    import torch
+    N, K = 40, 1024
+    W, widths, q, s, o, resid, _ = _cell_inputs(N, K, seed=13)
+    release = vbq.vbq_pack(_t(W), widths)
+    served = release.clone()
+    served.stream[0:1].bitwise_xor_(1)        # lowest code bit of the first record of the stream
+    mism, ooc, first, rq = vbq.cell_requant_verify(served, _t(resid, torch.float16), requant_codes=True)
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    assert torch.equal(rq, served.stream)
+    diff = torch.nonzero(rq != release.stream).flatten().tolist()
+    assert diff == [0]
+
+
 def test_requant_verify_in_cell_near_half(vbq):
     """Residuals inside their cells but within 2^-11 .. 2^-8 of half a cell
     most quarters keep every code and take the kernel's estimated-quotient
