@@ -353,9 +353,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
         load_codes(a, S, base16, min(g + 3, g1 - 1) & (kTileGroups - 1), nvalid, tid, reload);
         if (g + 1 < g1) store_weights(S, buf ^ 1, next, tid);
       } else {
-        if (x_loader)
-          copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
-                 lane);
         if (g < g1) {
           // All operands of the group are read from LDS before the first
           // MFMA, so the wavefront waits for LDS once per group, not per step.
@@ -381,6 +378,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
               for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
         }
+        // The copy of group g + 2 goes out after the MFMAs are issued, so a
+        // copy that waits for the memory pipeline does not hold them back;
+        // its slot was last read in the previous step, before the barrier.
+        if (x_loader)
+          copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
+                 lane);
         if (x_loader) __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g + 1 landed
       }
       gemm_barrier();
