@@ -123,21 +123,18 @@ __device__ inline void pair_step(const Consts<C>& k, const uint32_t* w, const ui
   for (int nb = 0; nb < NB; ++nb) acc[nb] = dot2(hv, lane_of<J & 3>(xv[nb]), acc[nb]);
 }
 
-// Two accumulators per batch row (even and odd pairs) halve the chain of
-// dependent dot products.
 template <int C, int CH, int NB>
-__device__ inline void chunk_compute(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[NB], float (&acc)[NB],
-                                     float (&acc2)[NB]) {
+__device__ inline void chunk_compute(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[NB], float (&acc)[NB]) {
   pair_step<C, 4 * CH + 0, NB>(k, w, xv, acc);
-  pair_step<C, 4 * CH + 1, NB>(k, w, xv, acc2);
+  pair_step<C, 4 * CH + 1, NB>(k, w, xv, acc);
   pair_step<C, 4 * CH + 2, NB>(k, w, xv, acc);
-  pair_step<C, 4 * CH + 3, NB>(k, w, xv, acc2);
+  pair_step<C, 4 * CH + 3, NB>(k, w, xv, acc);
 }
 
 template <int C, int NB, int CH0, int G, int... g>
 __device__ inline void compute_group(const Consts<C>& k, const uint32_t* w, const uint4 (&xv)[G][NB], float (&acc)[NB],
-                                     float (&acc2)[NB], std::integer_sequence<int, g...>) {
-  (chunk_compute<C, CH0 + g, NB>(k, w, xv[g], acc, acc2), ...);
+                                     std::integer_sequence<int, g...>) {
+  (chunk_compute<C, CH0 + g, NB>(k, w, xv[g], acc), ...);
 }
 
 // acc[nb] += sum_j (bias_j + q_2j) x_2j + (bias_j + q_2j+1) x_2j+1 over the
@@ -148,7 +145,7 @@ __device__ inline void compute_group(const Consts<C>& k, const uint32_t* w, cons
 // barrier keeps the compiler from interleaving loads and uses again.
 template <int C, int NB, int CH0>
 __device__ inline void dot_from(const Consts<C>& k, const uint32_t* w, const uint32_t* xk, int xstride,
-                                float (&acc)[NB], float (&acc2)[NB]) {
+                                float (&acc)[NB]) {
   constexpr int NCH = Geo<C>::NP / 4;
   if constexpr (CH0 < NCH) {
     constexpr int GMAX = 8 / NB > 1 ? 8 / NB : 1;
@@ -159,8 +156,8 @@ __device__ inline void dot_from(const Consts<C>& k, const uint32_t* w, const uin
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) xv[g][nb] = *reinterpret_cast<const uint4*>(xk + nb * xstride + 4 * (CH0 + g));
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<C, NB, CH0, G>(k, w, xv, acc, acc2, std::make_integer_sequence<int, G>{});
-    dot_from<C, NB, CH0 + G>(k, w, xk, xstride, acc, acc2);
+    compute_group<C, NB, CH0, G>(k, w, xv, acc, std::make_integer_sequence<int, G>{});
+    dot_from<C, NB, CH0 + G>(k, w, xk, xstride, acc);
   }
 }
 
@@ -431,16 +428,11 @@ __device__ inline void record_part(const Consts<C>& k, const Smem& S, const uint
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = q == 0 ? -S.cx[(nb * 4 + C) * kTileGroups + kgl] : 0.0f;
   const uint32_t* xk = S.xs + kgl * kXStride + q * (uint32_t)Geo<C>::NP;
-  float acc2[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc2[nb] = 0.0f;
-  dot_from<C, NB, 0>(k, w, xk, kTileGroups * kXStride, acc, acc2);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] += acc2[nb];
+  dot_from<C, NB, 0>(k, w, xk, kTileGroups * kXStride, acc);
   const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
   const float o = q == 0 ? __half2float(__ushort_as_half((unsigned short)(so >> 16))) : 0.0f;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) v[nb] = s * acc[nb] + o * S.xsum[nb * kTileGroups + kgl];
+  for (int nb = 0; nb < NB; ++nb) v[nb] = __builtin_fmaf(s, acc[nb], o * S.xsum[nb * kTileGroups + kgl]);
 }
 
 // Decodes one block of class C (m records) at ring offset `boff` and adds each
