@@ -172,13 +172,18 @@ __device__ inline void check_quarter(const Quarter& Qr, int q, int r0, int g0, i
 // points at.
 constexpr int kVerifyThreads = 256;
 
+// Without the re-quantised stream, a tile's records are split over
+// kVerifyParts workgroups (more round trips in flight per CU); with it, one
+// workgroup per tile copies the tile and rewrites its codes.
+constexpr int kVerifyParts = 4;
+
 __global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __restrict__ tiles,
                                                            const uint8_t* __restrict__ stream, int G, int RT,
                                                            const uint16_t* __restrict__ resid, uint64_t* result,
-                                                           uint8_t* requant) {
+                                                           uint8_t* requant, int parts) {
   __shared__ uint32_t s_mism, s_ooc;
   __shared__ unsigned long long s_first;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = (int)blockIdx.x / parts, part = (int)blockIdx.x - t * parts, tid = threadIdx.x;
   if (tid == 0) {
     s_mism = 0;
     s_ooc = 0;
@@ -206,11 +211,13 @@ __global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __
   uint64_t first = ~0ull;
   constexpr int kPer = kTile * kTileGroups * 4 / kVerifyThreads;   // quarters per thread: 16
   constexpr int kBatch = 2;                                         // quarters loaded together
-  for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+  const int per = kPer / parts;                                     // quarters of this workgroup per thread
+  const uint32_t ibase = (uint32_t)(part * per) * (kVerifyThreads / 4);
+  for (int b0 = 0; b0 < per; b0 += kBatch) {
     Quarter Q[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const uint32_t i = (uint32_t)(tid >> 2) + (uint32_t)(b0 + u) * (kVerifyThreads / 4);
+      const uint32_t i = ibase + (uint32_t)(tid >> 2) + (uint32_t)(b0 + u) * (kVerifyThreads / 4);
       Q[u].c = -1;
       Q[u].wbyte = 0;
       if (i < total) {
@@ -280,9 +287,11 @@ __global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
-  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(kVerifyThreads), 0, s, m.tiles,
+  const int parts = requant ? 1 : kVerifyParts;
+  if ((int64_t)m.n_tiles * parts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_verify, dim3((unsigned)(m.n_tiles * parts)), dim3(kVerifyThreads), 0, s, m.tiles,
                      reinterpret_cast<const uint8_t*>(m.stream), m.n_cols / kGroup, row_tiles(m.n_rows), resid,
-                     result, reinterpret_cast<uint8_t*>(requant));
+                     result, reinterpret_cast<uint8_t*>(requant), parts);
   return hipGetLastError();
 }
 

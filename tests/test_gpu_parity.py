@@ -285,12 +285,22 @@ def test_residual_gemv_and_revocation(vbq, shape):
     assert np.allclose(yz, y0, rtol=1e-6, atol=1e-6)
 
 
+def _verify_both(vbq, pm, resid_t):
+    """cell_requant_verify with the re-quantised stream (one workgroup per
+    tile) and without it (a tile's records split over several workgroups):
+    the counts and first index must agree; returns the first call's result."""
+    got = vbq.cell_requant_verify(pm, resid_t, requant_codes=True)
+    bare = vbq.cell_requant_verify(pm, resid_t)
+    assert bare[:3] == got[:3] and bare[3] is None
+    return got
+
+
 def test_requant_verify_small(vbq):
     import torch
     N, K = 40, 1024
     W, widths, q, s, o, resid, _ = _cell_inputs(N, K, seed=9)
     pm = vbq.vbq_pack(_t(W), widths)
-    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, pm, _t(resid, torch.float16))
     assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
     assert torch.equal(rq, pm.stream), "re-quantised artifact differs from the release"
     # planted: exactly half a cell at three places, 0.6 of a cell at two interior codes
@@ -302,7 +312,7 @@ def test_requant_verify_small(vbq):
     for n, k in interior[[10, 2000]]:
         bad[n, k] = oracle.f16_from_f64(np.array([0.6 * sf[n, k]]))[0]
     ref = oracle.requant_verify(q, s, o, widths, bad, want_codes=True)
-    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(bad, torch.float16), requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, pm, _t(bad, torch.float16))
     assert (mism, ooc, first) == ref[:3]
     # half a cell can round the code across (ties to even), so >= 2 mismatches
     assert ref[0] >= 2 and ref[1] == 5
@@ -329,7 +339,7 @@ def test_requant_verify_near_half_cells(vbq):
     resid = oracle.make_cell_residual(u, s)
     pm = vbq.vbq_pack(_t(W), widths)
     ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
-    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, pm, _t(resid, torch.float16))
     assert (mism, ooc, first) == ref[:3]
     assert ref[0] > 0 and ref[1] > 0
     lay_rq = pm.host_layout()
@@ -349,7 +359,7 @@ def test_requant_verify_flipped_bit(vbq):
     release = vbq.vbq_pack(_t(W), widths)
     served = release.clone()
     served.stream[0:1].bitwise_xor_(1)        # lowest code bit of the first record of the stream
-    mism, ooc, first, rq = vbq.cell_requant_verify(served, _t(resid, torch.float16), requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, served, _t(resid, torch.float16))
     assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
     assert torch.equal(rq, served.stream)
     diff = torch.nonzero(rq != release.stream).flatten().tolist()
@@ -375,7 +385,7 @@ def test_requant_verify_in_cell_near_half(vbq):
     resid = oracle.make_cell_residual(u, s)
     pm = vbq.vbq_pack(_t(W), widths)
     ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
-    mism, ooc, first, rq = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, pm, _t(resid, torch.float16))
     assert (mism, ooc, first) == ref[:3]
     lay_rq = pm.host_layout()
     lay_rq["stream"] = rq.cpu().numpy().view(np.uint32)
@@ -393,7 +403,7 @@ def test_requant_verify_mixed_widths(vbq):
     u = r.uniform(-0.7, 0.7, (N, K))              # some residuals leave their cells
     resid = oracle.make_cell_residual(u, s)
     pm = vbq.vbq_pack(_t(W), widths)
-    got = vbq.cell_requant_verify(pm, _t(resid, torch.float16), requant_codes=True)
+    got = _verify_both(vbq, pm, _t(resid, torch.float16))
     ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
     assert got[:3] == ref[:3]
     assert ref[0] > 0 and ref[1] > 0
@@ -493,7 +503,7 @@ def test_workload_in_cell_full_size(vbq):
     rows = _sample_rows(N, np.random.default_rng(2))
     ref = oracle.gemv(q[rows], s[rows], o[rows], x, resid[rows])
     assert rel_l2(y[:, rows], ref) <= TOL
-    mism, ooc, first, rq = vbq.cell_requant_verify(pm, rt, requant_codes=True)
+    mism, ooc, first, rq = _verify_both(vbq, pm, rt)
     assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
     assert torch.equal(rq, pm.stream)
     ref_v = oracle.requant_verify(q[rows], s[rows], o[rows], widths[rows], resid[rows])
