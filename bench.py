@@ -234,6 +234,35 @@ def copy_calibration():
     log(f"copy calibration: {COPY_CAL_REPS} x torch.neg over {COPY_CAL_BYTES} B")
 
 
+def stream_ceilings():
+    """Practical HBM ceilings measured in the same run, next to the 8 TB/s
+    specification: a read-only pass (row sums of 2 GiB of fp32 in rows of 1024:
+    reads each byte once, writes 1/1024 as much; the fastest read-only torch
+    kernel found) and a copy (torch.neg over 1 GiB: reads and writes each byte
+    once), each the best of a few timed repetitions."""
+    import torch
+    a = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    c = a[: (1 << 30) // 4]
+    d = torch.empty_like(c)
+    out = {}
+    for name, fn, nbytes in (("read_gbs", lambda: a.view(-1, 1024).sum(1), 2 << 30),
+                             ("copy_gbs", lambda: torch.neg(c, out=d), 2 << 30)):
+        fn()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        out[name] = round(nbytes / best / 1e9, 1)
+    del a, c, d
+    out["kernels"] = "row sums of 2 GiB fp32, rows of 1024 (read); torch.neg over 1 GiB fp32 (read + write)"
+    return out
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 result summaries (CPU only; read the SQLite result files)
 
@@ -627,6 +656,9 @@ def main(argv=None):
     layer_us = (ms * 1e3 - head_us) / args.layers
     log(f"  event pair per launch: layer {d[:-1].mean():.2f} us, lm_head {head_us:.2f} us")
 
+    ceilings = stream_ceilings()
+    log(f"  measured ceilings: read {ceilings['read_gbs']:.0f} GB/s, copy {ceilings['copy_gbs']:.0f} GB/s")
+
     workloads = None
     if not args.no_workloads:
         log("other workloads")
@@ -680,6 +712,7 @@ def main(argv=None):
             "kernel": KERNEL,
             "avg_launch_us": round(launch_avg_us, 3),
             "algorithmic_bytes_per_launch": bytes_per_launch,
+            "measured_ceilings": ceilings,
         },
         "cpu_baseline": cpu,
         "parity": parity,
