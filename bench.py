@@ -274,7 +274,7 @@ def _db_files(path):
 
 
 def _short(name):
-    name = name.split("(")[0]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
     return name.replace("void ", "")
 
 
@@ -296,6 +296,70 @@ def _pmc_rows(path, counter):
         out += c.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
                          "where counter_name = ? group by dispatch_id, kernel_name", (counter,)).fetchall()
     return out
+
+
+def _pmc_max_rows(path, counter):
+    """Per dispatch, the largest value of `counter` over its instances (a
+    counter kept once per XCD, such as GRBM_GUI_ACTIVE, is the time the
+    busiest XCD was active, not the sum over XCDs)."""
+    import sqlite3
+    out = []
+    for f in _db_files(path):
+        c = sqlite3.connect(f)
+        out += c.execute("select K.dispatch_id, max(E.value), K.end - K.start from rocpd_pmc_event E "
+                         "join rocpd_info_pmc I on I.id = E.pmc_id and I.guid = E.guid "
+                         "join rocpd_kernel_dispatch K on K.event_id = E.event_id and K.guid = E.guid "
+                         "where I.name = ? group by E.guid, K.dispatch_id", (counter,)).fetchall()
+    return out
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                 "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4                # MI355X: 256 compute units of 4 SIMDs
+
+
+def summarize_mfma(path, command, flops_per_call):
+    """Markdown summary of one --pmc pass over the GEMM: MFMA utilisation
+    (busy cycles of the matrix units over 1024 SIMDs x the active cycles of
+    the busiest XCD), counted bf16 flops against 2 M N K, co-issue of vector
+    work beside the MFMAs, and the clock those cycles imply."""
+    per = {}
+    for counter in MFMA_COUNTERS:
+        if counter == "GRBM_GUI_ACTIVE":
+            rows = [(d, v, dur) for (d, v, dur) in _pmc_max_rows(path, counter)]
+        else:
+            rows = [(d, v, None) for (d, k, v) in _pmc_rows(path, counter) if "k_gemm" in k]
+        per[counter] = {d: (v, dur) for (d, v, dur) in rows}
+    ids = sorted(per["SQ_VALU_MFMA_BUSY_CYCLES"])
+    if not ids:
+        raise SystemExit("no k_gemm dispatches with MFMA counters")
+
+    def mean(counter):
+        return float(np.mean([per[counter][d][0] for d in ids]))
+    gui = mean("GRBM_GUI_ACTIVE")
+    dur_ns = float(np.mean([per["GRBM_GUI_ACTIVE"][d][1] for d in ids]))
+    busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    rows = [
+        ("k_gemm dispatches", f"{len(ids)}"),
+        ("dispatch duration (kernel trace, under counters)", f"{dur_ns / 1e3:.2f} us"),
+        ("GRBM_GUI_ACTIVE, busiest XCD", f"{gui:.0f} cycles ({gui / dur_ns:.2f} GHz over the duration)"),
+        ("SQ_VALU_MFMA_BUSY_CYCLES, sum over SIMDs", f"{busy:.0f}"),
+        ("**MFMA utilisation** = busy / (1024 SIMDs x GUI_ACTIVE)", f"**{100 * busy / (SIMDS * gui):.1f} %**"),
+        ("SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512", f"{mops * 512:.4g} flop (2 M N K = {flops_per_call:.4g})"),
+        ("SQ_INSTS_MFMA", f"{mean('SQ_INSTS_MFMA'):.0f}"),
+        ("SQ_INSTS_VALU (includes the MFMAs)", f"{mean('SQ_INSTS_VALU'):.0f}"),
+        ("SQ_VALU_MFMA_COEXEC_CYCLES / busy", f"{100 * mean('SQ_VALU_MFMA_COEXEC_CYCLES') / busy:.1f} %"),
+        ("SQ_BUSY_CU_CYCLES / (256 CUs x GUI_ACTIVE): CUs holding work", f"{100 * mean('SQ_BUSY_CU_CYCLES') / (256 * gui):.1f} %"),
+        ("bf16 flop/s over the duration", f"{flops_per_call / (dur_ns * 1e-9) / 1e12:.1f} TFLOP/s "
+                                           f"({100 * flops_per_call / (dur_ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.1f} % "
+                                           f"of {PEAK_BF16_TFLOPS:.0f})"),
+    ]
+    text = ["# rocprofv3 MFMA counters: k_gemm", "",
+            "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+            "| quantity | value |", "|---|---|"]
+    text += [f"| {a} | {b} |" for a, b in rows]
+    return "\n".join(text) + "\n"
 
 
 def summarize_trace(path, command):
@@ -524,19 +588,30 @@ def measure_workloads(stack, calls):
                           {"mismatches": int(counts[0]), "out_of_cell": int(counts[1])}))
     del pool
 
-    # Batched GEMM on MFMA: M = 256 tokens, K = 4096, N = 14336, default mix
+    out.append(gemm_workload(vbq, calls))
+    return out
+
+
+def gemm_workload(vbq, calls):
+    """The batched GEMM on MFMA: M = 256 tokens, K = 4096, N = 14336, default
+    width mix; one timed line."""
+    import torch
+
+    import synth
+    dev = torch.device("cuda")
     proj = synth.C4.projs[0]
     M = synth.C4.gemm_m
-    pm, _, key = packed(4, 0, 0, proj)
+    key = synth.proj_key(4, 0, 0)
+    widths = synth.widths(synth.SEED, key, proj.n, proj.k // 64, proj.mix)
+    pm = vbq.vbq_pack(torch.from_numpy(synth.weights(synth.SEED, key, proj.n, proj.k)).to(dev), widths)
     xb = torch.from_numpy(synth.x_bf16(synth.SEED, key, M, proj.k).view(np.int16)).to(dev).view(torch.bfloat16)
     yg = torch.empty(M, proj.n, dtype=torch.float32, device=dev)
     us = _events_time(lambda i: vbq.vbq_gemm(pm, xb, out=yg), calls)
     flops = 2.0 * M * proj.n * proj.k
     tf = flops / (us * 1e-6) / 1e12
-    out.append(dict(workload=f"batched GEMM M={M} K={proj.k} N={proj.n} (bf16 MFMA)", us_per_call=round(us, 3),
-                    tflop_per_s=round(tf, 1), roofline_frac=round(tf / PEAK_BF16_TFLOPS, 4), bound="mfma",
-                    peak_tflop_per_s=PEAK_BF16_TFLOPS, flops=flops))
-    return out
+    return dict(workload=f"batched GEMM M={M} K={proj.k} N={proj.n} (bf16 MFMA)", us_per_call=round(us, 3),
+                tflop_per_s=round(tf, 1), roofline_frac=round(tf / PEAK_BF16_TFLOPS, 4), bound="mfma",
+                peak_tflop_per_s=PEAK_BF16_TFLOPS, flops=flops, M=M, K=proj.k, N=proj.n)
 
 
 def cpu_baseline(stack, budget_s):
@@ -605,12 +680,20 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="RESULTS")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_RESULTS", "WRITE_RESULTS"))
+    ap.add_argument("--summarize-mfma", metavar="RESULTS", help="MFMA counters of a --gemm-only run")
+    ap.add_argument("--gemm-only", action="store_true", help="time only the batched GEMM and print its line")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--out", help="summary file to write")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
         text = summarize_trace(args.summarize_trace, args.command)
+        open(args.out, "w").write(text) if args.out else sys.stdout.write(text)
+        return 0
+    if args.summarize_mfma:
+        import synth
+        p = synth.C4.projs[0]
+        text = summarize_mfma(args.summarize_mfma, args.command, 2.0 * synth.C4.gemm_m * p.n * p.k)
         open(args.out, "w").write(text) if args.out else sys.stdout.write(text)
         return 0
     if args.summarize_pmc:
@@ -633,6 +716,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.gemm_only:
+        import packed_decode_gemv_amd as vbq
+        print(json.dumps(gemm_workload(vbq, args.workload_calls)), flush=True)
+        return 0
     log(f"building the 9B-class stack: {args.layers} layers + LM head, batch {args.batch}")
     stack = Stack(args.layers, args.batch)
     stack.check_packed()
