@@ -7,24 +7,30 @@
 // contracted on MFMA with fp32 accumulation:
 //   y[m][n] = sum_k x[m][k] * bf16(fma(s, q, o))      (x bfloat16; fma rounds s*q + o once)
 //
-// A workgroup owns 128 tokens x 128 weight rows (8 row-tiles) of y and walks
-// K one 64-weight group at a time. Four producer wavefronts load the codes
-// and decode the weights; four consumer wavefronts copy x into an LDS ring
-// with buffer-to-LDS loads and run the MFMAs. Per group the workgroup stages
-// x[128 tokens][64] (rows XOR-swizzled by 16-byte column) and the 128 rows'
-// decoded weights W[128 rows][64] in LDS (bf16, rows padded to 72 elements so
+// A workgroup owns 256 tokens x 64 weight rows (4 row-tiles) of y and walks K
+// one 64-weight group at a time, so at up to 256 tokens every weight is
+// decoded once. Four producer wavefronts load the codes and decode the
+// weights; four consumer wavefronts copy x into an LDS ring with
+// buffer-to-LDS loads and run the MFMAs. Per group the workgroup stages
+// x[256 tokens][64] (rows XOR-swizzled by 16-byte column) and the 64 rows'
+// decoded weights W[64 rows][64] in LDS (bf16, rows padded to 72 elements so
 // the 16-byte operand reads of 16 consecutive lanes hit disjoint banks), and
 // each consumer wavefront runs 2 x 2 v_mfma_f32_32x32x16_bf16 tiles over the
-// group: 64 tokens x 64 rows.
+// group: its 64 tokens x the 64 rows.
 //
 // Finding a row's record for a given k-group: the layout keeps a tile's
 // records by width class, then (row, k-group). At every k-tile the workgroup
 // reads the meta of all its records once and builds, per k-group, the list of
-// its 128 rows' records grouped by width class (LDS, 64 KiB). The decode of a
-// group then gives lane pairs consecutive entries of that list, so a
-// wavefront decodes one or two widths.
+// its 64 rows' records grouped by width class (LDS, 32 KiB). The decode of a
+// group then gives four consecutive lanes one entry of that list (a quarter
+// of the record each, 16 codes), so a wavefront decodes one or two widths.
+// A quarter decodes without per-code conversions where the width is small:
+// a 1- or 2-bit record has only 2 or 4 distinct weights, computed once as
+// bf16(fma(s, q, o)) and looked up per code pair with a byte permute; 4- and
+// 8-bit codes are spread to bytes and converted with the byte-to-float
+// conversions.
 //
-// Producers load groups into registers three ahead of the one being
+// Producers load groups into registers four ahead of the one being
 // multiplied (covering the load latency) and decode into the other half of
 // double-buffered LDS while the consumers run the MFMAs.
 #include <atomic>
@@ -38,8 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;              // tokens per workgroup
-constexpr int kBN = 128;              // weight rows per workgroup
+constexpr int kBM = 256;              // tokens per workgroup
+constexpr int kBN = 64;               // weight rows per workgroup
 constexpr int kRowTilesPerWg = kBN / kTile;
 constexpr int kStride = 72;           // bf16 elements per LDS row
 constexpr int kThreads = 512;           // 4 producer + 4 consumer wavefronts
@@ -63,6 +69,8 @@ struct GemmSmem {
   __bf16 ws[2][kBN][kStride];         // decoded weights, double-buffered
   uint8_t xs[kXSlots][kBM * kXRow];   // x rows of 128 bytes, 16-byte columns swizzled
 };
+
+static_assert(sizeof(GemmSmem) <= 160 * 1024, "LDS of one workgroup");
 
 // x tile of one group in LDS: token row R at R * 128 bytes, its 16-byte column
 // c at position c ^ ((R >> 1) & 7). Sixteen consecutive rows read at one
@@ -90,73 +98,69 @@ __device__ inline void record_offsets(int c, uint32_t idx, uint32_t n_c, uint32_
 
 // Builds the per-k-group record lists of k-tile kt for row-tiles
 // [rt0, rt0 + nrt). Offsets are relative to the first byte of tile (kt, rt0).
-// Every thread owns up to 4 records of each of the 8 tiles; all their meta and
+// Every thread owns up to 2 records of each of the 4 tiles; all their meta and
 // scale/offset loads are issued together (two memory round trips in all),
 // then the lists are built in LDS: count per (k-group, class), turn counts
 // into starts, place.
-constexpr int kRecPerThread = kTile * kTileGroups / kThreads;   // 4 per tile
+constexpr int kRecPerThread = kTile * kTileGroups / kThreads;   // 2 per tile
 
 __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs& a, GemmSmem& S, int kt, int rt0, int nrt,
                                                                   uint32_t base16, int tid) {
-  constexpr int kHalf = kRowTilesPerWg / 2;
   for (int i = tid; i < kTileGroups * 4; i += kThreads) (&S.cnt[0][0])[i] = 0;
   const uint8_t* wg_bytes = a.stream + (size_t)base16 * 16u;
+  // The headers of all row-tiles are loaded before any is used (a row-tile
+  // past the matrix reads the last one's and then counts as empty).
+  uint4 hdr[kRowTilesPerWg];
+#pragma unroll
+  for (int r = 0; r < kRowTilesPerWg; ++r)
+    hdr[r] = *reinterpret_cast<const uint4*>(a.tiles + 4 * (size_t)(kt * a.RT + min(rt0 + r, a.RT - 1)));
   // per record slot: tag = codes offset / 8 | row << 17 | class << 24 | k-group << 26
   uint32_t tag[kRowTilesPerWg][kRecPerThread], sov[kRowTilesPerWg][kRecPerThread];
+  uint32_t meta[kRowTilesPerWg][kRecPerThread], co[kRowTilesPerWg][kRecPerThread];
+  uint32_t cls[kRowTilesPerWg][kRecPerThread];
   uint32_t valid = 0;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {   // four tiles at a time keeps the registers in flight bounded
-    uint4 hdr[kHalf];
+  for (int r = 0; r < kRowTilesPerWg; ++r) {
+    const uint4 h = hdr[r];
+    const bool live = r < nrt;
+    const uint32_t n[4] = {live ? h.z & 0xFFFFu : 0u, live ? h.z >> 16 : 0u, live ? h.w & 0xFFFFu : 0u,
+                           live ? h.w >> 16 : 0u};
+    const uint32_t total = n[0] + n[1] + n[2] + n[3];
+    uint32_t seg[4];
+    seg[0] = (h.y - base16) * 16u;   // tile start, relative
+    seg[1] = seg[0] + (uint32_t)seg_bytes(0, n[0]);
+    seg[2] = seg[1] + (uint32_t)seg_bytes(1, n[1]);
+    seg[3] = seg[2] + (uint32_t)seg_bytes(2, n[2]);
 #pragma unroll
-    for (int rr = 0; rr < kHalf; ++rr) {
-      const int r = hh * kHalf + rr;
-      hdr[rr] = r < nrt ? *reinterpret_cast<const uint4*>(a.tiles + 4 * (size_t)(kt * a.RT + rt0 + r))
-                        : make_uint4(0, 0, 0, 0);
-    }
-    uint32_t meta[kHalf][kRecPerThread], co[kHalf][kRecPerThread], cls[kHalf][kRecPerThread];
-#pragma unroll
-    for (int rr = 0; rr < kHalf; ++rr) {
-      const int r = hh * kHalf + rr;
-      const uint4 h = hdr[rr];
-      const uint32_t n[4] = {h.z & 0xFFFFu, h.z >> 16, h.w & 0xFFFFu, h.w >> 16};
-      const uint32_t total = n[0] + n[1] + n[2] + n[3];
-      uint32_t seg[4];
-      seg[0] = (h.y - base16) * 16u;   // tile start, relative
-      seg[1] = seg[0] + (uint32_t)seg_bytes(0, n[0]);
-      seg[2] = seg[1] + (uint32_t)seg_bytes(1, n[1]);
-      seg[3] = seg[2] + (uint32_t)seg_bytes(2, n[2]);
-#pragma unroll
-      for (int it = 0; it < kRecPerThread; ++it) {
-        // every slot issues its two loads, a slot without a record from the
-        // workgroup's first byte (always inside the stream; a row-tile past
-        // the matrix has no header to take a position from), and nothing
-        // reads them before all are issued
-        const uint32_t i = (uint32_t)(tid + it * kThreads);
-        const bool has = i < total;
-        int c = 0;
-        uint32_t idx = has ? i : 0u;
-        while (c < 3 && idx >= n[c]) {
-          idx -= n[c];
-          ++c;
-        }
-        uint32_t so = 0, mo = 0;
-        co[rr][it] = 0;
-        if (has) record_offsets(c, idx, n[c], seg[c], co[rr][it], so, mo);
-        meta[rr][it] = *reinterpret_cast<const uint16_t*>(wg_bytes + mo);
-        sov[r][it] = *reinterpret_cast<const uint32_t*>(wg_bytes + so);
-        cls[rr][it] = (uint32_t)c;
-        valid |= has ? 1u << (r * kRecPerThread + it) : 0u;
+    for (int it = 0; it < kRecPerThread; ++it) {
+      // every slot issues its two loads, a slot without a record from the
+      // workgroup's first byte (always inside the stream), and nothing reads
+      // them before all are issued
+      const uint32_t i = (uint32_t)(tid + it * kThreads);
+      const bool has = i < total;
+      int c = 0;
+      uint32_t idx = has ? i : 0u;
+      while (c < 3 && idx >= n[c]) {
+        idx -= n[c];
+        ++c;
       }
+      uint32_t so = 0, mo = 0;
+      co[r][it] = 0;
+      if (has) record_offsets(c, idx, n[c], seg[c], co[r][it], so, mo);
+      meta[r][it] = *reinterpret_cast<const uint16_t*>(wg_bytes + mo);
+      sov[r][it] = *reinterpret_cast<const uint32_t*>(wg_bytes + so);
+      cls[r][it] = (uint32_t)c;
+      valid |= has ? 1u << (r * kRecPerThread + it) : 0u;
     }
-#pragma unroll
-    for (int rr = 0; rr < kHalf; ++rr)
-#pragma unroll
-      for (int it = 0; it < kRecPerThread; ++it) {
-        const uint32_t mt = meta[rr][it];
-        const uint32_t row = (uint32_t)(hh * kHalf + rr) * kTile + (mt & 15u);
-        tag[hh * kHalf + rr][it] = (co[rr][it] >> 3) | (row << 17) | (cls[rr][it] << 24) | (((mt >> 4) & 63u) << 26);
-      }
   }
+#pragma unroll
+  for (int r = 0; r < kRowTilesPerWg; ++r)
+#pragma unroll
+    for (int it = 0; it < kRecPerThread; ++it) {
+      const uint32_t mt = meta[r][it];
+      const uint32_t row = (uint32_t)r * kTile + (mt & 15u);
+      tag[r][it] = (co[r][it] >> 3) | (row << 17) | (cls[r][it] << 24) | (((mt >> 4) & 63u) << 26);
+    }
   gemm_barrier();   // counters zeroed
 #pragma unroll
   for (int r = 0; r < kRowTilesPerWg; ++r)
@@ -191,33 +195,40 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
   gemm_barrier();
 }
 
-// The half (32 codes) of one record a lane decodes, as loaded from HBM.
+// The quarter (16 codes) of one record a lane decodes, as loaded from HBM.
 struct CodeRegs {
-  uint4 lo, hi;       // up to 8 words
+  uint4 v;            // the 16-byte aligned window holding the quarter's code words
   uint32_t sov;       // scale | offset << 16
-  int32_t row;        // row within the workgroup, or -1
-  int32_t c;          // width class
+  uint32_t info;      // row | class << 6 | first word in v << 8 | valid << 10
 };
 
-// Every thread issues the same two 16-byte loads for every group, whatever the
+// Every thread issues the same 16-byte load for every group, whatever the
 // width (and also for rows past N, from the workgroup's first byte), so that
 // the compiler's load-count waits are exact: a wait for an older stage never
-// has to assume fewer loads in flight and drain the newer ones. Reading 32
-// bytes from a record's half stays inside its block: the scale/offset and meta
-// areas (at least 32 bytes) follow the codes.
-__device__ inline void load_codes(const GemmArgs& a, const GemmSmem& S, uint32_t base16, int kgl, int nvalid,
-                                  int tid, CodeRegs& R) {
-  const int slot = tid >> 1, half = tid & 1;
-  uint2 e = make_uint2(0, 0);
-  if (slot < nvalid) e = S.ent[kgl][slot];
-  R.c = (int)(e.x >> 24) & 3;
-  R.row = slot < nvalid ? (int)(e.x >> 17) & 127 : -1;
+// has to assume fewer loads in flight and drain the newer ones.
+//
+// Quarter Q of a record (codes 16Q .. 16Q + 15) lies in half Q / 2, pairs
+// 8 (Q % 2) .. + 7 of it. Its code words start at record word Q * b / 2 for
+// b >= 2 (b / 2 words); a 1-bit quarter is bits 8 (Q % 2) + [0, 8) and
+// 16 + 8 (Q % 2) + [0, 8) of word Q / 2. Records are 8 << class bytes and
+// blocks 16-byte aligned, so those words never cross a 16-byte boundary, and
+// the window stays inside the record's block (its scale/offset and meta
+// areas follow the codes).
+__device__ inline uint2 list_entry(const GemmSmem& S, int kgl, int nvalid, int tid) {
+  const int slot = tid >> 2;
+  return slot < nvalid ? S.ent[kgl][slot] : make_uint2(0, 0);
+}
+
+__device__ inline void load_codes(const GemmArgs& a, uint32_t base16, uint2 e, int nvalid, int tid, CodeRegs& R) {
+  const int slot = tid >> 2, qtr = tid & 3;
+  const bool has = slot < nvalid;
+  const uint32_t c = (e.x >> 24) & 3u;
+  const uint32_t wi = c == 0 ? (uint32_t)(qtr >> 1) : (uint32_t)qtr << (c - 1);
+  const uint32_t byte = ((e.x & 0x1FFFFu) << 3) + 4u * wi;
   R.sov = e.y;
-  // half h of a record of width b is its words [h*b, h*b + b)
-  const uint32_t off = slot < nvalid ? ((e.x & 0x1FFFFu) << 3) + (uint32_t)half * (4u << R.c) : 0u;
-  const uint8_t* p = a.stream + (size_t)base16 * 16u + off;
-  R.lo = *reinterpret_cast<const uint4*>(p);
-  R.hi = *reinterpret_cast<const uint4*>(p + 16);
+  R.info = has ? (((e.x >> 17) & 63u) | (c << 6) | (((byte >> 2) & 3u) << 8) | (1u << 10)) : 0u;
+  const uint32_t off = has ? (byte & ~15u) : 0u;
+  R.v = *reinterpret_cast<const uint4*>(a.stream + (size_t)base16 * 16u + off);
 }
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
@@ -225,51 +236,82 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Word i (< 8) of the loaded half.
-__device__ inline uint32_t word(const CodeRegs& R, int i) {
-  const uint4& v = i < 4 ? R.lo : R.hi;
-  const int j = i & 3;
+__device__ inline uint32_t word_at(const uint4& v, uint32_t j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// Decodes 32 codes of width 2^C into 16 bf16 pairs (natural k order): pair p
-// of the half sits in word p / H, code 2p at bit (p % H) * b, code 2p+1 at
-// bit 16 + (p % H) * b.
+// 1- and 2-bit quarters: the 2 or 4 weights bf16(fma(s, q, o)) of the record
+// form a table of bf16 in bytes 0..7 of {hi, lo}; the pair of codes (e, o) of
+// pair p, at bits p << C and 16 + (p << C) of the quarter's word, selects
+// bytes {2e, 2e + 1, 2o, 2o + 1} of it.
 template <int C>
-__device__ inline void decode_half(const CodeRegs& R, float s, float o, uint32_t out[16]) {
-  constexpr int B = 1 << C, H = 16 / B;
-  constexpr uint32_t L = (1u << B) - 1u;
+__device__ inline void decode_table(const CodeRegs& R, uint32_t j, int qtr, float s, float o, uint32_t out[8]) {
+  const uint32_t w = word_at(R.v, j);
+  const uint32_t lo = pack_bf16(__builtin_fmaf(s, 0.0f, o), __builtin_fmaf(s, 1.0f, o));
+  const uint32_t hi = C == 1 ? pack_bf16(__builtin_fmaf(s, 2.0f, o), __builtin_fmaf(s, 3.0f, o)) : 0u;
+  constexpr uint32_t M = C == 0 ? 0x00010001u : 0x00030003u;
+  const uint32_t ws = C == 0 ? w >> (8 * (qtr & 1)) : w;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const uint32_t w = word(R, p / H);
-    const int sh = (p % H) * B;
-    const float q0 = (float)((w >> sh) & L);
-    const float q1 = (float)((w >> (16 + sh)) & L);
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t t = (ws >> (p << C)) & M;
+    out[p] = __builtin_amdgcn_perm(hi, lo, t * 0x202u + 0x01000100u);
+  }
+}
+
+// 4-bit quarter: two words of four pairs, pair m of a word holding its even
+// code at bit 4m and its odd code at bit 16 + 4m; masking the word and the
+// word shifted by 4 with 0x0F0F0F0F puts every code in a byte of its own.
+__device__ inline void decode_4bit(const CodeRegs& R, uint32_t j, float s, float o, uint32_t out[8]) {
+  const uint32_t w[2] = {j == 0 ? R.v.x : R.v.z, j == 0 ? R.v.y : R.v.w};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t e = w[k] & 0x0F0F0F0Fu, d = (w[k] >> 4) & 0x0F0F0F0Fu;
+    // pair 0: bytes 0, 2 of e; pair 1: of d; pair 2: bytes 1, 3 of e; pair 3: of d
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t src = (m & 1) ? d : e;
+      const int b0 = (m >> 1) * 8;
+      const float q0 = (float)((src >> b0) & 0xFFu), q1 = (float)((src >> (16 + b0)) & 0xFFu);
+      out[4 * k + m] = pack_bf16(__builtin_fmaf(s, q0, o), __builtin_fmaf(s, q1, o));
+    }
+  }
+}
+
+// 8-bit quarter: four words of two pairs, pair m of a word at bytes m and 2 + m.
+__device__ inline void decode_8bit(const CodeRegs& R, float s, float o, uint32_t out[8]) {
+  const uint32_t w[4] = {R.v.x, R.v.y, R.v.z, R.v.w};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t x = w[p >> 1];
+    const int b0 = (p & 1) * 8;
+    const float q0 = (float)((x >> b0) & 0xFFu), q1 = (float)((x >> (16 + b0)) & 0xFFu);
     out[p] = pack_bf16(__builtin_fmaf(s, q0, o), __builtin_fmaf(s, q1, o));
   }
 }
 
 __device__ inline void store_weights(GemmSmem& S, int buf, const CodeRegs& R, int tid) {
-  if (R.row < 0) return;
+  if (!((R.info >> 10) & 1u)) return;
+  const int qtr = tid & 3;
+  const uint32_t row = R.info & 63u, c = (R.info >> 6) & 3u, j = (R.info >> 8) & 3u;
   const float s = __half2float(__ushort_as_half((unsigned short)(R.sov & 0xFFFFu)));
   const float o = __half2float(__ushort_as_half((unsigned short)(R.sov >> 16)));
-  uint32_t out[16];
-  switch (R.c) {
-    case 0: decode_half<0>(R, s, o, out); break;
-    case 1: decode_half<1>(R, s, o, out); break;
-    case 2: decode_half<2>(R, s, o, out); break;
-    default: decode_half<3>(R, s, o, out); break;
+  uint32_t out[8];
+  switch (c) {
+    case 0: decode_table<0>(R, j, qtr, s, o, out); break;
+    case 1: decode_table<1>(R, j, qtr, s, o, out); break;
+    case 2: decode_4bit(R, j, s, o, out); break;
+    default: decode_8bit(R, s, o, out); break;
   }
-  uint4* dst = reinterpret_cast<uint4*>(&S.ws[buf][R.row][32 * (tid & 1)]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  uint4* dst = reinterpret_cast<uint4*>(&S.ws[buf][row][16 * qtr]);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-// One consumer wavefront copies the 32 token rows [r0, r0 + 32) of group g
-// into slot `slot`: four copies of 1 KiB (eight rows each), lane l taking
+// One consumer wavefront copies the 64 token rows [r0, r0 + 64) of group g
+// into slot `slot`: eight copies of 1 KiB (eight rows each), lane l taking
 // row r0 + 8i + l / 8, stored column l % 8. Rows past M read as zeros (the
 // buffer ends at M rows).
-constexpr int kXCopies = 4;   // copies per consumer wavefront and group
+constexpr int kXCopies = 8;   // copies per consumer wavefront and group
 
 __device__ inline void copy_x(const GemmArgs& a, const u32x4& rsrc, uint32_t slot_lds, int m0, int r0, int g,
                               int lane) {
@@ -311,13 +353,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int cw = wave - kProducers / kWave;   // consumer wavefront 0..3
-  const int wm = (cw >> 1) & 1, wn = cw & 1;
+  const int wm = cw;   // tokens [64 wm, 64 wm + 64) of the workgroup, all its rows
   // Per k-tile: build the record lists, then run the pipeline over its
   // groups, one barrier per group:
-  //  - producers hold the codes of groups g+1..g+3 in three register stages:
-  //    they load group g + 3 and decode group g + 1 into the free weight
+  //  - producers hold the codes of groups g+1..g+4 in four register stages:
+  //    they load group g + 4 and decode group g + 1 into the free weight
   //    buffer while the consumers multiply group g;
-  //  - each consumer wavefront also copies a quarter of x of group g + 2
+  //  - each consumer wavefront also copies its quarter of x of group g + 2
   //    into the free x slot (buffer-to-LDS, no registers) and, before the
   //    barrier, waits until its copy of group g + 1 has landed.
   // Producers issue only register loads and consumers only copies, so the
@@ -325,8 +367,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   // are waited for explicitly. Every step issues the same loads (group
   // indices clamped to the k-tile's last), steps past the end only keep the
   // barrier schedule.
-  const bool x_loader = !producer;
-  const int xr0 = cw * 32;   // this wavefront's x rows
+  const int xr0 = cw * 64;   // this wavefront's x rows
   const u32x4 xrsrc = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.G * kXRow);
   const uint32_t xs_lds = lds_addr(&S.xs[0][0]);
   const int KT = (a.G + kTileGroups - 1) / kTileGroups;
@@ -334,29 +375,46 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
     const int g0 = kt * kTileGroups, g1 = min(a.G, g0 + kTileGroups);
     const uint32_t base16 = a.tiles[4 * (size_t)(kt * a.RT + rt0) + 1];
     build_index(a, S, kt, rt0, nrt, base16, tid);
-    CodeRegs st0, st1, st2;
+    // The two roles run loops of their own with the same barrier schedule:
+    // in one shared loop body the compiler merges their load-count state and
+    // waits for every load in flight where a register of one role's load is
+    // reused by the other.
     if (producer) {
-      load_codes(a, S, base16, g0 & (kTileGroups - 1), nvalid, tid, st0);
-      load_codes(a, S, base16, min(g0 + 1, g1 - 1) & (kTileGroups - 1), nvalid, tid, st1);
-      load_codes(a, S, base16, min(g0 + 2, g1 - 1) & (kTileGroups - 1), nvalid, tid, st2);
+      // The list entry of a group is read from LDS one step before its codes
+      // are loaded, so the load goes out right after the barrier.
+      auto entry = [&](int g) { return list_entry(S, min(g, g1 - 1) & (kTileGroups - 1), nvalid, tid); };
+      CodeRegs st0, st1, st2, st3;
+      load_codes(a, base16, entry(g0), nvalid, tid, st0);
+      load_codes(a, base16, entry(g0 + 1), nvalid, tid, st1);
+      load_codes(a, base16, entry(g0 + 2), nvalid, tid, st2);
+      load_codes(a, base16, entry(g0 + 3), nvalid, tid, st3);
+      uint2 ahead = entry(g0 + 4);
       store_weights(S, g0 & 1, st0, tid);
-    } else if (x_loader) {
+      gemm_barrier();
+      auto step = [&](int g, CodeRegs& reload, const CodeRegs& next) {
+        load_codes(a, base16, ahead, nvalid, tid, reload);   // group g + 4
+        ahead = entry(g + 5);
+        if (g + 1 < g1) store_weights(S, (g & 1) ^ 1, next, tid);
+        gemm_barrier();
+      };
+      for (int g = g0; g < g1; g += 4) {
+        step(g, st0, st1);
+        step(g + 1, st1, st2);
+        step(g + 2, st2, st3);
+        step(g + 3, st3, st0);
+      }
+    } else {
       copy_x(a, xrsrc, xs_lds + (uint32_t)(g0 % kXSlots) * kBM * kXRow, m0, xr0, g0, lane);
       copy_x(a, xrsrc, xs_lds + (uint32_t)((g0 + 1) % kXSlots) * kBM * kXRow, m0, xr0, min(g0 + 1, g1 - 1),
              lane);
       __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g0 landed
-    }
-    gemm_barrier();
-    auto step = [&](int g, CodeRegs& reload, const CodeRegs& next) {
-      const int buf = g & 1;
-      if (producer) {
-        load_codes(a, S, base16, min(g + 3, g1 - 1) & (kTileGroups - 1), nvalid, tid, reload);
-        if (g + 1 < g1) store_weights(S, buf ^ 1, next, tid);
-      } else {
+      gemm_barrier();
+      auto step = [&](int g) {
         if (g < g1) {
           // All operands of the group are read from LDS before the first
           // MFMA, so the wavefront waits for LDS once per group, not per step.
           const uint8_t* xslot = S.xs[g % kXSlots];
+          const int buf = g & 1;
           bf16x8 av[4][2], bv[4][2];
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
@@ -368,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               bv[kk][j] = *reinterpret_cast<const bf16x8*>(
-                  &S.ws[buf][wn * 64 + 32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+                  &S.ws[buf][32 * j + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
           }
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
@@ -381,28 +439,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
         // The copy of group g + 2 goes out after the MFMAs are issued, so a
         // copy that waits for the memory pipeline does not hold them back;
         // its slot was last read in the previous step, before the barrier.
-        if (x_loader)
-          copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
-                 lane);
-        if (x_loader) __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g + 1 landed
+        copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
+               lane);
+        __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g + 1 landed
+        gemm_barrier();
+      };
+      for (int g = g0; g < g1; g += 4) {
+        step(g);
+        step(g + 1);
+        step(g + 2);
+        step(g + 3);
       }
-      gemm_barrier();
-    };
-    for (int g = g0; g < g1; g += 3) {
-      step(g, st0, st1);
-      step(g + 1, st1, st2);
-      step(g + 2, st2, st0);
+      __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));   // no copy left in flight
     }
-    if (x_loader) __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));   // no copy left in flight
   }
   if (producer) return;
 
-  // acc[i][j][r]: token wm*64 + 32i + 8(r/4) + 4(lane/32) + r%4, row wn*64 + 32j + lane%32
+  // acc[i][j][r]: token wm*64 + 32i + 8(r/4) + 4(lane/32) + r%4, row 32j + lane%32
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = rt0 * kTile + wn * 64 + 32 * j + (lane & 31);
+      const int n = rt0 * kTile + 32 * j + (lane & 31);
       if (n >= a.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
