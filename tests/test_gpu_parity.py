@@ -348,6 +348,25 @@ def test_requant_verify_near_half_cells(vbq):
     assert np.array_equal(q_rq, ref[3])
 
 
+def test_requant_verify_calls_independent(vbq):
+    """Each call reports only its own counts: a failing check, then a clean
+    one, then the failing one again on the same stream, in both modes."""
+    import torch
+    N, K = 48, 2048
+    W, widths, q, s, o, resid, _ = _cell_inputs(N, K, seed=21)
+    pm = vbq.vbq_pack(_t(W), widths)
+    bad = resid.copy()
+    sf = oracle.f64_from_f16(np.repeat(s, 64, axis=1))
+    for (n, k) in [(0, 0), (20, 1500), (47, 2047)]:
+        bad[n, k] = oracle.f16_from_f64(np.array([0.7 * sf[n, k]]))[0]
+    ref_bad = oracle.requant_verify(q, s, o, widths, bad)[:3]
+    assert ref_bad[1] == 3
+    for _ in range(2):
+        assert _verify_both(vbq, pm, _t(bad, torch.float16))[:3] == ref_bad
+        assert _verify_both(vbq, pm, _t(resid, torch.float16))[:3] == (0, 0, 2 ** 64 - 1)
+    torch.cuda.synchronize()
+
+
 def test_requant_verify_flipped_bit(vbq):
     """A served artifact with one code bit flipped: the check re-quantises
     against the artifact it is given, so it passes, and the re-quantised
