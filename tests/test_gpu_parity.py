@@ -91,6 +91,35 @@ def test_gemv_parity(vbq, case):
         assert rel_l2(y[b], ref[b]) <= TOL
 
 
+@pytest.mark.parametrize("width", [1, 2, 4, 8])
+def test_single_width_with_constant_groups(vbq, width):
+    """Every group of one width, so that class's full and partial blocks make
+    up the whole stream, and rows past a tile (N = 37); three constant groups
+    have scale 0, so every weight there equals the offset (one is all zero).
+    Layout bit-exact; GEMV and GEMM within tolerance of the oracle."""
+    import torch
+    from test_gpu_gemm import check_gemm
+    N, K, B = 37, 64 * 9, 2
+    r = np.random.default_rng(100 + width)
+    widths = np.full((N, K // 64), width, np.uint8)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    for n, g, v in [(0, 0, 0.01), (17, 4, -0.03), (36, 8, 0.0)]:
+        W[n, 64 * g:64 * (g + 1)] = v
+    print(f"case single width {width}: {N}x{K} B={B}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    layout_equal(pm, oracle.pack(W, widths))
+    q, s, o = oracle.quantize_matrix(W, widths)
+    assert all(s[n, g] == 0 for n, g in [(0, 0), (17, 4), (36, 8)])
+    x = r.standard_normal((B, K)).astype(np.float16).view(np.uint16)
+    y = vbq.vbq_gemv(pm, _t(x, torch.float16)).cpu().numpy()
+    ref = oracle.gemv(q, s, o, x)
+    for b in range(B):
+        assert rel_l2(y[b], ref[b]) <= TOL
+    xb = synth.x_bf16(7, (width,), 70, K)
+    yg = vbq.vbq_gemm(pm, _t(xb, torch.bfloat16)).cpu().numpy()
+    check_gemm(yg, q, s, o, xb)
+
+
 def test_gemv_exact_integer(vbq):
     """All groups 8-bit with integer weights (0 and 255 in every group) and small
     integer x: scale 1, offset 0, every partial sum an exact integer in fp32,
