@@ -71,7 +71,8 @@ def test_pack_bit_exact(vbq, shape):
 
 
 GEMV_CASES = [(1, 64, 1), (15, 128, 1), (17, 320, 2), (100, 448, 3), (768, 768, 1), (300, 64 * 70, 4),
-              (40, 14336, 1), (64, 4096, 8), (33, 2048, 5), (48, 1024, 6), (20, 512, 7)]
+              (40, 14336, 1), (64, 4096, 8), (33, 2048, 5), (48, 1024, 6), (20, 512, 7),
+              (40, 8192, 8), (130, 4160, 8)]   # the largest batch with split K (the last: a 1-group k-tile)
 
 
 @pytest.mark.parametrize("case", GEMV_CASES, ids=[f"{n}x{k}b{b}" for n, k, b in GEMV_CASES])
@@ -199,12 +200,13 @@ def test_split_k_repeatable_across_streams(vbq):
             assert torch.equal(o, first), "split-K GEMV differs between calls"
 
 
-def test_split_k_batched_mix(vbq):
+@pytest.mark.parametrize("B", [1, 4])
+def test_split_k_batched_mix(vbq, B):
     """A batched launch mixing split (K > 4096) and unsplit matrices."""
     import torch
     mats, refs = [], []
     for i, (N, K) in enumerate([(4096, 14336), (512, 4096), (1024, 8192), (64, 4160)]):
-        W, widths, x = rand_case(N, K, seed=90 + i, B=1)
+        W, widths, x = rand_case(N, K, seed=90 + i, B=B)
         q, s, o = oracle.quantize_matrix(W, widths)
         mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
         refs.append(oracle.gemv(q, s, o, x))
