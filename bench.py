@@ -386,6 +386,37 @@ def summarize_trace(path, command):
     return "\n".join(lines) + "\n"
 
 
+def summarize_counters(path, kernel, command):
+    """Markdown table of every counter in one --pmc pass, averaged over the
+    dispatches of `kernel` (summed over a counter's instances; GRBM_GUI_ACTIVE
+    taken from the busiest XCD), split by launch shape (workgroups)."""
+    import collections
+    import sqlite3
+    shape = {}
+    for f in _db_files(path):
+        c = sqlite3.connect(f)
+        for did, grid, wg in c.execute("select dispatch_id, grid_size, workgroup_size from counters_collection "
+                                       "where kernel_name like ? group by dispatch_id", (f"%{kernel}%",)):
+            shape[did] = grid // max(wg, 1)
+        names = [r[0] for r in c.execute("select distinct counter_name from counters_collection")]
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for n in names:
+        if n == "GRBM_GUI_ACTIVE":
+            rows = [(d, v) for (d, v, _) in _pmc_max_rows(path, n) if d in shape]
+        else:
+            rows = [(d, v) for (d, k, v) in _pmc_rows(path, n) if kernel in k]
+        for d, v in rows:
+            vals[shape[d]][n].append(v)
+    lines = [f"# rocprofv3 counters: {kernel}", "", "Command (from the repository root on the GPU box):", "",
+             "```", command, "```", ""]
+    for wgs in sorted(vals):
+        lines += [f"Launches of {wgs} workgroups ({len(next(iter(vals[wgs].values())))} dispatches), "
+                  "average per dispatch:", "", "| counter | value |", "|---|---|"]
+        lines += [f"| {n} | {np.mean(v):.4g} |" for n, v in sorted(vals[wgs].items())]
+        lines.append("")
+    return "\n".join(lines)
+
+
 def summarize_pmc(fetch_path, write_path):
     """HBM bytes per k_gemv dispatch from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by the reading of the calibration copy, which moves
@@ -681,6 +712,8 @@ def main(argv=None):
     ap.add_argument("--summarize-trace", metavar="RESULTS")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_RESULTS", "WRITE_RESULTS"))
     ap.add_argument("--summarize-mfma", metavar="RESULTS", help="MFMA counters of a --gemm-only run")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("RESULTS", "KERNEL"),
+                    help="every counter of a --pmc pass, averaged over one kernel's dispatches")
     ap.add_argument("--gemm-only", action="store_true", help="time only the batched GEMM and print its line")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--out", help="summary file to write")
@@ -688,6 +721,10 @@ def main(argv=None):
 
     if args.summarize_trace:
         text = summarize_trace(args.summarize_trace, args.command)
+        open(args.out, "w").write(text) if args.out else sys.stdout.write(text)
+        return 0
+    if args.summarize_counters:
+        text = summarize_counters(*args.summarize_counters, args.command)
         open(args.out, "w").write(text) if args.out else sys.stdout.write(text)
         return 0
     if args.summarize_mfma:

@@ -27,7 +27,7 @@ def _pmc_db(path, dispatches):
     c.execute("create table rocpd_kernel_dispatch (event_id integer, guid text, dispatch_id integer, "
               "start integer, end integer)")
     c.execute("create table counters_collection (dispatch_id integer, kernel_name text, counter_name text, "
-              "value real)")
+              "value real, grid_size integer, workgroup_size integer)")
     names = sorted({n for d in dispatches for n in d[4]})
     for i, n in enumerate(names):
         c.execute("insert into rocpd_info_pmc values (?, 'g', ?)", (i, n))
@@ -39,7 +39,8 @@ def _pmc_db(path, dispatches):
             for v in values:
                 c.execute("insert into rocpd_pmc_event (guid, event_id, pmc_id, value) values ('g', ?, ?, ?)",
                           (ev, names.index(n), v))
-                c.execute("insert into counters_collection values (?, ?, ?, ?)", (did, kernel, n, v))
+                c.execute("insert into counters_collection values (?, ?, ?, ?, ?, 512)",
+                          (did, kernel, n, v, 512 * (729 if did % 2 else 498)))
     c.commit()
     c.close()
 
@@ -125,3 +126,18 @@ def test_read_traffic_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.read_traffic(8, 1) is None                        # another workload
     p.write_text(json.dumps(dict(doc, kernel_source_sha="0" * 16)))
     assert bench.read_traffic(32, 1) is None                       # counters of other kernel sources
+
+
+def test_summarize_counters(tmp_path):
+    _pmc_db(str(tmp_path / "g_results.db"),
+            [(1, GEMV, 0, 10, {"SQ_INSTS_VALU": [100.0, 300.0], "GRBM_GUI_ACTIVE": [50.0, 70.0]}),
+             (2, GEMV, 0, 10, {"SQ_INSTS_VALU": [500.0], "GRBM_GUI_ACTIVE": [90.0, 80.0]}),
+             (4, GEMV, 0, 10, {"SQ_INSTS_VALU": [700.0], "GRBM_GUI_ACTIVE": [110.0]}),
+             (3, "at::native::other", 0, 10, {"SQ_INSTS_VALU": [1e9], "GRBM_GUI_ACTIVE": [1e9]})])
+    text = bench.summarize_counters(str(tmp_path), "k_gemv", "cmd")
+    assert "Launches of 498 workgroups (2 dispatches)" in text     # dispatches 2 and 4
+    assert "Launches of 729 workgroups (1 dispatches)" in text     # dispatch 1
+    part498 = text.split("Launches of 498")[1].split("Launches of 729")[0]
+    assert "| SQ_INSTS_VALU | 600 |" in part498                      # (500 + 700) / 2
+    assert "| GRBM_GUI_ACTIVE | 100 |" in part498                    # busiest XCD: (90 + 110) / 2
+    assert "| SQ_INSTS_VALU | 400 |" in text.split("Launches of 729")[1]
