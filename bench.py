@@ -356,7 +356,7 @@ def summarize_mfma(path, command, flops_per_call):
                                            f"of {PEAK_BF16_TFLOPS:.0f})"),
     ]
     text = ["# rocprofv3 MFMA counters: k_gemm", "",
-            "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+            "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
             "| quantity | value |", "|---|---|"]
     text += [f"| {a} | {b} |" for a, b in rows]
     return "\n".join(text) + "\n"
@@ -371,7 +371,7 @@ def summarize_trace(path, command):
         k = _short(name)
         key = (k, wgs, wgsize, lds, vgpr, sgpr) if "k_gemv" in k else (k, None, wgsize, lds, vgpr, sgpr)
         by[key].append(dur / 1e3)
-    lines = ["# rocprofv3 kernel trace", "", "Command (from the repository root on the GPU box):", "",
+    lines = ["# rocprofv3 kernel trace", "", "Command (from the repository root, on an MI355X):", "",
              "```", command, "```", "",
              "| kernel | workgroups | threads/WG | LDS B | VGPR | SGPR | calls | avg us | min us | max us | total us |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -407,7 +407,7 @@ def summarize_counters(path, kernel, command):
             rows = [(d, v) for (d, k, v) in _pmc_rows(path, n) if kernel in k]
         for d, v in rows:
             vals[shape[d]][n].append(v)
-    lines = [f"# rocprofv3 counters: {kernel}", "", "Command (from the repository root on the GPU box):", "",
+    lines = [f"# rocprofv3 counters: {kernel}", "", "Command (from the repository root, on an MI355X):", "",
              "```", command, "```", ""]
     for wgs in sorted(vals):
         lines += [f"Launches of {wgs} workgroups ({len(next(iter(vals[wgs].values())))} dispatches), "
