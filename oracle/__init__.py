@@ -249,6 +249,20 @@ def gemv(q, s16, o16, x, resid=None, bf16: bool = False) -> np.ndarray:
     return y
 
 
+def drift_bound(s16, x) -> np.ndarray:
+    """Bound on how far an in-cell residual can move each output (page
+    "Nothing Changed but the Model: CellFill -- Bounded In-Cell Learning for
+    Bit-Identical, Revocable Updates to Quantized LLMs", section Abstract:
+    bounded drift). With every |r[n][k]| below half its group's scale,
+    |sum_k x[b][k] r[n][k]| <= sum_k |x[b][k]| s[n][g(k)] / 2; the supremum
+    over such residuals. Returns [B][N] fp64 = 0.5 * sum_g s[n][g] * sum_{k in g} |x[b][k]|."""
+    s = f64_from_f16(_c(s16, np.uint16))                       # [N][G]
+    xa = np.abs(f64_from_f16(_c(np.atleast_2d(x), np.uint16)))  # [B][K]
+    B, K = xa.shape
+    assert K == s.shape[1] * 64
+    return 0.5 * (xa.reshape(B, K // 64, 64).sum(axis=2) @ s.T)
+
+
 def f32_to_bf16(v: float) -> int:
     return int(lib().orc_f32_to_bf16(float(np.float32(v))))
 

@@ -538,6 +538,34 @@ def pin_drift_bound_and_revocation():
     assert np.array_equal(oracle.gemv(q, s, o, x, None), y0)
 
 
+def pin_drift_bound_attained():
+    """The closed-form drift bound is attained by the extremal residual
+    r = sign(x) s/2 (the supremum over residuals inside their cells): its
+    drift, computed through the GEMV, which shares no arithmetic with the
+    closed form, equals the bound for every width; in-cell residuals stay
+    below it."""
+    for b, std in ((1, 0.02), (2, 0.02), (4, 0.02), (8, 0.5)):
+        r = _rng(40 + b)
+        N, K = 12, 192
+        widths = np.full((N, K // 64), b, np.uint8)
+        W = (r.standard_normal((N, K)) * std).astype(np.float32)
+        q, s, o = oracle.quantize_matrix(W, widths)
+        s_full = oracle.f64_from_f16(np.repeat(s, 64, axis=1))
+        x = r.standard_normal((3, K)).astype(np.float16).view(np.uint16)
+        xd = oracle.f64_from_f16(x)
+        bound = oracle.drift_bound(s, x)
+        assert bound.shape == (3, N)
+        y0 = oracle.gemv(q, s, o, x)
+        for bi in range(3):
+            half = s_full / 2 * np.sign(xd[bi])[None, :]
+            r16 = oracle.f16_from_f64(half)
+            assert np.array_equal(oracle.f64_from_f16(r16), half)     # s/2 is exact in fp16 here
+            drift = oracle.gemv(q, s, o, x[bi:bi + 1], r16)[0] - y0[bi]
+            assert np.allclose(drift, bound[bi], rtol=1e-12, atol=1e-12)
+        resid = oracle.make_cell_residual(r.uniform(-0.49, 0.49, (N, K)), s)
+        assert np.all(np.abs(oracle.gemv(q, s, o, x, resid) - y0) <= bound)
+
+
 def pin_requant_verify():
     r, widths, q, s, o, s_full, resid = _cell_case(31)
     N, K = q.shape
@@ -680,7 +708,7 @@ ALL_PINS = [
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
     pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
-    pin_drift_bound_and_revocation, pin_requant_verify, pin_residual_inside_cell,
+    pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_requant_verify, pin_residual_inside_cell,
     pin_mean_bits_accounting,
     pin_abstract_storage_ratios, pin_bf16_weights, pin_layout_big_blocks,
 ]
