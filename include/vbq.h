@@ -203,6 +203,19 @@ vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, floa
 vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
                                uint32_t* requant_codes, hipStream_t stream);
 
+/* Drift bound of an in-cell update (page "Nothing Changed but the Model:
+ * CellFill -- Bounded In-Cell Learning for Bit-Identical, Revocable Updates
+ * to Quantized LLMs", section Abstract: bounded drift). For every residual
+ * with each |r[n][k]| below half its group's scale,
+ *   |y_r[b][n] - y[b][n]| = |sum_k x[b][k] r[n][k]| <= bound[b][n], where
+ *   bound[b][n] = 0.5 * sum_g s[n][g] * sum_{k in g} |x[b][k]|
+ * with s the stored fp16 scales. It is computed in binary32: the group sums
+ * in k order, then the groups in order, so repeated calls agree bit for bit.
+ * It is the supremum: r = sign(x) s/2 attains it.
+ * x: device, B x K fp16 (B = 1..8, else VBQ_ERR_UNSUPPORTED), 2-byte aligned.
+ * bound: device, B x N float32, 4-byte aligned, fully overwritten. */
+vbq_status cell_drift_bound(const vbq_matrix* m, const uint16_t* x, int32_t B, float* bound, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

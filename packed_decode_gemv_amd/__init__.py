@@ -6,7 +6,7 @@ PyTorch provides device memory and streams. There is no fallback: if the
 library is not built, importing this package raises.
 
 Function names follow the C ABI: ``vbq_pack``, ``vbq_gemv``,
-``vbq_gemv_batched``, ``vbq_gemm``, ``cell_requant_verify``.
+``vbq_gemv_batched``, ``vbq_gemm``, ``cell_requant_verify``, ``cell_drift_bound``.
 """
 from __future__ import annotations
 
@@ -46,13 +46,13 @@ class vbq_layout_sizes(C.Structure):
 
 
 EXPORTS = ("vbq_abi_version", "vbq_status_string", "vbq_pack_query", "vbq_pack", "vbq_matrix_check",
-           "vbq_gemv", "vbq_gemv_batched", "vbq_gemm", "cell_requant_verify")
+           "vbq_gemv", "vbq_gemv_batched", "vbq_gemm", "cell_requant_verify", "cell_drift_bound")
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libvbq.so is not built ({LIB_PATH}); run __graft_entry__.build() or "
-                          "python -m packed_decode_gemv_amd.build")
+                          "python packed_decode_gemv_amd/build.py")
     lib = C.CDLL(LIB_PATH)
     P, I32 = C.c_void_p, C.c_int32
     lib.vbq_abi_version.restype = C.c_int
@@ -73,6 +73,8 @@ def _load():
     lib.vbq_gemm.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P]
     lib.cell_requant_verify.restype = C.c_int
     lib.cell_requant_verify.argtypes = [C.POINTER(vbq_matrix), P, P, P, P]
+    lib.cell_drift_bound.restype = C.c_int
+    lib.cell_drift_bound.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P]
     return lib
 
 
@@ -218,3 +220,15 @@ def cell_requant_verify(pm: PackedMatrix, residual, requant_codes: bool = False,
            "cell_requant_verify")
     r = res.cpu().numpy().view(np.uint64)
     return int(r[0]), int(r[1]), int(r[2]), rq
+
+
+def cell_drift_bound(pm: PackedMatrix, x, out=None, stream=None):
+    """bound [B][N] float32 = 0.5 * sum_g s[n][g] * sum_{k in g} |x[b][k]|: no
+    residual inside its cells moves y[b][n] further."""
+    import torch
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    B = x2.shape[0]
+    if out is None:
+        out = torch.empty(B, pm.N, dtype=torch.float32, device=x.device)
+    _check(lib.cell_drift_bound(C.byref(pm.desc), _ptr(x2), B, _ptr(out), _stream(stream)), "cell_drift_bound")
+    return out

@@ -1,6 +1,8 @@
 """Builds libvbq.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m packed_decode_gemv_amd.build   (or call build()).
+Usage: python packed_decode_gemv_amd/build.py   (or call build()). It imports
+only the standard library, so it runs before the library exists; importing
+the package instead would load the library first.
 Every source is compiled each time build() runs; objects go to _build/.
 """
 from __future__ import annotations

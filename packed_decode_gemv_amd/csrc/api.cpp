@@ -332,4 +332,13 @@ vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, ui
   return from_hip(launch_verify(*m, residual, result, requant_codes, stream));
 }
 
+vbq_status cell_drift_bound(const vbq_matrix* m, const uint16_t* x, int32_t B, float* bound, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!x || !bound) return VBQ_ERR_INVALID_ARG;
+  if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
+  if (!aligned(x, 2) || !aligned(bound, 4)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_drift(*m, x, B, bound, stream));
+}
+
 }  // extern "C"

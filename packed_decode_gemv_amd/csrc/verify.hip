@@ -295,4 +295,94 @@ hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* r
   return hipGetLastError();
 }
 
+// ---- Drift bound ------------------------------------------------------------
+// bound[b][n] = 0.5 * sum_g s[n][g] * X[b][g],  X[b][g] = sum_{k in g} |x[b][k]|:
+// with every residual strictly inside half its group's scale, no output moves
+// further than this (CellFill abstract: bounded drift). One workgroup per
+// row-tile walks its k-tiles in order. Per k-tile it forms X for the tile's
+// groups (fp32, in k order); every record puts 0.5 s X[b][g] at its (row,
+// group) slot in LDS (a row has exactly one record per group); and one thread
+// per (batch row, row) adds its slots in group order, so the sum order is
+// fixed.
+constexpr int kDriftThreads = 256;
+
+template <int NB>
+__global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restrict__ tiles,
+                                                         const uint8_t* __restrict__ stream,
+                                                         const uint16_t* __restrict__ x, int N, int G, int RT,
+                                                         float* __restrict__ bound) {
+  __shared__ float X[NB][kTileGroups];
+  __shared__ float P[NB][kTile][kTileGroups + 1];
+  const int rt = (int)blockIdx.x, tid = threadIdx.x;
+  const int K = G * kGroup;
+  const int b_own = tid / kTile, r_own = tid % kTile;   // summed by this thread while tid < NB * 16
+  float acc = 0.0f;
+  const int KT = k_tiles(G);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
+    for (int i = tid; i < NB * kTileGroups; i += kDriftThreads) {
+      const int b = i / kTileGroups, g = i - b * kTileGroups;
+      float sx = 0.0f;
+      if (g < ng) {
+        const uint16_t* xr = x + (size_t)b * K + (size_t)(g0 + g) * kGroup;
+        for (int j = 0; j < kGroup; ++j) sx += fabsf(__half2float(__ushort_as_half(xr[j])));
+      }
+      X[b][g] = sx;
+    }
+    __syncthreads();
+    const int t = kt * RT + rt;
+    const uint8_t* tb = stream + (size_t)tiles[4 * t + 1] * 16;
+    const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
+    const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
+    const uint32_t s1 = (uint32_t)seg_bytes(0, n[0]), s2 = s1 + (uint32_t)seg_bytes(1, n[1]);
+    const uint32_t sb[4] = {0u, s1, s2, s2 + (uint32_t)seg_bytes(2, n[2])};
+    const uint32_t total = n[0] + n[1] + n[2] + n[3];
+    for (uint32_t i = tid; i < total; i += kDriftThreads) {
+      int c = 0;
+      uint32_t idx = i;
+      while (c < 3 && idx >= n[c]) {
+        idx -= n[c];
+        ++c;
+      }
+      const uint32_t br = block_records(c), k = idx / br, l = idx - k * br, m = min(br, n[c] - k * br);
+      const uint32_t blk = sb[c] + k * (uint32_t)block_bytes(c, br);
+      const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + blk + codes_area(c, m) + 4u * l);
+      const uint32_t meta = *reinterpret_cast<const uint16_t*>(tb + blk + codes_area(c, m) + so_area(m) + 2u * l);
+      const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+      const int row = (int)(meta & 15u), g = (int)((meta >> 4) & (uint32_t)(kTileGroups - 1));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) P[b][row][g] = hs * X[b][g];
+    }
+    __syncthreads();
+    if (tid < NB * kTile)
+      for (int g = 0; g < ng; ++g) acc += P[b_own][r_own][g];
+    __syncthreads();   // X and P are rewritten for the next k-tile
+  }
+  const int row = rt * kTile + r_own;
+  if (tid < NB * kTile && row < N) bound[(size_t)b_own * N + row] = acc;
+}
+
+hipError_t launch_drift(const vbq_matrix& m, const uint16_t* x, int B, float* bound, hipStream_t s) {
+  const int RT = row_tiles(m.n_rows), G = m.n_cols / kGroup;
+  const uint8_t* st = reinterpret_cast<const uint8_t*>(m.stream);
+#define VBQ_DRIFT(NB)                                                                                   \
+  case NB:                                                                                              \
+    hipLaunchKernelGGL(k_drift<NB>, dim3(RT), dim3(kDriftThreads), 0, s, m.tiles, st, x, m.n_rows, G, RT, bound); \
+    break;
+  switch (B) {
+    VBQ_DRIFT(1)
+    VBQ_DRIFT(2)
+    VBQ_DRIFT(3)
+    VBQ_DRIFT(4)
+    VBQ_DRIFT(5)
+    VBQ_DRIFT(6)
+    VBQ_DRIFT(7)
+    VBQ_DRIFT(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef VBQ_DRIFT
+  return hipGetLastError();
+}
+
 }  // namespace vbq

@@ -326,6 +326,45 @@ def _verify_both(vbq, pm, resid_t):
     return got
 
 
+DRIFT_CASES = [(37, 576, 1), (64, 8192 + 128, 3), (20, 4096, 8), (1, 64, 2)]
+
+
+@pytest.mark.parametrize("case", DRIFT_CASES, ids=[f"{n}x{k}b{b}" for n, k, b in DRIFT_CASES])
+def test_drift_bound(vbq, case):
+    """cell_drift_bound against the oracle's closed form, repeatable bit for
+    bit, and a true bound on the library's own residual GEMV: in-cell
+    residuals stay inside it and the extremal residual sign(x) s/2 reaches it
+    (up to the rounding of two binary32 GEMVs)."""
+    import torch
+    N, K, B = case
+    W, widths, x = rand_case(N, K, seed=7 * N + K + B, B=B)
+    print(f"case drift bound {N}x{K} B={B}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    xt = _t(x, torch.float16)
+    got = vbq.cell_drift_bound(pm, xt).cpu().numpy()
+    ref = oracle.drift_bound(s, x)
+    assert got.shape == ref.shape == (B, N)
+    assert np.all(np.abs(got - ref) <= 5e-5 * ref)
+    assert np.array_equal(vbq.cell_drift_bound(pm, xt).cpu().numpy(), got)
+    s_full = oracle.f64_from_f16(np.repeat(s, 64, axis=1))
+    xd = oracle.f64_from_f16(x)
+    wdq = s_full * q + oracle.f64_from_f16(np.repeat(o, 64, axis=1))
+    slack = 1e-5 * (np.abs(xd) @ (np.abs(wdq) + s_full).T)      # rounding of the two GEMVs
+    y0 = vbq.vbq_gemv(pm, xt).cpu().numpy()
+    resid = oracle.make_cell_residual(np.random.default_rng(N + B).uniform(-0.49, 0.49, (N, K)), s)
+    yr = vbq.vbq_gemv(pm, xt, residual=_t(resid, torch.float16)).cpu().numpy()
+    assert np.all(np.abs(yr.astype(np.float64) - y0) <= got + slack)
+    for b in range(B):
+        half = s_full / 2 * np.sign(xd[b])[None, :]
+        r16 = oracle.f16_from_f64(half)
+        assert np.array_equal(oracle.f64_from_f16(r16), half)
+        xb = xt[b:b + 1].contiguous()
+        ye = vbq.vbq_gemv(pm, xb, residual=_t(r16, torch.float16)).cpu().numpy()[0]
+        yb = vbq.vbq_gemv(pm, xb).cpu().numpy()[0]
+        assert np.all(np.abs((ye.astype(np.float64) - yb) - got[b]) <= 1e-5 * got[b] + slack[b])
+
+
 def test_requant_verify_small(vbq):
     import torch
     N, K = 40, 1024
