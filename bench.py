@@ -499,7 +499,7 @@ def measure_workloads(stack, calls):
     rotated over a pool larger than the caches where they would fit):
     131M-class projection, 1.0B-class layer at batch 1 and 4, the 9B-class
     stack at batch 4 and, at batch 1, as one batched call, the in-cell update
-    (residual GEMV and the re-quantisation check) and the batched GEMM on
+    (residual GEMV, re-quantisation check, drift bound) and the batched GEMM on
     MFMA."""
     import torch
 
@@ -617,6 +617,12 @@ def measure_workloads(stack, calls):
     nbv = algorithmic_bytes(pm.sizes, N, K, 1, resid=True) - 2 * K - 4 * N + 24
     out.append(_gemv_line(f"in-cell update {N}x{K}: re-quantisation check (cell_requant_verify)", us, nbv,
                           {"mismatches": int(counts[0]), "out_of_cell": int(counts[1])}))
+    # Drift bound of the update: scale/offset (4 B) and meta (2 B) of every
+    # group, x, one float per row; the codes are not read.
+    bound = torch.empty(1, N, dtype=torch.float32, device=dev)
+    us = _events_time(lambda i: vbq.cell_drift_bound(pool[i % len(pool)][0], x, out=bound), calls)
+    nbd = N * (K // 64) * (4 + 2) + 2 * K + 4 * N
+    out.append(_gemv_line(f"in-cell update {N}x{K}: drift bound (cell_drift_bound), batch 1", us, nbd))
     del pool
 
     out.append(gemm_workload(vbq, calls))
