@@ -263,6 +263,35 @@ def drift_bound(s16, x) -> np.ndarray:
     return 0.5 * (xa.reshape(B, K // 64, 64).sum(axis=2) @ s.T)
 
 
+def rrq_levels(W, n_levels: int):
+    """Recurrent residual levels (page "Recurrent Residual Quantization",
+    section Abstract): a 2-bit RTN base, then 2-bit RTN of what remains. In
+    binary32: E_0 = W; level i = RTN(E_i) with every group 2-bit;
+    E_{i+1} = E_i - (f32(s_i q_i) + o_i) (s q is exact in binary32, so this
+    rounds once per operation). Returns ([(q, s16, o16) per level], E_n)."""
+    E = np.ascontiguousarray(W, np.float32)
+    N, K = E.shape
+    widths = np.full((N, K // 64), 2, np.uint8)
+    levels = []
+    for _ in range(n_levels):
+        q, s16, o16 = quantize_matrix(E, widths)
+        s = f64_from_f16(np.repeat(s16, 64, axis=1)).astype(np.float32)
+        o = f64_from_f16(np.repeat(o16, 64, axis=1)).astype(np.float32)
+        deq = (s * q.astype(np.float32)) + o
+        E = (E - deq).astype(np.float32)
+        levels.append((q, s16, o16))
+    return levels, E
+
+
+def rrq_gemv(levels, x) -> np.ndarray:
+    """y [B][N] fp64 = x . (sum of the levels' dequantised weights)^T."""
+    x = f64_from_f16(_c(np.atleast_2d(x), np.uint16))
+    Wsum = 0.0
+    for q, s16, o16 in levels:
+        Wsum = Wsum + f64_from_f16(np.repeat(s16, 64, axis=1)) * q + f64_from_f16(np.repeat(o16, 64, axis=1))
+    return x @ np.asarray(Wsum).T
+
+
 def f32_to_bf16(v: float) -> int:
     return int(lib().orc_f32_to_bf16(float(np.float32(v))))
 

@@ -566,6 +566,39 @@ def pin_drift_bound_attained():
         assert np.all(np.abs(oracle.gemv(q, s, o, x, resid) - y0) <= bound)
 
 
+def pin_rrq_levels():
+    """Recurrent residual levels: every level leaves at most half its scale
+    of error (RTN on the fp16 grid, up to the fp16 rounding of the scale and
+    offset); a group already on a 4-level fp16 grid is exact after the base
+    (the next level is the degenerate group: scale 0, codes 0); the error
+    and the GEMV error shrink level by level."""
+    r = _rng(50)
+    N, K = 16, 256
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[3, 64:128] = np.float32(0.0078125) + np.float32(0.001953125) * r.integers(0, 4, 64).astype(np.float32)
+    W[3, 64] = np.float32(0.0078125)
+    W[3, 65] = np.float32(0.0078125 + 3 * 0.001953125)
+    levels, E = oracle.rrq_levels(W, 4)
+    prev = np.abs(W).max()
+    Ei = W.astype(np.float64)
+    for i, (q, s16, o16) in enumerate(levels):
+        s = oracle.f64_from_f16(np.repeat(s16, 64, axis=1))
+        o = oracle.f64_from_f16(np.repeat(o16, 64, axis=1))
+        assert q.max() <= 3
+        Ei = Ei - (s * q + o)                          # fp64 accumulation of the same levels
+        err = np.abs(Ei)
+        assert np.all(err <= 0.5 * s * (1 + 2.0 ** -6) + 4.0 ** -12), i
+        assert err.max() < prev, i
+        prev = err.max()
+    _, s1, _ = levels[1]
+    assert s1[3, 1] == 0 and np.all(levels[1][0][3, 64:128] == 0)
+    assert np.allclose(E, Ei, rtol=0, atol=1e-9)       # binary32 recursion vs fp64 bookkeeping
+    x = r.standard_normal((2, K)).astype(np.float16).view(np.uint16)
+    exact = oracle.f64_from_f16(x) @ W.astype(np.float64).T
+    errs = [np.abs(oracle.rrq_gemv(levels[:k + 1], x) - exact).max() for k in range(4)]
+    assert all(errs[k + 1] < errs[k] for k in range(3)), errs
+
+
 def pin_requant_verify():
     r, widths, q, s, o, s_full, resid = _cell_case(31)
     N, K = q.shape
@@ -708,7 +741,8 @@ ALL_PINS = [
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
     pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
-    pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_requant_verify, pin_residual_inside_cell,
+    pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_rrq_levels, pin_requant_verify,
+    pin_residual_inside_cell,
     pin_mean_bits_accounting,
     pin_abstract_storage_ratios, pin_bf16_weights, pin_layout_big_blocks,
 ]
