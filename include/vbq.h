@@ -203,6 +203,25 @@ vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, floa
 vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
                                uint32_t* requant_codes, hipStream_t stream);
 
+/* Recurrent residual levels (page "Recurrent Residual Quantization",
+ * section Abstract: a 2-bit base, then 2-bit RTN residual corrections that
+ * give 4-, 6- and 8-bit representations from one checkpoint). A level is an
+ * ordinary packed matrix (every width 2, from vbq_pack). The error it leaves:
+ *   E_out[n][k] = E_in[n][k] - (f32(s*q) + o)
+ * in binary32, one rounding per operation; the next level is vbq_pack of
+ * E_out. E_in, E_out: device, N x K float32 natural order, 4-byte aligned;
+ * E_out may be E_in. Every width is accepted. */
+vbq_status vbq_residual_error(const vbq_matrix* m, const float* E_in, float* E_out, hipStream_t stream);
+
+/* GEMV over several levels of one weight matrix (same N and K):
+ *   y[b][n] = sum_i x[b] . dequant(W_i)[n]  (levels added in order, binary32)
+ * x: device, B x K fp16 (B = 1..8), 16-byte aligned. scratch: device,
+ * count x B x N float32 (caller-owned; the per-level outputs), 4-byte
+ * aligned. y: device, B x N float32, fully overwritten. Shares the GEMV's
+ * workspace rules (vbq_gemv_batched). */
+vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* x, int32_t B, float* scratch,
+                           float* y, hipStream_t stream);
+
 /* Drift bound of an in-cell update (page "Nothing Changed but the Model:
  * CellFill -- Bounded In-Cell Learning for Bit-Identical, Revocable Updates
  * to Quantized LLMs", section Abstract: bounded drift). For every residual

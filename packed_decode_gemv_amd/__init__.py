@@ -46,7 +46,8 @@ class vbq_layout_sizes(C.Structure):
 
 
 EXPORTS = ("vbq_abi_version", "vbq_status_string", "vbq_pack_query", "vbq_pack", "vbq_matrix_check",
-           "vbq_gemv", "vbq_gemv_batched", "vbq_gemm", "cell_requant_verify", "cell_drift_bound")
+           "vbq_gemv", "vbq_gemv_batched", "vbq_gemm", "cell_requant_verify", "cell_drift_bound",
+           "vbq_residual_error", "vbq_gemv_levels")
 
 
 def _load():
@@ -75,6 +76,10 @@ def _load():
     lib.cell_requant_verify.argtypes = [C.POINTER(vbq_matrix), P, P, P, P]
     lib.cell_drift_bound.restype = C.c_int
     lib.cell_drift_bound.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P]
+    lib.vbq_residual_error.restype = C.c_int
+    lib.vbq_residual_error.argtypes = [C.POINTER(vbq_matrix), P, P, P]
+    lib.vbq_gemv_levels.restype = C.c_int
+    lib.vbq_gemv_levels.argtypes = [I32, C.POINTER(vbq_matrix), P, I32, P, P, P]
     return lib
 
 
@@ -231,4 +236,41 @@ def cell_drift_bound(pm: PackedMatrix, x, out=None, stream=None):
     if out is None:
         out = torch.empty(B, pm.N, dtype=torch.float32, device=x.device)
     _check(lib.cell_drift_bound(C.byref(pm.desc), _ptr(x2), B, _ptr(out), _stream(stream)), "cell_drift_bound")
+    return out
+
+
+def vbq_residual_error(pm: PackedMatrix, E, out=None, stream=None):
+    """E - dequant(W) in binary32 (N x K float32): what the next residual level quantises."""
+    import torch
+    if out is None:
+        out = torch.empty_like(E)
+    _check(lib.vbq_residual_error(C.byref(pm.desc), _ptr(E), _ptr(out), _stream(stream)), "vbq_residual_error")
+    return out
+
+
+def rrq_pack(W, n_levels: int, stream=None):
+    """Recurrent residual levels of W: a 2-bit base and n_levels - 1 2-bit
+    levels, each packed from the error the levels before it leave."""
+    import torch
+    widths = np.full((W.shape[0], W.shape[1] // GROUP), 2, np.uint8)
+    E = W.contiguous().float()
+    levels = []
+    for i in range(n_levels):
+        pm = vbq_pack(E, widths, stream=stream)
+        levels.append(pm)
+        if i + 1 < n_levels:
+            E = vbq_residual_error(pm, E, stream=stream)
+    return levels
+
+
+def vbq_gemv_levels(pms, x, out=None, stream=None):
+    """y [B][N] float32 = sum over levels of x . dequant(W_i)^T."""
+    import torch
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    B, n = x2.shape[0], len(pms)
+    descs = (vbq_matrix * n)(*[pm.desc for pm in pms])
+    scratch = torch.empty(n, B, pms[0].N, dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty(B, pms[0].N, dtype=torch.float32, device=x.device)
+    _check(lib.vbq_gemv_levels(n, descs, _ptr(x2), B, _ptr(scratch), _ptr(out), _stream(stream)), "vbq_gemv_levels")
     return out

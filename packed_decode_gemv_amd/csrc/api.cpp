@@ -332,6 +332,33 @@ vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, ui
   return from_hip(launch_verify(*m, residual, result, requant_codes, stream));
 }
 
+vbq_status vbq_residual_error(const vbq_matrix* m, const float* E_in, float* E_out, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!E_in || !E_out) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(E_in, 4) || !aligned(E_out, 4)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_residual_error(*m, E_in, E_out, stream));
+}
+
+vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* x, int32_t B, float* scratch,
+                           float* y, hipStream_t stream) {
+  if (count < 1 || !ms || !x || !scratch || !y) return VBQ_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    vbq_status st = check_matrix(&ms[i]);
+    if (st != VBQ_OK) return st;
+    if (ms[i].n_rows != ms[0].n_rows || ms[i].n_cols != ms[0].n_cols) return VBQ_ERR_SHAPE;
+  }
+  if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
+  if (!aligned(scratch, 4) || !aligned(y, 4)) return VBQ_ERR_ALIGNMENT;
+  const size_t per = (size_t)B * (size_t)ms[0].n_rows;
+  std::vector<const uint16_t*> xs(count, x);
+  std::vector<float*> ys(count);
+  for (int i = 0; i < count; ++i) ys[i] = scratch + (size_t)i * per;
+  vbq_status st = gemv_impl(count, ms, xs.data(), nullptr, ys.data(), B, stream);
+  if (st != VBQ_OK) return st;
+  return from_hip(launch_sum_levels(scratch, count, per, y, stream));
+}
+
 vbq_status cell_drift_bound(const vbq_matrix* m, const uint16_t* x, int32_t B, float* bound, hipStream_t stream) {
   vbq_status st = check_matrix(m);
   if (st != VBQ_OK) return st;

@@ -272,4 +272,74 @@ hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& 
   return hipGetLastError();
 }
 
+// ---- Recurrent residual levels ---------------------------------------------------
+// Each level after the base is the 2-bit RTN of the error the levels before it
+// leave (page "Recurrent Residual Quantization", section Abstract). The error
+// a packed level leaves:
+//   E_out[n][k] = E_in[n][k] - (f32(s q) + o)
+// in binary32 with one rounding per operation (s q is exact). One workgroup
+// per tile; each wavefront takes whole records with lane j on code j, so a
+// record's 64 weights are one contiguous 256-byte segment of a row. Code j of
+// a record lies in half j / 32, pair p = (j % 32) / 2: word h b + p / (16 / b),
+// bit 16 (j % 2) + (p % (16 / b)) b. E_out may be E_in.
+__global__ __launch_bounds__(256) void k_residual_error(const uint32_t* __restrict__ tiles,
+                                                        const uint8_t* __restrict__ stream, int G, int RT,
+                                                        const float* E_in, float* E_out) {
+  const int t = (int)blockIdx.x, kt = t / RT, rt = t - kt * RT;
+  const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const size_t K = (size_t)G * kGroup;
+  const uint8_t* tb = stream + (size_t)tiles[4 * t + 1] * 16;
+  const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
+  const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
+  const uint32_t s1 = (uint32_t)seg_bytes(0, n[0]), s2 = s1 + (uint32_t)seg_bytes(1, n[1]);
+  const uint32_t sb[4] = {0u, s1, s2, s2 + (uint32_t)seg_bytes(2, n[2])};
+  const uint32_t total = n[0] + n[1] + n[2] + n[3];
+  for (uint32_t i = (uint32_t)wave; i < total; i += 4) {
+    int c = 0;
+    uint32_t idx = i;
+    while (c < 3 && idx >= n[c]) {
+      idx -= n[c];
+      ++c;
+    }
+    const uint32_t br = block_records(c), k = idx / br, l = idx - k * br, m = min(br, n[c] - k * br);
+    const uint32_t blk = sb[c] + k * (uint32_t)block_bytes(c, br);
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(tb + blk + (8u << c) * l);
+    const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + blk + codes_area(c, m) + 4u * l);
+    const uint32_t meta = *reinterpret_cast<const uint16_t*>(tb + blk + codes_area(c, m) + so_area(m) + 2u * l);
+    const int b = 1 << c, H = 16 >> c;
+    const int h = lane >> 5, p = (lane & 31) >> 1, odd = lane & 1;
+    const uint32_t q = (codes[h * b + p / H] >> (16 * odd + (p % H) * b)) & ((1u << b) - 1u);
+    const float sc = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+    const float of = __half2float(__ushort_as_half((unsigned short)(so >> 16)));
+    const size_t e = (size_t)(rt * kTile + (int)(meta & 15u)) * K +
+                     (size_t)(kt * kTileGroups + (int)((meta >> 4) & (uint32_t)(kTileGroups - 1))) * kGroup +
+                     (size_t)lane;
+    E_out[e] = __fsub_rn(E_in[e], __fadd_rn(__fmul_rn(sc, (float)q), of));
+  }
+}
+
+// y[i] = sum over levels l in order of parts[l][i] (binary32).
+__global__ __launch_bounds__(256) void k_sum_levels(const float* __restrict__ parts, int count, size_t n,
+                                                    float* __restrict__ y) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float v = parts[i];
+    for (int l = 1; l < count; ++l) v += parts[(size_t)l * n + i];
+    y[i] = v;
+  }
+}
+
+hipError_t launch_residual_error(const vbq_matrix& m, const float* E_in, float* E_out, hipStream_t s) {
+  const int G = m.n_cols / kGroup, RT = row_tiles(m.n_rows);
+  hipLaunchKernelGGL(k_residual_error, dim3((unsigned)m.n_tiles), dim3(256), 0, s, m.tiles,
+                     reinterpret_cast<const uint8_t*>(m.stream), G, RT, E_in, E_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_levels(const float* parts, int count, size_t n, float* y, hipStream_t s) {
+  const size_t want = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  hipLaunchKernelGGL(k_sum_levels, dim3(blocks), dim3(256), 0, s, parts, count, n, y);
+  return hipGetLastError();
+}
+
 }  // namespace vbq

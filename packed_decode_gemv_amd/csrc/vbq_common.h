@@ -140,6 +140,8 @@ uint32_t gemv_ring_min_bytes();
 
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s);
+hipError_t launch_residual_error(const vbq_matrix& m, const float* E_in, float* E_out, hipStream_t s);
+hipError_t launch_sum_levels(const float* parts, int count, size_t n, float* y, hipStream_t s);
 hipError_t launch_drift(const vbq_matrix& m, const uint16_t* x, int B, float* bound, hipStream_t s);
 hipError_t launch_gemm(const vbq_matrix& m, const uint16_t* x, int M, float* y, hipStream_t s);
 

@@ -20,6 +20,7 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("vbq_pack", "vbq_gemv", "vbq_gemm", "cell_requant_verify", "cell_drift_bound", "vbq_pack_query",
+              "vbq_residual_error", "vbq_gemv_levels",
               "vbq_gemv_batched", "vbq_matrix_check", "vbq_abi_version", "vbq_status_string"):
         assert n in names
 
@@ -103,6 +104,14 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     assert L.cell_drift_bound(C.byref(m), C.c_void_p(0x7F0000100001), 1, y, None) == 4
     assert L.cell_drift_bound(C.byref(m), x, 1, C.c_void_p(0x7F0000200002), None) == 4
     assert L.cell_drift_bound(C.byref(_fake_matrix(vbq, K=100)), x, 1, y, None) == 2
+    assert L.vbq_residual_error(C.byref(m), None, y, None) == 1
+    assert L.vbq_residual_error(C.byref(m), x, C.c_void_p(0x7F0000200002), None) == 4
+    two = (vbq.vbq_matrix * 2)(m, _fake_matrix(vbq, N=48))
+    assert L.vbq_gemv_levels(2, two, x, 1, y, y, None) == 2          # levels of different shapes
+    assert L.vbq_gemv_levels(0, two, x, 1, y, y, None) == 1
+    same = (vbq.vbq_matrix * 2)(m, m)
+    assert L.vbq_gemv_levels(2, same, x, 9, y, y, None) == 5
+    assert L.vbq_gemv_levels(2, same, x, 1, None, y, None) == 1
     assert L.vbq_pack(None, x, C.byref(m), None) == 1
     assert L.vbq_pack(C.c_void_p(0x7F0000100004), x, C.byref(m), None) == 4
     ms = (vbq.vbq_matrix * 2)(m, m)

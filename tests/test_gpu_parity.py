@@ -365,6 +365,54 @@ def test_drift_bound(vbq, case):
         assert np.all(np.abs((ye.astype(np.float64) - yb) - got[b]) <= 1e-5 * got[b] + slack[b])
 
 
+@pytest.mark.parametrize("shape", [(37, 576), (64, 8192 + 128)], ids=["37x576", "64x8320"])
+def test_rrq_levels_bit_exact_and_gemv(vbq, shape):
+    """Recurrent residual levels: each level's layout is bit-exact against the
+    oracle's pack of the error the levels before it leave, and that error is
+    bit-exact against the oracle's binary32 recursion; rrq_pack gives the same
+    levels; the GEMV over the first 1..4 levels (2 to 8 effective bits)
+    matches the oracle at batch 1 and 4."""
+    import torch
+    N, K = shape
+    r = np.random.default_rng(N + K)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w2 = np.full((N, K // 64), 2, np.uint8)
+    print(f"case rrq {N}x{K}", flush=True)
+    E = _t(W)
+    pms = []
+    for i in range(4):
+        E_ref_in = oracle.rrq_levels(W, i)[1]
+        pm = vbq.vbq_pack(E, w2)
+        layout_equal(pm, oracle.pack(E_ref_in, w2))
+        E = vbq.vbq_residual_error(pm, E)
+        assert np.array_equal(E.cpu().numpy(), oracle.rrq_levels(W, i + 1)[1]), f"level {i}"
+        pms.append(pm)
+    for a, b in zip(vbq.rrq_pack(_t(W), 4), pms):
+        layout_equal(a, b.host_layout())
+    levels, _ = oracle.rrq_levels(W, 4)
+    for B in (1, 4):
+        x = r.standard_normal((B, K)).astype(np.float16).view(np.uint16)
+        for k in range(4):
+            y = vbq.vbq_gemv_levels(pms[:k + 1], _t(x, torch.float16)).cpu().numpy()
+            assert rel_l2(y, oracle.rrq_gemv(levels[:k + 1], x)) <= TOL, (B, k)
+
+
+def test_residual_error_any_width(vbq):
+    """vbq_residual_error on a mixed-width matrix is E - (f32(s q) + o) bit
+    for bit, in place too."""
+    N, K = 40, 640
+    W, widths, _ = rand_case(N, K, seed=5)
+    pm = vbq.vbq_pack(_t(W), widths)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    sf = oracle.f64_from_f16(np.repeat(s, 64, axis=1)).astype(np.float32)
+    of = oracle.f64_from_f16(np.repeat(o, 64, axis=1)).astype(np.float32)
+    ref = (W - ((sf * q.astype(np.float32)) + of)).astype(np.float32)
+    E = _t(W)
+    assert np.array_equal(vbq.vbq_residual_error(pm, E).cpu().numpy(), ref)
+    vbq.vbq_residual_error(pm, E, out=E)
+    assert np.array_equal(E.cpu().numpy(), ref)
+
+
 def test_requant_verify_small(vbq):
     import torch
     N, K = 40, 1024
