@@ -499,7 +499,8 @@ def measure_workloads(stack, calls):
     rotated over a pool larger than the caches where they would fit):
     131M-class projection, 1.0B-class layer at batch 1 and 4, the 9B-class
     stack at batch 4 and, at batch 1, as one batched call, the in-cell update
-    (residual GEMV, re-quantisation check, drift bound) and the batched GEMM on
+    (residual GEMV, re-quantisation check, drift bound), the GEMV over recurrent
+    residual levels and the batched GEMM on
     MFMA."""
     import torch
 
@@ -624,6 +625,20 @@ def measure_workloads(stack, calls):
     nbd = N * (K // 64) * (4 + 2) + 2 * K + 4 * N
     out.append(_gemv_line(f"in-cell update {N}x{K}: drift bound (cell_drift_bound), batch 1", us, nbd))
     del pool
+
+    # Recurrent residual levels of the same shape: a 2-bit base and three
+    # 2-bit residual levels (8 effective bits), GEMV over all four at batch 1.
+    Wr = torch.from_numpy(synth.weights(synth.SEED, key, N, K)).to(dev)
+    levels = vbq.rrq_pack(Wr, 4)
+    del Wr
+    lv_bytes = sum(pm_.nbytes for pm_ in levels)
+    pool = [levels] + [[pm_.clone() for pm_ in levels] for _ in range(max(1, POOL_BYTES // lv_bytes) - 1)]
+    us = _events_time(lambda i: vbq.vbq_gemv_levels(pool[i % len(pool)], x, out=y), calls)
+    groups = N * (K // 64)
+    nbr = sum(pm_.sizes.code_bits / 8 + 4 * groups + groups / 4 for pm_ in levels) + 2 * K + 4 * N
+    out.append(_gemv_line(f"recurrent residual levels {N}x{K}: 2-bit base + 3 levels (8 effective bits), "
+                          "GEMV over the levels, batch 1", us, nbr))
+    del pool, levels
 
     out.append(gemm_workload(vbq, calls))
     return out
