@@ -203,8 +203,8 @@ vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, floa
 vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, uint64_t* result,
                                uint32_t* requant_codes, hipStream_t stream);
 
-/* Recurrent residual levels (page "Recurrent Residual Quantization",
- * section Abstract: a 2-bit base, then 2-bit RTN residual corrections that
+/* Recurrent residual levels (RRQ abstract on page
+ * thelatestinai.com/papers/2512.18934: a 2-bit base, then 2-bit RTN residual corrections that
  * give 4-, 6- and 8-bit representations from one checkpoint). A level is an
  * ordinary packed matrix (every width 2, from vbq_pack). The error it leaves:
  *   E_out[n][k] = E_in[n][k] - (f32(s*q) + o)

@@ -264,8 +264,8 @@ def drift_bound(s16, x) -> np.ndarray:
 
 
 def rrq_levels(W, n_levels: int):
-    """Recurrent residual levels (page "Recurrent Residual Quantization",
-    section Abstract): a 2-bit RTN base, then 2-bit RTN of what remains. In
+    """Recurrent residual levels (RRQ abstract on page
+    thelatestinai.com/papers/2512.18934): a 2-bit RTN base, then 2-bit RTN of what remains. In
     binary32: E_0 = W; level i = RTN(E_i) with every group 2-bit;
     E_{i+1} = E_i - (f32(s_i q_i) + o_i) (s q is exact in binary32, so this
     rounds once per operation). Returns ([(q, s16, o16) per level], E_n)."""

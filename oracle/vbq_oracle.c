@@ -514,7 +514,7 @@ void orc_requant_verify(const uint8_t* q, const uint16_t* s16, const uint16_t* o
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) {
       int64_t gi = n * G + k / 64;
-      int L = (1 << widths[gi]) - 1;
+      int L = (g_mut == 12) ? 255 : (1 << widths[gi]) - 1;  /* mutation: L not from the group's width */
       float s = orc_f16_to_f32(s16[gi]), o = orc_f16_to_f32(o16[gi]);
       float r = orc_f16_to_f32(r16[n * K + k]);
       float qf = (float)q[n * K + k];
@@ -527,8 +527,10 @@ void orc_requant_verify(const uint8_t* q, const uint16_t* s16, const uint16_t* o
         float d = v - o;
         float t = d / s;
         float rr = rintf(t);
-        if (rr < 0.0f) rr = 0.0f;
-        if (rr > (float)L) rr = (float)L;
+        if (g_mut != 11) {                              /* mutation: clamp dropped */
+          if (rr < 0.0f) rr = 0.0f;
+          if (rr > (float)L) rr = (float)L;
+        }
         qp = (int)rr;
       }
       int bad_code = qp != (int)q[n * K + k];

@@ -274,7 +274,7 @@ hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& 
 
 // ---- Recurrent residual levels ---------------------------------------------------
 // Each level after the base is the 2-bit RTN of the error the levels before it
-// leave (page "Recurrent Residual Quantization", section Abstract). The error
+// leave (RRQ abstract on page thelatestinai.com/papers/2512.18934). The error
 // a packed level leaves:
 //   E_out[n][k] = E_in[n][k] - (f32(s q) + o)
 // in binary32 with one rounding per operation (s q is exact). One workgroup

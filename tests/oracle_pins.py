@@ -636,6 +636,47 @@ def pin_requant_verify():
     assert diff.tolist() == [[11, 77]]
 
 
+def pin_requant_verify_edge_cells():
+    """Edge codes clamp (CellFill abstract: re-quantisation returns the released
+    codes; the grid of a b-bit group is q in [0, 2^b - 1]). Hand-worked, one
+    64-weight group per width b = 1, 2, 4, 8 with s = 0.25, o = -1 (both exact
+    in binary16). Weight 0 has q = 0 and r = -0.15625 (= -0.625 s); weight 1
+    has q = L = 2^b - 1 and r = +0.15625. Then (v - o) / s = -0.625 and
+    L + 0.625 exactly, which round to -1 and L + 1 and clamp back to 0 and L:
+    no code changes, but both residuals leave their cells (|r| >= s/2).
+    A third residual, +0.625 s at an interior code q = 1 (b >= 2), moves the
+    code to 2. Only a clamp to the group's own [0, L] gives these counts."""
+    widths = np.array([[1], [2], [4], [8]], np.uint8)
+    N, K = 4, 64
+    s16 = np.full((N, 1), 0x3400, np.uint16)            # 0.25
+    o16 = np.full((N, 1), 0xBC00, np.uint16)            # -1.0
+    assert oracle.f64_from_f16(s16[0])[0] == 0.25 and oracle.f64_from_f16(o16[0])[0] == -1.0
+    q = np.zeros((N, K), np.uint8)
+    r16 = np.zeros((N, K), np.uint16)
+    minus, plus = 0xB100, 0x3100                        # -0.15625, +0.15625
+    assert list(oracle.f64_from_f16(np.array([minus, plus], np.uint16))) == [-0.15625, 0.15625]
+    for i in range(N):
+        L = (1 << int(widths[i, 0])) - 1
+        q[i, 0], r16[i, 0] = 0, minus
+        q[i, 1], r16[i, 1] = L, plus
+        q[i, 2:] = np.arange(K - 2) % (L + 1)
+    mism, ooc, first, qp = oracle.requant_verify(q, s16, o16, widths, r16, want_codes=True)
+    assert (mism, ooc, first) == (0, 8, 0)
+    assert np.array_equal(qp, q)
+    # the same residuals inside their cells at interior codes (b >= 2): q = 1
+    # with +0.625 s moves to 2 (a real mismatch the clamp must not hide)
+    q2, r2 = q.copy(), r16.copy()
+    for i in range(1, N):
+        q2[i, 3], r2[i, 3] = 1, plus
+    mism, ooc, first, qp = oracle.requant_verify(q2, s16, o16, widths, r2, want_codes=True)
+    assert (mism, ooc, first) == (3, 11, 0)
+    assert [int(qp[i, 3]) for i in range(1, N)] == [2, 2, 2]
+    # only the edge weights of the 1-bit row: first bad index is its weight 0
+    r3 = np.zeros_like(r16)
+    r3[0, 1] = plus
+    assert oracle.requant_verify(q, s16, o16, widths, r3)[:3] == (0, 1, 1)
+
+
 def pin_residual_inside_cell():
     """The generated residual satisfies |r| < s/2 and so stays in the cell."""
     _, _, q, s, o, s_full, resid = _cell_case(32)
@@ -742,6 +783,7 @@ ALL_PINS = [
     pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_rrq_levels, pin_requant_verify,
+    pin_requant_verify_edge_cells,
     pin_residual_inside_cell,
     pin_mean_bits_accounting,
     pin_abstract_storage_ratios, pin_bf16_weights, pin_layout_big_blocks,

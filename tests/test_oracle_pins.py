@@ -29,6 +29,8 @@ MUTATIONS = {
     8: "records ordered by (k-group, row)",
     9: "record halves swapped",
     10: "bfloat16 rounding breaks ties away from zero",
+    11: "re-quantisation drops the clamp to [0, L]",
+    12: "re-quantisation takes L from the wrong width",
 }
 
 
