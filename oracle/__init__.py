@@ -181,7 +181,7 @@ def unpack_group_record(words, b):
     return _group_codes("orc_unpack_group_record", words, b)
 
 
-TILE_ROWS = 16
+TILE_ROWS = 32
 TILE_GROUPS = 64
 
 

@@ -31,26 +31,24 @@
  *
  * Execution layout written and read here (the format the GPU library uses;
  * this file implements it independently from its written specification):
- *   the matrix is cut into tiles of 16 rows x 64 k-groups (4096 columns),
- *   stored k-tile major: tile t = kt * RT + rt covers rows 16rt.. and k-groups
- *   64kt.., RT = ceil(N/16), KT = ceil(G/64). Inside a tile the groups are
- *   split by width class c (b = 1,2,4,8 -> c = 0..3) and, inside a class,
- *   ordered by (row ascending, k-group ascending). Each group is a "record":
- *     codes: 2b u32 words; with h = 16/b, pair p = (code 2p, code 2p+1), p < 32,
- *            sits in word p/h: code 2p at bit (p%h)*b, code 2p+1 at bit 16+(p%h)*b
- *     so   : u32, fp16 scale in bits 0-15, fp16 offset in bits 16-31
- *     meta : u16, row in the tile in bits 0-3, k-group in the tile in bits 4-9
- *   A class segment holds its records in blocks of 256, 64, 64, 16 records
- *   (b = 1, 2, 4, 8: 2048, 1024, 2048, 1024 code bytes per full block); the
- *   last block may be short (m records). A block of m records is, in order:
- *     codes area: record l's 2b words at byte 8b*l, in order (for b = 1
- *                 the area is rounded up to 16 bytes)
- *     so area   : record l at byte 4l, rounded up to 16 bytes
- *     meta area : record l at byte 2l, rounded up to 16 bytes
- *   with zero padding. A tile is its class segments 0..3 in order; tiles follow
- *   each other in storage order in one byte stream. Per tile 4 u32: record
- *   base, byte base (16-byte units), n0|n1<<16, n2|n3<<16; one extra entry
- *   after the last tile holds the totals (records, 16-byte units, 0, 0).
+ *   the matrix is cut into tiles of 32 rows x 64 k-groups (4096 columns),
+ *   stored k-tile major: tile t = kt * RT + rt covers rows 32rt.. and k-groups
+ *   64kt.., RT = ceil(N/32), KT = ceil(G/64); a tile has R <= 32 rows and
+ *   Gt <= 64 columns (k-groups). Width class c = 0..3 for b = 1,2,4,8. For
+ *   column l and class c, the rows of that class are visited in the order of
+ *   (r - l) mod 32 ascending; n_c(l) counts them and I_c = max over l.
+ *   A tile is, each area padded with zeros to a multiple of 16 bytes:
+ *     map   : per column l, u32 plane0 (bit r = class & 1) then u32 plane1
+ *             (bit r = class >> 1);
+ *     blocks: for c = 0..3, i = 0..I_c-1: the columns with n_c(l) > i in
+ *             increasing order (m of them); the k-th holds the group of its
+ *             i-th visited row: codes area (2b words per record at 8bk), then
+ *             so area (u32 scale | offset << 16 at 4k).
+ *   Record words: with h = 16/b, pair p = (code 2p, code 2p+1) sits in word
+ *   p/h, code 2p at bit (p%h)*b and code 2p+1 at bit 16+(p%h)*b.
+ *   Per tile 4 u32: first 16-byte unit, size in 16-byte units,
+ *   I_0 | I_1<<8 | I_2<<16 | I_3<<24, 0; one extra entry after the last tile
+ *   holds (total 16-byte units, 0, 0, 0).
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,7 +57,7 @@
 
 #define ORC_GROUP 64
 
-#define ORC_TILE_ROWS 16
+#define ORC_TILE_ROWS 32
 #define ORC_TILE_GROUPS 64
 
 /* Deliberate-mistake switch used only by the tests that show the pins catch
@@ -201,43 +199,6 @@ static int class_bits(int c) { return 1 << c; }
 
 static int64_t up16(int64_t v) { return (v + 15) / 16 * 16; }
 
-/* Records per block of class c (full blocks hold 2048, 1024, 2048, 1024 code
- * bytes for b = 1, 2, 4, 8). */
-static int64_t block_records(int c) { return c == 0 ? 256 : c == 1 ? 64 : c == 2 ? 64 : 16; }
-
-/* Areas of a block of class c holding m records: codes, scale/offset words,
- * meta halfwords, each rounded up to 16 bytes. */
-static int64_t codes_area(int c, int64_t m) { return c == 0 ? up16(8 * m) : 8 * (int64_t)class_bits(c) * m; }
-static int64_t so_area(int64_t m) { return up16(4 * m); }
-static int64_t meta_area(int64_t m) { return up16(2 * m); }
-static int64_t block_bytes(int c, int64_t m) { return codes_area(c, m) + so_area(m) + meta_area(m); }
-
-/* Bytes of class segment c with n records (full blocks, then the remainder). */
-static int64_t seg_bytes(int c, int64_t n) {
-  int64_t br = block_records(c);
-  return (n / br) * block_bytes(c, br) + ((n % br) ? block_bytes(c, n % br) : 0);
-}
-
-static int64_t tile_bytes(const int64_t n[4]) {
-  return seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2]) + seg_bytes(3, n[3]);
-}
-
-/* Where record i of class segment c (n records) lives, relative to the
- * segment: block base, its record count m, and the index l inside it. */
-static void record_place(int c, int64_t n, int64_t i, int64_t* base, int64_t* m, int64_t* l) {
-  int64_t br = block_records(c), k = i / br;
-  *base = k * block_bytes(c, br);
-  *m = (n - k * br < br) ? n - k * br : br;
-  *l = i % br;
-}
-
-/* Byte offset, inside a block, of 16-byte chunk q of record l (b >= 2), or of
- * the 8-byte record l (b == 1, q == 0): records are contiguous. */
-static int64_t chunk_offset(int c, int64_t m, int64_t l, int q) {
-  (void)m;
-  return 8 * (int64_t)class_bits(c) * l + 16 * q;
-}
-
 /* Tile geometry: number of row-tiles and k-tiles. */
 static void tile_grid(int N, int K, int64_t* RT, int64_t* KT) {
   int G = K / 64;
@@ -245,16 +206,65 @@ static void tile_grid(int N, int K, int64_t* RT, int64_t* KT) {
   *KT = (G + ORC_TILE_GROUPS - 1) / ORC_TILE_GROUPS;
 }
 
-/* Class counts of tile (rt, kt). Returns -1 on an invalid width. */
-static int tile_counts(const uint8_t* widths, int N, int G, int64_t rt, int64_t kt, int64_t n[4]) {
-  n[0] = n[1] = n[2] = n[3] = 0;
-  for (int64_t r = rt * ORC_TILE_ROWS; r < N && r < (rt + 1) * ORC_TILE_ROWS; ++r)
-    for (int64_t g = kt * ORC_TILE_GROUPS; g < G && g < (kt + 1) * ORC_TILE_GROUPS; ++g) {
-      int c = width_class(widths[r * G + g]);
-      if (c < 0) return -1;
-      n[c]++;
+/* Everything the layout of one tile depends on: its rows and columns, the
+ * class of every group, and per (class, column) the rows of that class in
+ * visiting order. */
+typedef struct {
+  int r0, R, g0, Gt;
+  int cls[ORC_TILE_ROWS][ORC_TILE_GROUPS];
+  int n[4][ORC_TILE_GROUPS];
+  int rows[4][ORC_TILE_GROUPS][ORC_TILE_ROWS];
+  int I[4];
+} orc_tile;
+
+/* Fills T for tile (rt, kt). Returns -1 on an invalid width. */
+static int tile_info(const uint8_t* widths, int N, int G, int64_t rt, int64_t kt, orc_tile* T) {
+  T->r0 = (int)(rt * ORC_TILE_ROWS);
+  T->R = N - T->r0 < ORC_TILE_ROWS ? N - T->r0 : ORC_TILE_ROWS;
+  T->g0 = (int)(kt * ORC_TILE_GROUPS);
+  T->Gt = G - T->g0 < ORC_TILE_GROUPS ? G - T->g0 : ORC_TILE_GROUPS;
+  for (int r = 0; r < T->R; ++r)
+    for (int l = 0; l < T->Gt; ++l) {
+      T->cls[r][l] = width_class(widths[(int64_t)(T->r0 + r) * G + T->g0 + l]);
+      if (T->cls[r][l] < 0) return -1;
     }
+  for (int c = 0; c < 4; ++c) {
+    T->I[c] = 0;
+    for (int l = 0; l < T->Gt; ++l) {
+      int cnt = 0;
+      /* key = (r - l) mod 32 ascending, i.e. r = (key + l) mod 32;
+       * mutation 8 visits the rows in plain ascending order instead */
+      for (int key = 0; key < ORC_TILE_ROWS; ++key) {
+        int r = (g_mut == 8) ? key : (key + l) % ORC_TILE_ROWS;
+        if (r < T->R && T->cls[r][l] == c) T->rows[c][l][cnt++] = r;
+      }
+      T->n[c][l] = cnt;
+      if (cnt > T->I[c]) T->I[c] = cnt;
+    }
+  }
   return 0;
+}
+
+/* Columns active in block (c, i), in increasing order; returns m. */
+static int block_columns(const orc_tile* T, int c, int i, int* cols) {
+  int m = 0;
+  for (int l = 0; l < T->Gt; ++l)
+    if (T->n[c][l] > i) cols[m++] = l;
+  return m;
+}
+
+static int64_t block_bytes(int c, int m) { return up16(8 * (int64_t)class_bits(c) * m) + up16(4 * (int64_t)m); }
+
+static int64_t tile_bytes(const orc_tile* T) {
+  int64_t bytes = up16(8 * (int64_t)T->Gt);
+  int cols[ORC_TILE_GROUPS];
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < T->I[c]; ++i) bytes += block_bytes(c, block_columns(T, c, i, cols));
+  return bytes;
+}
+
+static uint32_t iter_word(const orc_tile* T) {
+  return (uint32_t)T->I[0] | ((uint32_t)T->I[1] << 8) | ((uint32_t)T->I[2] << 16) | ((uint32_t)T->I[3] << 24);
 }
 
 /* Counts the sizes of the layout. Returns 0, or -1 for a bad shape or width. */
@@ -264,12 +274,13 @@ int orc_layout_sizes(const uint8_t* widths, int N, int K, int64_t* n_tiles, int6
   int G = K / 64;
   int64_t RT, KT, bytes = 0;
   tile_grid(N, K, &RT, &KT);
+  orc_tile* T = (orc_tile*)malloc(sizeof(orc_tile));
   for (int64_t kt = 0; kt < KT; ++kt)
     for (int64_t rt = 0; rt < RT; ++rt) {
-      int64_t n[4];
-      if (tile_counts(widths, N, G, rt, kt, n) != 0) return -1;
-      bytes += tile_bytes(n);
+      if (tile_info(widths, N, G, rt, kt, T) != 0) { free(T); return -1; }
+      bytes += tile_bytes(T);
     }
+  free(T);
   *n_tiles = RT * KT;
   *n_records = (int64_t)N * G;
   *n_bytes16 = bytes / 16;
@@ -280,72 +291,73 @@ int orc_layout_sizes(const uint8_t* widths, int N, int K, int64_t* n_tiles, int6
  * layout: tiles [(n_tiles+1)*4] and the byte stream [n_bytes16*4 u32].
  * Returns 0 or -1. */
 int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tiles, uint32_t* stream) {
-  int64_t T, R, B16;
-  if (orc_layout_sizes(widths, N, K, &T, &R, &B16) != 0) return -1;
+  int64_t T_, R_, B16;
+  if (orc_layout_sizes(widths, N, K, &T_, &R_, &B16) != 0) return -1;
   int G = K / 64;
   int64_t RT, KT;
   tile_grid(N, K, &RT, &KT);
   memset(stream, 0, (size_t)B16 * 16);
-  int64_t rec = 0, byte = 0;
-  for (int64_t t = 0; t < T; ++t) {
+  orc_tile* T = (orc_tile*)malloc(sizeof(orc_tile));
+  int64_t byte = 0;
+  for (int64_t t = 0; t < T_; ++t) {
     int64_t kt = t / RT, rt = t % RT;                   /* k-tile major */
-    int r0 = (int)(rt * ORC_TILE_ROWS), r1 = r0 + ORC_TILE_ROWS;
-    if (r1 > N) r1 = N;
-    int g0 = (int)(kt * ORC_TILE_GROUPS), g1 = g0 + ORC_TILE_GROUPS;
-    if (g1 > G) g1 = G;
-    int64_t n[4];
-    tile_counts(widths, N, G, rt, kt, n);
-    tiles[4 * t + 0] = (uint32_t)rec;
-    tiles[4 * t + 1] = (uint32_t)(byte / 16);
-    tiles[4 * t + 2] = (uint32_t)(n[0] | (n[1] << 16));
-    tiles[4 * t + 3] = (uint32_t)(n[2] | (n[3] << 16));
-    uint8_t* seg = (uint8_t*)stream + byte;
-    const int nr = r1 - r0, ng = g1 - g0;
+    tile_info(widths, N, G, rt, kt, T);
+    uint8_t* tb = (uint8_t*)stream + byte;
+    for (int l = 0; l < T->Gt; ++l) {
+      uint32_t p0 = 0, p1 = 0;
+      for (int r = 0; r < T->R; ++r) {
+        p0 |= (uint32_t)(T->cls[r][l] & 1) << r;
+        p1 |= (uint32_t)(T->cls[r][l] >> 1) << r;
+      }
+      memcpy(tb + 8 * l, &p0, 4);
+      memcpy(tb + 8 * l + 4, &p1, 4);
+    }
+    int64_t pos = up16(8 * (int64_t)T->Gt);
+    int cols[ORC_TILE_GROUPS];
     for (int c = 0; c < 4; ++c) {
       int b = class_bits(c);
-      int64_t i = 0;
-      for (int it = 0; it < ng * nr; ++it) {
-        /* (row, k-group) order; mutation 8 walks (k-group, row) instead */
-        int g = g0 + ((g_mut == 8) ? it / nr : it % ng);
-        int r = r0 + ((g_mut == 8) ? it % nr : it / ng);
-        if (width_class(widths[(int64_t)r * G + g]) != c) continue;
-        uint16_t s16, o16;
-        uint8_t q[64];
-        uint32_t words[16];
-        orc_quantize_group(W + (int64_t)r * K + 64 * g, b, &s16, &o16, q);
-        orc_pack_group_record(q, b, words);
-        int64_t base, m, l;
-        record_place(c, n[c], i, &base, &m, &l);
-        uint8_t* blk = seg + base;
-        if (b == 1) {
-          memcpy(blk + chunk_offset(c, m, l, 0), words, 8);
-        } else {
-          for (int ch = 0; ch < b / 2; ++ch) memcpy(blk + chunk_offset(c, m, l, ch), words + 4 * ch, 16);
+      for (int i = 0; i < T->I[c]; ++i) {
+        int m = block_columns(T, c, i, cols);
+        for (int k = 0; k < m; ++k) {
+          int l = cols[k], r = T->rows[c][l][i];
+          uint16_t s16, o16;
+          uint8_t q[64];
+          uint32_t words[16];
+          orc_quantize_group(W + (int64_t)(T->r0 + r) * K + 64 * (int64_t)(T->g0 + l), b, &s16, &o16, q);
+          orc_pack_group_record(q, b, words);
+          memcpy(tb + pos + 8 * (int64_t)b * k, words, 8 * (size_t)b);
+          uint32_t so = (uint32_t)s16 | ((uint32_t)o16 << 16);
+          memcpy(tb + pos + up16(8 * (int64_t)b * m) + 4 * k, &so, 4);
         }
-        uint32_t so = (uint32_t)s16 | ((uint32_t)o16 << 16);
-        uint16_t mt = (uint16_t)((r - r0) | ((g - g0) << 4));
-        memcpy(blk + codes_area(c, m) + 4 * l, &so, 4);
-        memcpy(blk + codes_area(c, m) + so_area(m) + 2 * l, &mt, 2);
-        ++i;
+        pos += block_bytes(c, m);
       }
-      seg += seg_bytes(c, n[c]);
     }
-    rec += n[0] + n[1] + n[2] + n[3];
-    byte += tile_bytes(n);
+    tiles[4 * t + 0] = (uint32_t)(byte / 16);
+    tiles[4 * t + 1] = (uint32_t)(pos / 16);
+    tiles[4 * t + 2] = iter_word(T);
+    tiles[4 * t + 3] = 0;
+    byte += pos;
   }
-  tiles[4 * T + 0] = (uint32_t)rec;
-  tiles[4 * T + 1] = (uint32_t)(byte / 16);
-  tiles[4 * T + 2] = 0;
-  tiles[4 * T + 3] = 0;
+  free(T);
+  tiles[4 * T_ + 0] = (uint32_t)(byte / 16);
+  tiles[4 * T_ + 1] = 0;
+  tiles[4 * T_ + 2] = 0;
+  tiles[4 * T_ + 3] = 0;
   return 0;
+}
+
+static int all_zero(const uint8_t* p, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (p[i]) return 0;
+  return 1;
 }
 
 /* Reads the execution layout back into natural order: codes [N][K], and per
  * group scale16/offset16/width [N][G]. Rows listed in `rows` only (n_rows of
  * them) when rows != NULL; outputs are then [n_rows][...] in that order.
- * Returns 0, or -1 if the layout is inconsistent (a group missing or repeated,
- * a meta field out of range, a tile that does not end where the next begins,
- * nonzero padding). */
+ * The classes come from each tile's map alone. Returns 0, or -1 if the layout
+ * is inconsistent (a tile entry that disagrees with its map, a tile that does
+ * not end where the next begins, nonzero padding or unused map bits). */
 int orc_unpack(const uint32_t* tiles, const uint32_t* stream, int N, int K, const int64_t* rows, int64_t n_rows,
                uint8_t* q_out, uint16_t* s_out, uint16_t* o_out, uint8_t* w_out) {
   if (N < 1 || K < 64 || K % 64 != 0) return -1;
@@ -354,57 +366,73 @@ int orc_unpack(const uint32_t* tiles, const uint32_t* stream, int N, int K, cons
   tile_grid(N, K, &RT, &KT);
   int64_t nr = rows ? n_rows : N;
   for (int64_t i = 0; i < nr * G; ++i) w_out[i] = 0;
-  for (int64_t ri = 0; ri < nr; ++ri) {
+  orc_tile* T = (orc_tile*)malloc(sizeof(orc_tile));
+  uint8_t* wmap = (uint8_t*)malloc((size_t)ORC_TILE_ROWS * G);   /* widths of one row-tile, from the maps */
+  int rc = 0;
+  for (int64_t ri = 0; ri < nr && rc == 0; ++ri) {
     int64_t row = rows ? rows[ri] : ri;
-    if (row < 0 || row >= N) return -1;
+    if (row < 0 || row >= N) { rc = -1; break; }
     int64_t rt = row / ORC_TILE_ROWS;
-    for (int64_t kt = 0; kt < KT; ++kt) {
+    for (int64_t kt = 0; kt < KT && rc == 0; ++kt) {
       int64_t t = kt * RT + rt;
-      int64_t n[4] = {tiles[4 * t + 2] & 0xFFFF, tiles[4 * t + 2] >> 16, tiles[4 * t + 3] & 0xFFFF,
-                      tiles[4 * t + 3] >> 16};
-      if ((int64_t)tiles[4 * t + 5] * 16 - (int64_t)tiles[4 * t + 1] * 16 != tile_bytes(n)) return -1;
-      const uint8_t* seg = (const uint8_t*)stream + (int64_t)tiles[4 * t + 1] * 16;
-      for (int c = 0; c < 4; ++c) {
+      const uint8_t* tb = (const uint8_t*)stream + (int64_t)tiles[4 * t] * 16;
+      int r0 = (int)(rt * ORC_TILE_ROWS), R = N - r0 < ORC_TILE_ROWS ? N - r0 : ORC_TILE_ROWS;
+      int g0 = (int)(kt * ORC_TILE_GROUPS), Gt = G - g0 < ORC_TILE_GROUPS ? G - g0 : ORC_TILE_GROUPS;
+      /* widths of this tile from its map */
+      for (int l = 0; l < Gt; ++l) {
+        uint32_t p0, p1;
+        memcpy(&p0, tb + 8 * l, 4);
+        memcpy(&p1, tb + 8 * l + 4, 4);
+        if (R < 32 && ((p0 | p1) >> R) != 0) { rc = -1; break; }
+        for (int r = 0; r < R; ++r) {
+          int c = (int)((p0 >> r) & 1u) | (int)(((p1 >> r) & 1u) << 1);
+          wmap[(int64_t)r * G + g0 + l] = (uint8_t)class_bits(c);
+        }
+      }
+      if (rc) break;
+      if (!all_zero(tb + 8 * Gt, up16(8 * (int64_t)Gt) - 8 * Gt)) { rc = -1; break; }
+      /* the tile as the writer sees it, built from the map's widths */
+      tile_info(wmap, R, G, 0, kt, T);
+      T->r0 = r0;
+      if (tiles[4 * t + 2] != iter_word(T) || (int64_t)tiles[4 * t + 1] * 16 != tile_bytes(T) ||
+          tiles[4 * t + 0] + tiles[4 * t + 1] != tiles[4 * t + 4]) { rc = -1; break; }
+      int64_t pos = up16(8 * (int64_t)Gt);
+      int cols[ORC_TILE_GROUPS];
+      for (int c = 0; c < 4 && rc == 0; ++c) {
         int b = class_bits(c);
-        for (int64_t i = 0; i < n[c]; ++i) {
-          int64_t base, m, l;
-          record_place(c, n[c], i, &base, &m, &l);
-          const uint8_t* blk = seg + base;
-          uint16_t mt;
-          uint32_t so;
-          memcpy(&mt, blk + codes_area(c, m) + so_area(m) + 2 * l, 2);
-          memcpy(&so, blk + codes_area(c, m) + 4 * l, 4);
-          int64_t r = rt * ORC_TILE_ROWS + (mt & 15);
-          int64_t g = kt * ORC_TILE_GROUPS + (mt >> 4);
-          if ((mt >> 4) >= ORC_TILE_GROUPS || g >= G || r >= N) return -1;
-          if (r != row) continue;
-          if (w_out[ri * G + g] != 0) return -1;
-          uint32_t words[16];
-          if (b == 1) memcpy(words, blk + chunk_offset(c, m, l, 0), 8);
-          else
-            for (int ch = 0; ch < b / 2; ++ch) memcpy(words + 4 * ch, blk + chunk_offset(c, m, l, ch), 16);
-          uint8_t q[64];
-          orc_unpack_group_record(words, b, q);
-          memcpy(q_out + ri * K + 64 * g, q, 64);
-          s_out[ri * G + g] = (uint16_t)(so & 0xFFFF);
-          o_out[ri * G + g] = (uint16_t)(so >> 16);
-          w_out[ri * G + g] = (uint8_t)b;
+        for (int i = 0; i < T->I[c]; ++i) {
+          int m = block_columns(T, c, i, cols);
+          if (!all_zero(tb + pos + 8 * (int64_t)b * m, up16(8 * (int64_t)b * m) - 8 * (int64_t)b * m) ||
+              !all_zero(tb + pos + up16(8 * (int64_t)b * m) + 4 * m, up16(4 * (int64_t)m) - 4 * m)) {
+            rc = -1;
+            break;
+          }
+          for (int k = 0; k < m; ++k) {
+            int l = cols[k], r = T->rows[c][l][i];
+            if (r0 + r != row) continue;
+            uint32_t words[16], so;
+            memcpy(words, tb + pos + 8 * (int64_t)b * k, 8 * (size_t)b);
+            memcpy(&so, tb + pos + up16(8 * (int64_t)b * m) + 4 * k, 4);
+            uint8_t q[64];
+            orc_unpack_group_record(words, b, q);
+            int64_t g = g0 + l;
+            if (w_out[ri * G + g] != 0) { rc = -1; break; }
+            memcpy(q_out + ri * K + 64 * g, q, 64);
+            s_out[ri * G + g] = (uint16_t)(so & 0xFFFF);
+            o_out[ri * G + g] = (uint16_t)(so >> 16);
+            w_out[ri * G + g] = (uint8_t)b;
+          }
+          pos += block_bytes(c, m);
         }
-        /* padding of the last block's areas must be zero */
-        if (n[c] % block_records(c)) {
-          int64_t m = n[c] % block_records(c);
-          const uint8_t* blk = seg + (n[c] / block_records(c)) * block_bytes(c, block_records(c));
-          for (int64_t k = (c == 0 ? 8 * m : codes_area(c, m)); k < codes_area(c, m); ++k) if (blk[k]) return -1;
-          for (int64_t k = codes_area(c, m) + 4 * m; k < codes_area(c, m) + so_area(m); ++k) if (blk[k]) return -1;
-          for (int64_t k = codes_area(c, m) + so_area(m) + 2 * m; k < block_bytes(c, m); ++k) if (blk[k]) return -1;
-        }
-        seg += seg_bytes(c, n[c]);
       }
     }
-    for (int g = 0; g < G; ++g)
-      if (w_out[ri * G + g] == 0) return -1;
+    if (rc == 0)
+      for (int g = 0; g < G; ++g)
+        if (w_out[ri * G + g] == 0) { rc = -1; break; }
   }
-  return 0;
+  free(wmap);
+  free(T);
+  return rc;
 }
 
 /* ------------------------------------------------------------------ */

@@ -205,32 +205,39 @@ def _u16_at(stream, byte):
     return (w >> 16) if (byte & 2) else (w & 0xFFFF)
 
 
+def _record(W, row, kg, b):
+    """(so word, record words) of group (row, kg) quantised at width b."""
+    s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], b)
+    return s16 | (o16 << 16), [int(v) for v in oracle.pack_group_record(q, b)]
+
+
 def pin_layout_worked_example():
-    """N=2, K=128, widths [[1,8],[2,1]] (hand-worked). One tile. Class 0
-    (1-bit) in (row, k-group) order: (row0,kg0), (row1,kg1); class 1: (row1,kg0);
-    class 3: (row0,kg1). Blocks: class 0, m=2: codes 16 B, so 8 -> 16 B,
-    meta 4 -> 16 B = 48 B at byte 0; class 1, m=1: 16 + 16 + 16 = 48 B at 48;
-    class 3, m=1: 64 + 16 + 16 = 96 B at 96; total 192 B = 12 units.
-    meta = row | kg<<4 -> 0, 17 (class 0), 1 (class 1), 16 (class 3)."""
+    """N=2, K=128, widths [[1,8],[2,1]] (hand-worked). One tile, R=2 rows,
+    2 columns. Classes (r,l): (0,0)=0, (0,1)=3, (1,0)=1, (1,1)=0.
+    Map: column 0 plane0 = 0b10, plane1 = 0; column 1 plane0 = 0b01,
+    plane1 = 0b01 -> words [2, 0, 1, 1] (16 B).
+    Visiting order (r - l) mod 32: column 0 rows 0, 1; column 1 rows 1, 0.
+    Class 0: both columns hold one row -> I_0 = 1, block (0,0) with columns
+    0, 1 (m=2): groups (0,0), (1,1): codes 16 B, so 8 -> 16 B (32 B at 16).
+    Class 1: I_1 = 1, block (1,0) column 0: group (1,0): 16 + 16 B at 48.
+    Class 3: I_3 = 1, block (3,0) column 1: group (0,1): 64 + 16 B at 80.
+    Total 160 B = 10 units; iteration word 1 | 1<<8 | 1<<24."""
     widths = np.array([[1, 8], [2, 1]], np.uint8)
-    r = _rng(16)
-    W = (r.standard_normal((2, 128)) * 0.02).astype(np.float32)
+    W = (_rng(16).standard_normal((2, 128)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 4, 12)
-    assert list(lay["tiles"]) == [0, 0, 2 | (1 << 16), 0 | (1 << 16), 4, 12, 0, 0]
-    qs = {}
-    for (row, kg, b) in ((0, 0, 1), (1, 1, 1), (1, 0, 2), (0, 1, 8)):
-        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], b)
-        qs[(row, kg)] = (s16 | (o16 << 16), list(oracle.pack_group_record(q, b)))
+    assert oracle.layout_sizes(widths) == (1, 4, 10)
+    assert list(lay["tiles"]) == [0, 10, 1 | (1 << 8) | (1 << 24), 0, 10, 0, 0, 0]
+    so00, w00 = _record(W, 0, 0, 1)
+    so11, w11 = _record(W, 1, 1, 1)
+    so10, w10 = _record(W, 1, 0, 2)
+    so01, w01 = _record(W, 0, 1, 8)
     st = [int(v) for v in lay["stream"]]
-    assert len(st) == 48
-    expect = ([*qs[(0, 0)][1], *qs[(1, 1)][1], qs[(0, 0)][0], qs[(1, 1)][0], 0, 0, 0 | (17 << 16), 0, 0, 0]
-              + [*qs[(1, 0)][1], qs[(1, 0)][0], 0, 0, 0, 1, 0, 0, 0]
-              + [*qs[(0, 1)][1], qs[(0, 1)][0], 0, 0, 0, 16, 0, 0, 0])
+    expect = ([2, 0, 1, 1] + w00 + w11 + [so00, so11, 0, 0] + w10 + [so10, 0, 0, 0]
+              + w01 + [so01, 0, 0, 0])
     assert st == expect
-    # the reader rejects a nonzero padding byte (class 0 so padding, word 6)
+    # the reader rejects a nonzero padding byte (class 0 so padding, word 10)
     bad = dict(lay, stream=lay["stream"].copy())
-    bad["stream"][6] = 1
+    bad["stream"][10] = 1
     try:
         oracle.unpack(bad)
         raise AssertionError("nonzero padding accepted")
@@ -238,130 +245,127 @@ def pin_layout_worked_example():
         pass
 
 
-def pin_layout_block_chunks():
-    """Records are contiguous inside a block: 16-byte chunk q of record l
-    (b >= 2) sits at (l*b/2 + q)*16 bytes. One tile with 3 four-bit records
-    (m=3): codes 96 B, then so (12 -> 16 B), then meta (6 -> 16 B)."""
-    widths = np.array([[4, 4, 4]], np.uint8)
-    W = (_rng(17).standard_normal((1, 192)) * 0.02).astype(np.float32)
+def pin_layout_rotation():
+    """Visiting order and shrinking blocks (hand-worked): N=32, K=192, width 1
+    everywhere except (r5, l0) = 8 and (r1, l2) = (r3, l2) = 2.
+    Class 0: n(0)=31, n(1)=32, n(2)=30 -> I_0 = 32; blocks (0,i): columns
+    {0,1,2} for i < 30 (48 B each: codes 24 -> 32, so 12 -> 16), {0,1} at
+    i = 30 (32 B), {1} at i = 31 (32 B): 1504 B after the 32-byte map.
+    Rows in visiting order: column 0: 0,1,2,3,4,6,...,31; column 1:
+    1,2,...,31,0; column 2 (key (r-2) mod 32): 2,4,5,...,31,0.
+    So block (0,0) = groups (0,0),(1,1),(2,2); block (0,29) = (30,0),
+    (30,1),(0,2); block (0,30) = (31,0),(31,1); block (0,31) = (0,1).
+    Class 1 (column 2, rows 3 then 1): blocks at 1536 and 1568 (32 B each).
+    Class 3: block (3,0) at 1600 holding (5,0): codes 64 B, so at 1664.
+    Total 1680 B = 105 units."""
+    N, G = 32, 3
+    widths = np.ones((N, G), np.uint8)
+    widths[5, 0] = 8
+    widths[1, 2] = widths[3, 2] = 2
+    W = (_rng(21).standard_normal((N, 64 * G)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 3, 8)
-    chunks = lay["stream"].reshape(-1, 4)               # 16-byte chunks
-    for kg in range(3):
-        s16, o16, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
-        words = oracle.pack_group_record(q, 4)
-        assert list(chunks[2 * kg + 0]) == list(words[0:4])
-        assert list(chunks[2 * kg + 1]) == list(words[4:8])
-        assert _u32_at(lay["stream"], 96 + 4 * kg) == s16 | (o16 << 16)
-        assert _u16_at(lay["stream"], 112 + 2 * kg) == kg << 4
-
-
-def pin_layout_block_split():
-    """A class segment longer than one block (hand-worked): N=16, K=192, widths
-    8 in k-group 0 and at (row 0, kg 1), 1 elsewhere. In (row, kg) order the
-    17 eight-bit records are (0,0), (0,1), (1,0), (2,0), ..., (15,0) and the 31
-    one-bit records (0,2), (1,1), (1,2), ..., (15,1), (15,2).
-    Class 0: one block m=31: codes 248 -> 256, so 124 -> 128, meta 62 -> 64:
-    448 B. Class 3 (capacity 16): a full block at 448 (codes 1024: record l at
-    448 + 64 l; so at 1472; meta at 1536; 1120 B), then a block of m=1 at 1568
-    holding (15,0): codes at 1568, so at 1632, meta at 1648. Total 1664 B."""
-    widths = np.ones((16, 3), np.uint8)
-    widths[:, 0] = 8
-    widths[0, 1] = 8
-    W = (_rng(20).standard_normal((16, 192)) * 0.02).astype(np.float32)
-    lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 48, 104)
-    assert list(lay["tiles"]) == [0, 0, 31, 17 << 16, 48, 104, 0, 0]
+    assert oracle.layout_sizes(widths) == (1, 96, 105)
+    assert list(lay["tiles"]) == [0, 105, 32 | (2 << 8) | (1 << 24), 0, 105, 0, 0, 0]
     st = lay["stream"]
-    full = [(0, 0), (0, 1)] + [(r, 0) for r in range(1, 15)]
-    for l in (0, 1, 2, 9, 15):
-        row, kg = full[l]
-        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], 8)
-        at = 448 + 64 * l
-        assert [int(v) for v in st[at // 4:at // 4 + 16]] == list(oracle.pack_group_record(q, 8))
-        assert _u32_at(st, 1472 + 4 * l) == s16 | (o16 << 16)
-        assert _u16_at(st, 1536 + 2 * l) == row | (kg << 4)
-    s16, o16, q = oracle.quantize_group(W[15, 0:64], 8)
-    assert [int(v) for v in st[1568 // 4:1568 // 4 + 16]] == list(oracle.pack_group_record(q, 8))
-    assert _u32_at(st, 1632) == s16 | (o16 << 16)
-    assert _u16_at(st, 1648) == 15
-    # class 0 block: record l at 8l, so at 256 + 4l, meta at 384 + 2l
-    s16, o16, q = oracle.quantize_group(W[0, 128:192], 1)
-    assert [int(v) for v in st[0:2]] == list(oracle.pack_group_record(q, 1))
-    assert _u32_at(st, 256) == s16 | (o16 << 16) and _u16_at(st, 384) == 0 | (2 << 4)
-    assert _u16_at(st, 386) == 1 | (1 << 4) and _u16_at(st, 384 + 2 * 30) == 15 | (2 << 4)
-    assert _u16_at(st, 384 + 2 * 31) == 0 and _u32_at(st, 256 + 4 * 31) == 0   # padding
+    words = lambda at, n: [int(v) for v in st[at // 4:at // 4 + n]]
+    # map: column 0 plane0/1 = bit 5 (class 3); column 2 plane0 = bits 1, 3
+    assert words(0, 8) == [1 << 5, 1 << 5, 0, 0, (1 << 1) | (1 << 3), 0, 0, 0]
+    def block0(i, groups):
+        at = 32 + 48 * i if i < 30 else (32 + 48 * 30 + 32 * (i - 30))
+        m = len(groups)
+        so_at = at + (-(-8 * m // 16) * 16)
+        for k, (r, l) in enumerate(groups):
+            so, w = _record(W, r, l, 1)
+            assert words(at + 8 * k, 2) == w and words(so_at + 4 * k, 1) == [so], (i, k)
+    block0(0, [(0, 0), (1, 1), (2, 2)])
+    block0(4, [(4, 0), (5, 1), (7, 2)])
+    block0(5, [(6, 0), (6, 1), (8, 2)])
+    block0(29, [(30, 0), (30, 1), (0, 2)])
+    block0(30, [(31, 0), (31, 1)])
+    block0(31, [(0, 1)])
+    for at, (r, l) in ((1536, (3, 2)), (1568, (1, 2))):
+        so, w = _record(W, r, l, 2)
+        assert words(at, 4) == w and words(at + 16, 4) == [so, 0, 0, 0]
+    so, w = _record(W, 5, 0, 8)
+    assert words(1600, 16) == w and words(1664, 4) == [so, 0, 0, 0]
 
 
-def pin_layout_big_blocks():
-    """Block capacities (hand-worked): N=16, K=64*20, widths 4 at (row 0,
-    kg 0..3) and 1 elsewhere: 316 one-bit records, 4 four-bit records, one
-    tile. In (row, kg) order the one-bit records are (0,4..19) then
-    (r, 0..19) for r = 1..15, so record i >= 16 is (1 + (i-16)//20, (i-16)%20).
-    Class 0, capacity 256: block 0 full (codes 2048, so 1024, meta 512 =
-    3584 B: record l at 8l, so at 2048+4l, meta at 3072+2l); block 1 holds
-    m=60 at 3584 (codes 480, so 240, meta 120 -> 128: record l at 3584+8l,
-    so at 4064+4l, meta at 4304+2l). Class 2 at 4432: codes 4*32 = 128, so
-    16, meta 16 (record l at 4432+32l, so at 4560+4l, meta at 4576+2l).
-    Total 4592 B = 287 units."""
-    N, K = 16, 64 * 20
-    widths = np.ones((N, 20), np.uint8)
-    widths[0, 0:4] = 4
-    W = (_rng(23).standard_normal((N, K)) * 0.02).astype(np.float32)
+def pin_layout_k_tiles():
+    """Tile order and ragged tiles (hand-worked): N=40, K=64*65, all widths 1.
+    2 row-tiles x 2 k-tiles, t = kt*2 + rt. Tile 0 (32 rows, 64 columns):
+    map 512 B + 32 blocks of m=64 (codes 512 + so 256 = 768 B) = 25088 B
+    (1568 units). Tile 1 (8 rows, 64 columns): 512 + 8*768 = 6656 B (416).
+    Tile 2 (32 rows, 1 column): map 8 -> 16 + 32 blocks of 32 B = 1040 B
+    (65). Tile 3 (8 rows, 1 column): 16 + 8*32 = 272 B (17). Iteration words
+    32, 8, 32, 8."""
+    N, G = 40, 65
+    widths = np.ones((N, G), np.uint8)
+    W = (_rng(22).standard_normal((N, 64 * G)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 320, 287)
-    assert list(lay["tiles"]) == [0, 0, 316, 4, 320, 287, 0, 0]
+    assert oracle.layout_sizes(widths) == (4, N * G, 2066)
+    tiles = lay["tiles"].reshape(-1, 4)
+    assert [list(map(int, t)) for t in tiles] == [[0, 1568, 32, 0], [1568, 416, 8, 0], [1984, 65, 32, 0],
+                                                  [2049, 17, 8, 0], [2066, 0, 0, 0]]
     st = lay["stream"]
-
-    def one_bit(i):
-        return (0, 4 + i) if i < 16 else (1 + (i - 16) // 20, (i - 16) % 20)
-
-    for i, (code_at, so_at, meta_at) in ((0, (0, 2048, 3072)), (15, (120, 2108, 3102)),
-                                         (16, (128, 2112, 3104)), (255, (2040, 3068, 3582)),
-                                         (256, (3584, 4064, 4304)), (315, (4056, 4300, 4422))):
-        row, kg = one_bit(i)
-        s16, o16, q = oracle.quantize_group(W[row, 64 * kg:64 * kg + 64], 1)
-        assert [int(v) for v in st[code_at // 4:code_at // 4 + 2]] == list(oracle.pack_group_record(q, 1))
-        assert _u32_at(st, so_at) == s16 | (o16 << 16)
-        assert _u16_at(st, meta_at) == row | (kg << 4)
-    assert one_bit(255) == (12, 19) and one_bit(256) == (13, 0) and one_bit(315) == (15, 19)
-    assert _u16_at(st, 4424) == 0 and _u32_at(st, 4428) == 0          # meta padding of block 1
-    for kg in range(4):
-        s16, o16, q = oracle.quantize_group(W[0, 64 * kg:64 * kg + 64], 4)
-        at = 4432 + 32 * kg
-        assert [int(v) for v in st[at // 4:at // 4 + 8]] == list(oracle.pack_group_record(q, 4))
-        assert _u32_at(st, 4560 + 4 * kg) == s16 | (o16 << 16)
-        assert _u16_at(st, 4576 + 2 * kg) == kg << 4
+    # tile 1 (rows 32..39): block (0, i) column l holds row 32 + ((i + l) % 32)
+    # among its 8 rows visited from key (r - l) mod 32: rows >= l % 32 first
+    base = 1568 * 16 + 512
+    for l, i in ((0, 0), (5, 0), (5, 2), (7, 7), (63, 7)):
+        order = sorted(range(8), key=lambda r: (r - l) % 32)
+        so, w = _record(W, 32 + order[i], l, 1)
+        at = base + 768 * i
+        assert [int(v) for v in st[(at + 8 * l) // 4:(at + 8 * l) // 4 + 2]] == w
+        assert int(st[(at + 512 + 4 * l) // 4]) == so
+    # tile 3 (rows 32..39, column 64): one column, row order 0..7
+    base = 2049 * 16 + 16
+    for i in (0, 7):
+        so, w = _record(W, 32 + i, 64, 1)
+        assert [int(v) for v in st[(base + 32 * i) // 4:(base + 32 * i) // 4 + 2]] == w
+        assert int(st[(base + 32 * i + 16) // 4]) == so
 
 
-CAP = (256, 64, 64, 16)       # records per block of each width class
-
-
-def _areas(c, m):
-    """(codes, so, meta) area bytes of a block of class c with m records."""
+def _walk_layout(widths, N, K):
+    """Independent reading of the layout rules (written from the header text,
+    not from the oracle's C): yields, per tile, (base byte, size, iteration
+    word, map words, [(byte of codes, byte of so, row, kg, b)])."""
+    G = K // 64
+    RT, KT = -(-N // 32), -(-G // 64)
     up = lambda v: -(-v // 16) * 16
-    return (up(8 * m) if c == 0 else 8 * (1 << c) * m), up(4 * m), up(2 * m)
-
-
-def _walk_tile(base, n):
-    """Independent reading of one tile from the block rules: yields
-    (class, m, l, block byte offset, codes area) per record; returns the tile's
-    end byte via StopIteration.value."""
-    seg = base
-    for c in range(4):
-        full = sum(_areas(c, CAP[c]))
-        for i in range(n[c]):
-            k, l = divmod(i, CAP[c])
-            m = min(CAP[c], n[c] - k * CAP[c])
-            yield c, m, l, seg + k * full, _areas(c, m)
-        k, rem = divmod(n[c], CAP[c])
-        seg += k * full + (sum(_areas(c, rem)) if rem else 0)
-    return seg
+    cls = {1: 0, 2: 1, 4: 2, 8: 3}
+    base = 0
+    for t in range(RT * KT):
+        kt, rt = divmod(t, RT)
+        rows = range(32 * rt, min(N, 32 * rt + 32))
+        ks = range(64 * kt, min(G, 64 * kt + 64))
+        mp = []
+        for kg in ks:
+            p0 = sum((cls[int(widths[r, kg])] & 1) << (r - 32 * rt) for r in rows)
+            p1 = sum((cls[int(widths[r, kg])] >> 1) << (r - 32 * rt) for r in rows)
+            mp += [p0, p1]
+        visit = {}
+        for c in range(4):
+            for l, kg in enumerate(ks):
+                rr = [r - 32 * rt for r in rows if cls[int(widths[r, kg])] == c]
+                visit[c, l] = sorted(rr, key=lambda r: (r - l) % 32)
+        I = [max(len(visit[c, l]) for l in range(len(ks))) for c in range(4)]
+        pos = up(8 * len(ks))
+        recs = []
+        for c in range(4):
+            b = 1 << c
+            for i in range(I[c]):
+                act = [l for l in range(len(ks)) if len(visit[c, l]) > i]
+                m = len(act)
+                for k, l in enumerate(act):
+                    recs.append((base + pos + 8 * b * k, base + pos + up(8 * b * m) + 4 * k,
+                                 32 * rt + visit[c, l][i], 64 * kt + l, b))
+                pos += up(8 * b * m) + up(4 * m)
+        yield base, pos, I[0] | (I[1] << 8) | (I[2] << 16) | (I[3] << 24), mp, recs
+        base += pos
 
 
 def pin_layout_invariants():
     r = _rng(18)
-    cases = [(1, 64), (5, 128), (16, 256), (17, 192), (40, 640), (33, 64 * 70), (18, 64 * 130), (64, 512)]
+    cases = [(1, 64), (5, 128), (32, 256), (33, 192), (40, 640), (33, 64 * 70), (18, 64 * 130), (64, 512)]
     for (N, K) in cases:
         G = K // 64
         widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G), p=[0.55, 0.2, 0.15, 0.1])
@@ -372,40 +376,27 @@ def pin_layout_invariants():
         assert T == RT * KT and R == N * G
         tiles = lay["tiles"].reshape(-1, 4)
         st = lay["stream"]
-        rec = byte = 0
-        for t in range(T):
-            kt, rt = divmod(t, RT)                 # k-tile major storage
-            blkw = widths[16 * rt:16 * rt + 16, 64 * kt:64 * kt + 64]
-            n = [int((blkw == b).sum()) for b in (1, 2, 4, 8)]
-            assert list(tiles[t]) == [rec, byte // 16, n[0] | (n[1] << 16), n[2] | (n[3] << 16)]
-            seen, keys = set(), {0: [], 1: [], 2: [], 3: []}
-            walker = _walk_tile(byte, n)
-            while True:
-                try:
-                    c, m, l, blk, (ca, sa, ma) = next(walker)
-                except StopIteration as e:
-                    end = e.value
-                    break
-                mt = _u16_at(st, blk + ca + sa + 2 * l)
-                row, kg = 16 * rt + (mt & 15), 64 * kt + (mt >> 4)
-                assert (mt >> 10) == 0 and widths[row, kg] == (1 << c)
-                keys[c].append(row * 64 + (kg - 64 * kt))
-                seen.add((row, kg))
-            for c in range(4):
-                assert all(a < b for a, b in zip(keys[c], keys[c][1:]))     # (row, kg) order
-            assert len(seen) == blkw.size
-            rec += sum(n)
-            byte = end
-        assert list(tiles[T]) == [rec, byte // 16, 0, 0] and byte == 16 * B16
+        q2, s2, o2 = oracle.quantize_matrix(W, widths)
+        seen = np.zeros((N, G), np.int32)
+        end = 0
+        for t, (base, size, iw, mp, recs) in enumerate(_walk_layout(widths, N, K)):
+            assert list(tiles[t]) == [base // 16, size // 16, iw, 0]
+            assert [int(v) for v in st[base // 4:base // 4 + len(mp)]] == mp
+            for (cat, sat, row, kg, b) in recs:
+                words = [int(v) for v in oracle.pack_group_record(q2[row, 64 * kg:64 * kg + 64], b)]
+                assert [int(v) for v in st[cat // 4:cat // 4 + 2 * b]] == words
+                assert int(st[sat // 4]) == int(s2[row, kg]) | (int(o2[row, kg]) << 16)
+                seen[row, kg] += 1
+            end = base + size
+        assert (seen == 1).all()
+        assert list(tiles[T]) == [end // 16, 0, 0, 0] and end == 16 * B16
         # reading back gives the quantiser's output in natural order
         q, s, o, w = oracle.unpack(lay)
-        q2, s2, o2 = oracle.quantize_matrix(W, widths)
         assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(o, o2)
         assert np.array_equal(w, widths)
         rows = r.choice(N, min(N, 5), replace=False)
         qr, sr, orr, wr = oracle.unpack(lay, rows)
         assert np.array_equal(qr, q2[rows]) and np.array_equal(wr, widths[rows])
-
 
 
 # --------------------------------------------------------------------------
@@ -732,59 +723,25 @@ def pin_mean_bits_accounting():
     se = math.sqrt(var / w.size)
     assert abs(mean - 1.79) < 4 * se and abs(mean - 1.82) < 4 * se + 0.03
     assert abs(float((w == 1).mean()) - 0.69) < 0.03
-    # bytes of a layout: codes 8*sum(b) per group plus 4 (scale+offset) + 2 (meta),
-    # plus at most 8 + 12 + 14 bytes of padding per class segment of a tile
+    # bytes of a layout: codes 8*sum(b) per group, 4 (scale+offset) per group,
+    # 2 bits of width per group (8 bytes per column of a tile); padding at most
+    # 8 bytes per map and 8 + 12 per block, a tile having at most 4 * 32 blocks
     lay_w = w[:64]
     T, R, B16 = oracle.layout_sizes(lay_w)
-    code_bytes = 8 * int(lay_w.astype(np.int64).sum())
-    assert code_bytes + 6 * R <= 16 * B16 <= code_bytes + 6 * R + 4 * 34 * T
-
-
-def pin_layout_k_tiles():
-    """Tiles are 16 rows x 64 k-groups, stored k-tile major. N=17, K=64*65
-    (hand-worked): 2 row-tiles x 2 k-tiles, t = kt*2 + rt. Tile 0 (rt0, kt0):
-    1024 one-bit records = 4 full blocks of 2048+1024+512 = 3584 B (896
-    units); tile 1 (rt1, kt0): row 16 x 64 groups = one block of m=64,
-    512+256+128 = 896 B; tile 2 (rt0, kt1):
-    15 one-bit records (codes 120 -> 128, so 60 -> 64, meta 30 -> 32 = 224 B)
-    and the 2-bit record of row 3 (16+16+16 = 48 B); tile 3 (rt1, kt1): the
-    8-bit record of row 16 (64+16+16 = 96 B)."""
-    N, K = 17, 64 * 65
-    assert oracle.tile_grid(N, K) == (2, 2)
-    widths = np.ones((N, 65), np.uint8)
-    widths[16, 64] = 8
-    widths[3, 64] = 2
-    W = (_rng(19).standard_normal((N, K)) * 0.02).astype(np.float32)
-    lay = oracle.pack(W, widths)
-    tiles = lay["tiles"].reshape(-1, 4)
-    assert oracle.layout_sizes(widths) == (4, N * 65, 975)
-    assert [int(t[0]) for t in tiles[:4]] == [0, 1024, 1088, 1104]
-    assert [int(t[1]) for t in tiles[:4]] == [0, 896, 952, 969]
-    assert [int(t[2]) for t in tiles[:4]] == [1024, 64, 15 | (1 << 16), 0]
-    assert [int(t[3]) for t in tiles[:4]] == [0, 0, 0, 1 << 16]
-    assert list(tiles[4]) == [1105, 975, 0, 0]
-    st = lay["stream"]
-    # meta holds the row in the tile and the k-group in the tile
-    assert _u16_at(st, 896 * 16 + 512 + 256) == 0                 # tile 1, (row 16, kg 0)
-    assert _u16_at(st, 896 * 16 + 512 + 256 + 10) == 5 << 4       # tile 1, (row 16, kg 5)
-    assert _u16_at(st, 952 * 16 + 128 + 64) == 0                  # tile 2, (row 0, kg 64)
-    assert _u16_at(st, 952 * 16 + 128 + 64 + 28) == 15            # tile 2, (row 15, kg 64)
-    assert _u16_at(st, 952 * 16 + 224 + 32) == 3                  # tile 2, 2-bit record of row 3
-    assert _u16_at(st, 969 * 16 + 64 + 16) == 0                   # tile 3, (row 16, kg 64)
-    s16, o16, q = oracle.quantize_group(W[16, 64 * 64:], 8)
-    assert [int(v) for v in st[969 * 4:969 * 4 + 16]] == list(oracle.pack_group_record(q, 8))
-    assert _u32_at(st, 969 * 16 + 64) == s16 | (o16 << 16)
-
+    RT, KT = oracle.tile_grid(64, 64 * 12)
+    lo = 8 * int(lay_w.astype(np.int64).sum()) + 4 * R + 8 * RT * 12
+    assert lo == 8 * int(lay_w.astype(np.int64).sum()) + 4.25 * R
+    assert lo <= 16 * B16 <= lo + 8 * T + 20 * 128 * T
 
 
 ALL_PINS = [
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
-    pin_layout_worked_example, pin_layout_block_chunks, pin_layout_block_split, pin_layout_invariants,
+    pin_layout_worked_example, pin_layout_rotation, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_rrq_levels, pin_requant_verify,
     pin_requant_verify_edge_cells,
     pin_residual_inside_cell,
     pin_mean_bits_accounting,
-    pin_abstract_storage_ratios, pin_bf16_weights, pin_layout_big_blocks,
+    pin_abstract_storage_ratios, pin_bf16_weights,
 ]

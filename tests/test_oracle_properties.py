@@ -26,7 +26,7 @@ SETTINGS = dict(max_examples=25, deadline=None, suppress_health_check=[HealthChe
 
 @st.composite
 def cases(draw):
-    N = draw(st.integers(1, 40))
+    N = draw(st.integers(1, 70))
     G = draw(st.sampled_from([1, 2, 3, 63, 64, 65, 130]))
     p = np.array(draw(st.lists(st.floats(0.0, 1.0), min_size=4, max_size=4)), np.float64) + 1e-3
     seed = draw(st.integers(0, 2 ** 31 - 1))
@@ -47,7 +47,11 @@ def test_layout_round_trip(case):
     T, R, B16 = oracle.layout_sizes(widths)
     assert lay["stream"].size * 4 == B16 * 16 and R == N * (K // 64)
     tiles = lay["tiles"].reshape(-1, 4)
-    assert tiles.shape[0] == T + 1 and int(tiles[T][0]) == R and int(tiles[T][1]) == B16
+    assert tiles.shape[0] == T + 1 and int(tiles[T][0]) == B16
+    # tiles are back to back: each starts where the one before it ends
+    assert all(int(tiles[t][0]) + int(tiles[t][1]) == int(tiles[t + 1][0]) for t in range(T))
+    # no column of a tile holds more than 32 records of one class
+    assert all(((int(tiles[t][2]) >> (8 * c)) & 0xFF) <= 32 for t in range(T) for c in range(4))
     q, s, o, w = oracle.unpack(lay)
     q2, s2, o2 = oracle.quantize_matrix(W, widths)
     assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(o, o2)
