@@ -145,16 +145,11 @@ def time_steps(stack, steps, warmup):
 
 def capture(fn, n):
     """A HIP graph of n calls fn(0) .. fn(n-1), captured on a stream of our
-    own (fn takes the current stream itself). The calls run once eagerly on
-    that stream first, so that nothing allocates during capture (the
-    library's split-K workspace is per stream)."""
+    own (fn takes the current stream itself). The library allocates nothing,
+    so no call has to run on that stream before the capture."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(n):
-            fn(i)
-    side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         for i in range(n):
@@ -184,7 +179,7 @@ def time_steps_graph(stack, steps, warmup):
     replayed outputs are checked bit for bit against an eager step."""
     import torch
     vbq = stack.vbq
-    stack.step(vbq._stream())   # eager: allocates the workspace before capture
+    stack.step(vbq._stream())   # an eager step, the reference for the replays
     torch.cuda.synchronize()
     eager = [y.clone() for (_, _, y) in list(stack.mats.values())[:8]]
     g = capture(lambda i: stack.step(vbq._stream()), 1)
@@ -498,7 +493,7 @@ def measure_workloads(stack, calls):
     """Timed lines for the other workloads (weights and inputs resident in HBM,
     rotated over a pool larger than the caches where they would fit):
     131M-class projection, 1.0B-class layer at batch 1 and 4, the 9B-class
-    stack at batch 4 and, at batch 1, as one batched call, the in-cell update
+    stack at batch 4, the in-cell update
     (residual GEMV, re-quantisation check, drift bound), the GEMV over recurrent
     residual levels and the batched GEMM on
     MFMA."""
@@ -570,21 +565,6 @@ def measure_workloads(stack, calls):
                           {"us_per_layer": round((us) / (stack.layers + 1), 3)}))
     del plans
 
-    # 9B-class stack at batch 1 with all its matrices in one vbq_gemv_batched
-    # call (the library splits it into launches of up to 32 matrices): the
-    # headline's work, with one launch's start-up and tail overlapping the
-    # streaming of other workgroups. Reported beside the headline, which keeps
-    # one launch per layer.
-    if stack.B == 1:
-        keys = list(stack.mats.keys())
-        whole = vbq.GemvPlan([stack.mats[k][0] for k in keys], [stack.mats[k][1] for k in keys],
-                             [stack.mats[k][2] for k in keys])
-        us = _events_time(lambda i: whole.launch(vbq._stream()), 1, reps=max(3, calls // 20))
-        out.append(_gemv_line(f"9B-class stack ({stack.layers} layers + LM head), batch 1, all {len(keys)} matrices "
-                              f"in one batched call", us, float(sum(stack.launch_bytes)),
-                              {"us_per_layer": round(us / (stack.layers + 1), 3)}))
-        del whole
-
     # In-cell update: 4-bit release 14336 x 4096 with an fp16 residual inside
     # each cell (r = u * scale, u ~ U(-0.49, 0.49)), GEMV and re-quantisation check
     proj = synth.C2.projs[0]
@@ -618,11 +598,11 @@ def measure_workloads(stack, calls):
     nbv = algorithmic_bytes(pm.sizes, N, K, 1, resid=True) - 2 * K - 4 * N + 24
     out.append(_gemv_line(f"in-cell update {N}x{K}: re-quantisation check (cell_requant_verify)", us, nbv,
                           {"mismatches": int(counts[0]), "out_of_cell": int(counts[1])}))
-    # Drift bound of the update: scale/offset (4 B) and meta (2 B) of every
-    # group, x, one float per row; the codes are not read.
+    # Drift bound of the update: scale/offset (4 B) and the 2-bit width of
+    # every group, x, one float per row; the codes are not read.
     bound = torch.empty(1, N, dtype=torch.float32, device=dev)
     us = _events_time(lambda i: vbq.cell_drift_bound(pool[i % len(pool)][0], x, out=bound), calls)
-    nbd = N * (K // 64) * (4 + 2) + 2 * K + 4 * N
+    nbd = N * (K // 64) * (4 + 0.25) + 2 * K + 4 * N
     out.append(_gemv_line(f"in-cell update {N}x{K}: drift bound (cell_drift_bound), batch 1", us, nbd))
     del pool
 

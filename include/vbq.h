@@ -19,18 +19,11 @@
  *
  * Conventions for every call:
  *   - Ownership: the caller allocates and frees every buffer it passes. The
- *     library allocates nothing and keeps no state between calls (apart from
- *     cached device attributes). Buffers marked "device" live in GPU memory
- *     of the current HIP device; "host" buffers are ordinary CPU memory.
- *   - Workspace: the GEMV calls of matrices that span several k-tiles (K >
- *     4096), and the residual and level forms, combine partial rows through a
- *     caller-owned device workspace whose size the matching *_workspace_bytes
- *     call returns (0 when none is needed; the pointer may then be NULL). It
- *     must be 256-byte aligned and filled with zeros before its first use; a
- *     call that completes leaves it ready for the next one (its arrival
- *     counters back at zero). Calls that use one workspace must not overlap
- *     in time (calls on one stream never do). Nothing is allocated at call
- *     time, so the calls can be captured into a HIP graph as they are.
+ *     library allocates nothing, keeps no state between calls (apart from
+ *     cached device attributes) and needs no workspace: partial sums stay
+ *     on-chip inside a workgroup. The calls can therefore be captured into a
+ *     HIP graph as they are. Buffers marked "device" live in GPU memory of
+ *     the current HIP device; "host" buffers are ordinary CPU memory.
  *   - Asynchrony: compute calls enqueue work on `stream` and return without
  *     waiting. Argument errors are found before anything is enqueued: the
  *     call returns a non-zero vbq_status and enqueues nothing. A failed kernel
@@ -101,7 +94,7 @@ typedef enum vbq_status {
   VBQ_ERR_BITWIDTH = 3,      /* a width not in {1,2,4,8} */
   VBQ_ERR_ALIGNMENT = 4,     /* a buffer not aligned as documented */
   VBQ_ERR_UNSUPPORTED = 5,   /* batch out of range, or a size the kernels do not take */
-  VBQ_ERR_CAPACITY = 6,      /* the layout or workspace does not match the buffers it was given */
+  VBQ_ERR_CAPACITY = 6,      /* the layout does not match the buffers it was given */
   VBQ_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed */
 } vbq_status;
 
@@ -158,29 +151,20 @@ vbq_status vbq_pack(const float* W, const uint8_t* widths, const vbq_matrix* m, 
  * VBQ_ERR_CAPACITY (layout larger than the descriptor's sizes). */
 vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
 
-/* Workspace bytes that vbq_gemv needs for matrix m at batch B (1..8), with
- * (with_residual != 0) or without a residual. Host only; 0 when none. */
-vbq_status vbq_gemv_workspace_bytes(const vbq_matrix* m, int32_t B, int32_t with_residual, uint64_t* bytes);
-
 /* Fused dequantise-and-multiply (VBQ abstract: a kernel that dequantises and
  * multiplies in one pass, for memory-bandwidth-bound decode):
  *   y[b][n] = sum_k x[b][k] * (s*q + o + r[n][k])     (r only if residual != NULL)
  * accumulated in fp32; codes are never expanded in memory. The sum over a
  * tile's 4096 columns is formed first; several k-tiles (and the residual's
- * part) are then added in a fixed order.
+ * part) are then added in a fixed order inside one workgroup.
  * x: device, B x K fp16, 16-byte aligned. B in [1, VBQ_MAX_BATCH].
  * residual: device, N x K fp16 row-major (natural order), 16-byte aligned, or
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.
  * y: device, B x N float32, 4-byte aligned; fully overwritten.
- * workspace, workspace_bytes: see the conventions above; workspace_bytes must
- *   be at least vbq_gemv_workspace_bytes(m, B, residual != NULL), else
- *   VBQ_ERR_CAPACITY. */
+ * Batches above 4 rows are run as passes of at most 4 rows. */
 vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
-                    void* workspace, uint64_t workspace_bytes, hipStream_t stream);
-
-/* Workspace bytes of vbq_gemv_batched for these matrices at batch B. */
-vbq_status vbq_gemv_batched_workspace_bytes(int32_t count, const vbq_matrix* ms, int32_t B, uint64_t* bytes);
+                    hipStream_t stream);
 
 /* Several independent GEMVs in one launch (same batch B, no residual; VBQ
  * abstract, fused dequantise-and-multiply): y_i = x_i . dequant(W_i)^T for
@@ -188,20 +172,18 @@ vbq_status vbq_gemv_batched_workspace_bytes(int32_t count, const vbq_matrix* ms,
  * entries (descriptors and device pointers as for vbq_gemv). Used to run all
  * projections of a decoder layer as one launch. */
 vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
-                            int32_t B, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
-
-/* Workspace bytes of vbq_gemv_levels for these levels at batch B. */
-vbq_status vbq_gemv_levels_workspace_bytes(int32_t count, const vbq_matrix* ms, int32_t B, uint64_t* bytes);
+                            int32_t B, hipStream_t stream);
 
 /* GEMV over several levels of one weight matrix (RRQ abstract on page
  * thelatestinai.com/papers/2512.18934: a 2-bit base plus 2-bit residual
  * levels served from one checkpoint), in one launch:
- *   y[b][n] = sum over levels i, in order, of x[b] . dequant(W_i)[n]
+ *   y[b][n] = sum over levels i of x[b] . dequant(W_i)[n]
+ * (the levels' k-tiles are summed in a fixed order, fp32)
  * ms: host array of `count` <= VBQ_MAX_LAUNCH_MATS descriptors of equal N
  * and K (else VBQ_ERR_SHAPE). x: device, B x K fp16 (B = 1..8), 16-byte
  * aligned. y: device, B x N float32, 4-byte aligned, fully overwritten. */
 vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* x, int32_t B, float* y,
-                           void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+                           hipStream_t stream);
 
 /* Batched dequantise-and-multiply for M >= 64 tokens (VBQ abstract: the fused
  * dequantise-and-multiply, here for many tokens at once): tiles of W are
@@ -239,7 +221,7 @@ vbq_status cell_requant_verify(const vbq_matrix* m, const uint16_t* residual, ui
  * levels before it leave):
  *   E_out[n][k] = E_in[n][k] - (f32(s*q) + o)
  * in binary32, one rounding per operation; the next level is vbq_pack of
- * E_out. E_in, E_out: device, N x K float32 natural order, 4-byte aligned;
+ * E_out. E_in, E_out: device, N x K float32 natural order, 8-byte aligned;
  * E_out may be E_in. Every width is accepted. */
 vbq_status vbq_residual_error(const vbq_matrix* m, const float* E_in, float* E_out, hipStream_t stream);
 

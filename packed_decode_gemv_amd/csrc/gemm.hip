@@ -18,12 +18,14 @@
 // each consumer wavefront runs 2 x 2 v_mfma_f32_32x32x16_bf16 tiles over the
 // group: its 64 tokens x the 64 rows.
 //
-// Finding a row's record for a given k-group: the layout keeps a tile's
-// records by width class, then (row, k-group). At every k-tile the workgroup
-// reads the meta of all its records once and builds, per k-group, the list of
-// its 64 rows' records grouped by width class (LDS, 32 KiB). The decode of a
-// group then gives four consecutive lanes one entry of that list (a quarter
-// of the record each, 16 codes), so a wavefront decodes one or two widths.
+// Finding a row's record for a given k-group: the workgroup's 64 rows are two
+// layout tiles. At every k-tile the workgroup reads the two tiles' width maps,
+// counts the records per (k-group, width), walks the tiles' blocks (lane l on
+// column l, which gives each record's row) and builds, per k-group, the list
+// of its 64 rows' records grouped by width class (LDS, 32 KiB); then it loads
+// every listed record's scale/offset at once. The decode of a group then gives
+// four consecutive lanes one entry of that list (a quarter of the record
+// each, 16 codes), so a wavefront decodes one or two widths.
 // A quarter decodes without per-code conversions where the width is small:
 // a 1- or 2-bit record has only 2 or 4 distinct weights, computed once as
 // bf16(fma(s, q, o)) and looked up per code pair with a byte permute; 4- and
@@ -46,7 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;              // tokens per workgroup
 constexpr int kBN = 64;               // weight rows per workgroup
-constexpr int kRowTilesPerWg = kBN / kTile;
+constexpr int kRowTilesPerWg = kBN / kTileRows;
 constexpr int kStride = 72;           // bf16 elements per LDS row
 constexpr int kThreads = 512;           // 4 producer + 4 consumer wavefronts
 constexpr int kProducers = 256;         // threads that load and decode
@@ -83,90 +85,40 @@ __device__ inline void gemm_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Stream position of record `idx` of class c in a tile whose class segments
-// start at seg[c]: byte offsets (from the tile) of its codes and of its meta.
-__device__ inline void record_offsets(int c, uint32_t idx, uint32_t n_c, uint32_t seg, uint32_t& codes,
-                                      uint32_t& so, uint32_t& meta) {
-  const uint32_t br = block_records(c);
-  const uint32_t k = idx / br, l = idx - k * br;
-  const uint32_t m = min(br, n_c - k * br);
-  const uint32_t base = seg + k * block_bytes(c, br);
-  codes = base + (8u << c) * l;
-  so = base + codes_area(c, m) + 4u * l;
-  meta = base + codes_area(c, m) + so_area(m) + 2u * l;
-}
-
 // Builds the per-k-group record lists of k-tile kt for row-tiles
-// [rt0, rt0 + nrt). Offsets are relative to the first byte of tile (kt, rt0).
-// Every thread owns up to 2 records of each of the 4 tiles; all their meta and
-// scale/offset loads are issued together (two memory round trips in all),
-// then the lists are built in LDS: count per (k-group, class), turn counts
-// into starts, place.
-constexpr int kRecPerThread = kTile * kTileGroups / kThreads;   // 2 per tile
-
+// [rt0, rt0 + nrt). Code offsets are relative to the first byte of tile
+// (kt, rt0) (the two tiles are consecutive in the stream).
+//   1. wavefront r < nrt reads the map of tile (kt, rt0 + r), lane l on
+//      column l, and adds its per-class row counts to cnt[l][class];
+//   2. counts become list starts per k-group in class order 8, 1, 2, 4-bit;
+//   3. the same wavefronts walk their tile's blocks and place every record
+//      (codes offset, row, class; the scale/offset's stream offset for now);
+//   4. every thread loads the scale/offset words of eight list entries, all
+//      at once, and writes them into the entries.
 __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs& a, GemmSmem& S, int kt, int rt0, int nrt,
                                                                   uint32_t base16, int tid) {
   for (int i = tid; i < kTileGroups * 4; i += kThreads) (&S.cnt[0][0])[i] = 0;
-  const uint8_t* wg_bytes = a.stream + (size_t)base16 * 16u;
-  // The headers of all row-tiles are loaded before any is used (a row-tile
-  // past the matrix reads the last one's and then counts as empty).
-  uint4 hdr[kRowTilesPerWg];
-#pragma unroll
-  for (int r = 0; r < kRowTilesPerWg; ++r)
-    hdr[r] = *reinterpret_cast<const uint4*>(a.tiles + 4 * (size_t)(kt * a.RT + min(rt0 + r, a.RT - 1)));
-  // per record slot: tag = codes offset / 8 | row << 17 | class << 24 | k-group << 26
-  uint32_t tag[kRowTilesPerWg][kRecPerThread], sov[kRowTilesPerWg][kRecPerThread];
-  uint32_t meta[kRowTilesPerWg][kRecPerThread], co[kRowTilesPerWg][kRecPerThread];
-  uint32_t cls[kRowTilesPerWg][kRecPerThread];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int r = 0; r < kRowTilesPerWg; ++r) {
-    const uint4 h = hdr[r];
-    const bool live = r < nrt;
-    const uint32_t n[4] = {live ? h.z & 0xFFFFu : 0u, live ? h.z >> 16 : 0u, live ? h.w & 0xFFFFu : 0u,
-                           live ? h.w >> 16 : 0u};
-    const uint32_t total = n[0] + n[1] + n[2] + n[3];
-    uint32_t seg[4];
-    seg[0] = (h.y - base16) * 16u;   // tile start, relative
-    seg[1] = seg[0] + (uint32_t)seg_bytes(0, n[0]);
-    seg[2] = seg[1] + (uint32_t)seg_bytes(1, n[1]);
-    seg[3] = seg[2] + (uint32_t)seg_bytes(2, n[2]);
-#pragma unroll
-    for (int it = 0; it < kRecPerThread; ++it) {
-      // every slot issues its two loads, a slot without a record from the
-      // workgroup's first byte (always inside the stream), and nothing reads
-      // them before all are issued
-      const uint32_t i = (uint32_t)(tid + it * kThreads);
-      const bool has = i < total;
-      int c = 0;
-      uint32_t idx = has ? i : 0u;
-      while (c < 3 && idx >= n[c]) {
-        idx -= n[c];
-        ++c;
-      }
-      uint32_t so = 0, mo = 0;
-      co[r][it] = 0;
-      if (has) record_offsets(c, idx, n[c], seg[c], co[r][it], so, mo);
-      meta[r][it] = *reinterpret_cast<const uint16_t*>(wg_bytes + mo);
-      sov[r][it] = *reinterpret_cast<const uint32_t*>(wg_bytes + so);
-      cls[r][it] = (uint32_t)c;
-      valid |= has ? 1u << (r * kRecPerThread + it) : 0u;
-    }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, a.G - g0);
+  const bool mine = wave < nrt;
+  const bool live = mine && lane < Gt;
+  uint32_t tbase = 0, iw = 0;
+  ClassMasks km = class_masks(0u, 0u, 0);
+  if (mine) {
+    const int rt = rt0 + wave;
+    const uint4 h = *reinterpret_cast<const uint4*>(a.tiles + 4 * (size_t)(kt * a.RT + rt));
+    tbase = (h.x - base16) * 16u;
+    iw = h.z;
+    const int R = min(kTileRows, a.N - rt * kTileRows);
+    const uint2 mp = live ? *reinterpret_cast<const uint2*>(a.stream + (size_t)h.x * 16u + 8u * (uint32_t)lane)
+                          : make_uint2(0u, 0u);
+    km = class_masks(mp.x, mp.y, live ? R : 0);
   }
-#pragma unroll
-  for (int r = 0; r < kRowTilesPerWg; ++r)
-#pragma unroll
-    for (int it = 0; it < kRecPerThread; ++it) {
-      const uint32_t mt = meta[r][it];
-      const uint32_t row = (uint32_t)r * kTile + (mt & 15u);
-      tag[r][it] = (co[r][it] >> 3) | (row << 17) | (cls[r][it] << 24) | (((mt >> 4) & 63u) << 26);
-    }
   gemm_barrier();   // counters zeroed
+  if (live)
 #pragma unroll
-  for (int r = 0; r < kRowTilesPerWg; ++r)
-#pragma unroll
-    for (int it = 0; it < kRecPerThread; ++it)
-      if (valid >> (r * kRecPerThread + it) & 1u) atomicAdd(&S.cnt[tag[r][it] >> 26][(tag[r][it] >> 24) & 3u], 1u);
+    for (int c = 0; c < 4; ++c)
+      if (km.m[c]) atomicAdd(&S.cnt[lane][c], (uint32_t)__popc(km.m[c]));
   gemm_barrier();
   if (tid < kTileGroups) {
     // Class order in a k-group's list: 8-bit, 1-bit, 2-bit, 4-bit. Producer
@@ -183,15 +135,48 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
     }
   }
   gemm_barrier();
+  if (mine) {
+    uint32_t pos = tbase + map_bytes((uint32_t)Gt);
 #pragma unroll
-  for (int r = 0; r < kRowTilesPerWg; ++r)
-#pragma unroll
-    for (int it = 0; it < kRecPerThread; ++it)
-      if (valid >> (r * kRecPerThread + it) & 1u) {
-        const uint32_t tg = tag[r][it];
-        const uint32_t slot = atomicAdd(&S.cnt[tg >> 26][(tg >> 24) & 3u], 1u);
-        S.ent[tg >> 26][slot] = make_uint2(tg & 0x3FFFFFFu, sov[r][it]);
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t I = (iw >> (8 * c)) & 0xFFu;
+      const uint32_t n = (uint32_t)__popc(km.m[c]);
+      uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
+      for (uint32_t i = 0; i < I; ++i) {
+        const bool act = n > i;
+        const uint64_t bal = __ballot(act);
+        const uint32_t m = (uint32_t)__popcll(bal);
+        const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
+        if (act) {
+          const uint32_t j = (uint32_t)__builtin_ctz(rot);
+          rot &= rot - 1u;
+          const uint32_t row = (uint32_t)wave * kTileRows + ((j + (uint32_t)lane) & 31u);
+          const uint32_t co = pos + (8u << c) * kk, so = pos + codes_area(c, m) + 4u * kk;
+          const uint32_t slot = atomicAdd(&S.cnt[lane][c], 1u);
+          S.ent[lane][slot] = make_uint2((co >> 3) | (row << 17) | ((uint32_t)c << 24), so);
+        }
+        pos += block_bytes(c, m);
       }
+    }
+  }
+  gemm_barrier();
+  // Each k-group lists one record per row of the workgroup.
+  const int nvalid = min(kBN, a.N - rt0 * kTileRows);
+  constexpr int kPer = kTileGroups * kBN / kThreads;   // entries per thread: 8
+  uint32_t sov[kPer];
+  const uint8_t* wg_bytes = a.stream + (size_t)base16 * 16u;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int idx = tid + e * kThreads, kg = idx / kBN, slot = idx % kBN;
+    const bool has = kg < Gt && slot < nvalid;
+    const uint32_t off = has ? S.ent[kg][slot].y : 0u;
+    sov[e] = *reinterpret_cast<const uint32_t*>(wg_bytes + off);
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int idx = tid + e * kThreads, kg = idx / kBN, slot = idx % kBN;
+    if (kg < Gt && slot < nvalid) S.ent[kg][slot].y = sov[e];
+  }
   gemm_barrier();
 }
 
@@ -212,8 +197,8 @@ struct CodeRegs {
 // b >= 2 (b / 2 words); a 1-bit quarter is bits 8 (Q % 2) + [0, 8) and
 // 16 + 8 (Q % 2) + [0, 8) of word Q / 2. Records are 8 << class bytes and
 // blocks 16-byte aligned, so those words never cross a 16-byte boundary, and
-// the window stays inside the record's block (its scale/offset and meta
-// areas follow the codes).
+// the window stays inside the record's block (its scale/offset area follows
+// the codes).
 __device__ inline uint2 list_entry(const GemmSmem& S, int kgl, int nvalid, int tid) {
   const int slot = tid >> 2;
   return slot < nvalid ? S.ent[kgl][slot] : make_uint2(0, 0);
@@ -342,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   const int m0 = mt * kBM;
   const int rt0 = nt * kRowTilesPerWg;
   const int nrt = min(kRowTilesPerWg, a.RT - rt0);
-  const int nvalid = min(kBN, a.N - rt0 * kTile);
+  const int nvalid = min(kBN, a.N - rt0 * kTileRows);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -373,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   const int KT = (a.G + kTileGroups - 1) / kTileGroups;
   for (int kt = 0; kt < KT; ++kt) {
     const int g0 = kt * kTileGroups, g1 = min(a.G, g0 + kTileGroups);
-    const uint32_t base16 = a.tiles[4 * (size_t)(kt * a.RT + rt0) + 1];
+    const uint32_t base16 = a.tiles[4 * (size_t)(kt * a.RT + rt0) + 0];
     build_index(a, S, kt, rt0, nrt, base16, tid);
     // The two roles run loops of their own with the same barrier schedule:
     // in one shared loop body the compiler merges their load-count state and
@@ -460,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = rt0 * kTile + 32 * j + (lane & 31);
+      const int n = rt0 * kTileRows + 32 * j + (lane & 31);
       if (n >= a.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

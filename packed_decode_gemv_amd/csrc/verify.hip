@@ -2,9 +2,9 @@
 //
 // CellFill abstract (page "Nothing Changed but the Model: CellFill -- Bounded
 // In-Cell Learning for Bit-Identical, Revocable Updates to Quantized LLMs"):
-// with the integer codes and scales of a release frozen, the update lives in a
-// per-weight residual strictly inside each quantisation cell, and
-// re-quantisation returns the released artifact bit-for-bit. For every weight
+// the release's codes and scales are not touched, an update is a per-weight
+// residual that must stay within the weight's rounding cell, and rounding the
+// updated weights again must reproduce the released codes exactly. For every weight
 // this kernel re-quantises the served value (dequantised code + residual)
 // against the frozen scale and offset, counts codes that change and residuals
 // that leave the cell, keeps the smallest failing index, and optionally writes
@@ -27,19 +27,6 @@ __global__ void k_verify_init(uint64_t* result) {
     result[2] = ~0ull;
   }
 }
-
-// One quarter of a record: 16 consecutive weights (codes 16q .. 16q + 15).
-// The pair layout puts them in pairs 8q .. 8q + 7, i.e. in words
-// [8q / H, (8q + 7) / H] of the record (H = 16 / b pairs per word): loaded as
-// one 16-byte read starting at word 8q / H (reading past the record stays in
-// its block, whose scale/offset and meta areas follow the codes).
-struct Quarter {
-  uint4 w;         // words from 8q / H on
-  uint32_t so;     // scale | offset << 16
-  uint32_t meta;   // row | k-group << 4
-  uint32_t wbyte;  // byte offset of w in the stream
-  int c;           // width class, -1 if no record
-};
 
 // Re-quantises the 16 weights of a quarter with correctly rounded quotients:
 // counts into lm / lo, smallest failing index into lf, re-quantised code words
@@ -143,134 +130,149 @@ __device__ __attribute__((noinline)) QuarterResult quarter_exact(uint4 w4, uint4
   return res;
 }
 
+// Checks one record (its 64 weights as four quarters of 16) of class C:
+// w = the record's 2b code words, rv = its 64 residuals (32 pairs), lin0 =
+// linear index of its first weight. Counts, first failing index and the
+// re-quantised words (nw) are accumulated into the lane's state.
 template <int C>
-__device__ inline void check_quarter(const Quarter& Qr, int q, int r0, int g0, int K, const uint4 (&rv)[2],
-                                     uint32_t& mism, uint32_t& ooc, uint64_t& first, uint32_t (&nw)[4]) {
-  const uint32_t w[4] = {Qr.w.x, Qr.w.y, Qr.w.z, Qr.w.w};
-  const float s = __half2float(__ushort_as_half((unsigned short)(Qr.so & 0xFFFF)));
-  const float o = __half2float(__ushort_as_half((unsigned short)(Qr.so >> 16)));
-  const bool fast = s > 0.0f && s <= 65504.0f && quarter_fast<C>(w, rv, s, o, q, nw);
-  if (!fast) {
-    const int row = r0 + (int)(Qr.meta & 15), kg = g0 + (int)(Qr.meta >> 4);
-    const uint64_t lin0 = (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * (uint32_t)q;
-    const QuarterResult e = quarter_exact<C>(Qr.w, rv[0], rv[1], s, o, q, lin0);
-    nw[0] = e.nw.x;
-    nw[1] = e.nw.y;
-    nw[2] = e.nw.z;
-    nw[3] = e.nw.w;
-    mism += e.lm;
-    ooc += e.lo;
-    first = e.lf < first ? e.lf : first;
+__device__ inline void check_record(const uint32_t* w, const uint4 (&rv)[8], uint32_t so, uint64_t lin0,
+                                    uint32_t& mism, uint32_t& ooc, uint64_t& first, uint32_t* nw) {
+  constexpr int B = 1 << C, H = 16 / B, NWORD = 2 * B;
+  const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
+  const float o = __half2float(__ushort_as_half((unsigned short)(so >> 16)));
+#pragma unroll
+  for (int i = 0; i < NWORD; ++i) nw[i] = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int wbase = (8 * q) / H;
+    uint32_t win[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) win[i] = (wbase + i < NWORD) ? w[wbase + i < NWORD ? wbase + i : 0] : 0u;
+    const uint4 rq[2] = {rv[2 * q], rv[2 * q + 1]};
+    uint32_t qw[4];
+    const bool fast = s > 0.0f && s <= 65504.0f && quarter_fast<C>(win, rq, s, o, q, qw);
+    if (!fast) {
+      const QuarterResult e = quarter_exact<C>(make_uint4(win[0], win[1], win[2], win[3]), rq[0], rq[1], s, o, q,
+                                               lin0 + 16u * (uint32_t)q);
+      qw[0] = e.nw.x;
+      qw[1] = e.nw.y;
+      qw[2] = e.nw.z;
+      qw[3] = e.nw.w;
+      mism += e.lm;
+      ooc += e.lo;
+      first = e.lf < first ? e.lf : first;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (wbase + i < NWORD) nw[(wbase + i) < NWORD ? wbase + i : 0] |= qw[i];
   }
 }
 
-// One workgroup of 256 threads per tile (several resident per CU, so one's
-// memory round trips overlap another's arithmetic), four lanes per record (a
-// quarter each), sixteen quarters per lane in batches of two (at most 96
-// VGPRs: five wavefronts per SIMD). All loads of a batch are issued together:
-// the records' codes, scale/offset and meta, then the residuals the meta
-// points at.
-constexpr int kVerifyThreads = 256;
+// One workgroup of four wavefronts per tile. Every wavefront walks the tile's
+// blocks (lane l on column l, so that it knows each record's row) and checks
+// the records of every fourth block: codes and scale/offset from the block,
+// the record's 64 residuals from row row, columns 64 (64 kt + l) .. + 63.
+constexpr int kVerifyWaves = 4;
 
-// Without the re-quantised stream, a tile's records are split over
-// kVerifyParts workgroups (more round trips in flight per CU); with it, one
-// workgroup per tile copies the tile and rewrites its codes.
-constexpr int kVerifyParts = 4;
+template <int C>
+__device__ inline void verify_block(const uint8_t* tb, uint8_t* rb, uint32_t pos, uint32_t m, uint32_t kk,
+                                    const uint16_t* __restrict__ resid, uint64_t lin0, size_t roff, uint32_t& mism,
+                                    uint32_t& ooc, uint64_t& first) {
+  constexpr int B = 1 << C;
+  uint32_t w[2 * B];
+  const uint8_t* cp = tb + pos + (8u * B) * kk;
+  if constexpr (C == 0) {
+    const uint2 u = *reinterpret_cast<const uint2*>(cp);
+    w[0] = u.x;
+    w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < B / 2; ++h) {
+      const uint4 u = reinterpret_cast<const uint4*>(cp)[h];
+      w[4 * h + 0] = u.x;
+      w[4 * h + 1] = u.y;
+      w[4 * h + 2] = u.z;
+      w[4 * h + 3] = u.w;
+    }
+  }
+  const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + pos + codes_area(C, m) + 4u * kk);
+  uint4 rv[8];
+  const uint4* rp = reinterpret_cast<const uint4*>(resid + roff);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rv[i] = rp[i];
+  uint32_t nw[2 * B];
+  check_record<C>(w, rv, so, lin0, mism, ooc, first, nw);
+  if (rb) {
+    uint8_t* dp = rb + pos + (8u * B) * kk;
+    if constexpr (C == 0) {
+      *reinterpret_cast<uint2*>(dp) = make_uint2(nw[0], nw[1]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < B / 2; ++h)
+        reinterpret_cast<uint4*>(dp)[h] = make_uint4(nw[4 * h + 0], nw[4 * h + 1], nw[4 * h + 2], nw[4 * h + 3]);
+    }
+  }
+}
 
-__global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __restrict__ tiles,
-                                                           const uint8_t* __restrict__ stream, int G, int RT,
-                                                           const uint16_t* __restrict__ resid, uint64_t* result,
-                                                           uint8_t* requant, int parts) {
+__global__ __launch_bounds__(kVerifyWaves * 64) void k_verify(const uint32_t* __restrict__ tiles,
+                                                               const uint8_t* __restrict__ stream, int N, int G,
+                                                               int RT, const uint16_t* __restrict__ resid,
+                                                               uint64_t* result, uint8_t* requant) {
   __shared__ uint32_t s_mism, s_ooc;
   __shared__ unsigned long long s_first;
-  const int t = (int)blockIdx.x / parts, part = (int)blockIdx.x - t * parts, tid = threadIdx.x;
+  const int t = (int)blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid == 0) {
     s_mism = 0;
     s_ooc = 0;
     s_first = ~0ull;
   }
-  const int K = G * kGroup;
+  const size_t K = (size_t)G * kGroup;
   const int kt = t / RT, rt = t - kt * RT;
-  const int r0 = rt * kTile, g0 = kt * kTileGroups;
-  const uint64_t tb = (uint64_t)tiles[4 * t + 1] * 16;
-  const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
-  const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
-  const uint32_t sb[4] = {0, (uint32_t)seg_bytes(0, n[0]), (uint32_t)(seg_bytes(0, n[0]) + seg_bytes(1, n[1])),
-                          (uint32_t)(seg_bytes(0, n[0]) + seg_bytes(1, n[1]) + seg_bytes(2, n[2]))};
-  const uint32_t size = sb[3] + (uint32_t)seg_bytes(3, n[3]);
-  const uint8_t* tbytes = stream + tb;
-  uint8_t* rbytes = requant ? requant + tb : nullptr;
-  // Copy the tile (scales, offsets, meta, padding); codes are rewritten below.
-  if (rbytes)
-    for (uint32_t i = tid; i < size / 16; i += kVerifyThreads)
-      reinterpret_cast<uint4*>(rbytes)[i] = reinterpret_cast<const uint4*>(tbytes)[i];
+  const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
+  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
+  const uint64_t tbyte = (uint64_t)tiles[4 * t + 0] * 16;
+  const uint32_t size = tiles[4 * t + 1] * 16, iw = tiles[4 * t + 2];
+  const uint8_t* tb = stream + tbyte;
+  uint8_t* rb = requant ? requant + tbyte : nullptr;
+  // Copy the tile (map, scales, offsets, padding); codes are rewritten below.
+  if (rb)
+    for (uint32_t i = tid; i < size / 16; i += kVerifyWaves * 64)
+      reinterpret_cast<uint4*>(rb)[i] = reinterpret_cast<const uint4*>(tb)[i];
   __syncthreads();
-  const uint32_t total = n[0] + n[1] + n[2] + n[3];
-  const int q = tid & 3;
+  const bool live = lane < Gt;
+  const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
+  const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
   uint32_t mism = 0, ooc = 0;
   uint64_t first = ~0ull;
-  constexpr int kPer = kTile * kTileGroups * 4 / kVerifyThreads;   // quarters per thread: 16
-  constexpr int kBatch = 2;                                         // quarters loaded together
-  const int per = kPer / parts;                                     // quarters of this workgroup per thread
-  const uint32_t ibase = (uint32_t)(part * per) * (kVerifyThreads / 4);
-  for (int b0 = 0; b0 < per; b0 += kBatch) {
-    Quarter Q[kBatch];
+  uint32_t pos = map_bytes((uint32_t)Gt);
+  uint32_t blk = 0;   // block index within the tile
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t i = ibase + (uint32_t)(tid >> 2) + (uint32_t)(b0 + u) * (kVerifyThreads / 4);
-      Q[u].c = -1;
-      Q[u].wbyte = 0;
-      if (i < total) {
-        int c = 0;
-        uint32_t idx = i;
-        while (c < 3 && idx >= n[c]) {
-          idx -= n[c];
-          ++c;
-        }
-        const uint32_t br = block_records(c), k = idx / br, l = idx - k * br, m = min(br, n[c] - k * br);
-        const uint32_t blk = sb[c] + k * (uint32_t)block_bytes(c, br);
-        const uint32_t H = 16u >> c;
-        Q[u].c = c;
-        Q[u].wbyte = blk + (8u << c) * l + 4u * ((8u * (uint32_t)q) / H);
-        Q[u].so = *reinterpret_cast<const uint32_t*>(tbytes + blk + codes_area(c, m) + 4u * l);
-        Q[u].meta = *reinterpret_cast<const uint16_t*>(tbytes + blk + codes_area(c, m) + so_area(m) + 2u * l);
-        // 4-byte aligned; a 16-byte read from here stays inside the block
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(tbytes + Q[u].wbyte);
-        Q[u].w = make_uint4(wp[0], wp[1], wp[2], wp[3]);
-      }
-    }
-    uint4 R[kBatch][2];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      R[u][0] = R[u][1] = make_uint4(0, 0, 0, 0);
-      if (Q[u].c >= 0) {
-        const int row = r0 + (int)(Q[u].meta & 15), kg = g0 + (int)(Q[u].meta >> 4);
-        const uint4* rp =
-            reinterpret_cast<const uint4*>(resid + (uint64_t)row * K + (uint64_t)kg * kGroup + 16u * q);
-        R[u][0] = rp[0];
-        R[u][1] = rp[1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int c = Q[u].c;
-      uint32_t nw[4];
-      if (c == 0) check_quarter<0>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
-      else if (c == 1) check_quarter<1>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
-      else if (c == 2) check_quarter<2>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
-      else if (c == 3) check_quarter<3>(Q[u], q, r0, g0, K, R[u], mism, ooc, first, nw);
-      if (c < 0) continue;
-      // 1-bit: the two quarters of one code word combine their bits
-      if (c == 0) nw[0] |= __shfl_xor(nw[0], 1, kWave);
-      if (rbytes) {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(rbytes + Q[u].wbyte);
-        if (c == 0) {
-          if ((q & 1) == 0) dst[0] = nw[0];
-        } else {
-          const int nword = c == 1 ? 1 : c == 2 ? 2 : 4;
-          for (int i = 0; i < nword; ++i) dst[i] = nw[i];
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t I = (iw >> (8 * c)) & 0xFFu;
+    const uint32_t n = (uint32_t)__popc(km.m[c]);
+    uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
+    for (uint32_t i = 0; i < I; ++i, ++blk) {
+      const bool act = n > i;
+      const uint64_t bal = __ballot(act);
+      const uint32_t m = (uint32_t)__popcll(bal);
+      const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
+      if (act) {
+        const uint32_t j = (uint32_t)__builtin_ctz(rot);
+        rot &= rot - 1u;
+        if ((int)(blk % kVerifyWaves) == wave) {
+          const int row = r0 + (int)((j + (uint32_t)lane) & 31u);
+          const size_t roff = (size_t)row * K + (size_t)(g0 + lane) * kGroup;
+          const uint64_t lin0 = (uint64_t)roff;
+          switch (c) {
+            case 0: verify_block<0>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
+            case 1: verify_block<1>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
+            case 2: verify_block<2>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
+            default: verify_block<3>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
+          }
         }
       }
+      pos += block_bytes(c, m);
     }
   }
   if (mism) atomicAdd(&s_mism, mism);
@@ -287,24 +289,25 @@ __global__ __launch_bounds__(kVerifyThreads, 5) void k_verify(const uint32_t* __
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
-  const int parts = requant ? 1 : kVerifyParts;
-  if ((int64_t)m.n_tiles * parts > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_verify, dim3((unsigned)(m.n_tiles * parts)), dim3(kVerifyThreads), 0, s, m.tiles,
-                     reinterpret_cast<const uint8_t*>(m.stream), m.n_cols / kGroup, row_tiles(m.n_rows), resid,
-                     result, reinterpret_cast<uint8_t*>(requant), parts);
+  if (m.n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(kVerifyWaves * 64), 0, s, m.tiles,
+                     reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, m.n_cols / kGroup, row_tiles(m.n_rows),
+                     resid, result, reinterpret_cast<uint8_t*>(requant));
   return hipGetLastError();
 }
 
 // ---- Drift bound ------------------------------------------------------------
 // bound[b][n] = 0.5 * sum_g s[n][g] * X[b][g],  X[b][g] = sum_{k in g} |x[b][k]|:
 // with every residual strictly inside half its group's scale, no output moves
-// further than this (CellFill abstract: bounded drift). One workgroup per
-// row-tile walks its k-tiles in order. Per k-tile it forms X for the tile's
-// groups (fp32, in k order); every record puts 0.5 s X[b][g] at its (row,
-// group) slot in LDS (a row has exactly one record per group); and one thread
-// per (batch row, row) adds its slots in group order, so the sum order is
-// fixed.
+// further than this (CellFill abstract: bounded drift). One workgroup of four
+// wavefronts per row-tile walks its k-tiles in order. Per k-tile it forms X
+// for the tile's groups (fp32, in k order); the wavefronts split the tile's
+// blocks (lane l on column l) and every record puts 0.5 s X[b][l] at its
+// (row, column) slot in LDS (a row has exactly one record per column); then
+// one thread per (batch row, row) adds its slots in column order, so the sum
+// order is fixed. Batches above four rows run as passes.
 constexpr int kDriftThreads = 256;
+constexpr int kDriftNb = 4;
 
 template <int NB>
 __global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restrict__ tiles,
@@ -312,18 +315,20 @@ __global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restr
                                                          const uint16_t* __restrict__ x, int N, int G, int RT,
                                                          float* __restrict__ bound) {
   __shared__ float X[NB][kTileGroups];
-  __shared__ float P[NB][kTile][kTileGroups + 1];
-  const int rt = (int)blockIdx.x, tid = threadIdx.x;
+  __shared__ float P[NB][kTileRows][kTileGroups + 1];
+  const int rt = (int)blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = G * kGroup;
-  const int b_own = tid / kTile, r_own = tid % kTile;   // summed by this thread while tid < NB * 16
+  const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
+  const int b_own = tid / kTileRows, r_own = tid % kTileRows;   // summed by this thread while tid < NB * 32
   float acc = 0.0f;
   const int KT = k_tiles(G);
   for (int kt = 0; kt < KT; ++kt) {
-    const int g0 = kt * kTileGroups, ng = min(kTileGroups, G - g0);
+    const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
     for (int i = tid; i < NB * kTileGroups; i += kDriftThreads) {
       const int b = i / kTileGroups, g = i - b * kTileGroups;
       float sx = 0.0f;
-      if (g < ng) {
+      if (g < Gt) {
         const uint16_t* xr = x + (size_t)b * K + (size_t)(g0 + g) * kGroup;
         for (int j = 0; j < kGroup; ++j) sx += fabsf(__half2float(__ushort_as_half(xr[j])));
       }
@@ -331,57 +336,65 @@ __global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restr
     }
     __syncthreads();
     const int t = kt * RT + rt;
-    const uint8_t* tb = stream + (size_t)tiles[4 * t + 1] * 16;
-    const uint32_t a = tiles[4 * t + 2], bb = tiles[4 * t + 3];
-    const uint32_t n[4] = {a & 0xFFFF, a >> 16, bb & 0xFFFF, bb >> 16};
-    const uint32_t s1 = (uint32_t)seg_bytes(0, n[0]), s2 = s1 + (uint32_t)seg_bytes(1, n[1]);
-    const uint32_t sb[4] = {0u, s1, s2, s2 + (uint32_t)seg_bytes(2, n[2])};
-    const uint32_t total = n[0] + n[1] + n[2] + n[3];
-    for (uint32_t i = tid; i < total; i += kDriftThreads) {
-      int c = 0;
-      uint32_t idx = i;
-      while (c < 3 && idx >= n[c]) {
-        idx -= n[c];
-        ++c;
-      }
-      const uint32_t br = block_records(c), k = idx / br, l = idx - k * br, m = min(br, n[c] - k * br);
-      const uint32_t blk = sb[c] + k * (uint32_t)block_bytes(c, br);
-      const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + blk + codes_area(c, m) + 4u * l);
-      const uint32_t meta = *reinterpret_cast<const uint16_t*>(tb + blk + codes_area(c, m) + so_area(m) + 2u * l);
-      const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
-      const int row = (int)(meta & 15u), g = (int)((meta >> 4) & (uint32_t)(kTileGroups - 1));
+    const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
+    const uint32_t iw = tiles[4 * t + 2];
+    const bool live = lane < Gt;
+    const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
+    const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
+    uint32_t pos = map_bytes((uint32_t)Gt), blk = 0;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) P[b][row][g] = hs * X[b][g];
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t I = (iw >> (8 * c)) & 0xFFu;
+      const uint32_t n = (uint32_t)__popc(km.m[c]);
+      uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
+      for (uint32_t i = 0; i < I; ++i, ++blk) {
+        const bool act = n > i;
+        const uint64_t bal = __ballot(act);
+        const uint32_t m = (uint32_t)__popcll(bal);
+        const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
+        if (act) {
+          const uint32_t j = (uint32_t)__builtin_ctz(rot);
+          rot &= rot - 1u;
+          if ((int)(blk % 4u) == wave) {
+            const int row = (int)((j + (uint32_t)lane) & 31u);
+            const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + pos + codes_area(c, m) + 4u * kk);
+            const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) P[b][row][lane] = hs * X[b][lane];
+          }
+        }
+        pos += block_bytes(c, m);
+      }
     }
     __syncthreads();
-    if (tid < NB * kTile)
-      for (int g = 0; g < ng; ++g) acc += P[b_own][r_own][g];
+    if (tid < NB * kTileRows)
+      for (int g = 0; g < Gt; ++g) acc += P[b_own][r_own][g];
     __syncthreads();   // X and P are rewritten for the next k-tile
   }
-  const int row = rt * kTile + r_own;
-  if (tid < NB * kTile && row < N) bound[(size_t)b_own * N + row] = acc;
+  if (tid < NB * kTileRows && r_own < R) bound[(size_t)b_own * N + r0 + r_own] = acc;
 }
 
 hipError_t launch_drift(const vbq_matrix& m, const uint16_t* x, int B, float* bound, hipStream_t s) {
   const int RT = row_tiles(m.n_rows), G = m.n_cols / kGroup;
   const uint8_t* st = reinterpret_cast<const uint8_t*>(m.stream);
-#define VBQ_DRIFT(NB)                                                                                   \
-  case NB:                                                                                              \
-    hipLaunchKernelGGL(k_drift<NB>, dim3(RT), dim3(kDriftThreads), 0, s, m.tiles, st, x, m.n_rows, G, RT, bound); \
+  for (int b0 = 0; b0 < B; b0 += kDriftNb) {
+    const int nb = B - b0 < kDriftNb ? B - b0 : kDriftNb;
+    const uint16_t* xb = x + (size_t)b0 * m.n_cols;
+    float* yb = bound + (size_t)b0 * m.n_rows;
+#define VBQ_DRIFT(NB)                                                                                        \
+  case NB:                                                                                                   \
+    hipLaunchKernelGGL(k_drift<NB>, dim3(RT), dim3(kDriftThreads), 0, s, m.tiles, st, xb, m.n_rows, G, RT, yb); \
     break;
-  switch (B) {
-    VBQ_DRIFT(1)
-    VBQ_DRIFT(2)
-    VBQ_DRIFT(3)
-    VBQ_DRIFT(4)
-    VBQ_DRIFT(5)
-    VBQ_DRIFT(6)
-    VBQ_DRIFT(7)
-    VBQ_DRIFT(8)
-    default:
-      return hipErrorInvalidValue;
-  }
+    switch (nb) {
+      VBQ_DRIFT(1)
+      VBQ_DRIFT(2)
+      VBQ_DRIFT(3)
+      VBQ_DRIFT(4)
+      default:
+        return hipErrorInvalidValue;
+    }
 #undef VBQ_DRIFT
+  }
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = C.CDLL(vbq.LIB_PATH)
     for n in header_functions():
         assert hasattr(lib, n), f"{n} declared in vbq.h but not exported"
-    assert vbq.abi_version() == 2
+    assert vbq.abi_version() == 3
     assert vbq.lib.vbq_status_string(3) == b"width not in {1,2,4,8}"
 
 
@@ -45,9 +45,7 @@ def test_pack_query_matches_oracle(shape):
     assert (s.n_tiles, s.n_records, s.n_bytes16) == oracle.layout_sizes(w)
     lay = oracle.pack((np.random.default_rng(1).standard_normal((N, K)) * 0.02).astype(np.float32), w)
     tiles = lay["tiles"].reshape(-1, 4).astype(np.int64)
-    recs = (tiles[:-1, 2] & 0xFFFF) + (tiles[:-1, 2] >> 16) + (tiles[:-1, 3] & 0xFFFF) + (tiles[:-1, 3] >> 16)
-    bytes16 = np.diff(tiles[:, 1])
-    assert s.max_tile_records == int(recs.max()) and s.max_tile_bytes16 == int(bytes16.max())
+    assert s.max_tile_bytes16 == int(tiles[:-1, 1].max())
     assert s.code_bits == 64 * int(w.astype(np.int64).sum())
     assert list(s.groups_by_width) == [int((w == b).sum()) for b in (1, 2, 4, 8)]
 
@@ -66,9 +64,9 @@ def test_pack_query_rejects_bad_input():
 
 def _fake_matrix(vbq, N=32, K=128, align=256):
     # Descriptor with plausible (never dereferenced) device addresses.
-    T = ((N + 15) // 16) * ((K // 64 + 63) // 64)
+    T = ((N + 31) // 32) * ((K // 64 + 63) // 64)
     base = 0x7F0000000000
-    return vbq.vbq_matrix(N, K, T, N * (K // 64), 10, 8, base, base + align * 64)
+    return vbq.vbq_matrix(N, K, T, 10, base, base + align * 64)
 
 
 def test_compute_calls_reject_bad_arguments_without_a_gpu():
@@ -105,13 +103,14 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     assert L.cell_drift_bound(C.byref(m), x, 1, C.c_void_p(0x7F0000200002), None) == 4
     assert L.cell_drift_bound(C.byref(_fake_matrix(vbq, K=100)), x, 1, y, None) == 2
     assert L.vbq_residual_error(C.byref(m), None, y, None) == 1
-    assert L.vbq_residual_error(C.byref(m), x, C.c_void_p(0x7F0000200002), None) == 4
+    assert L.vbq_residual_error(C.byref(m), x, C.c_void_p(0x7F0000200004), None) == 4
     two = (vbq.vbq_matrix * 2)(m, _fake_matrix(vbq, N=48))
-    assert L.vbq_gemv_levels(2, two, x, 1, y, y, None) == 2          # levels of different shapes
-    assert L.vbq_gemv_levels(0, two, x, 1, y, y, None) == 1
+    assert L.vbq_gemv_levels(2, two, x, 1, y, None) == 2             # levels of different shapes
+    assert L.vbq_gemv_levels(0, two, x, 1, y, None) == 1
+    assert L.vbq_gemv_levels(33, two, x, 1, y, None) == 1           # more than one launch takes
     same = (vbq.vbq_matrix * 2)(m, m)
-    assert L.vbq_gemv_levels(2, same, x, 9, y, y, None) == 5
-    assert L.vbq_gemv_levels(2, same, x, 1, None, y, None) == 1
+    assert L.vbq_gemv_levels(2, same, x, 9, y, None) == 5
+    assert L.vbq_gemv_levels(2, same, x, 1, None, None) == 1
     assert L.vbq_pack(None, x, C.byref(m), None) == 1
     assert L.vbq_pack(C.c_void_p(0x7F0000100004), x, C.byref(m), None) == 4
     ms = (vbq.vbq_matrix * 2)(m, m)
@@ -119,3 +118,50 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     ys = (C.c_void_p * 2)(y.value, None)
     assert L.vbq_gemv_batched(2, ms, xs, ys, 1, None) == 1
     assert L.vbq_gemv_batched(0, ms, xs, ys, 1, None) == 1
+    many = (vbq.vbq_matrix * 33)(*([m] * 33))
+    xs33 = (C.c_void_p * 33)(*([x.value] * 33))
+    ys33 = (C.c_void_p * 33)(*([y.value] * 33))
+    assert L.vbq_gemv_batched(33, many, xs33, ys33, 1, None) == 1     # more than one launch takes
+
+
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """The C ABI cannot see tensor sizes, so the binding checks dtype, shape,
+    contiguity and device first; every case here raises ValueError without
+    reaching the library (no GPU is needed)."""
+    import torch
+
+    import packed_decode_gemv_amd as vbq
+    W = torch.zeros(32, 128)
+    widths = np.ones((32, 2), np.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        vbq.vbq_pack(W, widths)                                   # host tensor
+    with pytest.raises(ValueError, match="dtype"):
+        vbq.vbq_pack(W.half(), widths)
+    with pytest.raises(ValueError, match="contiguous"):
+        vbq.vbq_pack(torch.zeros(128, 32).t(), widths)
+    pm = vbq.PackedMatrix(32, 128, vbq.pack_query(widths), device="cpu")   # descriptor only, never launched
+    with pytest.raises(ValueError, match="dtype"):
+        vbq.vbq_gemv(pm, torch.zeros(1, 128, dtype=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        vbq.vbq_gemv(pm, torch.zeros(1, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="contiguous"):
+        vbq.vbq_gemv(pm, torch.zeros(256, dtype=torch.float16)[::2].view(1, 128))
+    with pytest.raises(ValueError, match="batch"):
+        vbq.vbq_gemv(pm, torch.zeros(9, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="residual: dtype"):
+        vbq.vbq_gemv(pm, torch.zeros(1, 128, dtype=torch.float16), residual=torch.zeros(32, 128))
+    with pytest.raises(ValueError, match="out: shape"):
+        vbq.vbq_gemv(pm, torch.zeros(2, 128, dtype=torch.float16), out=torch.zeros(1, 32))
+    with pytest.raises(ValueError, match="E: dtype"):
+        vbq.vbq_residual_error(pm, torch.zeros(32, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="residual: shape"):
+        vbq.cell_requant_verify(pm, torch.zeros(16, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="x: dtype"):
+        vbq.vbq_gemm(pm, torch.zeros(64, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="x: shape"):
+        vbq.cell_drift_bound(pm, torch.zeros(1, 256, dtype=torch.float16))
+    with pytest.raises(ValueError, match="different shapes"):
+        vbq.vbq_gemv_levels([pm, vbq.PackedMatrix(64, 128, vbq.pack_query(np.ones((64, 2), np.uint8)),
+                                                  device="cpu")], torch.zeros(1, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="widths"):
+        vbq.pack_query(np.ones(4, np.uint8))
