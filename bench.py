@@ -96,6 +96,8 @@ class Stack:
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
         self.weight_bytes = sum(pm.nbytes for (pm, _, _) in self.mats.values())
+        self.weights = sum(pm.N * pm.K for (pm, _, _) in self.mats.values())
+        self.code_bits = sum(pm.sizes.code_bits for (pm, _, _) in self.mats.values())
 
     def _make(self, cid, layer, pi, proj, B, dev):
         import torch
@@ -646,46 +648,71 @@ def gemm_workload(vbq, calls):
                 peak_tflop_per_s=PEAK_BF16_TFLOPS, flops=flops, M=M, K=proj.k, N=proj.n)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(stack, budget_s):
-    """The CPU oracle (single-threaded, as it stands) on a bounded sample of the
-    same workload: whole projections of the first layers, then LM head rows,
-    until about budget_s seconds of oracle GEMV time. The oracle packs the
-    same synthetic W itself (untimed); the timed part is its GEMV from the
-    packed layout: unpack, fp64 dequantise, fp64 dot. Its outputs double as a
-    sampled parity check of the GPU results."""
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    whole projections of the first layers, then LM head rows, until about
+    budget_s seconds of wall time. The oracle packs the same synthetic W
+    itself (untimed); the timed part is its GEMV from the packed layout
+    (unpack, fp64 dequantise, fp64 dot), run on every core this process may
+    use: the rows of a matrix are cut into slices and each worker thread
+    calls the oracle on its slice (the oracle runs in C and releases the
+    interpreter lock). Its outputs double as a sampled parity check of the GPU
+    results."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     import synth
     wl = synth.C3
     B = stack.B
+    cores = sorted(os.sched_getaffinity(0))
+    n_threads = len(cores)
     spent, done_bytes, done_w = 0.0, 0.0, 0
     worst, checked = 0.0, []
     order = [(layer, pi, proj) for layer in range(stack.layers) for pi, proj in enumerate(wl.projs)]
     order.insert(7, (-1, 0, wl.head))
-    for (layer, pi, proj) in order:
-        if spent >= budget_s:
-            break
-        key = synth.proj_key(3, layer, pi)
-        rows = proj.n
-        if layer == -1:
-            rows = min(proj.n, 16384)
-        G = proj.k // 64
-        widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix, rows=np.arange(rows))
-        W = synth.weights(synth.SEED, key, proj.n, proj.k, rows=np.arange(rows))
-        x = synth.x_f16(synth.SEED, key, B, proj.k)
-        lay = oracle.pack(W, widths)
-        t0 = time.perf_counter()
-        q, s, o, _ = oracle.unpack(lay)
-        y = oracle.gemv(q, s, o, x)
-        dt = time.perf_counter() - t0
-        spent += dt
-        sizes = stack.vbq.pack_query(widths)
-        done_bytes += algorithmic_bytes(sizes, rows, proj.k, B)
-        done_w += rows * proj.k
-        yg = stack.mats[(layer, pi)][2].cpu().numpy()[:, :rows].astype(np.float64)
-        rel = float(np.linalg.norm(yg - y) / np.linalg.norm(y))
-        worst = max(worst, rel)
-        checked.append(f"{'lm_head' if layer < 0 else f'L{layer}.{proj.name}'}[{rows}x{proj.k}]")
-    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=1, kind="oracle",
+    with ThreadPoolExecutor(n_threads) as ex:
+        for (layer, pi, proj) in order:
+            if spent >= budget_s:
+                break
+            key = synth.proj_key(3, layer, pi)
+            rows = proj.n
+            if layer == -1:
+                rows = min(proj.n, 16384 * max(1, n_threads // 8))
+            G = proj.k // 64
+            widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix, rows=np.arange(rows))
+            W = synth.weights(synth.SEED, key, proj.n, proj.k, rows=np.arange(rows))
+            x = synth.x_f16(synth.SEED, key, B, proj.k)
+            lay = oracle.pack(W, widths)
+            slices = np.array_split(np.arange(rows, dtype=np.int64), 4 * n_threads)
+
+            def run(sl, lay=lay, x=x):
+                q, s_, o, _ = oracle.unpack(lay, rows=sl)
+                return oracle.gemv(q, s_, o, x)
+
+            t0 = time.perf_counter()
+            parts = list(ex.map(run, slices))
+            dt = time.perf_counter() - t0
+            y = np.concatenate(parts, axis=1)
+            spent += dt
+            sizes = stack.vbq.pack_query(widths)
+            done_bytes += algorithmic_bytes(sizes, rows, proj.k, B)
+            done_w += rows * proj.k
+            yg = stack.mats[(layer, pi)][2].cpu().numpy()[:, :rows].astype(np.float64)
+            rel = float(np.linalg.norm(yg - y) / np.linalg.norm(y))
+            worst = max(worst, rel)
+            checked.append(f"{'lm_head' if layer < 0 else f'L{layer}.{proj.name}'}[{rows}x{proj.k}]")
+    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=n_threads, kind="oracle",
+                cpu=cpu_model(), threads="one oracle call per row slice on every core of the process's affinity",
                 sample=f"{len(checked)} matrices ({done_w / 1e6:.0f}M weights, batch {B}): "
                        + ", ".join(checked[:4]) + (" ..." if len(checked) > 4 else ""),
                 seconds=round(spent, 2)), dict(max_rel_l2=worst, matrices=len(checked), tol=2e-3)
@@ -823,6 +850,10 @@ def main(argv=None):
                       "a step's launches replayed as one HIP graph",
             "algorithmic_bytes_per_step": step_bytes,
             "packed_bytes_resident": stack.weight_bytes,
+            "weights": stack.weights,
+            "mean_code_bits": round(stack.code_bits / stack.weights, 4),
+            "algorithmic_bits_read_per_weight": round(8 * step_bytes / stack.weights, 4),
+            "stream_bits_per_weight": round(8 * stack.weight_bytes / stack.weights, 4),
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "us_per_layer": round(layer_us, 3),

@@ -104,7 +104,7 @@ typedef struct vbq_matrix {
   int32_t n_rows;      /* N, output features */
   int32_t n_cols;      /* K, input features, multiple of 64 */
   int64_t n_tiles;     /* ceil(N / 32) * ceil(K / 4096) */
-  int64_t n_bytes16;   /* size of `stream` in 16-byte units */
+  int64_t n_bytes16;   /* size of `stream` in 16-byte units, at most 2^27 - 1 (2 GiB - 16 bytes) */
   uint32_t* tiles;     /* device, (n_tiles + 1) * 4 words, 16-byte aligned */
   uint32_t* stream;    /* device, n_bytes16 * 4 words, 16-byte aligned */
 } vbq_matrix;
@@ -128,7 +128,8 @@ const char* vbq_status_string(int status);
 /* Host-only sizing of the execution layout (VBQ abstract: one width per
  * 64-weight group). widths_host: host, N x K/64 uint8 in natural (row,
  * k-group) order. out: host. Returns VBQ_ERR_SHAPE or VBQ_ERR_BITWIDTH on bad
- * input. Touches no GPU. */
+ * input, VBQ_ERR_UNSUPPORTED for a stream above 2 GiB - 16 bytes. Touches no
+ * GPU. */
 vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_layout_sizes* out);
 
 /* Quantise W and write the execution layout (offline step).

@@ -14,6 +14,9 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Largest stream, in 16-byte units: 2 GiB - 16 bytes.
+constexpr int64_t kMaxStream16 = 0x07FFFFFFll;
+
 vbq_status check_shape(int32_t N, int32_t K) {
   if (N < 1 || K < kGroup || K % kGroup != 0 || K / kGroup > VBQ_MAX_GROUPS) return VBQ_ERR_SHAPE;
   return VBQ_OK;
@@ -25,8 +28,10 @@ vbq_status check_matrix(const vbq_matrix* m) {
   if (st != VBQ_OK) return st;
   const int G = m->n_cols / kGroup;
   if (m->n_tiles != (int64_t)row_tiles(m->n_rows) * k_tiles(G)) return VBQ_ERR_CAPACITY;
-  // Stream byte offsets are 32-bit on the device.
-  if (m->n_bytes16 < 1 || m->n_bytes16 > 0x0FFFFFFFll) return VBQ_ERR_CAPACITY;
+  // Stream byte offsets are 32-bit on the device, and offsets from 2 GiB up
+  // are the GEMV's "no record" loads.
+  if (m->n_bytes16 < 1) return VBQ_ERR_CAPACITY;
+  if (m->n_bytes16 > kMaxStream16) return VBQ_ERR_UNSUPPORTED;
   if (!m->tiles || !m->stream) return VBQ_ERR_INVALID_ARG;
   if (!aligned(m->tiles, 16) || !aligned(m->stream, 16)) return VBQ_ERR_ALIGNMENT;
   return VBQ_OK;
@@ -77,10 +82,6 @@ uint64_t host_tile_bytes(const uint8_t* widths, int N, int G, int rt, int kt, ui
   return bytes;
 }
 
-// LDS ring per wavefront: 16 KiB while two workgroups per CU hold the whole
-// launch, else 8 KiB so that four fit.
-uint32_t pick_ring_bytes(int64_t n_wg) { return n_wg <= 2 * (int64_t)cu_count() ? 16384u : 8192u; }
-
 }  // namespace
 
 extern "C" {
@@ -122,6 +123,7 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
       bytes += tb;
       max_b = std::max(max_b, tb / 16);
     }
+  if (bytes / 16 > kMaxStream16) return VBQ_ERR_UNSUPPORTED;
   out->n_tiles = (int64_t)RT * KT;
   out->n_records = (int64_t)N * G;
   out->n_bytes16 = bytes / 16;
@@ -208,7 +210,6 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     }
     if (wg > 0x7FFFFFFF) return VBQ_ERR_UNSUPPORTED;
     L.n_mats = count;
-    L.ring_bytes = pick_ring_bytes(wg);
     if (launch_gemv(L, nb, resid != nullptr, (int)wg, stream) != hipSuccess) return VBQ_ERR_HIP;
   }
   return VBQ_OK;

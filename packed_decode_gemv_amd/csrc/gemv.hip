@@ -91,7 +91,11 @@ struct Consts {
 template <int C, int... P>
 __device__ inline Consts<C> make_consts_impl(std::integer_sequence<int, P...>) {
   Consts<C> k;
-  ((k.mask[P] = vconst<field_mask(C, P)>(), k.magic[P] = vconst<field_magic(P)>()), ...);
+  if constexpr (C == 3) {
+    k.magic[0] = vconst<0x64646464u>();
+  } else {
+    ((k.mask[P] = vconst<field_mask(C, P)>(), k.magic[P] = vconst<field_magic(P)>()), ...);
+  }
   return k;
 }
 
@@ -100,22 +104,33 @@ __device__ inline Consts<C> make_consts() {
   return make_consts_impl<C>(std::make_integer_sequence<int, 10>{});
 }
 
-// acc[nb][P % 4] += (bias + q_2P) x_2P + (bias + q_2P+1) x_2P+1 for pair P of
-// the record (four accumulators split the dependent chain).
-template <int C, int P, int NB>
-__device__ inline void pair_step(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32],
-                                 float (&a)[NB][4]) {
+// The fp16 pair (bias + q_2P, bias + q_2P+1) of pair P of a record. Eight-bit
+// codes take one byte permute: bytes q_2P and q_2P+1 of the word, each under
+// the exponent byte 0x64 (fp16 1024 + q); narrower codes take an AND-OR of
+// the field, shifted down first when it lies above the mantissa.
+template <int C, int P>
+__device__ inline uint32_t pair_h2(const Consts<C>& k, const uint32_t* w) {
   constexpr int H = 16 >> C, F = P % H, FP = field_pos(C, F);
-  const uint32_t src = shifted<shift_kind(C, F)>(w[P / H]);
-  const uint32_t hv = (src & k.mask[FP]) | k.magic[FP];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) a[nb][P & 3] = dot2(hv, xr[nb][P], a[nb][P & 3]);
+  if constexpr (C == 3) {
+    return __builtin_amdgcn_perm(k.magic[0], w[P / H], F ? 0x04030401u : 0x04020400u);
+  } else {
+    const uint32_t src = shifted<shift_kind(C, F)>(w[P / H]);
+    return (src & k.mask[FP]) | k.magic[FP];
+  }
 }
 
+// acc[nb][P % 2] += (bias + q_2P) x_2P + (bias + q_2P+1) x_2P+1 for pair P of
+// the record (two accumulators split the dependent chain).
 template <int C, int NB, int... P>
-__device__ inline void record_dot(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32], float (&a)[NB][4],
+__device__ inline void record_dot(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32], float (&a)[NB][2],
                                   std::integer_sequence<int, P...>) {
-  (pair_step<C, P, NB>(k, w, xr, a), ...);
+  (
+      [&] {
+        const uint32_t hv = pair_h2<C, P>(k, w);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) a[nb][P & 1] = dot2(hv, xr[nb][P], a[nb][P & 1]);
+      }(),
+      ...);
 }
 
 // sum over the record's pairs of bias(field) * (x_2P + x_2P+1).
@@ -129,116 +144,6 @@ __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB
   }
 }
 
-// ---- Synchronisation helpers ---------------------------------------------------
-
-// Waits until at most n vector-memory instructions of this wavefront are
-// outstanding (n is wavefront-uniform, clamped to [0, 63]). Loads complete in
-// issue order, so this waits for everything issued before the last n.
-// s_waitcnt takes its count as an immediate, so this jumps into a table of
-// 64 (wait, branch) pairs of 8 bytes each: s_getpc_b64 yields the address of
-// the next instruction and the table starts four 4-byte instructions later.
-__device__ inline void wait_vmcnt(int n) {
-  n = n < 0 ? 0 : (n > 63 ? 63 : n);
-  asm volatile(
-      "s_getpc_b64 s[94:95]\n\t"
-      "s_lshl3_add_u32 s96, %0, 16\n\t"
-      "s_add_u32 s94, s94, s96\n\t"
-      "s_addc_u32 s95, s95, 0\n\t"
-      "s_setpc_b64 s[94:95]\n\t"
-      "s_waitcnt vmcnt(0)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(1)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(2)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(3)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(4)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(5)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(6)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(7)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(8)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(9)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(10)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(11)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(12)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(13)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(14)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(15)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(16)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(17)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(18)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(19)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(20)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(21)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(22)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(23)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(24)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(25)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(26)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(27)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(28)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(29)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(30)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(31)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(32)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(33)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(34)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(35)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(36)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(37)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(38)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(39)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(40)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(41)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(42)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(43)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(44)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(45)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(46)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(47)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(48)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(49)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(50)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(51)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(52)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(53)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(54)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(55)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(56)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(57)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(58)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(59)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(60)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(61)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(62)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      "s_waitcnt vmcnt(63)\n\ts_branch .Lvbq_wait_end_%=\n\t"
-      ".Lvbq_wait_end_%=:"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(n))
-      : "s94", "s95", "s96", "scc", "memory");
-}
-
-// ---- Streaming ring --------------------------------------------------------------
-// A wavefront streams bytes [src, src + span) of a matrix's stream into its
-// LDS ring in 1 KiB pieces: piece p (stream bytes [1024 p, 1024 p + 1024) of
-// the span) goes to ring slot p mod S. Piece p is issued once every block
-// ending before byte 1024 (p - S + 1) of the span is decoded, i.e. up to
-// floor(pos / 1024) + S pieces are out after the blocks before pos; a block
-// ending at e needs the first ceil(e / 1024). A block holds at most 4352
-// bytes (64 eight-bit records and their scale/offset words), so it spans at
-// most six pieces and S >= 8 always has them in the ring at once.
-struct Ring {
-  u32x4 rsrc;
-  uint32_t lds;       // LDS address of slot 0
-  uint32_t slots;     // S (a power of two)
-  uint32_t src;       // stream byte of the first piece
-  uint32_t np;        // pieces of the span
-  uint32_t issued;    // pieces issued so far
-};
-
-__device__ inline void ring_issue(Ring& r, uint32_t upto, uint32_t lane16) {
-  upto = min(upto, r.np);
-  for (; r.issued < upto; ++r.issued)
-    dma16(r.rsrc, r.lds + ((r.issued & (r.slots - 1u)) << 10), r.src + (r.issued << 10) + lane16);
-}
-
 // ---- One tile -------------------------------------------------------------------
 template <int NB>
 struct TileX {
@@ -246,90 +151,133 @@ struct TileX {
   float xsum[NB];        // sum of the group's 64 activations
 };
 
-// Decodes the blocks of class C of a tile: I blocks, the lane's column holding
-// n records of the class (rows in mask, visited from the rotation at row l).
+// Per-wavefront row slots: the record of column l in row r puts its value at
+// slot l * kSlotPitch + r (each (row, column) pair has exactly one record per
+// tile, so plain stores suffice); slot 32 of a column takes the stores of
+// blocks the column has no record in. The pitch of 33 words puts the 32 rows
+// read at one column on different banks.
+constexpr int kSlotPitch = 33;
+constexpr int kSlotWords = kWave * kSlotPitch;   // per batch row: 2112 words, 8448 bytes
+
+// Buffer offset that lies outside every stream: loads from it return zeros
+// without touching memory.
+constexpr uint32_t kNoRecord = 0x80000000u;
+
+// The record of the lane in one block.
+template <int C>
+struct Rec {
+  uint32_t w[2 << C];
+  uint32_t so;
+};
+
+// Blocks of a class whose records are in flight while one is decoded: about
+// 6-9 KiB per wavefront at one batch row, fewer at more rows (their
+// activations take the registers).
 template <int C, int NB>
-__device__ inline void run_class(Ring& rg, const uint8_t* ring, uint32_t ring_mask, uint32_t I, uint32_t n,
-                                 uint32_t mask, const TileX<NB>& X, uint32_t& pos, float* Y, uint32_t lane) {
-  constexpr int B = 1 << C;
+__host__ __device__ constexpr int depth() {
+  return (16 >> C) / NB < 2 ? 2 : (16 >> C) / NB;
+}
+
+// Issues the loads of the lane's record in block i of a class whose stream
+// position is ipos (advanced past the block). A column takes part in block i
+// when it holds more than i records of the class; its record is the kk-th of
+// the block, kk counting the taking-part columns below it. Columns that do
+// not take part (and every column past the class's last block) load from
+// kNoRecord, so every block issues the same loads and the count waits stay
+// fixed.
+template <int C>
+__device__ inline void issue_block(__amdgpu_buffer_rsrc_t rs, uint32_t& ipos, uint32_t i, uint32_t n, Rec<C>& r) {
+  constexpr uint32_t RB = 8u << C;
+  const bool act = n > i;
+  const uint64_t bal = __ballot(act);
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)__popcll(bal));
+  const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
+  const uint32_t ca = codes_area(C, m);
+  const uint32_t oc = act ? ipos + RB * kk : kNoRecord;
+  const uint32_t os = act ? ipos + ca + 4u * kk : kNoRecord;
+  if constexpr (C == 0) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)oc, 0, 0);
+    r.w[0] = u.x;
+    r.w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < (int)RB / 16; ++h) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(oc + 16u * h), 0, 0);
+      r.w[4 * h + 0] = u.x;
+      r.w[4 * h + 1] = u.y;
+      r.w[4 * h + 2] = u.z;
+      r.w[4 * h + 3] = u.w;
+    }
+  }
+  r.so = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)os, 0, 0);
+  ipos += ca + up16(4u * m);
+}
+
+// Decodes the lane's record of one block into its row slot: the dot starts
+// from -bias, so it ends as sum_k q_k x_k; the slot gets s * dot + o * sum(x).
+template <int C, int NB>
+__device__ inline void decode_block(const Consts<C>& k, const Rec<C>& r, const TileX<NB>& X, const float (&bias)[NB],
+                                    bool act, uint32_t& rot, float* slot, uint32_t lane) {
+  float a[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    a[nb][0] = -bias[nb];
+    a[nb][1] = 0.f;
+  }
+  record_dot<C, NB>(k, r.w, X.xr, a, std::make_integer_sequence<int, 32>{});
+  // rot is empty exactly when the column sits the block out; then the slot
+  // is the spare one and the row is not used.
+  const uint32_t j = (uint32_t)__builtin_ctz(rot);
+  rot &= rot - 1u;
+  const uint32_t row = act ? ((j + lane) & 31u) : 32u;
+  const float s = __half2float(__ushort_as_half((unsigned short)(r.so & 0xFFFFu)));
+  const float o = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) slot[nb * kSlotWords + row] = __builtin_fmaf(s, a[nb][0] + a[nb][1], o * X.xsum[nb]);
+}
+
+// The blocks of class C of a tile (I of them, starting at stream position
+// pos): the loads of block i + D go out as block i is decoded, so D blocks
+// are in flight. The loop is unrolled D times so that every block in flight
+// has registers of its own.
+template <int C, int NB>
+__device__ inline void run_class(__amdgpu_buffer_rsrc_t rs, uint32_t I, uint32_t mask, const TileX<NB>& X,
+                                 uint32_t& pos, float* slot, uint32_t lane) {
+  constexpr int D = depth<C, NB>();
   const Consts<C> k = make_consts<C>();
   float bias[NB];
   class_bias<C, NB>(X.xr, bias, std::make_integer_sequence<int, 32>{});
   uint32_t rot = rotate_rows(mask, lane);
-  const uint32_t lane16 = 16u * lane;
-  for (uint32_t i = 0; i < I; ++i) {
-    const bool act = n > i;
-    const uint64_t bal = __ballot(act);
-    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)__popcll(bal));
-    const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-    const uint32_t ca = codes_area(C, m), bytes = ca + up16(4u * m);
-    wait_vmcnt((int)rg.issued - (int)((pos + bytes + 1023u) >> 10));
-    if (act) {
-      uint32_t w[2 * B];
-      const uint32_t cb = pos + (8u * B) * kk;
-      if constexpr (C == 0) {
-        const uint2 u = *reinterpret_cast<const uint2*>(ring + (cb & ring_mask));
-        w[0] = u.x;
-        w[1] = u.y;
-      } else {
+  const uint32_t n = (uint32_t)__builtin_popcount(mask);
+  Rec<C> R[D];
 #pragma unroll
-        for (int h = 0; h < B / 2; ++h) {
-          const uint4 u = *reinterpret_cast<const uint4*>(ring + ((cb + 16u * h) & ring_mask));
-          w[4 * h + 0] = u.x;
-          w[4 * h + 1] = u.y;
-          w[4 * h + 2] = u.z;
-          w[4 * h + 3] = u.w;
-        }
-      }
-      const uint32_t so = *reinterpret_cast<const uint32_t*>(ring + ((pos + ca + 4u * kk) & ring_mask));
-      const uint32_t j = (uint32_t)__builtin_ctz(rot);
-      rot &= rot - 1u;
-      const uint32_t row = (j + lane) & 31u;
-      float a[NB][4];
+  for (int d = 0; d < D; ++d) issue_block<C>(rs, pos, (uint32_t)d, n, R[d]);
+  for (uint32_t i0 = 0; i0 < I; i0 += D) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a[nb][0] = a[nb][1] = a[nb][2] = a[nb][3] = 0.f;
-      record_dot<C, NB>(k, w, X.xr, a, std::make_integer_sequence<int, 32>{});
-      const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
-      const float o = __half2float(__ushort_as_half((unsigned short)(so >> 16)));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float dot = (a[nb][0] + a[nb][1]) + (a[nb][2] + a[nb][3]);
-        atomicAdd(&Y[nb * kTileRows + row], __builtin_fmaf(s, dot - bias[nb], o * X.xsum[nb]));
-      }
+    for (int d = 0; d < D; ++d) {
+      const uint32_t i = i0 + d;
+      if (i >= I) break;
+      decode_block<C, NB>(k, R[d], X, bias, n > i, rot, slot, lane);
+      issue_block<C>(rs, pos, i + D, n, R[d]);
     }
-    pos += bytes;
-    // Refill the freed ring slots once this block's LDS reads are complete.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    ring_issue(rg, (pos >> 10) + rg.slots, lane16);
   }
 }
 
-// Adds tile (rt, kt) of matrix T into the wavefront's row slice Y [NB][32].
+// Adds tile (rt, kt) of matrix T into the lanes' row sums yacc (lane r < 32
+// holds row r of the tile). S: this wavefront's slots, NB * kSlotWords.
 template <int NB>
-__device__ inline void packed_tile(const GemvMat& T, int rt, int kt, float* Y, const uint8_t* ring, uint32_t ring_bytes,
-                                   uint32_t lane) {
+__device__ inline void packed_tile(const GemvMat& T, int rt, int kt, float (&yacc)[NB], float* S, uint32_t lane) {
   const int t = kt * T.row_tiles + rt;
   const uint4 hdr = *reinterpret_cast<const uint4*>(T.tiles + 4 * (size_t)t);
   const uint32_t base = __builtin_amdgcn_readfirstlane(hdr.x) * 16u;
-  const uint32_t size = __builtin_amdgcn_readfirstlane(hdr.y) * 16u;
   const uint32_t iw = __builtin_amdgcn_readfirstlane(hdr.z);
   const int R = min(kTileRows, T.n_rows - rt * kTileRows);
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, T.n_groups - g0);
-  const uint32_t mb = map_bytes((uint32_t)Gt);
-  Ring rg;
-  rg.rsrc = make_rsrc(T.stream, T.stream_bytes);
-  rg.lds = lds_addr(ring);
-  rg.slots = ring_bytes >> 10;
-  rg.src = base + mb;
-  rg.np = (size - mb + 1023u) >> 10;
-  rg.issued = 0;
-  // The first pieces go out before the map and x loads: those loads complete
-  // in order after the pieces, so once x is in registers the pieces are in
-  // the ring as well.
-  ring_issue(rg, rg.slots, 16u * lane);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(T.stream), (short)0, (int)T.stream_bytes, 0x00020000);
   const int lc = min((int)lane, Gt - 1);
   const bool live = (int)lane < Gt;
-  const uint2 mp = *reinterpret_cast<const uint2*>(T.stream + base + 8u * (uint32_t)lc);
+  const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(base + 8u * (uint32_t)lc), 0, 0);
   TileX<NB> X;
   const size_t K = (size_t)T.n_groups * kGroup;
 #pragma unroll
@@ -344,6 +292,11 @@ __device__ inline void packed_tile(const GemvMat& T, int rt, int kt, float* Y, c
       X.xr[nb][4 * i + 3] = v.w;
     }
   }
+  // A full tile writes every slot once; a partial one clears them first, so
+  // the rows and columns it lacks add zero.
+  if (R < kTileRows || Gt < kTileGroups)
+    for (uint32_t i = lane; i < NB * kSlotWords / 4; i += kWave)
+      reinterpret_cast<float4*>(S)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const ClassMasks km = class_masks(live ? mp.x : 0u, live ? mp.y : 0u, live ? R : 0);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -352,13 +305,25 @@ __device__ inline void packed_tile(const GemvMat& T, int rt, int kt, float* Y, c
     for (int p = 0; p < 32; ++p) a[p & 3] = dot2(X.xr[nb][p], 0x3C003C00u, a[p & 3]);
     X.xsum[nb] = (a[0] + a[1]) + (a[2] + a[3]);
   }
-  const uint32_t ring_mask = ring_bytes - 1u;
-  uint32_t pos = 0;
+  float* slot = S + lane * kSlotPitch;
+  uint32_t pos = base + map_bytes((uint32_t)Gt);
   uint32_t I;
-  if ((I = iw & 0xFFu)) run_class<0, NB>(rg, ring, ring_mask, I, __popc(km.m[0]), km.m[0], X, pos, Y, lane);
-  if ((I = (iw >> 8) & 0xFFu)) run_class<1, NB>(rg, ring, ring_mask, I, __popc(km.m[1]), km.m[1], X, pos, Y, lane);
-  if ((I = (iw >> 16) & 0xFFu)) run_class<2, NB>(rg, ring, ring_mask, I, __popc(km.m[2]), km.m[2], X, pos, Y, lane);
-  if ((I = (iw >> 24) & 0xFFu)) run_class<3, NB>(rg, ring, ring_mask, I, __popc(km.m[3]), km.m[3], X, pos, Y, lane);
+  if ((I = iw & 0xFFu)) run_class<0, NB>(rs, I, km.m[0], X, pos, slot, lane);
+  if ((I = (iw >> 8) & 0xFFu)) run_class<1, NB>(rs, I, km.m[1], X, pos, slot, lane);
+  if ((I = (iw >> 16) & 0xFFu)) run_class<2, NB>(rs, I, km.m[2], X, pos, slot, lane);
+  if ((I = (iw >> 24) & 0xFFu)) run_class<3, NB>(rs, I, km.m[3], X, pos, slot, lane);
+  // Row sums: lanes r and r + 32 add the slots of columns 0-31 and 32-63 of
+  // row r, in column order, then combine.
+  const uint32_t r = lane & 31u, h = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float* col = S + nb * kSlotWords + h * 32u * kSlotPitch + r;
+    float v = 0.f;
+#pragma unroll 8
+    for (int l = 0; l < 32; ++l) v += col[l * kSlotPitch];
+    v += __shfl_xor(v, 32, kWave);
+    yacc[nb] += v;
+  }
 }
 
 // Sum over the 64 lanes (the total lands in every lane).
@@ -434,22 +399,23 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(const GemvLaunch L) {
   for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
   const GemvMat& M = L.mats[mi];
   const int j = (int)blockIdx.x - M.wg_begin;
-  float* Ys = reinterpret_cast<float*>(smem);                       // [waves][NB][32]
-  float* Y = Ys + wave * NB * kTileRows;
-  const uint8_t* ring = smem + kGemvWaves * NB * kTileRows * 4 + wave * L.ring_bytes;
-  for (int i = (int)lane; i < NB * kTileRows; i += kWave) Y[i] = 0.f;
+  // LDS: the wavefronts' row sums [waves][NB][32], then per wavefront its
+  // slots (NB * kSlotWords words).
+  float* Ys = reinterpret_cast<float*>(smem);
+  float* S = reinterpret_cast<float*>(smem + kGemvWaves * NB * kTileRows * 4) + wave * NB * kSlotWords;
+  float yacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
 
   if (!M.shared) {
     // Four row-tiles of a matrix with one k-tile: the wavefronts are independent.
     const int rt = j * kGemvWaves + wave;
     if (rt >= M.row_tiles) return;
-    packed_tile<NB>(M, rt, 0, Y, ring, L.ring_bytes, lane);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row slice is complete
+    packed_tile<NB>(M, rt, 0, yacc, S, lane);
     const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-    for (int i = (int)lane; i < NB * kTileRows; i += kWave) {
-      const int nb = i / kTileRows, r = i - nb * kTileRows;
-      if (r < R) M.y[(size_t)nb * M.n_rows + r0 + r] = Y[i];
-    }
+    if ((int)lane < R)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + lane] = yacc[nb];
     return;
   }
 
@@ -457,18 +423,26 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(const GemvLaunch L) {
   // with a residual the packed k-tiles on wavefront 0 and the residual's rows
   // on wavefronts 1-3.
   const int rt = j;
+  float* Y = Ys + wave * NB * kTileRows;
   if (RESID && M.resid) {
     if (wave == 0) {
-      for (int kt = 0; kt < M.k_tiles; ++kt) packed_tile<NB>(M, rt, kt, Y, ring, L.ring_bytes, lane);
+      for (int kt = 0; kt < M.k_tiles; ++kt) packed_tile<NB>(M, rt, kt, yacc, S, lane);
+      if (lane < 32)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) Y[nb * kTileRows + lane] = yacc[nb];
     } else {
+      for (int i = (int)lane; i < NB * kTileRows; i += kWave) Y[i] = 0.f;
       residual_rows<NB>(M, rt, wave - 1, Y, lane);
     }
   } else {
     const int pairs = M.levels * M.k_tiles;
     for (int p = wave; p < pairs; p += kGemvWaves) {
       const int lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
-      packed_tile<NB>(L.mats[mi + lv], rt, kt, Y, ring, L.ring_bytes, lane);
+      packed_tile<NB>(L.mats[mi + lv], rt, kt, yacc, S, lane);
     }
+    if (lane < 32)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Y[nb * kTileRows + lane] = yacc[nb];
   }
   __syncthreads();
   const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
@@ -481,13 +455,13 @@ __global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(const GemvLaunch L) {
   }
 }
 
-size_t gemv_lds_bytes(int nb, uint32_t ring_bytes) {
-  return (size_t)kGemvWaves * ((size_t)nb * kTileRows * 4 + ring_bytes);
+size_t gemv_lds_bytes(int nb) {
+  return (size_t)kGemvWaves * ((size_t)nb * kTileRows * 4 + (size_t)nb * kSlotWords * 4);
 }
 
 template <int NB, bool RESID>
 static hipError_t launch_one(const GemvLaunch& L, int n_wg, hipStream_t s) {
-  const size_t lds = gemv_lds_bytes(NB, L.ring_bytes);
+  const size_t lds = gemv_lds_bytes(NB);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, RESID>),

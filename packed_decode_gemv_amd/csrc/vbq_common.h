@@ -89,8 +89,11 @@ __host__ __device__ inline uint32_t walk_row(ClassWalk& w, uint32_t lane) {
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // the wavefront are outstanding (and for nothing else).
 #define VBQ_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// s_waitcnt immediate that waits for every LDS/scalar-memory operation only.
+#define VBQ_LGKMCNT0_IMM (15 | (3 << 14) | (7 << 4))
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer descriptor (base, no stride, size in bytes): loads past `bytes`
 // return zeros instead of touching memory.
@@ -151,14 +154,13 @@ constexpr int kGemvMaxNb = 4;   // batch rows per pass (x of a k-group kept in r
 struct GemvLaunch {
   GemvMat mats[kMaxMats];
   int32_t n_mats;
-  uint32_t ring_bytes;     // LDS ring of each wavefront (power of two, >= 8 KiB)
 };
 static_assert(sizeof(GemvLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Host-side launch helpers.
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s);
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, hipStream_t s);
-size_t gemv_lds_bytes(int nb, uint32_t ring_bytes);
+size_t gemv_lds_bytes(int nb);
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s);
 hipError_t launch_residual_error(const vbq_matrix& m, const float* E_in, float* E_out, hipStream_t s);
