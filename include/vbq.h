@@ -34,8 +34,10 @@
  *     inputs and shapes (fixed summation order; nothing depends on timing).
  *
  * Execution layout of a packed matrix (see vbq_matrix). The pages give no
- * layout; this one lets a wavefront keep the activations of one k-group per
- * lane in registers while it decodes groups of one width at a time.
+ * layout; this one fills every block of 64 records of one width and makes
+ * the byte position of every record a closed form of its tile's header, so
+ * a kernel can issue all of a tile's loads at once and give each lane one
+ * record of any column.
  *   Tiles. The matrix is cut into tiles of VBQ_TILE_ROWS = 32 rows by
  *   VBQ_TILE_GROUPS = 64 k-groups (4096 columns), stored k-tile major: tile
  *   t = kt * RT + rt covers rows 32 rt .. 32 rt + R - 1 and k-groups
@@ -43,30 +45,34 @@
  *   R = min(32, N - 32 rt), G_t = min(64, K/64 - 64 kt). Column l < G_t of a
  *   tile is its k-group 64 kt + l; r < R is its row 32 rt + r.
  *   Width class c = 0, 1, 2, 3 for b = 1, 2, 4, 8.
- *   For every column l and class c: mask_c(l) = the set of rows r < R whose
- *   group (r, l) has class c, n_c(l) = |mask_c(l)|, and I_c = max_l n_c(l).
- *   The rows of mask_c(l) are taken in the order of (r - l) mod 32
- *   ascending; the i-th of them (i = 0, 1, ...) is row_c(l, i).
+ *   Records. The groups of class c of a tile are numbered e = 0 .. N_c - 1
+ *   in column-major order: column l ascending and, within a column, its
+ *   rows of class c ascending. Record e of class c is entry e % 64 of block
+ *   e / 64 of the class; block k holds m_k = min(64, N_c - 64 k) records.
  *   A tile's bytes are, in order (every area starts 16-byte aligned and is
  *   zero-padded to a multiple of 16 bytes):
  *     map   : for l < G_t, 8 bytes at 8 l: u32 plane0 then u32 plane1, where
  *             bit r of plane0 is (class of group (r, l)) & 1 and bit r of
  *             plane1 is (class of group (r, l)) >> 1, for r < R (higher bits
  *             zero). These are the 2 bits of width per group.
- *     blocks: for c = 0, 1, 2, 3 and i = 0 .. I_c - 1, the block (c, i) of
- *             the columns A = { l : n_c(l) > i } in increasing order, m = |A|;
- *             the k-th column of A (k = 0 .. m-1) holds the record of group
- *             (row_c(l, i), l):
- *               codes area: record k's 2b u32 words at byte 8 b k;
- *               so area   : record k's u32 at byte 4 k, fp16 scale in bits
+ *     blocks: for c = 0, 1, 2, 3 and k = 0 .. ceil(N_c / 64) - 1, block
+ *             (c, k):
+ *               codes area: entry j's 2b u32 words at byte 8 b j;
+ *               so area   : entry j's u32 at byte 4 j, fp16 scale in bits
  *                           0-15 and fp16 offset in bits 16-31.
+ *   A full block takes 512 b + 256 bytes, so with C_c the byte (from the
+ *   tile's start) where class c's first block begins, record e of class c
+ *   has its codes at C_c + (e / 64)(512 b + 256) + 8 b (e % 64) and its
+ *   scale/offset word at C_c + (e / 64)(512 b + 256) + up16(8 b m) +
+ *   4 (e % 64), m being its block's record count; C_0 is the map's size and
+ *   C_(c+1) = C_c + (bytes of class c's blocks).
  *   Record words: with h = 16/b, the pair p = (code 2p, code 2p+1), p < 32,
  *   sits in word p/h: code 2p at bit (p%h)*b (LSB first) and code 2p+1 at
  *   bit 16 + (p%h)*b.
  *   The tiles follow each other in storage order in one byte stream.
  *   tiles[4t..4t+3] = { first 16-byte unit of tile t, its size in 16-byte
- *   units, I_0 | I_1 << 8 | I_2 << 16 | I_3 << 24, 0 }. Entry t = n_tiles
- *   holds { total 16-byte units, invalid-width count, error flags, 0 }.
+ *   units, N_0 | N_1 << 16, N_2 | N_3 << 16 }. Entry t = n_tiles holds
+ *   { total 16-byte units, invalid-width count, error flags, 0 }.
  */
 #ifndef VBQ_H
 #define VBQ_H
@@ -79,7 +85,7 @@
 extern "C" {
 #endif
 
-#define VBQ_ABI_VERSION 3
+#define VBQ_ABI_VERSION 4
 #define VBQ_GROUP 64          /* weights per quantisation group (along K) */
 #define VBQ_TILE_ROWS 32      /* rows per layout tile */
 #define VBQ_TILE_GROUPS 64    /* k-groups (of 64 weights) per layout tile */

@@ -34,21 +34,21 @@
  *   the matrix is cut into tiles of 32 rows x 64 k-groups (4096 columns),
  *   stored k-tile major: tile t = kt * RT + rt covers rows 32rt.. and k-groups
  *   64kt.., RT = ceil(N/32), KT = ceil(G/64); a tile has R <= 32 rows and
- *   Gt <= 64 columns (k-groups). Width class c = 0..3 for b = 1,2,4,8. For
- *   column l and class c, the rows of that class are visited in the order of
- *   (r - l) mod 32 ascending; n_c(l) counts them and I_c = max over l.
+ *   Gt <= 64 columns (k-groups). Width class c = 0..3 for b = 1,2,4,8. The
+ *   groups of class c of a tile form a list of N_c records in column-major
+ *   order (by column, then by row); records 64k .. 64k+63 of the list make
+ *   block k of the class.
  *   A tile is, each area padded with zeros to a multiple of 16 bytes:
  *     map   : per column l, u32 plane0 (bit r = class & 1) then u32 plane1
  *             (bit r = class >> 1);
- *     blocks: for c = 0..3, i = 0..I_c-1: the columns with n_c(l) > i in
- *             increasing order (m of them); the k-th holds the group of its
- *             i-th visited row: codes area (2b words per record at 8bk), then
- *             so area (u32 scale | offset << 16 at 4k).
+ *     blocks: for c = 0..3, the class's blocks in order; a block of m
+ *             records is a codes area (2b words per record, record j at
+ *             byte 8bj) then an so area (u32 scale | offset << 16 at 4j).
  *   Record words: with h = 16/b, pair p = (code 2p, code 2p+1) sits in word
  *   p/h, code 2p at bit (p%h)*b and code 2p+1 at bit 16+(p%h)*b.
  *   Per tile 4 u32: first 16-byte unit, size in 16-byte units,
- *   I_0 | I_1<<8 | I_2<<16 | I_3<<24, 0; one extra entry after the last tile
- *   holds (total 16-byte units, 0, 0, 0).
+ *   N_0 | N_1<<16, N_2 | N_3<<16; one extra entry after the last tile holds
+ *   (total 16-byte units, 0, 0, 0).
  */
 #include <math.h>
 #include <stdint.h>
@@ -207,14 +207,13 @@ static void tile_grid(int N, int K, int64_t* RT, int64_t* KT) {
 }
 
 /* Everything the layout of one tile depends on: its rows and columns, the
- * class of every group, and per (class, column) the rows of that class in
- * visiting order. */
+ * class of every group, and per class its records in list order. */
 typedef struct {
   int r0, R, g0, Gt;
   int cls[ORC_TILE_ROWS][ORC_TILE_GROUPS];
-  int n[4][ORC_TILE_GROUPS];
-  int rows[4][ORC_TILE_GROUPS][ORC_TILE_ROWS];
-  int I[4];
+  int N[4];
+  int rec_row[4][ORC_TILE_ROWS * ORC_TILE_GROUPS];
+  int rec_col[4][ORC_TILE_ROWS * ORC_TILE_GROUPS];
 } orc_tile;
 
 /* Fills T for tile (rt, kt). Returns -1 on an invalid width. */
@@ -229,42 +228,38 @@ static int tile_info(const uint8_t* widths, int N, int G, int64_t rt, int64_t kt
       if (T->cls[r][l] < 0) return -1;
     }
   for (int c = 0; c < 4; ++c) {
-    T->I[c] = 0;
-    for (int l = 0; l < T->Gt; ++l) {
-      int cnt = 0;
-      /* key = (r - l) mod 32 ascending, i.e. r = (key + l) mod 32;
-       * mutation 8 visits the rows in plain ascending order instead */
-      for (int key = 0; key < ORC_TILE_ROWS; ++key) {
-        int r = (g_mut == 8) ? key : (key + l) % ORC_TILE_ROWS;
-        if (r < T->R && T->cls[r][l] == c) T->rows[c][l][cnt++] = r;
+    int e = 0;
+    /* column-major: outer loop over columns, inner over rows (ascending);
+     * mutation 8 lists the records row-major instead */
+    int outer = (g_mut == 8) ? T->R : T->Gt, inner = (g_mut == 8) ? T->Gt : T->R;
+    for (int a = 0; a < outer; ++a)
+      for (int b = 0; b < inner; ++b) {
+        int l = (g_mut == 8) ? b : a, r = (g_mut == 8) ? a : b;
+        if (T->cls[r][l] == c) {
+          T->rec_row[c][e] = r;
+          T->rec_col[c][e] = l;
+          ++e;
+        }
       }
-      T->n[c][l] = cnt;
-      if (cnt > T->I[c]) T->I[c] = cnt;
-    }
+    T->N[c] = e;
   }
   return 0;
 }
 
-/* Columns active in block (c, i), in increasing order; returns m. */
-static int block_columns(const orc_tile* T, int c, int i, int* cols) {
-  int m = 0;
-  for (int l = 0; l < T->Gt; ++l)
-    if (T->n[c][l] > i) cols[m++] = l;
-  return m;
-}
+/* Records in block k of a class with n records. */
+static int block_records(int n, int k) { return n - 64 * k < 64 ? n - 64 * k : 64; }
 
 static int64_t block_bytes(int c, int m) { return up16(8 * (int64_t)class_bits(c) * m) + up16(4 * (int64_t)m); }
 
 static int64_t tile_bytes(const orc_tile* T) {
   int64_t bytes = up16(8 * (int64_t)T->Gt);
-  int cols[ORC_TILE_GROUPS];
   for (int c = 0; c < 4; ++c)
-    for (int i = 0; i < T->I[c]; ++i) bytes += block_bytes(c, block_columns(T, c, i, cols));
+    for (int k = 0; 64 * k < T->N[c]; ++k) bytes += block_bytes(c, block_records(T->N[c], k));
   return bytes;
 }
 
-static uint32_t iter_word(const orc_tile* T) {
-  return (uint32_t)T->I[0] | ((uint32_t)T->I[1] << 8) | ((uint32_t)T->I[2] << 16) | ((uint32_t)T->I[3] << 24);
+static uint32_t count_word(const orc_tile* T, int half) {
+  return (uint32_t)T->N[2 * half] | ((uint32_t)T->N[2 * half + 1] << 16);
 }
 
 /* Counts the sizes of the layout. Returns 0, or -1 for a bad shape or width. */
@@ -313,29 +308,28 @@ int orc_pack(const float* W, const uint8_t* widths, int N, int K, uint32_t* tile
       memcpy(tb + 8 * l + 4, &p1, 4);
     }
     int64_t pos = up16(8 * (int64_t)T->Gt);
-    int cols[ORC_TILE_GROUPS];
     for (int c = 0; c < 4; ++c) {
       int b = class_bits(c);
-      for (int i = 0; i < T->I[c]; ++i) {
-        int m = block_columns(T, c, i, cols);
-        for (int k = 0; k < m; ++k) {
-          int l = cols[k], r = T->rows[c][l][i];
+      for (int k = 0; 64 * k < T->N[c]; ++k) {
+        int m = block_records(T->N[c], k);
+        for (int j = 0; j < m; ++j) {
+          int e = 64 * k + j, l = T->rec_col[c][e], r = T->rec_row[c][e];
           uint16_t s16, o16;
           uint8_t q[64];
           uint32_t words[16];
           orc_quantize_group(W + (int64_t)(T->r0 + r) * K + 64 * (int64_t)(T->g0 + l), b, &s16, &o16, q);
           orc_pack_group_record(q, b, words);
-          memcpy(tb + pos + 8 * (int64_t)b * k, words, 8 * (size_t)b);
+          memcpy(tb + pos + 8 * (int64_t)b * j, words, 8 * (size_t)b);
           uint32_t so = (uint32_t)s16 | ((uint32_t)o16 << 16);
-          memcpy(tb + pos + up16(8 * (int64_t)b * m) + 4 * k, &so, 4);
+          memcpy(tb + pos + up16(8 * (int64_t)b * m) + 4 * j, &so, 4);
         }
         pos += block_bytes(c, m);
       }
     }
     tiles[4 * t + 0] = (uint32_t)(byte / 16);
     tiles[4 * t + 1] = (uint32_t)(pos / 16);
-    tiles[4 * t + 2] = iter_word(T);
-    tiles[4 * t + 3] = 0;
+    tiles[4 * t + 2] = count_word(T, 0);
+    tiles[4 * t + 3] = count_word(T, 1);
     byte += pos;
   }
   free(T);
@@ -394,25 +388,27 @@ int orc_unpack(const uint32_t* tiles, const uint32_t* stream, int N, int K, cons
       /* the tile as the writer sees it, built from the map's widths */
       tile_info(wmap, R, G, 0, kt, T);
       T->r0 = r0;
-      if (tiles[4 * t + 2] != iter_word(T) || (int64_t)tiles[4 * t + 1] * 16 != tile_bytes(T) ||
-          tiles[4 * t + 0] + tiles[4 * t + 1] != tiles[4 * t + 4]) { rc = -1; break; }
+      if (tiles[4 * t + 2] != count_word(T, 0) || tiles[4 * t + 3] != count_word(T, 1) ||
+          (int64_t)tiles[4 * t + 1] * 16 != tile_bytes(T) || tiles[4 * t + 0] + tiles[4 * t + 1] != tiles[4 * t + 4]) {
+        rc = -1;
+        break;
+      }
       int64_t pos = up16(8 * (int64_t)Gt);
-      int cols[ORC_TILE_GROUPS];
       for (int c = 0; c < 4 && rc == 0; ++c) {
         int b = class_bits(c);
-        for (int i = 0; i < T->I[c]; ++i) {
-          int m = block_columns(T, c, i, cols);
+        for (int k = 0; 64 * k < T->N[c] && rc == 0; ++k) {
+          int m = block_records(T->N[c], k);
           if (!all_zero(tb + pos + 8 * (int64_t)b * m, up16(8 * (int64_t)b * m) - 8 * (int64_t)b * m) ||
               !all_zero(tb + pos + up16(8 * (int64_t)b * m) + 4 * m, up16(4 * (int64_t)m) - 4 * m)) {
             rc = -1;
             break;
           }
-          for (int k = 0; k < m; ++k) {
-            int l = cols[k], r = T->rows[c][l][i];
+          for (int j = 0; j < m; ++j) {
+            int e = 64 * k + j, l = T->rec_col[c][e], r = T->rec_row[c][e];
             if (r0 + r != row) continue;
             uint32_t words[16], so;
-            memcpy(words, tb + pos + 8 * (int64_t)b * k, 8 * (size_t)b);
-            memcpy(&so, tb + pos + up16(8 * (int64_t)b * m) + 4 * k, 4);
+            memcpy(words, tb + pos + 8 * (int64_t)b * j, 8 * (size_t)b);
+            memcpy(&so, tb + pos + up16(8 * (int64_t)b * m) + 4 * j, 4);
             uint8_t q[64];
             orc_unpack_group_record(words, b, q);
             int64_t g = g0 + l;

@@ -53,10 +53,10 @@ int cu_count() {
 
 // Bytes of one tile from the widths (host): the same rules the pack kernel
 // and the GEMV follow (see vbq.h).
-uint64_t host_tile_bytes(const uint8_t* widths, int N, int G, int rt, int kt, uint32_t* iw_out, bool* bad) {
+uint64_t host_tile_bytes(const uint8_t* widths, int N, int G, int rt, int kt, bool* bad) {
   const int r0 = rt * kTileRows, R = std::min(kTileRows, N - r0);
   const int g0 = kt * kTileGroups, Gt = std::min(kTileGroups, G - g0);
-  uint32_t n[4][kTileGroups] = {};
+  uint32_t n[4] = {0, 0, 0, 0};
   for (int r = 0; r < R; ++r)
     for (int l = 0; l < Gt; ++l) {
       const int c = class_of_width(widths[(int64_t)(r0 + r) * G + g0 + l]);
@@ -64,21 +64,10 @@ uint64_t host_tile_bytes(const uint8_t* widths, int N, int G, int rt, int kt, ui
         *bad = true;
         return 0;
       }
-      n[c][l]++;
+      n[c]++;
     }
   uint64_t bytes = map_bytes((uint32_t)Gt);
-  uint32_t iw = 0;
-  for (int c = 0; c < 4; ++c) {
-    uint32_t I = 0;
-    for (int l = 0; l < Gt; ++l) I = std::max(I, n[c][l]);
-    for (uint32_t i = 0; i < I; ++i) {
-      uint32_t m = 0;
-      for (int l = 0; l < Gt; ++l) m += n[c][l] > i;
-      bytes += block_bytes(c, m);
-    }
-    iw |= I << (8 * c);
-  }
-  if (iw_out) *iw_out = iw;
+  for (int c = 0; c < 4; ++c) bytes += class_bytes(c, n[c]);
   return bytes;
 }
 
@@ -118,7 +107,7 @@ vbq_status vbq_pack_query(const uint8_t* widths_host, int32_t N, int32_t K, vbq_
   for (int kt = 0; kt < KT; ++kt)
     for (int rt = 0; rt < RT; ++rt) {
       bool bad = false;
-      const int64_t tb = (int64_t)host_tile_bytes(widths_host, N, G, rt, kt, nullptr, &bad);
+      const int64_t tb = (int64_t)host_tile_bytes(widths_host, N, G, rt, kt, &bad);
       if (bad) return VBQ_ERR_BITWIDTH;
       bytes += tb;
       max_b = std::max(max_b, tb / 16);
@@ -157,7 +146,7 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream) {
 
 // One GEMV launch sequence: `count` matrices (independent outputs), or with
 // levels > 1 one output summed over `count` levels, or one matrix with a
-// residual. Batches above four rows run as passes of up to four rows.
+// residual. Batches above two rows run as passes of up to two rows.
 static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, const uint16_t* resid,
                             float* const* ys, int32_t B, bool levels, hipStream_t stream) {
   if (count < 1 || count > kMaxMats || !ms || !xs || !ys) return VBQ_ERR_INVALID_ARG;
@@ -206,7 +195,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.stream_bytes = (uint32_t)(m.n_bytes16 * 16);
       g.wg_begin = (int32_t)wg;
       if (!levels || pos == 0)
-        wg += g.shared ? g.row_tiles : (g.row_tiles + kGemvWaves - 1) / kGemvWaves;
+        wg += g.row_tiles;
     }
     if (wg > 0x7FFFFFFF) return VBQ_ERR_UNSUPPORTED;
     L.n_mats = count;

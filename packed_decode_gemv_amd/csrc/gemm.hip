@@ -102,13 +102,14 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, a.G - g0);
   const bool mine = wave < nrt;
   const bool live = mine && lane < Gt;
-  uint32_t tbase = 0, iw = 0;
+  uint32_t tbase = 0, w2 = 0, w3 = 0;
   ClassMasks km = class_masks(0u, 0u, 0);
   if (mine) {
     const int rt = rt0 + wave;
     const uint4 h = *reinterpret_cast<const uint4*>(a.tiles + 4 * (size_t)(kt * a.RT + rt));
     tbase = (h.x - base16) * 16u;
-    iw = h.z;
+    w2 = h.z;
+    w3 = h.w;
     const int R = min(kTileRows, a.N - rt * kTileRows);
     const uint2 mp = live ? *reinterpret_cast<const uint2*>(a.stream + (size_t)h.x * 16u + 8u * (uint32_t)lane)
                           : make_uint2(0u, 0u);
@@ -136,27 +137,19 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
   }
   gemm_barrier();
   if (mine) {
-    uint32_t pos = tbase + map_bytes((uint32_t)Gt);
+    uint32_t cbase = tbase + map_bytes((uint32_t)Gt);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t I = (iw >> (8 * c)) & 0xFFu;
-      const uint32_t n = (uint32_t)__popc(km.m[c]);
-      uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
-      for (uint32_t i = 0; i < I; ++i) {
-        const bool act = n > i;
-        const uint64_t bal = __ballot(act);
-        const uint32_t m = (uint32_t)__popcll(bal);
-        const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-        if (act) {
-          const uint32_t j = (uint32_t)__builtin_ctz(rot);
-          rot &= rot - 1u;
-          const uint32_t row = (uint32_t)wave * kTileRows + ((j + (uint32_t)lane) & 31u);
-          const uint32_t co = pos + (8u << c) * kk, so = pos + codes_area(c, m) + 4u * kk;
-          const uint32_t slot = atomicAdd(&S.cnt[lane][c], 1u);
-          S.ent[lane][slot] = make_uint2((co >> 3) | (row << 17) | ((uint32_t)c << 24), so);
-        }
-        pos += block_bytes(c, m);
+      const uint32_t n = class_count(w2, w3, c);
+      uint32_t mask = km.m[c];
+      uint32_t e = wave_excl_scan((uint32_t)__popc(mask), (uint32_t)lane);
+      for (; mask; mask &= mask - 1u, ++e) {
+        const uint32_t row = (uint32_t)wave * kTileRows + (uint32_t)__builtin_ctz(mask);
+        const RecPos rp = record_pos(c, n, cbase, e);
+        const uint32_t slot = atomicAdd(&S.cnt[lane][c], 1u);
+        S.ent[lane][slot] = make_uint2((rp.codes >> 3) | (row << 17) | ((uint32_t)c << 24), rp.so);
       }
+      cbase += class_bytes(c, n);
     }
   }
   gemm_barrier();

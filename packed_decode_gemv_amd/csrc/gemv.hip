@@ -94,7 +94,7 @@ __device__ inline Consts<C> make_consts_impl(std::integer_sequence<int, P...>) {
   if constexpr (C == 3) {
     k.magic[0] = vconst<0x64646464u>();
   } else {
-    ((k.mask[P] = vconst<field_mask(C, P)>(), k.magic[P] = vconst<field_magic(P)>()), ...);
+    ((k.mask[P] = vconst<field_mask(C, P)>(), k.magic[P] = field_magic(P)), ...);
   }
   return k;
 }
@@ -133,6 +133,20 @@ __device__ inline void record_dot(const Consts<C>& k, const uint32_t* w, const u
       ...);
 }
 
+// The same for pairs 16..31 (activation registers indexed from the record's
+// pair 0, so the halves of one record share an array).
+template <int C, int NB, int... P>
+__device__ inline void record_dot_hi(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32],
+                                     float (&a)[NB][2], std::integer_sequence<int, P...>) {
+  (
+      [&] {
+        const uint32_t hv = pair_h2<C, P + 16>(k, w);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) a[nb][P & 1] = dot2(hv, xr[nb][P + 16], a[nb][P & 1]);
+      }(),
+      ...);
+}
+
 // sum over the record's pairs of bias(field) * (x_2P + x_2P+1).
 template <int C, int NB, int... P>
 __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB], std::integer_sequence<int, P...>) {
@@ -144,186 +158,310 @@ __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB
   }
 }
 
-// ---- One tile -------------------------------------------------------------------
-template <int NB>
-struct TileX {
-  uint32_t xr[NB][32];   // x pairs (x_2p, x_2p+1) of the lane's k-group, per batch row
-  float xsum[NB];        // sum of the group's 64 activations
-};
+// ---- Cooperative tile -------------------------------------------------------------
+// The four wavefronts of a workgroup process one tile together. Every record
+// position is a closed form of the tile header (records of a width class are
+// listed column by column, 64 to a block), so every load of a tile goes out
+// as soon as its header is known:
+//  1. Wavefront 0 copies the activations of the tile's 64 columns into LDS
+//     with buffer-to-LDS loads; every wavefront loads the width map of its
+//     lane's column and issues its first chunks of every class (chunk j of a
+//     class = its records 64 j .. 64 j + 63; wavefront w takes chunks w,
+//     w + 4, ...).
+//  2. Wavefront 0 forms, per column, the bias sum of every class and the sum
+//     of the activations; wavefronts 1-3 list the (column, row) of every
+//     record in an LDS table (wavefront 1 class 0, 2 class 1, 3 classes 2
+//     and 3; lane l writes the entries of its column's rows). Barrier.
+//  3. The wavefronts decode their chunks class by class; lane e of a chunk
+//     takes record 64 j + e, reads its column and row from the table and the
+//     column's activations from LDS (in two halves, to bound the registers),
+//     and puts s (dot) + o sum(x) at the slot of its (column, row). Later
+//     chunks of a class are loaded D ahead. Barrier.
+//  4. Wavefront w adds the slots of rows 8w..8w+7 over the 64 columns in a
+//     fixed order and clears them.
+constexpr int kSlotPitch = 33;                            // slot (column l, row r) at l * 33 + r; 32 is spare
+constexpr int kSlotWords = kWave * kSlotPitch;            // 2112 per batch row
+constexpr int kXWords = kTileGroups * 32;                 // 64 columns x 64 fp16, 128 bytes apart
+constexpr int kMaxRecs = kTileRows * kTileGroups;         // 2048 table entries of 16 bits
 
-// Per-wavefront row slots: the record of column l in row r puts its value at
-// slot l * kSlotPitch + r (each (row, column) pair has exactly one record per
-// tile, so plain stores suffice); slot 32 of a column takes the stores of
-// blocks the column has no record in. The pitch of 33 words puts the 32 rows
-// read at one column on different banks.
-constexpr int kSlotPitch = 33;
-constexpr int kSlotWords = kWave * kSlotPitch;   // per batch row: 2112 words, 8448 bytes
+template <int NB>
+struct LdsMap {
+  static constexpr int x = 0;                             // [NB][64][32] fp16 pairs
+  static constexpr int xsum = x + NB * kXWords;           // [NB][64]
+  static constexpr int bias = xsum + NB * kWave;          // [NB][4][64]
+  static constexpr int table = bias + NB * 4 * kWave;     // [2048] u16: column << 5 | row
+  static constexpr int slots = table + kMaxRecs / 2;      // [NB][64][33]
+  static constexpr int ys = slots + NB * kSlotWords;      // [NB][32] residual row sums
+  static constexpr int words = ys + NB * kTileRows;
+};
 
 // Buffer offset that lies outside every stream: loads from it return zeros
 // without touching memory.
 constexpr uint32_t kNoRecord = 0x80000000u;
 
-// The record of the lane in one block.
+// One record in flight: its words and its scale/offset word.
 template <int C>
 struct Rec {
   uint32_t w[2 << C];
   uint32_t so;
 };
 
-// Blocks of a class whose records are in flight while one is decoded: about
-// 6-9 KiB per wavefront at one batch row, fewer at more rows (their
-// activations take the registers).
+// Chunks of a class each wavefront has in flight: issued at the tile's start
+// and refilled while the class is decoded.
 template <int C, int NB>
 __host__ __device__ constexpr int depth() {
-  return (16 >> C) / NB < 2 ? 2 : (16 >> C) / NB;
+  return C == 0 ? 4 / NB : C == 1 ? 2 / NB : 1;
 }
 
-// Issues the loads of the lane's record in block i of a class whose stream
-// position is ipos (advanced past the block). A column takes part in block i
-// when it holds more than i records of the class; its record is the kk-th of
-// the block, kk counting the taking-part columns below it. Columns that do
-// not take part (and every column past the class's last block) load from
-// kNoRecord, so every block issues the same loads and the count waits stay
-// fixed.
+struct TileRef {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t base;      // byte offset of the tile in the stream
+  uint32_t n[4];      // records per class
+  uint32_t cb[4];     // byte (from the tile's start) of each class's first block
+  uint32_t t0[4];     // first table entry of each class
+  int R, Gt, g0;
+};
+
+__device__ inline TileRef tile_ref(const GemvMat& T, int rt, int kt) {
+  TileRef t;
+  const int ti = kt * T.row_tiles + rt;
+  const uint4 hdr = *reinterpret_cast<const uint4*>(T.tiles + 4 * (size_t)ti);
+  t.base = __builtin_amdgcn_readfirstlane(hdr.x) * 16u;
+  const uint32_t w2 = __builtin_amdgcn_readfirstlane(hdr.z), w3 = __builtin_amdgcn_readfirstlane(hdr.w);
+  t.R = min(kTileRows, T.n_rows - rt * kTileRows);
+  t.g0 = kt * kTileGroups;
+  t.Gt = min(kTileGroups, T.n_groups - t.g0);
+  uint32_t cb = map_bytes((uint32_t)t.Gt), e = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    t.n[c] = class_count(w2, w3, c);
+    t.cb[c] = cb;
+    t.t0[c] = e;
+    cb += class_bytes(c, t.n[c]);
+    e += t.n[c];
+  }
+  t.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(T.stream), (short)0, (int)T.stream_bytes, 0x00020000);
+  return t;
+}
+
+// Issues the loads of chunk j of class C (records 64 j + lane); lanes past
+// the class's last record load from kNoRecord.
 template <int C>
-__device__ inline void issue_block(__amdgpu_buffer_rsrc_t rs, uint32_t& ipos, uint32_t i, uint32_t n, Rec<C>& r) {
+__device__ inline void issue_chunk(const TileRef& t, uint32_t j, Rec<C>& r, uint32_t lane) {
   constexpr uint32_t RB = 8u << C;
-  const bool act = n > i;
-  const uint64_t bal = __ballot(act);
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)__popcll(bal));
-  const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-  const uint32_t ca = codes_area(C, m);
-  const uint32_t oc = act ? ipos + RB * kk : kNoRecord;
-  const uint32_t os = act ? ipos + ca + 4u * kk : kNoRecord;
+  const uint32_t e = 64u * j + lane;
+  uint32_t oc = kNoRecord, os = kNoRecord;
+  if (e < t.n[C]) {
+    const RecPos rp = record_pos(C, t.n[C], t.cb[C], e);
+    oc = t.base + rp.codes;
+    os = t.base + rp.so;
+  }
   if constexpr (C == 0) {
-    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)oc, 0, 0);
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)oc, 0, 0);
     r.w[0] = u.x;
     r.w[1] = u.y;
   } else {
 #pragma unroll
     for (int h = 0; h < (int)RB / 16; ++h) {
-      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(oc + 16u * h), 0, 0);
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(t.rs, (int)(oc + 16u * h), 0, 0);
       r.w[4 * h + 0] = u.x;
       r.w[4 * h + 1] = u.y;
       r.w[4 * h + 2] = u.z;
       r.w[4 * h + 3] = u.w;
     }
   }
-  r.so = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)os, 0, 0);
-  ipos += ca + up16(4u * m);
+  r.so = __builtin_amdgcn_raw_buffer_load_b32(t.rs, (int)os, 0, 0);
 }
 
-// Decodes the lane's record of one block into its row slot: the dot starts
-// from -bias, so it ends as sum_k q_k x_k; the slot gets s * dot + o * sum(x).
+// Chunks of a class with n records that wavefront w takes.
+__device__ inline uint32_t wave_chunks(uint32_t n, int wave) {
+  const uint32_t J = (n + 63u) >> 6;
+  return J > (uint32_t)wave ? (J - (uint32_t)wave + kGemvWaves - 1) / kGemvWaves : 0u;
+}
+
 template <int C, int NB>
-__device__ inline void decode_block(const Consts<C>& k, const Rec<C>& r, const TileX<NB>& X, const float (&bias)[NB],
-                                    bool act, uint32_t& rot, float* slot, uint32_t lane) {
-  float a[NB][2];
+struct Flight {
+  Rec<C> r[depth<C, NB>()];
+};
+
+template <int C, int NB>
+__device__ inline void issue_first(const TileRef& t, int wave, Flight<C, NB>& f, uint32_t lane) {
+  const uint32_t nS = wave_chunks(t.n[C], wave);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    a[nb][0] = -bias[nb];
-    a[nb][1] = 0.f;
+  for (int d = 0; d < depth<C, NB>(); ++d)
+    issue_chunk<C>(t, (uint32_t)d < nS ? (uint32_t)wave + kGemvWaves * d : 0x3FFFFFFu, f.r[d], lane);
+}
+
+// Table entries of class c: lane l writes those of its column's rows, in
+// row order, after the entries of the columns before it.
+template <int NB>
+__device__ inline void table_class(const TileRef& t, int c, uint32_t p0, uint32_t p1, uint32_t valid, uint32_t* S,
+                                   uint32_t lane) {
+  uint32_t mask = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
+  const uint32_t first = (c > 0 ? t.n[0] : 0u) + (c > 1 ? t.n[1] : 0u) + (c > 2 ? t.n[2] : 0u);
+  uint32_t e = first + wave_excl_scan((uint32_t)__builtin_popcount(mask), lane);
+  uint16_t* tab = reinterpret_cast<uint16_t*>(S + LdsMap<NB>::table);
+  for (; mask; mask &= mask - 1u, ++e) tab[e] = (uint16_t)((lane << 5) | (uint32_t)__builtin_ctz(mask));
+}
+
+// Step 2.
+template <int NB>
+__device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, uint32_t* S, uint32_t lane) {
+  if (wave == 0) {
+    // the activation copies of this wavefront are complete once nothing of
+    // its own is in flight
+    __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t xr[1][32];
+      const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * 32u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
+        xr[0][4 * i + 0] = v.x;
+        xr[0][4 * i + 1] = v.y;
+        xr[0][4 * i + 2] = v.z;
+        xr[0][4 * i + 3] = v.w;
+      }
+      float b[4][1];
+      class_bias<0, 1>(xr, b[0], std::make_integer_sequence<int, 32>{});
+      class_bias<1, 1>(xr, b[1], std::make_integer_sequence<int, 32>{});
+      class_bias<2, 1>(xr, b[2], std::make_integer_sequence<int, 32>{});
+      class_bias<3, 1>(xr, b[3], std::make_integer_sequence<int, 32>{});
+      float* bias = reinterpret_cast<float*>(S + LdsMap<NB>::bias) + nb * 4 * kWave + lane;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bias[c * kWave] = b[c][0];
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 32; ++p) a[p & 3] = dot2(xr[0][p], 0x3C003C00u, a[p & 3]);
+      reinterpret_cast<float*>(S + LdsMap<NB>::xsum)[nb * kWave + lane] = (a[0] + a[1]) + (a[2] + a[3]);
+    }
+  } else {
+    const bool live = (int)lane < t.Gt;
+    const uint32_t p0 = live ? mp.x : 0u, p1 = live ? mp.y : 0u;
+    const uint32_t valid = !live ? 0u : t.R >= 32 ? 0xFFFFFFFFu : ((1u << t.R) - 1u);
+    table_class<NB>(t, wave - 1, p0, p1, valid, S, lane);
+    if (wave == 3) table_class<NB>(t, 3, p0, p1, valid, S, lane);
   }
-  record_dot<C, NB>(k, r.w, X.xr, a, std::make_integer_sequence<int, 32>{});
-  // rot is empty exactly when the column sits the block out; then the slot
-  // is the spare one and the row is not used.
-  const uint32_t j = (uint32_t)__builtin_ctz(rot);
-  rot &= rot - 1u;
-  const uint32_t row = act ? ((j + lane) & 31u) : 32u;
+}
+
+// Decodes lane's record of chunk j: the dot starts from -bias, so it ends as
+// sum_k q_k x_k; the slot of (column, row) gets s * dot + o * sum(x). Lanes
+// past the class's last record write the spare slot of column 31.
+template <int C, int NB>
+__device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const TileRef& t, uint32_t j, uint32_t* S,
+                                    uint32_t lane) {
+  const uint32_t e = 64u * j + lane;
+  const bool valid = e < t.n[C];
+  const uint32_t ent = valid ? reinterpret_cast<const uint16_t*>(S + LdsMap<NB>::table)[t.t0[C] + e] : (31u << 5);
+  const uint32_t col = ent >> 5, row = valid ? (ent & 31u) : 32u;
   const float s = __half2float(__ushort_as_half((unsigned short)(r.so & 0xFFFFu)));
   const float o = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) slot[nb * kSlotWords + row] = __builtin_fmaf(s, a[nb][0] + a[nb][1], o * X.xsum[nb]);
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + col * 32u;
+    const float xsum = reinterpret_cast<const float*>(S + LdsMap<NB>::xsum)[nb * kWave + col];
+    const float bias = reinterpret_cast<const float*>(S + LdsMap<NB>::bias)[(nb * 4 + C) * kWave + col];
+    float a[1][2] = {{-bias, 0.f}};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t xr[1][32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xs + 16 * half + 4 * i);
+        xr[0][16 * half + 4 * i + 0] = v.x;
+        xr[0][16 * half + 4 * i + 1] = v.y;
+        xr[0][16 * half + 4 * i + 2] = v.z;
+        xr[0][16 * half + 4 * i + 3] = v.w;
+      }
+      if (half == 0) record_dot<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
+      else record_dot_hi<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
+    }
+    reinterpret_cast<float*>(S + LdsMap<NB>::slots)[nb * kSlotWords + col * kSlotPitch + row] =
+        __builtin_fmaf(s, a[0][0] + a[0][1], o * xsum);
+  }
 }
 
-// The blocks of class C of a tile (I of them, starting at stream position
-// pos): the loads of block i + D go out as block i is decoded, so D blocks
-// are in flight. The loop is unrolled D times so that every block in flight
-// has registers of its own.
+// Step 3 for class C: the chunks in flight are decoded in turn and each
+// slot is refilled with the chunk D further on.
 template <int C, int NB>
-__device__ inline void run_class(__amdgpu_buffer_rsrc_t rs, uint32_t I, uint32_t mask, const TileX<NB>& X,
-                                 uint32_t& pos, float* slot, uint32_t lane) {
+__device__ inline void run_class(const TileRef& t, Flight<C, NB>& f, uint32_t* S, int wave, uint32_t lane) {
   constexpr int D = depth<C, NB>();
+  const uint32_t nS = wave_chunks(t.n[C], wave);
+  if (nS == 0) return;
   const Consts<C> k = make_consts<C>();
-  float bias[NB];
-  class_bias<C, NB>(X.xr, bias, std::make_integer_sequence<int, 32>{});
-  uint32_t rot = rotate_rows(mask, lane);
-  const uint32_t n = (uint32_t)__builtin_popcount(mask);
-  Rec<C> R[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue_block<C>(rs, pos, (uint32_t)d, n, R[d]);
-  for (uint32_t i0 = 0; i0 < I; i0 += D) {
+  for (uint32_t s0 = 0; s0 < nS; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const uint32_t i = i0 + d;
-      if (i >= I) break;
-      decode_block<C, NB>(k, R[d], X, bias, n > i, rot, slot, lane);
-      issue_block<C>(rs, pos, i + D, n, R[d]);
+      const uint32_t sq = s0 + d;
+      if (sq >= nS) break;
+      decode_chunk<C, NB>(k, f.r[d], t, (uint32_t)wave + kGemvWaves * sq, S, lane);
+      const uint32_t sn = sq + D;
+      if (sn < nS) issue_chunk<C>(t, (uint32_t)wave + kGemvWaves * sn, f.r[d], lane);
     }
   }
 }
 
-// Adds tile (rt, kt) of matrix T into the lanes' row sums yacc (lane r < 32
-// holds row r of the tile). S: this wavefront's slots, NB * kSlotWords.
+// Step 4: rows 8w..8w+7; lane = 8 r + g adds columns 8g..8g+7 of row 8w + r,
+// the eight partial sums are combined by a fixed butterfly (every lane of the
+// group ends with the same value), and the slots are cleared for the next
+// tile.
 template <int NB>
-__device__ inline void packed_tile(const GemvMat& T, int rt, int kt, float (&yacc)[NB], float* S, uint32_t lane) {
-  const int t = kt * T.row_tiles + rt;
-  const uint4 hdr = *reinterpret_cast<const uint4*>(T.tiles + 4 * (size_t)t);
-  const uint32_t base = __builtin_amdgcn_readfirstlane(hdr.x) * 16u;
-  const uint32_t iw = __builtin_amdgcn_readfirstlane(hdr.z);
-  const int R = min(kTileRows, T.n_rows - rt * kTileRows);
-  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, T.n_groups - g0);
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(T.stream), (short)0, (int)T.stream_bytes, 0x00020000);
-  const int lc = min((int)lane, Gt - 1);
-  const bool live = (int)lane < Gt;
-  const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(base + 8u * (uint32_t)lc), 0, 0);
-  TileX<NB> X;
-  const size_t K = (size_t)T.n_groups * kGroup;
+__device__ inline void fold_rows(uint32_t* S, int wave, float (&yacc)[NB], uint32_t lane) {
+  const uint32_t r = lane >> 3, g = lane & 7u, row = 8u * wave + r;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint4* xp = reinterpret_cast<const uint4*>(T.x + nb * K + (size_t)(g0 + lc) * kGroup);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 v = xp[i];
-      X.xr[nb][4 * i + 0] = v.x;
-      X.xr[nb][4 * i + 1] = v.y;
-      X.xr[nb][4 * i + 2] = v.z;
-      X.xr[nb][4 * i + 3] = v.w;
-    }
-  }
-  // A full tile writes every slot once; a partial one clears them first, so
-  // the rows and columns it lacks add zero.
-  if (R < kTileRows || Gt < kTileGroups)
-    for (uint32_t i = lane; i < NB * kSlotWords / 4; i += kWave)
-      reinterpret_cast<float4*>(S)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  const ClassMasks km = class_masks(live ? mp.x : 0u, live ? mp.y : 0u, live ? R : 0);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 32; ++p) a[p & 3] = dot2(X.xr[nb][p], 0x3C003C00u, a[p & 3]);
-    X.xsum[nb] = (a[0] + a[1]) + (a[2] + a[3]);
-  }
-  float* slot = S + lane * kSlotPitch;
-  uint32_t pos = base + map_bytes((uint32_t)Gt);
-  uint32_t I;
-  if ((I = iw & 0xFFu)) run_class<0, NB>(rs, I, km.m[0], X, pos, slot, lane);
-  if ((I = (iw >> 8) & 0xFFu)) run_class<1, NB>(rs, I, km.m[1], X, pos, slot, lane);
-  if ((I = (iw >> 16) & 0xFFu)) run_class<2, NB>(rs, I, km.m[2], X, pos, slot, lane);
-  if ((I = (iw >> 24) & 0xFFu)) run_class<3, NB>(rs, I, km.m[3], X, pos, slot, lane);
-  // Row sums: lanes r and r + 32 add the slots of columns 0-31 and 32-63 of
-  // row r, in column order, then combine.
-  const uint32_t r = lane & 31u, h = lane >> 5;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float* col = S + nb * kSlotWords + h * 32u * kSlotPitch + r;
+    float* sl = reinterpret_cast<float*>(S + LdsMap<NB>::slots) + nb * kSlotWords + (8u * g) * kSlotPitch + row;
     float v = 0.f;
-#pragma unroll 8
-    for (int l = 0; l < 32; ++l) v += col[l * kSlotPitch];
-    v += __shfl_xor(v, 32, kWave);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v += sl[q * kSlotPitch];
+      sl[q * kSlotPitch] = 0.f;
+    }
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave);
     yacc[nb] += v;
   }
+}
+
+// One tile, all steps; the caller has passed a barrier since the last fold.
+template <int NB>
+__device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, int wave, float (&yacc)[NB],
+                                 uint32_t lane) {
+  const TileRef t = tile_ref(T, rt, kt);
+  if (wave == 0) {
+    // activations of columns 8 i + (lane >> 3), 16 bytes (lane & 7) each, to
+    // x + 128 column + 16 (lane & 7); past the matrix's last group the loads
+    // return zeros
+    const size_t K = (size_t)T.n_groups * kGroup;
+    const uint32_t voff = (uint32_t)t.g0 * 128u + lane * 16u;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
+      const uint32_t lds = lds_addr(S + LdsMap<NB>::x + nb * kXWords);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma16(xrs, lds + 1024u * i, voff + 1024u * i);
+    }
+  }
+  const int lc = min((int)lane, t.Gt - 1);
+  const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)(t.base + 8u * (uint32_t)lc), 0, 0);
+  Flight<0, NB> f0;
+  Flight<1, NB> f1;
+  Flight<2, NB> f2;
+  Flight<3, NB> f3;
+  issue_first<0, NB>(t, wave, f0, lane);
+  issue_first<1, NB>(t, wave, f1, lane);
+  issue_first<2, NB>(t, wave, f2, lane);
+  issue_first<3, NB>(t, wave, f3, lane);
+  tile_prepare<NB>(t, wave, mp, S, lane);
+  __syncthreads();
+  run_class<0, NB>(t, f0, S, wave, lane);
+  run_class<1, NB>(t, f1, S, wave, lane);
+  run_class<2, NB>(t, f2, S, wave, lane);
+  run_class<3, NB>(t, f3, S, wave, lane);
+  __syncthreads();
+  fold_rows<NB>(S, wave, yacc, lane);
 }
 
 // Sum over the 64 lanes (the total lands in every lane).
@@ -333,13 +471,19 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// Residual rows r = part, part + 3, ... of row-tile rt over all k-tiles:
-// y += sum_k x[k] r[n][k], lane l on column l of each k-tile (64 fp16 of the
-// row), the next row's loads issued before the current row is summed.
+// Residual rows r = part, part + 4, ... of row-tile rt over all k-tiles:
+// sum_k x[k] r[n][k], lane l on column l of each k-tile (64 fp16 of the
+// row). The row sums go to Y[nb][r] (one wavefront per row).
 template <int NB>
 __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* Y, uint32_t lane) {
   const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
   const size_t K = (size_t)M.n_groups * kGroup;
+  constexpr int kRows = kTileRows / kGemvWaves;
+  float acc[NB][kRows];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) acc[nb][i] = 0.f;
   for (int kt = 0; kt < M.k_tiles; ++kt) {
     const int g0 = kt * kTileGroups, Gt = min(kTileGroups, M.n_groups - g0);
     const int lc = min((int)lane, Gt - 1);
@@ -357,106 +501,87 @@ __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* 
         xr[nb][4 * i + 3] = live ? v.w : 0u;
       }
     }
-    auto load_row = [&](int r, uint4 (&d)[8]) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int r = part + kGemvWaves * i;
+      if (r >= R) break;
+      uint4 cur[8];
       const uint4* rp = reinterpret_cast<const uint4*>(M.resid + (size_t)(r0 + r) * K + (size_t)(g0 + lc) * kGroup);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) d[i] = rp[i];
-    };
-    if (part >= R) continue;
-    uint4 cur[8], nxt[8];
-    load_row(part, cur);
-    for (int r = part; r < R; r += 3) {
-      const bool more = r + 3 < R;
-      if (more) load_row(r + 3, nxt);
+      for (int q = 0; q < 8; ++q) cur[q] = rp[q];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          a[0] = dot2(cur[i].x, xr[nb][4 * i + 0], a[0]);
-          a[1] = dot2(cur[i].y, xr[nb][4 * i + 1], a[1]);
-          a[2] = dot2(cur[i].z, xr[nb][4 * i + 2], a[2]);
-          a[3] = dot2(cur[i].w, xr[nb][4 * i + 3], a[3]);
+        for (int q = 0; q < 8; ++q) {
+          a[0] = dot2(cur[q].x, xr[nb][4 * q + 0], a[0]);
+          a[1] = dot2(cur[q].y, xr[nb][4 * q + 1], a[1]);
+          a[2] = dot2(cur[q].z, xr[nb][4 * q + 2], a[2]);
+          a[3] = dot2(cur[q].w, xr[nb][4 * q + 3], a[3]);
         }
-        const float v = wave_sum((a[0] + a[1]) + (a[2] + a[3]));
-        if (lane == 0) Y[nb * kTileRows + r] += v;
-      }
-      if (more) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+        acc[nb][i] += wave_sum((a[0] + a[1]) + (a[2] + a[3]));
       }
     }
   }
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int r = part + kGemvWaves * i;
+      if (r < R)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) Y[nb * kTileRows + r] = acc[nb][i];
+    }
 }
 
+// One workgroup per row-tile of every matrix of the launch. A matrix with one
+// k-tile and no residual or levels is one tile per workgroup; otherwise the
+// workgroup takes the row-tile's k-tiles (of every level) in order, then the
+// residual's rows, at a raised wavefront priority (those workgroups come
+// first in the launch and carry several tiles' work).
 template <int NB, bool RESID>
-__global__ __launch_bounds__(kGemvWaves * 64) void k_gemv(const GemvLaunch L) {
-  extern __shared__ __align__(16) uint8_t smem[];
+__global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const GemvLaunch L) {
+  extern __shared__ __align__(16) uint32_t S[];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int mi = 0;
   for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
   const GemvMat& M = L.mats[mi];
-  const int j = (int)blockIdx.x - M.wg_begin;
-  // LDS: the wavefronts' row sums [waves][NB][32], then per wavefront its
-  // slots (NB * kSlotWords words).
-  float* Ys = reinterpret_cast<float*>(smem);
-  float* S = reinterpret_cast<float*>(smem + kGemvWaves * NB * kTileRows * 4) + wave * NB * kSlotWords;
+  const int rt = (int)blockIdx.x - M.wg_begin;
+  for (int i = tid; i < NB * kSlotWords; i += kGemvWaves * kWave) S[LdsMap<NB>::slots + i] = 0u;
   float yacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
-
   if (!M.shared) {
-    // Four row-tiles of a matrix with one k-tile: the wavefronts are independent.
-    const int rt = j * kGemvWaves + wave;
-    if (rt >= M.row_tiles) return;
-    packed_tile<NB>(M, rt, 0, yacc, S, lane);
-    const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-    if ((int)lane < R)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + lane] = yacc[nb];
-    return;
-  }
-
-  // One row-tile: its k-tiles (of every level) spread over the wavefronts, or
-  // with a residual the packed k-tiles on wavefront 0 and the residual's rows
-  // on wavefronts 1-3.
-  const int rt = j;
-  float* Y = Ys + wave * NB * kTileRows;
-  if (RESID && M.resid) {
-    if (wave == 0) {
-      for (int kt = 0; kt < M.k_tiles; ++kt) packed_tile<NB>(M, rt, kt, yacc, S, lane);
-      if (lane < 32)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) Y[nb * kTileRows + lane] = yacc[nb];
-    } else {
-      for (int i = (int)lane; i < NB * kTileRows; i += kWave) Y[i] = 0.f;
-      residual_rows<NB>(M, rt, wave - 1, Y, lane);
-    }
+    coop_tile<NB>(M, rt, 0, S, wave, yacc, lane);
   } else {
-    const int pairs = M.levels * M.k_tiles;
-    for (int p = wave; p < pairs; p += kGemvWaves) {
+    __builtin_amdgcn_s_setprio(2);
+    const int tiles = M.levels * M.k_tiles;
+    for (int p = 0; p < tiles; ++p) {
       const int lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
-      packed_tile<NB>(L.mats[mi + lv], rt, kt, yacc, S, lane);
+      coop_tile<NB>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
     }
-    if (lane < 32)
+    if (RESID && M.resid) {
+      float* Y = reinterpret_cast<float*>(S + LdsMap<NB>::ys);
+      residual_rows<NB>(M, rt, wave, Y, lane);
+      __syncthreads();
+      const uint32_t row = 8u * wave + (lane >> 3);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) Y[nb * kTileRows + lane] = yacc[nb];
+      for (int nb = 0; nb < NB; ++nb) yacc[nb] += Y[nb * kTileRows + row];
+    }
   }
-  __syncthreads();
   const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-  for (int i = tid; i < NB * kTileRows; i += kGemvWaves * kWave) {
-    const int nb = i / kTileRows, r = i - nb * kTileRows;
-    float v = Ys[i];
+  const int row = 8 * wave + (int)(lane >> 3);
+  if ((lane & 7u) == 0 && row < R)
 #pragma unroll
-    for (int w = 1; w < kGemvWaves; ++w) v += Ys[w * NB * kTileRows + i];
-    if (r < R) M.y[(size_t)nb * M.n_rows + r0 + r] = v;
-  }
+    for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + row] = yacc[nb];
 }
 
 size_t gemv_lds_bytes(int nb) {
-  return (size_t)kGemvWaves * ((size_t)nb * kTileRows * 4 + (size_t)nb * kSlotWords * 4);
+  switch (nb) {
+    case 1: return 4u * LdsMap<1>::words;
+    default: return 4u * LdsMap<2>::words;
+  }
 }
 
 template <int NB, bool RESID>
@@ -465,7 +590,7 @@ static hipError_t launch_one(const GemvLaunch& L, int n_wg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, RESID>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -480,8 +605,6 @@ hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, hipStr
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)
-    VBQ_CASE(3)
-    VBQ_CASE(4)
     default:
       return hipErrorInvalidValue;
   }

@@ -1,8 +1,7 @@
 // Device-side packing: per-group round-to-nearest quantisation to fp16
 // scale/offset and the tiled byte stream (tiles of 32 rows x 64 k-groups,
-// a 2-bit width map per column, width-class blocks with one record per
-// column, rows visited from a per-column rotation; the exact rules are in
-// vbq.h).
+// a 2-bit width map per column, then per width class its records listed
+// column by column in blocks of 64; the exact rules are in vbq.h).
 //
 // Groups of 64 weights with per-group widths {1,2,4,8} and packed low-bit
 // storage: VBQ abstract (page "In-Cell Learning: Language Models That Update
@@ -11,11 +10,12 @@
 //
 // Three launches on the caller's stream, one wavefront per tile with lane l
 // on column l (k-group 64 kt + l):
-//   1. k_pack_sizes: class masks per column, block sizes, tile size.
+//   1. k_pack_sizes: class masks per column, records per class, tile size.
 //   2. k_pack_scan : one workgroup scans the tile sizes into byte bases and
 //                    writes the totals entry (with error flags).
-//   3. k_pack_tiles: clears the tile, writes its map, then visits the blocks
-//                    and writes every record (codes and scale/offset).
+//   3. k_pack_tiles: clears the tile, writes its map, then every lane writes
+//                    the records of its column (codes and scale/offset) at
+//                    their closed-form positions.
 // The quantiser's arithmetic must give the same bits on every run and match the
 // documented binary32 sequence, so this file is built with -ffp-contract=off and
 // uses correctly rounded division and round-half-even conversions.
@@ -50,19 +50,6 @@ __device__ inline ColumnInfo read_column(const uint8_t* __restrict__ widths, int
   return ci;
 }
 
-__device__ inline uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, kWave));
-  return v;
-}
-
-// Bytes of the blocks of class c (uniform result).
-__device__ inline uint32_t class_bytes(int c, const ClassWalk& w, uint32_t I) {
-  uint32_t bytes = 0;
-  for (uint32_t i = 0; i < I; ++i) bytes += block_bytes(c, (uint32_t)__popcll(__ballot(walk_active(w, i))));
-  return bytes;
-}
-
 // Tiles are stored k-tile major: t = kt * RT + rt.
 __global__ __launch_bounds__(64) void k_pack_sizes(const uint8_t* __restrict__ widths, int N, int G, int RT,
                                                    uint32_t* __restrict__ tiles) {
@@ -71,20 +58,18 @@ __global__ __launch_bounds__(64) void k_pack_sizes(const uint8_t* __restrict__ w
   const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
   const ColumnInfo ci = read_column(widths, G, r0, R, g0 + lane, lane < Gt);
-  uint32_t bytes = map_bytes((uint32_t)Gt), iw = 0;
+  uint32_t bytes = map_bytes((uint32_t)Gt), n[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const ClassWalk w = class_walk(ci.k.m[c], (uint32_t)lane);
-    const uint32_t I = wave_max(w.n);
-    bytes += class_bytes(c, w, I);
-    iw |= I << (8 * c);
+    n[c] = wave_total((uint32_t)__builtin_popcount(ci.k.m[c]));
+    bytes += class_bytes(c, n[c]);
   }
   const uint32_t bad = (uint32_t)__popcll(__ballot(ci.bad));
   if (lane == 0) {
     tiles[4 * t + 0] = bad;                 // invalid count, replaced by the scan
     tiles[4 * t + 1] = bytes / 16;
-    tiles[4 * t + 2] = iw;
-    tiles[4 * t + 3] = 0;
+    tiles[4 * t + 2] = n[0] | (n[1] << 16);
+    tiles[4 * t + 3] = n[2] | (n[3] << 16);
   }
 }
 
@@ -217,7 +202,7 @@ __global__ __launch_bounds__(64) void k_pack_tiles(const float* __restrict__ W, 
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
   const size_t K = (size_t)G * kGroup;
   uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
-  const uint32_t tsize = tiles[4 * t + 1] * 16, iw = tiles[4 * t + 2];
+  const uint32_t tsize = tiles[4 * t + 1] * 16, w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
   // Clear the tile (padding must be zero); the records are written over it
   // after these stores have completed.
   for (uint32_t i = lane; i < tsize / 16; i += kWave) reinterpret_cast<uint4*>(tb)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -226,31 +211,27 @@ __global__ __launch_bounds__(64) void k_pack_tiles(const float* __restrict__ W, 
   const bool live = lane < Gt;
   const ColumnInfo ci = read_column(widths, G, r0, R, g0 + lane, live);
   if (live) *reinterpret_cast<uint2*>(tb + 8 * lane) = make_uint2(ci.p0, ci.p1);
-  uint32_t pos = map_bytes((uint32_t)Gt);
+  uint32_t cbase = map_bytes((uint32_t)Gt);
   const float* wcol = W + (size_t)(g0 + lane) * kGroup;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t I = (iw >> (8 * c)) & 0xFFu;
-    ClassWalk wk = class_walk(ci.k.m[c], (uint32_t)lane);
-    for (uint32_t i = 0; i < I; ++i) {
-      const bool act = walk_active(wk, i);
-      const uint64_t bal = __ballot(act);
-      const uint32_t m = (uint32_t)__popcll(bal);
-      const uint32_t k = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-      if (act) {
-        const int row = (int)walk_row(wk, (uint32_t)lane);
-        const float* wg = wcol + (size_t)(r0 + row) * K;
-        uint8_t* codes = tb + pos + (8u << c) * k;
-        uint32_t* so = reinterpret_cast<uint32_t*>(tb + pos + codes_area(c, m) + 4u * k);
-        switch (c) {
-          case 0: write_record<0>(wg, codes, so); break;
-          case 1: write_record<1>(wg, codes, so); break;
-          case 2: write_record<2>(wg, codes, so); break;
-          default: write_record<3>(wg, codes, so); break;
-        }
+    const uint32_t n = class_count(w2, w3, c);
+    uint32_t mask = ci.k.m[c];
+    uint32_t e = wave_excl_scan((uint32_t)__builtin_popcount(mask), (uint32_t)lane);
+    for (; mask; mask &= mask - 1u, ++e) {
+      const int row = __builtin_ctz(mask);
+      const RecPos rp = record_pos(c, n, cbase, e);
+      const float* wg = wcol + (size_t)(r0 + row) * K;
+      uint8_t* codes = tb + rp.codes;
+      uint32_t* so = reinterpret_cast<uint32_t*>(tb + rp.so);
+      switch (c) {
+        case 0: write_record<0>(wg, codes, so); break;
+        case 1: write_record<1>(wg, codes, so); break;
+        case 2: write_record<2>(wg, codes, so); break;
+        default: write_record<3>(wg, codes, so); break;
       }
-      pos += block_bytes(c, m);
     }
+    cbase += class_bytes(c, n);
   }
 }
 
@@ -271,8 +252,8 @@ hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& 
 // a packed level leaves:
 //   E_out[n][k] = E_in[n][k] - (f32(s q) + o)
 // in binary32 with one rounding per operation (s q is exact). One wavefront
-// per tile walks the blocks; lane l handles the record of its column, and
-// the code pair p of that record is pair (p % h) of word p / h.
+// per tile; lane l handles the records of its column, and the code pair p of
+// a record is pair (p % h) of word p / h.
 template <int C>
 __device__ inline void residual_record(const uint8_t* codes, uint32_t so, const float* ein, float* eout) {
   constexpr int B = 1 << C, H = 16 / B;
@@ -303,34 +284,29 @@ __global__ __launch_bounds__(64) void k_residual_error(const uint32_t* __restric
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
   const size_t K = (size_t)G * kGroup;
   const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
-  const uint32_t iw = tiles[4 * t + 2];
+  const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
   const bool live = lane < Gt;
   const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
   const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
-  uint32_t pos = map_bytes((uint32_t)Gt);
+  uint32_t cbase = map_bytes((uint32_t)Gt);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t I = (iw >> (8 * c)) & 0xFFu;
-    ClassWalk wk = class_walk(km.m[c], (uint32_t)lane);
-    for (uint32_t i = 0; i < I; ++i) {
-      const bool act = walk_active(wk, i);
-      const uint64_t bal = __ballot(act);
-      const uint32_t m = (uint32_t)__popcll(bal);
-      const uint32_t k = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-      if (act) {
-        const int row = (int)walk_row(wk, (uint32_t)lane);
-        const size_t e = (size_t)(r0 + row) * K + (size_t)(g0 + lane) * kGroup;
-        const uint8_t* codes = tb + pos + (8u << c) * k;
-        const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + pos + codes_area(c, m) + 4u * k);
-        switch (c) {
-          case 0: residual_record<0>(codes, so, E_in + e, E_out + e); break;
-          case 1: residual_record<1>(codes, so, E_in + e, E_out + e); break;
-          case 2: residual_record<2>(codes, so, E_in + e, E_out + e); break;
-          default: residual_record<3>(codes, so, E_in + e, E_out + e); break;
-        }
+    const uint32_t n = class_count(w2, w3, c);
+    uint32_t mask = km.m[c];
+    uint32_t e = wave_excl_scan((uint32_t)__builtin_popcount(mask), (uint32_t)lane);
+    for (; mask; mask &= mask - 1u, ++e) {
+      const int row = __builtin_ctz(mask);
+      const RecPos rp = record_pos(c, n, cbase, e);
+      const size_t at = (size_t)(r0 + row) * K + (size_t)(g0 + lane) * kGroup;
+      const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + rp.so);
+      switch (c) {
+        case 0: residual_record<0>(tb + rp.codes, so, E_in + at, E_out + at); break;
+        case 1: residual_record<1>(tb + rp.codes, so, E_in + at, E_out + at); break;
+        case 2: residual_record<2>(tb + rp.codes, so, E_in + at, E_out + at); break;
+        default: residual_record<3>(tb + rp.codes, so, E_in + at, E_out + at); break;
       }
-      pos += block_bytes(c, m);
     }
+    cbase += class_bytes(c, n);
   }
 }
 

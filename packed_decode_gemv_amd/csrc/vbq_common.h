@@ -28,13 +28,40 @@ __host__ __device__ inline int class_of_width(int b) {
 }
 
 // ---- Tile geometry ---------------------------------------------------------------
-// A tile's map takes 8 bytes per column; a block (c, i) of m columns holds m
-// records of 8 * 2^c code bytes, then m scale/offset words, each area rounded
-// up to 16 bytes.
+// A tile's map takes 8 bytes per column; a block of m records of class c
+// holds m records of 8 * 2^c code bytes, then m scale/offset words, each
+// area rounded up to 16 bytes. The records of class c are listed column by
+// column (rows ascending) and cut into blocks of 64.
 __host__ __device__ constexpr uint32_t up16(uint32_t v) { return (v + 15u) & ~15u; }
 __host__ __device__ constexpr uint32_t map_bytes(uint32_t cols) { return up16(8u * cols); }
 __host__ __device__ constexpr uint32_t codes_area(int c, uint32_t m) { return up16((8u << c) * m); }
 __host__ __device__ constexpr uint32_t block_bytes(int c, uint32_t m) { return codes_area(c, m) + up16(4u * m); }
+__host__ __device__ constexpr uint32_t full_block_bytes(int c) { return (512u << c) + 256u; }
+
+// Bytes of the blocks of a class with n records.
+__host__ __device__ inline uint32_t class_bytes(int c, uint32_t n) {
+  return (n >> 6) * full_block_bytes(c) + ((n & 63u) ? block_bytes(c, n & 63u) : 0u);
+}
+
+// Records of class c in a tile, from the header's count words.
+__host__ __device__ inline uint32_t class_count(uint32_t w2, uint32_t w3, int c) {
+  return ((c < 2 ? w2 : w3) >> (16 * (c & 1))) & 0xFFFFu;
+}
+
+// Byte offsets (from the tile's start) of record e of a class with n records
+// whose first block starts at cbase.
+struct RecPos {
+  uint32_t codes, so;
+};
+__host__ __device__ inline RecPos record_pos(int c, uint32_t n, uint32_t cbase, uint32_t e) {
+  const uint32_t k = e >> 6, j = e & 63u;
+  const uint32_t m = n - 64u * k < 64u ? n - 64u * k : 64u;
+  const uint32_t bb = cbase + k * full_block_bytes(c);
+  RecPos p;
+  p.codes = bb + (8u << c) * j;
+  p.so = bb + codes_area(c, m) + 4u * j;
+  return p;
+}
 
 // Rows of one column per width class from the column's map planes (bit r of
 // plane0 / plane1 = low / high bit of row r's class); rows >= R are empty.
@@ -51,41 +78,25 @@ __host__ __device__ inline ClassMasks class_masks(uint32_t p0, uint32_t p1, int 
   return k;
 }
 
-// Rotation that starts a column's visiting order at row l mod 32: bit j of
-// the result is row (j + l) mod 32, so taking set bits from the lowest visits
-// rows in the order of (r - l) mod 32.
-__host__ __device__ inline uint32_t rotate_rows(uint32_t mask, uint32_t l) {
-  const uint32_t s = l & 31u;
-  return s ? ((mask >> s) | (mask << (32u - s))) : mask;
-}
-
-// How one column (lane) takes part in the blocks of one class of a tile:
-// block i holds the columns with more than i records of the class, each with
-// its i-th row in the order of (r - l) mod 32.
-struct ClassWalk {
-  uint32_t rot;    // rows not yet visited, rotated so that bit j is row (j + l) mod 32
-  uint32_t n;      // records of the class in this column
-};
-
-__host__ __device__ inline ClassWalk class_walk(uint32_t mask, uint32_t lane) {
-  ClassWalk w;
-  w.rot = rotate_rows(mask, lane);
-  w.n = (uint32_t)__builtin_popcount(mask);
-  return w;
-}
-
-// Whether the column takes part in block i.
-__host__ __device__ inline bool walk_active(const ClassWalk& w, uint32_t i) { return w.n > i; }
-
-// The row of the column's record in block i (call only when active, in block
-// order: it advances the column's visiting order).
-__host__ __device__ inline uint32_t walk_row(ClassWalk& w, uint32_t lane) {
-  const uint32_t j = (uint32_t)__builtin_ctz(w.rot);
-  w.rot &= w.rot - 1u;
-  return (j + lane) & 31u;
-}
-
 // ---- Device helpers shared by the kernels -----------------------------------
+// Sum of v over the lanes below this one (lanes of a 64-wide wavefront).
+__device__ inline uint32_t wave_excl_scan(uint32_t v, uint32_t lane) {
+  uint32_t s = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_up((int)s, d, 64);
+    if (lane >= (uint32_t)d) s += u;
+  }
+  return s - v;
+}
+
+// Sum of v over the wavefront (every lane gets it).
+__device__ inline uint32_t wave_total(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += (uint32_t)__shfl_xor((int)v, d, 64);
+  return v;
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // the wavefront are outstanding (and for nothing else).
 #define VBQ_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -125,12 +136,8 @@ __device__ inline void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
 }
 
 // ---- Launch descriptions ---------------------------------------------------------
-// One matrix of a GEMV launch. A launch runs workgroups of four wavefronts.
-// A matrix with one k-tile and no residual gives each wavefront its own
-// row-tile (four per workgroup); otherwise a workgroup owns one row-tile and
-// its wavefronts share the row-tile's k-tiles (and levels), or, with a
-// residual, wavefront 0 takes the packed k-tiles and wavefronts 1-3 the
-// residual's rows.
+// One matrix of a GEMV launch. A launch runs one workgroup of four
+// wavefronts per row-tile of each matrix; the wavefronts share each tile.
 struct GemvMat {
   const uint32_t* tiles;
   const uint8_t* stream;
@@ -149,7 +156,7 @@ struct GemvMat {
 
 constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
 constexpr int kGemvWaves = 4;
-constexpr int kGemvMaxNb = 4;   // batch rows per pass (x of a k-group kept in registers)
+constexpr int kGemvMaxNb = 2;   // batch rows per pass
 
 struct GemvLaunch {
   GemvMat mats[kMaxMats];

@@ -168,19 +168,19 @@ __device__ inline void check_record(const uint32_t* w, const uint4 (&rv)[8], uin
   }
 }
 
-// One workgroup of four wavefronts per tile. Every wavefront walks the tile's
-// blocks (lane l on column l, so that it knows each record's row) and checks
-// the records of every fourth block: codes and scale/offset from the block,
-// the record's 64 residuals from row row, columns 64 (64 kt + l) .. + 63.
+// One workgroup of four wavefronts per tile, lane l on column l: a column's
+// records of each class are taken in row order, wavefront w checking every
+// fourth of them (those with index w mod 4 in the column): codes and
+// scale/offset at the record's position, the record's 64 residuals from its
+// row, columns 64 (64 kt + l) .. + 63.
 constexpr int kVerifyWaves = 4;
 
 template <int C>
-__device__ inline void verify_block(const uint8_t* tb, uint8_t* rb, uint32_t pos, uint32_t m, uint32_t kk,
-                                    const uint16_t* __restrict__ resid, uint64_t lin0, size_t roff, uint32_t& mism,
-                                    uint32_t& ooc, uint64_t& first) {
+__device__ inline void verify_record(const uint8_t* tb, uint8_t* rb, RecPos rp, const uint16_t* __restrict__ resid,
+                                     uint64_t lin0, size_t roff, uint32_t& mism, uint32_t& ooc, uint64_t& first) {
   constexpr int B = 1 << C;
   uint32_t w[2 * B];
-  const uint8_t* cp = tb + pos + (8u * B) * kk;
+  const uint8_t* cp = tb + rp.codes;
   if constexpr (C == 0) {
     const uint2 u = *reinterpret_cast<const uint2*>(cp);
     w[0] = u.x;
@@ -195,15 +195,15 @@ __device__ inline void verify_block(const uint8_t* tb, uint8_t* rb, uint32_t pos
       w[4 * h + 3] = u.w;
     }
   }
-  const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + pos + codes_area(C, m) + 4u * kk);
+  const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + rp.so);
   uint4 rv[8];
-  const uint4* rp = reinterpret_cast<const uint4*>(resid + roff);
+  const uint4* rp16 = reinterpret_cast<const uint4*>(resid + roff);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rv[i] = rp[i];
+  for (int i = 0; i < 8; ++i) rv[i] = rp16[i];
   uint32_t nw[2 * B];
   check_record<C>(w, rv, so, lin0, mism, ooc, first, nw);
   if (rb) {
-    uint8_t* dp = rb + pos + (8u * B) * kk;
+    uint8_t* dp = rb + rp.codes;
     if constexpr (C == 0) {
       *reinterpret_cast<uint2*>(dp) = make_uint2(nw[0], nw[1]);
     } else {
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kVerifyWaves * 64) void k_verify(const uint32_t* __
   const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
   const uint64_t tbyte = (uint64_t)tiles[4 * t + 0] * 16;
-  const uint32_t size = tiles[4 * t + 1] * 16, iw = tiles[4 * t + 2];
+  const uint32_t size = tiles[4 * t + 1] * 16, w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
   const uint8_t* tb = stream + tbyte;
   uint8_t* rb = requant ? requant + tbyte : nullptr;
   // Copy the tile (map, scales, offsets, padding); codes are rewritten below.
@@ -245,35 +245,26 @@ __global__ __launch_bounds__(kVerifyWaves * 64) void k_verify(const uint32_t* __
   const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
   uint32_t mism = 0, ooc = 0;
   uint64_t first = ~0ull;
-  uint32_t pos = map_bytes((uint32_t)Gt);
-  uint32_t blk = 0;   // block index within the tile
+  uint32_t cbase = map_bytes((uint32_t)Gt);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t I = (iw >> (8 * c)) & 0xFFu;
-    const uint32_t n = (uint32_t)__popc(km.m[c]);
-    uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
-    for (uint32_t i = 0; i < I; ++i, ++blk) {
-      const bool act = n > i;
-      const uint64_t bal = __ballot(act);
-      const uint32_t m = (uint32_t)__popcll(bal);
-      const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-      if (act) {
-        const uint32_t j = (uint32_t)__builtin_ctz(rot);
-        rot &= rot - 1u;
-        if ((int)(blk % kVerifyWaves) == wave) {
-          const int row = r0 + (int)((j + (uint32_t)lane) & 31u);
-          const size_t roff = (size_t)row * K + (size_t)(g0 + lane) * kGroup;
-          const uint64_t lin0 = (uint64_t)roff;
-          switch (c) {
-            case 0: verify_block<0>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
-            case 1: verify_block<1>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
-            case 2: verify_block<2>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
-            default: verify_block<3>(tb, rb, pos, m, kk, resid, lin0, roff, mism, ooc, first); break;
-          }
-        }
+    const uint32_t n = class_count(w2, w3, c);
+    uint32_t mask = km.m[c];
+    uint32_t e = wave_excl_scan((uint32_t)__popc(mask), (uint32_t)lane);
+    for (uint32_t j = 0; mask; mask &= mask - 1u, ++e, ++j) {
+      if ((int)(j % kVerifyWaves) != wave) continue;
+      const int row = r0 + __builtin_ctz(mask);
+      const RecPos rp = record_pos(c, n, cbase, e);
+      const size_t roff = (size_t)row * K + (size_t)(g0 + lane) * kGroup;
+      const uint64_t lin0 = (uint64_t)roff;
+      switch (c) {
+        case 0: verify_record<0>(tb, rb, rp, resid, lin0, roff, mism, ooc, first); break;
+        case 1: verify_record<1>(tb, rb, rp, resid, lin0, roff, mism, ooc, first); break;
+        case 2: verify_record<2>(tb, rb, rp, resid, lin0, roff, mism, ooc, first); break;
+        default: verify_record<3>(tb, rb, rp, resid, lin0, roff, mism, ooc, first); break;
       }
-      pos += block_bytes(c, m);
     }
+    cbase += class_bytes(c, n);
   }
   if (mism) atomicAdd(&s_mism, mism);
   if (ooc) atomicAdd(&s_ooc, ooc);
@@ -301,11 +292,12 @@ hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* r
 // with every residual strictly inside half its group's scale, no output moves
 // further than this (CellFill abstract: bounded drift). One workgroup of four
 // wavefronts per row-tile walks its k-tiles in order. Per k-tile it forms X
-// for the tile's groups (fp32, in k order); the wavefronts split the tile's
-// blocks (lane l on column l) and every record puts 0.5 s X[b][l] at its
-// (row, column) slot in LDS (a row has exactly one record per column); then
-// one thread per (batch row, row) adds its slots in column order, so the sum
-// order is fixed. Batches above four rows run as passes.
+// for the tile's groups (fp32, in k order); lane l takes the records of
+// column l (wavefront w every fourth of them) and each record puts
+// 0.5 s X[b][l] at its (row, column) slot in LDS (a row has exactly one
+// record per column); then one thread per (batch row, row) adds its slots in
+// column order, so the sum order is fixed. Batches above four rows run as
+// passes.
 constexpr int kDriftThreads = 256;
 constexpr int kDriftNb = 4;
 
@@ -337,34 +329,25 @@ __global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restr
     __syncthreads();
     const int t = kt * RT + rt;
     const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
-    const uint32_t iw = tiles[4 * t + 2];
+    const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
     const bool live = lane < Gt;
     const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
     const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
-    uint32_t pos = map_bytes((uint32_t)Gt), blk = 0;
+    uint32_t cbase = map_bytes((uint32_t)Gt);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t I = (iw >> (8 * c)) & 0xFFu;
-      const uint32_t n = (uint32_t)__popc(km.m[c]);
-      uint32_t rot = rotate_rows(km.m[c], (uint32_t)lane);
-      for (uint32_t i = 0; i < I; ++i, ++blk) {
-        const bool act = n > i;
-        const uint64_t bal = __ballot(act);
-        const uint32_t m = (uint32_t)__popcll(bal);
-        const uint32_t kk = __mbcnt_hi((uint32_t)(bal >> 32), __mbcnt_lo((uint32_t)bal, 0u));
-        if (act) {
-          const uint32_t j = (uint32_t)__builtin_ctz(rot);
-          rot &= rot - 1u;
-          if ((int)(blk % 4u) == wave) {
-            const int row = (int)((j + (uint32_t)lane) & 31u);
-            const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + pos + codes_area(c, m) + 4u * kk);
-            const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+      const uint32_t n = class_count(w2, w3, c);
+      uint32_t mask = km.m[c];
+      uint32_t e = wave_excl_scan((uint32_t)__popc(mask), (uint32_t)lane);
+      for (uint32_t j = 0; mask; mask &= mask - 1u, ++e, ++j) {
+        if ((int)(j % 4u) != wave) continue;
+        const int row = __builtin_ctz(mask);
+        const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + record_pos(c, n, cbase, e).so);
+        const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
 #pragma unroll
-            for (int b = 0; b < NB; ++b) P[b][row][lane] = hs * X[b][lane];
-          }
-        }
-        pos += block_bytes(c, m);
+        for (int b = 0; b < NB; ++b) P[b][row][lane] = hs * X[b][lane];
       }
+      cbase += class_bytes(c, n);
     }
     __syncthreads();
     if (tid < NB * kTileRows)

@@ -216,17 +216,15 @@ def pin_layout_worked_example():
     2 columns. Classes (r,l): (0,0)=0, (0,1)=3, (1,0)=1, (1,1)=0.
     Map: column 0 plane0 = 0b10, plane1 = 0; column 1 plane0 = 0b01,
     plane1 = 0b01 -> words [2, 0, 1, 1] (16 B).
-    Visiting order (r - l) mod 32: column 0 rows 0, 1; column 1 rows 1, 0.
-    Class 0: both columns hold one row -> I_0 = 1, block (0,0) with columns
-    0, 1 (m=2): groups (0,0), (1,1): codes 16 B, so 8 -> 16 B (32 B at 16).
-    Class 1: I_1 = 1, block (1,0) column 0: group (1,0): 16 + 16 B at 48.
-    Class 3: I_3 = 1, block (3,0) column 1: group (0,1): 64 + 16 B at 80.
-    Total 160 B = 10 units; iteration word 1 | 1<<8 | 1<<24."""
+    Class 0 list (by column, then row): (0,0), (1,1) -> N_0 = 2, one block:
+    codes 16 B at 16, so 8 -> 16 B at 32. Class 1: (1,0): 16 + 16 B at 48.
+    Class 3: (0,1): codes 64 B at 80, so 16 B at 144.
+    Total 160 B = 10 units; count words 2 | 1<<16 and 0 | 1<<16."""
     widths = np.array([[1, 8], [2, 1]], np.uint8)
     W = (_rng(16).standard_normal((2, 128)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
     assert oracle.layout_sizes(widths) == (1, 4, 10)
-    assert list(lay["tiles"]) == [0, 10, 1 | (1 << 8) | (1 << 24), 0, 10, 0, 0, 0]
+    assert list(lay["tiles"]) == [0, 10, 2 | (1 << 16), 1 << 16, 10, 0, 0, 0]
     so00, w00 = _record(W, 0, 0, 1)
     so11, w11 = _record(W, 1, 1, 1)
     so10, w10 = _record(W, 1, 0, 2)
@@ -245,89 +243,80 @@ def pin_layout_worked_example():
         pass
 
 
-def pin_layout_rotation():
-    """Visiting order and shrinking blocks (hand-worked): N=32, K=192, width 1
+def pin_layout_column_major():
+    """Record order and a partial block (hand-worked): N=32, K=192, width 1
     everywhere except (r5, l0) = 8 and (r1, l2) = (r3, l2) = 2.
-    Class 0: n(0)=31, n(1)=32, n(2)=30 -> I_0 = 32; blocks (0,i): columns
-    {0,1,2} for i < 30 (48 B each: codes 24 -> 32, so 12 -> 16), {0,1} at
-    i = 30 (32 B), {1} at i = 31 (32 B): 1504 B after the 32-byte map.
-    Rows in visiting order: column 0: 0,1,2,3,4,6,...,31; column 1:
-    1,2,...,31,0; column 2 (key (r-2) mod 32): 2,4,5,...,31,0.
-    So block (0,0) = groups (0,0),(1,1),(2,2); block (0,29) = (30,0),
-    (30,1),(0,2); block (0,30) = (31,0),(31,1); block (0,31) = (0,1).
-    Class 1 (column 2, rows 3 then 1): blocks at 1536 and 1568 (32 B each).
-    Class 3: block (3,0) at 1600 holding (5,0): codes 64 B, so at 1664.
-    Total 1680 B = 105 units."""
+    Class 0 list: column 0 rows 0-4, 6-31 (e = 0..30), column 1 rows 0-31
+    (e = 31..62), column 2 rows 0, 2, 4-31 (e = 63..92): N_0 = 93.
+    Map 24 -> 32 B. Block (0,0), 64 records, at 32: codes 512 B, so 256 B
+    at 544. Block (0,1), 29 records, at 800: codes 232 -> 240 B, so 116 ->
+    128 B at 1040. Class 1 list (1,2), (3,2): block at 1168, so at 1200.
+    Class 3 (5,0): codes at 1216, so at 1280. Total 1296 B = 81 units.
+    A row-major list would put (1,1) at e = 4 instead of (4,0)."""
     N, G = 32, 3
     widths = np.ones((N, G), np.uint8)
     widths[5, 0] = 8
     widths[1, 2] = widths[3, 2] = 2
     W = (_rng(21).standard_normal((N, 64 * G)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (1, 96, 105)
-    assert list(lay["tiles"]) == [0, 105, 32 | (2 << 8) | (1 << 24), 0, 105, 0, 0, 0]
+    assert oracle.layout_sizes(widths) == (1, 96, 81)
+    assert list(lay["tiles"]) == [0, 81, 93 | (2 << 16), 1 << 16, 81, 0, 0, 0]
     st = lay["stream"]
     words = lambda at, n: [int(v) for v in st[at // 4:at // 4 + n]]
     # map: column 0 plane0/1 = bit 5 (class 3); column 2 plane0 = bits 1, 3
     assert words(0, 8) == [1 << 5, 1 << 5, 0, 0, (1 << 1) | (1 << 3), 0, 0, 0]
-    def block0(i, groups):
-        at = 32 + 48 * i if i < 30 else (32 + 48 * 30 + 32 * (i - 30))
-        m = len(groups)
-        so_at = at + (-(-8 * m // 16) * 16)
-        for k, (r, l) in enumerate(groups):
-            so, w = _record(W, r, l, 1)
-            assert words(at + 8 * k, 2) == w and words(so_at + 4 * k, 1) == [so], (i, k)
-    block0(0, [(0, 0), (1, 1), (2, 2)])
-    block0(4, [(4, 0), (5, 1), (7, 2)])
-    block0(5, [(6, 0), (6, 1), (8, 2)])
-    block0(29, [(30, 0), (30, 1), (0, 2)])
-    block0(30, [(31, 0), (31, 1)])
-    block0(31, [(0, 1)])
-    for at, (r, l) in ((1536, (3, 2)), (1568, (1, 2))):
+    # (e, row, column, codes byte, so byte) of class 0
+    for e, r, l, cat, sat in ((0, 0, 0, 32, 544), (4, 4, 0, 64, 560), (5, 6, 0, 72, 564), (30, 31, 0, 272, 664),
+                              (31, 0, 1, 280, 668), (62, 31, 1, 528, 792), (63, 0, 2, 536, 796),
+                              (64, 2, 2, 800, 1040), (65, 4, 2, 808, 1044), (92, 31, 2, 1024, 1152)):
+        so, w = _record(W, r, l, 1)
+        assert words(cat, 2) == w and words(sat, 1) == [so], e
+    assert words(1032, 2) == [0, 0] and words(1156, 3) == [0, 0, 0]
+    for cat, sat, (r, l) in ((1168, 1200, (1, 2)), (1184, 1204, (3, 2))):
         so, w = _record(W, r, l, 2)
-        assert words(at, 4) == w and words(at + 16, 4) == [so, 0, 0, 0]
+        assert words(cat, 4) == w and words(sat, 1) == [so]
     so, w = _record(W, 5, 0, 8)
-    assert words(1600, 16) == w and words(1664, 4) == [so, 0, 0, 0]
+    assert words(1216, 16) == w and words(1280, 4) == [so, 0, 0, 0]
 
 
 def pin_layout_k_tiles():
     """Tile order and ragged tiles (hand-worked): N=40, K=64*65, all widths 1.
     2 row-tiles x 2 k-tiles, t = kt*2 + rt. Tile 0 (32 rows, 64 columns):
-    map 512 B + 32 blocks of m=64 (codes 512 + so 256 = 768 B) = 25088 B
+    map 512 B + 32 full blocks (codes 512 + so 256 = 768 B) = 25088 B
     (1568 units). Tile 1 (8 rows, 64 columns): 512 + 8*768 = 6656 B (416).
-    Tile 2 (32 rows, 1 column): map 8 -> 16 + 32 blocks of 32 B = 1040 B
-    (65). Tile 3 (8 rows, 1 column): 16 + 8*32 = 272 B (17). Iteration words
-    32, 8, 32, 8."""
+    Tile 2 (32 rows, 1 column): map 8 -> 16 + one block of 32 records
+    (codes 256, so 128) = 400 B (25). Tile 3 (8 rows, 1 column): 16 + 64 +
+    32 = 112 B (7). Counts N_0 = 2048, 512, 32, 8."""
     N, G = 40, 65
     widths = np.ones((N, G), np.uint8)
     W = (_rng(22).standard_normal((N, 64 * G)) * 0.02).astype(np.float32)
     lay = oracle.pack(W, widths)
-    assert oracle.layout_sizes(widths) == (4, N * G, 2066)
+    assert oracle.layout_sizes(widths) == (4, N * G, 2016)
     tiles = lay["tiles"].reshape(-1, 4)
-    assert [list(map(int, t)) for t in tiles] == [[0, 1568, 32, 0], [1568, 416, 8, 0], [1984, 65, 32, 0],
-                                                  [2049, 17, 8, 0], [2066, 0, 0, 0]]
+    assert [list(map(int, t)) for t in tiles] == [[0, 1568, 2048, 0], [1568, 416, 512, 0], [1984, 25, 32, 0],
+                                                  [2009, 7, 8, 0], [2016, 0, 0, 0]]
     st = lay["stream"]
-    # tile 1 (rows 32..39): block (0, i) column l holds row 32 + ((i + l) % 32)
-    # among its 8 rows visited from key (r - l) mod 32: rows >= l % 32 first
+    # tile 1 (rows 32..39): record e = 8 l + r, block e // 64, entry e % 64
     base = 1568 * 16 + 512
-    for l, i in ((0, 0), (5, 0), (5, 2), (7, 7), (63, 7)):
-        order = sorted(range(8), key=lambda r: (r - l) % 32)
-        so, w = _record(W, 32 + order[i], l, 1)
-        at = base + 768 * i
-        assert [int(v) for v in st[(at + 8 * l) // 4:(at + 8 * l) // 4 + 2]] == w
-        assert int(st[(at + 512 + 4 * l) // 4]) == so
-    # tile 3 (rows 32..39, column 64): one column, row order 0..7
-    base = 2049 * 16 + 16
-    for i in (0, 7):
-        so, w = _record(W, 32 + i, 64, 1)
-        assert [int(v) for v in st[(base + 32 * i) // 4:(base + 32 * i) // 4 + 2]] == w
-        assert int(st[(base + 32 * i + 16) // 4]) == so
+    for l, r in ((0, 0), (5, 0), (5, 2), (7, 7), (63, 7)):
+        e = 8 * l + r
+        so, w = _record(W, 32 + r, l, 1)
+        at = base + 768 * (e // 64)
+        j = e % 64
+        assert [int(v) for v in st[(at + 8 * j) // 4:(at + 8 * j) // 4 + 2]] == w
+        assert int(st[(at + 512 + 4 * j) // 4]) == so
+    # tile 3 (rows 32..39, column 64): one block of 8, rows in order
+    base = 2009 * 16 + 16
+    for r in (0, 7):
+        so, w = _record(W, 32 + r, 64, 1)
+        assert [int(v) for v in st[(base + 8 * r) // 4:(base + 8 * r) // 4 + 2]] == w
+        assert int(st[(base + 64 + 4 * r) // 4]) == so
 
 
 def _walk_layout(widths, N, K):
     """Independent reading of the layout rules (written from the header text,
-    not from the oracle's C): yields, per tile, (base byte, size, iteration
-    word, map words, [(byte of codes, byte of so, row, kg, b)])."""
+    not from the oracle's C): yields, per tile, (base byte, size, the two
+    count words, map words, [(byte of codes, byte of so, row, kg, b)])."""
     G = K // 64
     RT, KT = -(-N // 32), -(-G // 64)
     up = lambda v: -(-v // 16) * 16
@@ -342,24 +331,19 @@ def _walk_layout(widths, N, K):
             p0 = sum((cls[int(widths[r, kg])] & 1) << (r - 32 * rt) for r in rows)
             p1 = sum((cls[int(widths[r, kg])] >> 1) << (r - 32 * rt) for r in rows)
             mp += [p0, p1]
-        visit = {}
-        for c in range(4):
-            for l, kg in enumerate(ks):
-                rr = [r - 32 * rt for r in rows if cls[int(widths[r, kg])] == c]
-                visit[c, l] = sorted(rr, key=lambda r: (r - l) % 32)
-        I = [max(len(visit[c, l]) for l in range(len(ks))) for c in range(4)]
+        lists = [[(r, kg) for kg in ks for r in rows if cls[int(widths[r, kg])] == c] for c in range(4)]
         pos = up(8 * len(ks))
         recs = []
         for c in range(4):
             b = 1 << c
-            for i in range(I[c]):
-                act = [l for l in range(len(ks)) if len(visit[c, l]) > i]
-                m = len(act)
-                for k, l in enumerate(act):
-                    recs.append((base + pos + 8 * b * k, base + pos + up(8 * b * m) + 4 * k,
-                                 32 * rt + visit[c, l][i], 64 * kt + l, b))
+            for k0 in range(0, len(lists[c]), 64):
+                blk = lists[c][k0:k0 + 64]
+                m = len(blk)
+                for j, (r, kg) in enumerate(blk):
+                    recs.append((base + pos + 8 * b * j, base + pos + up(8 * b * m) + 4 * j, r, kg, b))
                 pos += up(8 * b * m) + up(4 * m)
-        yield base, pos, I[0] | (I[1] << 8) | (I[2] << 16) | (I[3] << 24), mp, recs
+        n = [len(x) for x in lists]
+        yield base, pos, (n[0] | (n[1] << 16), n[2] | (n[3] << 16)), mp, recs
         base += pos
 
 
@@ -380,7 +364,7 @@ def pin_layout_invariants():
         seen = np.zeros((N, G), np.int32)
         end = 0
         for t, (base, size, iw, mp, recs) in enumerate(_walk_layout(widths, N, K)):
-            assert list(tiles[t]) == [base // 16, size // 16, iw, 0]
+            assert list(tiles[t]) == [base // 16, size // 16, iw[0], iw[1]]
             assert [int(v) for v in st[base // 4:base // 4 + len(mp)]] == mp
             for (cat, sat, row, kg, b) in recs:
                 words = [int(v) for v in oracle.pack_group_record(q2[row, 64 * kg:64 * kg + 64], b)]
@@ -737,7 +721,7 @@ def pin_mean_bits_accounting():
 ALL_PINS = [
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
-    pin_layout_worked_example, pin_layout_rotation, pin_layout_invariants,
+    pin_layout_worked_example, pin_layout_column_major, pin_layout_invariants,
     pin_exact_integer_matvec, pin_gemv_exact_rationals, pin_gemm_bf16_exact,
     pin_drift_bound_and_revocation, pin_drift_bound_attained, pin_rrq_levels, pin_requant_verify,
     pin_requant_verify_edge_cells,

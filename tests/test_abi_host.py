@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = C.CDLL(vbq.LIB_PATH)
     for n in header_functions():
         assert hasattr(lib, n), f"{n} declared in vbq.h but not exported"
-    assert vbq.abi_version() == 3
+    assert vbq.abi_version() == 4
     assert vbq.lib.vbq_status_string(3) == b"width not in {1,2,4,8}"
 
 

@@ -26,7 +26,7 @@ MUTATIONS = {
     5: "cell test uses > instead of >=",
     6: "residual added with the wrong sign",
     7: "scale divides by 2^b instead of 2^b - 1",
-    8: "rows of a column visited in ascending order, not from the column's rotation",
+    8: "records of a class listed row-major instead of column-major",
     9: "record halves swapped",
     10: "bfloat16 rounding breaks ties away from zero",
     11: "re-quantisation drops the clamp to [0, L]",

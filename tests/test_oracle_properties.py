@@ -50,8 +50,13 @@ def test_layout_round_trip(case):
     assert tiles.shape[0] == T + 1 and int(tiles[T][0]) == B16
     # tiles are back to back: each starts where the one before it ends
     assert all(int(tiles[t][0]) + int(tiles[t][1]) == int(tiles[t + 1][0]) for t in range(T))
-    # no column of a tile holds more than 32 records of one class
-    assert all(((int(tiles[t][2]) >> (8 * c)) & 0xFF) <= 32 for t in range(T) for c in range(4))
+    # the class counts of a tile add up to its groups (32 rows x 64 columns at most)
+    RT, KT = oracle.tile_grid(N, K)
+    for t in range(T):
+        kt, rt = divmod(t, RT)
+        rows, cols = min(32, N - 32 * rt), min(64, K // 64 - 64 * kt)
+        counts = [int(tiles[t][2]) & 0xFFFF, int(tiles[t][2]) >> 16, int(tiles[t][3]) & 0xFFFF, int(tiles[t][3]) >> 16]
+        assert sum(counts) == rows * cols
     q, s, o, w = oracle.unpack(lay)
     q2, s2, o2 = oracle.quantize_matrix(W, widths)
     assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(o, o2)
