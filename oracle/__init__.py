@@ -85,6 +85,10 @@ def _declare(L):
     L.orc_requant_verify.argtypes = [P, P, P, P, P, C.c_int, C.c_int, P, P]
     L.orc_set_mutation.restype = None
     L.orc_set_mutation.argtypes = [C.c_int]
+    L.orc_cell8_encode.restype = None
+    L.orc_cell8_encode.argtypes = [P, P, C.c_int, C.c_int, P]
+    L.orc_gemv_cell8.restype = None
+    L.orc_gemv_cell8.argtypes = [P, P, P, C.c_int, C.c_int, P, C.c_int, P, P]
 
 
 def _p(a):
@@ -338,3 +342,33 @@ def requant_verify(q, s16, o16, widths, r16, want_codes: bool = False):
     lib().orc_requant_verify(_p(q), _p(_c(s16, np.uint16)), _p(_c(o16, np.uint16)),
                              _p(_c(widths, np.uint8)), _p(_c(r16, np.uint16)), N, K, _p(counts), _p(qp))
     return int(counts[0]), int(counts[1]), int(counts[2]), qp
+
+
+def cell8_encode(r16, s16) -> np.ndarray:
+    """Compact in-cell residual (this library's own encoding: the CellFill
+    page keeps the residual inside its rounding cell but fixes no storage):
+    a signed byte f per weight stands for r = s * f / 256, |f| <= 127, so
+    every encoded residual is inside its cell. Encodes an fp16 residual in
+    binary32: f = clamp(rint(f32(r / s) * 256), -127, 127), 0 where s = 0.
+    Returns int8 [N][K]."""
+    r16 = _c(r16, np.uint16)
+    s16 = _c(s16, np.uint16)
+    N, K = r16.shape
+    assert s16.shape == (N, K // 64)
+    f = np.zeros((N, K), np.int8)
+    lib().orc_cell8_encode(_p(r16), _p(s16), N, K, _p(f))
+    return f
+
+
+def gemv_cell8(q, s16, o16, x, f) -> np.ndarray:
+    """y [B][N] fp64 = x . (s*q + o + s*f/256)^T, natural k order."""
+    q = _c(q, np.uint8)
+    s16 = _c(s16, np.uint16)
+    o16 = _c(o16, np.uint16)
+    x = _c(np.atleast_2d(x), np.uint16)
+    f = _c(f, np.int8)
+    N, K = q.shape
+    assert f.shape == (N, K) and x.shape[1] == K
+    y = np.zeros((x.shape[0], N), np.float64)
+    lib().orc_gemv_cell8(_p(q), _p(s16), _p(o16), N, K, _p(x), x.shape[0], _p(f), _p(y))
+    return y

@@ -576,6 +576,55 @@ void orc_requant_verify(const uint8_t* q, const uint16_t* s16, const uint16_t* o
 }
 
 /* ------------------------------------------------------------------ */
+/* Compact in-cell residual: one byte per weight                        */
+/* ------------------------------------------------------------------ */
+/* An encoding of the in-cell residual of this library's own (the CellFill
+ * page keeps the residual inside the weight's rounding cell but fixes no
+ * storage for it): a signed byte f in [-127, 127] per weight stands for
+ *   r = s * f / 256        (s = the group's fp16 scale)
+ * so |r| <= (127/256) s < s/2: every encoded residual lies inside its cell.
+ * Encoding an fp16 residual, in binary32 with one rounding per operation:
+ *   f = s == 0 ? 0 : clamp(rint(f32(r / s) * 256), -127, 127)   (ties even) */
+void orc_cell8_encode(const uint16_t* r16, const uint16_t* s16, int N, int K, int8_t* f) {
+  int G = K / 64;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      float sc = orc_f16_to_f32(s16[n * G + k / 64]);
+      float r = orc_f16_to_f32(r16[n * K + k]);
+      int v = 0;
+      if (sc != 0.0f) {
+        float t = (r / sc) * 256.0f;
+        float rr = (g_mut == 14) ? truncf(t) : rintf(t);   /* mutation: truncation */
+        if (rr < -127.0f) rr = -127.0f;
+        if (rr > 127.0f) rr = 127.0f;
+        v = (int)rr;
+      }
+      f[n * K + k] = (int8_t)v;
+    }
+}
+
+/* y[b][n] = sum_k x[b][k] * (s*q + o + s*f/256), fp64 (exact widening; the
+ * products and the division by 256 are exact in fp64). */
+void orc_gemv_cell8(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, int N, int K, const uint16_t* x,
+                    int B, const int8_t* f, double* y) {
+  int G = K / 64;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)B * K);
+  for (int64_t i = 0; i < (int64_t)B * K; ++i) xd[i] = orc_f16_to_f64(x[i]);
+  double frac = (g_mut == 13) ? 128.0 : 256.0;          /* mutation: wrong fraction unit */
+  for (int64_t n = 0; n < N; ++n)
+    for (int b = 0; b < B; ++b) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double sc = orc_f16_to_f64(s16[n * G + k / 64]);
+        double w = dequant(q, s16, o16, NULL, n, k, K) + sc * (double)f[n * K + k] / frac;
+        acc += xd[(int64_t)b * K + k] * w;
+      }
+      y[(int64_t)b * N + n] = acc;
+    }
+  free(xd);
+}
+
+/* ------------------------------------------------------------------ */
 /* Array helpers for the Python wrapper                                 */
 /* ------------------------------------------------------------------ */
 void orc_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {

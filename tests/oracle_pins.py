@@ -674,6 +674,69 @@ def _golden(name):
     return vals
 
 
+def pin_cell8_encode_values():
+    """Compact in-cell residual, hand-worked (scale s = 0.25 = 0x3400):
+    r = fp16(0.1) = 0.0999755859375 -> r/s*256 = 102.375 -> f = 102;
+    r = 0.125 -> 128 -> clamped to 127; r = -0.125 -> -127;
+    r = -2^-10 -> -1; r = 1.75*2^-9 (0x1B00) -> 3.5 -> 4 (tie to even);
+    r = 1.375*2^-9 (0x1980) -> 2.75 -> 3; r = 1.25*2^-9 (0x1900) -> 2.5 -> 2;
+    a zero scale gives 0 whatever r."""
+    vals = [(0x2E66, 102), (0x3000, 127), (0xB000, -127), (0x9400, -1), (0x1B00, 4), (0x1980, 3), (0x1900, 2)]
+    r16 = np.zeros((2, 64), np.uint16)
+    for i, (r, _) in enumerate(vals):
+        r16[0, i] = r
+        r16[1, i] = r
+    s16 = np.array([[0x3400], [0x0000]], np.uint16)
+    f = oracle.cell8_encode(r16, s16)
+    assert [int(v) for v in f[0, :len(vals)]] == [e for _, e in vals]
+    assert (f[1] == 0).all()
+
+
+def pin_cell8_gemv_equals_fp16_residual():
+    """With power-of-two scales every s*f/256 is an exact fp16 value, so the
+    GEMV with the compact residual must equal, bit for bit, the GEMV with the
+    fp16 residual r = fp16(s*f/256) (the two oracle paths share no code for
+    the residual term)."""
+    r = _rng(31)
+    N, K = 5, 256
+    G = K // 64
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G))
+    q = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        for g in range(G):
+            q[n, 64 * g:64 * g + 64] = r.integers(0, 1 << int(widths[n, g]), 64)
+    s = oracle.f16_from_f64(2.0 ** r.integers(-8, -2, (N, G)).astype(np.float64))
+    o = oracle.f16_from_f64(r.standard_normal((N, G)) * 0.05)
+    f = r.integers(-127, 128, (N, K)).astype(np.int8)
+    sd = np.repeat(oracle.f64_from_f16(s), 64, axis=1)
+    r16 = oracle.f16_from_f64(sd * f.astype(np.float64) / 256.0)
+    assert np.array_equal(oracle.f64_from_f16(r16), sd * f.astype(np.float64) / 256.0)
+    x = oracle.f16_from_f64(r.standard_normal((2, K)))
+    y8 = oracle.gemv_cell8(q, s, o, x, f)
+    y16 = oracle.gemv(q, s, o, x, resid=r16)
+    assert np.array_equal(y8, y16)
+
+
+def pin_cell8_inside_cell():
+    """Whatever residual is encoded, the decoded s*f/256 is inside the cell
+    (|.| <= 127/256 s < s/2); a residual already inside the representable
+    range comes back within s/512 (half a step of the fraction) plus the
+    binary32 rounding of r/s."""
+    r = _rng(32)
+    N, K = 6, 128
+    G = K // 64
+    s = oracle.f16_from_f64(np.abs(r.standard_normal((N, G))) * 0.01 + 1e-3)
+    sd = np.repeat(oracle.f64_from_f16(s), 64, axis=1)
+    wide = oracle.f16_from_f64(r.uniform(-2, 2, (N, K)) * sd)
+    f = oracle.cell8_encode(wide, s)
+    dec = sd * f.astype(np.float64) / 256.0
+    assert (np.abs(dec) <= 127.0 / 256.0 * sd).all() and (np.abs(dec) < 0.5 * sd).all()
+    inside = oracle.f16_from_f64(r.uniform(-127 / 256, 127 / 256, (N, K)) * sd)
+    f2 = oracle.cell8_encode(inside, s)
+    err = np.abs(sd * f2.astype(np.float64) / 256.0 - oracle.f64_from_f16(inside))
+    assert (err <= sd / 512.0 * (1 + 1e-6)).all()
+
+
 def pin_abstract_storage_ratios():
     """The VBQ abstract's storage ratios follow from its mean bits when only
     code bits are counted (16 / mean bits per parameter), and do not when the
@@ -719,6 +782,7 @@ def pin_mean_bits_accounting():
 
 
 ALL_PINS = [
+    pin_cell8_encode_values, pin_cell8_gemv_equals_fp16_residual, pin_cell8_inside_cell,
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
     pin_layout_worked_example, pin_layout_column_major, pin_layout_invariants,

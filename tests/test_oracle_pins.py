@@ -27,6 +27,8 @@ MUTATIONS = {
     6: "residual added with the wrong sign",
     7: "scale divides by 2^b instead of 2^b - 1",
     8: "records of a class listed row-major instead of column-major",
+    13: "compact in-cell fraction counted in 1/128 of the scale instead of 1/256",
+    14: "compact in-cell encoding truncates instead of rounding to nearest",
     9: "record halves swapped",
     10: "bfloat16 rounding breaks ties away from zero",
     11: "re-quantisation drops the clamp to [0, L]",
