@@ -181,6 +181,24 @@ vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uin
 vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
                             int32_t B, hipStream_t stream);
 
+/* vbq_gemv_batched for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation), spread
+ * over more workgroups: every k-tile of a matrix with K > 4096 gets a
+ * workgroup of its own, and the row sums of a row-tile's k-tiles meet in a
+ * scratch area the library keeps in static device memory (one copy per
+ * device, 1 MiB of partial sums and 16384 row-tile counters, held until the
+ * process ends; nothing is allocated per call). The workgroup that finishes
+ * a row-tile's last k-tile adds the partial sums in k-tile order, the order
+ * vbq_gemv_batched uses, so both calls give the same bits, and sets the
+ * row-tile's counter back to zero. Arguments and results as for
+ * vbq_gemv_batched. A launch needing more than the scratch holds (more than
+ * 8192 tiles of such matrices at one batch row, 4096 at two or more) returns
+ * VBQ_ERR_UNSUPPORTED before anything is enqueued. Calls that overlap in
+ * time on one device race on the scratch and must not be made; a call whose
+ * kernels do not complete can leave counters behind for the next call. */
+vbq_status vbq_gemv_batched_static(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs,
+                                   float* const* ys, int32_t B, hipStream_t stream);
+
 /* GEMV over several levels of one weight matrix (RRQ abstract on page
  * thelatestinai.com/papers/2512.18934: a 2-bit base plus 2-bit residual
  * levels served from one checkpoint), in one launch:

@@ -50,8 +50,8 @@ class vbq_layout_sizes(C.Structure):
 
 
 EXPORTS = ("vbq_abi_version", "vbq_status_string", "vbq_pack_query", "vbq_pack", "vbq_matrix_check",
-           "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_levels", "vbq_gemm", "cell_requant_verify",
-           "cell_drift_bound", "vbq_residual_error")
+           "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_batched_static", "vbq_gemv_levels", "vbq_gemm",
+           "cell_requant_verify", "cell_drift_bound", "vbq_residual_error")
 
 
 def _load():
@@ -74,6 +74,9 @@ def _load():
     lib.vbq_gemv.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P, P]
     lib.vbq_gemv_batched.restype = C.c_int
     lib.vbq_gemv_batched.argtypes = [I32, C.POINTER(vbq_matrix), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), I32, P]
+    lib.vbq_gemv_batched_static.restype = C.c_int
+    lib.vbq_gemv_batched_static.argtypes = [I32, C.POINTER(vbq_matrix), C.POINTER(C.c_void_p),
+                                            C.POINTER(C.c_void_p), I32, P]
     lib.vbq_gemv_levels.restype = C.c_int
     lib.vbq_gemv_levels.argtypes = [I32, C.POINTER(vbq_matrix), P, I32, P, P]
     lib.vbq_gemm.restype = C.c_int
@@ -216,12 +219,15 @@ def vbq_gemv(pm: PackedMatrix, x, residual=None, out=None, stream=None):
     return out
 
 
-def vbq_gemv_batched(pms, xs, ys=None, stream=None):
-    """One launch for several independent GEMVs (same batch size)."""
+def vbq_gemv_batched(pms, xs, ys=None, stream=None, static=False):
+    """One launch for several independent GEMVs (same batch size). With
+    static=True it calls vbq_gemv_batched_static, which allocates nothing and
+    gives every k-tile of a long matrix a workgroup of its own."""
     import torch
+    name = "vbq_gemv_batched_static" if static else "vbq_gemv_batched"
     n = len(pms)
     if not 1 <= n <= MAX_LAUNCH_MATS or len(xs) != n or (ys is not None and len(ys) != n):
-        raise ValueError(f"vbq_gemv_batched: {n} matrices, {len(xs)} inputs (1..{MAX_LAUNCH_MATS} each)")
+        raise ValueError(f"{name}: {n} matrices, {len(xs)} inputs (1..{MAX_LAUNCH_MATS} each)")
     x2s = [_rows2(x) for x in xs]
     B = x2s[0].shape[0]
     for pm, x in zip(pms, x2s):
@@ -233,15 +239,16 @@ def vbq_gemv_batched(pms, xs, ys=None, stream=None):
     descs = (vbq_matrix * n)(*[pm.desc for pm in pms])
     xp = (C.c_void_p * n)(*[x.data_ptr() for x in x2s])
     yp = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
-    _check(lib.vbq_gemv_batched(n, descs, xp, yp, B, _stream(stream)), "vbq_gemv_batched")
+    _check(getattr(lib, name)(n, descs, xp, yp, B, _stream(stream)), name)
     return ys
 
 
 class GemvPlan:
-    """Pre-marshalled argument block of vbq_gemv_batched, for timing loops
-    (the tensors are checked once, here)."""
+    """Pre-marshalled argument block of vbq_gemv_batched (or, with
+    static=True, vbq_gemv_batched_static), for timing loops (the tensors are
+    checked once, here)."""
 
-    def __init__(self, pms, xs, ys):
+    def __init__(self, pms, xs, ys, static=False):
         import torch
         n = len(pms)
         if not 1 <= n <= MAX_LAUNCH_MATS:
@@ -255,11 +262,13 @@ class GemvPlan:
         self.xp = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
         self.yp = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
         self._keep = (pms, xs, ys)
+        self.name = "vbq_gemv_batched_static" if static else "vbq_gemv_batched"
+        self._fn = getattr(lib, self.name)
 
     def launch(self, stream_handle):
-        st = lib.vbq_gemv_batched(self.n, self.descs, self.xp, self.yp, self.B, stream_handle)
+        st = self._fn(self.n, self.descs, self.xp, self.yp, self.B, stream_handle)
         if st != 0:
-            raise VbqError(st, "vbq_gemv_batched")
+            raise VbqError(st, self.name)
 
 
 def vbq_gemm(pm: PackedMatrix, x_bf16, out=None, stream=None):

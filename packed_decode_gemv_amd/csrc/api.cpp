@@ -148,7 +148,7 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream) {
 // levels > 1 one output summed over `count` levels, or one matrix with a
 // residual. Batches above two rows run as passes of up to two rows.
 static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, const uint16_t* resid,
-                            float* const* ys, int32_t B, bool levels, hipStream_t stream) {
+                            float* const* ys, int32_t B, bool levels, hipStream_t stream, bool split = false) {
   if (count < 1 || count > kMaxMats || !ms || !xs || !ys) return VBQ_ERR_INVALID_ARG;
   if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
   if (resid && count != 1) return VBQ_ERR_INVALID_ARG;
@@ -160,10 +160,29 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     if (levels && (ms[i].n_rows != ms[0].n_rows || ms[i].n_cols != ms[0].n_cols)) return VBQ_ERR_SHAPE;
   }
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
+  float* partials = nullptr;
+  uint32_t* counters = nullptr;
+  if (split) {
+    // Every matrix with several tiles per row-tile takes a slot of partial
+    // sums per tile and a counter per row-tile in the scratch.
+    int64_t units = 0, ctrs = 0;
+    for (int i = 0; i < count; ++i) {
+      const int KT = k_tiles(ms[i].n_cols / kGroup);
+      if (KT > 1) {
+        units += (int64_t)row_tiles(ms[i].n_rows) * KT;
+        ctrs += row_tiles(ms[i].n_rows);
+      }
+    }
+    if (units * std::min(B, kGemvMaxNb) * kTileRows > (int64_t)kScratchPartials || ctrs > (int64_t)kScratchCounters)
+      return VBQ_ERR_UNSUPPORTED;
+    if (gemv_scratch(&partials, &counters) != hipSuccess) return VBQ_ERR_HIP;
+  }
   for (int b0 = 0; b0 < B; b0 += kGemvMaxNb) {
     const int nb = std::min(kGemvMaxNb, B - b0);
     GemvLaunch L;
     memset(&L, 0, sizeof(L));
+    L.partials = partials;
+    L.counters = counters;
     // Matrices whose workgroups share a row-tile (several k-tiles) take the
     // first workgroups: each of those does more work, so it starts first.
     int order[kMaxMats], no = 0;
@@ -175,7 +194,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     if (levels) {
       for (int i = 0; i < count; ++i) order[i] = i;   // levels stay together, in order
     }
-    int64_t wg = 0;
+    int64_t wg = 0, unit = 0, ctr = 0;
     for (int pos = 0; pos < count; ++pos) {
       const int i = order[pos];
       const vbq_matrix& m = ms[i];
@@ -194,8 +213,16 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.levels = (levels && pos == 0) ? count : 1;
       g.stream_bytes = (uint32_t)(m.n_bytes16 * 16);
       g.wg_begin = (int32_t)wg;
-      if (!levels || pos == 0)
+      g.split = (split && g.k_tiles > 1) ? 1 : 0;
+      g.unit_base = (int32_t)unit;
+      g.ctr_base = (int32_t)ctr;
+      if (g.split) {
+        wg += (int64_t)g.row_tiles * g.k_tiles;
+        unit += (int64_t)g.row_tiles * g.k_tiles;
+        ctr += g.row_tiles;
+      } else if (!levels || pos == 0) {
         wg += g.row_tiles;
+      }
     }
     if (wg > 0x7FFFFFFF) return VBQ_ERR_UNSUPPORTED;
     L.n_mats = count;
@@ -212,6 +239,11 @@ vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uin
 vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
                             int32_t B, hipStream_t stream) {
   return gemv_impl(count, ms, xs, nullptr, ys, B, false, stream);
+}
+
+vbq_status vbq_gemv_batched_static(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs,
+                                   float* const* ys, int32_t B, hipStream_t stream) {
+  return gemv_impl(count, ms, xs, nullptr, ys, B, false, stream, true);
 }
 
 vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* x, int32_t B, float* y,

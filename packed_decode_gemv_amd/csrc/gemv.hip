@@ -547,11 +547,53 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
   int mi = 0;
   for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
   const GemvMat& M = L.mats[mi];
-  const int rt = (int)blockIdx.x - M.wg_begin;
+  const int j = (int)blockIdx.x - M.wg_begin;
   for (int i = tid; i < NB * kSlotWords; i += kGemvWaves * kWave) S[LdsMap<NB>::slots + i] = 0u;
   float yacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
+  const int row = 8 * wave + (int)(lane >> 3);
+  if (M.split) {
+    // One tile of a row-tile with several: its row sums go to the scratch;
+    // the workgroup that finishes the row-tile's last tile adds them in tile
+    // order (the order the sequential path uses) and resets the counter.
+    const int tiles = M.levels * M.k_tiles;
+    const int rt = j / tiles, p = j - rt * tiles, lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
+    coop_tile<NB>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
+    // The partial sums are device-scope atomic stores, which write through
+    // the caches, so once they are complete (the wait before the barrier)
+    // the counter may count this tile; the last workgroup reads them with
+    // device-scope atomic loads. No cache-wide write-back is needed.
+    float* part = L.partials + (size_t)(M.unit_base + rt * tiles) * NB * kTileRows;
+    if ((lane & 7u) == 0)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        __hip_atomic_store(&part[((size_t)p * NB + nb) * kTileRows + row], yacc[nb], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));
+    __syncthreads();
+    __shared__ uint32_t last;
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(&L.counters[M.ctr_base + rt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(tiles - 1)
+                 ? 1u
+                 : 0u;
+    __syncthreads();
+    if (!last) return;
+    const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
+    if ((lane & 7u) == 0 && row < R)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float v = 0.f;
+        for (int q = 0; q < tiles; ++q)
+          v += __hip_atomic_load(&part[((size_t)q * NB + nb) * kTileRows + row], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        M.y[(size_t)nb * M.n_rows + r0 + row] = v;
+      }
+    if (tid == 0) __hip_atomic_store(&L.counters[M.ctr_base + rt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int rt = j;
   if (!M.shared) {
     coop_tile<NB>(M, rt, 0, S, wave, yacc, lane);
   } else {
@@ -571,10 +613,31 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
     }
   }
   const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-  const int row = 8 * wave + (int)(lane >> 3);
   if ((lane & 7u) == 0 && row < R)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + row] = yacc[nb];
+}
+
+// Scratch of the split GEMV, one copy per device: partial row sums, then
+// row-tile counters. Counters start at zero (static storage) and the last
+// workgroup of each row-tile sets its counter back to zero.
+static __device__ __align__(256) uint8_t scratch[kScratchPartials * 4 + kScratchCounters * 4];
+
+hipError_t gemv_scratch(float** partials, uint32_t** counters) {
+  static void* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *partials = reinterpret_cast<float*>(ptr[dev]);
+  *counters = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ptr[dev]) + kScratchPartials * 4);
+  return hipSuccess;
 }
 
 size_t gemv_lds_bytes(int nb) {

@@ -152,6 +152,9 @@ struct GemvMat {
   int32_t shared;          // 1: a workgroup per row-tile (k-tiles, levels or residual shared by its waves)
   int32_t levels;          // matrices summed into one output (levels), this one and the next levels-1
   uint32_t stream_bytes;   // size of the stream, for the buffer range checks
+  int32_t split;           // 1: a workgroup per (row-tile, tile); partial row sums meet in the scratch
+  int32_t unit_base;       // first partial-sum slot of this matrix in the scratch (split)
+  int32_t ctr_base;        // first row-tile counter of this matrix in the scratch (split)
 };
 
 constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
@@ -161,12 +164,19 @@ constexpr int kGemvMaxNb = 2;   // batch rows per pass
 struct GemvLaunch {
   GemvMat mats[kMaxMats];
   int32_t n_mats;
+  float* partials;         // split matrices: [slot][NB][32] row sums of one tile
+  uint32_t* counters;      // split matrices: tiles finished per row-tile (back to 0 when all are)
 };
 static_assert(sizeof(GemvLaunch) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Host-side launch helpers.
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s);
 hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, hipStream_t s);
+// The scratch of the split GEMV on the current device: partial row sums and
+// row-tile counters (sizes in elements).
+constexpr size_t kScratchPartials = 1u << 18;   // 1 MiB of float
+constexpr size_t kScratchCounters = 1u << 14;   // 64 KiB of uint32
+hipError_t gemv_scratch(float** partials, uint32_t** counters);
 size_t gemv_lds_bytes(int nb);
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s);
