@@ -169,9 +169,38 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.
  * y: device, B x N float32, 4-byte aligned; fully overwritten.
- * Batches above 4 rows are run as passes of at most 4 rows. */
+ * Batches above 2 rows are run as passes of at most 2 rows. */
 vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
                     hipStream_t stream);
+
+/* Compact in-cell residual (CellFill abstract, page "Nothing Changed but the
+ * Model: CellFill -- Bounded In-Cell Learning for Bit-Identical, Revocable
+ * Updates to Quantized LLMs": the update is a residual inside each weight's
+ * rounding cell, served beside the frozen artifact and revoked by dropping
+ * it). The page fixes no storage for the residual; this library's compact
+ * form is one signed byte f per weight in [-127, 127], standing for
+ *   r[n][k] = s[n][g] * f[n][k] / 256        (g = k / 64, s the fp16 scale)
+ * so |r| <= 127/256 s < s/2: every encodable residual is inside its cell.
+ *
+ * vbq_gemv_cell8: y[b][n] = sum_k x[b][k] * (s*q + o + s*f/256), fp32
+ *   accumulation, the residual term of each (row, group) added to the
+ *   group's record term before the tile's row sums. Arguments as vbq_gemv;
+ *   cell: device, N x K int8 row-major (natural order), 16-byte aligned,
+ *   not NULL (the base weights are vbq_gemv with residual NULL).
+ * cell8_encode: f = clamp(rint(f32(r / s) * 256), -127, 127) per weight in
+ *   binary32 (IEEE division, ties to even), f = 0 where s = 0; residuals
+ *   beyond the cell clamp to its edge. residual: device, N x K fp16 (finite
+ *   values), 16-byte aligned; cell: device, N x K int8, 16-byte aligned,
+ *   fully overwritten.
+ * cell8_decode: r = fp16(s * f / 256) (exact before the one rounding), the
+ *   fp16 residual that vbq_gemv and cell_requant_verify take. cell and
+ *   residual as above; residual fully overwritten.
+ * Scales come from the packed matrix m, so the residual follows the scales
+ * that are served. */
+vbq_status vbq_gemv_cell8(const vbq_matrix* m, const uint16_t* x, int32_t B, const int8_t* cell, float* y,
+                          hipStream_t stream);
+vbq_status cell8_encode(const vbq_matrix* m, const uint16_t* residual, int8_t* cell, hipStream_t stream);
+vbq_status cell8_decode(const vbq_matrix* m, const int8_t* cell, uint16_t* residual, hipStream_t stream);
 
 /* Several independent GEMVs in one launch (same batch B, no residual; VBQ
  * abstract, fused dequantise-and-multiply): y_i = x_i . dequant(W_i)^T for

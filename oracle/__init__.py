@@ -87,6 +87,8 @@ def _declare(L):
     L.orc_set_mutation.argtypes = [C.c_int]
     L.orc_cell8_encode.restype = None
     L.orc_cell8_encode.argtypes = [P, P, C.c_int, C.c_int, P]
+    L.orc_cell8_decode.restype = None
+    L.orc_cell8_decode.argtypes = [P, P, C.c_int, C.c_int, P]
     L.orc_gemv_cell8.restype = None
     L.orc_gemv_cell8.argtypes = [P, P, P, C.c_int, C.c_int, P, C.c_int, P, P]
 
@@ -358,6 +360,18 @@ def cell8_encode(r16, s16) -> np.ndarray:
     f = np.zeros((N, K), np.int8)
     lib().orc_cell8_encode(_p(r16), _p(s16), N, K, _p(f))
     return f
+
+
+def cell8_decode(f, s16) -> np.ndarray:
+    """The fp16 residual each fraction byte stands for: fp16(s * f / 256)
+    (exact before the one rounding). Returns uint16 fp16 bits [N][K]."""
+    f = _c(f, np.int8)
+    s16 = _c(s16, np.uint16)
+    N, K = f.shape
+    assert s16.shape == (N, K // 64)
+    r16 = np.zeros((N, K), np.uint16)
+    lib().orc_cell8_decode(_p(f), _p(s16), N, K, _p(r16))
+    return r16
 
 
 def gemv_cell8(q, s16, o16, x, f) -> np.ndarray:

@@ -603,6 +603,16 @@ void orc_cell8_encode(const uint16_t* r16, const uint16_t* s16, int N, int K, in
     }
 }
 
+/* The fp16 residual a fraction byte stands for: r = fp16(s f / 256). s f / 256
+ * is exact in fp64, so the result is one rounding to nearest even. */
+void orc_cell8_decode(const int8_t* f, const uint16_t* s16, int N, int K, uint16_t* r16) {
+  int G = K / 64;
+  double unit = (g_mut == 15) ? 255.0 : 256.0;          /* mutation: wrong fraction unit in the decode */
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      r16[n * K + k] = orc_f64_to_f16(orc_f16_to_f64(s16[n * G + k / 64]) * (double)f[n * K + k] / unit);
+}
+
 /* y[b][n] = sum_k x[b][k] * (s*q + o + s*f/256), fp64 (exact widening; the
  * products and the division by 256 are exact in fp64). */
 void orc_gemv_cell8(const uint8_t* q, const uint16_t* s16, const uint16_t* o16, int N, int K, const uint16_t* x,

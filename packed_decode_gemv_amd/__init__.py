@@ -10,8 +10,9 @@ tensors are checked here, before anything is launched (a wrong tensor raises
 ``ValueError``).
 
 Function names follow the C ABI: ``vbq_pack``, ``vbq_gemv``,
-``vbq_gemv_batched``, ``vbq_gemv_levels``, ``vbq_gemm``, ``cell_requant_verify``,
-``cell_drift_bound``, ``vbq_residual_error``.
+``vbq_gemv_batched``, ``vbq_gemv_batched_static``, ``vbq_gemv_levels``,
+``vbq_gemv_cell8``, ``vbq_gemm``, ``cell_requant_verify``, ``cell_drift_bound``,
+``cell8_encode``, ``cell8_decode``, ``vbq_residual_error``.
 """
 from __future__ import annotations
 
@@ -51,7 +52,8 @@ class vbq_layout_sizes(C.Structure):
 
 EXPORTS = ("vbq_abi_version", "vbq_status_string", "vbq_pack_query", "vbq_pack", "vbq_matrix_check",
            "vbq_gemv", "vbq_gemv_batched", "vbq_gemv_batched_static", "vbq_gemv_levels", "vbq_gemm",
-           "cell_requant_verify", "cell_drift_bound", "vbq_residual_error")
+           "cell_requant_verify", "cell_drift_bound", "vbq_residual_error", "vbq_gemv_cell8", "cell8_encode",
+           "cell8_decode")
 
 
 def _load():
@@ -87,6 +89,12 @@ def _load():
     lib.cell_drift_bound.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P]
     lib.vbq_residual_error.restype = C.c_int
     lib.vbq_residual_error.argtypes = [C.POINTER(vbq_matrix), P, P, P]
+    lib.vbq_gemv_cell8.restype = C.c_int
+    lib.vbq_gemv_cell8.argtypes = [C.POINTER(vbq_matrix), P, I32, P, P, P]
+    lib.cell8_encode.restype = C.c_int
+    lib.cell8_encode.argtypes = [C.POINTER(vbq_matrix), P, P, P]
+    lib.cell8_decode.restype = C.c_int
+    lib.cell8_decode.argtypes = [C.POINTER(vbq_matrix), P, P, P]
     return lib
 
 
@@ -216,6 +224,47 @@ def vbq_gemv(pm: PackedMatrix, x, residual=None, out=None, stream=None):
     _need(out, "out", torch.float32, (B, pm.N), pm.device)
     st = lib.vbq_gemv(C.byref(pm.desc), _ptr(x2), B, _ptr(residual), _ptr(out), _stream(stream))
     _check(st, "vbq_gemv")
+    return out
+
+
+def vbq_gemv_cell8(pm: PackedMatrix, x, cell, out=None, stream=None):
+    """y [B][N] float32 = x [B][K] (fp16) . (dequant(W) + s * cell / 256)^T,
+    cell int8 [N][K] (the compact in-cell residual)."""
+    import torch
+    x2 = _rows2(x)
+    B = x2.shape[0]
+    _need(x2, "x", torch.float16, (B, pm.K), pm.device)
+    if not 1 <= B <= MAX_BATCH:
+        raise ValueError(f"x: batch {B} outside 1..{MAX_BATCH}")
+    _need(cell, "cell", torch.int8, (pm.N, pm.K), pm.device)
+    if out is None:
+        out = torch.empty(B, pm.N, dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (B, pm.N), pm.device)
+    _check(lib.vbq_gemv_cell8(C.byref(pm.desc), _ptr(x2), B, _ptr(cell), _ptr(out), _stream(stream)),
+           "vbq_gemv_cell8")
+    return out
+
+
+def cell8_encode(pm: PackedMatrix, residual, out=None, stream=None):
+    """int8 [N][K] fractions f = clamp(rint(r / s * 256), -127, 127) of an fp16
+    residual, with the scales of the packed matrix."""
+    import torch
+    _need(residual, "residual", torch.float16, (pm.N, pm.K), pm.device)
+    if out is None:
+        out = torch.empty(pm.N, pm.K, dtype=torch.int8, device=residual.device)
+    _need(out, "out", torch.int8, (pm.N, pm.K), pm.device)
+    _check(lib.cell8_encode(C.byref(pm.desc), _ptr(residual), _ptr(out), _stream(stream)), "cell8_encode")
+    return out
+
+
+def cell8_decode(pm: PackedMatrix, cell, out=None, stream=None):
+    """fp16 [N][K] residual fp16(s * f / 256) of int8 fractions f."""
+    import torch
+    _need(cell, "cell", torch.int8, (pm.N, pm.K), pm.device)
+    if out is None:
+        out = torch.empty(pm.N, pm.K, dtype=torch.float16, device=cell.device)
+    _need(out, "out", torch.float16, (pm.N, pm.K), pm.device)
+    _check(lib.cell8_decode(C.byref(pm.desc), _ptr(cell), _ptr(out), _stream(stream)), "cell8_decode")
     return out
 
 

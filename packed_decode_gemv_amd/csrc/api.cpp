@@ -146,12 +146,15 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream) {
 
 // One GEMV launch sequence: `count` matrices (independent outputs), or with
 // levels > 1 one output summed over `count` levels, or one matrix with a
-// residual. Batches above two rows run as passes of up to two rows.
+// residual (fp16 per weight, or int8 cell fractions). Batches above two rows
+// run as passes of up to two rows.
 static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, const uint16_t* resid,
-                            float* const* ys, int32_t B, bool levels, hipStream_t stream, bool split = false) {
+                            const int8_t* cell, float* const* ys, int32_t B, bool levels, hipStream_t stream,
+                            bool split = false) {
   if (count < 1 || count > kMaxMats || !ms || !xs || !ys) return VBQ_ERR_INVALID_ARG;
   if (B < 1 || B > VBQ_MAX_BATCH) return VBQ_ERR_UNSUPPORTED;
-  if (resid && count != 1) return VBQ_ERR_INVALID_ARG;
+  if ((resid || cell) && (count != 1 || levels)) return VBQ_ERR_INVALID_ARG;
+  if (resid && cell) return VBQ_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
     vbq_status st = check_matrix(&ms[i]);
     if (st != VBQ_OK) return st;
@@ -160,6 +163,8 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     if (levels && (ms[i].n_rows != ms[0].n_rows || ms[i].n_cols != ms[0].n_cols)) return VBQ_ERR_SHAPE;
   }
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
+  if (cell && !aligned(cell, 16)) return VBQ_ERR_ALIGNMENT;
+  const int mode = resid ? kModeResid16 : cell ? kModeCell8 : kModePlain;
   float* partials = nullptr;
   uint32_t* counters = nullptr;
   if (split) {
@@ -204,6 +209,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
       g.stream = reinterpret_cast<const uint8_t*>(m.stream);
       g.x = xs[i] + (size_t)b0 * m.n_cols;
       g.resid = resid;
+      g.cell = cell;
       g.y = (levels ? ys[0] : ys[i]) + (size_t)b0 * m.n_rows;
       g.n_rows = m.n_rows;
       g.n_groups = G;
@@ -226,24 +232,46 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     }
     if (wg > 0x7FFFFFFF) return VBQ_ERR_UNSUPPORTED;
     L.n_mats = count;
-    if (launch_gemv(L, nb, resid != nullptr, (int)wg, stream) != hipSuccess) return VBQ_ERR_HIP;
+    if (launch_gemv(L, nb, mode, (int)wg, stream) != hipSuccess) return VBQ_ERR_HIP;
   }
   return VBQ_OK;
 }
 
 vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
                     hipStream_t stream) {
-  return gemv_impl(1, m, &x, residual, &y, B, false, stream);
+  return gemv_impl(1, m, &x, residual, nullptr, &y, B, false, stream);
+}
+
+vbq_status vbq_gemv_cell8(const vbq_matrix* m, const uint16_t* x, int32_t B, const int8_t* cell, float* y,
+                          hipStream_t stream) {
+  if (!cell) return VBQ_ERR_INVALID_ARG;
+  return gemv_impl(1, m, &x, nullptr, cell, &y, B, false, stream);
+}
+
+vbq_status cell8_encode(const vbq_matrix* m, const uint16_t* residual, int8_t* cell, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!residual || !cell) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(residual, 16) || !aligned(cell, 16)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_cell8_encode(*m, residual, cell, stream));
+}
+
+vbq_status cell8_decode(const vbq_matrix* m, const int8_t* cell, uint16_t* residual, hipStream_t stream) {
+  vbq_status st = check_matrix(m);
+  if (st != VBQ_OK) return st;
+  if (!residual || !cell) return VBQ_ERR_INVALID_ARG;
+  if (!aligned(residual, 16) || !aligned(cell, 16)) return VBQ_ERR_ALIGNMENT;
+  return from_hip(launch_cell8_decode(*m, cell, residual, stream));
 }
 
 vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs, float* const* ys,
                             int32_t B, hipStream_t stream) {
-  return gemv_impl(count, ms, xs, nullptr, ys, B, false, stream);
+  return gemv_impl(count, ms, xs, nullptr, nullptr, ys, B, false, stream);
 }
 
 vbq_status vbq_gemv_batched_static(int32_t count, const vbq_matrix* ms, const uint16_t* const* xs,
                                    float* const* ys, int32_t B, hipStream_t stream) {
-  return gemv_impl(count, ms, xs, nullptr, ys, B, false, stream, true);
+  return gemv_impl(count, ms, xs, nullptr, nullptr, ys, B, false, stream, true);
 }
 
 vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* x, int32_t B, float* y,
@@ -251,7 +279,7 @@ vbq_status vbq_gemv_levels(int32_t count, const vbq_matrix* ms, const uint16_t* 
   if (count < 1 || count > kMaxMats || !ms || !x || !y) return VBQ_ERR_INVALID_ARG;
   std::vector<const uint16_t*> xs(count, x);
   std::vector<float*> ys(count, y);
-  return gemv_impl(count, ms, xs.data(), nullptr, ys.data(), B, true, stream);
+  return gemv_impl(count, ms, xs.data(), nullptr, nullptr, ys.data(), B, true, stream);
 }
 
 vbq_status vbq_gemm(const vbq_matrix* m, const uint16_t* x_bf16, int32_t M, float* y, hipStream_t stream) {

@@ -193,6 +193,11 @@ struct LdsMap {
   static constexpr int slots = table + kMaxRecs / 2;      // [NB][64][33]
   static constexpr int ys = slots + NB * kSlotWords;      // [NB][32] residual row sums
   static constexpr int words = ys + NB * kTileRows;
+  // With a compact in-cell residual: the scale of slot (column, row) and the
+  // residual dot of slot (column, row) per batch row, same pitch as the slots.
+  static constexpr int sc = words;
+  static constexpr int cd = sc + kSlotWords;
+  static constexpr int words_cell = cd + NB * kSlotWords;
 };
 
 // Buffer offset that lies outside every stream: loads from it return zeros
@@ -348,7 +353,7 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
 // Decodes lane's record of chunk j: the dot starts from -bias, so it ends as
 // sum_k q_k x_k; the slot of (column, row) gets s * dot + o * sum(x). Lanes
 // past the class's last record write the spare slot of column 31.
-template <int C, int NB>
+template <int C, int NB, bool CELL>
 __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const TileRef& t, uint32_t j, uint32_t* S,
                                     uint32_t lane) {
   const uint32_t e = 64u * j + lane;
@@ -357,6 +362,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
   const uint32_t col = ent >> 5, row = valid ? (ent & 31u) : 32u;
   const float s = __half2float(__ushort_as_half((unsigned short)(r.so & 0xFFFFu)));
   const float o = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
+  if (CELL) reinterpret_cast<float*>(S + LdsMap<NB>::sc)[col * kSlotPitch + row] = s;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + col * 32u;
@@ -384,7 +390,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
 
 // Step 3 for class C: the chunks in flight are decoded in turn and each
 // slot is refilled with the chunk D further on.
-template <int C, int NB>
+template <int C, int NB, bool CELL>
 __device__ inline void run_class(const TileRef& t, Flight<C, NB>& f, uint32_t* S, int wave, uint32_t lane) {
   constexpr int D = depth<C, NB>();
   const uint32_t nS = wave_chunks(t.n[C], wave);
@@ -395,7 +401,7 @@ __device__ inline void run_class(const TileRef& t, Flight<C, NB>& f, uint32_t* S
     for (int d = 0; d < D; ++d) {
       const uint32_t sq = s0 + d;
       if (sq >= nS) break;
-      decode_chunk<C, NB>(k, f.r[d], t, (uint32_t)wave + kGemvWaves * sq, S, lane);
+      decode_chunk<C, NB, CELL>(k, f.r[d], t, (uint32_t)wave + kGemvWaves * sq, S, lane);
       const uint32_t sn = sq + D;
       if (sn < nS) issue_chunk<C>(t, (uint32_t)wave + kGemvWaves * sn, f.r[d], lane);
     }
@@ -425,11 +431,134 @@ __device__ inline void fold_rows(uint32_t* S, int wave, float (&yacc)[NB], uint3
   }
 }
 
-// One tile, all steps; the caller has passed a barrier since the last fold.
+// ---- Compact in-cell residual ---------------------------------------------------
+// Weight (n, k) of group g carries f[n][k] (int8, |f| <= 127), the residual
+// s_g f / 256. Per (row, column) of a tile the slot gets s / 256 times
+// D = sum_k f_k x_k on top of the record's value. Byte f ^ 0x80 = f + 128
+// under the fp16 exponent byte 0x64 reads as 1152 + f, so two byte permutes
+// and two v_dot2 take four weights, and the dot starts from -1152 sum(x).
+// D needs no scale, so four more wavefronts of the workgroup form it while
+// the first four decode the tile: cell wavefront c takes rows 8c..8c+7, lane
+// l its column l (the lane's 64 activations stay in registers for the eight
+// rows, and a row's 64 bytes per lane are one 4 KiB contiguous stretch per
+// wavefront), and leaves D in LDS. After the decode barrier it adds
+// s / 256 D to the slots of its rows, whose scales the decode left in LDS,
+// and folds those rows.
 template <int NB>
-__device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, int wave, float (&yacc)[NB],
-                                 uint32_t lane) {
-  const TileRef t = tile_ref(T, rt, kt);
+__host__ __device__ constexpr int cell_depth() {
+  return NB == 1 ? 3 : 2;   // rows of fractions in flight per wavefront
+}
+
+struct CellRows {
+  __amdgpu_buffer_rsrc_t rs;   // from the wavefront's first row, column g0
+  uint32_t pitch;              // K bytes
+  int rows;                    // rows of the tile this wavefront takes (may be <= 0)
+  bool live;                   // lane's column inside the matrix
+};
+
+__device__ inline CellRows cell_rows_of(const GemvMat& T, int rt, int kt, int cw, uint32_t lane) {
+  CellRows c;
+  const uint32_t K = (uint32_t)T.n_groups * kGroup;
+  const int R = min(kTileRows, T.n_rows - rt * kTileRows);
+  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, T.n_groups - g0);
+  c.pitch = K;
+  c.rows = min(8, R - 8 * cw);
+  c.live = (int)lane < Gt;
+  const int rows = max(c.rows, 1);
+  const size_t first = (size_t)(rt * kTileRows + 8 * cw) * K + (size_t)g0 * kGroup;
+  // the fractions this wavefront may read: its rows, columns g0 .. g0 + Gt - 1
+  const uint32_t extent = (uint32_t)(rows - 1) * K + (uint32_t)Gt * kGroup;
+  c.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(T.cell) + (c.rows > 0 ? first : 0), (short)0,
+                                           (int)extent, 0x00020000);
+  return c;
+}
+
+__device__ inline void cell_issue(const CellRows& c, int i, u32x4 (&v)[4], uint32_t lane) {
+  const uint32_t off = (c.live && i < c.rows) ? (uint32_t)i * c.pitch + lane * kGroup : kNoRecord;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) v[h] = __builtin_amdgcn_raw_buffer_load_b128(c.rs, (int)(off + 16u * h), 0, 0);
+}
+
+template <int NB>
+struct CellFlight {
+  u32x4 v[cell_depth<NB>()][4];
+};
+
+// D of rows 8c..8c+7 of the lane's column, to LDS (rows of the tile only).
+template <int NB>
+__device__ inline void cell_dots(const CellRows& c, CellFlight<NB>& f, uint32_t* S, int cw, uint32_t lane) {
+  constexpr int D = cell_depth<NB>();
+  uint32_t xr[NB][32];
+  float base[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * 32u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
+      xr[nb][4 * i + 0] = v.x;
+      xr[nb][4 * i + 1] = v.y;
+      xr[nb][4 * i + 2] = v.z;
+      xr[nb][4 * i + 3] = v.w;
+    }
+    base[nb] = -1152.f * reinterpret_cast<const float*>(S + LdsMap<NB>::xsum)[nb * kWave + lane];
+  }
+  const uint32_t magic = vconst<0x64646464u>();
+  float* cd = reinterpret_cast<float*>(S + LdsMap<NB>::cd) + lane * kSlotPitch + 8 * cw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i >= c.rows) break;
+    const u32x4(&v)[4] = f.v[i % D];
+    float a[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      a[nb][0] = base[nb];
+      a[nb][1] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t u = w[q] ^ 0x80808080u;
+        const uint32_t lo = __builtin_amdgcn_perm(magic, u, 0x04010400u);
+        const uint32_t hi = __builtin_amdgcn_perm(magic, u, 0x04030402u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          a[nb][0] = dot2(lo, xr[nb][8 * h + 2 * q], a[nb][0]);
+          a[nb][1] = dot2(hi, xr[nb][8 * h + 2 * q + 1], a[nb][1]);
+        }
+      }
+    }
+    if (i + D < 8) cell_issue(c, i + D, f.v[i % D], lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) cd[nb * kSlotWords + i] = a[nb][0] + a[nb][1];
+  }
+}
+
+// After the decode barrier: slot (l, 8c + i) += s / 256 D_i for the lane's
+// column (columns past the matrix hold no record and stay zero).
+template <int NB>
+__device__ inline void cell_apply(const CellRows& c, uint32_t* S, int cw, uint32_t lane) {
+  if (!c.live) return;
+  const float* sc = reinterpret_cast<const float*>(S + LdsMap<NB>::sc) + lane * kSlotPitch + 8 * cw;
+  const float* cd = reinterpret_cast<const float*>(S + LdsMap<NB>::cd) + lane * kSlotPitch + 8 * cw;
+  float* slot = reinterpret_cast<float*>(S + LdsMap<NB>::slots) + lane * kSlotPitch + 8 * cw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i >= c.rows) break;
+    const float s256 = sc[i] * (1.f / 256.f);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      slot[nb * kSlotWords + i] = __builtin_fmaf(s256, cd[nb * kSlotWords + i], slot[nb * kSlotWords + i]);
+  }
+}
+
+// Step 1 and 2 of a tile for the decoding wavefronts: activation copies, the
+// first loads of every class, the biases and the record table.
+template <int NB>
+__device__ inline void tile_start(const GemvMat& T, const TileRef& t, uint32_t* S, int wave, Flight<0, NB>& f0,
+                                  Flight<1, NB>& f1, Flight<2, NB>& f2, Flight<3, NB>& f3, uint32_t lane) {
   if (wave == 0) {
     // activations of columns 8 i + (lane >> 3), 16 bytes (lane & 7) each, to
     // x + 128 column + 16 (lane & 7); past the matrix's last group the loads
@@ -446,23 +575,58 @@ __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, 
   }
   const int lc = min((int)lane, t.Gt - 1);
   const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)(t.base + 8u * (uint32_t)lc), 0, 0);
-  Flight<0, NB> f0;
-  Flight<1, NB> f1;
-  Flight<2, NB> f2;
-  Flight<3, NB> f3;
   issue_first<0, NB>(t, wave, f0, lane);
   issue_first<1, NB>(t, wave, f1, lane);
   issue_first<2, NB>(t, wave, f2, lane);
   issue_first<3, NB>(t, wave, f3, lane);
   tile_prepare<NB>(t, wave, mp, S, lane);
-  __syncthreads();
-  run_class<0, NB>(t, f0, S, wave, lane);
-  run_class<1, NB>(t, f1, S, wave, lane);
-  run_class<2, NB>(t, f2, S, wave, lane);
-  run_class<3, NB>(t, f3, S, wave, lane);
-  __syncthreads();
-  fold_rows<NB>(S, wave, yacc, lane);
 }
+
+// One tile, all steps; the caller has passed a barrier since the last fold.
+// With a compact in-cell residual (CELL) the workgroup has eight wavefronts:
+// 0-3 decode, 4-7 form the residual dots and then fold the rows. Every
+// wavefront meets the same two barriers, at the same points of the code
+// (only the work between them depends on the wavefront's role), and nothing
+// of one role's work stays in registers across a barrier.
+template <int NB, bool CELL>
+__device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, int wave, float (&yacc)[NB],
+                                 uint32_t lane) {
+  const bool cell_wave = CELL && wave >= kGemvWaves;
+  TileRef t;
+  Flight<0, NB> f0;
+  Flight<1, NB> f1;
+  Flight<2, NB> f2;
+  Flight<3, NB> f3;
+  if (!cell_wave) {
+    t = tile_ref(T, rt, kt);
+    tile_start<NB>(T, t, S, wave, f0, f1, f2, f3, lane);
+  }
+  __syncthreads();
+  if (!cell_wave) {
+    run_class<0, NB, CELL>(t, f0, S, wave, lane);
+    run_class<1, NB, CELL>(t, f1, S, wave, lane);
+    run_class<2, NB, CELL>(t, f2, S, wave, lane);
+    run_class<3, NB, CELL>(t, f3, S, wave, lane);
+  } else if constexpr (CELL) {
+    const int cw = wave - kGemvWaves;
+    const CellRows c = cell_rows_of(T, rt, kt, cw, lane);
+    CellFlight<NB> cf;
+#pragma unroll
+    for (int i = 0; i < cell_depth<NB>(); ++i) cell_issue(c, i, cf.v[i], lane);
+    cell_dots<NB>(c, cf, S, cw, lane);
+  }
+  __syncthreads();
+  if constexpr (CELL) {
+    if (cell_wave) {
+      const int cw = wave - kGemvWaves;
+      cell_apply<NB>(cell_rows_of(T, rt, kt, cw, lane), S, cw, lane);
+      fold_rows<NB>(S, cw, yacc, lane);
+    }
+  } else {
+    fold_rows<NB>(S, wave, yacc, lane);
+  }
+}
+
 
 // Sum over the 64 lanes (the total lands in every lane).
 __device__ inline float wave_sum(float v) {
@@ -538,8 +702,14 @@ __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* 
 // workgroup takes the row-tile's k-tiles (of every level) in order, then the
 // residual's rows, at a raised wavefront priority (those workgroups come
 // first in the launch and carry several tiles' work).
-template <int NB, bool RESID>
-__global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const GemvLaunch L) {
+template <int MODE>
+__host__ __device__ constexpr int gemv_waves() {
+  return MODE == kModeCell8 ? 2 * kGemvWaves : kGemvWaves;
+}
+
+template <int NB, int MODE>
+__global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_gemv(const GemvLaunch L) {
+  constexpr bool RESID = MODE == kModeResid16, CELL = MODE == kModeCell8;
   extern __shared__ __align__(16) uint32_t S[];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -548,24 +718,28 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
   for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
   const GemvMat& M = L.mats[mi];
   const int j = (int)blockIdx.x - M.wg_begin;
-  for (int i = tid; i < NB * kSlotWords; i += kGemvWaves * kWave) S[LdsMap<NB>::slots + i] = 0u;
+  for (int i = tid; i < NB * kSlotWords; i += gemv_waves<MODE>() * kWave) S[LdsMap<NB>::slots + i] = 0u;
   float yacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
-  const int row = 8 * wave + (int)(lane >> 3);
+  // the wavefronts that fold rows (all four, or the four cell wavefronts)
+  // hold row 8 fw + lane / 8 in lanes 8 r
+  const int fw = CELL ? wave - kGemvWaves : wave;
+  const bool folds = fw >= 0;
+  const int row = 8 * fw + (int)(lane >> 3);
   if (M.split) {
     // One tile of a row-tile with several: its row sums go to the scratch;
     // the workgroup that finishes the row-tile's last tile adds them in tile
     // order (the order the sequential path uses) and resets the counter.
     const int tiles = M.levels * M.k_tiles;
     const int rt = j / tiles, p = j - rt * tiles, lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
-    coop_tile<NB>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
+    coop_tile<NB, CELL>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
     // The partial sums are device-scope atomic stores, which write through
     // the caches, so once they are complete (the wait before the barrier)
     // the counter may count this tile; the last workgroup reads them with
     // device-scope atomic loads. No cache-wide write-back is needed.
     float* part = L.partials + (size_t)(M.unit_base + rt * tiles) * NB * kTileRows;
-    if ((lane & 7u) == 0)
+    if (folds && (lane & 7u) == 0)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         __hip_atomic_store(&part[((size_t)p * NB + nb) * kTileRows + row], yacc[nb], __ATOMIC_RELAXED,
@@ -581,7 +755,7 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
     __syncthreads();
     if (!last) return;
     const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-    if ((lane & 7u) == 0 && row < R)
+    if (folds && (lane & 7u) == 0 && row < R)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float v = 0.f;
@@ -595,13 +769,13 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
   }
   const int rt = j;
   if (!M.shared) {
-    coop_tile<NB>(M, rt, 0, S, wave, yacc, lane);
+    coop_tile<NB, CELL>(M, rt, 0, S, wave, yacc, lane);
   } else {
     __builtin_amdgcn_s_setprio(2);
     const int tiles = M.levels * M.k_tiles;
     for (int p = 0; p < tiles; ++p) {
       const int lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
-      coop_tile<NB>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
+      coop_tile<NB, CELL>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
     }
     if (RESID && M.resid) {
       float* Y = reinterpret_cast<float*>(S + LdsMap<NB>::ys);
@@ -613,7 +787,7 @@ __global__ __launch_bounds__(kGemvWaves * 64, NB == 1 ? 4 : 2) void k_gemv(const
     }
   }
   const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
-  if ((lane & 7u) == 0 && row < R)
+  if (folds && (lane & 7u) == 0 && row < R)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + row] = yacc[nb];
 }
@@ -640,31 +814,34 @@ hipError_t gemv_scratch(float** partials, uint32_t** counters) {
   return hipSuccess;
 }
 
-size_t gemv_lds_bytes(int nb) {
+size_t gemv_lds_bytes(int nb, int mode) {
+  const bool cell = mode == kModeCell8;
   switch (nb) {
-    case 1: return 4u * LdsMap<1>::words;
-    default: return 4u * LdsMap<2>::words;
+    case 1: return 4u * (cell ? LdsMap<1>::words_cell : LdsMap<1>::words);
+    default: return 4u * (cell ? LdsMap<2>::words_cell : LdsMap<2>::words);
   }
 }
 
-template <int NB, bool RESID>
+template <int NB, int MODE>
 static hipError_t launch_one(const GemvLaunch& L, int n_wg, hipStream_t s) {
-  const size_t lds = gemv_lds_bytes(NB);
+  const size_t lds = gemv_lds_bytes(NB, MODE);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, RESID>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<NB, MODE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemv<NB, RESID>), dim3(n_wg), dim3(kGemvWaves * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemv<NB, MODE>), dim3(n_wg), dim3(gemv_waves<MODE>() * kWave), lds, s, L);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, hipStream_t s) {
-#define VBQ_CASE(N)                                                                        \
-  case N:                                                                                  \
-    return resid ? launch_one<N, true>(L, n_wg, s) : launch_one<N, false>(L, n_wg, s);
+hipError_t launch_gemv(const GemvLaunch& L, int nb, int mode, int n_wg, hipStream_t s) {
+#define VBQ_CASE(N)                                                                      \
+  case N:                                                                                \
+    return mode == kModeResid16  ? launch_one<N, kModeResid16>(L, n_wg, s)               \
+           : mode == kModeCell8 ? launch_one<N, kModeCell8>(L, n_wg, s)                  \
+                                : launch_one<N, kModePlain>(L, n_wg, s);
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)

@@ -317,4 +317,115 @@ hipError_t launch_residual_error(const vbq_matrix& m, const float* E_in, float* 
   return hipGetLastError();
 }
 
+// ---- Compact in-cell residual ----------------------------------------------------
+// CellFill abstract (page "Nothing Changed but the Model: CellFill -- Bounded
+// In-Cell Learning for Bit-Identical, Revocable Updates to Quantized LLMs"):
+// an update is a residual that stays inside each weight's rounding cell. The
+// compact form keeps one signed byte f per weight, standing for s f / 256 with
+// s the scale of the weight's group; |f| <= 127 keeps every such residual
+// strictly inside its cell. In binary32:
+//   encode  f = clamp(rint(f32(r / s) * 256), -127, 127), and 0 where s = 0;
+//   decode  r = fp16(s f / 256) (s f / 256 is exact, so one rounding).
+// One wavefront per tile; lane l handles the records of its column.
+__device__ inline uint32_t cell8_code(uint32_t h, float s) {
+  const float r = __half2float(__ushort_as_half((unsigned short)h));
+  float t = s != 0.f ? rintf(__fdiv_rn(r, s) * 256.f) : 0.f;
+  t = fminf(fmaxf(t, -127.f), 127.f);
+  return (uint32_t)(int32_t)t & 0xFFu;
+}
+
+// fp16(s f / 256). The conversion is written out as v_cvt_f16_f32: folded into
+// a mixed-precision fma with a +0 addend, it would turn the -0 of a zero scale
+// times a negative f into +0.
+__device__ inline uint32_t cell8_value(uint32_t byte, float s) {
+  const float v = (float)(int32_t)(int8_t)(uint8_t)byte;
+  const float r = (s * v) * (1.f / 256.f);
+  uint32_t h;
+  asm("v_cvt_f16_f32 %0, %1" : "=v"(h) : "v"(r));
+  return h & 0xFFFFu;
+}
+
+template <bool ENCODE>
+__device__ inline void cell8_record(float s, const void* in, void* out) {
+  if constexpr (ENCODE) {
+    const uint4* rp = reinterpret_cast<const uint4*>(in);
+    uint4* fp = reinterpret_cast<uint4*>(out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 a = rp[2 * q], b = rp[2 * q + 1];
+      const uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = cell8_code(h[2 * i] & 0xFFFFu, s) | (cell8_code(h[2 * i] >> 16, s) << 8) |
+               (cell8_code(h[2 * i + 1] & 0xFFFFu, s) << 16) | (cell8_code(h[2 * i + 1] >> 16, s) << 24);
+      fp[q] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    const uint4* fp = reinterpret_cast<const uint4*>(in);
+    uint4* rp = reinterpret_cast<uint4*>(out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = fp[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[2 * i] = cell8_value(w[i] & 0xFFu, s) | (cell8_value((w[i] >> 8) & 0xFFu, s) << 16);
+        h[2 * i + 1] = cell8_value((w[i] >> 16) & 0xFFu, s) | (cell8_value(w[i] >> 24, s) << 16);
+      }
+      rp[2 * q] = make_uint4(h[0], h[1], h[2], h[3]);
+      rp[2 * q + 1] = make_uint4(h[4], h[5], h[6], h[7]);
+    }
+  }
+}
+
+// ENCODE: in = fp16 residual [N][K], out = int8 [N][K]; else the reverse.
+template <bool ENCODE>
+__global__ __launch_bounds__(64) void k_cell8(const uint32_t* __restrict__ tiles, const uint8_t* __restrict__ stream,
+                                              int N, int G, int RT, const void* in, void* out) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int kt = t / RT, rt = t - kt * RT;
+  const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
+  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
+  const size_t K = (size_t)G * kGroup;
+  const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
+  const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
+  const bool live = lane < Gt;
+  const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
+  const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
+  constexpr size_t kIn = ENCODE ? 2 : 1, kOut = ENCODE ? 1 : 2;   // bytes per weight
+  uint32_t cbase = map_bytes((uint32_t)Gt);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t n = class_count(w2, w3, c);
+    uint32_t mask = km.m[c];
+    uint32_t e = wave_excl_scan((uint32_t)__builtin_popcount(mask), (uint32_t)lane);
+    for (; mask; mask &= mask - 1u, ++e) {
+      const int row = __builtin_ctz(mask);
+      const RecPos rp = record_pos(c, n, cbase, e);
+      const size_t at = (size_t)(r0 + row) * K + (size_t)(g0 + lane) * kGroup;
+      const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + rp.so);
+      const float sc = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+      cell8_record<ENCODE>(sc, reinterpret_cast<const uint8_t*>(in) + at * kIn,
+                           reinterpret_cast<uint8_t*>(out) + at * kOut);
+    }
+    cbase += class_bytes(c, n);
+  }
+}
+
+hipError_t launch_cell8_encode(const vbq_matrix& m, const uint16_t* r16, int8_t* f, hipStream_t s) {
+  const int G = m.n_cols / kGroup, RT = row_tiles(m.n_rows);
+  hipLaunchKernelGGL(k_cell8<true>, dim3((unsigned)m.n_tiles), dim3(64), 0, s, m.tiles,
+                     reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, G, RT, (const void*)r16, (void*)f);
+  return hipGetLastError();
+}
+
+hipError_t launch_cell8_decode(const vbq_matrix& m, const int8_t* f, uint16_t* r16, hipStream_t s) {
+  const int G = m.n_cols / kGroup, RT = row_tiles(m.n_rows);
+  hipLaunchKernelGGL(k_cell8<false>, dim3((unsigned)m.n_tiles), dim3(64), 0, s, m.tiles,
+                     reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, G, RT, (const void*)f, (void*)r16);
+  return hipGetLastError();
+}
+
 }  // namespace vbq

@@ -143,6 +143,7 @@ struct GemvMat {
   const uint8_t* stream;
   const uint16_t* x;       // [B][K] fp16
   const uint16_t* resid;   // [N][K] fp16 or null
+  const int8_t* cell;      // [N][K] compact in-cell residual fractions or null
   float* y;                // [B][N]
   int32_t n_rows;
   int32_t n_groups;        // K / 64
@@ -160,6 +161,8 @@ struct GemvMat {
 constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
 constexpr int kGemvWaves = 4;
 constexpr int kGemvMaxNb = 2;   // batch rows per pass
+// Residual kinds of a launch: none, fp16 per weight, int8 cell fractions.
+constexpr int kModePlain = 0, kModeResid16 = 1, kModeCell8 = 2;
 
 struct GemvLaunch {
   GemvMat mats[kMaxMats];
@@ -171,16 +174,18 @@ static_assert(sizeof(GemvLaunch) <= 4096, "kernel arguments are limited to 4 KiB
 
 // Host-side launch helpers.
 hipError_t launch_pack(const float* W, const uint8_t* widths, const vbq_matrix& m, hipStream_t s);
-hipError_t launch_gemv(const GemvLaunch& L, int nb, bool resid, int n_wg, hipStream_t s);
+hipError_t launch_gemv(const GemvLaunch& L, int nb, int mode, int n_wg, hipStream_t s);
 // The scratch of the split GEMV on the current device: partial row sums and
 // row-tile counters (sizes in elements).
 constexpr size_t kScratchPartials = 1u << 18;   // 1 MiB of float
 constexpr size_t kScratchCounters = 1u << 14;   // 64 KiB of uint32
 hipError_t gemv_scratch(float** partials, uint32_t** counters);
-size_t gemv_lds_bytes(int nb);
+size_t gemv_lds_bytes(int nb, int mode);
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s);
 hipError_t launch_residual_error(const vbq_matrix& m, const float* E_in, float* E_out, hipStream_t s);
+hipError_t launch_cell8_encode(const vbq_matrix& m, const uint16_t* r16, int8_t* f, hipStream_t s);
+hipError_t launch_cell8_decode(const vbq_matrix& m, const int8_t* f, uint16_t* r16, hipStream_t s);
 hipError_t launch_drift(const vbq_matrix& m, const uint16_t* x, int B, float* bound, hipStream_t s);
 hipError_t launch_gemm(const vbq_matrix& m, const uint16_t* x, int M, float* y, hipStream_t s);
 

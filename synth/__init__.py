@@ -30,7 +30,7 @@ GROUP = 64
 ROW_BLOCK = 1024
 
 # Stream ids inside a seed key.
-S_WIDTHS, S_WEIGHTS, S_X, S_RESID = 0, 1, 2, 3
+S_WIDTHS, S_WEIGHTS, S_X, S_RESID, S_CELL = 0, 1, 2, 3, 4
 
 # Bit-width mixes.
 MIX_DEFAULT = {1: 0.69, 2: 0.15, 4: 0.12, 8: 0.04}   # mean 1.79 bits
@@ -133,6 +133,16 @@ def cell_u(seed: int, key: tuple, n_rows: int, n_cols: int, half_width: float = 
         rng = np.random.default_rng(_ss(seed, key + (S_RESID, blk)))
         return rng.uniform(-half_width, half_width, size=(n, n_cols))
     return _fill_rows(n_rows, (n_cols,), np.float64, fill, rows)
+
+
+def cell_f(seed: int, key: tuple, n_rows: int, n_cols: int, rows=None) -> np.ndarray:
+    """Uniform integer draws in [-127, 127], int8 [n_rows][n_cols]: the
+    fraction bytes of a compact in-cell residual, drawn directly (any byte in
+    that range stands for a residual inside its cell, whatever the scale)."""
+    def fill(blk, n):
+        rng = np.random.default_rng(_ss(seed, key + (S_CELL, blk)))
+        return rng.integers(-127, 128, size=(n, n_cols), dtype=np.int8)
+    return _fill_rows(n_rows, (n_cols,), np.int8, fill, rows)
 
 
 # ---------------------------------------------------------------------------

@@ -737,6 +737,49 @@ def pin_cell8_inside_cell():
     assert (err <= sd / 512.0 * (1 + 1e-6)).all()
 
 
+def pin_cell8_decode_values():
+    """fp16(s f / 256), hand-worked: s = 0.5, f = 1 -> 2^-9 (0x1800);
+    s = 1, f = -127 -> -0.49609375 (0xB7F0, exact); s = 2047/2048 (0x3BFF),
+    f = 3 -> 6141 * 2^-19, 13 significant bits, rounded to 6140 * 2^-19
+    (0x21FF); s = 1027/1024 (0x3C03), f = 3 -> 3081 * 2^-18, a tie between
+    1540 and 1541 units of 2^-17, to even 1540 (0x2204); s = 2^-14 (0x0400),
+    f = 1 -> 2^-22, subnormal 4 * 2^-24 (0x0004); s = 0x0401, f = 5 ->
+    20.02 units of 2^-24, to 20 (0x0014); a zero scale gives +0 for f >= 0
+    and, as IEEE multiplication does, -0 (0x8000) for f < 0."""
+    cases = [(0x3800, 1, 0x1800), (0x3C00, -127, 0xB7F0), (0x3BFF, 3, 0x21FF), (0x3C03, 3, 0x2204),
+             (0x0400, 1, 0x0004), (0x0401, 5, 0x0014), (0x0000, 77, 0x0000), (0x0000, -5, 0x8000)]
+    f = np.zeros((len(cases), 64), np.int8)
+    s16 = np.zeros((len(cases), 1), np.uint16)
+    for i, (s, v, _) in enumerate(cases):
+        s16[i, 0] = s
+        f[i, :] = v
+    r16 = oracle.cell8_decode(f, s16)
+    for i, (_, _, want) in enumerate(cases):
+        assert (r16[i] == want).all(), (i, hex(int(r16[i, 0])), hex(want))
+
+
+def pin_cell8_decode_in_cell():
+    """Every fraction decodes to a residual the re-quantisation check passes
+    (inside its cell, codes come back unchanged), and encoding the decoded
+    residual gives the fraction back (r / s * 256 is within binary32 and fp16
+    rounding of f, far below half a step)."""
+    r = _rng(33)
+    N, K = 9, 192
+    G = K // 64
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, G))
+    q, s, o = oracle.quantize_matrix(W, widths)
+    f = r.integers(-127, 128, (N, K)).astype(np.int8)
+    f[0, :] = 127
+    f[1, :] = -127
+    r16 = oracle.cell8_decode(f, s)
+    mism, ooc, first, _ = oracle.requant_verify(q, s, o, widths, r16)
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    live = np.repeat(oracle.f64_from_f16(s), 64, axis=1) > 2.0 ** -14    # normal fp16 scales
+    back = oracle.cell8_encode(r16, s)
+    assert np.array_equal(back[live], f[live])
+
+
 def pin_abstract_storage_ratios():
     """The VBQ abstract's storage ratios follow from its mean bits when only
     code bits are counted (16 / mean bits per parameter), and do not when the
@@ -783,6 +826,7 @@ def pin_mean_bits_accounting():
 
 ALL_PINS = [
     pin_cell8_encode_values, pin_cell8_gemv_equals_fp16_residual, pin_cell8_inside_cell,
+    pin_cell8_decode_values, pin_cell8_decode_in_cell,
     pin_f16_conversion, pin_rtn_nearest_level, pin_rtn_scale_offset_nearest, pin_rtn_exact_grid,
     pin_rtn_degenerate_group, pin_canonical_lsb_first, pin_record_even_odd, pin_layout_k_tiles,
     pin_layout_worked_example, pin_layout_column_major, pin_layout_invariants,

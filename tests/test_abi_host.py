@@ -20,7 +20,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("vbq_pack", "vbq_gemv", "vbq_gemm", "cell_requant_verify", "cell_drift_bound", "vbq_pack_query",
-              "vbq_residual_error", "vbq_gemv_levels",
+              "vbq_residual_error", "vbq_gemv_levels", "vbq_gemv_batched_static", "vbq_gemv_cell8",
+              "cell8_encode", "cell8_decode",
               "vbq_gemv_batched", "vbq_matrix_check", "vbq_abi_version", "vbq_status_string"):
         assert n in names
 
@@ -102,6 +103,15 @@ def test_compute_calls_reject_bad_arguments_without_a_gpu():
     assert L.cell_drift_bound(C.byref(m), C.c_void_p(0x7F0000100001), 1, y, None) == 4
     assert L.cell_drift_bound(C.byref(m), x, 1, C.c_void_p(0x7F0000200002), None) == 4
     assert L.cell_drift_bound(C.byref(_fake_matrix(vbq, K=100)), x, 1, y, None) == 2
+    assert L.vbq_gemv_cell8(C.byref(m), x, 1, None, y, None) == 1           # the fractions are required
+    assert L.vbq_gemv_cell8(C.byref(m), x, 1, C.c_void_p(0x7F0000300008), y, None) == 4
+    assert L.vbq_gemv_cell8(C.byref(m), x, 9, C.c_void_p(0x7F0000300000), y, None) == 5
+    assert L.vbq_gemv_cell8(C.byref(_fake_matrix(vbq, K=100)), x, 1, C.c_void_p(0x7F0000300000), y, None) == 2
+    assert L.cell8_encode(C.byref(m), None, C.c_void_p(0x7F0000300000), None) == 1
+    assert L.cell8_encode(C.byref(m), x, None, None) == 1
+    assert L.cell8_encode(C.byref(m), x, C.c_void_p(0x7F0000300004), None) == 4
+    assert L.cell8_decode(C.byref(m), C.c_void_p(0x7F0000300000), C.c_void_p(0x7F0000100002), None) == 4
+    assert L.cell8_decode(None, C.c_void_p(0x7F0000300000), x, None) == 1
     assert L.vbq_residual_error(C.byref(m), None, y, None) == 1
     assert L.vbq_residual_error(C.byref(m), x, C.c_void_p(0x7F0000200004), None) == 4
     two = (vbq.vbq_matrix * 2)(m, _fake_matrix(vbq, N=48))
@@ -152,6 +162,12 @@ def test_binding_rejects_bad_tensors_before_any_launch():
         vbq.vbq_gemv(pm, torch.zeros(1, 128, dtype=torch.float16), residual=torch.zeros(32, 128))
     with pytest.raises(ValueError, match="out: shape"):
         vbq.vbq_gemv(pm, torch.zeros(2, 128, dtype=torch.float16), out=torch.zeros(1, 32))
+    with pytest.raises(ValueError, match="cell: dtype"):
+        vbq.vbq_gemv_cell8(pm, torch.zeros(1, 128, dtype=torch.float16), torch.zeros(32, 128, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="cell: shape"):
+        vbq.cell8_decode(pm, torch.zeros(32, 64, dtype=torch.int8))
+    with pytest.raises(ValueError, match="residual: dtype"):
+        vbq.cell8_encode(pm, torch.zeros(32, 128))
     with pytest.raises(ValueError, match="E: dtype"):
         vbq.vbq_residual_error(pm, torch.zeros(32, 128, dtype=torch.float16))
     with pytest.raises(ValueError, match="residual: shape"):

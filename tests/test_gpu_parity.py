@@ -64,7 +64,7 @@ def _field_bias(b):
     return 2.0 ** (10 - p)
 
 
-def gemv_bound(q, s16, o16, widths, x, resid=None):
+def gemv_bound(q, s16, o16, widths, x, resid=None, cell=None):
     """Worst-case rounding bound |y - y_exact| per output [B][N] of the
     library's fp32 GEMV, y = sum_g s_g (D_g - beta_g) + o_g X_g (+ residual):
       - D_g = sum (bias_k + q_k) x_k and beta_g = sum bias_k x_k are four
@@ -77,6 +77,12 @@ def gemv_bound(q, s16, o16, widths, x, resid=None):
         (G + 10) u C with C = sum_k |w_k||x_k|;
       - residual rows: four chains of eight dot2 and a 64-lane sum, 26 u R with
         R = sum_k |r_k||x_k|.
+      - compact in-cell residual f (int8): per group the dot D8 of the values
+        1152 + f_k with x, started from -1152 X_g (X_g itself within 20 u of
+        sum |x|), two chains of sixteen dot2, then times s/256 and added to
+        the record's slot: within u (s/256) (40 sum (2304 + f_k)|x_k| +
+        23040 sum |x_k|) per group; C then takes the full weight
+        s q + o + s f / 256.
     u = 2^-24."""
     N, K = q.shape
     G = K // 64
@@ -90,21 +96,28 @@ def gemv_bound(q, s16, o16, widths, x, resid=None):
     o_full = np.repeat(o, 64, axis=1)
     A = xd @ (s_full * (bias_full + q)).T
     Bo = xd @ np.abs(o_full).T
-    C = xd @ np.abs(s_full * q + o_full).T
+    w_full = s_full * q + o_full
+    if cell is not None:
+        fd = cell.astype(np.float64)
+        s256 = s_full / 256.0
+        w_full = w_full + s256 * fd
+    C = xd @ np.abs(w_full).T
     b = U * (40 * A + 20 * Bo + (G + 10) * C)
+    if cell is not None:
+        b = b + U * (40 * (xd @ (s256 * (2304.0 + fd)).T) + 23040 * (xd @ s256.T))
     if resid is not None:
         b = b + U * 26 * (xd @ np.abs(oracle.f64_from_f16(resid)).T)
     return b
 
 
-def check_gemv(y, q, s, o, widths, x, resid=None, tol=None):
+def check_gemv(y, q, s, o, widths, x, resid=None, tol=None, cell=None):
     """rel-L2 of the whole output and every output within its bound."""
-    ref = oracle.gemv(q, s, o, x, resid)
+    ref = oracle.gemv(q, s, o, x, resid) if cell is None else oracle.gemv_cell8(q, s, o, x, cell)
     y = np.asarray(y, np.float64)
     assert y.shape == ref.shape
     assert rel_l2(y, ref) <= (TOL if tol is None else tol)
     err = np.abs(y - ref)
-    bound = gemv_bound(q, s, o, widths, x, resid)
+    bound = gemv_bound(q, s, o, widths, x, resid, cell)
     worst = np.unravel_index(np.argmax(err - bound), err.shape)
     assert np.all(err <= bound), f"output {worst}: error {err[worst]:.3e} above its bound {bound[worst]:.3e}"
     return ref
@@ -379,6 +392,91 @@ def test_residual_gemv_and_revocation(vbq, shape):
     # a zero residual serves the base weights
     yz = vbq.vbq_gemv(pm, xt, residual=torch.zeros_like(rt)).cpu().numpy()
     assert np.allclose(yz, y0, rtol=1e-6, atol=1e-6)
+
+
+CELL_SHAPES = [(1, 64), (17, 320), (33, 4096), (70, 64 * 70), (20, 8192 + 192)]
+
+
+@pytest.mark.parametrize("shape", CELL_SHAPES, ids=[f"{n}x{k}" for n, k in CELL_SHAPES])
+def test_cell8_encode_decode_bit_exact(vbq, shape):
+    """Compact in-cell residual: the device encoder and decoder against the
+    oracle's, bit for bit, with the scales the packed matrix holds (mixed
+    widths, a zero-scale group, residuals inside, at the edge of and beyond
+    the representable range, ties of the rounding)."""
+    import torch
+    N, K = shape
+    W, widths, _ = rand_case(N, K, seed=3 * N + K)
+    if N > 2:
+        W[N // 2, :64] = 0.015                  # constant group: scale 0
+    if N > 1:
+        # row 1: every group spans (2^b - 1) / 16, so its scale is 1/16
+        for g in range(K // 64):
+            L = (1 << int(widths[1, g])) - 1
+            W[1, 64 * g:64 * g + 64] = np.where(np.arange(64) % 2 == 0, 0.0, L / 16.0)
+    print(f"case cell8 encode/decode {N}x{K}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    r = np.random.default_rng(N + 5 * K)
+    sd = np.repeat(oracle.f64_from_f16(s), 64, axis=1)
+    r16 = oracle.f16_from_f64(r.uniform(-0.8, 0.8, (N, K)) * sd)
+    r16[::2] = oracle.f16_from_f64(r.standard_normal((N, K)) * 0.01)[::2]
+    if N > 1:
+        # half steps of the fraction at an exact scale: r / s * 256 is a tie
+        assert (s[1] == 0x2C00).all()
+        t = r.integers(-100, 100, K) + 0.5
+        r16[1] = oracle.f16_from_f64(t / 256.0 / 16.0)
+        assert np.array_equal(oracle.f64_from_f16(r16[1]), t / 4096.0)
+    f_gpu = vbq.cell8_encode(pm, _t(r16, torch.float16)).cpu().numpy()
+    f_ref = oracle.cell8_encode(r16, s)
+    if not np.array_equal(f_gpu, f_ref):
+        bad = np.argwhere(f_gpu != f_ref)
+        raise AssertionError(f"{len(bad)} fractions differ, first at {bad[:3].tolist()}")
+    fr = r.integers(-127, 128, (N, K)).astype(np.int8)
+    fr[0, :64] = -127
+    d_gpu = vbq.cell8_decode(pm, _t(fr)).cpu().numpy().view(np.uint16)
+    assert np.array_equal(d_gpu, oracle.cell8_decode(fr, s))
+
+
+CELL_GEMV = [(1, 64, 1), (17, 320, 2), (33, 4096, 1), (100, 448, 3), (70, 64 * 70, 1), (20, 8192 + 192, 4),
+             (64, 256, 8)]
+
+
+@pytest.mark.parametrize("case", CELL_GEMV, ids=[f"{n}x{k}b{b}" for n, k, b in CELL_GEMV])
+def test_cell8_gemv_parity(vbq, case):
+    """GEMV with the compact in-cell residual against the oracle (every
+    output within its bound), repeatable bit for bit, each batch row equal to
+    its batch-1 call; the update moves no output further than the drift
+    bound, and the base GEMV (the update revoked) is untouched."""
+    import torch
+    N, K, B = case
+    W, widths, x = rand_case(N, K, seed=11 * N + K + B, B=B)
+    if N > 2:
+        W[N // 2, 64:128 if K > 64 else 64] = -0.01
+    print(f"case cell8 gemv {N}x{K} B={B}", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    r = np.random.default_rng(N * K + B)
+    f = r.integers(-127, 128, (N, K)).astype(np.int8)
+    f[0] = 127
+    if N > 1:
+        f[1] = -127
+    xt = _t(x, torch.float16)
+    ft = _t(f)
+    y0 = vbq.vbq_gemv(pm, xt)
+    yt = vbq.vbq_gemv_cell8(pm, xt, ft)
+    y = yt.cpu().numpy()
+    check_gemv(y, q, s, o, widths, x, cell=f)
+    assert torch.equal(vbq.vbq_gemv_cell8(pm, xt, ft), yt)
+    for b in range(B):
+        assert torch.equal(vbq.vbq_gemv_cell8(pm, xt[b:b + 1].contiguous(), ft)[0], yt[b])
+    bound = vbq.cell_drift_bound(pm, xt).cpu().numpy()
+    s_full = oracle.f64_from_f16(np.repeat(s, 64, axis=1))
+    xd = oracle.f64_from_f16(x)
+    wdq = s_full * q + oracle.f64_from_f16(np.repeat(o, 64, axis=1))
+    slack = 1e-5 * (np.abs(xd) @ (np.abs(wdq) + s_full).T)
+    base = y0.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(y - base) <= bound + slack)
+    assert torch.equal(vbq.vbq_gemv(pm, xt), y0)
 
 
 def _verify_both(vbq, pm, resid_t):
@@ -711,6 +809,33 @@ def test_workload_in_cell_full_size(vbq):
     assert torch.equal(rq, pm.stream)
     ref_v = oracle.requant_verify(q[rows], s[rows], o[rows], widths[rows], resid[rows])
     assert ref_v[:2] == (0, 0)
+
+
+def test_workload_in_cell_compact_full_size(vbq):
+    """The same 4-bit 14336 x 4096 release with the compact in-cell residual:
+    the in-cell fp16 residual encoded on the device equals the oracle's
+    encoding over the whole matrix, the fractions decode bit-exactly, and the
+    GEMV with random fractions matches the oracle on sampled rows."""
+    import torch
+    proj = synth.C2.projs[0]
+    key = synth.proj_key(2, 0, 0)
+    N, K = proj.n, proj.k
+    widths = synth.widths(synth.SEED, key, N, K // 64, proj.mix)
+    W = synth.weights(synth.SEED, key, N, K)
+    x = synth.x_f16(synth.SEED, key, 1, K)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    resid = oracle.make_cell_residual(synth.cell_u(synth.SEED, key, N, K), s)
+    print("case workload 2 compact in-cell 14336x4096", flush=True)
+    pm = vbq.vbq_pack(_t(W), widths)
+    f_gpu = vbq.cell8_encode(pm, _t(resid, torch.float16)).cpu().numpy()
+    assert np.array_equal(f_gpu, oracle.cell8_encode(resid, s))
+    f = synth.cell_f(synth.SEED, key, N, K)
+    ft = _t(f)
+    r16 = vbq.cell8_decode(pm, ft).cpu().numpy().view(np.uint16)
+    assert np.array_equal(r16, oracle.cell8_decode(f, s))
+    y = vbq.vbq_gemv_cell8(pm, _t(x, torch.float16), ft).cpu().numpy()
+    rows = _sample_rows(N, np.random.default_rng(3))
+    check_gemv(y[:, rows], q[rows], s[rows], o[rows], widths[rows], x, cell=f[rows])
 
 
 def test_workload_9b_layer_one_launch_sampled(vbq):

@@ -29,6 +29,7 @@ MUTATIONS = {
     8: "records of a class listed row-major instead of column-major",
     13: "compact in-cell fraction counted in 1/128 of the scale instead of 1/256",
     14: "compact in-cell encoding truncates instead of rounding to nearest",
+    15: "compact in-cell decoding divides by 255 instead of 256",
     9: "record halves swapped",
     10: "bfloat16 rounding breaks ties away from zero",
     11: "re-quantisation drops the clamp to [0, L]",
