@@ -59,70 +59,74 @@ def algorithmic_bytes(sizes, N, K, B, resid=False):
 
 
 class Stack:
-    """Packed matrices of the 9B-class stack, their x and y buffers, and plans."""
+    """Packed matrices of the 9B-class stack, their x and y buffers, and plans.
+    The step's launches are vbq_gemv_batched_static calls (every k-tile of
+    the 14336-wide down projection gets a workgroup); `batched_plans` holds
+    the same launches through vbq_gemv_batched. With recipe=True the same
+    weights are also packed with the structured recipe's widths
+    (`recipe_plans`)."""
 
-    def __init__(self, layers: int, B: int):
+    def __init__(self, layers: int, B: int, recipe: bool = False):
         import torch
 
         import packed_decode_gemv_amd as vbq
         import synth
         self.vbq = vbq
         self.layers, self.B = layers, B
-        self.plans, self.launch_bytes, self.launch_names = [], [], []
+        self.plans, self.batched_plans, self.launch_bytes, self.launch_names = [], [], [], []
+        self.recipe_plans, self.recipe_bytes, self.recipe_mats = [], [], {}
         self.mats = {}
         t0 = time.time()
         dev = torch.device("cuda")
         wl = synth.C3
-        for layer in range(layers):
-            pms, xs, ys = [], [], []
-            nbytes = 0.0
-            for pi, proj in enumerate(wl.projs):
-                pm, x, y, nb = self._make(3, layer, pi, proj, B, dev)
+        for layer in range(layers + 1):
+            projs = [wl.head] if layer == layers else wl.projs
+            lid = -1 if layer == layers else layer
+            pms, xs, ys, rpms, rys = [], [], [], [], []
+            nbytes, rbytes = 0.0, 0.0
+            for pi, proj in enumerate(projs):
+                key = synth.proj_key(3, lid, pi)
+                W = torch.from_numpy(synth.weights(synth.SEED, key, proj.n, proj.k)).to(dev)
+                pm = vbq.vbq_pack(W, synth.widths(synth.SEED, key, proj.n, proj.k // 64, proj.mix), check=False)
+                x = torch.from_numpy(synth.x_f16(synth.SEED, key, B, proj.k).view(np.float16)).to(dev)
+                y = torch.empty(B, proj.n, dtype=torch.float32, device=dev)
                 pms.append(pm)
                 xs.append(x)
                 ys.append(y)
-                nbytes += nb
-                self.mats[(layer, pi)] = (pm, x, y)
-            self.plans.append(vbq.GemvPlan(pms, xs, ys))
+                nbytes += algorithmic_bytes(pm.sizes, proj.n, proj.k, B)
+                self.mats[(lid, pi)] = (pm, x, y)
+                if recipe:
+                    rpm = vbq.vbq_pack(W, synth.recipe_widths(lid, pi, proj, layers), check=False)
+                    ry = torch.empty(B, proj.n, dtype=torch.float32, device=dev)
+                    rpms.append(rpm)
+                    rys.append(ry)
+                    rbytes += algorithmic_bytes(rpm.sizes, proj.n, proj.k, B)
+                    self.recipe_mats[(lid, pi)] = (rpm, x, ry)
+                del W
+            self.plans.append(vbq.GemvPlan(pms, xs, ys, static=True))
+            self.batched_plans.append(vbq.GemvPlan(pms, xs, ys))
             self.launch_bytes.append(nbytes)
-            self.launch_names.append(f"layer{layer}")
+            self.launch_names.append("lm_head" if lid < 0 else f"layer{layer}")
+            if recipe:
+                self.recipe_plans.append(vbq.GemvPlan(rpms, xs, rys, static=True))
+                self.recipe_bytes.append(rbytes)
             if layer % 8 == 7:
                 log(f"  packed {layer + 1}/{layers} layers ({time.time() - t0:.0f} s)")
-        pm, x, y, nb = self._make(3, -1, 0, wl.head, B, dev)
-        self.mats[(-1, 0)] = (pm, x, y)
-        self.plans.append(vbq.GemvPlan([pm], [x], [y]))
-        self.launch_bytes.append(nb)
-        self.launch_names.append("lm_head")
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
         self.weight_bytes = sum(pm.nbytes for (pm, _, _) in self.mats.values())
         self.weights = sum(pm.N * pm.K for (pm, _, _) in self.mats.values())
         self.code_bits = sum(pm.sizes.code_bits for (pm, _, _) in self.mats.values())
 
-    def _make(self, cid, layer, pi, proj, B, dev):
-        import torch
-
-        import synth
-        key = synth.proj_key(cid, layer, pi)
-        G = proj.k // 64
-        widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix)
-        W = torch.from_numpy(synth.weights(synth.SEED, key, proj.n, proj.k)).to(dev)
-        pm = self.vbq.vbq_pack(W, widths, check=False)
-        del W
-        x = torch.from_numpy(synth.x_f16(synth.SEED, key, B, proj.k).view(np.float16)).to(dev)
-        y = torch.empty(B, proj.n, dtype=torch.float32, device=dev)
-        nb = algorithmic_bytes(pm.sizes, proj.n, proj.k, B)
-        return pm, x, y, nb
-
     def check_packed(self):
         import ctypes as C
-        for (pm, _, _) in self.mats.values():
+        for (pm, _, _) in list(self.mats.values()) + list(self.recipe_mats.values()):
             st = self.vbq.lib.vbq_matrix_check(C.byref(pm.desc), self.vbq._stream())
             if st != 0:
                 raise RuntimeError(f"packed layout check failed: status {st}")
 
-    def step(self, stream_handle):
-        for p in self.plans:
+    def step(self, stream_handle, plans=None):
+        for p in (self.plans if plans is None else plans):
             p.launch(stream_handle)
 
 
@@ -175,18 +179,21 @@ def time_graph(g, reps, warmup=2):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def time_steps_graph(stack, steps, warmup):
-    """One step (all launches) captured as a HIP graph, warmed up, then exactly
-    `steps` replays timed with HIP events. Returns (ms per step, graph). The
-    replayed outputs are checked bit for bit against an eager step."""
+def time_steps_graph(stack, steps, warmup, plans=None, mats=None):
+    """One step (all launches of `plans`, default the headline's) captured as
+    a HIP graph, warmed up, then exactly `steps` replays timed with HIP
+    events. Returns (ms per step, graph). The replayed outputs (of `mats`)
+    are checked bit for bit against an eager step."""
     import torch
     vbq = stack.vbq
-    stack.step(vbq._stream())   # an eager step, the reference for the replays
+    mats = list((stack.mats if mats is None else mats).values())
+    stack.step(vbq._stream(), plans)   # an eager step, the reference for the replays
     torch.cuda.synchronize()
-    eager = [y.clone() for (_, _, y) in list(stack.mats.values())[:8]]
-    g = capture(lambda i: stack.step(vbq._stream()), 1)
+    watch = mats[:8] + mats[-1:]
+    eager = [y.clone() for (_, _, y) in watch]
+    g = capture(lambda i: stack.step(vbq._stream(), plans), 1)
     us = time_graph(g, steps, warmup)
-    for (_, _, y), ref in zip(list(stack.mats.values())[:8], eager):
+    for (_, _, y), ref in zip(watch, eager):
         if not torch.equal(y, ref):
             raise RuntimeError("graph replay differs from the eager step")
     return us / 1e3, g
@@ -552,7 +559,7 @@ def measure_workloads(stack, calls):
             xs.append(xf16(synth.proj_key(3, layer, pi), B, p.k))
             ys.append(torch.empty(B, p.n, dtype=torch.float32, device=dev))
             nb += algorithmic_bytes(pmx.sizes, p.n, p.k, B)
-        plans.append(vbq.GemvPlan(pms, xs, ys))
+        plans.append(vbq.GemvPlan(pms, xs, ys, static=True))
     pmh = stack.mats[(-1, 0)][0]
     hx = xf16(synth.proj_key(3, -1, 0), B, synth.C3.head.k)
     plans.append(vbq.GemvPlan([pmh], [hx], [torch.empty(B, synth.C3.head.n, dtype=torch.float32, device=dev)]))
@@ -567,30 +574,44 @@ def measure_workloads(stack, calls):
                           {"us_per_layer": round((us) / (stack.layers + 1), 3)}))
     del plans
 
-    # In-cell update: 4-bit release 14336 x 4096 with an fp16 residual inside
-    # each cell (r = u * scale, u ~ U(-0.49, 0.49)), GEMV and re-quantisation check
+    # In-cell update on a 4-bit release 14336 x 4096. The update is drawn as
+    # compact fraction bytes f (uniform in [-127, 127]); the fp16 residual
+    # r = fp16(s f / 256) is decoded on the device from the packed scales, so
+    # both residual forms stand for the same in-cell update.
     proj = synth.C2.projs[0]
     pm, W, key = packed(2, 0, 0, proj)
+    del W
     N, K = proj.n, proj.k
-    Wg = W.view(N, K // 64, 64)
-    s_grp = ((Wg.amax(-1) - Wg.amin(-1)) / 15.0).half().float()
-    u = torch.from_numpy(synth.cell_u(synth.SEED, key, N, K)).to(dev)
-    resid = (u.view(N, K // 64, 64) * s_grp.double().unsqueeze(-1)).half().view(N, K)
-    del u, Wg, W
+    f8 = torch.from_numpy(synth.cell_f(synth.SEED, key, N, K)).to(dev)
+    resid = vbq.cell8_decode(pm, f8)
     x = xf16(key, 1, K)
     y = torch.empty(1, N, dtype=torch.float32, device=dev)
     rbytes = resid.numel() * 2
-    n_copies = max(1, POOL_BYTES // (pm.nbytes + rbytes))
-    pool = [(pm, resid)] + [(pm.clone(), resid.clone()) for _ in range(n_copies - 1)]
+    n_copies = max(1, POOL_BYTES // (pm.nbytes + rbytes + f8.numel()))
+    pool = [(pm, resid, f8)] + [(pm.clone(), resid.clone(), f8.clone()) for _ in range(n_copies - 1)]
     us = _events_time(lambda i: vbq.vbq_gemv(pool[i % len(pool)][0], x, residual=pool[i % len(pool)][1], out=y),
                       calls)
     nb = algorithmic_bytes(pm.sizes, N, K, 1, resid=True)
     out.append(_gemv_line(f"in-cell update {N}x{K} (all 4-bit) + fp16 residual, residual GEMV, batch 1", us, nb))
+    # the same update as one signed byte per weight (vbq_gemv_cell8)
+    us = _events_time(lambda i: vbq.vbq_gemv_cell8(pool[i % len(pool)][0], x, pool[i % len(pool)][2], out=y),
+                      calls)
+    nb8 = algorithmic_bytes(pm.sizes, N, K, 1) + N * K
+    out.append(_gemv_line(f"in-cell update {N}x{K} (all 4-bit) + compact residual (int8 cell fraction), "
+                          "residual GEMV, batch 1", us, nb8))
+    # encoding an fp16 residual into fraction bytes: reads r (2 B/weight), the
+    # scale of every group and the width map, writes f (1 B/weight)
+    f_out = torch.empty_like(f8)
+    us = _events_time(lambda i: vbq.cell8_encode(pool[i % len(pool)][0], pool[i % len(pool)][1], out=f_out), calls)
+    groups = N * (K // 64)
+    nbe = 3.0 * N * K + 4 * groups + groups / 4
+    out.append(_gemv_line(f"in-cell update {N}x{K}: encoding the fp16 residual to fraction bytes (cell8_encode)",
+                          us, nbe, {"matches_drawn_bytes": bool(torch.equal(f_out, pool[(calls - 1) % len(pool)][2]))}))
     res = torch.empty(3, dtype=torch.int64, device=dev)
     import ctypes as C
 
     def verify(i):
-        pmv, rv = pool[i % len(pool)]
+        pmv, rv, _ = pool[i % len(pool)]
         st = vbq.lib.cell_requant_verify(C.byref(pmv.desc), C.c_void_p(rv.data_ptr()), C.c_void_p(res.data_ptr()),
                                          None, vbq._stream())
         if st != 0:
@@ -624,6 +645,39 @@ def measure_workloads(stack, calls):
 
     out.append(gemm_workload(vbq, calls))
     return out
+
+
+def recipe_line(stack, steps, warmup):
+    """The 9B-class stack with the structured recipe's widths (same weights
+    and activations): one step replayed as a HIP graph, plus the spread of
+    its per-launch times (event pairs around each launch)."""
+    import torch
+    ms, _ = time_steps_graph(stack, steps, warmup, plans=stack.recipe_plans, mats=stack.recipe_mats)
+    nb = float(sum(stack.recipe_bytes))
+    sh = stack.vbq._stream()
+    reps = 5
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in stack.recipe_plans] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for i, p in enumerate(stack.recipe_plans):
+            evs[r][i][0].record()
+            p.launch(sh)
+            evs[r][i][1].record()
+    torch.cuda.synchronize()
+    d = np.array([[a.elapsed_time(b) * 1e3 for (a, b) in row] for row in evs]).mean(axis=0)
+    per_layer = [nbl / (t * 1e-6) / 1e9 for nbl, t in zip(stack.recipe_bytes[:-1], d[:-1])]
+    mats = stack.recipe_mats.values()
+    weights = sum(pm.N * pm.K for (pm, _, _) in mats)
+    code_bits = sum(pm.sizes.code_bits for (pm, _, _) in mats)
+    return _gemv_line(
+        f"9B-class stack ({stack.layers} layers + LM head), structured recipe: first MLP block 2.5 bits, "
+        f"SLQ-style per-layer mixes (ends widest), LM head 1.1 bits, wide groups on hot rows and input "
+        f"channels; batch {stack.B}, one step", ms * 1e3, nb,
+        {"mean_code_bits": round(code_bits / weights, 4),
+         "layer0_us": round(float(d[0]), 3), "layer15_us": round(float(d[15]), 3) if len(d) > 16 else None,
+         "lm_head_us": round(float(d[-1]), 3),
+         "layer_gb_per_s_min": round(min(per_layer), 1), "layer_gb_per_s_max": round(max(per_layer), 1)})
 
 
 def gemm_workload(vbq, calls):
@@ -786,13 +840,15 @@ def main(argv=None):
         print(json.dumps(gemm_workload(vbq, args.workload_calls)), flush=True)
         return 0
     log(f"building the 9B-class stack: {args.layers} layers + LM head, batch {args.batch}")
-    stack = Stack(args.layers, args.batch)
+    stack = Stack(args.layers, args.batch, recipe=not args.no_workloads)
     stack.check_packed()
     log(f"  setup {stack.setup_s:.1f} s, packed weights {stack.weight_bytes / 1e9:.3f} GB")
 
     ms_eager = time_steps(stack, args.steps, args.warmup)
     ms, _ = time_steps_graph(stack, args.steps, args.warmup)
-    log(f"  eager launches {ms_eager * 1e3:.1f} us/step, graph replay {ms * 1e3:.1f} us/step")
+    ms_batched, _ = time_steps_graph(stack, args.steps, args.warmup, plans=stack.batched_plans)
+    log(f"  eager launches {ms_eager * 1e3:.1f} us/step, graph replay {ms * 1e3:.1f} us/step "
+        f"(vbq_gemv_batched launches: {ms_batched * 1e3:.1f} us/step)")
     n_launch = len(stack.plans)
     step_bytes = float(sum(stack.launch_bytes))
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -813,8 +869,10 @@ def main(argv=None):
 
     workloads = None
     if not args.no_workloads:
+        log("structured recipe stack")
+        workloads = [recipe_line(stack, args.steps, args.warmup)]
         log("other workloads")
-        workloads = measure_workloads(stack, args.workload_calls)
+        workloads += measure_workloads(stack, args.workload_calls)
         for w in workloads:
             log(f"  {w['workload']}: {w['us_per_call']:.2f} us, frac {w['roofline_frac']:.3f}")
 
@@ -836,6 +894,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager_launches": round(ms_eager, 4),
+        "ms_per_step_vbq_gemv_batched": round(ms_batched, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -846,8 +905,9 @@ def main(argv=None):
             "batch": args.batch,
             "layers": args.layers,
             "launches_per_step": n_launch,
-            "launch": "one vbq_gemv_batched launch per layer (its 7 projections) + one for the LM head; "
-                      "a step's launches replayed as one HIP graph",
+            "launch": "one vbq_gemv_batched_static launch per layer (its 7 projections; every k-tile of the "
+                      "down projection a workgroup of its own) + one for the LM head; a step's launches "
+                      "replayed as one HIP graph",
             "algorithmic_bytes_per_step": step_bytes,
             "packed_bytes_resident": stack.weight_bytes,
             "weights": stack.weights,

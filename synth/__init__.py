@@ -30,12 +30,14 @@ GROUP = 64
 ROW_BLOCK = 1024
 
 # Stream ids inside a seed key.
-S_WIDTHS, S_WEIGHTS, S_X, S_RESID, S_CELL = 0, 1, 2, 3, 4
+S_WIDTHS, S_WEIGHTS, S_X, S_RESID, S_CELL, S_SALIENCE = 0, 1, 2, 3, 4, 5
 
 # Bit-width mixes.
 MIX_DEFAULT = {1: 0.69, 2: 0.15, 4: 0.12, 8: 0.04}   # mean 1.79 bits
 MIX_LM_HEAD = {1: 0.92, 2: 0.07, 4: 0.01}            # mean 1.10 bits
 MIX_UNIFORM4 = {4: 1.0}
+# First MLP block of a structured recipe: mean 2.52 bits.
+MIX_FIRST_MLP = {1: 0.40, 2: 0.30, 4: 0.22, 8: 0.08}
 
 
 def _ss(seed: int, key: tuple) -> np.random.SeedSequence:
@@ -95,6 +97,70 @@ def widths(seed: int, key: tuple, n_rows: int, n_groups: int, mix: dict, rows=No
         u = rng.random((n, n_groups))
         return vals[np.searchsorted(cum, u, side="right").clip(0, len(vals) - 1)]
     return _fill_rows(n_rows, (n_groups,), np.uint8, fill, rows)
+
+
+def structured_widths(seed: int, key: tuple, n_rows: int, n_groups: int, mix: dict, rows=None,
+                      row_scale: float = 1.0, col_scale: float = 0.7) -> np.ndarray:
+    """Per-group bit-widths with the fractions of ``mix`` but placed by a
+    salience score, so that wide groups gather on hot rows and hot input
+    channels as a learned allocation's do (the VBQ abstract reports the
+    allocation as strongly heterogeneous within projection types). Each group
+    (n, g) scores z = a_n + c_g + e_ng with a_n ~ row_scale * t_3 per row,
+    c_g ~ col_scale * t_3 per k-group (shared by all rows) and e ~ N(0, 1);
+    the groups are ranked by z over the whole matrix and the lowest share
+    mix[1] of the ranks get the narrowest width, the next share the next
+    width, and so on (each width's count is its share of the groups, up to
+    rounding). Returns uint8 [n_rows][n_groups] (only ``rows`` if given;
+    the ranking always spans the whole matrix)."""
+    vals = np.array(sorted(mix), dtype=np.uint8)
+    shares = np.array([mix[v] for v in sorted(mix)], np.float64)
+    cg = np.random.default_rng(_ss(seed, key + (S_SALIENCE, 1 << 30))).standard_t(3, n_groups) * col_scale
+
+    def fill(blk, n):
+        rng = np.random.default_rng(_ss(seed, key + (S_SALIENCE, blk)))
+        a = rng.standard_t(3, (n, 1)) * row_scale
+        return (a + cg[None, :] + rng.standard_normal((n, n_groups))).astype(np.float32)
+    z = _fill_rows(n_rows, (n_groups,), np.float32, fill)
+    order = np.argsort(z, axis=None, kind="stable")
+    counts = np.floor(np.cumsum(shares) / shares.sum() * z.size + 0.5).astype(np.int64)
+    flat = np.empty(z.size, np.uint8)
+    start = 0
+    for v, end in zip(vals, counts):
+        flat[order[start:end]] = v
+        start = end
+    w = flat.reshape(n_rows, n_groups)
+    return w if rows is None else w[np.asarray(rows, dtype=np.int64)]
+
+
+def layer_mix(layer: int, n_layers: int) -> dict:
+    """Per-layer width mix of a structured recipe, in the spirit of the SLQ
+    abstract's layer-wise non-uniform widths: the share of 1-bit groups is
+    0.72 - 0.25 * 2^-d with d the layer's distance to the nearer end of the
+    stack (so the first and last layers are the widest), and the rest is
+    split 15 : 12 : 4 over 2, 4 and 8 bits as in MIX_DEFAULT. Over 32 layers
+    about 69% of the groups are 1-bit."""
+    d = min(layer, n_layers - 1 - layer)
+    p1 = 0.72 - 0.25 * 2.0 ** (-d)
+    rest = 1.0 - p1
+    return {1: p1, 2: rest * 15 / 31, 4: rest * 12 / 31, 8: rest * 4 / 31}
+
+
+def recipe_mix(layer: int, proj_name: str, n_layers: int) -> dict:
+    """Mix of one matrix of the structured 9B-class recipe: the LM head
+    (layer -1) at MIX_LM_HEAD, the first MLP block (layer 0 gate, up, down)
+    at MIX_FIRST_MLP, everything else at its layer's layer_mix."""
+    if layer < 0:
+        return MIX_LM_HEAD
+    if layer == 0 and proj_name in ("gate", "up", "down"):
+        return MIX_FIRST_MLP
+    return layer_mix(layer, n_layers)
+
+
+def recipe_widths(layer: int, pi: int, proj, n_layers: int, rows=None) -> np.ndarray:
+    """Widths of matrix (layer, pi) of the structured 9B-class recipe; the
+    weights and activations of that matrix are those of workload 3."""
+    return structured_widths(SEED, proj_key(5, layer, pi), proj.n, proj.k // GROUP,
+                             recipe_mix(layer, proj.name, n_layers), rows=rows)
 
 
 def weights(seed: int, key: tuple, n_rows: int, n_cols: int, std: float = 0.02, rows=None) -> np.ndarray:

@@ -741,11 +741,14 @@ def _sample_rows(N, r, n=96):
     return np.array(sorted(rows), np.int64)
 
 
-def _check_proj(vbq, cid, layer, pi, proj, B, full=False):
+def _check_proj(vbq, cid, layer, pi, proj, B, full=False, recipe=False):
     import torch
     key = synth.proj_key(cid, layer, pi)
     G = proj.k // 64
-    widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix)
+    if recipe:
+        widths = synth.recipe_widths(layer, pi, proj, synth.C3.layers)
+    else:
+        widths = synth.widths(synth.SEED, key, proj.n, G, proj.mix)
     W = synth.weights(synth.SEED, key, proj.n, proj.k)
     x = synth.x_f16(synth.SEED, key, B, proj.k)
     print(f"case workload {cid} layer {layer} {proj.name} {proj.n}x{proj.k} B={B}", flush=True)
@@ -783,6 +786,46 @@ def test_workload_9b_lm_head_sampled(vbq):
 def test_workload_9b_layer_batch4_sampled(vbq):
     for pi in (0, 4, 6):
         _check_proj(vbq, 3, 5, pi, synth.C3.projs[pi], 4)
+
+
+RECIPE_CASES = [(0, 0), (0, 4), (0, 6), (1, 2), (15, 5), (31, 6), (-1, 0)]
+
+
+@pytest.mark.parametrize("case", RECIPE_CASES, ids=[f"L{l}p{p}" for l, p in RECIPE_CASES])
+def test_workload_9b_recipe_sampled(vbq, case):
+    """Matrices of the 9B-class stack under the structured recipe (first MLP
+    block at 2.5 bits, SLQ-style per-layer mixes, LM head at 1.1 bits, wide
+    groups gathered on hot rows and input channels): sampled rows against
+    the oracle and the layout read back, at full shape."""
+    layer, pi = case
+    proj = synth.C3.head if layer < 0 else synth.C3.projs[pi]
+    _check_proj(vbq, 3, layer, pi, proj, 1, recipe=True)
+
+
+def test_workload_9b_recipe_layer_one_launch(vbq):
+    """Layer 0 of the structured recipe (its MLP at 2.5 bits) as one launch of
+    both batched entry points: the outputs equal single calls bit for bit,
+    and sampled rows match the oracle."""
+    import torch
+    pms, xs, cases = [], [], []
+    for pi, proj in enumerate(synth.C3.projs):
+        key = synth.proj_key(3, 0, pi)
+        widths = synth.recipe_widths(0, pi, proj, synth.C3.layers)
+        W = synth.weights(synth.SEED, key, proj.n, proj.k)
+        x = synth.x_f16(synth.SEED, key, 1, proj.k)
+        print(f"case 9b recipe layer 0 launch: {proj.name} {proj.n}x{proj.k}", flush=True)
+        pms.append(vbq.vbq_pack(_t(W), widths))
+        xs.append(_t(x, torch.float16))
+        rows = _sample_rows(proj.n, np.random.default_rng(900 + pi), n=48)
+        cases.append((rows, W[rows], widths[rows], x))
+    ys = vbq.vbq_gemv_batched(pms, xs)
+    ys_static = vbq.vbq_gemv_batched(pms, xs, static=True)
+    torch.cuda.synchronize()
+    for pm, x_t, y, ys_, (rows, Wr, wr, x) in zip(pms, xs, ys, ys_static, cases):
+        q, s, o = oracle.quantize_matrix(Wr, wr)
+        check_gemv(y.cpu().numpy()[:, rows], q, s, o, wr, x)
+        assert torch.equal(y, vbq.vbq_gemv(pm, x_t))
+        assert torch.equal(ys_, y)
 
 
 def test_workload_in_cell_full_size(vbq):
