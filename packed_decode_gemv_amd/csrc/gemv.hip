@@ -181,12 +181,16 @@ __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB
 //     fixed order and clears them.
 constexpr int kSlotPitch = 33;                            // slot (column l, row r) at l * 33 + r; 32 is spare
 constexpr int kSlotWords = kWave * kSlotPitch;            // 2112 per batch row
-constexpr int kXWords = kTileGroups * 32;                 // 64 columns x 64 fp16, 128 bytes apart
+// Activations of a tile's 64 columns: 64 fp16 per column, 144 bytes apart
+// (128 bytes and a 16-byte gap), so that the 16-byte reads of lanes on
+// different columns fall on different LDS banks.
+constexpr int kXPitch = 36;                               // words per column
+constexpr int kXWords = kTileGroups * kXPitch;
 constexpr int kMaxRecs = kTileRows * kTileGroups;         // 2048 table entries of 16 bits
 
 template <int NB>
 struct LdsMap {
-  static constexpr int x = 0;                             // [NB][64][32] fp16 pairs
+  static constexpr int x = 0;                             // [NB][64][36] fp16 pairs (32 used)
   static constexpr int xsum = x + NB * kXWords;           // [NB][64]
   static constexpr int bias = xsum + NB * kWave;          // [NB][4][64]
   static constexpr int table = bias + NB * 4 * kWave;     // [2048] u16: column << 5 | row
@@ -319,7 +323,7 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t xr[1][32];
-      const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * 32u;
+      const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * (uint32_t)kXPitch;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
@@ -365,7 +369,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
   if (CELL) reinterpret_cast<float*>(S + LdsMap<NB>::sc)[col * kSlotPitch + row] = s;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + col * 32u;
+    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + col * (uint32_t)kXPitch;
     const float xsum = reinterpret_cast<const float*>(S + LdsMap<NB>::xsum)[nb * kWave + col];
     const float bias = reinterpret_cast<const float*>(S + LdsMap<NB>::bias)[(nb * 4 + C) * kWave + col];
     float a[1][2] = {{-bias, 0.f}};
@@ -492,7 +496,7 @@ __device__ inline void cell_dots(const CellRows& c, CellFlight<NB>& f, uint32_t*
   float base[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * 32u;
+    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * (uint32_t)kXPitch;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
@@ -560,17 +564,25 @@ template <int NB>
 __device__ inline void tile_start(const GemvMat& T, const TileRef& t, uint32_t* S, int wave, Flight<0, NB>& f0,
                                   Flight<1, NB>& f1, Flight<2, NB>& f2, Flight<3, NB>& f3, uint32_t lane) {
   if (wave == 0) {
-    // activations of columns 8 i + (lane >> 3), 16 bytes (lane & 7) each, to
-    // x + 128 column + 16 (lane & 7); past the matrix's last group the loads
-    // return zeros
+    // activations: copy i writes LDS chunk m = 64 i + lane, i.e. chunk m % 9
+    // of column m / 9 (144 bytes per column); chunks 0-7 of a column are its
+    // 128 bytes of x, chunk 8 is the gap and loads from outside the buffer
+    // (zeros), as do columns past the matrix's last group
     const size_t K = (size_t)T.n_groups * kGroup;
-    const uint32_t voff = (uint32_t)t.g0 * 128u + lane * 16u;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
       const uint32_t lds = lds_addr(S + LdsMap<NB>::x + nb * kXWords);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(xrs, lds + 1024u * i, voff + 1024u * i);
+      for (int i = 0; i < 9; ++i) {
+        // (the empty asm keeps the compiler from hoisting these lane-only
+        // offsets out of the tile loop, where they would hold registers
+        // through the decode)
+        uint32_t m = 64u * i + lane;
+        asm volatile("" : "+v"(m));
+        const uint32_t c = m / 9u, p = m - 9u * c;
+        dma16(xrs, lds + 1024u * i, p < 8u ? ((uint32_t)t.g0 + c) * 128u + 16u * p : kNoRecord);
+      }
     }
   }
   const int lc = min((int)lane, t.Gt - 1);
