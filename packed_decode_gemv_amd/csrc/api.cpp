@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks, sizing and kernel dispatch.
 // Every check happens before anything is enqueued; no C++ exception leaves
 // these functions, and nothing here allocates device memory.
+#include <stdint.h>
 #include <string.h>
 
 #include <algorithm>
@@ -232,6 +233,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
     }
     if (wg > 0x7FFFFFFF) return VBQ_ERR_UNSUPPORTED;
     L.n_mats = count;
+    for (int i = 0; i < kMaxMats; ++i) L.wg_begin[i] = i < count ? L.mats[i].wg_begin : INT32_MAX;
     if (launch_gemv(L, nb, mode, (int)wg, stream) != hipSuccess) return VBQ_ERR_HIP;
   }
   return VBQ_OK;

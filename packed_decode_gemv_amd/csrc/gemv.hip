@@ -558,33 +558,38 @@ __device__ inline void cell_apply(const CellRows& c, uint32_t* S, int cw, uint32
   }
 }
 
-// Step 1 and 2 of a tile for the decoding wavefronts: activation copies, the
+// Step 1, first part (wavefront 0): the activations of the tile's columns into
+// LDS. It needs no tile header, so it goes out before the header is read.
+template <int NB>
+__device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t lane) {
+  const int g0 = kt * kTileGroups;
+  // copy i writes LDS chunk m = 64 i + lane, i.e. chunk m % 9
+  // of column m / 9 (144 bytes per column); chunks 0-7 of a column are its
+  // 128 bytes of x, chunk 8 is the gap and loads from outside the buffer
+  // (zeros), as do columns past the matrix's last group
+  const size_t K = (size_t)T.n_groups * kGroup;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
+    const uint32_t lds = lds_addr(S + LdsMap<NB>::x + nb * kXWords);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      // (the empty asm keeps the compiler from hoisting these lane-only
+      // offsets out of the tile loop, where they would hold registers
+      // through the decode)
+      uint32_t m = 64u * i + lane;
+      asm volatile("" : "+v"(m));
+      const uint32_t c = m / 9u, p = m - 9u * c;
+      dma16(xrs, lds + 1024u * i, p < 8u ? ((uint32_t)g0 + c) * 128u + 16u * p : kNoRecord);
+    }
+  }
+}
+
+// The rest of steps 1 and 2 for the decoding wavefronts: the width map, the
 // first loads of every class, the biases and the record table.
 template <int NB>
 __device__ inline void tile_start(const GemvMat& T, const TileRef& t, uint32_t* S, int wave, Flight<0, NB>& f0,
                                   Flight<1, NB>& f1, Flight<2, NB>& f2, Flight<3, NB>& f3, uint32_t lane) {
-  if (wave == 0) {
-    // activations: copy i writes LDS chunk m = 64 i + lane, i.e. chunk m % 9
-    // of column m / 9 (144 bytes per column); chunks 0-7 of a column are its
-    // 128 bytes of x, chunk 8 is the gap and loads from outside the buffer
-    // (zeros), as do columns past the matrix's last group
-    const size_t K = (size_t)T.n_groups * kGroup;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
-      const uint32_t lds = lds_addr(S + LdsMap<NB>::x + nb * kXWords);
-#pragma unroll
-      for (int i = 0; i < 9; ++i) {
-        // (the empty asm keeps the compiler from hoisting these lane-only
-        // offsets out of the tile loop, where they would hold registers
-        // through the decode)
-        uint32_t m = 64u * i + lane;
-        asm volatile("" : "+v"(m));
-        const uint32_t c = m / 9u, p = m - 9u * c;
-        dma16(xrs, lds + 1024u * i, p < 8u ? ((uint32_t)t.g0 + c) * 128u + 16u * p : kNoRecord);
-      }
-    }
-  }
   const int lc = min((int)lane, t.Gt - 1);
   const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)(t.base + 8u * (uint32_t)lc), 0, 0);
   issue_first<0, NB>(t, wave, f0, lane);
@@ -610,6 +615,7 @@ __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, 
   Flight<2, NB> f2;
   Flight<3, NB> f3;
   if (!cell_wave) {
+    if (wave == 0) copy_x<NB>(T, kt, S, lane);
     t = tile_ref(T, rt, kt);
     tile_start<NB>(T, t, S, wave, f0, f1, f2, f3, lane);
   }
@@ -726,10 +732,26 @@ __global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_ge
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int mi = 0;
-  for (int i = 1; i < L.n_mats; ++i) mi = ((int)blockIdx.x >= L.mats[i].wg_begin) ? i : mi;
+  // the workgroup's matrix: the last whose first workgroup is at or before
+  // this one (the start table is read in one go)
+  int mi = 0, wb = 0;
+#pragma unroll
+  for (int i = 1; i < 9; ++i) {
+    const int b = L.wg_begin[i];
+    mi = ((int)blockIdx.x >= b) ? i : mi;
+    wb = ((int)blockIdx.x >= b) ? b : wb;
+  }
+  if (mi == 8)
+    for (int i = 9; i < kMaxMats && (int)blockIdx.x >= L.wg_begin[i]; ++i) {
+      mi = i;
+      wb = L.wg_begin[i];
+    }
+  // the fields the first steps need are read together (one wait instead of
+  // a wait per field)
   const GemvMat& M = L.mats[mi];
-  const int j = (int)blockIdx.x - M.wg_begin;
+  asm volatile("" ::"s"(M.tiles), "s"(M.stream), "s"(M.x), "s"(M.n_groups), "s"(M.row_tiles), "s"(M.k_tiles),
+               "s"(M.stream_bytes), "s"(M.split), "s"(M.shared));
+  const int j = (int)blockIdx.x - wb;
   for (int i = tid; i < NB * kSlotWords; i += gemv_waves<MODE>() * kWave) S[LdsMap<NB>::slots + i] = 0u;
   float yacc[NB];
 #pragma unroll
@@ -743,9 +765,10 @@ __global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_ge
     // One tile of a row-tile with several: its row sums go to the scratch;
     // the workgroup that finishes the row-tile's last tile adds them in tile
     // order (the order the sequential path uses) and resets the counter.
-    const int tiles = M.levels * M.k_tiles;
-    const int rt = j / tiles, p = j - rt * tiles, lv = p / M.k_tiles, kt = p - lv * M.k_tiles;
-    coop_tile<NB, CELL>(L.mats[mi + lv], rt, kt, S, wave, yacc, lane);
+    // (split launches have one level per matrix)
+    const int tiles = M.k_tiles;
+    const int rt = j / tiles, p = j - rt * tiles;
+    coop_tile<NB, CELL>(M, rt, p, S, wave, yacc, lane);
     // The partial sums are device-scope atomic stores, which write through
     // the caches, so once they are complete (the wait before the barrier)
     // the counter may count this tile; the last workgroup reads them with

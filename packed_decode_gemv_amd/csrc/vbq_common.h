@@ -139,25 +139,29 @@ __device__ inline void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
 // One matrix of a GEMV launch. A launch runs one workgroup of four
 // wavefronts per row-tile of each matrix; the wavefronts share each tile.
 struct GemvMat {
+  // the fields every workgroup needs first, in the first 64 bytes (read in
+  // one scalar load)
   const uint32_t* tiles;
   const uint8_t* stream;
   const uint16_t* x;       // [B][K] fp16
-  const uint16_t* resid;   // [N][K] fp16 or null
-  const int8_t* cell;      // [N][K] compact in-cell residual fractions or null
-  float* y;                // [B][N]
   int32_t n_rows;
   int32_t n_groups;        // K / 64
   int32_t row_tiles;       // ceil(N / 32)
   int32_t k_tiles;         // ceil(G / 64)
-  int32_t wg_begin;        // first workgroup of this matrix in the launch
-  int32_t shared;          // 1: a workgroup per row-tile (k-tiles, levels or residual shared by its waves)
-  int32_t levels;          // matrices summed into one output (levels), this one and the next levels-1
   uint32_t stream_bytes;   // size of the stream, for the buffer range checks
   int32_t split;           // 1: a workgroup per (row-tile, tile); partial row sums meet in the scratch
+  int32_t shared;          // 1: a workgroup per row-tile (k-tiles, levels or residual shared by its waves)
+  int32_t levels;          // matrices summed into one output (levels), this one and the next levels-1
   int32_t unit_base;       // first partial-sum slot of this matrix in the scratch (split)
   int32_t ctr_base;        // first row-tile counter of this matrix in the scratch (split)
+  // the rest
+  float* y;                // [B][N]
+  const uint16_t* resid;   // [N][K] fp16 or null
+  const int8_t* cell;      // [N][K] compact in-cell residual fractions or null
+  int32_t wg_begin;        // first workgroup of this matrix in the launch
+  int32_t pad_;
 };
-
+static_assert(sizeof(GemvMat) == 96, "GemvMat layout");
 constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
 constexpr int kGemvWaves = 4;
 constexpr int kGemvMaxNb = 2;   // batch rows per pass
@@ -165,6 +169,7 @@ constexpr int kGemvMaxNb = 2;   // batch rows per pass
 constexpr int kModePlain = 0, kModeResid16 = 1, kModeCell8 = 2;
 
 struct GemvLaunch {
+  int32_t wg_begin[kMaxMats];   // first workgroup of each matrix (non-decreasing; INT32_MAX past n_mats)
   GemvMat mats[kMaxMats];
   int32_t n_mats;
   float* partials;         // split matrices: [slot][NB][32] row sums of one tile
