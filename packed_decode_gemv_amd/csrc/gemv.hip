@@ -20,23 +20,19 @@
 // bias part, sum_j bias_j (x_2j + x_2j+1), depends only on x and the width,
 // so it is computed once per (k-group, width) and subtracted per record.
 //
-// Work split: one wavefront decodes one tile (32 rows x 64 k-groups). Lane l
-// owns the tile's column l, i.e. k-group 64 kt + l, and keeps that group's 64
-// activations (per batch row) in registers for the whole tile. The tile's
-// blocks each hold one record per active column, all of one width, so a
-// wavefront decodes without divergence and without reading x from LDS. The
-// lane finds its record's row from the column's 2-bit width map: the rows of
-// one class, taken from a rotation that starts at row l, one per block. Each
-// record adds s (dot - bias) + o sum(x) to its row in the wavefront's LDS row
-// slice; the rotation spreads the lanes of one block over different rows.
-// The blocks stream from HBM into a private LDS ring in 1 KiB pieces with
-// buffer-to-LDS loads, so several kilobytes are in flight per wavefront
-// without spending registers; the wait before a block is a closed form of its
-// stream position. A workgroup of four wavefronts takes four row-tiles of a
-// matrix with one k-tile, or one row-tile whose k-tiles (and levels) its
-// wavefronts share, with a residual wavefronts 1-3 take the residual's rows;
-// the wavefront slices are added in a fixed order at the end, so results are
-// identical from run to run and no memory outside the workgroup is needed.
+// Work split: the four wavefronts of a workgroup decode one tile (32 rows x
+// 64 k-groups) together; the steps are described at coop_tile. The tile's
+// activations are copied into LDS once, every record's position is a closed
+// form of the tile header's class counts (records of a width class are listed
+// column by column, 64 to a block), and each record's value goes to an LDS
+// slot of its (column, row), so the row sums are added in a fixed order and
+// results repeat bit for bit with no atomics. A matrix with one k-tile takes a
+// workgroup per tile; a longer one either has a workgroup walk its row-tile's
+// k-tiles (and residual levels, then residual rows) in order, or, in the
+// launches that may not allocate, a workgroup per tile whose row sums meet in
+// a static device array and are added in k-tile order by the last one to
+// finish. With a compact in-cell residual the workgroup has four more
+// wavefronts that stream the residual bytes while the tile is decoded.
 #include <utility>
 
 #include "vbq_common.h"
