@@ -541,11 +541,11 @@ def measure_workloads(stack, calls):
     for B in (1, 4):
         xs = [xf16(k, B, p.k) for (_, _, k), p in zip(mats, synth.C1.projs)]
         ys = [torch.empty(B, p.n, dtype=torch.float32, device=dev) for p in synth.C1.projs]
-        plans = [vbq.GemvPlan(L, xs, ys) for L in layers]
+        plans = [vbq.GemvPlan(L, xs, ys, static=True) for L in layers]
         us = _events_time(lambda i: plans[i % len(plans)].launch(vbq._stream()), calls)
         nb = sum(algorithmic_bytes(m.sizes, p.n, p.k, B) for (m, _, _), p in zip(mats, synth.C1.projs))
         out.append(_gemv_line(f"1.0B-class layer (qkv 6144x2048, o 2048x2048, up/gate 8192x2048, "
-                              f"down 2048x8192), one launch, batch {B}", us, nb))
+                              f"down 2048x8192), one vbq_gemv_batched_static launch, batch {B}", us, nb))
     del mats, layers, plans
 
     # 9B-class stack at batch 4: the same packed weights, batch-4 activations
@@ -789,6 +789,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="only the headline stack")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the step through vbq_gemv_batched (profiles of the headline launches only)")
     ap.add_argument("--workload-calls", type=int, default=100)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="RESULTS")
@@ -846,9 +848,11 @@ def main(argv=None):
 
     ms_eager = time_steps(stack, args.steps, args.warmup)
     ms, _ = time_steps_graph(stack, args.steps, args.warmup)
-    ms_batched, _ = time_steps_graph(stack, args.steps, args.warmup, plans=stack.batched_plans)
+    ms_batched = None
+    if not args.no_compare:
+        ms_batched, _ = time_steps_graph(stack, args.steps, args.warmup, plans=stack.batched_plans)
     log(f"  eager launches {ms_eager * 1e3:.1f} us/step, graph replay {ms * 1e3:.1f} us/step "
-        f"(vbq_gemv_batched launches: {ms_batched * 1e3:.1f} us/step)")
+        f"(vbq_gemv_batched launches: {ms_batched and round(ms_batched * 1e3, 1)} us/step)")
     n_launch = len(stack.plans)
     step_bytes = float(sum(stack.launch_bytes))
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -894,7 +898,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager_launches": round(ms_eager, 4),
-        "ms_per_step_vbq_gemv_batched": round(ms_batched, 4),
+        "ms_per_step_vbq_gemv_batched": None if ms_batched is None else round(ms_batched, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -177,20 +177,21 @@ __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB
 //     fixed order and clears them.
 constexpr int kSlotPitch = 33;                            // slot (column l, row r) at l * 33 + r; 32 is spare
 constexpr int kSlotWords = kWave * kSlotPitch;            // 2112 per batch row
-// Activations of a tile's 64 columns: 64 fp16 per column, 144 bytes apart
-// (128 bytes and a 16-byte gap), so that the 16-byte reads of lanes on
-// different columns fall on different LDS banks.
+// Activations of a tile's 64 columns: per column 64 fp16 (32 words) and 4
+// words of sums, 144 bytes apart, so that the 16-byte reads of lanes on
+// different columns fall on different LDS banks. The sums are sum(x) and
+// -bias of classes 0, 1, 2 (the bias of 8-bit codes is 1024 sum(x)).
 constexpr int kXPitch = 36;                               // words per column
+constexpr int kXSum = 32;                                 // word of sum(x) in a column; -bias of class c at 33 + c
 constexpr int kXWords = kTileGroups * kXPitch;
-constexpr int kMaxRecs = kTileRows * kTileGroups;         // 2048 table entries of 16 bits
+constexpr int kMaxRecs = kTileRows * kTileGroups;         // 2048 table entries
 
 template <int NB>
 struct LdsMap {
-  static constexpr int x = 0;                             // [NB][64][36] fp16 pairs (32 used)
-  static constexpr int xsum = x + NB * kXWords;           // [NB][64]
-  static constexpr int bias = xsum + NB * kWave;          // [NB][4][64]
-  static constexpr int table = bias + NB * 4 * kWave;     // [2048] u16: column << 5 | row
-  static constexpr int slots = table + kMaxRecs / 2;      // [NB][64][33]
+  static constexpr int x = 0;                             // [NB][64][36] fp16 pairs and the column's sums
+  static constexpr int xbuf = NB * kXWords;               // words per activation buffer
+  static constexpr int table = x + xbuf;                  // [2048] u32: slot byte << 16 | column byte (from S)
+  static constexpr int slots = table + kMaxRecs;          // [NB][64][33]
   static constexpr int ys = slots + NB * kSlotWords;      // [NB][32] residual row sums
   static constexpr int words = ys + NB * kTileRows;
   // With a compact in-cell residual: the scale of slot (column, row) and the
@@ -227,10 +228,12 @@ struct TileRef {
   int R, Gt, g0;
 };
 
-__device__ inline TileRef tile_ref(const GemvMat& T, int rt, int kt) {
+__device__ inline uint4 tile_header(const GemvMat& T, int rt, int kt) {
+  return *reinterpret_cast<const uint4*>(T.tiles + 4 * ((size_t)kt * T.row_tiles + rt));
+}
+
+__device__ inline TileRef tile_ref_from(const GemvMat& T, int rt, int kt, const uint4 hdr) {
   TileRef t;
-  const int ti = kt * T.row_tiles + rt;
-  const uint4 hdr = *reinterpret_cast<const uint4*>(T.tiles + 4 * (size_t)ti);
   t.base = __builtin_amdgcn_readfirstlane(hdr.x) * 16u;
   const uint32_t w2 = __builtin_amdgcn_readfirstlane(hdr.z), w3 = __builtin_amdgcn_readfirstlane(hdr.w);
   t.R = min(kTileRows, T.n_rows - rt * kTileRows);
@@ -247,6 +250,14 @@ __device__ inline TileRef tile_ref(const GemvMat& T, int rt, int kt) {
   }
   t.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(T.stream), (short)0, (int)T.stream_bytes, 0x00020000);
   return t;
+}
+
+__device__ inline TileRef tile_ref(const GemvMat& T, int rt, int kt) { return tile_ref_from(T, rt, kt, tile_header(T, rt, kt)); }
+
+// The width map of the lane's column (columns past the tile repeat its last).
+__device__ inline u32x2 map_load(const TileRef& t, uint32_t lane) {
+  const int lc = min((int)lane, t.Gt - 1);
+  return __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)(t.base + 8u * (uint32_t)lc), 0, 0);
 }
 
 // Issues the loads of chunk j of class C (records 64 j + lane); lanes past
@@ -301,25 +312,34 @@ __device__ inline void issue_first(const TileRef& t, int wave, Flight<C, NB>& f,
 // row order, after the entries of the columns before it.
 template <int NB>
 __device__ inline void table_class(const TileRef& t, int c, uint32_t p0, uint32_t p1, uint32_t valid, uint32_t* S,
-                                   uint32_t lane) {
+                                   uint32_t lane, int buf) {
   uint32_t mask = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
   const uint32_t first = (c > 0 ? t.n[0] : 0u) + (c > 1 ? t.n[1] : 0u) + (c > 2 ? t.n[2] : 0u);
   uint32_t e = first + wave_excl_scan((uint32_t)__builtin_popcount(mask), lane);
-  uint16_t* tab = reinterpret_cast<uint16_t*>(S + LdsMap<NB>::table);
-  for (; mask; mask &= mask - 1u, ++e) tab[e] = (uint16_t)((lane << 5) | (uint32_t)__builtin_ctz(mask));
+  uint32_t* tab = S + LdsMap<NB>::table;
+  const uint32_t xb = 4u * (LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + lane * kXPitch);
+  const uint32_t sb = 4u * (LdsMap<NB>::slots + lane * kSlotPitch);
+  for (; mask; mask &= mask - 1u, ++e) tab[e] = ((sb + 4u * (uint32_t)__builtin_ctz(mask)) << 16) | xb;
+}
+
+// Table entry of the lanes past a class's last record: column 31, spare row 32.
+template <int NB>
+__host__ __device__ constexpr uint32_t spare_entry() {
+  return ((4u * (LdsMap<NB>::slots + 31 * kSlotPitch + 32)) << 16) | (4u * (LdsMap<NB>::x + 31 * kXPitch));
 }
 
 // Step 2.
 template <int NB>
-__device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, uint32_t* S, uint32_t lane) {
+__device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, uint32_t* S, uint32_t lane, int buf) {
   if (wave == 0) {
-    // the activation copies of this wavefront are complete once nothing of
-    // its own is in flight
-    __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(0));
+    // The activation copies of this wavefront were issued before its width
+    // map load, and loads complete in order: once the map has arrived (the
+    // wait the compiler inserts for this use of it) the copies are in LDS.
+    asm volatile("" ::"v"(mp.x), "v"(mp.y));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t xr[1][32];
-      const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * (uint32_t)kXPitch;
+      const uint32_t* xs = S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords + lane * (uint32_t)kXPitch;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
@@ -328,25 +348,23 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
         xr[0][4 * i + 2] = v.z;
         xr[0][4 * i + 3] = v.w;
       }
-      float b[4][1];
+      float b[3][1];
       class_bias<0, 1>(xr, b[0], std::make_integer_sequence<int, 32>{});
       class_bias<1, 1>(xr, b[1], std::make_integer_sequence<int, 32>{});
       class_bias<2, 1>(xr, b[2], std::make_integer_sequence<int, 32>{});
-      class_bias<3, 1>(xr, b[3], std::make_integer_sequence<int, 32>{});
-      float* bias = reinterpret_cast<float*>(S + LdsMap<NB>::bias) + nb * 4 * kWave + lane;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bias[c * kWave] = b[c][0];
       float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < 32; ++p) a[p & 3] = dot2(xr[0][p], 0x3C003C00u, a[p & 3]);
-      reinterpret_cast<float*>(S + LdsMap<NB>::xsum)[nb * kWave + lane] = (a[0] + a[1]) + (a[2] + a[3]);
+      float* sums = reinterpret_cast<float*>(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords +
+                                             lane * (uint32_t)kXPitch + kXSum);
+      *reinterpret_cast<float4*>(sums) = make_float4((a[0] + a[1]) + (a[2] + a[3]), -b[0][0], -b[1][0], -b[2][0]);
     }
   } else {
     const bool live = (int)lane < t.Gt;
     const uint32_t p0 = live ? mp.x : 0u, p1 = live ? mp.y : 0u;
     const uint32_t valid = !live ? 0u : t.R >= 32 ? 0xFFFFFFFFu : ((1u << t.R) - 1u);
-    table_class<NB>(t, wave - 1, p0, p1, valid, S, lane);
-    if (wave == 3) table_class<NB>(t, 3, p0, p1, valid, S, lane);
+    table_class<NB>(t, wave - 1, p0, p1, valid, S, lane, buf);
+    if (wave == 3) table_class<NB>(t, 3, p0, p1, valid, S, lane, buf);
   }
 }
 
@@ -357,18 +375,18 @@ template <int C, int NB, bool CELL>
 __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const TileRef& t, uint32_t j, uint32_t* S,
                                     uint32_t lane) {
   const uint32_t e = 64u * j + lane;
-  const bool valid = e < t.n[C];
-  const uint32_t ent = valid ? reinterpret_cast<const uint16_t*>(S + LdsMap<NB>::table)[t.t0[C] + e] : (31u << 5);
-  const uint32_t col = ent >> 5, row = valid ? (ent & 31u) : 32u;
+  const bool valid = 64u * (j + 1u) <= t.n[C] || e < t.n[C];
+  const uint32_t ent = valid ? S[LdsMap<NB>::table + t.t0[C] + e] : spare_entry<NB>();
+  const uint32_t xoff = ent & 0xFFFFu, soff = ent >> 16;   // byte offsets from S
   const float s = __half2float(__ushort_as_half((unsigned short)(r.so & 0xFFFFu)));
   const float o = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
-  if (CELL) reinterpret_cast<float*>(S + LdsMap<NB>::sc)[col * kSlotPitch + row] = s;
+  float* slot = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(S) + soff);
+  if (CELL) slot[LdsMap<NB>::sc - LdsMap<NB>::slots] = s;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + col * (uint32_t)kXPitch;
-    const float xsum = reinterpret_cast<const float*>(S + LdsMap<NB>::xsum)[nb * kWave + col];
-    const float bias = reinterpret_cast<const float*>(S + LdsMap<NB>::bias)[(nb * 4 + C) * kWave + col];
-    float a[1][2] = {{-bias, 0.f}};
+    const uint32_t* xs = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(S) + xoff) + nb * kXWords;
+    const float xsum = reinterpret_cast<const float*>(xs)[kXSum];
+    float a[1][2] = {{C == 3 ? -1024.f * xsum : reinterpret_cast<const float*>(xs)[kXSum + 1 + C], 0.f}};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t xr[1][32];
@@ -383,8 +401,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
       if (half == 0) record_dot<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
       else record_dot_hi<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
     }
-    reinterpret_cast<float*>(S + LdsMap<NB>::slots)[nb * kSlotWords + col * kSlotPitch + row] =
-        __builtin_fmaf(s, a[0][0] + a[0][1], o * xsum);
+    slot[nb * kSlotWords] = __builtin_fmaf(s, a[0][0] + a[0][1], o * xsum);
   }
 }
 
@@ -501,7 +518,7 @@ __device__ inline void cell_dots(const CellRows& c, CellFlight<NB>& f, uint32_t*
       xr[nb][4 * i + 2] = v.z;
       xr[nb][4 * i + 3] = v.w;
     }
-    base[nb] = -1152.f * reinterpret_cast<const float*>(S + LdsMap<NB>::xsum)[nb * kWave + lane];
+    base[nb] = -1152.f * reinterpret_cast<const float*>(xs)[kXSum];
   }
   const uint32_t magic = vconst<0x64646464u>();
   float* cd = reinterpret_cast<float*>(S + LdsMap<NB>::cd) + lane * kSlotPitch + 8 * cw;
@@ -557,7 +574,7 @@ __device__ inline void cell_apply(const CellRows& c, uint32_t* S, int cw, uint32
 // Step 1, first part (wavefront 0): the activations of the tile's columns into
 // LDS. It needs no tile header, so it goes out before the header is read.
 template <int NB>
-__device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t lane) {
+__device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t lane, int buf) {
   const int g0 = kt * kTileGroups;
   // copy i writes LDS chunk m = 64 i + lane, i.e. chunk m % 9
   // of column m / 9 (144 bytes per column); chunks 0-7 of a column are its
@@ -567,7 +584,7 @@ __device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t la
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
-    const uint32_t lds = lds_addr(S + LdsMap<NB>::x + nb * kXWords);
+    const uint32_t lds = lds_addr(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       // (the empty asm keeps the compiler from hoisting these lane-only
@@ -586,13 +603,12 @@ __device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t la
 template <int NB>
 __device__ inline void tile_start(const GemvMat& T, const TileRef& t, uint32_t* S, int wave, Flight<0, NB>& f0,
                                   Flight<1, NB>& f1, Flight<2, NB>& f2, Flight<3, NB>& f3, uint32_t lane) {
-  const int lc = min((int)lane, t.Gt - 1);
-  const u32x2 mp = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)(t.base + 8u * (uint32_t)lc), 0, 0);
+  const u32x2 mp = map_load(t, lane);
   issue_first<0, NB>(t, wave, f0, lane);
   issue_first<1, NB>(t, wave, f1, lane);
   issue_first<2, NB>(t, wave, f2, lane);
   issue_first<3, NB>(t, wave, f3, lane);
-  tile_prepare<NB>(t, wave, mp, S, lane);
+  tile_prepare<NB>(t, wave, mp, S, lane, 0);
 }
 
 // One tile, all steps; the caller has passed a barrier since the last fold.
@@ -611,7 +627,7 @@ __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, 
   Flight<2, NB> f2;
   Flight<3, NB> f3;
   if (!cell_wave) {
-    if (wave == 0) copy_x<NB>(T, kt, S, lane);
+    if (wave == 0) copy_x<NB>(T, kt, S, lane, 0);
     t = tile_ref(T, rt, kt);
     tile_start<NB>(T, t, S, wave, f0, f1, f2, f3, lane);
   }
