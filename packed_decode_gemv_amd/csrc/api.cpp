@@ -166,6 +166,7 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
   if (cell && !aligned(cell, 16)) return VBQ_ERR_ALIGNMENT;
   const int mode = resid ? kModeResid16 : cell ? kModeCell8 : kModePlain;
+  const int max_nb = mode == kModePlain ? kGemvMaxNb : kGemvMaxNbResid;
   float* partials = nullptr;
   uint32_t* counters = nullptr;
   if (split) {
@@ -179,12 +180,12 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
         ctrs += row_tiles(ms[i].n_rows);
       }
     }
-    if (units * std::min(B, kGemvMaxNb) * kTileRows > (int64_t)kScratchPartials || ctrs > (int64_t)kScratchCounters)
+    if (units * std::min(B, max_nb) * kTileRows > (int64_t)kScratchPartials || ctrs > (int64_t)kScratchCounters)
       return VBQ_ERR_UNSUPPORTED;
     if (gemv_scratch(&partials, &counters) != hipSuccess) return VBQ_ERR_HIP;
   }
-  for (int b0 = 0; b0 < B; b0 += kGemvMaxNb) {
-    const int nb = std::min(kGemvMaxNb, B - b0);
+  for (int b0 = 0; b0 < B; b0 += max_nb) {
+    const int nb = std::min(max_nb, B - b0);
     GemvLaunch L;
     memset(&L, 0, sizeof(L));
     L.partials = partials;

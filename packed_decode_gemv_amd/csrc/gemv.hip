@@ -216,7 +216,7 @@ struct Rec {
 // and refilled while the class is decoded.
 template <int C, int NB>
 __host__ __device__ constexpr int depth() {
-  return C == 0 ? 4 / NB : C == 1 ? 2 / NB : 1;
+  return C == 0 ? (NB >= 4 ? 1 : 4 / NB) : C == 1 ? (NB >= 2 ? 1 : 2) : 1;   // at least one
 }
 
 struct TileRef {
@@ -382,27 +382,35 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
   const float o = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
   float* slot = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(S) + soff);
   if (CELL) slot[LdsMap<NB>::sc - LdsMap<NB>::slots] = s;
+  // each code pair is decoded once and multiplied with every batch row's
+  // activations (read in two halves, to bound the registers)
+  const uint32_t* xs0 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(S) + xoff);
+  float xsum[NB], a[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t* xs = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(S) + xoff) + nb * kXWords;
-    const float xsum = reinterpret_cast<const float*>(xs)[kXSum];
-    float a[1][2] = {{C == 3 ? -1024.f * xsum : reinterpret_cast<const float*>(xs)[kXSum + 1 + C], 0.f}};
+    const float* sums = reinterpret_cast<const float*>(xs0 + nb * kXWords) + kXSum;
+    xsum[nb] = sums[0];
+    a[nb][0] = C == 3 ? -1024.f * xsum[nb] : sums[1 + C];
+    a[nb][1] = 0.f;
+  }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t xr[1][32];
+  for (int half = 0; half < 2; ++half) {
+    uint32_t xr[NB][32];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xs + 16 * half + 4 * i);
-        xr[0][16 * half + 4 * i + 0] = v.x;
-        xr[0][16 * half + 4 * i + 1] = v.y;
-        xr[0][16 * half + 4 * i + 2] = v.z;
-        xr[0][16 * half + 4 * i + 3] = v.w;
+        const uint4 v = *reinterpret_cast<const uint4*>(xs0 + nb * kXWords + 16 * half + 4 * i);
+        xr[nb][16 * half + 4 * i + 0] = v.x;
+        xr[nb][16 * half + 4 * i + 1] = v.y;
+        xr[nb][16 * half + 4 * i + 2] = v.z;
+        xr[nb][16 * half + 4 * i + 3] = v.w;
       }
-      if (half == 0) record_dot<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
-      else record_dot_hi<C, 1>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
-    }
-    slot[nb * kSlotWords] = __builtin_fmaf(s, a[0][0] + a[0][1], o * xsum);
+    if (half == 0) record_dot<C, NB>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
+    else record_dot_hi<C, NB>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
   }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) slot[nb * kSlotWords] = __builtin_fmaf(s, a[nb][0] + a[nb][1], o * xsum[nb]);
 }
 
 // Step 3 for class C: the chunks in flight are decoded in turn and each
@@ -865,7 +873,9 @@ size_t gemv_lds_bytes(int nb, int mode) {
   const bool cell = mode == kModeCell8;
   switch (nb) {
     case 1: return 4u * (cell ? LdsMap<1>::words_cell : LdsMap<1>::words);
-    default: return 4u * (cell ? LdsMap<2>::words_cell : LdsMap<2>::words);
+    case 2: return 4u * (cell ? LdsMap<2>::words_cell : LdsMap<2>::words);
+    case 3: return 4u * LdsMap<3>::words;
+    default: return 4u * LdsMap<4>::words;
   }
 }
 
@@ -884,6 +894,7 @@ static hipError_t launch_one(const GemvLaunch& L, int n_wg, hipStream_t s) {
 }
 
 hipError_t launch_gemv(const GemvLaunch& L, int nb, int mode, int n_wg, hipStream_t s) {
+  // passes of up to four batch rows without a residual, two with one
 #define VBQ_CASE(N)                                                                      \
   case N:                                                                                \
     return mode == kModeResid16  ? launch_one<N, kModeResid16>(L, n_wg, s)               \
@@ -892,6 +903,10 @@ hipError_t launch_gemv(const GemvLaunch& L, int nb, int mode, int n_wg, hipStrea
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)
+    case 3:
+      return mode == kModePlain ? launch_one<3, kModePlain>(L, n_wg, s) : hipErrorInvalidValue;
+    case 4:
+      return mode == kModePlain ? launch_one<4, kModePlain>(L, n_wg, s) : hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;
   }

@@ -164,7 +164,8 @@ struct GemvMat {
 static_assert(sizeof(GemvMat) == 96, "GemvMat layout");
 constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
 constexpr int kGemvWaves = 4;
-constexpr int kGemvMaxNb = 2;   // batch rows per pass
+constexpr int kGemvMaxNb = 4;   // batch rows per pass (two with a residual)
+constexpr int kGemvMaxNbResid = 2;
 // Residual kinds of a launch: none, fp16 per weight, int8 cell fractions.
 constexpr int kModePlain = 0, kModeResid16 = 1, kModeCell8 = 2;
 
