@@ -548,6 +548,23 @@ def measure_workloads(stack, calls):
                               f"down 2048x8192), one vbq_gemv_batched_static launch, batch {B}", us, nb))
     del mats, layers, plans
 
+    # The whole 9B-class step in as few launches as the ABI allows (32 matrices
+    # each): the 225 matrices in 8 vbq_gemv_batched_static calls, so later
+    # workgroups start while earlier ones stream (no layer order kept)
+    mats = list(stack.mats.values())
+    wplans = [vbq.GemvPlan([m[0] for m in mats[i:i + 32]], [m[1] for m in mats[i:i + 32]],
+                           [m[2] for m in mats[i:i + 32]], static=True) for i in range(0, len(mats), 32)]
+
+    def whole_step(i):
+        sh = vbq._stream()
+        for p in wplans:
+            p.launch(sh)
+    us = _events_time(whole_step, 1, reps=max(3, calls // 20))
+    out.append(_gemv_line(f"9B-class stack ({stack.layers} layers + LM head), batch 1, all {len(mats)} matrices "
+                          f"in {len(wplans)} batched launches (no layer order), one step", us,
+                          float(sum(stack.launch_bytes))))
+    del wplans
+
     # 9B-class stack at batch 4: the same packed weights, batch-4 activations
     B = 4
     plans, nb = [], 0.0

@@ -169,7 +169,8 @@ vbq_status vbq_matrix_check(const vbq_matrix* m, hipStream_t stream);
  *   NULL. NULL serves the released artifact; the in-cell update (CellFill
  *   abstract) is revoked simply by passing NULL.
  * y: device, B x N float32, 4-byte aligned; fully overwritten.
- * Batches above 2 rows are run as passes of at most 2 rows. */
+ * Batches run as passes of at most 4 rows (2 with a residual); each code is
+ * decoded once per pass and multiplied with every row of the pass. */
 vbq_status vbq_gemv(const vbq_matrix* m, const uint16_t* x, int32_t B, const uint16_t* residual, float* y,
                     hipStream_t stream);
 
@@ -221,7 +222,7 @@ vbq_status vbq_gemv_batched(int32_t count, const vbq_matrix* ms, const uint16_t*
  * vbq_gemv_batched uses, so both calls give the same bits, and sets the
  * row-tile's counter back to zero. Arguments and results as for
  * vbq_gemv_batched. A launch needing more than the scratch holds (more than
- * 8192 tiles of such matrices at one batch row, 4096 at two or more) returns
+ * 8192 tiles of such matrices at one batch row, 8192 / min(B, 4) at B rows) returns
  * VBQ_ERR_UNSUPPORTED before anything is enqueued. Calls that overlap in
  * time on one device race on the scratch and must not be made; a call whose
  * kernels do not complete can leave counters behind for the next call. */

@@ -268,6 +268,45 @@ def cell8_decode(pm: PackedMatrix, cell, out=None, stream=None):
     return out
 
 
+class CellUpdate:
+    """An in-cell update served beside a frozen packed matrix (CellFill
+    abstract: the release's codes and scales stay untouched, and dropping the
+    residual revokes the update). Holds the matrix and the update's fraction
+    bytes; gemv() calls vbq_gemv_cell8 while the update is applied and
+    vbq_gemv (the release) once it is revoked. Nothing in the matrix changes
+    either way, so revoke() and apply() can alternate freely."""
+
+    def __init__(self, pm: PackedMatrix, cell):
+        import torch
+        _need(cell, "cell", torch.int8, (pm.N, pm.K), pm.device)
+        self.pm, self.cell, self.applied = pm, cell, True
+
+    @classmethod
+    def from_residual(cls, pm: PackedMatrix, residual, stream=None) -> "CellUpdate":
+        """Encodes an fp16 residual with the matrix's scales (cell8_encode)."""
+        return cls(pm, cell8_encode(pm, residual, stream=stream))
+
+    def revoke(self):
+        self.applied = False
+
+    def apply(self):
+        self.applied = True
+
+    def gemv(self, x, out=None, stream=None):
+        if self.applied:
+            return vbq_gemv_cell8(self.pm, x, self.cell, out=out, stream=stream)
+        return vbq_gemv(self.pm, x, out=out, stream=stream)
+
+    def residual(self, stream=None):
+        """The fp16 residual the fraction bytes stand for (cell8_decode)."""
+        return cell8_decode(self.pm, self.cell, stream=stream)
+
+    def verify(self, stream=None):
+        """cell_requant_verify of the decoded residual: (mismatches,
+        out_of_cell, first_bad_index, None)."""
+        return cell_requant_verify(self.pm, self.residual(stream=stream), stream=stream)
+
+
 def vbq_gemv_batched(pms, xs, ys=None, stream=None, static=False):
     """One launch for several independent GEMVs (same batch size). With
     static=True it calls vbq_gemv_batched_static, which allocates nothing and

@@ -756,16 +756,19 @@ __global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_ge
   // this one (the start table is read in one go)
   int mi = 0, wb = 0;
 #pragma unroll
-  for (int i = 1; i < 9; ++i) {
+  for (int i = 1; i < 16; ++i) {
     const int b = L.wg_begin[i];
     mi = ((int)blockIdx.x >= b) ? i : mi;
     wb = ((int)blockIdx.x >= b) ? b : wb;
   }
-  if (mi == 8)
-    for (int i = 9; i < kMaxMats && (int)blockIdx.x >= L.wg_begin[i]; ++i) {
-      mi = i;
-      wb = L.wg_begin[i];
+  if (mi == 15) {
+#pragma unroll
+    for (int i = 16; i < kMaxMats; ++i) {
+      const int b = L.wg_begin[i];
+      mi = ((int)blockIdx.x >= b) ? i : mi;
+      wb = ((int)blockIdx.x >= b) ? b : wb;
     }
+  }
   // the fields the first steps need are read together (one wait instead of
   // a wait per field)
   const GemvMat& M = L.mats[mi];

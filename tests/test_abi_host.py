@@ -166,6 +166,8 @@ def test_binding_rejects_bad_tensors_before_any_launch():
         vbq.vbq_gemv_cell8(pm, torch.zeros(1, 128, dtype=torch.float16), torch.zeros(32, 128, dtype=torch.uint8))
     with pytest.raises(ValueError, match="cell: shape"):
         vbq.cell8_decode(pm, torch.zeros(32, 64, dtype=torch.int8))
+    with pytest.raises(ValueError, match="cell: dtype"):
+        vbq.CellUpdate(pm, torch.zeros(32, 128, dtype=torch.int16))
     with pytest.raises(ValueError, match="residual: dtype"):
         vbq.cell8_encode(pm, torch.zeros(32, 128))
     with pytest.raises(ValueError, match="E: dtype"):

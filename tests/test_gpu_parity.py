@@ -437,6 +437,34 @@ def test_cell8_encode_decode_bit_exact(vbq, shape):
     assert np.array_equal(d_gpu, oracle.cell8_decode(fr, s))
 
 
+def test_cell_update_revoke_and_reapply(vbq):
+    """CellUpdate: applied, the GEMV is vbq_gemv_cell8's; revoked, it is the
+    release's vbq_gemv bit for bit; applied again, the first result bit for
+    bit. The packed matrix is byte-identical throughout, and the update's
+    decoded residual passes the re-quantisation check."""
+    import torch
+    N, K = 70, 64 * 70
+    W, widths, x = rand_case(N, K, seed=17, B=2)
+    pm = vbq.vbq_pack(_t(W), widths)
+    stream0 = pm.stream.clone()
+    q, s, o = oracle.quantize_matrix(W, widths)
+    resid = oracle.make_cell_residual(np.random.default_rng(18).uniform(-0.45, 0.45, (N, K)), s)
+    upd = vbq.CellUpdate.from_residual(pm, _t(resid, torch.float16))
+    assert np.array_equal(upd.cell.cpu().numpy(), oracle.cell8_encode(resid, s))
+    xt = _t(x, torch.float16)
+    y_on = upd.gemv(xt)
+    assert torch.equal(y_on, vbq.vbq_gemv_cell8(pm, xt, upd.cell))
+    upd.revoke()
+    y_off = upd.gemv(xt)
+    assert torch.equal(y_off, vbq.vbq_gemv(pm, xt))
+    upd.apply()
+    assert torch.equal(upd.gemv(xt), y_on)
+    assert torch.equal(pm.stream, stream0)
+    mism, ooc, first, _ = upd.verify()
+    assert (mism, ooc, first) == (0, 0, 2 ** 64 - 1)
+    check_gemv(y_on.cpu().numpy(), q, s, o, widths, x, cell=upd.cell.cpu().numpy())
+
+
 CELL_GEMV = [(1, 64, 1), (17, 320, 2), (33, 4096, 1), (100, 448, 3), (70, 64 * 70, 1), (20, 8192 + 192, 4),
              (64, 256, 8)]
 
