@@ -4,7 +4,7 @@ Independent of ``vbq_oracle.c``: it decodes IEEE binary16 / bfloat16 bit
 patterns into ``fractions.Fraction`` from the format definition and forms the
 dequantised product exactly, so the C oracle's fp64 results can be checked
 against the exact value. Follows the same passages as ``vbq_oracle.c``
-(VBQ abstract: fused dequantise-and-multiply at equal output; CellFill
+(VBQ abstract: the fused kernel must match the plain dequantised product; CellFill
 abstract: dequantised weight plus an in-cell residual).
 """
 from __future__ import annotations

@@ -8,16 +8,16 @@
  *  - Variable bit-width quantisation (VBQ abstract, page "In-Cell Learning:
  *    Language Models That Update Their Own Weights in Sequence Without
  *    Changing the File They Ship"): every contiguous group of 64 weights along
- *    K carries its own width b in {1,2,4,8}; the recipe maps to packed low-bit
- *    storage; a fused dequantise-and-multiply gives "equal output", i.e. the
- *    GEMV result is the plain product with the dequantised matrix.
+ *    K carries its own width b in {1,2,4,8}; the widths are stored packed, and
+ *    the kernel that dequantises while it multiplies must give the same
+ *    result as the plain product with the dequantised matrix.
  *  - Asymmetric quantisation with a scale and an offset (SLQ abstract, page
  *    thelatestinai.com/papers/2512.18934): w = scale*q + offset, q in [0, 2^b-1].
  *  - CellFill (page "Nothing Changed but the Model: CellFill -- Bounded In-Cell
  *    Learning for Bit-Identical, Revocable Updates to Quantized LLMs",
- *    section Abstract): codes and scales frozen, a per-weight residual inside
- *    each quantisation cell, re-quantisation returns the artifact bit-for-bit,
- *    updates revocable by dropping the residual, drift bounded.
+ *    section Abstract): frozen codes and scales, a per-weight residual kept
+ *    within its rounding cell, so quantising again gives back identical codes;
+ *    removing the residual undoes an update; the output drift has a bound.
  *
  * Where the pages are silent the readings are: scale and offset stored as
  * IEEE binary16; round-to-nearest (min/max) quantiser evaluated in binary32 with
