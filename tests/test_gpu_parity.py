@@ -319,6 +319,52 @@ def test_batched_full_launch_of_mixed_shapes(vbq):
         vbq.vbq_gemv_batched([pm for pm, _ in mats] + [mats[0][0]], [x for _, x in mats] + [mats[0][1]])
 
 
+# 32800 rows of one k-group: 1025 row-tiles, more workgroups than an MI355X
+# holds at once (four per CU).
+FILLER = (32800, 64)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_large_launch_with_small_matrices(vbq, B):
+    """A launch with more workgroups than the device holds at once, carrying
+    small matrices (ragged row-tiles, shared and split k-tiles) beside a
+    filler of 1025 row-tiles: each small matrix's output is the same bits as
+    in a launch of its own, in the batched and the allocation-free launches;
+    every output is within its bound of the oracle; two levels of the
+    filler's shape summed in one launch equal the sum of their GEMVs."""
+    import torch
+    cases = [(200, 4160), (33, 64), (100, 448), (300, 8192 + 192), (64, 4096), (95, 12288)]
+    mats, refs = [], []
+    for i, (N, K) in enumerate(cases):
+        W, widths, x = rand_case(N, K, seed=500 + i, B=B)
+        q, s, o = oracle.quantize_matrix(W, widths)
+        mats.append((vbq.vbq_pack(_t(W), widths), _t(x, torch.float16)))
+        refs.append((q, s, o, widths, x))
+    Wf, wf, xf = rand_case(*FILLER, seed=599, B=B)
+    qf, sf, of = oracle.quantize_matrix(Wf, wf)
+    fill = (vbq.vbq_pack(_t(Wf), wf), _t(xf, torch.float16))
+    pms, xs = [pm for pm, _ in mats], [x for _, x in mats]
+    print(f"case large launch B={B}", flush=True)
+    alone = [vbq.vbq_gemv(pm, x) for pm, x in mats]
+    alone_static = vbq.vbq_gemv_batched(pms, xs, static=True)
+    big = vbq.vbq_gemv_batched([fill[0]] + pms, [fill[1]] + xs)
+    big_static = vbq.vbq_gemv_batched([fill[0]] + pms, [fill[1]] + xs, static=True)
+    torch.cuda.synchronize()
+    for i, (N, K) in enumerate(cases):
+        assert torch.equal(alone[i], big[i + 1]), f"{N}x{K}: differs beside the filler"
+        assert torch.equal(alone[i], alone_static[i]), f"{N}x{K}: split launch differs"
+        assert torch.equal(alone[i], big_static[i + 1]), f"{N}x{K}: split launch beside the filler differs"
+        check_gemv(big[i + 1].cpu().numpy(), *refs[i])
+    check_gemv(big[0].cpu().numpy(), qf, sf, of, wf, xf)
+    assert torch.equal(big[0], big_static[0])
+    # two levels of the filler's shape, summed in one launch
+    W2, w2, _ = rand_case(*FILLER, seed=598, B=B)
+    lv2 = vbq.vbq_pack(_t(W2), w2)
+    y_lv = vbq.vbq_gemv_levels([fill[0], lv2], fill[1])
+    y_sum = vbq.vbq_gemv(fill[0], fill[1]) + vbq.vbq_gemv(lv2, fill[1])
+    assert torch.equal(y_lv, y_sum), "levels in one launch differ from the sum of their GEMVs"
+
+
 def test_graph_replays_match_eager(vbq):
     """Launches captured in a HIP graph (as the benchmark replays a decode
     step) give the eager results on every replay, with other eager work and
