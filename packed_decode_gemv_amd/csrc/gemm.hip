@@ -338,8 +338,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   //    they load group g + 4 and decode group g + 1 into the free weight
   //    buffer while the consumers multiply group g;
   //  - each consumer wavefront also copies its quarter of x of group g + 2
-  //    into the free x slot (buffer-to-LDS, no registers) and, before the
-  //    barrier, waits until its copy of group g + 1 has landed.
+  //    into the free x slot (buffer-to-LDS, no registers) at the start of
+  //    the step and, before the barrier, waits until its copy of group g + 1
+  //    has landed.
   // Producers issue only register loads and consumers only copies, so the
   // compiler's load-count waits in the producers are exact and the copies
   // are waited for explicitly. Every step issues the same loads (group
@@ -388,6 +389,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
       __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g0 landed
       gemm_barrier();
       auto step = [&](int g) {
+        // The copy of group g + 2 goes out first: its slot was last read in
+        // the previous step, before the barrier, and the copy then has two
+        // steps to land.
+        copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
+               lane);
         if (g < g1) {
           // All operands of the group are read from LDS before the first
           // MFMA, so the wavefront waits for LDS once per group, not per step.
@@ -414,11 +420,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
               for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
         }
-        // The copy of group g + 2 goes out after the MFMAs are issued, so a
-        // copy that waits for the memory pipeline does not hold them back;
-        // its slot was last read in the previous step, before the barrier.
-        copy_x(a, xrsrc, xs_lds + (uint32_t)((g + 2) % kXSlots) * kBM * kXRow, m0, xr0, min(g + 2, g1 - 1),
-               lane);
         __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g + 1 landed
         gemm_barrier();
       };
