@@ -751,6 +751,7 @@ def cpu_baseline(stack, budget_s):
     worst, checked = 0.0, []
     order = [(layer, pi, proj) for layer in range(stack.layers) for pi, proj in enumerate(wl.projs)]
     order.insert(7, (-1, 0, wl.head))
+    first = None
     with ThreadPoolExecutor(n_threads) as ex:
         for (layer, pi, proj) in order:
             if spent >= budget_s:
@@ -776,13 +777,31 @@ def cpu_baseline(stack, budget_s):
             y = np.concatenate(parts, axis=1)
             spent += dt
             sizes = stack.vbq.pack_query(widths)
+            if first is None:
+                first = (lay, x, rows, proj.k, sizes)
             done_bytes += algorithmic_bytes(sizes, rows, proj.k, B)
             done_w += rows * proj.k
             yg = stack.mats[(layer, pi)][2].cpu().numpy()[:, :rows].astype(np.float64)
             rel = float(np.linalg.norm(yg - y) / np.linalg.norm(y))
             worst = max(worst, rel)
             checked.append(f"{'lm_head' if layer < 0 else f'L{layer}.{proj.name}'}[{rows}x{proj.k}]")
+    # The same oracle on one thread (the calling one), over row slices of the
+    # first matrix, for about a tenth of the budget.
+    one_thread = None
+    if first is not None:
+        lay0, x0, rows0, k0, sizes0 = first
+        t0, n1 = time.perf_counter(), 0
+        for sl in np.array_split(np.arange(rows0, dtype=np.int64), 64):
+            q, s_, o, _ = oracle.unpack(lay0, rows=sl)
+            oracle.gemv(q, s_, o, x0)
+            n1 += len(sl)
+            if time.perf_counter() - t0 >= budget_s / 10:
+                break
+        dt1 = time.perf_counter() - t0
+        one_thread = dict(value=algorithmic_bytes(sizes0, rows0, k0, B) * n1 / rows0 / dt1 / 1e9, unit="GB/s",
+                          rows=n1, seconds=round(dt1, 2))
     return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=n_threads, kind="oracle",
+                one_thread=one_thread,
                 cpu=cpu_model(), threads="one oracle call per row slice on every core of the process's affinity",
                 sample=f"{len(checked)} matrices ({done_w / 1e6:.0f}M weights, batch {B}): "
                        + ", ".join(checked[:4]) + (" ..." if len(checked) > 4 else ""),
