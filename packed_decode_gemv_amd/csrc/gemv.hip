@@ -16,9 +16,12 @@
 // The inner sum never materialises weights: a code field is OR-ed into the
 // mantissa of an fp16 whose exponent makes the field's unit exactly 1, so the
 // fp16 value is bias + q with bias = 2^(10-p) for a field at mantissa bit p.
-// v_dot2_f32_f16 multiplies two such values by two activations at once. The
-// bias part, sum_j bias_j (x_2j + x_2j+1), depends only on x and the width,
-// so it is computed once per (k-group, width) and subtracted per record.
+// Four such values and their four activations go to the matrix cores as one
+// 16-block v_mfma_f32_4x4x4f16, whose result holds each lane's own
+// four-term dot product in one of its four registers (the VALU only builds
+// the operands). The bias part, sum_j bias_j (x_2j + x_2j+1), depends only on
+// x and the width, so it is computed once per (k-group, width) and
+// subtracted per record.
 //
 // Work split: the four wavefronts of a workgroup decode one tile (32 rows x
 // 64 k-groups) together; the steps are described at coop_tile. The tile's
@@ -115,32 +118,43 @@ __device__ inline uint32_t pair_h2(const Consts<C>& k, const uint32_t* w) {
   }
 }
 
-// acc[nb][P % 2] += (bias + q_2P) x_2P + (bias + q_2P+1) x_2P+1 for pair P of
-// the record (two accumulators split the dependent chain).
-template <int C, int NB, int... P>
-__device__ inline void record_dot(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32], float (&a)[NB][2],
-                                  std::integer_sequence<int, P...>) {
+// The multiply-accumulate of a record on the matrix cores: two code pairs
+// (four weights) and their four activations go to one 16-block
+// v_mfma_f32_4x4x4f16, whose block of lanes 4b..4b+3 multiplies the four
+// lanes' codes by the four lanes' activations: lane l's own four-term dot
+// product lands in register l % 4 of its result (the other registers hold
+// products with the other lanes' activations and are not used). Two
+// accumulators take the record's 16 MFMAs in turn.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline half4_t as_h4(uint32_t lo, uint32_t hi) {
+  u32x2 v;
+  v.x = lo;
+  v.y = hi;
+  return __builtin_bit_cast(half4_t, v);
+}
+
+template <int C, int NB, int H, int... Q>
+__device__ inline void record_mfma(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32],
+                                   f32x4_t (&acc)[NB][2], std::integer_sequence<int, Q...>) {
   (
       [&] {
-        const uint32_t hv = pair_h2<C, P>(k, w);
+        constexpr int P = H + 2 * Q;
+        const half4_t a = as_h4(pair_h2<C, P>(k, w), pair_h2<C, P + 1>(k, w));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) a[nb][P & 1] = dot2(hv, xr[nb][P], a[nb][P & 1]);
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb][Q & 1] =
+              __builtin_amdgcn_mfma_f32_4x4x4f16(a, as_h4(xr[nb][P], xr[nb][P + 1]), acc[nb][Q & 1], 0, 0, 0);
       }(),
       ...);
 }
 
-// The same for pairs 16..31 (activation registers indexed from the record's
-// pair 0, so the halves of one record share an array).
-template <int C, int NB, int... P>
-__device__ inline void record_dot_hi(const Consts<C>& k, const uint32_t* w, const uint32_t (&xr)[NB][32],
-                                     float (&a)[NB][2], std::integer_sequence<int, P...>) {
-  (
-      [&] {
-        const uint32_t hv = pair_h2<C, P + 16>(k, w);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) a[nb][P & 1] = dot2(hv, xr[nb][P + 16], a[nb][P & 1]);
-      }(),
-      ...);
+// Register l % 4 of v (the lane's own dot product of a record_mfma), picked
+// by the two low bits of the lane index.
+__device__ inline float own_dot(const f32x4_t& v, bool b0, bool b1) {
+  const float lo = b0 ? v.y : v.x, hi = b0 ? v.w : v.z;
+  return b1 ? hi : lo;
 }
 
 // sum over the record's pairs of bias(field) * (x_2P + x_2P+1).
@@ -385,13 +399,14 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
   // each code pair is decoded once and multiplied with every batch row's
   // activations (read in two halves, to bound the registers)
   const uint32_t* xs0 = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(S) + xoff);
-  float xsum[NB], a[NB][2];
+  float xsum[NB], a0[NB];
+  f32x4_t acc[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float* sums = reinterpret_cast<const float*>(xs0 + nb * kXWords) + kXSum;
     xsum[nb] = sums[0];
-    a[nb][0] = C == 3 ? -1024.f * xsum[nb] : sums[1 + C];
-    a[nb][1] = 0.f;
+    a0[nb] = C == 3 ? -1024.f * xsum[nb] : sums[1 + C];   // -bias: the dot ends as sum_k q_k x_k
+    acc[nb][0] = acc[nb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -406,11 +421,14 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
         xr[nb][16 * half + 4 * i + 2] = v.z;
         xr[nb][16 * half + 4 * i + 3] = v.w;
       }
-    if (half == 0) record_dot<C, NB>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
-    else record_dot_hi<C, NB>(k, r.w, xr, a, std::make_integer_sequence<int, 16>{});
+    if (half == 0) record_mfma<C, NB, 0>(k, r.w, xr, acc, std::make_integer_sequence<int, 8>{});
+    else record_mfma<C, NB, 16>(k, r.w, xr, acc, std::make_integer_sequence<int, 8>{});
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) slot[nb * kSlotWords] = __builtin_fmaf(s, a[nb][0] + a[nb][1], o * xsum[nb]);
+  for (int nb = 0; nb < NB; ++nb) {
+    const float dot = a0[nb] + own_dot(acc[nb][0] + acc[nb][1], (lane & 1u) != 0, (lane & 2u) != 0);
+    slot[nb * kSlotWords] = __builtin_fmaf(s, dot, o * xsum[nb]);
+  }
 }
 
 // Step 3 for class C: the chunks in flight are decoded in turn and each
