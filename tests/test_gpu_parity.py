@@ -67,10 +67,13 @@ def _field_bias(b):
 def gemv_bound(q, s16, o16, widths, x, resid=None, cell=None):
     """Worst-case rounding bound |y - y_exact| per output [B][N] of the
     library's fp32 GEMV, y = sum_g s_g (D_g - beta_g) + o_g X_g (+ residual):
-      - D_g = sum (bias_k + q_k) x_k and beta_g = sum bias_k x_k are four
-        chains of eight v_dot2 steps (exact fp16 products, at most two
-        roundings a step) and three adds: each within 19u of its sum of
-        magnitudes, so 40 u A with A = sum_g s_g sum_k (bias_k + q_k)|x_k|;
+      - D_g = sum (bias_k + q_k) x_k runs on the matrix cores: two chains of
+        eight 4x4x4 MFMA steps, each adding four exact fp16 products to an
+        fp32 accumulator (at most four roundings a step), and one add of the
+        chains: within 33u of its sum of magnitudes. beta_g = sum bias_k x_k
+        is four chains of eight v_dot2 steps (at most two roundings a step)
+        and three adds: within 19u. With the add of the two and the final
+        fma, 56 u A with A = sum_g s_g sum_k (bias_k + q_k)|x_k|;
       - X_g = sum x_k likewise: 20 u B with B = sum_g |o_g| sum_k |x_k|;
       - the record's fma and its add into the row: the row is a sum of at
         most G + 8 terms (a record per group, four wavefront slices), so
@@ -102,7 +105,7 @@ def gemv_bound(q, s16, o16, widths, x, resid=None, cell=None):
         s256 = s_full / 256.0
         w_full = w_full + s256 * fd
     C = xd @ np.abs(w_full).T
-    b = U * (40 * A + 20 * Bo + (G + 10) * C)
+    b = U * (56 * A + 20 * Bo + (G + 10) * C)
     if cell is not None:
         b = b + U * (40 * (xd @ (s256 * (2304.0 + fd)).T) + 23040 * (xd @ s256.T))
     if resid is not None:
