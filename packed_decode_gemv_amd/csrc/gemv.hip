@@ -203,7 +203,11 @@ constexpr int kMaxRecs = kTileRows * kTileGroups;         // 2048 table entries
 template <int NB>
 struct LdsMap {
   static constexpr int x = 0;                             // [NB][64][36] fp16 pairs and the column's sums
-  static constexpr int xbuf = NB * kXWords;               // words per activation buffer
+  // words from one batch row's activations to the next: with four rows a
+  // 16-byte skew puts the same column of the four rows on different banks
+  // (the four lanes of an MFMA block read one row each)
+  static constexpr int xrow = NB >= 4 ? kXWords + 4 : kXWords;
+  static constexpr int xbuf = NB * xrow;                  // words per activation buffer
   static constexpr int table = x + xbuf;                  // [2048] u32: slot byte << 16 | column byte (from S)
   static constexpr int slots = table + kMaxRecs;          // [NB][64][33]
   static constexpr int ys = slots + NB * kSlotWords;      // [NB][32] residual row sums
@@ -224,13 +228,17 @@ template <int C>
 struct Rec {
   uint32_t w[2 << C];
   uint32_t so;
+  uint32_t ent;   // four-row passes: the record's quad entry
 };
 
 // Chunks of a class each wavefront has in flight: issued at the tile's start
 // and refilled while the class is decoded.
 template <int C, int NB>
 __host__ __device__ constexpr int depth() {
-  return C == 0 ? (NB >= 4 ? 1 : 4 / NB) : C == 1 ? (NB >= 2 ? 1 : 2) : 1;   // at least one
+  // (four-row passes hold one row's activations per lane, so they afford the
+  // one-row depths)
+  return NB == 4 ? (C == 0 ? 4 : C == 1 ? 2 : 1)
+                 : C == 0 ? (NB >= 4 ? 1 : 4 / NB) : C == 1 ? (NB >= 2 ? 1 : 2) : 1;   // at least one
 }
 
 struct TileRef {
@@ -342,6 +350,53 @@ __host__ __device__ constexpr uint32_t spare_entry() {
   return ((4u * (LdsMap<NB>::slots + 31 * kSlotPitch + 32)) << 16) | (4u * (LdsMap<NB>::x + 31 * kXPitch));
 }
 
+// ---- Four batch rows: record quads ----------------------------------------------
+// A pass of four batch rows puts the rows in the four B columns of the 4x4x4
+// MFMA: lane c of a block supplies batch row c's activations, and the block's
+// result holds the dot products of its four lanes' records with all four rows
+// (register q of lane c: the record of lane 4 (l / 4) + q with batch row c).
+// The four records of a block must then share a column (a k-group), so in
+// such a pass the records of a class are taken column by column in quads:
+// each column's records of the class in row order, padded with empty entries
+// to a multiple of four. Lane p of chunk j takes padded entry 64 j + p. The
+// record table holds the padded entries (u16: valid << 15 | column << 5 |
+// row); a record's index in the class, and with it its position in the
+// stream, is the number of the class's records in the columns before it plus
+// its rank among its column's rows.
+constexpr uint32_t kQuadPad = 3 * kTileGroups;          // padding entries of a class at most
+constexpr uint32_t kQuadTab = kMaxRecs + 4 * kQuadPad;  // 2816 entries
+struct QuadMap {   // words from LdsMap<4>::table
+  static constexpr int tab = 0;                          // u16 [2816]
+  static constexpr int masks = kQuadTab / 2;             // u32 [4][64]: each class's rows per column
+  static constexpr int pre = masks + 4 * kTileGroups;    // u16 [4][64]: the class's records in the columns before
+  static constexpr int cnt = pre + 2 * kTileGroups;      // u32 [4]: padded entries per class
+  static constexpr int words = cnt + 4;
+};
+static_assert(QuadMap::words <= kMaxRecs, "record quads fit the record table");
+
+// First padded entry of class c: worst-case regions, so that every wavefront
+// places them from the tile header alone.
+__device__ inline uint32_t quad_base(const TileRef& t, int c) {
+  return (c > 0 ? t.n[0] + kQuadPad : 0u) + (c > 1 ? t.n[1] + kQuadPad : 0u) + (c > 2 ? t.n[2] + kQuadPad : 0u);
+}
+
+// The padded entries, row masks and record counts of class c; lane l on
+// column l.
+__device__ inline void quad_class(const TileRef& t, int c, uint32_t p0, uint32_t p1, uint32_t valid, uint32_t* S,
+                                  uint32_t lane) {
+  const uint32_t mask = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
+  const uint32_t n = (uint32_t)__builtin_popcount(mask), np = (n + 3u) & ~3u;
+  const uint32_t pre = wave_excl_scan(n, lane), ppre = wave_excl_scan(np, lane);
+  uint32_t* Q = S + LdsMap<4>::table;
+  Q[QuadMap::masks + c * kTileGroups + lane] = mask;
+  reinterpret_cast<uint16_t*>(Q + QuadMap::pre)[c * kTileGroups + lane] = (uint16_t)pre;
+  if (lane == 63u) Q[QuadMap::cnt + c] = ppre + np;
+  uint16_t* tab = reinterpret_cast<uint16_t*>(Q + QuadMap::tab) + quad_base(t, c) + ppre;
+  uint32_t m = mask, k = 0;
+  for (; m; m &= m - 1u, ++k) tab[k] = (uint16_t)(0x8000u | (lane << 5) | (uint32_t)__builtin_ctz(m));
+  for (; k < np; ++k) tab[k] = (uint16_t)(lane << 5);
+}
+
 // Step 2.
 template <int NB>
 __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, uint32_t* S, uint32_t lane, int buf) {
@@ -353,7 +408,8 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t xr[1][32];
-      const uint32_t* xs = S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords + lane * (uint32_t)kXPitch;
+      const uint32_t* xs =
+          S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * LdsMap<NB>::xrow + lane * (uint32_t)kXPitch;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
@@ -369,7 +425,7 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
       float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < 32; ++p) a[p & 3] = dot2(xr[0][p], 0x3C003C00u, a[p & 3]);
-      float* sums = reinterpret_cast<float*>(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords +
+      float* sums = reinterpret_cast<float*>(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * LdsMap<NB>::xrow +
                                              lane * (uint32_t)kXPitch + kXSum);
       *reinterpret_cast<float4*>(sums) = make_float4((a[0] + a[1]) + (a[2] + a[3]), -b[0][0], -b[1][0], -b[2][0]);
     }
@@ -377,8 +433,13 @@ __device__ inline void tile_prepare(const TileRef& t, int wave, const u32x2 mp, 
     const bool live = (int)lane < t.Gt;
     const uint32_t p0 = live ? mp.x : 0u, p1 = live ? mp.y : 0u;
     const uint32_t valid = !live ? 0u : t.R >= 32 ? 0xFFFFFFFFu : ((1u << t.R) - 1u);
-    table_class<NB>(t, wave - 1, p0, p1, valid, S, lane, buf);
-    if (wave == 3) table_class<NB>(t, 3, p0, p1, valid, S, lane, buf);
+    if constexpr (NB == 4) {
+      quad_class(t, wave - 1, p0, p1, valid, S, lane);
+      if (wave == 3) quad_class(t, 3, p0, p1, valid, S, lane);
+    } else {
+      table_class<NB>(t, wave - 1, p0, p1, valid, S, lane, buf);
+      if (wave == 3) table_class<NB>(t, 3, p0, p1, valid, S, lane, buf);
+    }
   }
 }
 
@@ -403,7 +464,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
   f32x4_t acc[NB][2];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float* sums = reinterpret_cast<const float*>(xs0 + nb * kXWords) + kXSum;
+    const float* sums = reinterpret_cast<const float*>(xs0 + nb * LdsMap<NB>::xrow) + kXSum;
     xsum[nb] = sums[0];
     a0[nb] = C == 3 ? -1024.f * xsum[nb] : sums[1 + C];   // -bias: the dot ends as sum_k q_k x_k
     acc[nb][0] = acc[nb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -415,7 +476,7 @@ __device__ inline void decode_chunk(const Consts<C>& k, const Rec<C>& r, const T
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xs0 + nb * kXWords + 16 * half + 4 * i);
+        const uint4 v = *reinterpret_cast<const uint4*>(xs0 + nb * LdsMap<NB>::xrow + 16 * half + 4 * i);
         xr[nb][16 * half + 4 * i + 0] = v.x;
         xr[nb][16 * half + 4 * i + 1] = v.y;
         xr[nb][16 * half + 4 * i + 2] = v.z;
@@ -447,6 +508,123 @@ __device__ inline void run_class(const TileRef& t, Flight<C, NB>& f, uint32_t* S
       decode_chunk<C, NB, CELL>(k, f.r[d], t, (uint32_t)wave + kGemvWaves * sq, S, lane);
       const uint32_t sn = sq + D;
       if (sn < nS) issue_chunk<C>(t, (uint32_t)wave + kGemvWaves * sn, f.r[d], lane);
+    }
+  }
+}
+
+// Issues the loads of the record of padded entry 64 j + lane of class C (a
+// four-row pass); empty entries and lanes past the class load from
+// kNoRecord. The entry is kept with the record for the decode.
+template <int C>
+__device__ inline void issue_quad(const TileRef& t, uint32_t j, uint32_t cnt, Rec<C>& r, const uint32_t* S,
+                                  uint32_t lane) {
+  constexpr uint32_t RB = 8u << C;
+  const uint32_t p = 64u * j + lane;
+  const uint32_t* Q = S + LdsMap<4>::table;
+  const uint32_t ent = p < cnt ? (uint32_t)reinterpret_cast<const uint16_t*>(Q + QuadMap::tab)[quad_base(t, C) + p] : 0u;
+  uint32_t oc = kNoRecord, os = kNoRecord;
+  if (ent & 0x8000u) {
+    const uint32_t col = (ent >> 5) & 63u, row = ent & 31u;
+    const uint32_t mask = Q[QuadMap::masks + C * kTileGroups + col];
+    const uint32_t e = (uint32_t)reinterpret_cast<const uint16_t*>(Q + QuadMap::pre)[C * kTileGroups + col] +
+                       (uint32_t)__builtin_popcount(mask & ((1u << row) - 1u));
+    const RecPos rp = record_pos(C, t.n[C], t.cb[C], e);
+    oc = t.base + rp.codes;
+    os = t.base + rp.so;
+  }
+  r.ent = ent;
+  if constexpr (C == 0) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(t.rs, (int)oc, 0, 0);
+    r.w[0] = u.x;
+    r.w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < (int)RB / 16; ++h) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(t.rs, (int)(oc + 16u * h), 0, 0);
+      r.w[4 * h + 0] = u.x;
+      r.w[4 * h + 1] = u.y;
+      r.w[4 * h + 2] = u.z;
+      r.w[4 * h + 3] = u.w;
+    }
+  }
+  r.so = __builtin_amdgcn_raw_buffer_load_b32(t.rs, (int)os, 0, 0);
+}
+
+// v of lane 4 (l / 4) + q (a quad broadcast).
+template <int Q>
+__device__ inline uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, Q | (Q << 2) | (Q << 4) | (Q << 6), 0xF, 0xF, false);
+}
+
+// Decodes the record of lane l against batch row l % 4 of its quad's column
+// and writes the slots of the quad's records for that row: slot (column, row
+// of the record of lane 4 (l / 4) + q) of batch row l % 4 gets
+// s_q (dot_q - bias) + o_q sum(x), with the same operations in the same order
+// as a single-row pass.
+template <int C>
+__device__ inline void decode_quad(const Consts<C>& k, const Rec<C>& r, uint32_t* S, uint32_t lane) {
+  const uint32_t c = lane & 3u;
+  const uint32_t col = (r.ent >> 5) & 63u;   // the quad's column (empty entries carry it too)
+  const uint32_t* xs0 = S + LdsMap<4>::x + c * LdsMap<4>::xrow + col * kXPitch;
+  const float* sums = reinterpret_cast<const float*>(xs0) + kXSum;
+  const float xsum = sums[0];
+  const float a0 = C == 3 ? -1024.f * xsum : sums[1 + C];
+  f32x4_t acc[1][2];
+  acc[0][0] = acc[0][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t xr[1][32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xs0 + 16 * half + 4 * i);
+      xr[0][16 * half + 4 * i + 0] = v.x;
+      xr[0][16 * half + 4 * i + 1] = v.y;
+      xr[0][16 * half + 4 * i + 2] = v.z;
+      xr[0][16 * half + 4 * i + 3] = v.w;
+    }
+    if (half == 0) record_mfma<C, 1, 0>(k, r.w, xr, acc, std::make_integer_sequence<int, 8>{});
+    else record_mfma<C, 1, 16>(k, r.w, xr, acc, std::make_integer_sequence<int, 8>{});
+  }
+  const f32x4_t d = acc[0][0] + acc[0][1];
+  float* slot = reinterpret_cast<float*>(S + LdsMap<4>::slots) + c * kSlotWords + col * kSlotPitch;
+  const uint32_t e[4] = {quad_bcast<0>(r.ent), quad_bcast<1>(r.ent), quad_bcast<2>(r.ent), quad_bcast<3>(r.ent)};
+  const uint32_t so[4] = {quad_bcast<0>(r.so), quad_bcast<1>(r.so), quad_bcast<2>(r.so), quad_bcast<3>(r.so)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (e[q] & 0x8000u) {
+      const float s = __half2float(__ushort_as_half((unsigned short)(so[q] & 0xFFFFu)));
+      const float o = __half2float(__ushort_as_half((unsigned short)(so[q] >> 16)));
+      const float dot = a0 + d[q];
+      slot[e[q] & 31u] = __builtin_fmaf(s, dot, o * xsum);
+    }
+  }
+}
+
+template <int C>
+__device__ inline void issue_first_quad(const TileRef& t, int wave, Flight<C, 4>& f, uint32_t cnt, const uint32_t* S,
+                                        uint32_t lane) {
+  const uint32_t nS = wave_chunks(cnt, wave);
+#pragma unroll
+  for (int d = 0; d < depth<C, 4>(); ++d)
+    issue_quad<C>(t, (uint32_t)d < nS ? (uint32_t)wave + kGemvWaves * d : 0x3FFFFFFu, cnt, f.r[d], S, lane);
+}
+
+// Step 3 of a four-row pass for class C.
+template <int C>
+__device__ inline void run_class_quad(const TileRef& t, Flight<C, 4>& f, uint32_t cnt, uint32_t* S, int wave,
+                                      uint32_t lane) {
+  constexpr int D = depth<C, 4>();
+  const uint32_t nS = wave_chunks(cnt, wave);
+  if (nS == 0) return;
+  const Consts<C> k = make_consts<C>();
+  for (uint32_t s0 = 0; s0 < nS; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const uint32_t sq = s0 + d;
+      if (sq >= nS) break;
+      decode_quad<C>(k, f.r[d], S, lane);
+      const uint32_t sn = sq + D;
+      if (sn < nS) issue_quad<C>(t, (uint32_t)wave + kGemvWaves * sn, cnt, f.r[d], S, lane);
     }
   }
 }
@@ -535,7 +713,7 @@ __device__ inline void cell_dots(const CellRows& c, CellFlight<NB>& f, uint32_t*
   float base[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t* xs = S + LdsMap<NB>::x + nb * kXWords + lane * (uint32_t)kXPitch;
+    const uint32_t* xs = S + LdsMap<NB>::x + nb * LdsMap<NB>::xrow + lane * (uint32_t)kXPitch;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 v = *reinterpret_cast<const uint4*>(xs + 4 * i);
@@ -610,7 +788,7 @@ __device__ inline void copy_x(const GemvMat& T, int kt, uint32_t* S, uint32_t la
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const u32x4 xrs = make_rsrc(T.x + nb * K, (uint32_t)(K * 2));
-    const uint32_t lds = lds_addr(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * kXWords);
+    const uint32_t lds = lds_addr(S + LdsMap<NB>::x + buf * LdsMap<NB>::xbuf + nb * LdsMap<NB>::xrow);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       // (the empty asm keeps the compiler from hoisting these lane-only
@@ -646,6 +824,36 @@ __device__ inline void tile_start(const GemvMat& T, const TileRef& t, uint32_t* 
 template <int NB, bool CELL>
 __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, int wave, float (&yacc)[NB],
                                  uint32_t lane) {
+  if constexpr (NB == 4 && !CELL) {
+    // Four batch rows: the records go in quads (see issue_quad); their loads
+    // follow the record table, so they go out after the first barrier.
+    TileRef t;
+    Flight<0, 4> f0;
+    Flight<1, 4> f1;
+    Flight<2, 4> f2;
+    Flight<3, 4> f3;
+    if (wave == 0) copy_x<4>(T, kt, S, lane, 0);
+    t = tile_ref(T, rt, kt);
+    const u32x2 mp = map_load(t, lane);
+    tile_prepare<4>(t, wave, mp, S, lane, 0);
+    __syncthreads();
+    const uint32_t* Q = S + LdsMap<4>::table;
+    const uint32_t c0 = __builtin_amdgcn_readfirstlane(Q[QuadMap::cnt + 0]);
+    const uint32_t c1 = __builtin_amdgcn_readfirstlane(Q[QuadMap::cnt + 1]);
+    const uint32_t c2 = __builtin_amdgcn_readfirstlane(Q[QuadMap::cnt + 2]);
+    const uint32_t c3 = __builtin_amdgcn_readfirstlane(Q[QuadMap::cnt + 3]);
+    issue_first_quad<0>(t, wave, f0, c0, S, lane);
+    issue_first_quad<1>(t, wave, f1, c1, S, lane);
+    issue_first_quad<2>(t, wave, f2, c2, S, lane);
+    issue_first_quad<3>(t, wave, f3, c3, S, lane);
+    run_class_quad<0>(t, f0, c0, S, wave, lane);
+    run_class_quad<1>(t, f1, c1, S, wave, lane);
+    run_class_quad<2>(t, f2, c2, S, wave, lane);
+    run_class_quad<3>(t, f3, c3, S, wave, lane);
+    __syncthreads();
+    fold_rows<4>(S, wave, yacc, lane);
+    return;
+  }
   const bool cell_wave = CELL && wave >= kGemvWaves;
   TileRef t;
   Flight<0, NB> f0;
