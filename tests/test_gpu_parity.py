@@ -180,7 +180,9 @@ def test_single_width_with_constant_groups(vbq, width):
     """Every group of one width, so that class's full and partial blocks make
     up the whole stream, and rows past a tile (N = 37); three constant groups
     have scale 0, so every weight there equals the offset (one is all zero).
-    Layout bit-exact; GEMV and GEMM within tolerance of the oracle."""
+    Layout bit-exact; GEMV (batch 2, and 5: a four-row pass and a one-row
+    pass, each row equal to its single-row call) and GEMM within tolerance
+    of the oracle."""
     import torch
     from test_gpu_gemm import check_gemm
     N, K, B = 37, 64 * 9, 2
@@ -199,6 +201,15 @@ def test_single_width_with_constant_groups(vbq, width):
     ref = check_gemv(y, q, s, o, widths, x)
     for b in range(B):
         assert rel_l2(y[b], ref[b]) <= TOL
+    # a pass of four rows (records of the one class taken per column in
+    # quads) and one of a single row: within the bound, and every batch row
+    # the same bits as a single-row call
+    x5 = r.standard_normal((5, K)).astype(np.float16).view(np.uint16)
+    y5 = vbq.vbq_gemv(pm, _t(x5, torch.float16))
+    check_gemv(y5.cpu().numpy(), q, s, o, widths, x5)
+    for b in range(5):
+        yb = vbq.vbq_gemv(pm, _t(x5[b:b + 1], torch.float16))
+        assert torch.equal(y5[b:b + 1], yb), f"width {width}: batch row {b} differs from its single-row call"
     xb = synth.x_bf16(7, (width,), 70, K)
     yg = vbq.vbq_gemm(pm, _t(xb, torch.bfloat16)).cpu().numpy()
     check_gemm(yg, q, s, o, xb)
