@@ -67,7 +67,7 @@ constexpr int kXRow = kGroup * 2;     // bytes of one token's x per group
 
 struct GemmSmem {
   uint2 ent[kTileGroups][kBN];        // per k-group: {offset/8 | row << 17 | class << 24, scale|offset}
-  uint32_t cnt[kTileGroups][4];       // records per (k-group, class), then placement cursors
+  uint32_t cnt[kRowTilesPerWg][kTileGroups][4];   // records per (row-tile, k-group, class)
   __bf16 ws[2][kBN][kStride];         // decoded weights, double-buffered
   uint8_t xs[kXSlots][kBM * kXRow];   // x rows of 128 bytes, 16-byte columns swizzled
 };
@@ -88,16 +88,20 @@ __device__ inline void gemm_barrier() {
 // Builds the per-k-group record lists of k-tile kt for row-tiles
 // [rt0, rt0 + nrt). Code offsets are relative to the first byte of tile
 // (kt, rt0) (the two tiles are consecutive in the stream).
-//   1. wavefront r < nrt reads the map of tile (kt, rt0 + r), lane l on
-//      column l, and adds its per-class row counts to cnt[l][class];
-//   2. counts become list starts per k-group in class order 8, 1, 2, 4-bit;
+//   1. wavefront r < 2 reads the map of tile (kt, rt0 + r) (none past nrt),
+//      lane l on column l, and writes its per-class row counts to
+//      cnt[r][l][class];
+//   2. each of those wavefronts forms, for its lane's k-group, where its
+//      records of each class start in the group's list: class order 8, 1,
+//      2, 4-bit, and within a class row-tile 0's records before row-tile
+//      1's. No list position depends on another wavefront's progress, so the
+//      placement needs no atomics and the lists come out the same every call;
 //   3. the same wavefronts walk their tile's blocks and place every record
 //      (codes offset, row, class; the scale/offset's stream offset for now);
 //   4. every thread loads the scale/offset words of eight list entries, all
 //      at once, and writes them into the entries.
 __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs& a, GemmSmem& S, int kt, int rt0, int nrt,
                                                                   uint32_t base16, int tid) {
-  for (int i = tid; i < kTileGroups * 4; i += kThreads) (&S.cnt[0][0])[i] = 0;
   const int wave = tid >> 6, lane = tid & 63;
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, a.G - g0);
   const bool mine = wave < nrt;
@@ -115,38 +119,34 @@ __device__ __attribute__((always_inline)) inline void build_index(const GemmArgs
                           : make_uint2(0u, 0u);
     km = class_masks(mp.x, mp.y, live ? R : 0);
   }
-  gemm_barrier();   // counters zeroed
-  if (live)
+  if (wave < kRowTilesPerWg)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (km.m[c]) atomicAdd(&S.cnt[lane][c], (uint32_t)__popc(km.m[c]));
-  gemm_barrier();
-  if (tid < kTileGroups) {
+    for (int c = 0; c < 4; ++c) S.cnt[wave][lane][c] = (uint32_t)__popc(km.m[c]);
+  gemm_barrier();   // per-wavefront counts written
+  if (mine) {
     // Class order in a k-group's list: 8-bit, 1-bit, 2-bit, 4-bit. Producer
     // wavefronts take 32 consecutive entries each and run one decode path
     // per class they hold, so the short classes are kept apart: with the
     // usual mixes (mostly 1-bit) no wavefront holds more than two classes.
     constexpr int kOrder[4] = {3, 0, 1, 2};
-    uint32_t sum = 0;
+    uint32_t start[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t v = S.cnt[tid][kOrder[i]];
-      S.cnt[tid][kOrder[i]] = sum;
-      sum += v;
+      const int c = kOrder[i];
+      const uint32_t n0 = S.cnt[0][lane][c], n1 = S.cnt[1][lane][c];
+      start[c] = sum + (wave == 1 ? n0 : 0u);
+      sum += n0 + n1;
     }
-  }
-  gemm_barrier();
-  if (mine) {
     uint32_t cbase = tbase + map_bytes((uint32_t)Gt);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t n = class_count(w2, w3, c);
       uint32_t mask = km.m[c];
       uint32_t e = wave_excl_scan((uint32_t)__popc(mask), (uint32_t)lane);
-      for (; mask; mask &= mask - 1u, ++e) {
+      uint32_t slot = start[c];
+      for (; mask; mask &= mask - 1u, ++e, ++slot) {
         const uint32_t row = (uint32_t)wave * kTileRows + (uint32_t)__builtin_ctz(mask);
         const RecPos rp = record_pos(c, n, cbase, e);
-        const uint32_t slot = atomicAdd(&S.cnt[lane][c], 1u);
         S.ent[lane][slot] = make_uint2((rp.codes >> 3) | (row << 17) | ((uint32_t)c << 24), rp.so);
       }
       cbase += class_bytes(c, n);
@@ -353,6 +353,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
   for (int kt = 0; kt < KT; ++kt) {
     const int g0 = kt * kTileGroups, g1 = min(a.G, g0 + kTileGroups);
     const uint32_t base16 = a.tiles[4 * (size_t)(kt * a.RT + rt0) + 0];
+    // The consumers' copies of x for the k-tile's first two groups need no
+    // record list, so they go out before the lists are built (every x slot
+    // is free here: the previous k-tile ended with a barrier after its last
+    // reads).
+    if (!producer) {
+      copy_x(a, xrsrc, xs_lds + (uint32_t)(g0 % kXSlots) * kBM * kXRow, m0, xr0, g0, lane);
+      copy_x(a, xrsrc, xs_lds + (uint32_t)((g0 + 1) % kXSlots) * kBM * kXRow, m0, xr0, min(g0 + 1, g1 - 1),
+             lane);
+    }
     build_index(a, S, kt, rt0, nrt, base16, tid);
     // The two roles run loops of their own with the same barrier schedule:
     // in one shared loop body the compiler merges their load-count state and
@@ -383,9 +392,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs a) {
         step(g + 3, st3, st0);
       }
     } else {
-      copy_x(a, xrsrc, xs_lds + (uint32_t)(g0 % kXSlots) * kBM * kXRow, m0, xr0, g0, lane);
-      copy_x(a, xrsrc, xs_lds + (uint32_t)((g0 + 1) % kXSlots) * kBM * kXRow, m0, xr0, min(g0 + 1, g1 - 1),
-             lane);
       __builtin_amdgcn_s_waitcnt(VBQ_VMCNT_IMM(kXCopies));   // group g0 landed
       gemm_barrier();
       auto step = [&](int g) {

@@ -345,85 +345,133 @@ __device__ inline uint32_t cell8_value(uint32_t byte, float s) {
   return h & 0xFFFFu;
 }
 
-template <bool ENCODE>
-__device__ inline void cell8_record(float s, const void* in, void* out) {
-  if constexpr (ENCODE) {
-    const uint4* rp = reinterpret_cast<const uint4*>(in);
-    uint4* fp = reinterpret_cast<uint4*>(out);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 a = rp[2 * q], b = rp[2 * q + 1];
-      const uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = cell8_code(h[2 * i] & 0xFFFFu, s) | (cell8_code(h[2 * i] >> 16, s) << 8) |
-               (cell8_code(h[2 * i + 1] & 0xFFFFu, s) << 16) | (cell8_code(h[2 * i + 1] >> 16, s) << 24);
-      fp[q] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  } else {
-    const uint4* fp = reinterpret_cast<const uint4*>(in);
-    uint4* rp = reinterpret_cast<uint4*>(out);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = fp[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[2 * i] = cell8_value(w[i] & 0xFFu, s) | (cell8_value((w[i] >> 8) & 0xFFu, s) << 16);
-        h[2 * i + 1] = cell8_value((w[i] >> 16) & 0xFFu, s) | (cell8_value(w[i] >> 24, s) << 16);
-      }
-      rp[2 * q] = make_uint4(h[0], h[1], h[2], h[3]);
-      rp[2 * q + 1] = make_uint4(h[4], h[5], h[6], h[7]);
-    }
-  }
-}
-
 // ENCODE: in = fp16 residual [N][K], out = int8 [N][K]; else the reverse.
+// Rows are taken in order: a wavefront takes one row of a tile at a time, and
+// piece i of lane l is weights 8 (l % 8) .. + 7 of the record of column
+// 8 i + l / 8, i.e. the 8 * (64 i + l)-th weight of the row's stretch, so
+// consecutive lanes read and write consecutive bytes. A record's index in its
+// class follows from the map planes (the class's records in the columns
+// before, kept in LDS, plus the row's rank in its column). Workgroups of four
+// wavefronts take kCell8RowsPerWg rows of a tile each. Every weight is
+// converted on its own with its record's scale, so the order changes no
+// result.
+constexpr int kCell8Waves = 4;
+constexpr int kCell8RowsPerWg = 8;
+
+struct Cell8Cols {
+  uint32_t p0[kTileGroups], p1[kTileGroups];
+  uint16_t pre[4][kTileGroups];
+};
+
 template <bool ENCODE>
-__global__ __launch_bounds__(64) void k_cell8(const uint32_t* __restrict__ tiles, const uint8_t* __restrict__ stream,
-                                              int N, int G, int RT, const void* in, void* out) {
-  const int t = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(kCell8Waves * 64) void k_cell8(const uint32_t* __restrict__ tiles,
+                                                            const uint8_t* __restrict__ stream, int N, int G, int RT,
+                                                            const void* in, void* out) {
+  __shared__ Cell8Cols cols;
+  constexpr int kParts = kTileRows / kCell8RowsPerWg;
+  const int t = (int)blockIdx.x / kParts, part = (int)blockIdx.x % kParts;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kt = t / RT, rt = t - kt * RT;
   const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
   const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
   const size_t K = (size_t)G * kGroup;
   const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
   const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
-  const bool live = lane < Gt;
-  const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
-  const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
-  constexpr size_t kIn = ENCODE ? 2 : 1, kOut = ENCODE ? 1 : 2;   // bytes per weight
+  if (wave == 0) {
+    const bool live = lane < Gt;
+    const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
+    const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
+    cols.p0[lane] = mp.x;
+    cols.p1[lane] = mp.y;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      cols.pre[c][lane] = (uint16_t)wave_excl_scan((uint32_t)__builtin_popcount(km.m[c]), (uint32_t)lane);
+  }
+  uint32_t n[4], cb[4];
   uint32_t cbase = map_bytes((uint32_t)Gt);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t n = class_count(w2, w3, c);
-    uint32_t mask = km.m[c];
-    uint32_t e = wave_excl_scan((uint32_t)__builtin_popcount(mask), (uint32_t)lane);
-    for (; mask; mask &= mask - 1u, ++e) {
-      const int row = __builtin_ctz(mask);
-      const RecPos rp = record_pos(c, n, cbase, e);
-      const size_t at = (size_t)(r0 + row) * K + (size_t)(g0 + lane) * kGroup;
-      const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + rp.so);
-      const float sc = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
-      cell8_record<ENCODE>(sc, reinterpret_cast<const uint8_t*>(in) + at * kIn,
-                           reinterpret_cast<uint8_t*>(out) + at * kOut);
+    n[c] = class_count(w2, w3, c);
+    cb[c] = cbase;
+    cbase += class_bytes(c, n[c]);
+  }
+  __syncthreads();
+  const uint32_t valid = R >= 32 ? 0xFFFFFFFFu : ((1u << R) - 1u);
+  for (int rr = wave; rr < kCell8RowsPerWg; rr += kCell8Waves) {
+    const int row = part * kCell8RowsPerWg + rr;
+    if (row >= R) break;
+    const size_t at = (size_t)(r0 + row) * K + (size_t)g0 * kGroup;   // the row's first weight of the tile
+    uint32_t so[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * i + (lane >> 3);
+      so[i] = 0u;
+      if (g < Gt) {
+        const uint32_t p0 = cols.p0[g], p1 = cols.p1[g];
+        const int c = (int)((p0 >> row) & 1u) | (int)(((p1 >> row) & 1u) << 1);
+        const uint32_t mc = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
+        const uint32_t e = (uint32_t)cols.pre[c][g] + (uint32_t)__builtin_popcount(mc & ((1u << row) - 1u));
+        const uint32_t nc = c == 0 ? n[0] : c == 1 ? n[1] : c == 2 ? n[2] : n[3];
+        const uint32_t bc = c == 0 ? cb[0] : c == 1 ? cb[1] : c == 2 ? cb[2] : cb[3];
+        so[i] = *reinterpret_cast<const uint32_t*>(tb + record_pos(c, nc, bc, e).so);
+      }
     }
-    cbase += class_bytes(c, n);
+    if constexpr (ENCODE) {
+      const uint4* rp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(in) + at);
+      uint2* fp = reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(out) + at);
+      uint4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 8 * i + (lane >> 3) < Gt ? rp[64 * i + lane] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (8 * i + (lane >> 3) >= Gt) continue;
+        const float sc = __half2float(__ushort_as_half((unsigned short)(so[i] & 0xFFFFu)));
+        const uint32_t h[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t o[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          o[j] = cell8_code(h[2 * j] & 0xFFFFu, sc) | (cell8_code(h[2 * j] >> 16, sc) << 8) |
+                 (cell8_code(h[2 * j + 1] & 0xFFFFu, sc) << 16) | (cell8_code(h[2 * j + 1] >> 16, sc) << 24);
+        fp[64 * i + lane] = make_uint2(o[0], o[1]);
+      }
+    } else {
+      const uint2* fp = reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(in) + at);
+      uint4* rp = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + at);
+      uint2 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 8 * i + (lane >> 3) < Gt ? fp[64 * i + lane] : make_uint2(0u, 0u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (8 * i + (lane >> 3) >= Gt) continue;
+        const float sc = __half2float(__ushort_as_half((unsigned short)(so[i] & 0xFFFFu)));
+        const uint32_t w[2] = {v[i].x, v[i].y};
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          h[2 * j] = cell8_value(w[j] & 0xFFu, sc) | (cell8_value((w[j] >> 8) & 0xFFu, sc) << 16);
+          h[2 * j + 1] = cell8_value((w[j] >> 16) & 0xFFu, sc) | (cell8_value(w[j] >> 24, sc) << 16);
+        }
+        rp[64 * i + lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      }
+    }
   }
 }
 
 hipError_t launch_cell8_encode(const vbq_matrix& m, const uint16_t* r16, int8_t* f, hipStream_t s) {
   const int G = m.n_cols / kGroup, RT = row_tiles(m.n_rows);
-  hipLaunchKernelGGL(k_cell8<true>, dim3((unsigned)m.n_tiles), dim3(64), 0, s, m.tiles,
+  constexpr int64_t kParts = kTileRows / kCell8RowsPerWg;
+  if (m.n_tiles * kParts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cell8<true>, dim3((unsigned)(m.n_tiles * kParts)), dim3(kCell8Waves * 64), 0, s, m.tiles,
                      reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, G, RT, (const void*)r16, (void*)f);
   return hipGetLastError();
 }
 
 hipError_t launch_cell8_decode(const vbq_matrix& m, const int8_t* f, uint16_t* r16, hipStream_t s) {
   const int G = m.n_cols / kGroup, RT = row_tiles(m.n_rows);
-  hipLaunchKernelGGL(k_cell8<false>, dim3((unsigned)m.n_tiles), dim3(64), 0, s, m.tiles,
+  constexpr int64_t kParts = kTileRows / kCell8RowsPerWg;
+  if (m.n_tiles * kParts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cell8<false>, dim3((unsigned)(m.n_tiles * kParts)), dim3(kCell8Waves * 64), 0, s, m.tiles,
                      reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, G, RT, (const void*)f, (void*)r16);
   return hipGetLastError();
 }

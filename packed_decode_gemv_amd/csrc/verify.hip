@@ -134,12 +134,53 @@ __device__ __attribute__((noinline)) QuarterResult quarter_exact(uint4 w4, uint4
 // w = the record's 2b code words, rv = its 64 residuals (32 pairs), lin0 =
 // linear index of its first weight. Counts, first failing index and the
 // re-quantised words (nw) are accumulated into the lane's state.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest |r| (fp16 bits) that provably keeps every code of a record with a
+// finite scale s > 0, offset o and L = 2^b - 1, plus one: 0 when none does.
+// With a = ((f32(s q) + o) + r) - o and t = a / s (three roundings and a
+// correctly rounded quotient, unit roundoff u = 2^-24) the rounding errors
+// add at most u (4 s (L + 1) + 2 |o|) to |t - q| s, so
+//   |r| < 0.5 s - 2^-19 (s (L + 2) + |o|)
+// gives |t - q| < 0.5: rint(t) = q (inside [0, L], so the clamp keeps it) and
+// |r| < s / 2. The threshold is computed in binary32 (its own roundings are
+// far inside the eightfold slack of 2^-19 over 4u) and rounded down to fp16.
+__device__ inline uint32_t keep_bound_bits(float s, float o, int L) {
+  if (!(s > 0.0f && s <= 65504.0f)) return 0u;
+  const float thr = 0.5f * s - 0x1p-19f * (s * (float)(L + 2) + fabsf(o));
+  if (!(thr > 0.0f)) return 0u;
+  uint32_t h = __half_as_ushort(__float2half(thr));
+  if (__half2float(__ushort_as_half((unsigned short)h)) > thr) --h;   // round down (h >= 1 here)
+  return h;
+}
+
 template <int C>
 __device__ inline void check_record(const uint32_t* w, const uint4 (&rv)[8], uint32_t so, uint64_t lin0,
                                     uint32_t& mism, uint32_t& ooc, uint64_t& first, uint32_t* nw) {
   constexpr int B = 1 << C, H = 16 / B, NWORD = 2 * B;
   const float s = __half2float(__ushort_as_half((unsigned short)(so & 0xFFFF)));
   const float o = __half2float(__ushort_as_half((unsigned short)(so >> 16)));
+  // The common case: every |r| of the record under the bound above, so every
+  // code comes back unchanged and every residual is inside its cell. The
+  // largest |r| is taken on the fp16 bit patterns (sign cleared; the
+  // patterns of non-negative values, infinities and NaNs order as unsigned
+  // integers, and NaN or infinite residuals never pass).
+  {
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, v[j] & 0x7FFF7FFFu));
+    }
+    const uint32_t top = mx.x > mx.y ? mx.x : mx.y;
+    if (top < keep_bound_bits(s, o, (1 << B) - 1)) {
+#pragma unroll
+      for (int i = 0; i < NWORD; ++i) nw[i] = w[i];
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NWORD; ++i) nw[i] = 0;
 #pragma unroll
@@ -277,9 +318,180 @@ __global__ __launch_bounds__(kVerifyWaves * 64) void k_verify(const uint32_t* __
   }
 }
 
+// ---- Re-quantisation check without the re-quantised stream --------------------
+// The residual is read in row order: a wavefront takes one row of a tile at a
+// time, and load i of lane l is the 16 bytes (8 weights) at 16 (64 i + l) of
+// the row's 8 KiB stretch, so consecutive lanes read consecutive bytes. That
+// piece belongs to the record of column 8 i + l / 8 (weights 8 (l % 8) ..
+// + 7). Every weight is decided on its own, so a lane checks its eight
+// weights against the record's scale and offset: under the record-level
+// bound on |r| all eight keep their codes and stay in their cells; otherwise
+// they are redone one by one with correctly rounded quotients (the codes are
+// loaded only then). Workgroups of four wavefronts take kVerifyRowsPerWg
+// rows of a tile each.
+constexpr int kVerifyRowsPerWg = 8;
+
+// Per column of the tile, in LDS: the map planes and, per class, the class's
+// records in the columns before it.
+struct VerifyCols {
+  uint32_t p0[kTileGroups], p1[kTileGroups];
+  uint16_t pre[4][kTileGroups];
+};
+
+// The exact decision for weights 8m .. 8m + 7 of a record of width b = 2^C
+// (any scale): counts into lm / lo and the smallest failing linear index.
+template <int C>
+__device__ __attribute__((noinline)) void piece_exact(uint2 cw, uint4 rr, float s, float o, int m, uint64_t lin0,
+                                                      uint32_t& lm, uint32_t& lo, uint64_t& lf) {
+  constexpr int B = 1 << C, H = 16 / B, L = (1 << B) - 1;
+  const int w0 = (4 * m) / H;   // first code word of the piece (cw.x; cw.y the next)
+  const float half_s = __fmul_rn(0.5f, s);
+  const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = 8 * m + j, pr = k >> 1, odd = k & 1;
+    const int wi = pr / H - w0, sh = 16 * odd + (pr % H) * B;
+    const uint32_t code = ((wi == 0 ? cw.x : cw.y) >> sh) & (uint32_t)L;
+    const uint32_t h = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const float r = __half2float(__ushort_as_half((unsigned short)h));
+    const float deq = __fadd_rn(__fmul_rn(s, (float)code), o);
+    const float a = __fsub_rn(__fadd_rn(deq, r), o);
+    uint32_t qp = 0;
+    if (s != 0.0f) {
+      float t = rintf(__fdiv_rn(a, s));
+      t = t < 0.0f ? 0.0f : t;
+      t = t > (float)L ? (float)L : t;
+      qp = (uint32_t)t;
+    }
+    const bool bad_code = qp != code;
+    const bool bad_cell = (s > 0.0f) ? (fabsf(r) >= half_s) : (r != 0.0f);
+    lm += bad_code;
+    lo += bad_cell;
+    if ((bad_code || bad_cell) && lin0 + j < lf) lf = lin0 + j;
+  }
+}
+
+__global__ __launch_bounds__(kVerifyWaves * 64) void k_verify_rows(const uint32_t* __restrict__ tiles,
+                                                                    const uint8_t* __restrict__ stream, int N, int G,
+                                                                    int RT, const uint16_t* __restrict__ resid,
+                                                                    uint64_t* result) {
+  __shared__ VerifyCols cols;
+  __shared__ uint32_t s_mism, s_ooc;
+  __shared__ unsigned long long s_first;
+  constexpr int kParts = kTileRows / kVerifyRowsPerWg;
+  const int t = (int)blockIdx.x / kParts, part = (int)blockIdx.x % kParts;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t K = (size_t)G * kGroup;
+  const int kt = t / RT, rt = t - kt * RT;
+  const int r0 = rt * kTileRows, R = min(kTileRows, N - r0);
+  const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
+  const uint8_t* tb = stream + (uint64_t)tiles[4 * t + 0] * 16;
+  const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
+  if (wave == 0) {
+    const bool live = lane < Gt;
+    const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
+    const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
+    cols.p0[lane] = mp.x;
+    cols.p1[lane] = mp.y;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cols.pre[c][lane] = (uint16_t)wave_excl_scan((uint32_t)__popc(km.m[c]), (uint32_t)lane);
+  }
+  if (tid == 0) {
+    s_mism = 0;
+    s_ooc = 0;
+    s_first = ~0ull;
+  }
+  uint32_t n[4], cb[4];
+  uint32_t cbase = map_bytes((uint32_t)Gt);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    n[c] = class_count(w2, w3, c);
+    cb[c] = cbase;
+    cbase += class_bytes(c, n[c]);
+  }
+  __syncthreads();
+  uint32_t mism = 0, ooc = 0;
+  uint64_t first = ~0ull;
+  const int m = lane & 7;   // the lane's eight weights of a record
+  const uint32_t valid = R >= 32 ? 0xFFFFFFFFu : ((1u << R) - 1u);
+  for (int rr = wave; rr < kVerifyRowsPerWg; rr += kVerifyWaves) {
+    const int row = part * kVerifyRowsPerWg + rr;
+    if (row >= R) break;
+    const uint4* rrow = reinterpret_cast<const uint4*>(resid + (size_t)(r0 + row) * K + (size_t)g0 * kGroup);
+    uint4 rv[8];
+    uint32_t so[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * i + (lane >> 3);
+      so[i] = 0u;
+      rv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (g < Gt) {
+        rv[i] = rrow[64 * i + lane];
+        const uint32_t p0 = cols.p0[g], p1 = cols.p1[g];
+        const int c = (int)((p0 >> row) & 1u) | (int)(((p1 >> row) & 1u) << 1);
+        const uint32_t mc = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
+        const uint32_t e = (uint32_t)cols.pre[c][g] + (uint32_t)__popc(mc & ((1u << row) - 1u));
+        const uint32_t nc = c == 0 ? n[0] : c == 1 ? n[1] : c == 2 ? n[2] : n[3];
+        const uint32_t bc = c == 0 ? cb[0] : c == 1 ? cb[1] : c == 2 ? cb[2] : cb[3];
+        so[i] = *reinterpret_cast<const uint32_t*>(tb + record_pos(c, nc, bc, e).so);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * i + (lane >> 3);
+      if (g >= Gt) continue;
+      const uint32_t p0 = cols.p0[g], p1 = cols.p1[g];
+      const int c = (int)((p0 >> row) & 1u) | (int)(((p1 >> row) & 1u) << 1);
+      const float sc = __half2float(__ushort_as_half((unsigned short)(so[i] & 0xFFFFu)));
+      const float of = __half2float(__ushort_as_half((unsigned short)(so[i] >> 16)));
+      const uint32_t v[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = v[j] & 0x7FFF7FFFu;
+        mx = max(mx, max(a & 0xFFFFu, a >> 16));
+      }
+      if (mx < keep_bound_bits(sc, of, (1 << (1 << c)) - 1)) continue;
+      // the rare piece: its code word(s), then the exact decisions
+      const uint32_t mc = ((c & 1) ? p0 : ~p0) & ((c & 2) ? p1 : ~p1) & valid;
+      const uint32_t e = (uint32_t)cols.pre[c][g] + (uint32_t)__popc(mc & ((1u << row) - 1u));
+      const uint32_t nc = c == 0 ? n[0] : c == 1 ? n[1] : c == 2 ? n[2] : n[3];
+      const uint32_t bc = c == 0 ? cb[0] : c == 1 ? cb[1] : c == 2 ? cb[2] : cb[3];
+      const int h = 16 >> c, w0 = (4 * m) / h;
+      const uint32_t* cwp = reinterpret_cast<const uint32_t*>(tb + record_pos(c, nc, bc, e).codes) + w0;
+      const uint2 cw = make_uint2(cwp[0], c == 3 ? cwp[1] : 0u);
+      const uint64_t lin0 = (uint64_t)(r0 + row) * K + (uint64_t)(g0 + g) * kGroup + 8u * (uint32_t)m;
+      switch (c) {
+        case 0: piece_exact<0>(cw, rv[i], sc, of, m, lin0, mism, ooc, first); break;
+        case 1: piece_exact<1>(cw, rv[i], sc, of, m, lin0, mism, ooc, first); break;
+        case 2: piece_exact<2>(cw, rv[i], sc, of, m, lin0, mism, ooc, first); break;
+        default: piece_exact<3>(cw, rv[i], sc, of, m, lin0, mism, ooc, first); break;
+      }
+    }
+  }
+  if (mism) atomicAdd(&s_mism, mism);
+  if (ooc) atomicAdd(&s_ooc, ooc);
+  if (first != ~0ull) atomicMin(&s_first, (unsigned long long)first);
+  __syncthreads();
+  if (tid == 0) {
+    if (s_mism) atomicAdd(reinterpret_cast<unsigned long long*>(&result[0]), (unsigned long long)s_mism);
+    if (s_ooc) atomicAdd(reinterpret_cast<unsigned long long*>(&result[1]), (unsigned long long)s_ooc);
+    if (s_first != ~0ull) atomicMin(reinterpret_cast<unsigned long long*>(&result[2]), s_first);
+  }
+}
+
 hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* result, uint32_t* requant,
                          hipStream_t s) {
   hipLaunchKernelGGL(k_verify_init, dim3(1), dim3(64), 0, s, result);
+  if (!requant) {
+    constexpr int64_t kParts = kTileRows / kVerifyRowsPerWg;
+    if (m.n_tiles * kParts > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_verify_rows, dim3((unsigned)(m.n_tiles * kParts)), dim3(kVerifyWaves * 64), 0, s, m.tiles,
+                       reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, m.n_cols / kGroup, row_tiles(m.n_rows),
+                       resid, result);
+    return hipGetLastError();
+  }
   if (m.n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_verify, dim3((unsigned)m.n_tiles), dim3(kVerifyWaves * 64), 0, s, m.tiles,
                      reinterpret_cast<const uint8_t*>(m.stream), m.n_rows, m.n_cols / kGroup, row_tiles(m.n_rows),
@@ -292,8 +504,11 @@ hipError_t launch_verify(const vbq_matrix& m, const uint16_t* resid, uint64_t* r
 // with every residual strictly inside half its group's scale, no output moves
 // further than this (CellFill abstract: bounded drift). One workgroup of four
 // wavefronts per row-tile walks its k-tiles in order. Per k-tile it forms X
-// for the tile's groups (fp32, in k order); lane l takes the records of
-// column l (wavefront w every fourth of them) and each record puts
+// for the tile's groups (fp32, in k order, from 16-byte loads); lane l takes
+// the records of column l in rows 8w .. 8w + 7 (wavefront w): a record's
+// index in its class follows from the map planes (the class's records in the
+// columns before, from a wave scan, plus its rank in its column), so the
+// eight scale loads of a lane go out together. Each record puts
 // 0.5 s X[b][l] at its (row, column) slot in LDS (a row has exactly one
 // record per column); then one thread per (batch row, row) adds its slots in
 // column order, so the sum order is fixed. Batches above four rows run as
@@ -315,43 +530,85 @@ __global__ __launch_bounds__(kDriftThreads) void k_drift(const uint32_t* __restr
   const int b_own = tid / kTileRows, r_own = tid % kTileRows;   // summed by this thread while tid < NB * 32
   float acc = 0.0f;
   const int KT = k_tiles(G);
+  constexpr int kRowsPerWave = kTileRows / 4;
   for (int kt = 0; kt < KT; ++kt) {
     const int g0 = kt * kTileGroups, Gt = min(kTileGroups, G - g0);
-    for (int i = tid; i < NB * kTileGroups; i += kDriftThreads) {
-      const int b = i / kTileGroups, g = i - b * kTileGroups;
-      float sx = 0.0f;
-      if (g < Gt) {
-        const uint16_t* xr = x + (size_t)b * K + (size_t)(g0 + g) * kGroup;
-        for (int j = 0; j < kGroup; ++j) sx += fabsf(__half2float(__ushort_as_half(xr[j])));
-      }
-      X[b][g] = sx;
-    }
-    __syncthreads();
+    // The scale loads need only the tile header and the width map, so they
+    // go out before the activation sums are formed.
     const int t = kt * RT + rt;
     const uint8_t* tb = stream + (size_t)tiles[4 * t + 0] * 16;
     const uint32_t w2 = tiles[4 * t + 2], w3 = tiles[4 * t + 3];
     const bool live = lane < Gt;
     const uint2 mp = live ? *reinterpret_cast<const uint2*>(tb + 8 * lane) : make_uint2(0u, 0u);
     const ClassMasks km = class_masks(mp.x, mp.y, live ? R : 0);
+    // per class: its record count, first block and the records in the
+    // columns before this lane's
+    uint32_t n[4], cb[4], pre[4];
     uint32_t cbase = map_bytes((uint32_t)Gt);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t n = class_count(w2, w3, c);
-      uint32_t mask = km.m[c];
-      uint32_t e = wave_excl_scan((uint32_t)__popc(mask), (uint32_t)lane);
-      for (uint32_t j = 0; mask; mask &= mask - 1u, ++e, ++j) {
-        if ((int)(j % 4u) != wave) continue;
-        const int row = __builtin_ctz(mask);
-        const uint32_t so = *reinterpret_cast<const uint32_t*>(tb + record_pos(c, n, cbase, e).so);
-        const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so & 0xFFFFu)));
+      n[c] = class_count(w2, w3, c);
+      cb[c] = cbase;
+      pre[c] = wave_excl_scan((uint32_t)__popc(km.m[c]), (uint32_t)lane);
+      cbase += class_bytes(c, n[c]);
+    }
+    uint32_t so[kRowsPerWave];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) P[b][row][lane] = hs * X[b][lane];
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = kRowsPerWave * wave + i;
+      const uint32_t bit = 1u << row;
+      const int c = (int)((mp.x >> row) & 1u) | (int)(((mp.y >> row) & 1u) << 1);
+      const uint32_t mc = c == 0 ? km.m[0] : c == 1 ? km.m[1] : c == 2 ? km.m[2] : km.m[3];
+      const uint32_t nc = c == 0 ? n[0] : c == 1 ? n[1] : c == 2 ? n[2] : n[3];
+      const uint32_t bc = c == 0 ? cb[0] : c == 1 ? cb[1] : c == 2 ? cb[2] : cb[3];
+      const uint32_t pc = c == 0 ? pre[0] : c == 1 ? pre[1] : c == 2 ? pre[2] : pre[3];
+      so[i] = 0u;
+      if (mc & bit) {   // a record (live column, row < R)
+        const uint32_t e = pc + (uint32_t)__popc(mc & (bit - 1u));
+        so[i] = *reinterpret_cast<const uint32_t*>(tb + record_pos(c, nc, bc, e).so);
       }
-      cbase += class_bytes(c, n);
+    }
+    for (int i = tid; i < NB * kTileGroups; i += kDriftThreads) {
+      const int b = i / kTileGroups, g = i - b * kTileGroups;
+      float sx = 0.0f;
+      if (g < Gt) {
+        // x rows are 128-byte aligned per group (the caller's buffer is
+        // 16-byte aligned and K is a multiple of 64)
+        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)b * K + (size_t)(g0 + g) * kGroup);
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = xr[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            sx += fabsf(__half2float(__ushort_as_half((unsigned short)(w[h] & 0xFFFFu))));
+            sx += fabsf(__half2float(__ushort_as_half((unsigned short)(w[h] >> 16))));
+          }
+        }
+      }
+      X[b][g] = sx;
     }
     __syncthreads();
-    if (tid < NB * kTileRows)
-      for (int g = 0; g < Gt; ++g) acc += P[b_own][r_own][g];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = kRowsPerWave * wave + i;
+      const float hs = 0.5f * __half2float(__ushort_as_half((unsigned short)(so[i] & 0xFFFFu)));
+      if (live && row < R)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) P[b][row][lane] = hs * X[b][lane];
+    }
+    __syncthreads();
+    // the slots of a row in column order; columns past the tile add +0,
+    // which leaves the (non-negative) sum unchanged
+    if (tid < NB * kTileRows) {
+      float v[kTileGroups];
+#pragma unroll
+      for (int g = 0; g < kTileGroups; ++g) v[g] = g < Gt ? P[b_own][r_own][g] : 0.0f;
+#pragma unroll
+      for (int g = 0; g < kTileGroups; ++g) acc += v[g];
+    }
     __syncthreads();   // X and P are rewritten for the next k-tile
   }
   if (tid < NB * kTileRows && r_own < R) bound[(size_t)b_own * N + r0 + r_own] = acc;

@@ -784,6 +784,35 @@ def test_requant_verify_in_cell_near_half(vbq):
     assert np.array_equal(q_rq, ref[3])
 
 
+def test_requant_verify_large_offsets(vbq):
+    """Groups whose offset is large against their scale (rows centred at 0,
+    1, 30 and 1000), so the binary32 roundings of f32(s q) + o + r - o are a
+    sizeable fraction of a cell and the kernel's record-level bound on |r|
+    (under which every code provably comes back) is far below s / 2: residuals
+    spread over the whole cell, at every width, must still give the oracle's
+    counts, first index and re-quantised codes."""
+    import torch
+    r = np.random.default_rng(46)
+    N, K = 64, 2048
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+    centre = np.array([0.0, 1.0, 30.0, 1000.0], np.float32)[np.arange(N) % 4][:, None]
+    W = (centre + r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    u = r.uniform(-0.5, 0.5, (N, K))
+    near = r.random((N, K)) < 0.25
+    u[near] = np.sign(u[near]) * (0.5 - r.choice(np.array([2.0 ** -16, 2.0 ** -12, 2.0 ** -8, 2.0 ** -4]),
+                                                 size=int(near.sum())))
+    resid = oracle.make_cell_residual(u, s)
+    pm = vbq.vbq_pack(_t(W), widths)
+    got = _verify_both(vbq, pm, _t(resid, torch.float16))
+    ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    assert got[:3] == ref[:3]
+    assert ref[0] > 0
+    lay = pm.host_layout()
+    lay["stream"] = got[3].cpu().numpy().view(np.uint32)
+    assert np.array_equal(oracle.unpack(lay)[0], ref[3])
+
+
 def test_requant_verify_mixed_widths(vbq):
     import torch
     N, K = 48, 2048
