@@ -914,40 +914,53 @@ __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* 
     for (int i = 0; i < kRows; ++i) acc[nb][i] = 0.f;
   for (int kt = 0; kt < M.k_tiles; ++kt) {
     const int g0 = kt * kTileGroups, Gt = min(kTileGroups, M.n_groups - g0);
-    const int lc = min((int)lane, Gt - 1);
-    const bool live = (int)lane < Gt;
+    // Piece i of lane l is weights 8 (l % 8) .. + 7 of column 8 i + l / 8:
+    // the (64 i + l)-th 16 bytes of the tile's stretch of x and of a
+    // residual row, so consecutive lanes read consecutive bytes.
     uint32_t xr[NB][32];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint4* xp = reinterpret_cast<const uint4*>(M.x + nb * K + (size_t)(g0 + lc) * kGroup);
+      const uint4* xp = reinterpret_cast<const uint4*>(M.x + nb * K + (size_t)g0 * kGroup);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint4 v = xp[i];
-        xr[nb][4 * i + 0] = live ? v.x : 0u;
-        xr[nb][4 * i + 1] = live ? v.y : 0u;
-        xr[nb][4 * i + 2] = live ? v.z : 0u;
-        xr[nb][4 * i + 3] = live ? v.w : 0u;
+        const bool has = 8 * i + (int)(lane >> 3) < Gt;
+        const uint4 v = has ? xp[64 * i + lane] : make_uint4(0u, 0u, 0u, 0u);
+        xr[nb][4 * i + 0] = v.x;
+        xr[nb][4 * i + 1] = v.y;
+        xr[nb][4 * i + 2] = v.z;
+        xr[nb][4 * i + 3] = v.w;
       }
     }
+    // two rows' pieces in flight at a time
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      const int r = part + kGemvWaves * i;
-      if (r >= R) break;
-      uint4 cur[8];
-      const uint4* rp = reinterpret_cast<const uint4*>(M.resid + (size_t)(r0 + r) * K + (size_t)(g0 + lc) * kGroup);
+    for (int i = 0; i < kRows; i += 2) {
+      const int ra = part + kGemvWaves * i, rb = ra + kGemvWaves;
+      if (ra >= R) break;
+      uint4 cur[2][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) cur[q] = rp[q];
+      for (int h = 0; h < 2; ++h) {
+        const int r = h ? rb : ra;
+        const uint4* rp =
+            reinterpret_cast<const uint4*>(M.resid + (size_t)(r0 + min(r, R - 1)) * K + (size_t)g0 * kGroup);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 8; ++q)
+          cur[h][q] = (8 * q + (int)(lane >> 3) < Gt && r < R) ? rp[64 * q + lane] : make_uint4(0u, 0u, 0u, 0u);
+      }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          a[0] = dot2(cur[q].x, xr[nb][4 * q + 0], a[0]);
-          a[1] = dot2(cur[q].y, xr[nb][4 * q + 1], a[1]);
-          a[2] = dot2(cur[q].z, xr[nb][4 * q + 2], a[2]);
-          a[3] = dot2(cur[q].w, xr[nb][4 * q + 3], a[3]);
+      for (int h = 0; h < 2; ++h) {
+        if ((h ? rb : ra) >= R) break;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            a[0] = dot2(cur[h][q].x, xr[nb][4 * q + 0], a[0]);
+            a[1] = dot2(cur[h][q].y, xr[nb][4 * q + 1], a[1]);
+            a[2] = dot2(cur[h][q].z, xr[nb][4 * q + 2], a[2]);
+            a[3] = dot2(cur[h][q].w, xr[nb][4 * q + 3], a[3]);
+          }
+          acc[nb][i + h] += wave_sum((a[0] + a[1]) + (a[2] + a[3]));
         }
-        acc[nb][i] += wave_sum((a[0] + a[1]) + (a[2] + a[3]));
       }
     }
   }
