@@ -235,9 +235,10 @@ struct Rec {
 // and refilled while the class is decoded.
 template <int C, int NB>
 __host__ __device__ constexpr int depth() {
-  // (four-row passes hold one row's activations per lane, so they afford the
-  // one-row depths)
-  return NB == 4 ? (C == 0 ? 4 : C == 1 ? 2 : 1)
+  // (four-row passes run eight wavefronts per tile, each holding one row's
+  // activations per lane: together they keep as many chunks in flight as four
+  // wavefronts at the one-row depths)
+  return NB == 4 ? (C == 0 ? 2 : 1)
                  : C == 0 ? (NB >= 4 ? 1 : 4 / NB) : C == 1 ? (NB >= 2 ? 1 : 2) : 1;   // at least one
 }
 
@@ -311,10 +312,12 @@ __device__ inline void issue_chunk(const TileRef& t, uint32_t j, Rec<C>& r, uint
   r.so = __builtin_amdgcn_raw_buffer_load_b32(t.rs, (int)os, 0, 0);
 }
 
-// Chunks of a class with n records that wavefront w takes.
+// Chunks of a class with n records that wavefront w of W takes (chunks w,
+// w + W, ...).
+template <int W = kGemvWaves>
 __device__ inline uint32_t wave_chunks(uint32_t n, int wave) {
   const uint32_t J = (n + 63u) >> 6;
-  return J > (uint32_t)wave ? (J - (uint32_t)wave + kGemvWaves - 1) / kGemvWaves : 0u;
+  return J > (uint32_t)wave ? (J - (uint32_t)wave + W - 1) / W : 0u;
 }
 
 template <int C, int NB>
@@ -363,6 +366,7 @@ __host__ __device__ constexpr uint32_t spare_entry() {
 // row); a record's index in the class, and with it its position in the
 // stream, is the number of the class's records in the columns before it plus
 // its rank among its column's rows.
+constexpr int kQuadWaves = 8;                            // wavefronts of a four-row workgroup
 constexpr uint32_t kQuadPad = 3 * kTileGroups;          // padding entries of a class at most
 constexpr uint32_t kQuadTab = kMaxRecs + 4 * kQuadPad;  // 2816 entries
 struct QuadMap {   // words from LdsMap<4>::table
@@ -603,10 +607,10 @@ __device__ inline void decode_quad(const Consts<C>& k, const Rec<C>& r, uint32_t
 template <int C>
 __device__ inline void issue_first_quad(const TileRef& t, int wave, Flight<C, 4>& f, uint32_t cnt, const uint32_t* S,
                                         uint32_t lane) {
-  const uint32_t nS = wave_chunks(cnt, wave);
+  const uint32_t nS = wave_chunks<kQuadWaves>(cnt, wave);
 #pragma unroll
   for (int d = 0; d < depth<C, 4>(); ++d)
-    issue_quad<C>(t, (uint32_t)d < nS ? (uint32_t)wave + kGemvWaves * d : 0x3FFFFFFu, cnt, f.r[d], S, lane);
+    issue_quad<C>(t, (uint32_t)d < nS ? (uint32_t)wave + kQuadWaves * d : 0x3FFFFFFu, cnt, f.r[d], S, lane);
 }
 
 // Step 3 of a four-row pass for class C.
@@ -614,7 +618,7 @@ template <int C>
 __device__ inline void run_class_quad(const TileRef& t, Flight<C, 4>& f, uint32_t cnt, uint32_t* S, int wave,
                                       uint32_t lane) {
   constexpr int D = depth<C, 4>();
-  const uint32_t nS = wave_chunks(cnt, wave);
+  const uint32_t nS = wave_chunks<kQuadWaves>(cnt, wave);
   if (nS == 0) return;
   const Consts<C> k = make_consts<C>();
   for (uint32_t s0 = 0; s0 < nS; s0 += D) {
@@ -624,7 +628,7 @@ __device__ inline void run_class_quad(const TileRef& t, Flight<C, 4>& f, uint32_
       if (sq >= nS) break;
       decode_quad<C>(k, f.r[d], S, lane);
       const uint32_t sn = sq + D;
-      if (sn < nS) issue_quad<C>(t, (uint32_t)wave + kGemvWaves * sn, cnt, f.r[d], S, lane);
+      if (sn < nS) issue_quad<C>(t, (uint32_t)wave + kQuadWaves * sn, cnt, f.r[d], S, lane);
     }
   }
 }
@@ -834,8 +838,9 @@ __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, 
     Flight<3, 4> f3;
     if (wave == 0) copy_x<4>(T, kt, S, lane, 0);
     t = tile_ref(T, rt, kt);
-    const u32x2 mp = map_load(t, lane);
-    tile_prepare<4>(t, wave, mp, S, lane, 0);
+    // wavefronts 0-3 copy the activations and build the record table,
+    // 4-7 only decode
+    if (wave < kGemvWaves) tile_prepare<4>(t, wave, map_load(t, lane), S, lane, 0);
     __syncthreads();
     const uint32_t* Q = S + LdsMap<4>::table;
     const uint32_t c0 = __builtin_amdgcn_readfirstlane(Q[QuadMap::cnt + 0]);
@@ -851,7 +856,7 @@ __device__ inline void coop_tile(const GemvMat& T, int rt, int kt, uint32_t* S, 
     run_class_quad<2>(t, f2, c2, S, wave, lane);
     run_class_quad<3>(t, f3, c3, S, wave, lane);
     __syncthreads();
-    fold_rows<4>(S, wave, yacc, lane);
+    if (wave < kGemvWaves) fold_rows<4>(S, wave, yacc, lane);
     return;
   }
   const bool cell_wave = CELL && wave >= kGemvWaves;
@@ -979,13 +984,21 @@ __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* 
 // workgroup takes the row-tile's k-tiles (of every level) in order, then the
 // residual's rows, at a raised wavefront priority (those workgroups come
 // first in the launch and carry several tiles' work).
-template <int MODE>
+template <int NB, int MODE>
 __host__ __device__ constexpr int gemv_waves() {
-  return MODE == kModeCell8 ? 2 * kGemvWaves : kGemvWaves;
+  return MODE == kModeCell8 ? 2 * kGemvWaves : (NB == 4 && MODE == kModePlain) ? kQuadWaves : kGemvWaves;
+}
+
+// (the second bound is the minimum of wavefronts per SIMD: four caps a
+// wavefront at 128 VGPRs)
+template <int NB, int MODE>
+__host__ __device__ constexpr int gemv_min_waves() {
+  return (NB == 1 || gemv_waves<NB, MODE>() == kQuadWaves) ? 4 : 2;
 }
 
 template <int NB, int MODE>
-__global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_gemv(const GemvLaunch L) {
+__global__ __launch_bounds__((gemv_waves<NB, MODE>() * 64), (gemv_min_waves<NB, MODE>())) void k_gemv(
+    const GemvLaunch L) {
   constexpr bool RESID = MODE == kModeResid16, CELL = MODE == kModeCell8;
   extern __shared__ __align__(16) uint32_t S[];
   const int tid = threadIdx.x;
@@ -1014,14 +1027,14 @@ __global__ __launch_bounds__(gemv_waves<MODE>() * 64, NB == 1 ? 4 : 2) void k_ge
   asm volatile("" ::"s"(M.tiles), "s"(M.stream), "s"(M.x), "s"(M.n_groups), "s"(M.row_tiles), "s"(M.k_tiles),
                "s"(M.stream_bytes), "s"(M.split), "s"(M.shared));
   const int j = (int)blockIdx.x - wb;
-  for (int i = tid; i < NB * kSlotWords; i += gemv_waves<MODE>() * kWave) S[LdsMap<NB>::slots + i] = 0u;
+  for (int i = tid; i < NB * kSlotWords; i += gemv_waves<NB, MODE>() * kWave) S[LdsMap<NB>::slots + i] = 0u;
   float yacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
-  // the wavefronts that fold rows (all four, or the four cell wavefronts)
-  // hold row 8 fw + lane / 8 in lanes 8 r
+  // the wavefronts that fold rows (the first four, or the four cell
+  // wavefronts) hold row 8 fw + lane / 8 in lanes 8 r
   const int fw = CELL ? wave - kGemvWaves : wave;
-  const bool folds = fw >= 0;
+  const bool folds = fw >= 0 && fw < kGemvWaves;
   const int row = 8 * fw + (int)(lane >> 3);
   if (M.split) {
     // One tile of a row-tile with several: its row sums go to the scratch;
@@ -1131,7 +1144,7 @@ static hipError_t launch_one(const GemvLaunch& L, int n_wg, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemv<NB, MODE>), dim3(n_wg), dim3(gemv_waves<MODE>() * kWave), lds, s, L);
+  hipLaunchKernelGGL((k_gemv<NB, MODE>), dim3(n_wg), dim3(gemv_waves<NB, MODE>() * kWave), lds, s, L);
   return hipGetLastError();
 }
 
