@@ -190,7 +190,10 @@ __device__ inline void class_bias(const uint32_t (&xr)[NB][32], float (&bias)[NB
 //  4. Wavefront w adds the slots of rows 8w..8w+7 over the 64 columns in a
 //     fixed order and clears them.
 constexpr int kSlotPitch = 33;                            // slot (column l, row r) at l * 33 + r; 32 is spare
-constexpr int kSlotWords = kWave * kSlotPitch;            // 2112 per batch row
+// Words from one batch row's slots to the next: 2112 and a 16-word skew, so
+// that the four lanes of an MFMA block in a four-row pass, which write the
+// same slot for their four batch rows, hit four different LDS banks.
+constexpr int kSlotWords = kWave * kSlotPitch + 16;
 // Activations of a tile's 64 columns: per column 64 fp16 (32 words) and 4
 // words of sums, 144 bytes apart, so that the 16-byte reads of lanes on
 // different columns fall on different LDS banks. The sums are sum(x) and
@@ -204,9 +207,11 @@ template <int NB>
 struct LdsMap {
   static constexpr int x = 0;                             // [NB][64][36] fp16 pairs and the column's sums
   // words from one batch row's activations to the next: with four rows a
-  // 16-byte skew puts the same column of the four rows on different banks
-  // (the four lanes of an MFMA block read one row each)
-  static constexpr int xrow = NB >= 4 ? kXWords + 4 : kXWords;
+  // 64-byte skew (16 banks) puts the same column of the four rows on
+  // different banks (the four lanes of an MFMA block read one row each), and
+  // with the 36-word column pitch, blocks on columns fewer than four apart
+  // land on other banks as well
+  static constexpr int xrow = NB >= 4 ? kXWords + 16 : kXWords;
   static constexpr int xbuf = NB * xrow;                  // words per activation buffer
   static constexpr int table = x + xbuf;                  // [2048] u32: slot byte << 16 | column byte (from S)
   static constexpr int slots = table + kMaxRecs;          // [NB][64][33]
