@@ -596,16 +596,23 @@ __device__ inline void decode_quad(const Consts<C>& k, const Rec<C>& r, uint32_t
   }
   const f32x4_t d = acc[0][0] + acc[0][1];
   float* slot = reinterpret_cast<float*>(S + LdsMap<4>::slots) + c * kSlotWords + col * kSlotPitch;
-  const uint32_t e[4] = {quad_bcast<0>(r.ent), quad_bcast<1>(r.ent), quad_bcast<2>(r.ent), quad_bcast<3>(r.ent)};
-  const uint32_t so[4] = {quad_bcast<0>(r.so), quad_bcast<1>(r.so), quad_bcast<2>(r.so), quad_bcast<3>(r.so)};
+  // each lane converts its own record's scale and offset once; the block's
+  // four are then broadcast as floats. Empty entries write the spare row 32
+  // of the column's slots (never folded) instead of branching.
+  const float s_own = __half2float(__ushort_as_half((unsigned short)(r.so & 0xFFFFu)));
+  const float o_own = __half2float(__ushort_as_half((unsigned short)(r.so >> 16)));
+  const uint32_t row_own = (r.ent & 0x8000u) ? (r.ent & 31u) : 32u;
+  const uint32_t rows[4] = {quad_bcast<0>(row_own), quad_bcast<1>(row_own), quad_bcast<2>(row_own),
+                            quad_bcast<3>(row_own)};
+  const uint32_t sb = __float_as_uint(s_own), ob = __float_as_uint(o_own);
+  const float sq[4] = {__uint_as_float(quad_bcast<0>(sb)), __uint_as_float(quad_bcast<1>(sb)),
+                       __uint_as_float(quad_bcast<2>(sb)), __uint_as_float(quad_bcast<3>(sb))};
+  const float oq[4] = {__uint_as_float(quad_bcast<0>(ob)), __uint_as_float(quad_bcast<1>(ob)),
+                       __uint_as_float(quad_bcast<2>(ob)), __uint_as_float(quad_bcast<3>(ob))};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (e[q] & 0x8000u) {
-      const float s = __half2float(__ushort_as_half((unsigned short)(so[q] & 0xFFFFu)));
-      const float o = __half2float(__ushort_as_half((unsigned short)(so[q] >> 16)));
-      const float dot = a0 + d[q];
-      slot[e[q] & 31u] = __builtin_fmaf(s, dot, o * xsum);
-    }
+    const float dot = a0 + d[q];
+    slot[rows[q]] = __builtin_fmaf(sq[q], dot, oq[q] * xsum);
   }
 }
 
