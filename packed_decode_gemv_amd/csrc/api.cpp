@@ -165,8 +165,8 @@ static vbq_status gemv_impl(int32_t count, const vbq_matrix* ms, const uint16_t*
   }
   if (resid && !aligned(resid, 16)) return VBQ_ERR_ALIGNMENT;
   if (cell && !aligned(cell, 16)) return VBQ_ERR_ALIGNMENT;
-  const int mode = resid ? kModeResid16 : cell ? kModeCell8 : kModePlain;
-  const int max_nb = mode == kModePlain ? kGemvMaxNb : kGemvMaxNbResid;
+  const int mode = resid ? kModeResid16 : cell ? kModeCell8 : levels ? kModeLevelPairs : kModePlain;
+  const int max_nb = (mode == kModePlain || mode == kModeLevelPairs) ? kGemvMaxNb : kGemvMaxNbResid;
   float* partials = nullptr;
   uint32_t* counters = nullptr;
   if (split) {

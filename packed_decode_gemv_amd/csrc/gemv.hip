@@ -998,7 +998,9 @@ __device__ inline void residual_rows(const GemvMat& M, int rt, int part, float* 
 // first in the launch and carry several tiles' work).
 template <int NB, int MODE>
 __host__ __device__ constexpr int gemv_waves() {
-  return MODE == kModeCell8 ? 2 * kGemvWaves : (NB == 4 && MODE == kModePlain) ? kQuadWaves : kGemvWaves;
+  return (MODE == kModeCell8 || MODE == kModeLevelPairs) ? 2 * kGemvWaves
+         : (NB == 4 && MODE == kModePlain)              ? kQuadWaves
+                                                        : kGemvWaves;
 }
 
 // (the second bound is the minimum of wavefronts per SIMD: four caps a
@@ -1011,7 +1013,7 @@ __host__ __device__ constexpr int gemv_min_waves() {
 template <int NB, int MODE>
 __global__ __launch_bounds__((gemv_waves<NB, MODE>() * 64), (gemv_min_waves<NB, MODE>())) void k_gemv(
     const GemvLaunch L) {
-  constexpr bool RESID = MODE == kModeResid16, CELL = MODE == kModeCell8;
+  constexpr bool RESID = MODE == kModeResid16, CELL = MODE == kModeCell8, PAIRS = MODE == kModeLevelPairs;
   extern __shared__ __align__(16) uint32_t S[];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -1039,7 +1041,10 @@ __global__ __launch_bounds__((gemv_waves<NB, MODE>() * 64), (gemv_min_waves<NB, 
   asm volatile("" ::"s"(M.tiles), "s"(M.stream), "s"(M.x), "s"(M.n_groups), "s"(M.row_tiles), "s"(M.k_tiles),
                "s"(M.stream_bytes), "s"(M.split), "s"(M.shared));
   const int j = (int)blockIdx.x - wb;
-  for (int i = tid; i < NB * kSlotWords; i += gemv_waves<NB, MODE>() * kWave) S[LdsMap<NB>::slots + i] = 0u;
+  for (int i = tid; i < NB * kSlotWords; i += gemv_waves<NB, MODE>() * kWave) {
+    S[LdsMap<NB>::slots + i] = 0u;
+    if (PAIRS) S[LdsMap<NB>::words + LdsMap<NB>::slots + i] = 0u;   // the second tile's slots
+  }
   float yacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) yacc[nb] = 0.f;
@@ -1048,6 +1053,41 @@ __global__ __launch_bounds__((gemv_waves<NB, MODE>() * 64), (gemv_min_waves<NB, 
   const int fw = CELL ? wave - kGemvWaves : wave;
   const bool folds = fw >= 0 && fw < kGemvWaves;
   const int row = 8 * fw + (int)(lane >> 3);
+  if constexpr (PAIRS) {
+    // Levels of one matrix at one batch row: the row-tile's tiles (levels in
+    // order, k-tiles in order within a level) two at a time, wavefronts 0-3
+    // on tile p with the first half of LDS, 4-7 on tile p + 1 with the
+    // second. Each half's fold starts from -0 (which adds nothing), and the
+    // rows get the first tile's sum, then the second's: the order of the
+    // one-tile-at-a-time walk. With an odd count the second half repeats the
+    // last tile and its sum is dropped.
+    const int rt = j, grp = wave >> 2, gw = wave & 3;
+    uint32_t* Sg = S + grp * LdsMap<NB>::words;
+    float* xch = reinterpret_cast<float*>(S + 2 * LdsMap<NB>::words);   // [NB][32]: the second tile's row sums
+    __builtin_amdgcn_s_setprio(2);
+    const int tiles = M.levels * M.k_tiles;
+    for (int p = 0; p < tiles; p += 2) {
+      const int mp = min(p + grp, tiles - 1);
+      const int lv = mp / M.k_tiles, kt = mp - lv * M.k_tiles;
+      float part[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) part[nb] = -0.0f;
+      coop_tile<NB, false>(L.mats[mi + lv], rt, kt, Sg, gw, part, lane);
+      if (grp == 1 && (lane & 7u) == 0)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          xch[nb * kTileRows + row - 8 * kGemvWaves] = p + 1 < tiles ? part[nb] : -0.0f;
+      __syncthreads();
+      if (grp == 0)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) yacc[nb] = (yacc[nb] + part[nb]) + xch[nb * kTileRows + row];
+    }
+    const int r0 = rt * kTileRows, R = min(kTileRows, M.n_rows - r0);
+    if (folds && (lane & 7u) == 0 && row < R)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) M.y[(size_t)nb * M.n_rows + r0 + row] = yacc[nb];
+    return;
+  }
   if (M.split) {
     // One tile of a row-tile with several: its row sums go to the scratch;
     // the workgroup that finishes the row-tile's last tile adds them in tile
@@ -1137,6 +1177,7 @@ hipError_t gemv_scratch(float** partials, uint32_t** counters) {
 }
 
 size_t gemv_lds_bytes(int nb, int mode) {
+  if (mode == kModeLevelPairs) return 4u * (2 * LdsMap<1>::words + kTileRows);   // one batch row only
   const bool cell = mode == kModeCell8;
   switch (nb) {
     case 1: return 4u * (cell ? LdsMap<1>::words_cell : LdsMap<1>::words);
@@ -1167,6 +1208,10 @@ hipError_t launch_gemv(const GemvLaunch& L, int nb, int mode, int n_wg, hipStrea
     return mode == kModeResid16  ? launch_one<N, kModeResid16>(L, n_wg, s)               \
            : mode == kModeCell8 ? launch_one<N, kModeCell8>(L, n_wg, s)                  \
                                 : launch_one<N, kModePlain>(L, n_wg, s);
+  if (mode == kModeLevelPairs) {
+    if (nb == 1) return launch_one<1, kModeLevelPairs>(L, n_wg, s);
+    mode = kModePlain;   // several batch rows: one tile at a time
+  }
   switch (nb) {
     VBQ_CASE(1)
     VBQ_CASE(2)

@@ -166,8 +166,10 @@ constexpr int kMaxMats = VBQ_MAX_LAUNCH_MATS;
 constexpr int kGemvWaves = 4;
 constexpr int kGemvMaxNb = 4;   // batch rows per pass (two with a residual)
 constexpr int kGemvMaxNbResid = 2;
-// Residual kinds of a launch: none, fp16 per weight, int8 cell fractions.
-constexpr int kModePlain = 0, kModeResid16 = 1, kModeCell8 = 2;
+// Residual kinds of a launch: none, fp16 per weight, int8 cell fractions;
+// and residual levels of one matrix at one batch row, taken two tiles at a
+// time (no residual).
+constexpr int kModePlain = 0, kModeResid16 = 1, kModeCell8 = 2, kModeLevelPairs = 3;
 
 struct GemvLaunch {
   int32_t wg_begin[kMaxMats];   // first workgroup of each matrix (non-decreasing; INT32_MAX past n_mats)
