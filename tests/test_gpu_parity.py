@@ -650,6 +650,31 @@ def test_rrq_levels_bit_exact_and_gemv(vbq, shape):
             assert np.all(np.abs(y - ref) <= bound), (B, k)
 
 
+@pytest.mark.parametrize("n_levels", [2, 3])
+def test_levels_one_row_equals_batch_rows(vbq, n_levels):
+    """At one batch row the GEMV over levels takes a row-tile's tiles two at a
+    time; with more rows it walks them one at a time. Both add the tiles' row
+    sums in the same order, so every batch row of a multi-row call equals the
+    one-row call on that row bit for bit (odd and even tile counts, three
+    k-tiles per level, ragged rows)."""
+    import torch
+    N, K = 70, 8192 + 192
+    r = np.random.default_rng(71 + n_levels)
+    pms = []
+    for i in range(n_levels):
+        W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+        widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+        pms.append(vbq.vbq_pack(_t(W), widths))
+    x = _t(r.standard_normal((3, K)).astype(np.float16).view(np.uint16), torch.float16)
+    print(f"case levels one row vs batch, {n_levels} levels", flush=True)
+    yb = vbq.vbq_gemv_levels(pms, x)
+    for b in range(3):
+        y1 = vbq.vbq_gemv_levels(pms, x[b:b + 1].contiguous())
+        assert torch.equal(y1[0], yb[b]), f"batch row {b}"
+    y_sum = sum(vbq.vbq_gemv(pm, x[0:1].contiguous()) for pm in pms)
+    assert torch.allclose(vbq.vbq_gemv_levels(pms, x[0:1].contiguous()), y_sum, rtol=1e-5, atol=1e-5)
+
+
 def test_residual_error_any_width(vbq):
     """vbq_residual_error on a mixed-width matrix is E - (f32(s q) + o) bit
     for bit, in place too."""
