@@ -12,8 +12,10 @@
 // compared byte for byte.
 //
 // The decision is integer-valued, so the binary32 operation sequence is fixed
-// (built with -ffp-contract=off; the quotient decides as the correctly
-// rounded one does, see quarter_fast):
+// (built with -ffp-contract=off). Residuals under a record-level bound keep
+// every code provably (keep_bound_bits); the rest take an estimated quotient
+// that decides as the correctly rounded one does (quarter_fast) or the
+// correctly rounded quotient itself:
 //   deq = f32(s*q) + o;  v = deq + r;  q' = clamp(rint((v - o) / s), 0, L)
 //   out of cell: |r| >= 0.5*s  (or r != 0 when s == 0).
 #include "vbq_common.h"
@@ -209,11 +211,12 @@ __device__ inline void check_record(const uint32_t* w, const uint4 (&rv)[8], uin
   }
 }
 
-// One workgroup of four wavefronts per tile, lane l on column l: a column's
-// records of each class are taken in row order, wavefront w checking every
-// fourth of them (those with index w mod 4 in the column): codes and
-// scale/offset at the record's position, the record's 64 residuals from its
-// row, columns 64 (64 kt + l) .. + 63.
+// With the re-quantised stream (k_verify): one workgroup of four wavefronts
+// per tile, lane l on column l: a column's records of each class are taken in
+// row order, wavefront w checking every fourth of them (those with index
+// w mod 4 in the column): codes and scale/offset at the record's position,
+// the record's 64 residuals from its row, columns 64 (64 kt + l) .. + 63.
+// Without it, k_verify_rows (below) reads the residual in row order.
 constexpr int kVerifyWaves = 4;
 
 template <int C>
