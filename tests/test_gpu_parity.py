@@ -437,7 +437,7 @@ def _cell_inputs(N, K, seed, u_scale=1.0):
     return W, widths, q, s, o, resid, x
 
 
-@pytest.mark.parametrize("shape", [(16, 256), (50, 1024), (33, 4096), (20, 8192)])
+@pytest.mark.parametrize("shape", [(16, 256), (50, 1024), (33, 4096), (20, 8192), (37, 8192 + 192)])
 def test_residual_gemv_and_revocation(vbq, shape):
     import torch
     N, K = shape
@@ -833,6 +833,32 @@ def test_requant_verify_large_offsets(vbq):
     ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
     assert got[:3] == ref[:3]
     assert ref[0] > 0
+    lay = pm.host_layout()
+    lay["stream"] = got[3].cpu().numpy().view(np.uint32)
+    assert np.array_equal(oracle.unpack(lay)[0], ref[3])
+
+
+def test_requant_verify_several_k_tiles(vbq):
+    """Three k-tiles with a ragged last one (3 of 64 groups) and a ragged last
+    row-tile, mixed widths, residuals spread over the whole cell with some
+    outside it: counts, first index and re-quantised codes equal the
+    oracle's in both modes (the row-order kernel and the one that writes the
+    stream)."""
+    import torch
+    r = np.random.default_rng(47)
+    N, K = 45, 8192 + 192
+    widths = r.choice(np.array([1, 2, 4, 8], np.uint8), size=(N, K // 64))
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quantize_matrix(W, widths)
+    u = r.uniform(-0.5, 0.5, (N, K))
+    out = r.random((N, K)) < 0.001
+    u[out] = 0.8 * np.sign(u[out])
+    resid = oracle.make_cell_residual(u, s)
+    pm = vbq.vbq_pack(_t(W), widths)
+    got = _verify_both(vbq, pm, _t(resid, torch.float16))
+    ref = oracle.requant_verify(q, s, o, widths, resid, want_codes=True)
+    assert got[:3] == ref[:3]
+    assert ref[1] > 0
     lay = pm.host_layout()
     lay["stream"] = got[3].cpu().numpy().view(np.uint32)
     assert np.array_equal(oracle.unpack(lay)[0], ref[3])
