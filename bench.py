@@ -498,14 +498,15 @@ def _gemv_line(name, us, nbytes, extra=None):
     return d
 
 
-def measure_workloads(stack, calls):
+def measure_workloads(stack, calls, outputs=None):
     """Timed lines for the other workloads (weights and inputs resident in HBM,
     rotated over a pool larger than the caches where they would fit):
     131M-class projection, 1.0B-class layer at batch 1 and 4, the 9B-class
     stack at batch 4, the in-cell update
     (residual GEMV, re-quantisation check, drift bound), the GEMV over recurrent
     residual levels and the batched GEMM on
-    MFMA."""
+    MFMA. The GPU outputs of the timed calls go to ``outputs`` (host copies
+    with what regenerates their inputs) for the same-run parity check."""
     import torch
 
     import synth
@@ -532,6 +533,9 @@ def measure_workloads(stack, calls):
     us = _events_time(lambda i: vbq.vbq_gemv(pool[i % len(pool)], x, out=y), calls)
     out.append(_gemv_line(f"131M-class projection {proj.n}x{proj.k}, batch 1", us,
                           algorithmic_bytes(pm.sizes, proj.n, proj.k, 1)))
+    keep = outputs.append if outputs is not None else (lambda _: None)
+    keep(dict(name="131M-class projection", kind="gemv", cid=0, layer=0, pi=0, proj=proj, B=1,
+              y=y.cpu().numpy()))
 
     # 1.0B-class layer (5 projections in one launch), batch 1 and 4
     mats = [packed(1, 0, pi, p) for pi, p in enumerate(synth.C1.projs)]
@@ -543,6 +547,9 @@ def measure_workloads(stack, calls):
         ys = [torch.empty(B, p.n, dtype=torch.float32, device=dev) for p in synth.C1.projs]
         plans = [vbq.GemvPlan(L, xs, ys, static=True) for L in layers]
         us = _events_time(lambda i: plans[i % len(plans)].launch(vbq._stream()), calls)
+        for pi, p in enumerate(synth.C1.projs):
+            keep(dict(name=f"1.0B-class layer {p.name}, batch {B}", kind="gemv", cid=1, layer=0, pi=pi, proj=p,
+                      B=B, y=ys[pi].cpu().numpy()))
         nb = sum(algorithmic_bytes(m.sizes, p.n, p.k, B) for (m, _, _), p in zip(mats, synth.C1.projs))
         out.append(_gemv_line(f"1.0B-class layer (qkv 6144x2048, o 2048x2048, up/gate 8192x2048, "
                               f"down 2048x8192), one vbq_gemv_batched_static launch, batch {B}", us, nb))
@@ -610,12 +617,16 @@ def measure_workloads(stack, calls):
                       calls)
     nb = algorithmic_bytes(pm.sizes, N, K, 1, resid=True)
     out.append(_gemv_line(f"in-cell update {N}x{K} (all 4-bit) + fp16 residual, residual GEMV, batch 1", us, nb))
+    keep(dict(name="in-cell fp16 residual GEMV", kind="resid16", cid=2, layer=0, pi=0, proj=proj, B=1,
+              y=y.cpu().numpy()))
     # the same update as one signed byte per weight (vbq_gemv_cell8)
     us = _events_time(lambda i: vbq.vbq_gemv_cell8(pool[i % len(pool)][0], x, pool[i % len(pool)][2], out=y),
                       calls)
     nb8 = algorithmic_bytes(pm.sizes, N, K, 1) + N * K
     out.append(_gemv_line(f"in-cell update {N}x{K} (all 4-bit) + compact residual (int8 cell fraction), "
                           "residual GEMV, batch 1", us, nb8))
+    keep(dict(name="in-cell compact residual GEMV", kind="cell8", cid=2, layer=0, pi=0, proj=proj, B=1,
+              y=y.cpu().numpy()))
     # encoding an fp16 residual into fraction bytes: reads r (2 B/weight), the
     # scale of every group and the width map, writes f (1 B/weight)
     f_out = torch.empty_like(f8)
@@ -658,9 +669,11 @@ def measure_workloads(stack, calls):
     nbr = sum(pm_.sizes.code_bits / 8 + 4 * groups + groups / 4 for pm_ in levels) + 2 * K + 4 * N
     out.append(_gemv_line(f"recurrent residual levels {N}x{K}: 2-bit base + 3 levels (8 effective bits), "
                           "GEMV over the levels, batch 1", us, nbr))
+    keep(dict(name="recurrent residual levels", kind="levels", cid=2, layer=0, pi=0, proj=proj, B=1,
+              y=y.cpu().numpy()))
     del pool, levels
 
-    out.append(gemm_workload(vbq, calls))
+    out.append(gemm_workload(vbq, calls, outputs))
     return out
 
 
@@ -697,7 +710,7 @@ def recipe_line(stack, steps, warmup):
          "layer_gb_per_s_min": round(min(per_layer), 1), "layer_gb_per_s_max": round(max(per_layer), 1)})
 
 
-def gemm_workload(vbq, calls):
+def gemm_workload(vbq, calls, outputs=None):
     """The batched GEMM on MFMA: M = 256 tokens, K = 4096, N = 14336, default
     width mix; one timed line."""
     import torch
@@ -712,6 +725,9 @@ def gemm_workload(vbq, calls):
     xb = torch.from_numpy(synth.x_bf16(synth.SEED, key, M, proj.k).view(np.int16)).to(dev).view(torch.bfloat16)
     yg = torch.empty(M, proj.n, dtype=torch.float32, device=dev)
     us = _events_time(lambda i: vbq.vbq_gemm(pm, xb, out=yg), calls)
+    if outputs is not None:
+        outputs.append(dict(name=f"batched GEMM M={M}", kind="gemm", cid=4, layer=0, pi=0, proj=proj, B=M,
+                            y=yg.cpu().numpy()))
     flops = 2.0 * M * proj.n * proj.k
     tf = flops / (us * 1e-6) / 1e12
     return dict(workload=f"batched GEMM M={M} K={proj.k} N={proj.n} (bf16 MFMA)", us_per_call=round(us, 3),
@@ -806,6 +822,42 @@ def cpu_baseline(stack, budget_s):
                 sample=f"{len(checked)} matrices ({done_w / 1e6:.0f}M weights, batch {B}): "
                        + ", ".join(checked[:4]) + (" ..." if len(checked) > 4 else ""),
                 seconds=round(spent, 2)), dict(max_rel_l2=worst, matrices=len(checked), tol=2e-3)
+
+
+def workload_parity(outputs, max_rows=1024):
+    """Same-run parity of the other workloads' GPU outputs against the CPU
+    oracle (part of the CPU-baseline leg): for each output, the oracle
+    quantises the same synthetic rows (every row up to max_rows, else an even
+    sample of max_rows rows) and forms its fp64 result; the figure is the
+    rel-L2 distance over those rows. Widths, weights, activations and residual
+    bytes are regenerated from the seeded draws, row by row."""
+    import oracle
+    import synth
+    res = {}
+    for o in outputs:
+        p = o["proj"]
+        key = synth.proj_key(o["cid"], o["layer"], o["pi"])
+        rows = np.arange(p.n) if p.n <= max_rows else np.unique(np.linspace(0, p.n - 1, max_rows).astype(np.int64))
+        widths = synth.widths(synth.SEED, key, p.n, p.k // 64, p.mix, rows=rows)
+        W = synth.weights(synth.SEED, key, p.n, p.k, rows=rows)
+        if o["kind"] == "levels":
+            levels, _ = oracle.rrq_levels(W, 4)
+            ref = oracle.rrq_gemv(levels, synth.x_f16(synth.SEED, key, 1, p.k))
+        else:
+            q, s16, o16 = oracle.quantize_matrix(W, widths)
+            if o["kind"] == "gemm":
+                ref = oracle.gemm_bf16_weights(q, s16, o16, synth.x_bf16(synth.SEED, key, o["B"], p.k))
+            else:
+                x = synth.x_f16(synth.SEED, key, o["B"], p.k)
+                if o["kind"] == "gemv":
+                    ref = oracle.gemv(q, s16, o16, x)
+                else:
+                    f = synth.cell_f(synth.SEED, key, p.n, p.k, rows=rows)
+                    ref = (oracle.gemv(q, s16, o16, x, resid=oracle.cell8_decode(f, s16)) if o["kind"] == "resid16"
+                           else oracle.gemv_cell8(q, s16, o16, x, f))
+        y = o["y"][:, rows].astype(np.float64)
+        res[o["name"]] = dict(rel_l2=float(np.linalg.norm(y - ref) / np.linalg.norm(ref)), rows=int(len(rows)))
+    return dict(max_rel_l2=max((v["rel_l2"] for v in res.values()), default=0.0), tol=2e-3, outputs=res)
 
 
 def workload_name(layers, B):
@@ -907,12 +959,12 @@ def main(argv=None):
     ceilings = stream_ceilings()
     log(f"  measured ceilings: read {ceilings['read_gbs']:.0f} GB/s, copy {ceilings['copy_gbs']:.0f} GB/s")
 
-    workloads = None
+    workloads, outputs = None, []
     if not args.no_workloads:
         log("structured recipe stack")
         workloads = [recipe_line(stack, args.steps, args.warmup)]
         log("other workloads")
-        workloads += measure_workloads(stack, args.workload_calls)
+        workloads += measure_workloads(stack, args.workload_calls, outputs)
         for w in workloads:
             log(f"  {w['workload']}: {w['us_per_call']:.2f} us, frac {w['roofline_frac']:.3f}")
 
@@ -924,6 +976,9 @@ def main(argv=None):
         log(f"cpu baseline: oracle on a bounded sample (~{args.cpu_seconds:.0f} s)")
         cpu, parity = cpu_baseline(stack, args.cpu_seconds)
         log(f"  oracle {cpu['value']:.4f} GB/s; sampled parity max rel-L2 {parity['max_rel_l2']:.2e}")
+        if outputs:
+            parity["workloads"] = workload_parity(outputs)
+            log(f"  other workloads: max rel-L2 {parity['workloads']['max_rel_l2']:.2e}")
 
     out = {
         "metric": METRIC,
