@@ -141,3 +141,44 @@ def test_summarize_counters(tmp_path):
     assert "| SQ_INSTS_VALU | 600 |" in part498                      # (500 + 700) / 2
     assert "| GRBM_GUI_ACTIVE | 100 |" in part498                    # busiest XCD: (90 + 110) / 2
     assert "| SQ_INSTS_VALU | 400 |" in text.split("Launches of 729")[1]
+
+
+def test_workload_parity_recomputes_every_kind():
+    """bench.workload_parity regenerates each workload's rows from the seeded
+    draws and compares them with the given outputs: outputs equal to the
+    oracle's (here computed by the oracle itself, then perturbed by a known
+    relative 1e-6 or 1e-2) give that rel-L2 for every kind of output (GEMV at
+    one and four rows, fp16 and compact in-cell residuals, levels, GEMM), and
+    a sampled matrix is compared on its sampled rows only."""
+    import numpy as np
+
+    import oracle
+    import synth
+    outs = []
+    cases = [("gemv", 0, 0, synth.C0.projs[0], 1), ("gemv", 1, 1, synth.C1.projs[1], 4),
+             ("resid16", 2, 0, synth.C2.projs[0], 1), ("cell8", 2, 0, synth.C2.projs[0], 1),
+             ("levels", 2, 0, synth.C2.projs[0], 1), ("gemm", 4, 0, synth.C4.projs[0], 8)]
+    for i, (kind, cid, pi, proj, B) in enumerate(cases):
+        p = synth.Proj(proj.name, 96, proj.k, proj.mix)
+        key = synth.proj_key(cid, 0, pi)
+        W = synth.weights(synth.SEED, key, p.n, p.k)
+        q, s, o = oracle.quantize_matrix(W, synth.widths(synth.SEED, key, p.n, p.k // 64, p.mix))
+        if kind == "gemm":
+            y = oracle.gemm_bf16_weights(q, s, o, synth.x_bf16(synth.SEED, key, B, p.k))
+        elif kind == "levels":
+            lv, _ = oracle.rrq_levels(W, 4)
+            y = oracle.rrq_gemv(lv, synth.x_f16(synth.SEED, key, 1, p.k))
+        else:
+            x = synth.x_f16(synth.SEED, key, B, p.k)
+            f = synth.cell_f(synth.SEED, key, p.n, p.k)
+            y = (oracle.gemv(q, s, o, x) if kind == "gemv" else
+                 oracle.gemv(q, s, o, x, resid=oracle.cell8_decode(f, s)) if kind == "resid16" else
+                 oracle.gemv_cell8(q, s, o, x, f))
+        eps = 1e-2 if i == 2 else 1e-6
+        outs.append(dict(name=f"{kind}{i}", kind=kind, cid=cid, layer=0, pi=pi, proj=p, B=B, y=y * (1 + eps)))
+    res = bench.workload_parity(outs, max_rows=40)
+    for i, (kind, *_rest) in enumerate(cases):
+        r = res["outputs"][f"{kind}{i}"]
+        assert r["rows"] == 40
+        assert abs(r["rel_l2"] - (1e-2 if i == 2 else 1e-6)) < 1e-9
+    assert abs(res["max_rel_l2"] - 1e-2) < 1e-9
